@@ -1,0 +1,309 @@
+"""Pins of the double-precision oracle against facts fixed independently of it.
+
+Each test checks the oracle (``oracle.forward``, the token-by-token C
+recurrence) against something other than itself: a hand-worked example, a
+closed form, a brute-force formula of a different shape (explicit matrix
+products, plain causal linear attention), an invariant of the operator, or the
+independent chunked rewriting in ``oracle.chunked_ref``.  Together they are
+chosen so that a dropped term, a wrong sign, a shifted index or a transposed
+operand in the oracle fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import chunked_ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(seed, B=1, T=37, H=2, dk=8, dv=6, direction="fwd", la_shift=0.5, state_std=0.3):
+    w = synth.Workload("pin", B, H, T, dk, dv, "f32", direction, la_shift, state_std, seed)
+    return synth.generate(w)
+
+
+def _unit(x):
+    return x / np.maximum(np.linalg.norm(x, axis=-1, keepdims=True), 1e-6)
+
+
+def test_hand_worked_example():
+    """Two tokens worked by hand (tests/golden/hand_worked_2token.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_2token.json")))
+    inp, exp = g["inputs"], g["expected"]
+    q = np.array(inp["q"], np.float32)[None, :, None, :]
+    k = np.array(inp["k"], np.float32)[None, :, None, :]
+    v = np.array(inp["v"], np.float32)[None, :, None, :]
+    la = np.log(np.array([inp["alpha_fwd"], inp["alpha_rev"]], np.float64)).astype(np.float32)[:, None, :, None]
+    bt = np.array([inp["beta_fwd"], inp["beta_rev"]], np.float32)[:, None, :, None]
+    # log(1/2) is not exact in fp32: exp(fl(log 0.5)) differs from 0.5 by ~3e-8 relative
+    tol = dict(rtol=0, atol=1e-7)
+    o, s = oracle.forward(q, k, v, la[:1], bt[:1], None, "fwd")
+    np.testing.assert_allclose(o[0, :, 0], exp["out_fwd"], **tol)
+    np.testing.assert_allclose(s[0, 0, 0], exp["state_fwd"], **tol)
+    o, s = oracle.forward(q, k, v, la[1:], bt[1:], None, "rev")
+    np.testing.assert_allclose(o[0, :, 0], exp["out_rev"], **tol)
+    np.testing.assert_allclose(s[0, 0, 0], exp["state_rev"], **tol)
+    o, s = oracle.forward(q, k, v, la, bt, None, "bi")
+    np.testing.assert_allclose(o[0, :, 0], exp["out_bi"], **tol)
+    np.testing.assert_allclose(s[0, 0, 0], exp["state_fwd"], **tol)
+    np.testing.assert_allclose(s[1, 0, 0], exp["state_rev"], **tol)
+
+
+def test_no_write_no_decay_keeps_state():
+    """beta = 0, a = 1: nothing is written or erased, o_t = S_in q^_t exactly."""
+    x = _rand_problem(1)
+    la = np.zeros_like(x["log_alpha"])
+    bt = np.zeros_like(x["beta"])
+    o, s = oracle.forward(x["q"], x["k"], x["v"], la, bt, x["state_in"], "fwd")
+    S0 = x["state_in"][0, 0].astype(np.float64)
+    qh = _unit(x["q"][0].astype(np.float64))
+    ref = np.einsum("hvk,thk->thv", S0, qh)
+    np.testing.assert_allclose(o[0], ref, rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(s, x["state_in"].astype(np.float64))
+
+
+def _linear_attention(q, k, v, la, bt):
+    """Brute-force gated causal linear attention (no erase), one chain, double."""
+    qh, kh = _unit(q.astype(np.float64)), _unit(k.astype(np.float64))
+    g = np.cumsum(la.astype(np.float64))
+    T = q.shape[0]
+    out = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        for j in range(t + 1):
+            out[t] += np.exp(g[t] - g[j]) * bt[j] * (qh[t] @ kh[j]) * v[j]
+    return out
+
+
+def test_small_write_limit_is_linear_attention():
+    """a = 1, beta = eps: o_t / eps -> sum_{j<=t} (q^_t . k^_j) v_j (erase is O(eps^2))."""
+    x = _rand_problem(2, T=40, state_std=0.0)
+    eps = 1e-8
+    la = np.zeros_like(x["log_alpha"])
+    bt = np.full_like(x["beta"], eps)
+    o, _ = oracle.forward(x["q"], x["k"], x["v"], la, bt, None, "fwd")
+    for h in range(2):
+        ref = _linear_attention(x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h], la[0, 0, :, h],
+                                np.ones(40))
+        np.testing.assert_allclose(o[0, :, h] / np.float32(eps), ref, rtol=1e-5, atol=1e-6)
+
+
+def test_erase_off_equals_gated_linear_attention():
+    """Erase-off mode (S <- aS + beta v k^T) equals brute-force gated linear attention.
+
+    At a = 1, beta = 1 this is plain causal linear attention; the random gates
+    also pin where the decay is applied relative to the write.
+    """
+    x = _rand_problem(3, T=33, state_std=0.0)
+    o, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None, "fwd", erase=False)
+    for h in range(2):
+        ref = _linear_attention(x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h], x["log_alpha"][0, 0, :, h],
+                                x["beta"][0, 0, :, h].astype(np.float64))
+        np.testing.assert_allclose(o[0, :, h], ref, rtol=0, atol=1e-12)
+    ones = np.ones_like(x["beta"])
+    o, _ = oracle.forward(x["q"], x["k"], x["v"], np.zeros_like(x["log_alpha"]), ones, None, "fwd", erase=False)
+    ref = _linear_attention(x["q"][0, :, 0], x["k"][0, :, 0], x["v"][0, :, 0], np.zeros(33), np.ones(33))
+    np.testing.assert_allclose(o[0, :, 0], ref, rtol=0, atol=1e-12)
+
+
+def test_full_write_recalls_value():
+    """Unit keys, beta = 1, a = 1: after token t the state maps k^_t exactly to v_t."""
+    x = _rand_problem(4, T=12, dk=16, dv=5)
+    la = np.zeros_like(x["log_alpha"])
+    bt = np.ones_like(x["beta"])
+    for t in (0, 1, 5, 11):
+        sl = slice(0, t + 1)
+        _, s = oracle.forward(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], la[:, :, sl], bt[:, :, sl],
+                              x["state_in"], "fwd")
+        for h in range(2):
+            kh = _unit(x["k"][0, t, h].astype(np.float64))
+            np.testing.assert_allclose(s[0, 0, h] @ kh, x["v"][0, t, h], rtol=0, atol=1e-13)
+
+
+def test_transition_is_nonexpansive():
+    """beta in [0,1], unit keys: eigenvalues of I - beta k k^T are {1, 1-beta}, so with
+    v = 0 the state's Frobenius norm never grows (compare the non-expansive inherited
+    state of "Video DeltaNet", "Key Contributions" item 2)."""
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        kk = _unit(rng.standard_normal(9))
+        b = rng.uniform()
+        M = np.eye(9) - b * np.outer(kk, kk)
+        ev = np.sort(np.linalg.eigvalsh(M))
+        np.testing.assert_allclose(ev, np.sort(np.r_[1 - b, np.ones(8)]), atol=1e-12)
+        # power iteration on M^T M agrees: spectral norm <= 1
+        z = rng.standard_normal(9)
+        for _ in range(200):
+            z = M.T @ (M @ z)
+            z /= np.linalg.norm(z)
+        assert np.linalg.norm(M @ z) <= 1 + 1e-12
+    x = _rand_problem(5, T=30, state_std=1.0)
+    v0 = np.zeros_like(x["v"])
+    prev = np.linalg.norm(x["state_in"][0, 0, 0])
+    for t in range(30):
+        sl = slice(0, t + 1)
+        _, s = oracle.forward(x["q"][:, sl], x["k"][:, sl], v0[:, sl], x["log_alpha"][:, :, sl],
+                              x["beta"][:, :, sl], x["state_in"], "fwd")
+        cur = np.linalg.norm(s[0, 0, 0])
+        assert cur <= prev * (1 + 1e-14)
+        prev = cur
+
+
+def test_explicit_product_expansion():
+    """T <= 16: S_t = S_0 prod A_s + sum_j beta_j v_j k^_j^T prod_{j<s<=t} A_s with
+    A_s = a_s (I - beta_s k^_s k^_s^T) formed as explicit dk x dk matrices."""
+    x = _rand_problem(6, T=16, dk=7, dv=4)
+    o, s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "fwd")
+    for h in range(2):
+        kh = _unit(x["k"][0, :, h].astype(np.float64))
+        qh = _unit(x["q"][0, :, h].astype(np.float64))
+        a = np.exp(x["log_alpha"][0, 0, :, h].astype(np.float64))
+        b = x["beta"][0, 0, :, h].astype(np.float64)
+        v = x["v"][0, :, h].astype(np.float64)
+        A = [a[s_] * (np.eye(7) - b[s_] * np.outer(kh[s_], kh[s_])) for s_ in range(16)]
+        for t in range(16):
+            P = np.eye(7)
+            for s_ in range(t + 1):
+                P = P @ A[s_]
+            St = x["state_in"][0, 0, h].astype(np.float64) @ P
+            for j in range(t + 1):
+                Pj = np.eye(7)
+                for s_ in range(j + 1, t + 1):
+                    Pj = Pj @ A[s_]
+                St = St + b[j] * np.outer(v[j], kh[j]) @ Pj
+            np.testing.assert_allclose(o[0, t, h], St @ qh[t], rtol=0, atol=1e-13)
+            if t == 15:
+                np.testing.assert_allclose(s[0, 0, h], St, rtol=0, atol=1e-13)
+
+
+def test_linear_in_state_and_values():
+    """For fixed q, k and gates, (state_in, v) -> (out, state_out) is linear."""
+    x = _rand_problem(7, T=25)
+    y = _rand_problem(8, T=25)
+    c1, c2 = 0.75, -1.5
+    args = (x["q"], x["k"])
+    g = (x["log_alpha"], x["beta"])
+    o1, s1 = oracle.forward(*args, x["v"], *g, x["state_in"], "fwd")
+    o2, s2 = oracle.forward(*args, y["v"], *g, y["state_in"], "fwd")
+    vm = (c1 * x["v"].astype(np.float64) + c2 * y["v"].astype(np.float64)).astype(np.float32)
+    sm = (c1 * x["state_in"].astype(np.float64) + c2 * y["state_in"].astype(np.float64)).astype(np.float32)
+    # c1, c2 are exact binary fractions, but fp32 inputs of the combination are rounded:
+    # compare against the combination of the outputs with the rounded inputs' tolerance
+    o3, s3 = oracle.forward(*args, vm, *g, sm, "fwd")
+    np.testing.assert_allclose(o3, c1 * o1 + c2 * o2, rtol=0, atol=2e-6)
+    np.testing.assert_allclose(s3, c1 * s1 + c2 * s2, rtol=0, atol=2e-6)
+    # exact version: scaling by a power of two is exact in fp32
+    o4, s4 = oracle.forward(*args, x["v"] * 4, *g, x["state_in"] * 4, "fwd")
+    np.testing.assert_allclose(o4, 4 * o1, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(s4, 4 * s1, rtol=0, atol=1e-14)
+
+
+def test_reverse_is_flipped_forward_and_bidirectional_is_sum():
+    x = _rand_problem(9, T=29, direction="bi")
+    q, k, v, la, bt, s0 = x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"]
+    o_r, s_r = oracle.forward(q, k, v, la[1:], bt[1:], s0[1:], "rev")
+    f = lambda a, ax: np.ascontiguousarray(np.flip(a, axis=ax))
+    o_f, s_f = oracle.forward(f(q, 1), f(k, 1), f(v, 1), f(la[1:], 2), f(bt[1:], 2), s0[1:], "fwd")
+    np.testing.assert_allclose(o_r, f(o_f, 1), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(s_r, s_f, rtol=0, atol=1e-15)
+    o_fw, s_fw = oracle.forward(q, k, v, la[:1], bt[:1], s0[:1], "fwd")
+    o_b, s_b = oracle.forward(q, k, v, la, bt, s0, "bi")
+    np.testing.assert_allclose(o_b, o_fw + o_r, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(s_b[0], s_fw[0])
+    np.testing.assert_array_equal(s_b[1], s_r[0])
+
+
+def test_streaming_split_equals_one_call():
+    """State carried frame to frame equals one call over the concatenation."""
+    x = _rand_problem(10, T=50, H=3)
+    o, s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "fwd")
+    st = x["state_in"].astype(np.float64)
+    outs = []
+    for a, b in ((0, 13), (13, 14), (14, 50)):
+        sl = slice(a, b)
+        # the oracle takes a float32 state: carry in double through a float64 path
+        o_i, st_new = oracle.forward(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], x["log_alpha"][:, :, sl],
+                                     x["beta"][:, :, sl], st.astype(np.float32), "fwd")
+        outs.append(o_i)
+        st = st_new
+    # the carried state is rounded to fp32 between calls, so allow fp32-level error
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), o, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(st, s, rtol=0, atol=1e-6)
+    # exact version with zero state and split where the state is exactly representable:
+    # a = 0 at the split token resets the state, so frames are independent
+    la = x["log_alpha"].copy()
+    la[:, :, 20] = -1e3
+    o_full, _ = oracle.forward(x["q"], x["k"], x["v"], la, x["beta"], None, "fwd")
+    o_tail, _ = oracle.forward(x["q"][:, 20:], x["k"][:, 20:], x["v"][:, 20:], la[:, :, 20:],
+                               x["beta"][:, :, 20:], None, "fwd")
+    np.testing.assert_array_equal(o_full[:, 20:], o_tail)
+
+
+def test_zero_decay_closed_form():
+    """a = 0 (log_alpha = -1e3): o_t = beta_t (q^_t . k^_t) v_t and S_T = beta v k^^T."""
+    x = _rand_problem(11, T=21)
+    la = np.full_like(x["log_alpha"], -1e3)
+    o, s = oracle.forward(x["q"], x["k"], x["v"], la, x["beta"], x["state_in"], "fwd")
+    qh, kh = _unit(x["q"][0].astype(np.float64)), _unit(x["k"][0].astype(np.float64))
+    b = x["beta"][0, 0].astype(np.float64)
+    ref = (b * np.sum(qh * kh, -1))[..., None] * x["v"][0]
+    np.testing.assert_allclose(o[0], ref, rtol=0, atol=1e-15)
+    for h in range(2):
+        np.testing.assert_allclose(s[0, 0, h], b[-1, h] * np.outer(x["v"][0, -1, h], kh[-1, h]), atol=1e-15)
+
+
+def test_zero_key_token_only_decays():
+    """A zero key has no direction: k^ = 0, the step only decays the state."""
+    x = _rand_problem(12, T=3)
+    k = x["k"].copy()
+    k[:, 1] = 0
+    o, s = oracle.forward(x["q"][:, 1:2], k[:, 1:2], x["v"][:, 1:2], x["log_alpha"][:, :, 1:2],
+                          x["beta"][:, :, 1:2], x["state_in"], "fwd")
+    a = np.exp(x["log_alpha"][0, 0, 1].astype(np.float64))
+    np.testing.assert_allclose(s[0, 0], a[:, None, None] * x["state_in"][0, 0], rtol=1e-15, atol=0)
+
+
+def test_empty_sequence_passes_state_through():
+    x = _rand_problem(13, T=4)
+    sl = slice(0, 0)
+    o, s = oracle.forward(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], x["log_alpha"][:, :, sl],
+                          x["beta"][:, :, sl], x["state_in"], "fwd")
+    assert o.shape == (1, 0, 2, 6)
+    np.testing.assert_array_equal(s, x["state_in"].astype(np.float64))
+
+
+@pytest.mark.parametrize("direction", ["fwd", "rev", "bi"])
+@pytest.mark.parametrize("la_shift", [3.0, -5.0])
+def test_chunked_form_matches_token_oracle(direction, la_shift):
+    """The independent chunked rewriting agrees to ~1e-12 for every chunk size, with tails."""
+    x = _rand_problem(14, T=203, dk=16, dv=12, direction=direction, la_shift=la_shift)
+    o, s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction)
+    scale = np.sqrt(np.mean(o ** 2))
+    for C in (16, 32, 64, 128):
+        o2, s2 = chunked_ref.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"],
+                                     direction, C)
+        assert np.abs(o2 - o).max() <= 1e-12 * max(scale, 1)
+        assert np.abs(s2 - s).max() <= 1e-12 * max(np.abs(s).max(), 1)
+
+
+def test_bf16_inputs_are_widened_exactly():
+    w = synth.WORKLOADS["tiny"].replace(dtype="bf16", T=40)
+    x = synth.generate(w)
+    o1, s1 = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None, "fwd")
+    qf, kf, vf = (synth.bf16_to_f32(x[n]) for n in "qkv")
+    o2, s2 = oracle.forward(qf, kf, vf, x["log_alpha"], x["beta"], None, "fwd")
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_forward_heads_matches_full_run():
+    x = _rand_problem(15, B=2, H=3, T=20, direction="bi")
+    o, s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi")
+    heads = [(1, 2), (0, 1)]
+    oh, sh = oracle.forward_heads(x, heads, "bi")
+    for i, (b, h) in enumerate(heads):
+        np.testing.assert_array_equal(oh[i], o[b, :, h])
+        np.testing.assert_array_equal(sh[:, i], s[:, b, h])
