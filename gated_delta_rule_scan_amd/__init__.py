@@ -1,0 +1,160 @@
+"""Python binding of libgdn, the MI355X gated delta-rule scan.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libgdn.so`` (built in-tree by ``gated_delta_rule_scan_amd.build``).  PyTorch
+is used for device memory and the current stream.  There is no fallback: if
+the library is missing, every call raises.
+
+The C ABI (``include/gdn.h``) is mirrored name for name:
+``gdn_workspace_bytes``, ``gdn_forward``, ``gdn_status_string``,
+``gdn_version`` and the ``gdn_problem_t`` structure.  ``forward`` is a
+convenience wrapper that allocates outputs and workspace with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARGUMENT = 1
+GDN_ERR_UNSUPPORTED = 2
+GDN_ERR_WORKSPACE_TOO_SMALL = 3
+GDN_ERR_HIP = 4
+
+GDN_DIR_FORWARD = 0
+GDN_DIR_REVERSE = 1
+GDN_DIR_BIDIRECTIONAL = 2
+DIRECTIONS = {"fwd": GDN_DIR_FORWARD, "rev": GDN_DIR_REVERSE, "bi": GDN_DIR_BIDIRECTIONAL}
+
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+
+EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_status_string", "gdn_version")
+
+
+class gdn_problem_t(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("dv_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libgdn: {gdn_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_scan_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(gdn_problem_t)
+        vp = ctypes.c_void_p
+        L.gdn_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        L.gdn_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32]
+        L.gdn_forward.restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int32]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_version.argtypes = []
+        L.gdn_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def gdn_workspace_bytes(problem: gdn_problem_t, direction: int) -> int:
+    return int(lib().gdn_workspace_bytes(ctypes.byref(problem), int(direction)))
+
+
+def gdn_forward(problem: gdn_problem_t, q: int, k: int, v: int, log_alpha: int, beta: int,
+                state_in: Optional[int], state_out: Optional[int], out: int, direction: int) -> int:
+    """Raw call with integer device pointers (None for NULL); returns the status."""
+    return int(lib().gdn_forward(ctypes.byref(problem), q, k, v, log_alpha, beta, state_in, state_out, out,
+                                 int(direction)))
+
+
+def gdn_status_string(status: int) -> str:
+    return lib().gdn_status_string(int(status)).decode()
+
+
+def gdn_version() -> str:
+    return lib().gdn_version().decode()
+
+
+def make_problem(B, T, H, dk, dv, dtype: int, chunk: int = 0, dv_tile: int = 0, workspace: int = 0,
+                 workspace_bytes: int = 0, stream: int = 0) -> gdn_problem_t:
+    return gdn_problem_t(B, T, H, dk, dv, dtype, chunk, dv_tile, 0, workspace or None, workspace_bytes,
+                         stream or None)
+
+
+def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd", chunk: int = 0,
+                    dv_tile: int = 0) -> int:
+    dt = GDN_DTYPE_BF16 if dtype == "bf16" else GDN_DTYPE_F32
+    return gdn_workspace_bytes(make_problem(B, T, H, dk, dv, dt, chunk, dv_tile), DIRECTIONS[direction])
+
+
+def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chunk: int = 0, dv_tile: int = 0,
+            out=None, state_out=None, workspace=None, want_state: bool = True, stream=None) -> Tuple:
+    """Run the scan on torch CUDA tensors (layouts of include/gdn.h).
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv] (float32 or bfloat16, same dtype);
+    log_alpha, beta: [dirs,B,T,H] float32; state_in: [dirs,B,H,dv,dk] float32 or None.
+    Returns (out [B,T,H,dv] float32, state_out or None).  ``state_out`` may be
+    passed as the same tensor as ``state_in`` for an in-place carry.
+    """
+    import torch
+
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dirs = 2 if direction == "bi" else 1
+    if q.dtype == torch.bfloat16:
+        dt = GDN_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = GDN_DTYPE_F32
+    else:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous CUDA tensors of one dtype")
+    for t in (log_alpha, beta):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (dirs, B, T, H):
+            raise ValueError(f"gates must be contiguous float32 [{dirs},{B},{T},{H}]")
+    if state_in is not None and (state_in.dtype != torch.float32 or not state_in.is_contiguous()
+                                 or tuple(state_in.shape) != (dirs, B, H, dv, dk)):
+        raise ValueError(f"state_in must be contiguous float32 [{dirs},{B},{H},{dv},{dk}]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
+    prob = make_problem(B, T, H, dk, dv, dt, chunk, dv_tile)
+    nbytes = gdn_workspace_bytes(prob, DIRECTIONS[direction])
+    if nbytes == 0:
+        raise GdnError(GDN_ERR_UNSUPPORTED)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    prob.workspace = workspace.data_ptr()
+    prob.workspace_bytes = workspace.numel()
+    prob.stream = s.cuda_stream
+    st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
+                     None if state_in is None else state_in.data_ptr(),
+                     None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])
+    if st != GDN_OK:
+        raise GdnError(st)
+    return out, state_out

@@ -1,0 +1,163 @@
+// Shared device helpers for the libgdn kernels (gfx950 / CDNA4).
+//
+// Matrix-core fragments.  Every product in the chunked scan is issued as
+// 16x16 output tiles with a contraction slice of 32:
+//   * bf16 operands: one v_mfma_f32_16x16x32_bf16;
+//   * fp32 operands: eight v_mfma_f32_16x16x4_f32.
+// Both use the same lane layout (checked on gfx950):
+//   A (16 x 32, row-major source M[row][k]): lane l holds M[l%16][8*(l/16) .. +7]
+//   B (32 x 16, given transposed as Mt[col][k]): lane l holds Mt[l%16][8*(l/16) .. +7]
+//   D (16 x 16, fp32): lane l holds D[4*(l/16) + i][l%16], i = 0..3
+// For fp32 the eight k = 4 instructions take element j of every lane in
+// instruction j; the contraction is a sum over all 32 k, so pairing the same
+// (lane group, slot) of A and B gives the full product regardless of which
+// hardware k index a slot lands on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNormEps = 1e-6f;  // q^ = q / max(|q|, eps)
+
+template <typename MT>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const bf16* p) {  // 16-byte aligned
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  static __device__ __forceinline__ frag zero() {
+    frag z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+    return z;
+  }
+  static __device__ __forceinline__ float get(const frag& f, int e) { return (float)f[e]; }
+  static __device__ __forceinline__ void set(frag& f, int e, float x) { f[e] = (bf16)x; }
+  static __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {  // 8-byte aligned
+    bf16x4 v;
+    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *reinterpret_cast<bf16x4*>(p) = v;
+  }
+};
+
+template <>
+struct Mma<float> {
+  struct frag {
+    f32x4 lo, hi;
+  };
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ frag load(const float* p) {  // 16-byte aligned
+    frag f;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f;
+  }
+  static __device__ __forceinline__ frag zero() {
+    frag f;
+    f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+    f.hi = f.lo;
+    return f;
+  }
+  static __device__ __forceinline__ float get(const frag& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+  static __device__ __forceinline__ void set(frag& f, int e, float x) {
+    if (e < 4) f.lo[e] = x; else f.hi[e - 4] = x;
+  }
+  static __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {  // 16-byte aligned
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+// Load 8 consecutive input elements (16-byte aligned) as a fragment, or zeros.
+template <typename MT>
+__device__ __forceinline__ typename Mma<MT>::frag load_frag_global(const MT* p, bool valid) {
+  if (valid) return Mma<MT>::load(p);
+  return Mma<MT>::zero();
+}
+
+// Keep only the fragment elements whose column satisfies the triangle test
+// (lower: col < row; upper: col > row); the others become zero.
+template <typename MT>
+__device__ __forceinline__ typename Mma<MT>::frag mask_tri(typename Mma<MT>::frag f, int row, int col0, bool upper) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    int col = col0 + e;
+    bool keep = upper ? (col > row) : (col < row);
+    if (!keep) Mma<MT>::set(f, e, 0.0f);
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout (per problem; NBH = B*H chunk chains, NC chunks each,
+// dirs = number of computed directions):
+//   tri  [NBH*NC][C][C]  MT : strictly-lower part = forward (I+L)^{-1},
+//                             strictly-upper part = reverse (I+L)^{-1}
+//   pqk  [NBH*NC][C][C]  MT : strictly-lower = forward decayed q^.k^,
+//                             strictly-upper = reverse decayed q^.k^
+//   sc   [dirs][NBH*NC][C] float4 : {beta, e^g rk, e^g rq, e^(gn-g) rk}
+//   pd   [NBH*NC][C]     float : q^_t . k^_t (self term weight)
+//   gn   [dirs][NBH*NC]  float : e^(gn), the chunk's total decay
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  size_t tri, pqk, sc, pd, gn, total;
+};
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_t mt_bytes) {
+  WsLayout L;
+  size_t off = 0;
+  const size_t nch = (size_t)NBH * (size_t)NC;
+  L.tri = off; off = align_up(off + nch * C * C * mt_bytes, 256);
+  L.pqk = off; off = align_up(off + nch * C * C * mt_bytes, 256);
+  L.sc = off;  off = align_up(off + (size_t)dirs * nch * C * 16, 256);
+  L.pd = off;  off = align_up(off + nch * C * 4, 256);
+  L.gn = off;  off = align_up(off + (size_t)dirs * nch * 4, 256);
+  L.total = off;
+  return L;
+}
+
+// Arguments shared by both kernels.
+struct ScanArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const float* beta;
+  const float* state_in;
+  float* state_out;
+  float* out;
+  void* tri;
+  void* pqk;
+  float4* sc;
+  float* pd;
+  float* gn;
+  int64_t B, T, H, NC;
+  int dv;
+  int fwd_on, rev_on;  // which directions are computed
+  int dirs;            // number of computed directions (slots)
+};
+
+}  // namespace gdn

@@ -1,0 +1,335 @@
+// Chunk preparation kernel: everything of the chunked scan that does not
+// depend on the recurrent state.
+//
+// The recurrence S_t = a_t S_{t-1}(I - b_t k^_t k^_t^T) + b_t v_t k^_t^T can be
+// evaluated C tokens at a time.  The pages name the ingredients -- chunk-wise
+// scans and a fused blocked small-matrix inverse that stays on chip ("Video
+// DeltaNet", "Key Contributions" item 4 and "Main Findings", kernel
+// optimisations) -- and the chunk equations follow from the recurrence.  For
+// a chunk entered with state S (processing order r = 0..n-1):
+//
+//   g_r = sum_{j<=r} log_alpha_j,   Gam_ri = exp(g_r - g_i) (i <= r)
+//   L   = strictly_lower(diag(beta) (K^ K^^T) * Gam),   Tinv = (I + L)^{-1}
+//   X   = diag(beta)(V - diag(e^g) K^ S^T),   Vnew = Tinv X
+//   O   = diag(e^g) Q^ S^T + ((Q^ K^^T) * Gam) Vnew
+//   S'  = e^{g_last} S + Vnew^T diag(e^{g_last - g}) K^
+//
+// This kernel produces, per (batch, head, chunk), the state-independent
+// pieces: Tinv and the decayed Q^K^^T for both directions (the forward one
+// in the strictly-lower triangle, the reverse one -- the same recurrence with
+// tokens visited last-to-first -- in the strictly-upper triangle, both in
+// natural token order), the self-term weights q^_t.k^_t and the per-token
+// gate scales.  One Gram matrix K K^T serves both directions.
+//
+// Normalisation is never applied to the operands: K K^T and Q K^T are taken
+// on the raw inputs on the matrix cores (fp32 accumulation) and the fp32 row
+// scales rk = 1/max(|k|, eps), rq = 1/max(|q|, eps) are applied afterwards.
+//
+// The unit-triangular inverse is blocked in 16 x 16 tiles in LDS: the
+// diagonal tiles are inverted by substitution (one column per thread), then
+// off-diagonal tiles follow block diagonal by block diagonal from
+// T_IJ = -T_II sum_K L_IK T_KJ.
+#include "gdn_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+template <typename MT, int DK, int C>
+struct PrepSmem {
+  static constexpr int EP = 16 / (int)sizeof(MT);       // elements per 16-byte piece
+  static constexpr int KP = DK + EP;                    // padded row pitch of staged q/k
+  static constexpr int NB = C / 16;                     // 16 x 16 blocks per side
+  static constexpr int LP = C + 1;                      // pitch of fp32 C x C tiles
+  static constexpr size_t kq_bytes = (size_t)2 * C * KP * sizeof(MT);
+  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)2 * (NB > 1 ? NB - 1 : 1) * 16 * 17 * 4;
+  static constexpr size_t region = kq_bytes > inv_bytes ? kq_bytes : inv_bytes;
+};
+
+template <typename MT, int DK, int C>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
+  using SM = PrepSmem<MT, DK, C>;
+  using M = Mma<MT>;
+  constexpr int EP = SM::EP, KP = SM::KP, NB = SM::NB, LP = SM::LP;
+
+  __shared__ __align__(16) unsigned char smem[SM::region];
+  __shared__ float s_rk[C], s_rq[C];
+  __shared__ float s_la[2][C], s_bt[2][C], s_g[2][C];
+
+  MT* Ks = reinterpret_cast<MT*>(smem);
+  MT* Qs = Ks + C * KP;
+  float* Lm = reinterpret_cast<float*>(smem);  // reused after the Gram products
+  float* Ti = Lm + C * LP;
+  float* Wsc = Ti + C * LP;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t c = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int64_t T = a.T, H = a.H, B = a.B;
+  const int64_t t0 = c * C;
+  const int64_t cid = bh * a.NC + c;
+  const int fwd_on = a.fwd_on, rev_on = a.rev_on;
+  const int fslot = 0, rslot = fwd_on ? 1 : 0;
+
+  // ---- stage raw q and k of this chunk into LDS (padded rows are zero) ----
+  {
+    const MT* q = static_cast<const MT*>(a.q);
+    const MT* k = static_cast<const MT*>(a.k);
+    constexpr int PR = DK / EP;  // pieces per row
+    constexpr int NP = C * PR;   // pieces per matrix
+#pragma unroll
+    for (int p = tid; p < NP; p += 256) {
+      const int row = p / PR, cp = (p % PR) * EP;
+      const int64_t t = t0 + row;
+      f32x4 vq = {0.f, 0.f, 0.f, 0.f}, vk = {0.f, 0.f, 0.f, 0.f};
+      if (t < T) {
+        const int64_t off = ((b * T + t) * H + h) * DK + cp;
+        vq = *reinterpret_cast<const f32x4*>(q + off);
+        vk = *reinterpret_cast<const f32x4*>(k + off);
+      }
+      *reinterpret_cast<f32x4*>(Qs + row * KP + cp) = vq;
+      *reinterpret_cast<f32x4*>(Ks + row * KP + cp) = vk;
+    }
+  }
+  if (tid < C) {
+    const int64_t t = t0 + tid;
+    const bool in = t < T;
+    if (fwd_on) {
+      const int64_t gi = ((fslot * B + b) * T + t) * H + h;
+      s_la[0][tid] = in ? a.log_alpha[gi] : 0.f;
+      s_bt[0][tid] = in ? a.beta[gi] : 0.f;
+    }
+    if (rev_on) {
+      const int64_t gi = ((rslot * B + b) * T + t) * H + h;
+      s_la[1][tid] = in ? a.log_alpha[gi] : 0.f;
+      s_bt[1][tid] = in ? a.beta[gi] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- row scales and chunk-local cumulative log-gates ----
+  {
+    constexpr int G = 256 / C;        // threads per row
+    constexpr int PER = DK / G;       // elements per thread
+    const int row = tid / G, part = tid % G;
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float xq = to_f32(Qs[row * KP + part * PER + e]);
+      const float xk = to_f32(Ks[row * KP + part * PER + e]);
+      sq = fmaf(xq, xq, sq);
+      sk = fmaf(xk, xk, sk);
+    }
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) {
+      sq += __shfl_xor(sq, m, 64);
+      sk += __shfl_xor(sk, m, 64);
+    }
+    if (part == 0) {
+      s_rq[row] = 1.0f / fmaxf(sqrtf(sq), kNormEps);
+      s_rk[row] = 1.0f / fmaxf(sqrtf(sk), kNormEps);
+    }
+  }
+  if (tid < C) {
+    if (fwd_on) {  // inclusive prefix sum in token order
+      float s = 0.f;
+      for (int j = 0; j <= tid; ++j) s += s_la[0][j];
+      s_g[0][tid] = s;
+    }
+    if (rev_on) {  // inclusive suffix sum, accumulated in reverse visiting order
+      float s = 0.f;
+      for (int j = C - 1; j >= tid; --j) s += s_la[1][j];
+      s_g[1][tid] = s;
+    }
+  }
+  __syncthreads();
+
+  // ---- Gram K K^T and Q K^T on the matrix cores (raw operands, fp32 accumulate) ----
+  constexpr int NT2 = NB * NB;
+  constexpr int UPW = (NT2 + 3) / 4;
+  f32x4 accG[UPW], accP[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    accG[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accP[j] = accG[j];
+    const int u = wave + 4 * j;
+    if (u < NT2) {
+      const int ti = u / NB, tj = u % NB;
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const typename M::frag ka = M::load(Ks + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
+        const typename M::frag qa = M::load(Qs + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
+        const typename M::frag kb = M::load(Ks + (16 * tj + l16) * KP + 32 * ks + 8 * g4);
+        accG[j] = M::mma(ka, kb, accG[j]);
+        accP[j] = M::mma(qa, kb, accP[j]);
+      }
+    }
+  }
+  __syncthreads();  // q/k staging area is reused below
+
+  // ---- gated, scaled triangles: L into LDS, decayed Q^K^^T to the workspace ----
+  MT* pqk = static_cast<MT*>(a.pqk) + cid * C * C;
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int u = wave + 4 * j;
+    if (u < NT2) {
+      const int ti = u / NB, tj = u % NB;
+      const int col = 16 * tj + l16;
+      const float rkc = s_rk[col];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ti + 4 * g4 + i;
+        float lv = 0.f, pv = 0.f;
+        if (col < r) {
+          if (fwd_on) {
+            const float gam = expf(s_g[0][r] - s_g[0][col]);
+            lv = s_bt[0][r] * s_rk[r] * rkc * accG[j][i] * gam;
+            pv = s_rq[r] * rkc * accP[j][i] * gam;
+          }
+        } else if (col > r) {
+          if (rev_on) {
+            const float gam = expf(s_g[1][r] - s_g[1][col]);
+            lv = s_bt[1][r] * s_rk[r] * rkc * accG[j][i] * gam;
+            pv = s_rq[r] * rkc * accP[j][i] * gam;
+          }
+        } else {
+          a.pd[cid * C + r] = s_rq[r] * s_rk[r] * accP[j][i];
+        }
+        Lm[r * LP + col] = lv;
+        pqk[r * C + col] = (MT)pv;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- diagonal 16 x 16 blocks: one column of the inverse per thread ----
+  if (tid < 2 * NB * 16) {
+    const int dir = tid / (NB * 16);
+    const int blk = (tid / 16) % NB;
+    const int jc = tid % 16;
+    const int b0 = 16 * blk;
+    if (dir == 0 && fwd_on) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) s = fmaf(Lm[(b0 + r) * LP + b0 + i], x[i], s);
+        x[r] = (r < jc) ? 0.f : ((r == jc) ? 1.f : -s);
+        if (r >= jc) Ti[(b0 + r) * LP + b0 + jc] = x[r];
+      }
+    } else if (dir == 1 && rev_on) {
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int r = 15 - rr;
+        float s = 0.f;
+#pragma unroll
+        for (int i = r + 1; i < 16; ++i) s = fmaf(Lm[(b0 + r) * LP + b0 + i], x[i], s);
+        x[r] = (r > jc) ? 0.f : ((r == jc) ? 1.f : -s);
+        if (r <= jc) Ti[(b0 + r) * LP + b0 + jc] = x[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- off-diagonal blocks, one block diagonal at a time ----
+#pragma unroll
+  for (int d = 1; d < NB; ++d) {
+    const int nbk = NB - d;
+    const int items = 2 * nbk * 256;
+    for (int it = tid; it < items; it += 256) {
+      const int dir = it / (nbk * 256);
+      const int bk = (it / 256) % nbk;
+      const int r = (it / 16) % 16, cc = it % 16;
+      if ((dir == 0 && !fwd_on) || (dir == 1 && !rev_on)) continue;
+      float s = 0.f;
+      if (dir == 0) {
+        const int I = d + bk, J = bk;
+        for (int K = J; K < I; ++K)
+          for (int m = 0; m < 16; ++m) {
+            if (K == J && m < cc) continue;  // lower-triangular diagonal block
+            s = fmaf(Lm[(16 * I + r) * LP + 16 * K + m], Ti[(16 * K + m) * LP + 16 * J + cc], s);
+          }
+      } else {
+        const int I = bk, J = bk + d;
+        for (int K = I + 1; K <= J; ++K)
+          for (int m = 0; m < 16; ++m) {
+            if (K == J && m > cc) continue;  // upper-triangular diagonal block
+            s = fmaf(Lm[(16 * I + r) * LP + 16 * K + m], Ti[(16 * K + m) * LP + 16 * J + cc], s);
+          }
+      }
+      Wsc[((dir * (NB - 1) + bk) * 16 + r) * 17 + cc] = s;
+    }
+    __syncthreads();
+    for (int it = tid; it < items; it += 256) {
+      const int dir = it / (nbk * 256);
+      const int bk = (it / 256) % nbk;
+      const int r = (it / 16) % 16, cc = it % 16;
+      if ((dir == 0 && !fwd_on) || (dir == 1 && !rev_on)) continue;
+      const int I = dir == 0 ? d + bk : bk;
+      const int J = dir == 0 ? bk : bk + d;
+      float s = 0.f;
+      const float* w = Wsc + (dir * (NB - 1) + bk) * 16 * 17;
+      if (dir == 0) {
+        for (int m = 0; m <= r; ++m) s = fmaf(Ti[(16 * I + r) * LP + 16 * I + m], w[m * 17 + cc], s);
+      } else {
+        for (int m = r; m < 16; ++m) s = fmaf(Ti[(16 * I + r) * LP + 16 * I + m], w[m * 17 + cc], s);
+      }
+      Ti[(16 * I + r) * LP + 16 * J + cc] = -s;
+    }
+    __syncthreads();
+  }
+
+  // ---- write the strict triangles of both inverses ----
+  {
+    MT* tri = static_cast<MT*>(a.tri) + cid * C * C;
+    for (int p = tid; p < C * C; p += 256) {
+      const int r = p / C, col = p % C;
+      float v = 0.f;
+      if (col < r && fwd_on) v = Ti[r * LP + col];
+      if (col > r && rev_on) v = Ti[r * LP + col];
+      tri[p] = (MT)v;
+    }
+  }
+  // ---- per-token scales and the chunk decay ----
+  if (tid < C) {
+    const bool in = (t0 + tid) < T;
+    const float rk = s_rk[tid], rq = s_rq[tid];
+    if (fwd_on) {
+      const float g = s_g[0][tid], gl = s_g[0][C - 1];
+      const float eg = expf(g);
+      float4 v = in ? make_float4(s_bt[0][tid], eg * rk, eg * rq, expf(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      a.sc[(size_t)fslot * a.B * a.H * a.NC * C + cid * C + tid] = v;
+      if (tid == 0) a.gn[(size_t)fslot * a.B * a.H * a.NC + cid] = expf(gl);
+    }
+    if (rev_on) {
+      const float g = s_g[1][tid], gl = s_g[1][0];
+      const float eg = expf(g);
+      float4 v = in ? make_float4(s_bt[1][tid], eg * rk, eg * rq, expf(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      a.sc[(size_t)rslot * a.B * a.H * a.NC * C + cid * C + tid] = v;
+      if (tid == 0) a.gn[(size_t)rslot * a.B * a.H * a.NC + cid] = expf(gl);
+    }
+  }
+}
+
+template <typename MT, int DK, int C>
+hipError_t launch_prep(const ScanArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)a.NC, (unsigned)(a.B * a.H));
+  hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+#define GDN_INST_PREP(MT, DK, C) template hipError_t launch_prep<MT, DK, C>(const ScanArgs&, hipStream_t);
+GDN_INST_PREP(float, 64, 32)
+GDN_INST_PREP(float, 64, 64)
+GDN_INST_PREP(float, 128, 32)
+GDN_INST_PREP(float, 128, 64)
+GDN_INST_PREP(bf16, 64, 32)
+GDN_INST_PREP(bf16, 64, 64)
+GDN_INST_PREP(bf16, 128, 32)
+GDN_INST_PREP(bf16, 128, 64)
+
+}  // namespace gdn

@@ -1,0 +1,124 @@
+/*
+ * libgdn -- gated delta-rule linear-attention scan for AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the gated delta-net linear attention with a matrix-valued
+ * recurrent state per head ("[Research] Explore linear attention for the
+ * streaming video models", section "We already ship a hybrid linear-attention
+ * model"); the state is written one token at a time as standard delta-rule
+ * linear attention does ("Video DeltaNet: A Video-Native Hybrid Attention for
+ * Livestream Video Generation", section "Methodology in Plain English").
+ * Per (batch b, head h), with the state S in R^{dv x dk} (fp32):
+ *
+ *   q^_t = q_t / max(|q_t|_2, 1e-6),   k^_t = k_t / max(|k_t|_2, 1e-6)
+ *   S_t  = a_t S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,  a_t = exp(log_alpha_t)
+ *   o_t  = S_t q^_t
+ *
+ * Directions:
+ *   GDN_DIR_FORWARD       causal scan t = 0..T-1; the forward-only causal
+ *                         form used for streaming rollout (the issue's
+ *                         "Open questions and risks": causal streaming scan).
+ *   GDN_DIR_REVERSE       the same recurrence run from t = T-1 down to 0.
+ *   GDN_DIR_BIDIRECTIONAL out = forward readout + reverse readout, each
+ *                         direction with its own (log_alpha, beta) and its own
+ *                         initial state ("Video DeltaNet", "Methodology in
+ *                         Plain English": forward and backward recurrent
+ *                         states whose readouts are added).  The reverse
+ *                         readout includes the current token.
+ *
+ * Streaming: the final state of one call is the initial state of the next
+ * (the streaming state lifecycle of the issue's "Suggested phases", phase 1);
+ * chaining calls over consecutive token ranges equals one call over their
+ * concatenation.
+ *
+ * Layouts (all row-major and contiguous; base pointers 16-byte aligned):
+ *   q, k       [B, T, H, dk]   dtype (fp32 or bf16)
+ *   v          [B, T, H, dv]   dtype
+ *   log_alpha  [dirs, B, T, H] fp32, finite and <= 0 (caller's contract)
+ *   beta       [dirs, B, T, H] fp32, finite (beta in [0,1] keeps the
+ *                              transition non-expansive)
+ *   state_in   [dirs, B, H, dv, dk] fp32, or NULL for a zero initial state
+ *   state_out  [dirs, B, H, dv, dk] fp32, or NULL to skip writing it
+ *   out        [B, T, H, dv]   fp32
+ * dirs = 2 for GDN_DIR_BIDIRECTIONAL, else 1 (slot 0 then holds the single
+ * direction's gates and states).
+ *
+ * Ownership and execution: every pointer is caller-owned device memory.  The
+ * library allocates nothing, keeps no state between calls, does not
+ * synchronise and reads no environment variables, so a call can be captured
+ * in a HIP graph.  All work is enqueued on `stream` (NULL: the default stream)
+ * and completes asynchronously.  state_in == state_out is allowed (in-place
+ * streaming carry); any other overlap between `out`, the state buffers, the
+ * workspace and the inputs is rejected.  Results are bitwise deterministic for
+ * fixed inputs, chunk size and device (no atomics in any reduction).
+ *
+ * Errors: argument problems are reported before anything is enqueued and
+ * leave every output untouched.  GDN_ERR_HIP reports a failed launch; faults
+ * during execution surface at the caller's next synchronisation, as with any
+ * stream work.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1,   /* NULL/misaligned pointer, bad size, overlap, bad direction */
+  GDN_ERR_UNSUPPORTED = 2,        /* dk, dv, chunk, tile or dtype outside the compiled set */
+  GDN_ERR_WORKSPACE_TOO_SMALL = 3,
+  GDN_ERR_HIP = 4                 /* a kernel launch failed */
+} gdn_status_t;
+
+typedef enum {
+  GDN_DIR_FORWARD = 0,
+  GDN_DIR_REVERSE = 1,
+  GDN_DIR_BIDIRECTIONAL = 2
+} gdn_direction_t;
+
+typedef enum {
+  GDN_DTYPE_F32 = 0,
+  GDN_DTYPE_BF16 = 1
+} gdn_dtype_t;
+
+/* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
+ * chunk in {0 (= 64), 32, 64}; dv_tile in {0 (= automatic), 16, 32, 64}
+ * (must divide dv); B, H >= 1; T >= 0. */
+typedef struct {
+  int64_t B, T, H, dk, dv;
+  int32_t dtype;            /* gdn_dtype_t: type of q, k, v */
+  int32_t chunk;            /* tokens per chunk of the chunked evaluation */
+  int32_t dv_tile;          /* value columns per workgroup of the state chain */
+  int32_t reserved;         /* must be 0 */
+  void* workspace;          /* caller-owned device memory, 256-byte aligned */
+  size_t workspace_bytes;
+  void* stream;             /* hipStream_t; NULL = default stream */
+} gdn_problem_t;
+
+/* Bytes of workspace gdn_forward needs for this problem and direction
+ * (0 if the problem is invalid or unsupported).  Pure host arithmetic. */
+size_t gdn_workspace_bytes(const gdn_problem_t* p, int32_t direction);
+
+/* Enqueue the scan described by `p` on p->stream.  See the file comment for
+ * layouts; `direction` is a gdn_direction_t. */
+gdn_status_t gdn_forward(const gdn_problem_t* p,
+                         const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta,
+                         const float* state_in, float* state_out,
+                         float* out, int32_t direction);
+
+/* Static description of a status code. */
+const char* gdn_status_string(int32_t status);
+
+/* Library version string. */
+const char* gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */
