@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of libgdn on one MI355X: the gated delta-rule scan hot path.
+
+One step = one gdn_forward call (chunk preparation + state chain) over the
+whole synthetic input of the workload, inputs already resident in HBM.
+Default workload: the 480p bidirectional DiT linear block, B=2, H=16,
+T=32760 (21 latent frames of 30x52 tokens), dk=dv=128, bf16 inputs, fp32
+state and output, forward + reverse scans summed.
+
+Prints ONE JSON line with tokens/s (B*T tokens per step), the algorithmic
+TFLOP/s and fraction of the bf16 matrix-core peak, the per-kernel roofline of
+the dominant kernel measured live with HIP events, and the double-precision
+oracle timed on the host on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload bidir480]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_HBM_GBS = 8000.0          # published HBM3E bandwidth
+MI355X_BF16_TFLOPS = 2516.6      # dense bf16 matrix peak: 256 CU x 4096 flop/clk x 2.4 GHz
+MI355X_FP32_TFLOPS = 157.3
+REF_CHUNK = 64                   # chunk length the algorithmic flop count is quoted at
+
+
+def flops_per_token_head_dir(dk: int, dv: int, C: int = REF_CHUNK) -> float:
+    """Algorithmic flops of the chunked method per token, head and direction:
+    W S^T, Q S^T, K^T Vnew (2 C dk dv per chunk each); K K^T strict, Q K^T,
+    Tinv (beta gamma K) (C(C+-1) dk); Tinv (beta V) and P Vnew (C(C+1) dv);
+    the triangular inverse (C^3/3), all divided by C."""
+    return 6 * dk * dv + (3 * C + 1) * dk + 2 * (C + 1) * dv + C * C / 3.0
+
+
+def path_bytes(w, xs: int) -> float:
+    """Boundary tensors read once and written once (workspace excluded)."""
+    th = w.B * w.T * w.H
+    per_th = (2 * w.dk + w.dv) * xs + w.dirs * 8 + w.dv * 4
+    states = w.dirs * w.B * w.H * w.dv * w.dk * 4 * (2 if w.state_std > 0 else 1)
+    return th * per_th + states
+
+
+def kernel_bytes(w, xs: int, C: int) -> dict:
+    """Algorithmic bytes of each kernel: its own inputs and outputs, each once."""
+    th = w.B * w.T * w.H
+    chunk_ops = 2 * C * xs                      # Tinv and decayed QK^T (C x C per chunk) per token
+    scal = w.dirs * 16 + 4                      # per-token scales and self-term weight
+    prep = th * (2 * w.dk * xs + w.dirs * 8 + chunk_ops + scal)
+    states = w.dirs * w.B * w.H * w.dv * w.dk * 4 * (2 if w.state_std > 0 else 1)
+    chain = th * ((2 * w.dk + w.dv) * xs + chunk_ops + scal + w.dv * 4) + states
+    return {"prep": prep, "chain": chain}
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through the HIP runtime (the library records them
+    on the stream its kernels run on)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = h
+        self.n = n
+
+    def ptr(self, i: int) -> int:
+        return ctypes.addressof(self.arr) + i * ctypes.sizeof(ctypes.c_void_p)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def cpu_baseline(w, x, target_s: float) -> dict:
+    """Time the double-precision oracle on the host on a bounded sample of the
+    workload: every (batch, head) chain if that fits about `target_s` seconds,
+    else the first tokens of every chain."""
+    import oracle
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    cal_T = min(w.T, 1024)
+    t0 = time.perf_counter()
+    oracle.forward_heads({"q": x["q"][:, :cal_T], "k": x["k"][:, :cal_T], "v": x["v"][:, :cal_T],
+                          "log_alpha": x["log_alpha"][:1, :, :cal_T], "beta": x["beta"][:1, :, :cal_T],
+                          "state_in": None}, [(0, 0)], "fwd", nthreads=1)
+    per_tok = (time.perf_counter() - t0) / cal_T           # one chain, one thread
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    n_chains = len(heads) * w.dirs
+    waves = -(-n_chains // threads)
+    est = waves * w.T * per_tok
+    Ts = w.T if est <= target_s else max(1024, int(w.T * target_s / est))
+    xs = {"q": x["q"][:, :Ts], "k": x["k"][:, :Ts], "v": x["v"][:, :Ts],
+          "log_alpha": x["log_alpha"][:, :, :Ts], "beta": x["beta"][:, :, :Ts], "state_in": x["state_in"]}
+    t0 = time.perf_counter()
+    oracle.forward_heads(xs, heads, w.direction, nthreads=threads)
+    dt = time.perf_counter() - t0
+    thd = n_chains * Ts / dt                                # token-head-directions per second
+    used = min(threads, n_chains)
+    what = "the whole workload" if Ts == w.T else f"the first {Ts} of {w.T} tokens of every chain"
+    return {"value": thd / (w.H * w.dirs), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{what}: {len(heads)} heads x {w.dirs} direction(s), {used} threads, {dt:.1f} s; "
+                      f"tokens/s = token-head-directions/s / (H*dirs)",
+            "seconds": round(dt, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bidir480")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--dv-tile", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the scan shards over (batch, head, "
+                                   "direction) chains with no communication, see DESIGN.md; run with --gpus 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.frame:
+        raise SystemExit("the streaming workload is exercised by the tests; bench one-call workloads")
+    xs = 2 if w.dtype == "bf16" else 4
+    x = synth.generate(w)
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    s_out = torch.empty((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+    nws = gdn.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.direction, args.chunk, args.dv_tile)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    C = args.chunk or 64
+
+    def step(ev_ptr=None):
+        gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction, chunk=args.chunk,
+                    dv_tile=args.dv_tile, out=out, state_out=s_out, workspace=ws, timing_events=ev_ptr)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = HipEvents(3 * K)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(ev.ptr(3 * i))
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(stop) / K
+    prep_ms = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(K)) / K
+    chain_ms = sum(ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(K)) / K
+    ev.close()
+
+    tokens = w.B * w.T
+    th_dirs = w.B * w.T * w.H * w.dirs
+    flops = th_dirs * flops_per_token_head_dir(w.dk, w.dv)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    pbytes = path_bytes(w, xs)
+    kb = kernel_bytes(w, xs, C)
+    kt = {"prep": prep_ms, "chain": chain_ms}
+    dom = max(kt, key=kt.get)
+    achieved = kb[dom] / (kt[dom] * 1e-3) / 1e9
+    peak_mfma = MI355X_BF16_TFLOPS if w.dtype == "bf16" else MI355X_FP32_TFLOPS
+    res = {
+        "metric": "gated-delta scan tokens/s + TFLOP/s (% MFMA peak) at 480p latent, 1 MI355X",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "direction": w.direction, "chunk": C, "dv_tile": args.dv_tile or "auto",
+                   "inputs": "seeded synthetic video-latent-shaped (synth.WORKLOADS)"},
+        "tflops": tflops,
+        "mfma_frac": tflops / peak_mfma,
+        "path_hbm_gbs": pbytes / (ms_step * 1e-3) / 1e9,
+        "path_hbm_frac": pbytes / (ms_step * 1e-3) / 1e9 / MI355X_HBM_GBS,
+        "kernels_ms": {"chunk_prep": prep_ms, "state_chain": chain_ms},
+        "roofline": {"kernel": "chain_kernel" if dom == "chain" else "chunk_prep_kernel", "bound": "hbm",
+                     "achieved": achieved, "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": achieved / MI355X_HBM_GBS,
+                     "traffic": None, "alg_bytes_per_launch": kb[dom], "avg_launch_ms": kt[dom]},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        res["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

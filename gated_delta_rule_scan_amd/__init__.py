@@ -44,6 +44,7 @@ class gdn_problem_t(ctypes.Structure):
         ("dv_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("timing_events", ctypes.c_void_p),
     ]
 
 
@@ -99,7 +100,7 @@ def gdn_version() -> str:
 def make_problem(B, T, H, dk, dv, dtype: int, chunk: int = 0, dv_tile: int = 0, workspace: int = 0,
                  workspace_bytes: int = 0, stream: int = 0) -> gdn_problem_t:
     return gdn_problem_t(B, T, H, dk, dv, dtype, chunk, dv_tile, 0, workspace or None, workspace_bytes,
-                         stream or None)
+                         stream or None, None)
 
 
 def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd", chunk: int = 0,
@@ -109,7 +110,8 @@ def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd"
 
 
 def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chunk: int = 0, dv_tile: int = 0,
-            out=None, state_out=None, workspace=None, want_state: bool = True, stream=None) -> Tuple:
+            out=None, state_out=None, workspace=None, want_state: bool = True, stream=None,
+            timing_events: Optional[int] = None) -> Tuple:
     """Run the scan on torch CUDA tensors (layouts of include/gdn.h).
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv] (float32 or bfloat16, same dtype);
@@ -152,6 +154,7 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     prob.workspace = workspace.data_ptr()
     prob.workspace_bytes = workspace.numel()
     prob.stream = s.cuda_stream
+    prob.timing_events = timing_events
     st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                      None if state_in is None else state_in.data_ptr(),
                      None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])

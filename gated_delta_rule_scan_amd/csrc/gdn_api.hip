@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "gdn.h"
 #include "gdn_common.h"
 #include "gdn_internal.h"
@@ -26,6 +28,11 @@ struct Plan {
 };
 
 bool supported_dim(int64_t d) { return d == 64 || d == 128; }
+
+// fp32 operands with dk = 128 and 64-token chunks only fit LDS with 16-wide tiles.
+bool tile_fits(int32_t dtype, int64_t dk, int C, int NT) {
+  return !(NT == 2 && dtype == GDN_DTYPE_F32 && dk == 128 && C == 64);
+}
 
 int pick_tiles(int64_t nbh, int64_t dv) {
   // Largest tile width that still gives about one workgroup per compute unit.
@@ -48,9 +55,11 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   int NT;
   if (p->dv_tile == 0) {
     NT = pick_tiles(p->B * p->H, p->dv);
+    if (!tile_fits(p->dtype, p->dk, C, NT)) NT = 1;
   } else {
     if (p->dv_tile != 16 && p->dv_tile != 32) return GDN_ERR_UNSUPPORTED;
     NT = p->dv_tile / 16;
+    if (!tile_fits(p->dtype, p->dk, C, NT)) return GDN_ERR_UNSUPPORTED;
   }
   if (p->dv % (16 * NT) != 0) return GDN_ERR_UNSUPPORTED;
   pl->C = C;
@@ -89,7 +98,11 @@ prep_fn prep_for(int dk, int C) {
 template <typename MT, int DK, int C>
 chain_fn chain_for3(int NT, int dirs) {
   if (NT == 1) return dirs == 2 ? launch_chain<MT, DK, C, 1, 2> : launch_chain<MT, DK, C, 1, 1>;
-  return dirs == 2 ? launch_chain<MT, DK, C, 2, 2> : launch_chain<MT, DK, C, 2, 1>;
+  if constexpr (std::is_same<MT, float>::value && DK == 128 && C == 64) {
+    return nullptr;  // rejected by make_plan
+  } else {
+    return dirs == 2 ? launch_chain<MT, DK, C, 2, 2> : launch_chain<MT, DK, C, 2, 1>;
+  }
 }
 
 template <typename MT>
@@ -162,24 +175,30 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
     a.sc = reinterpret_cast<float4*>(ws + pl.ws.sc);
     a.pd = reinterpret_cast<float*>(ws + pl.ws.pd);
     a.gn = reinterpret_cast<float*>(ws + pl.ws.gn);
+    a.trash = reinterpret_cast<float*>(ws + pl.ws.trash);
   }
   a.B = B; a.T = T; a.H = H; a.NC = pl.NC; a.dv = (int)dv;
   a.fwd_on = pl.fwd_on; a.rev_on = pl.rev_on; a.dirs = pl.dirs;
 
   const bool bf = p->dtype == GDN_DTYPE_BF16;
+  hipEvent_t* ev = static_cast<hipEvent_t*>(p->timing_events);
   hipError_t e = hipSuccess;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return GDN_ERR_HIP;
   if (pl.NC > 0) {
     prep_fn pf = bf ? prep_for<bf16>((int)dk, pl.C) : prep_for<float>((int)dk, pl.C);
     e = pf(a, stream);
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return GDN_ERR_HIP;
   // bidirectional: both direction groups in one workgroup; single direction:
   // one group, told whether it runs in reverse
   const int dirs_in_wg = pl.dirs;
   chain_fn cf = bf ? chain_for<bf16>((int)dk, pl.C, pl.NT, dirs_in_wg)
                    : chain_for<float>((int)dk, pl.C, pl.NT, dirs_in_wg);
+  if (!cf) return GDN_ERR_UNSUPPORTED;
   e = cf(a, direction == GDN_DIR_REVERSE ? 1 : 0, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return GDN_ERR_HIP;
   return GDN_OK;
 }
 

@@ -119,9 +119,12 @@ __device__ __forceinline__ typename Mma<MT>::frag mask_tri(typename Mma<MT>::fra
 //   sc   [dirs][NBH*NC][C] float4 : {beta, e^g rk, e^g rq, e^(gn-g) rk}
 //   pd   [NBH*NC][C]     float : q^_t . k^_t (self term weight)
 //   gn   [dirs][NBH*NC]  float : e^(gn), the chunk's total decay
+//   trash [256]          float : sink for stores that must not land in `out`
+//                                (rows past the sequence end), so the state
+//                                chain can store without branching
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t tri, pqk, sc, pd, gn, total;
+  size_t tri, pqk, sc, pd, gn, trash, total;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -135,6 +138,7 @@ static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_
   L.sc = off;  off = align_up(off + (size_t)dirs * nch * C * 16, 256);
   L.pd = off;  off = align_up(off + nch * C * 4, 256);
   L.gn = off;  off = align_up(off + (size_t)dirs * nch * 4, 256);
+  L.trash = off; off = align_up(off + 256 * 4, 256);
   L.total = off;
   return L;
 }
@@ -154,6 +158,7 @@ struct ScanArgs {
   float4* sc;
   float* pd;
   float* gn;
+  float* trash;
   int64_t B, T, H, NC;
   int dv;
   int fwd_on, rev_on;  // which directions are computed

@@ -86,8 +86,9 @@ typedef enum {
 } gdn_dtype_t;
 
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
- * chunk in {0 (= 64), 32, 64}; dv_tile in {0 (= automatic), 16, 32, 64}
- * (must divide dv); B, H >= 1; T >= 0. */
+ * chunk in {0 (= 64), 32, 64}; dv_tile in {0 (= automatic), 16, 32}
+ * (must divide dv; fp32 inputs with dk = 128 and 64-token chunks take 16
+ * only); B, H >= 1, B*H <= 65535; 0 <= T <= 2^30. */
 typedef struct {
   int64_t B, T, H, dk, dv;
   int32_t dtype;            /* gdn_dtype_t: type of q, k, v */
@@ -97,6 +98,10 @@ typedef struct {
   void* workspace;          /* caller-owned device memory, 256-byte aligned */
   size_t workspace_bytes;
   void* stream;             /* hipStream_t; NULL = default stream */
+  void* timing_events;      /* NULL, or hipEvent_t[3] recorded on `stream`
+                               before the chunk-preparation kernel, between the
+                               two kernels and after the state-chain kernel
+                               (per-kernel timing; caller-owned events) */
 } gdn_problem_t;
 
 /* Bytes of workspace gdn_forward needs for this problem and direction
