@@ -25,10 +25,11 @@
 // on the raw inputs on the matrix cores (fp32 accumulation) and the fp32 row
 // scales rk = 1/max(|k|, eps), rq = 1/max(|q|, eps) are applied afterwards.
 //
-// The unit-triangular inverse is blocked in 16 x 16 tiles in LDS: the
+// The unit-triangular inverse is blocked in 16 x 16 tiles in LDS (fp32): the
 // diagonal tiles are inverted by substitution (one column per thread), then
-// off-diagonal tiles follow block diagonal by block diagonal from
-// T_IJ = -T_II sum_K L_IK T_KJ.
+// each column of off-diagonal tiles follows from T_IJ = -T_II sum_K L_IK T_KJ
+// on the fp32 matrix cores.  A block column only depends on itself and on
+// the diagonal tiles, so each column is one wave's private chain.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -40,8 +41,9 @@ struct PrepSmem {
   static constexpr int KP = DK + EP;                    // padded row pitch of staged q/k
   static constexpr int NB = C / 16;                     // 16 x 16 blocks per side
   static constexpr int LP = C + 1;                      // pitch of fp32 C x C tiles
+  static constexpr int PP = C + EP;                     // pitch of the staged decayed q.k tile
   static constexpr size_t kq_bytes = (size_t)2 * C * KP * sizeof(MT);
-  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)2 * (NB > 1 ? NB - 1 : 1) * 16 * 17 * 4;
+  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)C * PP * sizeof(MT) + (size_t)4 * 16 * 17 * 4;
   static constexpr size_t region = kq_bytes > inv_bytes ? kq_bytes : inv_bytes;
 };
 
@@ -55,14 +57,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   __shared__ float s_rk[C], s_rq[C];
   __shared__ float s_la[2][C], s_bt[2][C], s_g[2][C];
 
+  constexpr int PP = SM::PP;
   MT* Ks = reinterpret_cast<MT*>(smem);
   MT* Qs = Ks + C * KP;
   float* Lm = reinterpret_cast<float*>(smem);  // reused after the Gram products
   float* Ti = Lm + C * LP;
-  float* Wsc = Ti + C * LP;
+  MT* Pst = reinterpret_cast<MT*>(Ti + C * LP);                          // decayed q.k, staged
+  float* Wsc = reinterpret_cast<float*>(Pst + C * PP);                   // [4 waves][16][17]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int64_t c = blockIdx.x;
   const int64_t bh = blockIdx.y;
@@ -132,16 +137,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       s_rk[row] = 1.0f / fmaxf(sqrtf(sk), kNormEps);
     }
   }
+  // chunk-local cumulative log-gates, kept in log2 units so every decay
+  // factor below is one exp2 of a difference
+  constexpr float kLog2e = 1.4426950408889634f;
   if (tid < C) {
     if (fwd_on) {  // inclusive prefix sum in token order
       float s = 0.f;
       for (int j = 0; j <= tid; ++j) s += s_la[0][j];
-      s_g[0][tid] = s;
+      s_g[0][tid] = s * kLog2e;
     }
     if (rev_on) {  // inclusive suffix sum, accumulated in reverse visiting order
       float s = 0.f;
       for (int j = C - 1; j >= tid; --j) s += s_la[1][j];
-      s_g[1][tid] = s;
+      s_g[1][tid] = s * kLog2e;
     }
   }
   __syncthreads();
@@ -169,8 +177,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   }
   __syncthreads();  // q/k staging area is reused below
 
-  // ---- gated, scaled triangles: L into LDS, decayed Q^K^^T to the workspace ----
-  MT* pqk = static_cast<MT*>(a.pqk) + cid * C * C;
+  // ---- gated, scaled triangles: L and the decayed Q^K^^T into LDS ----
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     const int u = wave + 4 * j;
@@ -184,13 +191,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
         float lv = 0.f, pv = 0.f;
         if (col < r) {
           if (fwd_on) {
-            const float gam = expf(s_g[0][r] - s_g[0][col]);
+            const float gam = exp2f(s_g[0][r] - s_g[0][col]);
             lv = s_bt[0][r] * s_rk[r] * rkc * accG[j][i] * gam;
             pv = s_rq[r] * rkc * accP[j][i] * gam;
           }
         } else if (col > r) {
           if (rev_on) {
-            const float gam = expf(s_g[1][r] - s_g[1][col]);
+            const float gam = exp2f(s_g[1][r] - s_g[1][col]);
             lv = s_bt[1][r] * s_rk[r] * rkc * accG[j][i] * gam;
             pv = s_rq[r] * rkc * accP[j][i] * gam;
           }
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
           a.pd[cid * C + r] = s_rq[r] * s_rk[r] * accP[j][i];
         }
         Lm[r * LP + col] = lv;
-        pqk[r * C + col] = (MT)pv;
+        Pst[r * PP + col] = (MT)pv;
       }
     }
   }
@@ -235,63 +242,79 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   }
   __syncthreads();
 
-  // ---- off-diagonal blocks, one block diagonal at a time ----
-#pragma unroll
-  for (int d = 1; d < NB; ++d) {
-    const int nbk = NB - d;
-    const int items = 2 * nbk * 256;
-    for (int it = tid; it < items; it += 256) {
-      const int dir = it / (nbk * 256);
-      const int bk = (it / 256) % nbk;
-      const int r = (it / 16) % 16, cc = it % 16;
-      if ((dir == 0 && !fwd_on) || (dir == 1 && !rev_on)) continue;
-      float s = 0.f;
-      if (dir == 0) {
-        const int I = d + bk, J = bk;
-        for (int K = J; K < I; ++K)
-          for (int m = 0; m < 16; ++m) {
-            if (K == J && m < cc) continue;  // lower-triangular diagonal block
-            s = fmaf(Lm[(16 * I + r) * LP + 16 * K + m], Ti[(16 * K + m) * LP + 16 * J + cc], s);
-          }
-      } else {
-        const int I = bk, J = bk + d;
-        for (int K = I + 1; K <= J; ++K)
-          for (int m = 0; m < 16; ++m) {
-            if (K == J && m > cc) continue;  // upper-triangular diagonal block
-            s = fmaf(Lm[(16 * I + r) * LP + 16 * K + m], Ti[(16 * K + m) * LP + 16 * J + cc], s);
-          }
-      }
-      Wsc[((dir * (NB - 1) + bk) * 16 + r) * 17 + cc] = s;
-    }
-    __syncthreads();
-    for (int it = tid; it < items; it += 256) {
-      const int dir = it / (nbk * 256);
-      const int bk = (it / 256) % nbk;
-      const int r = (it / 16) % 16, cc = it % 16;
-      if ((dir == 0 && !fwd_on) || (dir == 1 && !rev_on)) continue;
-      const int I = dir == 0 ? d + bk : bk;
-      const int J = dir == 0 ? bk : bk + d;
-      float s = 0.f;
-      const float* w = Wsc + (dir * (NB - 1) + bk) * 16 * 17;
-      if (dir == 0) {
-        for (int m = 0; m <= r; ++m) s = fmaf(Ti[(16 * I + r) * LP + 16 * I + m], w[m * 17 + cc], s);
-      } else {
-        for (int m = r; m < 16; ++m) s = fmaf(Ti[(16 * I + r) * LP + 16 * I + m], w[m * 17 + cc], s);
-      }
-      Ti[(16 * I + r) * LP + 16 * J + cc] = -s;
-    }
-    __syncthreads();
-  }
-
-  // ---- write the strict triangles of both inverses ----
+  // ---- off-diagonal blocks: one block column per wave, on fp32 matrix cores ----
+  // v_mfma_f32_16x16x4f32: lane (l16, g4) supplies A[l16][k] and B[k][l16]
+  // with k = 4 ks + g4; D lands as D[4 g4 + i][l16].
   {
+    float* wsc = Wsc + wave * 16 * 17;
+    auto column = [&](int dir, int J) {
+      const bool up = dir == 1;
+      const int I0 = up ? J - 1 : J + 1;
+      const int I1 = up ? -1 : NB;
+      const int dI = up ? -1 : 1;
+      for (int I = I0; I != I1; I += dI) {
+        // W = sum_K L_IK T_KJ over K between J and I (T_JJ triangular)
+        f32x4 w = {0.f, 0.f, 0.f, 0.f};
+        const int K0 = up ? I + 1 : J, K1 = up ? J : I - 1;
+        for (int K = K0; K <= K1; ++K) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int k = 4 * ks + g4;
+            const float av = Lm[(16 * I + l16) * LP + 16 * K + k];
+            float bv = Ti[(16 * K + k) * LP + 16 * J + l16];
+            if (K == J && (up ? k > l16 : k < l16)) bv = 0.f;
+            w = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, w, 0, 0, 0);
+          }
+        }
+        // T_IJ = -T_II W (W through this wave's scratch; LDS is in order per wave)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsc[(4 * g4 + i) * 17 + l16] = w[i];
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int k = 4 * ks + g4;
+          float av = Ti[(16 * I + l16) * LP + 16 * I + k];
+          if (up ? k < l16 : k > l16) av = 0.f;
+          t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wsc[k * 17 + l16], t, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ti[(16 * I + 4 * g4 + i) * LP + 16 * J + l16] = -t[i];
+      }
+    };
+    if constexpr (NB == 4) {
+      if (wave == 0) {
+        if (fwd_on) column(0, 0);
+      } else if (wave == 1) {
+        if (rev_on) column(1, 3);
+      } else if (wave == 2) {
+        if (fwd_on) { column(0, 1); column(0, 2); }
+      } else {
+        if (rev_on) { column(1, 2); column(1, 1); }
+      }
+    } else {
+      if (wave == 0 && fwd_on) column(0, 0);
+      if (wave == 1 && rev_on) column(1, 1);
+    }
+  }
+  __syncthreads();
+
+  // ---- both triangles to the workspace, 16 bytes per store ----
+  {
+    constexpr int EPS = 16 / (int)sizeof(MT);
     MT* tri = static_cast<MT*>(a.tri) + cid * C * C;
-    for (int p = tid; p < C * C; p += 256) {
-      const int r = p / C, col = p % C;
-      float v = 0.f;
-      if (col < r && fwd_on) v = Ti[r * LP + col];
-      if (col > r && rev_on) v = Ti[r * LP + col];
-      tri[p] = (MT)v;
+    MT* pqk = static_cast<MT*>(a.pqk) + cid * C * C;
+    for (int p = tid; p < C * C / EPS; p += 256) {
+      const int r = (p * EPS) / C, c0 = (p * EPS) % C;
+      MT tv[EPS], pv[EPS];
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) {
+        const int col = c0 + e;
+        const bool keep = (col < r && fwd_on) || (col > r && rev_on);
+        tv[e] = (MT)(keep ? Ti[r * LP + col] : 0.f);
+        pv[e] = keep ? Pst[r * PP + col] : (MT)0.f;
+      }
+      __builtin_memcpy(tri + p * EPS, tv, 16);
+      __builtin_memcpy(pqk + p * EPS, pv, 16);
     }
   }
   // ---- per-token scales and the chunk decay ----
@@ -300,17 +323,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     const float rk = s_rk[tid], rq = s_rq[tid];
     if (fwd_on) {
       const float g = s_g[0][tid], gl = s_g[0][C - 1];
-      const float eg = expf(g);
-      float4 v = in ? make_float4(s_bt[0][tid], eg * rk, eg * rq, expf(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float eg = exp2f(g);
+      float4 v = in ? make_float4(s_bt[0][tid], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
       a.sc[(size_t)fslot * a.B * a.H * a.NC * C + cid * C + tid] = v;
-      if (tid == 0) a.gn[(size_t)fslot * a.B * a.H * a.NC + cid] = expf(gl);
+      if (tid == 0) a.gn[(size_t)fslot * a.B * a.H * a.NC + cid] = exp2f(gl);
     }
     if (rev_on) {
       const float g = s_g[1][tid], gl = s_g[1][0];
-      const float eg = expf(g);
-      float4 v = in ? make_float4(s_bt[1][tid], eg * rk, eg * rq, expf(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float eg = exp2f(g);
+      float4 v = in ? make_float4(s_bt[1][tid], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
       a.sc[(size_t)rslot * a.B * a.H * a.NC * C + cid * C + tid] = v;
-      if (tid == 0) a.gn[(size_t)rslot * a.B * a.H * a.NC + cid] = expf(gl);
+      if (tid == 0) a.gn[(size_t)rslot * a.B * a.H * a.NC + cid] = exp2f(gl);
     }
   }
 }
