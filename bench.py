@@ -59,6 +59,38 @@ def kernel_bytes(w, xs: int, C: int) -> dict:
     return {"prep": prep, "chain": chain}
 
 
+KERNEL_SOURCES = {
+    "chain_kernel": ["gdn_chain.hip", "gdn_common.h"],
+    "chunk_prep_kernel": ["gdn_prep.hip", "gdn_common.h"],
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources a kernel is built from (tells whether measured
+    counters still describe the code being timed)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_scan_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>_<workload>_traffic.md), or None when there is none or
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-json:"):
+            d = json.loads(line.split(":", 1)[1])
+            if d.get("source_hash") == kernel_source_hash(kernel):
+                return d["bytes_per_launch"]
+    return None
+
+
 class HipEvents:
     """Raw hipEvent_t handles through the HIP runtime (the library records them
     on the stream its kernels run on)."""
@@ -132,6 +164,8 @@ def main() -> int:
     ap.add_argument("--dv-tile", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -188,6 +222,13 @@ def main() -> int:
     chain_ms = sum(ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(K)) / K
     ev.close()
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     tokens = w.B * w.T
     th_dirs = w.B * w.T * w.H * w.dirs
     flops = th_dirs * flops_per_token_head_dir(w.dk, w.dv)
@@ -196,6 +237,7 @@ def main() -> int:
     kb = kernel_bytes(w, xs, C)
     kt = {"prep": prep_ms, "chain": chain_ms}
     dom = max(kt, key=kt.get)
+    dom_name = "chain_kernel" if dom == "chain" else "chunk_prep_kernel"
     achieved = kb[dom] / (kt[dom] * 1e-3) / 1e9
     peak_mfma = MI355X_BF16_TFLOPS if w.dtype == "bf16" else MI355X_FP32_TFLOPS
     res = {
@@ -219,9 +261,10 @@ def main() -> int:
         "path_hbm_gbs": pbytes / (ms_step * 1e-3) / 1e9,
         "path_hbm_frac": pbytes / (ms_step * 1e-3) / 1e9 / MI355X_HBM_GBS,
         "kernels_ms": {"chunk_prep": prep_ms, "state_chain": chain_ms},
-        "roofline": {"kernel": "chain_kernel" if dom == "chain" else "chunk_prep_kernel", "bound": "hbm",
+        "roofline": {"kernel": dom_name, "bound": "hbm",
                      "achieved": achieved, "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": achieved / MI355X_HBM_GBS,
-                     "traffic": None, "alg_bytes_per_launch": kb[dom], "avg_launch_ms": kt[dom]},
+                     "traffic": measured_traffic(dom_name, args.workload), "alg_bytes_per_launch": kb[dom],
+                     "avg_launch_ms": kt[dom], "source_hash": kernel_source_hash(dom_name)},
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

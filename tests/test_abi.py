@@ -1,0 +1,198 @@
+"""The libgdn C ABI on the host (no kernel runs here): exported symbols match
+include/gdn.h, the ctypes mirror of gdn_problem_t matches the C layout, and
+every argument check returns its status before anything is enqueued.
+
+A fully valid call on a machine without a GPU reaches the kernel launch and
+must report GDN_ERR_HIP (the launch-failure path)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_scan_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_exported_entry_points():
+    assert _declared_functions() == sorted(gdn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdn.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.check_output(["nm", "-D", "--defined-only", gdn.LIB_PATH], text=True)
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(_declared_functions()) <= exported
+
+
+def test_problem_struct_layout_matches_c(tmp_path):
+    prog = tmp_path / "layout.c"
+    prog.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "gdn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
+         offsetof(gdn_problem_t, chunk), offsetof(gdn_problem_t, dv_tile), offsetof(gdn_problem_t, workspace),
+         offsetof(gdn_problem_t, workspace_bytes), offsetof(gdn_problem_t, stream),
+         offsetof(gdn_problem_t, timing_events));
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", f"-I{os.path.join(ROOT, 'include')}", str(prog), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)], text=True).split()]
+    P = gdn.gdn_problem_t
+    want = [ctypes.sizeof(P), P.dtype.offset, P.chunk.offset, P.dv_tile.offset, P.workspace.offset,
+            P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset]
+    assert got == want
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in gdn.gdn_version()
+    assert gdn.gdn_status_string(gdn.GDN_OK) == "ok"
+    for st in range(1, 5):
+        assert gdn.gdn_status_string(st) not in ("ok", "unknown status")
+    assert gdn.gdn_status_string(99) == "unknown status"
+
+
+def _prob(B=1, T=300, H=2, dk=128, dv=128, dtype=gdn.GDN_DTYPE_BF16, chunk=0, dv_tile=0, ws=0, wsb=0):
+    return gdn.make_problem(B, T, H, dk, dv, dtype, chunk, dv_tile, ws, wsb)
+
+
+def test_workspace_bytes():
+    for d in ("fwd", "rev", "bi"):
+        assert gdn.workspace_bytes(1, 300, 2, 128, 128, "bf16", d) > 0
+    n1 = gdn.workspace_bytes(1, 300, 2, 128, 128, "bf16", "fwd")
+    n2 = gdn.workspace_bytes(1, 300, 2, 128, 128, "bf16", "bi")
+    assert n2 > n1
+    assert gdn.workspace_bytes(1, 300, 2, 64, 64, "f32", "fwd") > gdn.workspace_bytes(1, 300, 2, 64, 64, "bf16", "fwd")
+    # chunk count rounds up: one token more than a chunk multiple needs one chunk more
+    assert gdn.workspace_bytes(1, 129, 1, 64, 64, "bf16", "fwd") > gdn.workspace_bytes(1, 128, 1, 64, 64, "bf16", "fwd")
+    assert gdn.workspace_bytes(1, 0, 1, 64, 64, "bf16", "fwd") > 0  # sequence-independent parts only
+
+
+@pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=80), dict(chunk=48), dict(chunk=16), dict(dv_tile=64),
+                                dict(dtype=7), dict(B=0), dict(H=0), dict(T=-1), dict(B=300, H=300),
+                                dict(dtype=gdn.GDN_DTYPE_F32, dk=128, chunk=64, dv_tile=32)])
+def test_workspace_bytes_rejects(kw):
+    assert gdn.gdn_workspace_bytes(_prob(**kw), gdn.GDN_DIR_FORWARD) == 0
+
+
+def test_workspace_bytes_rejects_bad_direction():
+    assert gdn.gdn_workspace_bytes(_prob(), 3) == 0
+    assert gdn.gdn_workspace_bytes(_prob(), -1) == 0
+
+
+# Fake, well-aligned device addresses: validation never dereferences them.
+BASE = 1 << 40
+
+
+def _bufs(B=1, T=300, H=2, dk=128, dv=128, es=2, dirs=1):
+    """Disjoint fake buffers laid out one after another (256-byte aligned)."""
+    sizes = dict(q=B * T * H * dk * es, k=B * T * H * dk * es, v=B * T * H * dv * es, la=dirs * B * T * H * 4,
+                 beta=dirs * B * T * H * 4, s_in=dirs * B * H * dv * dk * 4, s_out=dirs * B * H * dv * dk * 4,
+                 out=B * T * H * dv * 4, ws=1 << 30)
+    addr, p = {}, BASE
+    for k_, n in sizes.items():
+        addr[k_] = p
+        p += (n + 255) // 256 * 256 + 256
+    return addr
+
+
+def _call(prob, a, direction=gdn.GDN_DIR_FORWARD, **over):
+    a = dict(a, **over)
+    return gdn.gdn_forward(prob, a["q"], a["k"], a["v"], a["la"], a["beta"], a["s_in"], a["s_out"], a["out"],
+                           direction)
+
+
+def _valid(direction=gdn.GDN_DIR_FORWARD, **kw):
+    a = _bufs(dirs=2 if direction == gdn.GDN_DIR_BIDIRECTIONAL else 1)
+    p = _prob(**kw)
+    p.workspace = a["ws"]
+    p.workspace_bytes = 1 << 30
+    return p, a
+
+
+def test_null_problem_is_invalid():
+    a = _bufs()
+    st = gdn.lib().gdn_forward(None, a["q"], a["k"], a["v"], a["la"], a["beta"], None, None, a["out"], 0)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "la", "beta", "out"])
+def test_null_required_pointer_is_invalid(field):
+    p, a = _valid()
+    assert _call(p, a, **{field: None}) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("field,offset", [("q", 8), ("k", 2), ("v", 4), ("out", 8), ("la", 2), ("s_in", 4),
+                                          ("s_out", 8)])
+def test_misaligned_pointer_is_invalid(field, offset):
+    p, a = _valid()
+    assert _call(p, a, **{field: a[field] + offset}) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_checks():
+    p, a = _valid()
+    need = gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_FORWARD)
+    p.workspace_bytes = need - 1
+    assert _call(p, a) == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    p.workspace_bytes = need
+    p.workspace = a["ws"] + 128
+    assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    p.workspace = None
+    assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_overlaps_are_invalid():
+    p, a = _valid()
+    assert _call(p, a, out=a["q"]) == gdn.GDN_ERR_INVALID_ARGUMENT           # out aliases an input
+    assert _call(p, a, out=a["v"] + 256) == gdn.GDN_ERR_INVALID_ARGUMENT     # partial overlap
+    assert _call(p, a, s_out=a["k"]) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert _call(p, a, s_out=a["s_in"] + 256) == gdn.GDN_ERR_INVALID_ARGUMENT  # partial state overlap
+    p.workspace = a["out"]
+    assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT                       # workspace over out
+
+
+def test_bad_problem_fields():
+    p, a = _valid()
+    assert _call(p, a, direction=5) == gdn.GDN_ERR_INVALID_ARGUMENT
+    p.reserved = 1
+    assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    p, a = _valid(dk=96)
+    assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED
+    p, a = _valid(chunk=48)
+    assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_empty_sequence_without_state_output_is_a_no_op():
+    p, a = _valid(T=0)
+    assert _call(p, a, q=None, k=None, v=None, la=None, beta=None, out=None, s_out=None) == gdn.GDN_OK
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present: the launch would succeed")
+@pytest.mark.parametrize("direction", [gdn.GDN_DIR_FORWARD, gdn.GDN_DIR_REVERSE, gdn.GDN_DIR_BIDIRECTIONAL])
+def test_valid_call_without_gpu_reports_launch_failure(direction):
+    p, a = _valid(direction)
+    assert _call(p, a, direction) == gdn.GDN_ERR_HIP
+    # state_in == state_out (in-place carry) passes validation too
+    assert _call(p, a, direction, s_out=a["s_in"]) == gdn.GDN_ERR_HIP
+
+
+def test_binding_raises_on_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        gdn.lib()
