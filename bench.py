@@ -52,7 +52,7 @@ def kernel_bytes(w, xs: int, C: int) -> dict:
     """Algorithmic bytes of each kernel: its own inputs and outputs, each once."""
     th = w.B * w.T * w.H
     chunk_ops = 2 * C * xs                      # Tinv and decayed QK^T (C x C per chunk) per token
-    scal = w.dirs * 16 + 4                      # per-token scales and self-term weight
+    scal = w.dirs * 16                          # per-token scales, per direction
     prep = th * (2 * w.dk * xs + w.dirs * 8 + chunk_ops + scal)
     states = w.dirs * w.B * w.H * w.dv * w.dk * 4 * (2 if w.state_std > 0 else 1)
     chain = th * ((2 * w.dk + w.dv) * xs + chunk_ops + scal + w.dv * 4) + states

@@ -146,13 +146,13 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
         state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
     prob = make_problem(B, T, H, dk, dv, dt, chunk, dv_tile)
     nbytes = gdn_workspace_bytes(prob, DIRECTIONS[direction])
-    if nbytes == 0:
+    if nbytes == 0 and T > 0:
         raise GdnError(GDN_ERR_UNSUPPORTED)
-    if workspace is None or workspace.numel() < nbytes:
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
-    prob.workspace = workspace.data_ptr()
-    prob.workspace_bytes = workspace.numel()
+    prob.workspace = workspace.data_ptr() if workspace is not None else None
+    prob.workspace_bytes = workspace.numel() if workspace is not None else 0
     prob.stream = s.cuda_stream
     prob.timing_events = timing_events
     st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),

@@ -173,9 +173,7 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
     a.tri = ws + pl.ws.tri;
     a.pqk = ws + pl.ws.pqk;
     a.sc = reinterpret_cast<float4*>(ws + pl.ws.sc);
-    a.pd = reinterpret_cast<float*>(ws + pl.ws.pd);
-    a.gn = reinterpret_cast<float*>(ws + pl.ws.gn);
-    a.trash = reinterpret_cast<float*>(ws + pl.ws.trash);
+    a.pdg = reinterpret_cast<float*>(ws + pl.ws.pdg);
   }
   a.B = B; a.T = T; a.H = H; a.NC = pl.NC; a.dv = (int)dv;
   a.fwd_on = pl.fwd_on; a.rev_on = pl.rev_on; a.dirs = pl.dirs;

@@ -9,7 +9,7 @@
 //   Y = K S^T,  Z = Q S^T                    (matrix cores; K, Q raw)
 //   X = beta * (V - (e^g rk) * Y)            (fp32, pseudo-values vs. entry state)
 //   Vnew = X + strict(Tinv) X                (matrix cores; X kept exact in fp32)
-//   O = (e^g rq) * Z + (q^.k^) Vnew + strict(P) Vnew   (self term in fp32)
+//   O = (e^g rq) * Z + P Vnew                (P: decayed q^.k^, self terms on the diagonal)
 //   S = e^{g_last} S + (e^{g_last-g} rk * Vnew)^T K    (matrix cores, fp32 accumulate)
 //
 // which is the chunked form of S_t = a_t S_{t-1}(I - b_t k^_t k^_t^T) +
@@ -17,11 +17,22 @@
 //
 // Bidirectional scans ("Video DeltaNet", "Methodology in Plain English": a
 // forward and a backward recurrent state whose readouts are added) run as two
-// direction groups of four waves in one workgroup.  At step s the forward
-// group handles chunk s and the reverse group chunk NC-1-s, so every chunk is
-// visited twice; the first visitor stores its readout, the second adds its
-// own after a workgroup barrier.  The sum therefore needs no atomics and no
+// direction groups of four waves in one workgroup, in step with each other.
+// At step s the forward group handles chunk s and the reverse group chunk
+// NC-1-s, so every chunk is visited twice.  The first visitor stores its
+// readout; the second loads that partial once a workgroup barrier has ordered
+// it after the store, and adds and stores its own one step later, so the load
+// has a whole step to arrive.  The sum needs no atomics and no
 // inter-workgroup synchronisation, and `out` is written by plain stores only.
+//
+// Every global access goes through a raw buffer resource whose extent is the
+// valid part of the chunk: reads past it return zero and writes past it are
+// dropped.  Rows past the end of the sequence therefore need no clamping and
+// no branches, and an access that must not happen this step (the partial of
+// a first visit, the store of a step that has nothing to store) is switched
+// off by an empty extent.  All loads of a step are issued by every wave
+// unconditionally, a step ahead of their use, so no prefetch ever forces a
+// wait on the in-order memory counter.
 //
 // Workgroups are numbered so that all value tiles of one (batch, head) land
 // on the same XCD (consecutive workgroups are dealt round-robin over the
@@ -31,9 +42,48 @@
 
 namespace gdn {
 
+// ---- raw buffer access -----------------------------------------------------
+// Word 3 of a gfx9 buffer resource for raw (unstructured) access with 32-bit
+// elements; the hardware bounds every access by num_records bytes.
+constexpr int kRawBufferWord3 = 0x00020000;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+__device__ __forceinline__ f32x4 bload16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  f32x4 f;
+  __builtin_memcpy(&f, &v, 16);
+  return f;
+}
+
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, f32x4 x) {
+  u32x4 v;
+  __builtin_memcpy(&v, &x, 16);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// A matrix-core fragment (8 consecutive elements) at byte offset `off`.
+template <typename MT>
+__device__ __forceinline__ typename Mma<MT>::frag bload_frag(rsrc_t r, uint32_t off) {
+  typename Mma<MT>::frag f;
+  if constexpr (sizeof(MT) == 2) {
+    const f32x4 v = bload16(r, off);
+    __builtin_memcpy(&f, &v, 16);
+  } else {
+    f.lo = bload16(r, off);
+    f.hi = bload16(r, off + 16);
+  }
+  return f;
+}
+
 template <typename MT, int DK, int C, int NT>
 struct ChainSmem {
-  static constexpr int EP = 16 / (int)sizeof(MT);
+  static constexpr int ES = (int)sizeof(MT);
+  static constexpr int EP = 16 / ES;
   static constexpr int TP = C + EP;   // pitch of token-contiguous rows
   static constexpr int SP = DK + EP;  // pitch of the state copy
   static constexpr int DT = 16 * NT;
@@ -41,31 +91,36 @@ struct ChainSmem {
   // operand of the state update is read with transposing LDS reads; the
   // pitch puts the four rows of one such read in distinct bank quarters).
   // fp32: token-contiguous [DK][TP].
-  static constexpr bool KROW = sizeof(MT) == 2;
+  static constexpr bool KROW = ES == 2;
   static constexpr int KP = DK + 16;
   static constexpr int k_elems = KROW ? C * KP : DK * TP;
   // bf16 operands: Vnew and the scaled update vectors are carried as hi + lo
   // bf16 pairs (two products each), so their rounding stays at fp32 level.
-  static constexpr bool SPLIT = sizeof(MT) == 2;
+  static constexpr bool SPLIT = ES == 2;
   static constexpr int NVT = SPLIT ? 5 : 3;  // token-contiguous value arrays
   static constexpr int per_group = k_elems + NVT * DT * TP + DT * SP;  // elements
+  // Staged per-chunk operands shared by a direction group (bytes): the
+  // per-token scales, the self-term remainders with the chunk decay, the
+  // value tile.  Double buffered by step parity.
+  static constexpr int ST_SC = 0;
+  static constexpr int ST_PD = C * 16;
+  static constexpr int ST_GN = ST_PD + C * 4;
+  static constexpr int ST_V = ST_PD + (C + 4) * 4;
+  static constexpr int ST_BYTES = ST_V + C * DT * ES;
 };
 
 template <typename MT, int DT, int C>
 struct VTile {
-  static constexpr int LPR = DT * (int)sizeof(MT) / 16;  // lanes per token row (16 bytes each)
+  static constexpr int LPR = DT * (int)sizeof(MT) / 16;  // 16-byte pieces per token row
   static constexpr int NVI = (C * LPR + 127) / 128;      // loads per wave (two waves share the tile)
 };
 
 // Raw operands of one chunk, loaded a step ahead of their use.  Every wave
 // loads its own matrix-core fragments (k, q rows of its token tile and the
-// matching rows of the two chunk triangles); the per-token scales, self-term
-// weights, chunk decay and the value tile are loaded once per direction group
-// by one or two waves (16 distinct bytes per lane) and staged through LDS.
-// Loads are unconditional: rows past the end of the sequence are clamped to
-// the last token (their gate scales are exactly zero, so they contribute
-// nothing) and all masking and conversion happens at the point of use, so a
-// prefetch never forces a wait on the memory pipeline.
+// matching rows of the two chunk triangles) and 16 bytes per lane of the
+// group-shared operands (wave 0: scales, wave 1: self-term remainders and
+// chunk decay, waves 2-3: the value tile), which go to LDS at the end of the
+// step.
 template <typename MT, int DK, int C, int NT>
 struct Stage {
   typedef typename Mma<MT>::frag frag;
@@ -73,9 +128,7 @@ struct Stage {
   frag qf[DK / 32];
   frag tf[C / 32];
   frag pf[C / 32];
-  float4 csc;                            // wave 0: scales of token `lane`
-  float cpd, cgn;                        // wave 1: self-term weight of token `lane`, chunk decay
-  f32x4 cv[VTile<MT, 16 * NT, C>::NVI];  // waves 2, 3: 16 raw bytes of the value tile
+  f32x4 cv[VTile<MT, 16 * NT, C>::NVI];
 };
 
 __device__ __forceinline__ bool tri_needed(bool rev, int kc, int rt) {
@@ -84,20 +137,21 @@ __device__ __forceinline__ bool tri_needed(bool rev, int kc, int rt) {
   return rev ? (32 * kc + 31 > 16 * rt) : (32 * kc <= 16 * rt + 15);
 }
 
-// Bit masks that keep the strictly-lower (forward) or strictly-upper
-// (reverse) elements of a triangle fragment; only the k-chunk that contains
-// the diagonal needs one, and it is loop-invariant per lane.
+// Bit masks that keep the lower (forward) or upper (reverse) elements of a
+// triangle fragment, with or without the diagonal; only the k-chunk that
+// contains the diagonal needs one (the others keep everything), and they are
+// loop-invariant per lane.
 template <typename MT>
 struct FragMask {
   static constexpr int NW = (int)(sizeof(typename Mma<MT>::frag) / 4);
   uint32_t m[NW];
-  __device__ __forceinline__ void make(int row, int col0, bool upper) {
+  __device__ __forceinline__ void make(int row, int col0, bool upper, bool diag, bool active) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) m[i] = 0u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int col = col0 + e;
-      const bool keep = upper ? (col > row) : (col < row);
+      const bool keep = !active || (upper ? (col > row) : (col < row)) || (diag && col == row);
       if (keep) {
         if (sizeof(MT) == 2) m[e / 2] |= 0xffffu << (16 * (e % 2));
         else m[e] = 0xffffffffu;
@@ -114,54 +168,42 @@ struct FragMask {
   }
 };
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// ds_read_b64_tr_b16 transposes within each 16-lane group: lane i receives
+// res[i][e] = src[4e + i/4][i % 4], where src[s] is the four consecutive bf16
+// at source lane s's address (lane mapping checked on gfx950).
+__device__ __forceinline__ v4s lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(const_cast<void*>(p)));
+}
+
 // Transposed k fragment for the state update, read from a row-major bf16 k
 // tile in LDS.  The A operand (m = dk row dk0 + l16, k = 32 tokens from tok0)
 // holds, in lane (l16, g4), k[tok0 + 8 g4 + j][dk0 + l16] for j = 0..7.
-// ds_read_b64_tr_b16 transposes within each 16-lane group: lane i receives
-// res[i][e] = src[4e + i/4][i % 4], where src[s] is the four consecutive bf16
-// at source lane s's address (lane mapping checked on gfx950).  Source lane s
-// therefore points at k[tok + s/4][dk0 + 4 (s % 4)]; two reads give j = 0..3
-// and j = 4..7.
+// Source lane s therefore points at k[tok + s/4][dk0 + 4 (s % 4)]; two reads
+// give j = 0..3 and j = 4..7.
 __device__ __forceinline__ bf16x8 load_kt_frag(const bf16* krow, int kp, int tok0, int dk0, int l16, int g4) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4s lds_v4s;
-  typedef __attribute__((address_space(3))) char lds_char;
-  lds_char* base = (lds_char*)(const_cast<bf16*>(krow));
-  const int off0 = ((tok0 + 8 * g4 + (l16 >> 2)) * kp + dk0 + 4 * (l16 & 3)) * 2;
-  const int off1 = off0 + 4 * kp * 2;
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off0));
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off1));
+  const int o0 = (tok0 + 8 * g4 + (l16 >> 2)) * kp + dk0 + 4 * (l16 & 3);
+  const v4s lo = lds_read_tr16(krow + o0);
+  const v4s hi = lds_read_tr16(krow + o0 + 4 * kp);
   bf16x8 r;
   __builtin_memcpy(&r, &lo, 8);
   __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
   return r;
 }
 
-// Barrier for the four waves of one direction group, on an LDS counter, so
-// the forward and reverse groups of a workgroup do not wait for each other.
-// Every wave finishes its own LDS traffic (lgkmcnt 0), arrives, and polls
-// until all four have arrived for this epoch.  All four waves of a group are
-// resident in the same workgroup, so the wait always ends.
-// Polls are bounded (kSpinLimit sleeps, far beyond any legitimate wait) so a
-// wave can never spin forever.
-constexpr int kSpinLimit = 1 << 22;
-
-__device__ __forceinline__ void spin_until_at_least(int* ctr, int target, int order) {
-  for (int n = 0; n < kSpinLimit; ++n) {
-    const int v = order == __ATOMIC_ACQUIRE
-                      ? __hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)
-                      : __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (v >= target) break;
-    __builtin_amdgcn_s_sleep(1);
+// hi + lo bf16 split of four fp32 values (hi = rounded value, lo = rounded
+// remainder), written as two 8-byte LDS stores.
+__device__ __forceinline__ void store_split4(bf16* hi_p, bf16* lo_p, f32x4 x) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = (bf16)x[i];
+    l[i] = (bf16)(x[i] - (float)h[i]);
   }
-}
-
-__device__ __forceinline__ void group_barrier(int* ctr, int target, int lane) {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are complete
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  spin_until_at_least(ctr, target, __ATOMIC_RELAXED);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  *reinterpret_cast<bf16x4*>(hi_p) = h;
+  *reinterpret_cast<bf16x4*>(lo_p) = l;
 }
 
 template <typename MT, int DK, int C, int NT, int DIRS>
@@ -170,6 +212,7 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   using frag = typename M::frag;
   using SM = ChainSmem<MT, DK, C, NT>;
   using F = Stage<MT, DK, C, NT>;
+  constexpr int ES = SM::ES;
   constexpr int TP = SM::TP, SP = SM::SP, DT = SM::DT;
   using VT = VTile<MT, DT, C>;
   constexpr int RT = C / 16;              // token row tiles per chunk
@@ -178,18 +221,10 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   constexpr int SUPW = SRT * NT / 4;      // state tiles per wave
   constexpr bool SPLIT = SM::SPLIT;
   constexpr bool ALL_UNITS = (RT * NT) % 4 == 0;
-  constexpr int EPV = 16 / (int)sizeof(MT);  // elements per 16 bytes
+  static_assert(SRT % 4 == 0, "each wave owns whole dk-tile columns of the state");
 
   __shared__ __align__(16) MT smem[DIRS * SM::per_group];
-  // group-shared per-chunk operands, double buffered by step parity
-  __shared__ float4 g_sc[DIRS][2][C];
-  __shared__ float g_pd[DIRS][2][C];
-  __shared__ float g_gn[DIRS][2];
-  __shared__ __align__(16) MT g_v[DIRS][2][C * DT];
-  // per-group barrier counters and crossing progress: s_prog[g] counts the
-  // waves of group g that have completed (and made visible) the readout
-  // stores of their first-visitor steps
-  __shared__ int s_gbar[2], s_prog[2];
+  __shared__ __align__(16) unsigned char stg[DIRS][2][SM::ST_BYTES];
 
   // XCD-aware numbering: workgroup id -> (chain, value tile)
   const int id = blockIdx.x;
@@ -197,7 +232,8 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   const int chain = (kk / ntiles) * 8 + xcd;
   const int tile = kk % ntiles;
   if (chain >= nbh) return;
-  const int64_t NC = a.NC, T = a.T, H = a.H;
+  const int NC = (int)a.NC;
+  const int64_t T = a.T, H = a.H;
   const int64_t b = chain / H, h = chain % H;
   const int dv = a.dv;
   const int dv0 = tile * DT;
@@ -220,109 +256,129 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   MT* VsL = SPLIT ? VnL + DT * TP : VnL;
   MT* Sb = VsT + (SM::NVT - 2) * DT * TP;    // [DT][SP]  state copy (operand type)
 
-  // ---- loop-invariant addressing: per-lane offsets relative to a chunk's
-  // first token, scalar per-chunk bases.  The last chunk may be partial; its
-  // offsets clamp rows to the last token. ----
-  const int n_last = NC > 0 ? (int)(T - (NC - 1) * C) : C;
-  const int HD = (int)(H * DK), HV = (int)(H * dv);
-  const int64_t CHD = (int64_t)C * HD, CHV = (int64_t)C * HV;
-  const MT* kbase = static_cast<const MT*>(a.k) + (b * T * H + h) * DK;
-  const MT* qbase = static_cast<const MT*>(a.q) + (b * T * H + h) * DK;
-  const MT* vbase = static_cast<const MT*>(a.v) + (b * T * H + h) * dv + dv0;
-  float* obase = a.out + (b * T * H + h) * dv + dv0;
+  // ---- loop-invariant addressing: per-lane byte offsets within a chunk,
+  // wave-uniform chunk bases and strides ----
+  const int n_last = NC > 0 ? (int)(T - (int64_t)(NC - 1) * C) : C;
+  const uint32_t HDB = (uint32_t)(H * DK * ES);  // token pitch of q, k
+  const uint32_t HVB = (uint32_t)(H * dv * ES);  // token pitch of v
+  const uint32_t HOB = (uint32_t)(H * dv * 4);   // token pitch of out
+  const size_t nch = (size_t)a.B * a.H * NC;
+  const char* kbase = static_cast<const char*>(a.k) + (size_t)((b * T * H + h) * DK) * ES;
+  const char* qbase = static_cast<const char*>(a.q) + (size_t)((b * T * H + h) * DK) * ES;
+  const char* vbase = static_cast<const char*>(a.v) + (size_t)((b * T * H + h) * dv + dv0) * ES;
+  char* obase = reinterpret_cast<char*>(a.out) + (size_t)((b * T * H + h) * dv + dv0) * 4;
+  const char* trib = static_cast<const char*>(a.tri) + (size_t)chain * NC * C * C * ES;
+  const char* pqkb = static_cast<const char*>(a.pqk) + (size_t)chain * NC * C * C * ES;
   const int kq_row = 16 * rt + l16;
-  const int kq_off = kq_row * HD + 8 * g4;
-  const int kq_off_last = min(kq_row, n_last - 1) * HD + 8 * g4;
-  int v_off[VT::NVI], v_off_last[VT::NVI];
+  const uint32_t kq_off = kq_row * HDB + 8 * g4 * ES;
+  const uint32_t tri_off = (kq_row * C + 8 * g4) * ES;
+  const int o_row0 = 16 * rt + 4 * g4;
+  const int kcd = rt / 2;  // k-chunk holding this row tile's diagonal
+  // triangle fragments: the k-chunks of this row tile that hold no element
+  // of this direction's triangle are read past the buffer extent (zeros);
+  // the diagonal k-chunk is masked (Tinv strictly, P with its diagonal)
+  uint32_t tri_offs[C / 32];
+  FragMask<MT> tmask[C / 32], pmask[C / 32];
+#pragma unroll
+  for (int kc = 0; kc < C / 32; ++kc) {
+    tri_offs[kc] = tri_needed(rev, kc, rt) ? tri_off + 32 * kc * ES : (uint32_t)(C * C * ES);
+    tmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, false, kc == kcd);
+    pmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, true, kc == kcd);
+  }
+  const int tok = 16 * rt + l16;  // token of this lane in the transposed readout
+  const uint32_t ot_off = tok * HOB + 16 * g4;
+  // bf16 operands: the self term's remainder enters as a diagonal fragment;
+  // in k-chunk kc this lane holds element `tok - 32 kc - 8 g4` of it when that
+  // lies in 0..7 (only ever in the k-chunk of the diagonal)
+  FragMask<MT> diag_only[C / 32];
+#pragma unroll
+  for (int kc = 0; kc < C / 32; ++kc) {
+#pragma unroll
+    for (int i = 0; i < FragMask<MT>::NW; ++i) diag_only[kc].m[i] = 0u;
+    const int e0 = tok - 32 * kc - 8 * g4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e == e0) {
+        if (sizeof(MT) == 2) diag_only[kc].m[e / 2] |= 0xffffu << (16 * (e % 2));
+        else diag_only[kc].m[e] = 0xffffffffu;
+      }
+  }
+  // valid bytes of a chunk's rows: the last row ends after `tail` bytes
+  auto rows_of = [&](int c) -> uint32_t { return (uint32_t)(c == NC - 1 ? n_last : C); };
+  auto extent = [&](int c, uint32_t pitch, uint32_t tail) { return (rows_of(c) - 1) * pitch + tail; };
+
+  // group-shared operand loads: which source this wave reads, per-lane offsets
+  // and where each piece lands in the staging buffer
+  const char* cbase;
+  size_t cstride;
+  uint32_t cbytes;  // extent of a whole chunk (the value tile is bounded per chunk below)
+  uint32_t c_off[VT::NVI], c_lds[VT::NVI];
+  if (w == 0) {
+    cbase = reinterpret_cast<const char*>(a.sc) + ((size_t)slot * nch + (size_t)chain * NC) * C * 16;
+    cstride = (size_t)C * 16;
+    cbytes = C * 16;
+  } else if (w == 1) {
+    cbase = reinterpret_cast<const char*>(a.pdg) + ((size_t)slot * nch + (size_t)chain * NC) * (C + 4) * 4;
+    cstride = (size_t)(C + 4) * 4;
+    cbytes = (C + 4) * 4;
+  } else {
+    cbase = vbase;
+    cstride = (size_t)C * HVB;
+    cbytes = 0;
+  }
 #pragma unroll
   for (int n = 0; n < VT::NVI; ++n) {
-    const int idx = min(max(w - 2, 0) * 64 + n * 128 + lane, C * VT::LPR - 1);
-    const int row = idx / VT::LPR, part = idx % VT::LPR;
-    v_off[n] = row * HV + part * EPV;
-    v_off_last[n] = min(row, n_last - 1) * HV + part * EPV;
-  }
-  const int o_row0 = 16 * rt + 4 * g4;
-  int o_off[4], o_off_last[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o_off[i] = (o_row0 + i) * HV + l16;
-    o_off_last[i] = min(o_row0 + i, n_last - 1) * HV + l16;
-  }
-  const int tri_off = kq_row * C + 8 * g4;
-  const int kcd = rt / 2;  // k-chunk holding this row tile's diagonal
-  FragMask<MT> dmask;
-  dmask.make(kq_row, 32 * kcd + 8 * g4, rev);
-  const size_t nch = (size_t)a.B * a.H * a.NC;
-  const float4* scb = a.sc + (size_t)slot * nch * C + (size_t)chain * NC * C;
-  const float* pdb = a.pd + (size_t)chain * NC * C;
-  const float* gnb = a.gn + (size_t)slot * nch + (size_t)chain * NC;
-  const MT* trib = static_cast<const MT*>(a.tri) + (size_t)chain * NC * C * C + tri_off;
-  const MT* pqkb = static_cast<const MT*>(a.pqk) + (size_t)chain * NC * C * C + tri_off;
-  float* const trash = a.trash + lane;
-
-  // ---- loaders (issued a step ahead, spread over the phases) ----
-  auto load_coop = [&](F& f, int64_t c) {
-    const bool last = c == NC - 1;
     if (w == 0) {
-      f.csc = scb[c * C + (lane % C)];
+      const int idx = lane % C;
+      c_off[n] = idx * 16;
+      c_lds[n] = SM::ST_SC + idx * 16;
     } else if (w == 1) {
-      f.cpd = pdb[c * C + (lane % C)];
-      f.cgn = gnb[c];
+      const int idx = min(lane, C / 4);
+      c_off[n] = idx * 16;
+      c_lds[n] = SM::ST_PD + idx * 16;
     } else {
-      const MT* p = vbase + c * CHV;
-#pragma unroll
-      for (int n = 0; n < VT::NVI; ++n) f.cv[n] = *reinterpret_cast<const f32x4*>(p + (last ? v_off_last[n] : v_off[n]));
+      const int idx = min((w - 2) * 64 + n * 128 + lane, C * VT::LPR - 1);
+      const int row = idx / VT::LPR, part = idx % VT::LPR;
+      c_off[n] = row * HVB + part * 16;
+      c_lds[n] = SM::ST_V + idx * 16;
     }
+  }
+
+  // ---- per-chunk resources ----
+  auto rs_rows = [&](const char* base, int c, uint32_t pitch, uint32_t tail) {
+    return make_rsrc(base + (size_t)c * C * pitch, extent(c, pitch, tail));
   };
-  auto load_rows = [&](frag* dst, const MT* base, int64_t c) {
-    const MT* p = base + c * CHD + (c == NC - 1 ? kq_off_last : kq_off);
+  auto rs_tri = [&](const char* base, int c) { return make_rsrc(base + (size_t)c * C * C * ES, C * C * ES); };
+  auto rs_coop = [&](int c) {
+    return make_rsrc(cbase + (size_t)c * cstride, w >= 2 ? extent(c, HVB, DT * ES) : cbytes);
+  };
+  // readout of chunk c; `on` = false gives an empty extent (nothing is read or written)
+  auto rs_out = [&](int c, bool on) {
+    return make_rsrc(obase + (size_t)c * C * HOB, on ? extent(c, HOB, DT * 4) : 0u);
+  };
+
+  // ---- loaders (issued a step ahead) ----
+  auto load_rows = [&](frag* dst, const char* base, int c) {
+    const rsrc_t r = rs_rows(base, c, HDB, DK * ES);
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) dst[ks] = M::load(p + 32 * ks);
+    for (int ks = 0; ks < DK / 32; ++ks) dst[ks] = bload_frag<MT>(r, kq_off + 32 * ks * ES);
   };
-  auto load_tri = [&](F& f, int64_t c) {
-    const MT* tp = trib + c * C * C;
-    const MT* pp = pqkb + c * C * C;
+  auto load_coop = [&](F& f, int c) {
+    const rsrc_t r = rs_coop(c);
+#pragma unroll
+    for (int n = 0; n < VT::NVI; ++n) f.cv[n] = bload16(r, c_off[n]);
+  };
+  auto load_tri = [&](F& f, int c) {  // every wave issues the same loads
+    const rsrc_t rt_ = rs_tri(trib, c), rp = rs_tri(pqkb, c);
 #pragma unroll
     for (int kc = 0; kc < C / 32; ++kc) {
-      if (tri_needed(rev, kc, rt)) {  // wave-uniform
-        f.tf[kc] = M::load(tp + 32 * kc);
-        f.pf[kc] = M::load(pp + 32 * kc);
-      }
+      f.tf[kc] = bload_frag<MT>(rt_, tri_offs[kc]);
+      f.pf[kc] = bload_frag<MT>(rp, tri_offs[kc]);
     }
   };
-  auto stash = [&](const F& f, int buf) {  // group-shared registers of a loaded stage -> LDS slot
-    if (w == 0) {
-      if (lane < C) g_sc[dg][buf][lane] = f.csc;
-    } else if (w == 1) {
-      if (lane < C) g_pd[dg][buf][lane] = f.cpd;
-      if (lane == 0) g_gn[dg][buf] = f.cgn;
-    } else {
+  auto stash = [&](const F& f, int buf) {  // group-shared pieces of a loaded stage -> LDS
 #pragma unroll
-      for (int n = 0; n < VT::NVI; ++n) {
-        const int idx = (w - 2) * 64 + n * 128 + lane;
-        if (idx < C * VT::LPR) *reinterpret_cast<f32x4*>(&g_v[dg][buf][idx * EPV]) = f.cv[n];
-      }
-    }
-  };
-  // output element (row o_row0+i, column tile of unit j) of chunk c
-  auto out_at = [&](int64_t c, int j, int i) -> float* {
-    const int ct = (w + 4 * j) / RT;
-    return obase + c * CHV + (c == NC - 1 ? o_off_last[i] : o_off[i]) + 16 * ct;
-  };
-  auto row_valid = [&](int64_t c, int i) { return o_row0 + i < (c == NC - 1 ? n_last : C); };
-
-  if (threadIdx.x == 0) {
-    s_gbar[0] = s_gbar[1] = 0;
-    s_prog[0] = s_prog[1] = 0;
-  }
-  int epoch = 0;  // group barriers passed (wave-uniform)
-  auto gsync = [&]() {
-    if (DIRS == 1) {
-      __syncthreads();
-    } else {
-      ++epoch;
-      group_barrier(&s_gbar[dg], 4 * epoch, lane);
-    }
+    for (int n = 0; n < VT::NVI; ++n) *reinterpret_cast<f32x4*>(&stg[dg][buf][c_lds[n]]) = f.cv[n];
   };
 
   // ---- initial state into accumulators (S^T tiles) and the operand copy ----
@@ -337,36 +393,28 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
     M::store4(Sb + (16 * sct + l16) * SP + 16 * srt + 4 * g4, Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
   }
 
-  // The other direction's readout of the chunk of step s, if it was stored
-  // in an earlier step.  A first visitor stores in the last phase of its
-  // step, so these loads are issued after the first barrier of step s (which
-  // orders them after every store of step s-1 and earlier), and before the
-  // next stage's remaining loads: the memory counter retires in order.
-  float part[UPW][4];
-  auto chunk_at = [&](int64_t s) { return rev ? NC - 1 - s : s; };
-  auto load_part = [&](int64_t s) {
-    if (DIRS == 2) {
-      const int64_t so = NC - 1 - s;
-      const bool second = s > so || (s == so && rev);
-      if (second) {  // the other group stored this chunk in its step so: wait for it
-        spin_until_at_least(&s_prog[1 - dg], 4 * (int)(so + 1), __ATOMIC_ACQUIRE);
-      }
-      const int64_t c = chunk_at(s);
-#pragma unroll
-      for (int j = 0; j < UPW; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[j][i] = *out_at(c, j, i);
-    }
+  auto chunk_at = [&](int s) { return rev ? NC - 1 - s : s; };
+  // a visit stores its readout directly unless the other direction visited
+  // the chunk before (bidirectional scans only)
+  auto first_visit = [&](int s) {
+    const int so = NC - 1 - s;  // step at which the other direction visits the same chunk
+    return DIRS == 1 || s < so || (s == so && !rev);
   };
 
-  auto step = [&](F& st, F& nx, int64_t s, int64_t cn) {
-    const int64_t c = chunk_at(s);
-    const int64_t so = NC - 1 - s;  // step at which the other direction visits chunk c
-    const bool first = DIRS == 1 || s < so || (s == so && !rev);
-    const int buf = (int)(s & 1);
+  // bidirectional: readout of the previous step (second visits) and the
+  // other direction's partial for it
+  f32x4 Oprev[UPW], part[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) Oprev[j] = part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](F& st, F& nx, const int s, const int cn) {
+    const int c = chunk_at(s);
+    const bool first = first_visit(s);
+    const int buf = s & 1;
+    const unsigned char* sg = stg[dg][buf];
     float4 sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = g_sc[dg][buf][o_row0 + i];
+    for (int i = 0; i < 4; ++i) sc[i] = *reinterpret_cast<const float4*>(sg + SM::ST_SC + (o_row0 + i) * 16);
 
     // [A] k tile into LDS; Y = K S^T, Z = Q S^T; X
     if (w < RT) {
@@ -378,10 +426,10 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            KT[(32 * ks + 8 * g4 + e) * TP + kq_row] = (MT)M::get(st.kf[ks], e);
+          for (int e = 0; e < 8; ++e) KT[(32 * ks + 8 * g4 + e) * TP + kq_row] = (MT)M::get(st.kf[ks], e);
       }
     }
+    load_coop(nx, cn);
     load_rows(nx.kf, kbase, cn);
     f32x4 X[UPW], Z[UPW], Vn[UPW];
 #pragma unroll
@@ -394,19 +442,30 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
         for (int ks = 0; ks < DK / 32; ++ks) {
           const frag sb = M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4);
           y = M::mma(st.kf[ks], sb, y);
-          z = M::mma(st.qf[ks], sb, z);
+          z = M::mma(sb, st.qf[ks], z);  // Z^T: lane (l16, g4) holds Z[token 16 rt + l16][16 ct + 4 g4 + i]
+        }
+        // raw values v[o_row0 + i][16 ct + l16], i = 0..3
+        f32x4 vv;
+        if constexpr (KROW) {
+          const v4s t4 = lds_read_tr16(sg + SM::ST_V + ((o_row0 + (l16 >> 2)) * DT + 16 * ct + 4 * (l16 & 3)) * 2);
+          bf16x4 b4;
+          __builtin_memcpy(&b4, &t4, 8);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vv[i] = (float)b4[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vv[i] = *reinterpret_cast<const float*>(sg + SM::ST_V + ((o_row0 + i) * DT + 16 * ct + l16) * 4);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          X[j][i] = sc[i].x * (to_f32(g_v[dg][buf][(o_row0 + i) * DT + 16 * ct + l16]) - sc[i].y * y[i]);
+        for (int i = 0; i < 4; ++i) X[j][i] = sc[i].x * (vv[i] - sc[i].y * y[i]);
         Z[j] = z;
         M::store4(XT + (16 * ct + l16) * TP + o_row0, X[j][0], X[j][1], X[j][2], X[j][3]);
       }
     }
-    gsync();
+    __syncthreads();
 
     // [B] Vnew = X + strict(Tinv) X
-    load_part(s);
     load_rows(nx.qf, qbase, cn);
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
@@ -415,100 +474,131 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
         const int ct = u / RT;
         f32x4 acc = X[j];
 #pragma unroll
-        for (int kc = 0; kc < C / 32; ++kc) {
-          if (tri_needed(rev, kc, rt)) {
-            const frag tf = kc == kcd ? dmask.apply(st.tf[kc]) : st.tf[kc];
-            acc = M::mma(tf, M::load(XT + (16 * ct + l16) * TP + 32 * kc + 8 * g4), acc);
-          }
-        }
+        for (int kc = 0; kc < C / 32; ++kc)
+          acc = M::mma(tmask[kc].apply(st.tf[kc]), M::load(XT + (16 * ct + l16) * TP + 32 * kc + 8 * g4), acc);
         Vn[j] = acc;
         const int o = (16 * ct + l16) * TP + o_row0;
         f32x4 vs;
 #pragma unroll
         for (int i = 0; i < 4; ++i) vs[i] = sc[i].w * acc[i];
-        M::store4(VnT + o, acc[0], acc[1], acc[2], acc[3]);
-        M::store4(VsT + o, vs[0], vs[1], vs[2], vs[3]);
-        if (SPLIT) {
-          f32x4 rn, rs;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            rn[i] = acc[i] - (float)(MT)acc[i];
-            rs[i] = vs[i] - (float)(MT)vs[i];
-          }
-          M::store4(VnL + o, rn[0], rn[1], rn[2], rn[3]);
-          M::store4(VsL + o, rs[0], rs[1], rs[2], rs[3]);
+        if constexpr (SPLIT) {
+          store_split4(VnT + o, VnL + o, acc);
+          store_split4(VsT + o, VsL + o, vs);
+        } else {
+          M::store4(VnT + o, acc[0], acc[1], acc[2], acc[3]);
+          M::store4(VsT + o, vs[0], vs[1], vs[2], vs[3]);
         }
       }
     }
-    gsync();
+    __syncthreads();
 
-    // [C] chunk readout (a causal scan stores it right away)
+    // [C] chunk readout (transposed: lane (l16, g4) of a unit holds
+    // O[token 16 rt + l16][16 ct + 4 g4 + i], four consecutive values of one
+    // output row, stored as one 16-byte piece); state update
     load_tri(nx, cn);
+    const float gn = *reinterpret_cast<const float*>(sg + SM::ST_GN);
+    const float scz = *reinterpret_cast<const float*>(sg + SM::ST_SC + tok * 16 + 8);
+    frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
+    if constexpr (SPLIT) {
+      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + tok * 4));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pdiag[e] = r;
+    }
     f32x4 O[UPW];
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
       const int u = w + 4 * j;
       if (ALL_UNITS || u < RT * NT) {
         const int ct = u / RT;
-        f32x4 acc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = sc[i].z * Z[j][i] + g_pd[dg][buf][o_row0 + i] * Vn[j][i];
+        f32x4 acc = Z[j] * scz;
 #pragma unroll
         for (int kc = 0; kc < C / 32; ++kc) {
-          if (tri_needed(rev, kc, rt)) {
-            const frag pf = kc == kcd ? dmask.apply(st.pf[kc]) : st.pf[kc];
-            const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
-            acc = M::mma(pf, M::load(VnT + o), acc);
-            if (SPLIT) acc = M::mma(pf, M::load(VnL + o), acc);
+          const frag pf = pmask[kc].apply(st.pf[kc]);
+          const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
+          const frag vh = M::load(VnT + o);
+          acc = M::mma(vh, pf, acc);
+          if constexpr (SPLIT) {
+            acc = M::mma(M::load(VnL + o), pf, acc);
+            // self-term remainder (pqk holds the rounded self term): an
+            // exact-enough diagonal product with the hi part of Vnew
+            acc = M::mma(vh, diag_only[kc].apply(pdiag), acc);
           }
         }
         O[j] = acc;
-        if (DIRS == 1) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) *(row_valid(c, i) ? out_at(c, j, i) : trash) = acc[i];
-        }
       }
     }
-    // state update S^T = gn S^T + K^T Vs
-    const float gn = g_gn[dg][buf];
-#pragma unroll
-    for (int j = 0; j < SUPW; ++j) {
-      const int u = w + 4 * j;
-      const int srt = u % SRT, sct = u / SRT;
-      f32x4 acc = Sacc[j] * gn;
-#pragma unroll
-      for (int kc = 0; kc < C / 32; ++kc) {
-        frag ka;
-        if constexpr (KROW) {
-          ka = load_kt_frag(KT, KP, 32 * kc, 16 * srt, l16, g4);
-        } else {
-          ka = M::load(KT + (16 * srt + l16) * TP + 32 * kc + 8 * g4);
-        }
-        const int o = (16 * sct + l16) * TP + 32 * kc + 8 * g4;
-        acc = M::mma(ka, M::load(VsT + o), acc);
-        if (SPLIT) acc = M::mma(ka, M::load(VsL + o), acc);
-      }
-      Sacc[j] = acc;
-      M::store4(Sb + (16 * sct + l16) * SP + 16 * srt + 4 * g4, acc[0], acc[1], acc[2], acc[3]);
-    }
-    stash(nx, buf ^ 1);  // next step's group-shared operands (its slot was last read one step ago)
-    gsync();
-
-    // [D] bidirectional: the first visitor stores its readout, the second
-    // adds its own to the one stored by the other group (loaded in [B]).  A
-    // first visitor then makes its stores visible and counts its progress.
-    if (DIRS == 2) {
+    // store: a first visit stores its own readout; a bidirectional second
+    // visit stores the previous step's readout plus the partial loaded for it
+    {
+      const bool pend = DIRS == 2 && s > 0 && !first_visit(s - 1);
+      const bool on = first || pend;
+      const rsrc_t ro = rs_out(first ? c : chunk_at(max(s - 1, 0)), on);
 #pragma unroll
       for (int j = 0; j < UPW; ++j) {
-        if (ALL_UNITS || w + 4 * j < RT * NT) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *(row_valid(c, i) ? out_at(c, j, i) : trash) = O[j][i] + (first ? 0.f : part[j][i]);
-        }
+        const int u = w + 4 * j;
+        if (ALL_UNITS || u < RT * NT) bstore16(ro, ot_off + (u / RT) * 64, first ? O[j] : Oprev[j] + part[j]);
       }
-      if (first) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        if (lane == 0) __hip_atomic_fetch_add(&s_prog[dg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    // state update S^T = gn S^T + K^T Vs.  Wave w owns the state tiles
+    // (dk tile w + 4 js, dv tile jt); every operand fragment is read once
+    // (the products only start after all reads, so no LDS store in between
+    // forces a re-read), then the operand copy for the next step is written.
+    {
+      constexpr int JS = SRT / 4;  // dk tiles per wave
+      frag ka[JS][C / 32], vh[NT][C / 32], vl[NT][C / 32];
+#pragma unroll
+      for (int js = 0; js < JS; ++js)
+#pragma unroll
+        for (int kc = 0; kc < C / 32; ++kc) {
+          const int srt = w + 4 * js;
+          if constexpr (KROW) {
+            ka[js][kc] = load_kt_frag(KT, KP, 32 * kc, 16 * srt, l16, g4);
+          } else {
+            ka[js][kc] = M::load(KT + (16 * srt + l16) * TP + 32 * kc + 8 * g4);
+          }
+        }
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+        for (int kc = 0; kc < C / 32; ++kc) {
+          const int o = (16 * jt + l16) * TP + 32 * kc + 8 * g4;
+          vh[jt][kc] = M::load(VsT + o);
+          if (SPLIT) vl[jt][kc] = M::load(VsL + o);
+        }
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+        for (int js = 0; js < JS; ++js) {
+          const int j = jt * JS + js;  // = (w + 4 j) / SRT and % SRT as in the state load and store
+          f32x4 acc = Sacc[j] * gn;
+#pragma unroll
+          for (int kc = 0; kc < C / 32; ++kc) {
+            acc = M::mma(ka[js][kc], vh[jt][kc], acc);
+            if (SPLIT) acc = M::mma(ka[js][kc], vl[jt][kc], acc);
+          }
+          Sacc[j] = acc;
+        }
+#pragma unroll
+      for (int j = 0; j < SUPW; ++j) {
+        const int srt = w + 4 * (j % JS), sct = j / JS;
+        M::store4(Sb + (16 * sct + l16) * SP + 16 * srt + 4 * g4, Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
+      }
+    }
+    stash(nx, buf ^ 1);  // next step's group-shared operands (its slot was last read one step ago)
+    __syncthreads();
+
+    // [D] bidirectional second visit: the first visitor stored this chunk's
+    // partial at a step no later than this one, before the barrier above;
+    // load it now, add it next step
+    if (DIRS == 2) {
+      const rsrc_t rp = rs_out(c, !first);
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) {
+        const int u = w + 4 * j;
+        if (ALL_UNITS || u < RT * NT) {
+          part[j] = bload16(rp, ot_off + (u / RT) * 64);
+          Oprev[j] = O[j];
+        }
       }
     }
   };
@@ -517,21 +607,25 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   // while step s computes (past the last step a valid chunk is reloaded)
   F sA, sB;
   if (NC > 0) {
-    const int64_t c0 = chunk_at(0);
+    const int c0 = chunk_at(0);
     load_coop(sA, c0);
     load_rows(sA.kf, kbase, c0);
     load_rows(sA.qf, qbase, c0);
     load_tri(sA, c0);
     stash(sA, 0);
     __syncthreads();
-    for (int64_t s = 0; s < NC; s += 2) {
-      const int64_t c1 = chunk_at(min(s + 1, NC - 1));
-      load_coop(sB, c1);
-      step(sA, sB, s, c1);
-      if (s + 1 < NC) {
-        const int64_t c2 = chunk_at(min(s + 2, NC - 1));
-        load_coop(sA, c2);
-        step(sB, sA, s + 1, c2);
+    int s = 0;
+    for (; s + 1 < NC; s += 2) {
+      step(sA, sB, s, chunk_at(s + 1));
+      step(sB, sA, s + 1, chunk_at(min(s + 2, NC - 1)));
+    }
+    if (s < NC) step(sA, sB, s, chunk_at(s));
+    if (DIRS == 2) {  // the last second visit's readout
+      const rsrc_t ro = rs_out(chunk_at(NC - 1), !first_visit(NC - 1));
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) {
+        const int u = w + 4 * j;
+        if (ALL_UNITS || u < RT * NT) bstore16(ro, ot_off + (u / RT) * 64, Oprev[j] + part[j]);
       }
     }
   } else {

@@ -114,17 +114,19 @@ __device__ __forceinline__ typename Mma<MT>::frag mask_tri(typename Mma<MT>::fra
 // dirs = number of computed directions):
 //   tri  [NBH*NC][C][C]  MT : strictly-lower part = forward (I+L)^{-1},
 //                             strictly-upper part = reverse (I+L)^{-1}
-//   pqk  [NBH*NC][C][C]  MT : strictly-lower = forward decayed q^.k^,
-//                             strictly-upper = reverse decayed q^.k^
+//   pqk  [NBH*NC][C][C]  MT : decayed q^.k^ with the self terms q^_t.k^_t on
+//                             the diagonal; strictly-lower part = forward,
+//                             strictly-upper part = reverse
 //   sc   [dirs][NBH*NC][C] float4 : {beta, e^g rk, e^g rq, e^(gn-g) rk}
-//   pd   [NBH*NC][C]     float : q^_t . k^_t (self term weight)
-//   gn   [dirs][NBH*NC]  float : e^(gn), the chunk's total decay
-//   trash [256]          float : sink for stores that must not land in `out`
-//                                (rows past the sequence end), so the state
-//                                chain can store without branching
+//   pdg  [dirs][NBH*NC][C+4] float : per token, the part of the self term
+//                             q^_t.k^_t that the operand type of pqk drops
+//                             (x - MT(x); zero for fp32 operands), then
+//                             e^(gn) (the chunk's total decay) and three
+//                             zeros, so one chunk record is a whole number of
+//                             16-byte pieces
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t tri, pqk, sc, pd, gn, trash, total;
+  size_t tri, pqk, sc, pdg, total;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -136,9 +138,7 @@ static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_
   L.tri = off; off = align_up(off + nch * C * C * mt_bytes, 256);
   L.pqk = off; off = align_up(off + nch * C * C * mt_bytes, 256);
   L.sc = off;  off = align_up(off + (size_t)dirs * nch * C * 16, 256);
-  L.pd = off;  off = align_up(off + nch * C * 4, 256);
-  L.gn = off;  off = align_up(off + (size_t)dirs * nch * 4, 256);
-  L.trash = off; off = align_up(off + 256 * 4, 256);
+  L.pdg = off; off = align_up(off + (size_t)dirs * nch * (C + 4) * 4, 256);
   L.total = off;
   return L;
 }
@@ -156,9 +156,7 @@ struct ScanArgs {
   void* tri;
   void* pqk;
   float4* sc;
-  float* pd;
-  float* gn;
-  float* trash;
+  float* pdg;
   int64_t B, T, H, NC;
   int dv;
   int fwd_on, rev_on;  // which directions are computed

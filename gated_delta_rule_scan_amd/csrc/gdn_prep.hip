@@ -18,8 +18,9 @@
 // pieces: Tinv and the decayed Q^K^^T for both directions (the forward one
 // in the strictly-lower triangle, the reverse one -- the same recurrence with
 // tokens visited last-to-first -- in the strictly-upper triangle, both in
-// natural token order), the self-term weights q^_t.k^_t and the per-token
-// gate scales.  One Gram matrix K K^T serves both directions.
+// natural token order, with the self terms q^_t.k^_t on the shared diagonal
+// of Q^K^^T), the per-token gate scales and the chunk decays.  One Gram matrix
+// K K^T serves both directions.
 //
 // Normalisation is never applied to the operands: K K^T and Q K^T are taken
 // on the raw inputs on the matrix cores (fp32 accumulation) and the fp32 row
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   const int64_t cid = bh * a.NC + c;
   const int fwd_on = a.fwd_on, rev_on = a.rev_on;
   const int fslot = 0, rslot = fwd_on ? 1 : 0;
+  const size_t nch = (size_t)a.B * a.H * a.NC;
 
   // ---- stage raw q and k of this chunk into LDS (padded rows are zero) ----
   {
@@ -202,7 +204,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
             pv = s_rq[r] * rkc * accP[j][i] * gam;
           }
         } else {
-          a.pd[cid * C + r] = s_rq[r] * s_rk[r] * accP[j][i];
+          // self term q^_r . k^_r: on the diagonal in the operand type, the
+          // remainder that type drops into each direction's record
+          pv = s_rq[r] * s_rk[r] * accP[j][i];
+          const float lo = pv - (float)(MT)pv;
+          if (fwd_on) a.pdg[((size_t)fslot * nch + cid) * (C + 4) + r] = lo;
+          if (rev_on) a.pdg[((size_t)rslot * nch + cid) * (C + 4) + r] = lo;
         }
         Lm[r * LP + col] = lv;
         Pst[r * PP + col] = (MT)pv;
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
         const int col = c0 + e;
         const bool keep = (col < r && fwd_on) || (col > r && rev_on);
         tv[e] = (MT)(keep ? Ti[r * LP + col] : 0.f);
-        pv[e] = keep ? Pst[r * PP + col] : (MT)0.f;
+        pv[e] = (keep || col == r) ? Pst[r * PP + col] : (MT)0.f;
       }
       __builtin_memcpy(tri + p * EPS, tv, 16);
       __builtin_memcpy(pqk + p * EPS, pv, 16);
@@ -325,15 +332,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       const float g = s_g[0][tid], gl = s_g[0][C - 1];
       const float eg = exp2f(g);
       float4 v = in ? make_float4(s_bt[0][tid], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
-      a.sc[(size_t)fslot * a.B * a.H * a.NC * C + cid * C + tid] = v;
-      if (tid == 0) a.gn[(size_t)fslot * a.B * a.H * a.NC + cid] = exp2f(gl);
+      a.sc[(fslot * nch + cid) * C + tid] = v;
+      if (tid < 4) a.pdg[((size_t)fslot * nch + cid) * (C + 4) + C + tid] = tid == 0 ? exp2f(gl) : 0.f;
     }
     if (rev_on) {
       const float g = s_g[1][tid], gl = s_g[1][0];
       const float eg = exp2f(g);
       float4 v = in ? make_float4(s_bt[1][tid], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
-      a.sc[(size_t)rslot * a.B * a.H * a.NC * C + cid * C + tid] = v;
-      if (tid == 0) a.gn[(size_t)rslot * a.B * a.H * a.NC + cid] = exp2f(gl);
+      a.sc[(rslot * nch + cid) * C + tid] = v;
+      if (tid < 4) a.pdg[((size_t)rslot * nch + cid) * (C + 4) + C + tid] = tid == 0 ? exp2f(gl) : 0.f;
     }
   }
 }

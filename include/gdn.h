@@ -105,7 +105,8 @@ typedef struct {
 } gdn_problem_t;
 
 /* Bytes of workspace gdn_forward needs for this problem and direction
- * (0 if the problem is invalid or unsupported).  Pure host arithmetic. */
+ * (0 if the problem is invalid or unsupported, and for T = 0, which needs
+ * none).  Pure host arithmetic. */
 size_t gdn_workspace_bytes(const gdn_problem_t* p, int32_t direction);
 
 /* Enqueue the scan described by `p` on p->stream.  See the file comment for

@@ -80,7 +80,7 @@ def test_workspace_bytes():
     assert gdn.workspace_bytes(1, 300, 2, 64, 64, "f32", "fwd") > gdn.workspace_bytes(1, 300, 2, 64, 64, "bf16", "fwd")
     # chunk count rounds up: one token more than a chunk multiple needs one chunk more
     assert gdn.workspace_bytes(1, 129, 1, 64, 64, "bf16", "fwd") > gdn.workspace_bytes(1, 128, 1, 64, 64, "bf16", "fwd")
-    assert gdn.workspace_bytes(1, 0, 1, 64, 64, "bf16", "fwd") > 0  # sequence-independent parts only
+    assert gdn.workspace_bytes(1, 0, 1, 64, 64, "bf16", "fwd") == 0  # an empty sequence needs none
 
 
 @pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=80), dict(chunk=48), dict(chunk=16), dict(dv_tile=64),
