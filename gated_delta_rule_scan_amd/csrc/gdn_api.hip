@@ -8,8 +8,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <type_traits>
-
 #include "gdn.h"
 #include "gdn_common.h"
 #include "gdn_internal.h"
@@ -19,7 +17,7 @@ namespace {
 
 struct Plan {
   int C;        // chunk length
-  int NT;       // 16-column value tiles per chain workgroup
+  int NT;       // 16-column value tiles per chain workgroup (0: chosen at launch)
   int dirs;     // computed directions (slots)
   int fwd_on, rev_on;
   int64_t NC;   // chunks per sequence
@@ -29,15 +27,27 @@ struct Plan {
 
 bool supported_dim(int64_t d) { return d == 64 || d == 128; }
 
-// fp32 operands with dk = 128 and 64-token chunks only fit LDS with 16-wide tiles.
-bool tile_fits(int32_t dtype, int64_t dk, int C, int NT) {
-  return !(NT == 2 && dtype == GDN_DTYPE_F32 && dk == 128 && C == 64);
+// Compute units of the current device (cached per device; 256 on MI355X).
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
-int pick_tiles(int64_t nbh, int64_t dv) {
-  // Largest tile width that still gives about one workgroup per compute unit.
-  const int64_t want = 240;
-  if (nbh * (dv / 32) >= want) return 2;
+int pick_tiles(int64_t nbh, int64_t dv, int dirs) {
+  // A 32-wide value tile amortises the per-step fixed work of a chain (k
+  // tile, triangles, barriers) over twice the columns.  That beats 16-wide
+  // chains as soon as those would have to share compute units (measured on
+  // MI355X: 1.4x for 384 16-wide chains on 256 units, even though the 192
+  // wider chains leave a quarter of the units idle); with fewer chains than
+  // units, the narrower tiles keep more units busy.
+  if (nbh * dirs * (dv / 16) > compute_units()) return 2;
   return 1;
 }
 
@@ -52,16 +62,12 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   if (p->T > ((int64_t)1 << 31) / 2) return GDN_ERR_UNSUPPORTED;
   const int C = p->chunk == 0 ? 64 : p->chunk;
   if (C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
-  int NT;
-  if (p->dv_tile == 0) {
-    NT = pick_tiles(p->B * p->H, p->dv);
-    if (!tile_fits(p->dtype, p->dk, C, NT)) NT = 1;
-  } else {
+  int NT = 0;  // 0: chosen at launch (any choice divides dv)
+  if (p->dv_tile != 0) {
     if (p->dv_tile != 16 && p->dv_tile != 32) return GDN_ERR_UNSUPPORTED;
     NT = p->dv_tile / 16;
-    if (!tile_fits(p->dtype, p->dk, C, NT)) return GDN_ERR_UNSUPPORTED;
+    if (p->dv % (16 * NT) != 0) return GDN_ERR_UNSUPPORTED;
   }
-  if (p->dv % (16 * NT) != 0) return GDN_ERR_UNSUPPORTED;
   pl->C = C;
   pl->NT = NT;
   pl->fwd_on = direction != GDN_DIR_REVERSE;
@@ -97,12 +103,8 @@ prep_fn prep_for(int dk, int C) {
 
 template <typename MT, int DK, int C>
 chain_fn chain_for3(int NT, int dirs) {
-  if (NT == 1) return dirs == 2 ? launch_chain<MT, DK, C, 1, 2> : launch_chain<MT, DK, C, 1, 1>;
-  if constexpr (std::is_same<MT, float>::value && DK == 128 && C == 64) {
-    return nullptr;  // rejected by make_plan
-  } else {
-    return dirs == 2 ? launch_chain<MT, DK, C, 2, 2> : launch_chain<MT, DK, C, 2, 1>;
-  }
+  if (NT == 1) return dirs == 2 ? launch_chain<MT, DK, C, 1, true> : launch_chain<MT, DK, C, 1, false>;
+  return dirs == 2 ? launch_chain<MT, DK, C, 2, true> : launch_chain<MT, DK, C, 2, false>;
 }
 
 template <typename MT>
@@ -177,8 +179,10 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   }
   a.B = B; a.T = T; a.H = H; a.NC = pl.NC; a.dv = (int)dv;
   a.fwd_on = pl.fwd_on; a.rev_on = pl.rev_on; a.dirs = pl.dirs;
+  a.zero_out = pl.dirs == 2;
 
   const bool bf = p->dtype == GDN_DTYPE_BF16;
+  if (pl.NT == 0) pl.NT = pick_tiles(B * H, dv, pl.dirs);
   hipEvent_t* ev = static_cast<hipEvent_t*>(p->timing_events);
   hipError_t e = hipSuccess;
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return GDN_ERR_HIP;
@@ -188,11 +192,11 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return GDN_ERR_HIP;
-  // bidirectional: both direction groups in one workgroup; single direction:
-  // one group, told whether it runs in reverse
-  const int dirs_in_wg = pl.dirs;
-  chain_fn cf = bf ? chain_for<bf16>((int)dk, pl.C, pl.NT, dirs_in_wg)
-                   : chain_for<float>((int)dk, pl.C, pl.NT, dirs_in_wg);
+  // bidirectional: one workgroup per direction, readouts accumulated into
+  // the output the preparation kernel zeroed; single direction: told whether
+  // it runs in reverse
+  chain_fn cf = bf ? chain_for<bf16>((int)dk, pl.C, pl.NT, pl.dirs)
+                   : chain_for<float>((int)dk, pl.C, pl.NT, pl.dirs);
   if (!cf) return GDN_ERR_UNSUPPORTED;
   e = cf(a, direction == GDN_DIR_REVERSE ? 1 : 0, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;

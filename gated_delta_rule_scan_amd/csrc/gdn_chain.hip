@@ -16,15 +16,15 @@
 // b_t v_t k^_t^T, o_t = S_t q^_t (derivation in the preparation kernel).
 //
 // Bidirectional scans ("Video DeltaNet", "Methodology in Plain English": a
-// forward and a backward recurrent state whose readouts are added) run as two
-// direction groups of four waves in one workgroup, in step with each other.
-// At step s the forward group handles chunk s and the reverse group chunk
-// NC-1-s, so every chunk is visited twice.  The first visitor stores its
-// readout; the second loads that partial once a workgroup barrier has ordered
-// it after the store, and adds and stores its own one step later, so the load
-// has a whole step to arrive.  The sum needs no atomics and no
-// inter-workgroup synchronisation, and `out` is written by plain stores only.
-//
+// forward and a backward recurrent state whose readouts are added) run the
+// two directions in separate workgroups, which the hardware overlaps freely
+// (two direction groups on one workgroup barrier would make every wave wait
+// for the slowest of both at every phase, and per-group LDS barriers are
+// slow under the groups' LDS traffic).  Both add their readouts into the
+// output with fp32 atomic adds; the preparation kernel zeroes it first, and
+// two addends onto zero give the same sum in either order, so the result is
+// deterministic and no workgroup ever waits for another.
+
 // Every global access goes through a raw buffer resource whose extent is the
 // valid part of the chunk: reads past it return zero and writes past it are
 // dropped.  Rows past the end of the sequence therefore need no clamping and
@@ -206,8 +206,27 @@ __device__ __forceinline__ void store_split4(bf16* hi_p, bf16* lo_p, f32x4 x) {
   *reinterpret_cast<bf16x4*>(lo_p) = l;
 }
 
-template <typename MT, int DK, int C, int NT, int DIRS>
-__global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
+
+// Readout of one chunk tile into `out`.  ACC = false: plain 16-byte stores of
+// the transposed tile (lane (l16, g4) holds out[token 16 rt + l16][16 ct +
+// 4 g4 + i]).  ACC = true (bidirectional scans, where the forward and the
+// reverse workgroup each add their readout into the zeroed output): fp32
+// atomic adds of the row-layout tile (lane (l16, g4) holds out[token
+// 16 rt + 4 g4 + i][16 ct + l16]), so each instruction covers whole 64-byte
+// row segments.  Two addends onto zero give the same sum in either order.
+template <bool ACC>
+__device__ __forceinline__ void put_out(rsrc_t r, uint32_t off, uint32_t row_pitch, f32x4 o) {
+  if constexpr (ACC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(o[i], r, (int)(off + i * row_pitch), 0, 0);
+  } else {
+    bstore16(r, off, o);
+  }
+}
+
+template <typename MT, int DK, int C, int NT, bool ACC>
+__global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
   using M = Mma<MT>;
   using frag = typename M::frag;
   using SM = ChainSmem<MT, DK, C, NT>;
@@ -223,13 +242,16 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   constexpr bool ALL_UNITS = (RT * NT) % 4 == 0;
   static_assert(SRT % 4 == 0, "each wave owns whole dk-tile columns of the state");
 
-  __shared__ __align__(16) MT smem[DIRS * SM::per_group];
-  __shared__ __align__(16) unsigned char stg[DIRS][2][SM::ST_BYTES];
+  __shared__ __align__(16) MT smem[SM::per_group];
+  __shared__ __align__(16) unsigned char stg[2][SM::ST_BYTES];
 
-  // XCD-aware numbering: workgroup id -> (chain, value tile)
+  // XCD-aware numbering: workgroup id -> (chain, direction, value tile); all
+  // workgroups of one (batch, head) land on the same XCD
+  const int ndir = ACC ? 2 : 1;
   const int id = blockIdx.x;
   const int xcd = id & 7, kk = id >> 3;
-  const int chain = (kk / ntiles) * 8 + xcd;
+  const int chain = (kk / (ntiles * ndir)) * 8 + xcd;
+  const int dslot = (kk % (ntiles * ndir)) / ntiles;
   const int tile = kk % ntiles;
   if (chain >= nbh) return;
   const int NC = (int)a.NC;
@@ -237,18 +259,17 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   const int64_t b = chain / H, h = chain % H;
   const int dv = a.dv;
   const int dv0 = tile * DT;
+  const bool rev = ACC ? (dslot == 1) : (rev_single != 0);
+  const int slot = dslot;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int dg = wave >> 2, w = wave & 3;
-  const bool rev = DIRS == 2 ? (dg == 1) : (rev_single != 0);
-  const int slot = DIRS == 2 ? dg : 0;
   const int rt = w % RT;
 
   constexpr bool KROW = SM::KROW;
   constexpr int KP = SM::KP;
-  MT* KT = smem + dg * SM::per_group;        // k tile (layout: see ChainSmem)
+  MT* KT = smem;                             // k tile (layout: see ChainSmem)
   MT* XT = KT + SM::k_elems;                 // [DT][TP]  pseudo-values X^T
   MT* VnT = XT + DT * TP;                    // [DT][TP]  Vnew^T (hi part)
   MT* VsT = VnT + DT * TP;                   // [DT][TP]  (scaled Vnew)^T (hi part)
@@ -285,17 +306,18 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
     tmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, false, kc == kcd);
     pmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, true, kc == kcd);
   }
-  const int tok = 16 * rt + l16;  // token of this lane in the transposed readout
-  const uint32_t ot_off = tok * HOB + 16 * g4;
+  // readout offsets of unit column tile 0: transposed (token kq_row, four
+  // columns from 4 g4) or row layout (rows o_row0 + i, column l16)
+  const uint32_t out_off = ACC ? o_row0 * HOB + l16 * 4 : kq_row * HOB + 16 * g4;
   // bf16 operands: the self term's remainder enters as a diagonal fragment;
-  // in k-chunk kc this lane holds element `tok - 32 kc - 8 g4` of it when that
-  // lies in 0..7 (only ever in the k-chunk of the diagonal)
+  // in k-chunk kc this lane (row kq_row of P) holds element `kq_row - 32 kc -
+  // 8 g4` of it when that lies in 0..7 (only ever in the k-chunk of the diagonal)
   FragMask<MT> diag_only[C / 32];
 #pragma unroll
   for (int kc = 0; kc < C / 32; ++kc) {
 #pragma unroll
     for (int i = 0; i < FragMask<MT>::NW; ++i) diag_only[kc].m[i] = 0u;
-    const int e0 = tok - 32 * kc - 8 * g4;
+    const int e0 = kq_row - 32 * kc - 8 * g4;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (e == e0) {
@@ -352,10 +374,7 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   auto rs_coop = [&](int c) {
     return make_rsrc(cbase + (size_t)c * cstride, w >= 2 ? extent(c, HVB, DT * ES) : cbytes);
   };
-  // readout of chunk c; `on` = false gives an empty extent (nothing is read or written)
-  auto rs_out = [&](int c, bool on) {
-    return make_rsrc(obase + (size_t)c * C * HOB, on ? extent(c, HOB, DT * 4) : 0u);
-  };
+  auto rs_out = [&](int c) { return make_rsrc(obase + (size_t)c * C * HOB, extent(c, HOB, DT * 4)); };
 
   // ---- loaders (issued a step ahead) ----
   auto load_rows = [&](frag* dst, const char* base, int c) {
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   };
   auto stash = [&](const F& f, int buf) {  // group-shared pieces of a loaded stage -> LDS
 #pragma unroll
-    for (int n = 0; n < VT::NVI; ++n) *reinterpret_cast<f32x4*>(&stg[dg][buf][c_lds[n]]) = f.cv[n];
+    for (int n = 0; n < VT::NVI; ++n) *reinterpret_cast<f32x4*>(&stg[buf][c_lds[n]]) = f.cv[n];
   };
 
   // ---- initial state into accumulators (S^T tiles) and the operand copy ----
@@ -394,24 +413,11 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   }
 
   auto chunk_at = [&](int s) { return rev ? NC - 1 - s : s; };
-  // a visit stores its readout directly unless the other direction visited
-  // the chunk before (bidirectional scans only)
-  auto first_visit = [&](int s) {
-    const int so = NC - 1 - s;  // step at which the other direction visits the same chunk
-    return DIRS == 1 || s < so || (s == so && !rev);
-  };
-
-  // bidirectional: readout of the previous step (second visits) and the
-  // other direction's partial for it
-  f32x4 Oprev[UPW], part[UPW];
-#pragma unroll
-  for (int j = 0; j < UPW; ++j) Oprev[j] = part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto step = [&](F& st, F& nx, const int s, const int cn) {
     const int c = chunk_at(s);
-    const bool first = first_visit(s);
     const int buf = s & 1;
-    const unsigned char* sg = stg[dg][buf];
+    const unsigned char* sg = stg[buf];
     float4 sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = *reinterpret_cast<const float4*>(sg + SM::ST_SC + (o_row0 + i) * 16);
@@ -442,7 +448,8 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
         for (int ks = 0; ks < DK / 32; ++ks) {
           const frag sb = M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4);
           y = M::mma(st.kf[ks], sb, y);
-          z = M::mma(sb, st.qf[ks], z);  // Z^T: lane (l16, g4) holds Z[token 16 rt + l16][16 ct + 4 g4 + i]
+          // Z in the readout's layout (transposed for plain stores)
+          z = ACC ? M::mma(st.qf[ks], sb, z) : M::mma(sb, st.qf[ks], z);
         }
         // raw values v[o_row0 + i][16 ct + l16], i = 0..3
         f32x4 vv;
@@ -492,51 +499,47 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
     }
     __syncthreads();
 
-    // [C] chunk readout (transposed: lane (l16, g4) of a unit holds
-    // O[token 16 rt + l16][16 ct + 4 g4 + i], four consecutive values of one
-    // output row, stored as one 16-byte piece); state update
+    // [C] chunk readout O = (e^g rq) Z + P Vnew; state update
     load_tri(nx, cn);
     const float gn = *reinterpret_cast<const float*>(sg + SM::ST_GN);
-    const float scz = *reinterpret_cast<const float*>(sg + SM::ST_SC + tok * 16 + 8);
     frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
     if constexpr (SPLIT) {
-      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + tok * 4));
+      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + kq_row * 4));
 #pragma unroll
       for (int e = 0; e < 8; ++e) pdiag[e] = r;
     }
-    f32x4 O[UPW];
-#pragma unroll
-    for (int j = 0; j < UPW; ++j) {
-      const int u = w + 4 * j;
-      if (ALL_UNITS || u < RT * NT) {
-        const int ct = u / RT;
-        f32x4 acc = Z[j] * scz;
-#pragma unroll
-        for (int kc = 0; kc < C / 32; ++kc) {
-          const frag pf = pmask[kc].apply(st.pf[kc]);
-          const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
-          const frag vh = M::load(VnT + o);
-          acc = M::mma(vh, pf, acc);
-          if constexpr (SPLIT) {
-            acc = M::mma(M::load(VnL + o), pf, acc);
-            // self-term remainder (pqk holds the rounded self term): an
-            // exact-enough diagonal product with the hi part of Vnew
-            acc = M::mma(vh, diag_only[kc].apply(pdiag), acc);
-          }
-        }
-        O[j] = acc;
-      }
-    }
-    // store: a first visit stores its own readout; a bidirectional second
-    // visit stores the previous step's readout plus the partial loaded for it
     {
-      const bool pend = DIRS == 2 && s > 0 && !first_visit(s - 1);
-      const bool on = first || pend;
-      const rsrc_t ro = rs_out(first ? c : chunk_at(max(s - 1, 0)), on);
+      const float scz = *reinterpret_cast<const float*>(sg + SM::ST_SC + kq_row * 16 + 8);
+      const rsrc_t ro = rs_out(c);
 #pragma unroll
       for (int j = 0; j < UPW; ++j) {
         const int u = w + 4 * j;
-        if (ALL_UNITS || u < RT * NT) bstore16(ro, ot_off + (u / RT) * 64, first ? O[j] : Oprev[j] + part[j]);
+        if (ALL_UNITS || u < RT * NT) {
+          const int ct = u / RT;
+          f32x4 acc;
+          if constexpr (ACC) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = sc[i].z * Z[j][i];
+          } else {
+            acc = Z[j] * scz;
+          }
+#pragma unroll
+          for (int kc = 0; kc < C / 32; ++kc) {
+            const frag pf = pmask[kc].apply(st.pf[kc]);
+            const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
+            const frag vh = M::load(VnT + o);
+            acc = ACC ? M::mma(pf, vh, acc) : M::mma(vh, pf, acc);
+            if constexpr (SPLIT) {
+              const frag vl = M::load(VnL + o);
+              acc = ACC ? M::mma(pf, vl, acc) : M::mma(vl, pf, acc);
+              // self-term remainder (pqk holds the rounded self term): a
+              // diagonal product with the hi part of Vnew
+              const frag pd = diag_only[kc].apply(pdiag);
+              acc = ACC ? M::mma(pd, vh, acc) : M::mma(vh, pd, acc);
+            }
+          }
+          put_out<ACC>(ro, out_off + ct * 64, HOB, acc);
+        }
       }
     }
     // state update S^T = gn S^T + K^T Vs.  Wave w owns the state tiles
@@ -586,21 +589,6 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
     }
     stash(nx, buf ^ 1);  // next step's group-shared operands (its slot was last read one step ago)
     __syncthreads();
-
-    // [D] bidirectional second visit: the first visitor stored this chunk's
-    // partial at a step no later than this one, before the barrier above;
-    // load it now, add it next step
-    if (DIRS == 2) {
-      const rsrc_t rp = rs_out(c, !first);
-#pragma unroll
-      for (int j = 0; j < UPW; ++j) {
-        const int u = w + 4 * j;
-        if (ALL_UNITS || u < RT * NT) {
-          part[j] = bload16(rp, ot_off + (u / RT) * 64);
-          Oprev[j] = O[j];
-        }
-      }
-    }
   };
 
   // two operand stages in ping-pong: the loads for step s+1 are in flight
@@ -620,16 +608,6 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
       step(sB, sA, s + 1, chunk_at(min(s + 2, NC - 1)));
     }
     if (s < NC) step(sA, sB, s, chunk_at(s));
-    if (DIRS == 2) {  // the last second visit's readout
-      const rsrc_t ro = rs_out(chunk_at(NC - 1), !first_visit(NC - 1));
-#pragma unroll
-      for (int j = 0; j < UPW; ++j) {
-        const int u = w + 4 * j;
-        if (ALL_UNITS || u < RT * NT) bstore16(ro, ot_off + (u / RT) * 64, Oprev[j] + part[j]);
-      }
-    }
-  } else {
-    __syncthreads();
   }
 
   // ---- final state ----
@@ -644,25 +622,25 @@ __global__ __launch_bounds__(256 * DIRS) void chain_kernel(ScanArgs a, int rev_s
   }
 }
 
-template <typename MT, int DK, int C, int NT, int DIRS>
+template <typename MT, int DK, int C, int NT, bool ACC>
 hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream) {
   const int ntiles = a.dv / (16 * NT);
   const int nbh = (int)(a.B * a.H);
   const int groups = (nbh + 7) / 8;
-  const unsigned nblocks = (unsigned)(groups * 8 * ntiles);
-  hipLaunchKernelGGL((chain_kernel<MT, DK, C, NT, DIRS>), dim3(nblocks), dim3(256 * DIRS), 0, stream, a,
-                     rev_single, ntiles, nbh);
+  const unsigned nblocks = (unsigned)(groups * 8 * ntiles * (ACC ? 2 : 1));
+  hipLaunchKernelGGL((chain_kernel<MT, DK, C, NT, ACC>), dim3(nblocks), dim3(256), 0, stream, a, rev_single,
+                     ntiles, nbh);
   return hipGetLastError();
 }
 
-#define GDN_INST_CHAIN(MT, DK, C, NT, DIRS) \
-  template hipError_t launch_chain<MT, DK, C, NT, DIRS>(const ScanArgs&, int, hipStream_t);
-#define GDN_INST_CHAIN_D(MT, DK, C, NT) GDN_INST_CHAIN(MT, DK, C, NT, 1) GDN_INST_CHAIN(MT, DK, C, NT, 2)
+#define GDN_INST_CHAIN(MT, DK, C, NT, ACC) \
+  template hipError_t launch_chain<MT, DK, C, NT, ACC>(const ScanArgs&, int, hipStream_t);
+#define GDN_INST_CHAIN_D(MT, DK, C, NT) GDN_INST_CHAIN(MT, DK, C, NT, false) GDN_INST_CHAIN(MT, DK, C, NT, true)
 #define GDN_INST_CHAIN_N(MT, DK, C) GDN_INST_CHAIN_D(MT, DK, C, 1) GDN_INST_CHAIN_D(MT, DK, C, 2)
 GDN_INST_CHAIN_N(float, 64, 32)
 GDN_INST_CHAIN_N(float, 64, 64)
 GDN_INST_CHAIN_N(float, 128, 32)
-GDN_INST_CHAIN_D(float, 128, 64, 1)  // fp32, dk 128, 32-wide tiles: exceeds LDS
+GDN_INST_CHAIN_N(float, 128, 64)
 GDN_INST_CHAIN_N(bf16, 64, 32)
 GDN_INST_CHAIN_N(bf16, 64, 64)
 GDN_INST_CHAIN_N(bf16, 128, 32)

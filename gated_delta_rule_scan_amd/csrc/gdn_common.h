@@ -161,6 +161,7 @@ struct ScanArgs {
   int dv;
   int fwd_on, rev_on;  // which directions are computed
   int dirs;            // number of computed directions (slots)
+  int zero_out;        // the preparation kernel zeroes `out` (bidirectional: both directions add into it)
 };
 
 }  // namespace gdn

@@ -8,14 +8,16 @@
 namespace gdn {
 
 // State-independent chunk quantities (triangular inverses, decayed q.k,
-// per-token scales).  Grid: (NC, B*H).
+// per-token scales); zeroes the output rows of its chunk when a.zero_out is
+// set (bidirectional scans accumulate into it).  Grid: (NC, B*H).
 template <typename MT, int DK, int C>
 hipError_t launch_prep(const ScanArgs& a, hipStream_t stream);
 
 // Sequential inter-chunk state chain with the chunk outputs fused in.
-// NT: 16-column value tiles per workgroup; DIRS: direction groups per
-// workgroup (2 = forward and reverse of the same tile together).
-template <typename MT, int DK, int C, int NT, int DIRS>
+// NT: 16-column value tiles per workgroup; ACC: bidirectional (one workgroup
+// per direction, readouts added into the output that the preparation kernel
+// zeroed) instead of one direction (`rev_single` tells which) stored directly.
+template <typename MT, int DK, int C, int NT, bool ACC>
 hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream);
 
 }  // namespace gdn

@@ -80,6 +80,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   const int fslot = 0, rslot = fwd_on ? 1 : 0;
   const size_t nch = (size_t)a.B * a.H * a.NC;
 
+  // ---- bidirectional scans accumulate both readouts into `out`: zero this
+  // chunk's rows of it first (the state chain runs after this kernel) ----
+  if (a.zero_out) {
+    const int dv4 = a.dv / 4;
+    for (int p = tid; p < C * dv4; p += 256) {
+      const int row = p / dv4, cp = (p % dv4) * 4;
+      const int64_t t = t0 + row;
+      if (t < T) *reinterpret_cast<f32x4*>(a.out + ((b * T + t) * H + h) * a.dv + cp) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
   // ---- stage raw q and k of this chunk into LDS (padded rows are zero) ----
   {
     const MT* q = static_cast<const MT*>(a.q);

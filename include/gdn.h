@@ -49,7 +49,10 @@
  * and completes asynchronously.  state_in == state_out is allowed (in-place
  * streaming carry); any other overlap between `out`, the state buffers, the
  * workspace and the inputs is rejected.  Results are bitwise deterministic for
- * fixed inputs, chunk size and device (no atomics in any reduction).
+ * fixed inputs and chunk size: the only atomics are the two fp32 adds that
+ * sum the forward and reverse readouts of a bidirectional scan into the
+ * zeroed output, and two addends onto zero give the same sum in either
+ * order.  The value-tile width changes the schedule, never the arithmetic.
  *
  * Errors: argument problems are reported before anything is enqueued and
  * leave every output untouched.  GDN_ERR_HIP reports a failed launch; faults
@@ -86,9 +89,9 @@ typedef enum {
 } gdn_dtype_t;
 
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
- * chunk in {0 (= 64), 32, 64}; dv_tile in {0 (= automatic), 16, 32}
- * (must divide dv; fp32 inputs with dk = 128 and 64-token chunks take 16
- * only); B, H >= 1, B*H <= 65535; 0 <= T <= 2^30. */
+ * chunk in {0 (= 64), 32, 64}; dv_tile in {0, 16, 32} (0: 32 when 16-wide
+ * state-chain workgroups would outnumber the compute units of the current
+ * device, else 16); B, H >= 1, B*H <= 65535; 0 <= T <= 2^30. */
 typedef struct {
   int64_t B, T, H, dk, dv;
   int32_t dtype;            /* gdn_dtype_t: type of q, k, v */

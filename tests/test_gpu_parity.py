@@ -52,3 +52,19 @@ def test_head_dims_bf16(d, direction):
 @pytest.mark.parametrize("dv_tile", [16, 32])
 def test_chunk_and_tile_fp32(chunk, dv_tile):
     _compare(_case("f32", "bi", T=333, H=2, dk=64, dv=64, state_std=0.1, seed=7), chunk=chunk, dv_tile=dv_tile)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bi"])
+def test_wide_tile_fp32_d128(direction):
+    """fp32 operands, d = 128, 64-token chunks and 32-wide value tiles."""
+    _compare(_case("f32", direction, T=260, H=2, dk=128, dv=128, state_std=0.05, seed=8), dv_tile=32)
+
+
+@pytest.mark.parametrize("dv_tile", [16, 32])
+def test_tile_width_does_not_change_results(dv_tile):
+    """The value-tile width changes only the schedule: results are bitwise equal."""
+    w = _case("bf16", "bi", T=300, B=2, H=2, dk=128, dv=128, state_std=0.02, seed=12)
+    x = synth.generate(w)
+    o1, s1 = run_gpu(x, "bi", dv_tile=16)
+    o2, s2 = run_gpu(x, "bi", dv_tile=dv_tile)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
