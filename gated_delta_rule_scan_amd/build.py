@@ -18,9 +18,14 @@ SOURCES = ["gdn_api.hip", "gdn_prep.hip", "gdn_chain.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
+# -amdgpu-mfma-vgpr-form: matrix-core results land in ordinary VGPRs (gfx950
+# has one register file for both), which saves the accumulator-register
+# copies around every product whose result feeds vector code (about 100
+# copies per state-chain step).
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

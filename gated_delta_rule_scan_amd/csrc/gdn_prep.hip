@@ -31,6 +31,8 @@
 // each column of off-diagonal tiles follows from T_IJ = -T_II sum_K L_IK T_KJ
 // on the fp32 matrix cores.  A block column only depends on itself and on
 // the diagonal tiles, so each column is one wave's private chain.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -80,17 +82,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   const int fslot = 0, rslot = fwd_on ? 1 : 0;
   const size_t nch = (size_t)a.B * a.H * a.NC;
 
-  // ---- bidirectional scans accumulate both readouts into `out`: zero this
-  // chunk's rows of it first (the state chain runs after this kernel) ----
-  if (a.zero_out) {
-    const int dv4 = a.dv / 4;
-    for (int p = tid; p < C * dv4; p += 256) {
-      const int row = p / dv4, cp = (p % dv4) * 4;
-      const int64_t t = t0 + row;
-      if (t < T) *reinterpret_cast<f32x4*>(a.out + ((b * T + t) * H + h) * a.dv + cp) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-
   // ---- stage raw q and k of this chunk into LDS (padded rows are zero) ----
   {
     const MT* q = static_cast<const MT*>(a.q);
@@ -130,15 +121,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   // ---- row scales and chunk-local cumulative log-gates ----
   {
     constexpr int G = 256 / C;        // threads per row
-    constexpr int PER = DK / G;       // elements per thread
+    constexpr int PER = DK / G;       // elements per thread (a multiple of 8)
     const int row = tid / G, part = tid % G;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const float xq = to_f32(Qs[row * KP + part * PER + e]);
-      const float xk = to_f32(Ks[row * KP + part * PER + e]);
-      sq = fmaf(xq, xq, sq);
-      sk = fmaf(xk, xk, sk);
+    for (int e8 = 0; e8 < PER; e8 += 8) {  // 8 elements per fragment-sized read
+      const typename M::frag fq = M::load(Qs + row * KP + part * PER + e8);
+      const typename M::frag fk = M::load(Ks + row * KP + part * PER + e8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xq = M::get(fq, e), xk = M::get(fk, e);
+        sq = fmaf(xq, xq, sq);
+        sk = fmaf(xk, xk, sk);
+      }
     }
 #pragma unroll
     for (int m = 1; m < G; m <<= 1) {
@@ -151,19 +146,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     }
   }
   // chunk-local cumulative log-gates, kept in log2 units so every decay
-  // factor below is one exp2 of a difference
+  // factor below is one exp2 of a difference: wave 0 forms the inclusive
+  // prefix sums in token order, wave 1 the inclusive suffix sums (the reverse
+  // visiting order), each as a wave-wide scan
   constexpr float kLog2e = 1.4426950408889634f;
-  if (tid < C) {
-    if (fwd_on) {  // inclusive prefix sum in token order
-      float s = 0.f;
-      for (int j = 0; j <= tid; ++j) s += s_la[0][j];
-      s_g[0][tid] = s * kLog2e;
+  if (wave < 2 && (wave == 0 ? fwd_on : rev_on)) {
+    const int dir = wave;
+    const int tok = dir == 0 ? lane : C - 1 - lane;  // position in visiting order = lane
+    float s = lane < C ? s_la[dir][tok] : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(s, d, 64);
+      if (lane >= d) s += o;
     }
-    if (rev_on) {  // inclusive suffix sum, accumulated in reverse visiting order
-      float s = 0.f;
-      for (int j = C - 1; j >= tid; --j) s += s_la[1][j];
-      s_g[1][tid] = s * kLog2e;
-    }
+    if (lane < C) s_g[dir][tok] = s * kLog2e;
   }
   __syncthreads();
 
@@ -235,28 +231,31 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     const int blk = (tid / 16) % NB;
     const int jc = tid % 16;
     const int b0 = 16 * blk;
-    if (dir == 0 && fwd_on) {
-      float x[16];
+    // column jc of (I + L_bb)^{-1} by forward substitution in visiting
+    // order, column-oriented: once x_i is known it is folded into every
+    // later row's running sum, so the dependent chain is 16 steps long.
+    // One instance per direction keeps every index a compile-time constant
+    // (the running sums stay in registers).
+    auto solve = [&](auto rev_tag) {
+      constexpr bool R = decltype(rev_tag)::value;
+      float acc[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = 0.f;
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) s = fmaf(Lm[(b0 + r) * LP + b0 + i], x[i], s);
-        x[r] = (r < jc) ? 0.f : ((r == jc) ? 1.f : -s);
-        if (r >= jc) Ti[(b0 + r) * LP + b0 + jc] = x[r];
+      for (int ii = 0; ii < 16; ++ii) {
+        const int i = R ? 15 - ii : ii;  // visiting order
+        const bool after = R ? (i < jc) : (i > jc);
+        const float x = i == jc ? 1.f : (after ? -acc[i] : 0.f);
+        if (i == jc || after) Ti[(b0 + i) * LP + b0 + jc] = x;
+#pragma unroll
+        for (int rr = ii + 1; rr < 16; ++rr) {
+          const int r = R ? 15 - rr : rr;
+          acc[r] = fmaf(Lm[(b0 + r) * LP + b0 + i], x, acc[r]);
+        }
       }
-    } else if (dir == 1 && rev_on) {
-      float x[16];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int r = 15 - rr;
-        float s = 0.f;
-#pragma unroll
-        for (int i = r + 1; i < 16; ++i) s = fmaf(Lm[(b0 + r) * LP + b0 + i], x[i], s);
-        x[r] = (r > jc) ? 0.f : ((r == jc) ? 1.f : -s);
-        if (r <= jc) Ti[(b0 + r) * LP + b0 + jc] = x[r];
-      }
-    }
+    };
+    if (dir == 0 && fwd_on) solve(std::false_type{});
+    if (dir == 1 && rev_on) solve(std::true_type{});
   }
   __syncthreads();
 
@@ -352,6 +351,18 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       float4 v = in ? make_float4(s_bt[1][tid], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
       a.sc[(rslot * nch + cid) * C + tid] = v;
       if (tid < 4) a.pdg[((size_t)rslot * nch + cid) * (C + 4) + C + tid] = tid == 0 ? exp2f(gl) : 0.f;
+    }
+  }
+
+  // ---- bidirectional scans accumulate both readouts into `out` (the state
+  // chain runs after this kernel): zero this chunk's rows of it.  Last, so
+  // these stores never queue ahead of the loads above. ----
+  if (a.zero_out) {
+    const int dv4 = a.dv / 4;
+    for (int p = tid; p < C * dv4; p += 256) {
+      const int row = p / dv4, cp = (p % dv4) * 4;
+      const int64_t t = t0 + row;
+      if (t < T) *reinterpret_cast<f32x4*>(a.out + ((b * T + t) * H + h) * a.dv + cp) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
