@@ -20,10 +20,19 @@
 // two directions in separate workgroups, which the hardware overlaps freely
 // (two direction groups on one workgroup barrier would make every wave wait
 // for the slowest of both at every phase, and per-group LDS barriers are
-// slow under the groups' LDS traffic).  Both add their readouts into the
-// output with fp32 atomic adds; the preparation kernel zeroes it first, and
-// two addends onto zero give the same sum in either order, so the result is
-// deterministic and no workgroup ever waits for another.
+// slow under the groups' LDS traffic).  Every chunk is visited by both: the
+// forward workgroup visits chunk s at its step s, the reverse one at its step
+// NC-1-s.  The first visitor (the forward one for the first half of the
+// chunks, the reverse one for the second half) stores its readout; the
+// second loads that partial a step ahead, adds its own readout and stores the
+// sum.  The preparation kernel fills `out` with an all-ones NaN pattern that
+// no readout produces, so the second visitor knows when the partial has
+// arrived: while any of its elements still holds the pattern, it re-reads
+// them past its L1 cache (rare: only near the middle of the sequence do the
+// two visits come close in time).  The first visits of a workgroup come
+// before all of its second visits, so a first visitor never waits; partner
+// workgroups have nearby ids, and with in-order dispatch every waiting
+// workgroup's partner runs, so every wait ends (the polls are bounded too).
 
 // Every global access goes through a raw buffer resource whose extent is the
 // valid part of the chunk: reads past it return zero and writes past it are
@@ -87,12 +96,14 @@ struct ChainSmem {
   static constexpr int TP = C + EP;   // pitch of token-contiguous rows
   static constexpr int SP = DK + EP;  // pitch of the state copy
   static constexpr int DT = 16 * NT;
-  // k tile of the chunk.  bf16: row-major [C][DK + 16] (the transposed
-  // operand of the state update is read with transposing LDS reads; the
-  // pitch puts the four rows of one such read in distinct bank quarters).
+  // k tile of the chunk.  bf16: row-major [C][DK + 8] (the transposed
+  // operand of the state update is read with transposing LDS reads).  The
+  // pitch is 68 dwords: the 16-byte row stores are then free of bank
+  // conflicts on gfx950 (a 72-dword pitch doubles their cost; measured), and
+  // the transposing reads cost the same at either pitch.
   // fp32: token-contiguous [DK][TP].
   static constexpr bool KROW = ES == 2;
-  static constexpr int KP = DK + 16;
+  static constexpr int KP = DK + 8;
   static constexpr int k_elems = KROW ? C * KP : DK * TP;
   // bf16 operands: Vnew and the scaled update vectors are carried as hi + lo
   // bf16 pairs (two products each), so their rounding stays at fp32 level.
@@ -207,26 +218,38 @@ __device__ __forceinline__ void store_split4(bf16* hi_p, bf16* lo_p, f32x4 x) {
 }
 
 
-// Readout of one chunk tile into `out`.  ACC = false: plain 16-byte stores of
-// the transposed tile (lane (l16, g4) holds out[token 16 rt + l16][16 ct +
-// 4 g4 + i]).  ACC = true (bidirectional scans, where the forward and the
-// reverse workgroup each add their readout into the zeroed output): fp32
-// atomic adds of the row-layout tile (lane (l16, g4) holds out[token
-// 16 rt + 4 g4 + i][16 ct + l16]), so each instruction covers whole 64-byte
-// row segments.  Two addends onto zero give the same sum in either order.
-template <bool ACC>
-__device__ __forceinline__ void put_out(rsrc_t r, uint32_t off, uint32_t row_pitch, f32x4 o) {
-  if constexpr (ACC) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(o[i], r, (int)(off + i * row_pitch), 0, 0);
-  } else {
-    bstore16(r, off, o);
-  }
+// All-ones NaN: the value the preparation kernel fills `out` with before a
+// bidirectional scan, meaning "not written yet".  Arithmetic never produces
+// it (generated NaNs are the canonical quiet NaN).
+constexpr uint32_t kUnwritten = 0xFFFFFFFFu;
+
+__device__ __forceinline__ bool any_unwritten(f32x4 p) {
+  return __float_as_uint(p[0]) == kUnwritten || __float_as_uint(p[1]) == kUnwritten ||
+         __float_as_uint(p[2]) == kUnwritten || __float_as_uint(p[3]) == kUnwritten;
 }
 
-template <typename MT, int DK, int C, int NT, bool ACC>
-__global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
+// 16-byte load that misses the L1 cache (system-scope cache policy), for
+// re-reading data another compute unit writes.
+__device__ __forceinline__ f32x4 bload16_fresh(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 17);
+  f32x4 f;
+  __builtin_memcpy(&f, &v, 16);
+  return f;
+}
+
+constexpr int kPollLimit = 1 << 20;
+
+// Waves per state-chain workgroup.  Four: one per SIMD.  (Eight waves with
+// one output tile each measured 1.4x slower on MI355X: every wave then reads
+// the whole update operand from LDS, and LDS is what a step waits on.)
+template <int C, int NT>
+struct ChainWaves {
+  static constexpr int value = 4;
+};
+
+template <typename MT, int DK, int C, int NT, bool BI>
+__global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(ScanArgs a, int rev_single, int ntiles,
+                                                                              int nbh) {
   using M = Mma<MT>;
   using frag = typename M::frag;
   using SM = ChainSmem<MT, DK, C, NT>;
@@ -235,35 +258,39 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
   constexpr int TP = SM::TP, SP = SM::SP, DT = SM::DT;
   using VT = VTile<MT, DT, C>;
   constexpr int RT = C / 16;              // token row tiles per chunk
-  constexpr int UPW = (RT * NT + 3) / 4;  // chunk-output tiles per wave
-  constexpr int SRT = DK / 16;            // state row tiles (dk)
-  constexpr int SUPW = SRT * NT / 4;      // state tiles per wave
+  constexpr int NW = ChainWaves<C, NT>::value;  // waves per workgroup
+  constexpr int UPW = (RT * NT + NW - 1) / NW;  // chunk-output tiles per wave
+  constexpr int SRT = DK / 16;                  // state row tiles (dk)
+  constexpr int SUPW = SRT * NT / NW;           // state tiles per wave
   constexpr bool SPLIT = SM::SPLIT;
-  constexpr bool ALL_UNITS = (RT * NT) % 4 == 0;
-  static_assert(SRT % 4 == 0, "each wave owns whole dk-tile columns of the state");
+  constexpr bool ALL_UNITS = (RT * NT) % NW == 0;
+  static_assert(SRT % NW == 0 || NW % SRT == 0, "state tiles split evenly over the waves");
+  static_assert(NW % RT == 0, "every wave keeps one token row tile");
 
   __shared__ __align__(16) MT smem[SM::per_group];
   __shared__ __align__(16) unsigned char stg[2][SM::ST_BYTES];
 
-  // XCD-aware numbering: workgroup id -> (chain, direction, value tile); all
-  // workgroups of one (batch, head) land on the same XCD
-  const int ndir = ACC ? 2 : 1;
+  // XCD-aware numbering: workgroup id -> (chain, value tile, direction); all
+  // workgroups of one (batch, head) land on the same XCD, and the two
+  // directions of a tile have ids 8 apart
+  const int ndir = BI ? 2 : 1;
   const int id = blockIdx.x;
   const int xcd = id & 7, kk = id >> 3;
   const int chain = (kk / (ntiles * ndir)) * 8 + xcd;
-  const int dslot = (kk % (ntiles * ndir)) / ntiles;
-  const int tile = kk % ntiles;
+  const int dslot = BI ? (kk & 1) : 0;
+  const int tile = (kk / ndir) % ntiles;
   if (chain >= nbh) return;
   const int NC = (int)a.NC;
   const int64_t T = a.T, H = a.H;
   const int64_t b = chain / H, h = chain % H;
   const int dv = a.dv;
   const int dv0 = tile * DT;
-  const bool rev = ACC ? (dslot == 1) : (rev_single != 0);
+  const bool rev = BI ? (dslot == 1) : (rev_single != 0);
   const int slot = dslot;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int cw = w & 3;  // role in the group-shared loads (waves 4-7 repeat 0-3: same data, same place)
   const int l16 = lane & 15, g4 = lane >> 4;
   const int rt = w % RT;
 
@@ -306,9 +333,9 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
     tmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, false, kc == kcd);
     pmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, true, kc == kcd);
   }
-  // readout offsets of unit column tile 0: transposed (token kq_row, four
-  // columns from 4 g4) or row layout (rows o_row0 + i, column l16)
-  const uint32_t out_off = ACC ? o_row0 * HOB + l16 * 4 : kq_row * HOB + 16 * g4;
+  // readout offset of unit column tile 0 (transposed tile: token kq_row, four
+  // columns from 4 g4)
+  const uint32_t out_off = kq_row * HOB + 16 * g4;
   // bf16 operands: the self term's remainder enters as a diagonal fragment;
   // in k-chunk kc this lane (row kq_row of P) holds element `kq_row - 32 kc -
   // 8 g4` of it when that lies in 0..7 (only ever in the k-chunk of the diagonal)
@@ -335,11 +362,11 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
   size_t cstride;
   uint32_t cbytes;  // extent of a whole chunk (the value tile is bounded per chunk below)
   uint32_t c_off[VT::NVI], c_lds[VT::NVI];
-  if (w == 0) {
+  if (cw == 0) {
     cbase = reinterpret_cast<const char*>(a.sc) + ((size_t)slot * nch + (size_t)chain * NC) * C * 16;
     cstride = (size_t)C * 16;
     cbytes = C * 16;
-  } else if (w == 1) {
+  } else if (cw == 1) {
     cbase = reinterpret_cast<const char*>(a.pdg) + ((size_t)slot * nch + (size_t)chain * NC) * (C + 4) * 4;
     cstride = (size_t)(C + 4) * 4;
     cbytes = (C + 4) * 4;
@@ -350,16 +377,16 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
   }
 #pragma unroll
   for (int n = 0; n < VT::NVI; ++n) {
-    if (w == 0) {
+    if (cw == 0) {
       const int idx = lane % C;
       c_off[n] = idx * 16;
       c_lds[n] = SM::ST_SC + idx * 16;
-    } else if (w == 1) {
+    } else if (cw == 1) {
       const int idx = min(lane, C / 4);
       c_off[n] = idx * 16;
       c_lds[n] = SM::ST_PD + idx * 16;
     } else {
-      const int idx = min((w - 2) * 64 + n * 128 + lane, C * VT::LPR - 1);
+      const int idx = min((cw - 2) * 64 + n * 128 + lane, C * VT::LPR - 1);
       const int row = idx / VT::LPR, part = idx % VT::LPR;
       c_off[n] = row * HVB + part * 16;
       c_lds[n] = SM::ST_V + idx * 16;
@@ -372,7 +399,7 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
   };
   auto rs_tri = [&](const char* base, int c) { return make_rsrc(base + (size_t)c * C * C * ES, C * C * ES); };
   auto rs_coop = [&](int c) {
-    return make_rsrc(cbase + (size_t)c * cstride, w >= 2 ? extent(c, HVB, DT * ES) : cbytes);
+    return make_rsrc(cbase + (size_t)c * cstride, cw >= 2 ? extent(c, HVB, DT * ES) : cbytes);
   };
   auto rs_out = [&](int c) { return make_rsrc(obase + (size_t)c * C * HOB, extent(c, HOB, DT * 4)); };
 
@@ -405,7 +432,7 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
   const size_t sbase = (((size_t)slot * a.B + b) * a.H + h) * (size_t)dv * DK;
 #pragma unroll
   for (int j = 0; j < SUPW; ++j) {
-    const int u = w + 4 * j;
+    const int u = w + NW * j;
     const int srt = u % SRT, sct = u / SRT;
     const size_t off = sbase + (size_t)(dv0 + 16 * sct + l16) * DK + 16 * srt + 4 * g4;
     Sacc[j] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + off) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -413,6 +440,61 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
   }
 
   auto chunk_at = [&](int s) { return rev ? NC - 1 - s : s; };
+  // bidirectional: whether this workgroup visits chunk_at(s) before the other
+  // direction does (see the file comment)
+  auto first_visit = [&](int s) {
+    const int so = NC - 1 - s;  // step at which the other direction visits the same chunk
+    return !BI || s < so || (s == so && !rev);
+  };
+
+  // Readout of step sp (chunk chunk_at(sp)): O = (e^g rq) Z + P Vnew.  It is
+  // software-pipelined one phase late: computed at the start of the next
+  // step, where its products and stores overlap that step's state products.
+  // Everything it reads is still intact there: Z (registers), the P fragments
+  // (the stage the next step's triangle loads overwrite only in its last
+  // phase), Vnew (LDS until the next step's second phase) and the staged
+  // scales (until the next step's last phase).  `on` = false: nothing is stored.
+  // Second visits of a bidirectional scan add the partial `part` the other
+  // direction stored, loaded and checked during the visit step.
+  f32x4 Zp[UPW], part[UPW], pnext[UPW];  // pnext: the partial of the step being computed
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) Zp[j] = part[j] = pnext[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto readout = [&](const F& sp, const int s_prev, const bool on) {
+    const unsigned char* sg = stg[s_prev & 1];
+    frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
+    if constexpr (SPLIT) {
+      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + kq_row * 4));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pdiag[e] = r;
+    }
+    const int c = chunk_at(s_prev);
+    const rsrc_t ro = make_rsrc(obase + (size_t)c * C * HOB, on ? extent(c, HOB, DT * 4) : 0u);
+    const float zs = *reinterpret_cast<const float*>(sg + SM::ST_SC + kq_row * 16 + 8);  // e^g rq of the token
+    const bool add = BI && !first_visit(s_prev);
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+      const int u = w + NW * j;
+      if (ALL_UNITS || u < RT * NT) {
+        const int ct = u / RT;
+        f32x4 acc = Zp[j] * zs;
+#pragma unroll
+        for (int kc = 0; kc < C / 32; ++kc) {
+          const frag pf = pmask[kc].apply(sp.pf[kc]);
+          const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
+          const frag vh = M::load(VnT + o);
+          acc = M::mma(vh, pf, acc);
+          if constexpr (SPLIT) {
+            acc = M::mma(M::load(VnL + o), pf, acc);
+            // self-term remainder (pqk holds the rounded self term): a
+            // diagonal product with the hi part of Vnew
+            acc = M::mma(vh, diag_only[kc].apply(pdiag), acc);
+          }
+        }
+        if (add) acc += part[j];
+        bstore16(ro, out_off + ct * 64, acc);
+      }
+    }
+  };
 
   auto step = [&](F& st, F& nx, const int s, const int cn) {
     const int c = chunk_at(s);
@@ -437,10 +519,21 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
     }
     load_coop(nx, cn);
     load_rows(nx.kf, kbase, cn);
-    f32x4 X[UPW], Z[UPW], Vn[UPW];
+    // bidirectional second visit of the next step's chunk: the other
+    // direction's partial, loaded a step ahead, checked at the end of the next
+    // step and consumed by its readout
+    f32x4 pq[UPW];
+    if constexpr (BI) {
+      const bool want = s + 1 < NC && !first_visit(s + 1);
+      const rsrc_t rp = make_rsrc(obase + (size_t)cn * C * HOB, want ? extent(cn, HOB, DT * 4) : 0u);
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) pq[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
+    }
+    readout(nx, s - 1, s > 0);  // the previous step's chunk (nx still holds its stage)
+    f32x4 X[UPW], Vn[UPW];
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
-      const int u = w + 4 * j;
+      const int u = w + NW * j;
       if (ALL_UNITS || u < RT * NT) {
         const int ct = u / RT;
         f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
@@ -448,8 +541,7 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
         for (int ks = 0; ks < DK / 32; ++ks) {
           const frag sb = M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4);
           y = M::mma(st.kf[ks], sb, y);
-          // Z in the readout's layout (transposed for plain stores)
-          z = ACC ? M::mma(st.qf[ks], sb, z) : M::mma(sb, st.qf[ks], z);
+          z = M::mma(sb, st.qf[ks], z);  // Z^T: lane (l16, g4) holds Z[token 16 rt + l16][16 ct + 4 g4 + i]
         }
         // raw values v[o_row0 + i][16 ct + l16], i = 0..3
         f32x4 vv;
@@ -466,7 +558,7 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[j][i] = sc[i].x * (vv[i] - sc[i].y * y[i]);
-        Z[j] = z;
+        Zp[j] = z;
         M::store4(XT + (16 * ct + l16) * TP + o_row0, X[j][0], X[j][1], X[j][2], X[j][3]);
       }
     }
@@ -476,7 +568,7 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
     load_rows(nx.qf, qbase, cn);
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
-      const int u = w + 4 * j;
+      const int u = w + NW * j;
       if (ALL_UNITS || u < RT * NT) {
         const int ct = u / RT;
         f32x4 acc = X[j];
@@ -499,61 +591,25 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
     }
     __syncthreads();
 
-    // [C] chunk readout O = (e^g rq) Z + P Vnew; state update
+    // [C] state update (the readout of this chunk follows in the next step)
     load_tri(nx, cn);
     const float gn = *reinterpret_cast<const float*>(sg + SM::ST_GN);
-    frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
-    if constexpr (SPLIT) {
-      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + kq_row * 4));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pdiag[e] = r;
-    }
-    {
-      const float scz = *reinterpret_cast<const float*>(sg + SM::ST_SC + kq_row * 16 + 8);
-      const rsrc_t ro = rs_out(c);
-#pragma unroll
-      for (int j = 0; j < UPW; ++j) {
-        const int u = w + 4 * j;
-        if (ALL_UNITS || u < RT * NT) {
-          const int ct = u / RT;
-          f32x4 acc;
-          if constexpr (ACC) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = sc[i].z * Z[j][i];
-          } else {
-            acc = Z[j] * scz;
-          }
-#pragma unroll
-          for (int kc = 0; kc < C / 32; ++kc) {
-            const frag pf = pmask[kc].apply(st.pf[kc]);
-            const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
-            const frag vh = M::load(VnT + o);
-            acc = ACC ? M::mma(pf, vh, acc) : M::mma(vh, pf, acc);
-            if constexpr (SPLIT) {
-              const frag vl = M::load(VnL + o);
-              acc = ACC ? M::mma(pf, vl, acc) : M::mma(vl, pf, acc);
-              // self-term remainder (pqk holds the rounded self term): a
-              // diagonal product with the hi part of Vnew
-              const frag pd = diag_only[kc].apply(pdiag);
-              acc = ACC ? M::mma(pd, vh, acc) : M::mma(vh, pd, acc);
-            }
-          }
-          put_out<ACC>(ro, out_off + ct * 64, HOB, acc);
-        }
-      }
-    }
     // state update S^T = gn S^T + K^T Vs.  Wave w owns the state tiles
-    // (dk tile w + 4 js, dv tile jt); every operand fragment is read once
-    // (the products only start after all reads, so no LDS store in between
-    // forces a re-read), then the operand copy for the next step is written.
+    // u = w + NW j, i.e. dk tiles srt(js) and dv tiles sct(jt) below; every
+    // operand fragment is read once (the products only start after all
+    // reads, so no LDS store in between forces a re-read), then the operand
+    // copy for the next step is written.
     {
-      constexpr int JS = SRT / 4;  // dk tiles per wave
-      frag ka[JS][C / 32], vh[NT][C / 32], vl[NT][C / 32];
+      constexpr int JS = SRT >= NW ? SRT / NW : 1;  // dk tiles per wave
+      constexpr int JT = SUPW / JS;                 // dv tiles per wave
+      auto srt_of = [&](int js) { return (w % SRT) + NW * js; };
+      auto sct_of = [&](int jt) { return SRT >= NW ? jt : w / SRT + (NW / SRT) * jt; };
+      frag ka[JS][C / 32], vh[JT][C / 32], vl[JT][C / 32];
 #pragma unroll
       for (int js = 0; js < JS; ++js)
 #pragma unroll
         for (int kc = 0; kc < C / 32; ++kc) {
-          const int srt = w + 4 * js;
+          const int srt = srt_of(js);
           if constexpr (KROW) {
             ka[js][kc] = load_kt_frag(KT, KP, 32 * kc, 16 * srt, l16, g4);
           } else {
@@ -561,18 +617,18 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
           }
         }
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt)
+      for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
         for (int kc = 0; kc < C / 32; ++kc) {
-          const int o = (16 * jt + l16) * TP + 32 * kc + 8 * g4;
+          const int o = (16 * sct_of(jt) + l16) * TP + 32 * kc + 8 * g4;
           vh[jt][kc] = M::load(VsT + o);
           if (SPLIT) vl[jt][kc] = M::load(VsL + o);
         }
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt)
+      for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
         for (int js = 0; js < JS; ++js) {
-          const int j = jt * JS + js;  // = (w + 4 j) / SRT and % SRT as in the state load and store
+          const int j = jt * JS + js;  // tile u = w + NW j: srt = u % SRT = srt_of(js), sct = u / SRT = sct_of(jt)
           f32x4 acc = Sacc[j] * gn;
 #pragma unroll
           for (int kc = 0; kc < C / 32; ++kc) {
@@ -583,8 +639,36 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
         }
 #pragma unroll
       for (int j = 0; j < SUPW; ++j) {
-        const int srt = w + 4 * (j % JS), sct = j / JS;
+        const int srt = srt_of(j % JS), sct = sct_of(j / JS);
         M::store4(Sb + (16 * sct + l16) * SP + 16 * srt + 4 * g4, Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
+      }
+    }
+    // bidirectional second visit: this step's partial was loaded a step ago;
+    // while any of it still holds the fill pattern, the other direction has
+    // not stored it yet -- re-read it past the L1 cache
+    if constexpr (BI) {
+      if (!first_visit(s)) {
+        const rsrc_t rp = make_rsrc(obase + (size_t)c * C * HOB, extent(c, HOB, DT * 4));
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+          // first test outside any loop: a loop that reloads the tested value
+          // makes the compiler wait for every load in flight at its head
+          if (__any(any_unwritten(pnext[j]))) {
+            const uint32_t off = out_off + ((w + NW * j) / RT) * 64;
+            f32x4 q = pnext[j];
+            for (int n = 0; n < kPollLimit; ++n) {
+              __builtin_amdgcn_s_sleep(2);
+              q = bload16_fresh(rp, off);
+              if (!__any(any_unwritten(q))) break;
+            }
+            pnext[j] = q;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) {
+        part[j] = pnext[j];
+        pnext[j] = pq[j];
       }
     }
     stash(nx, buf ^ 1);  // next step's group-shared operands (its slot was last read one step ago)
@@ -600,6 +684,11 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
     load_rows(sA.kf, kbase, c0);
     load_rows(sA.qf, qbase, c0);
     load_tri(sA, c0);
+    if constexpr (BI) {  // the partial of step 0 (a single-chunk scan's reverse visit)
+      const rsrc_t rp = make_rsrc(obase + (size_t)c0 * C * HOB, first_visit(0) ? 0u : extent(c0, HOB, DT * 4));
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) pnext[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
+    }
     stash(sA, 0);
     __syncthreads();
     int s = 0;
@@ -608,13 +697,14 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
       step(sB, sA, s + 1, chunk_at(min(s + 2, NC - 1)));
     }
     if (s < NC) step(sA, sB, s, chunk_at(s));
+    readout((NC & 1) ? sA : sB, NC - 1, true);  // the last chunk's readout (its stage is the last one stepped)
   }
 
   // ---- final state ----
   if (a.state_out) {
 #pragma unroll
     for (int j = 0; j < SUPW; ++j) {
-      const int u = w + 4 * j;
+      const int u = w + NW * j;
       const int srt = u % SRT, sct = u / SRT;
       const size_t off = sbase + (size_t)(dv0 + 16 * sct + l16) * DK + 16 * srt + 4 * g4;
       *reinterpret_cast<f32x4*>(a.state_out + off) = Sacc[j];
@@ -622,19 +712,19 @@ __global__ __launch_bounds__(256) void chain_kernel(ScanArgs a, int rev_single, 
   }
 }
 
-template <typename MT, int DK, int C, int NT, bool ACC>
+template <typename MT, int DK, int C, int NT, bool BI>
 hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream) {
   const int ntiles = a.dv / (16 * NT);
   const int nbh = (int)(a.B * a.H);
   const int groups = (nbh + 7) / 8;
-  const unsigned nblocks = (unsigned)(groups * 8 * ntiles * (ACC ? 2 : 1));
-  hipLaunchKernelGGL((chain_kernel<MT, DK, C, NT, ACC>), dim3(nblocks), dim3(256), 0, stream, a, rev_single,
-                     ntiles, nbh);
+  const unsigned nblocks = (unsigned)(groups * 8 * ntiles * (BI ? 2 : 1));
+  hipLaunchKernelGGL((chain_kernel<MT, DK, C, NT, BI>), dim3(nblocks), dim3(64 * ChainWaves<C, NT>::value), 0, stream,
+                     a, rev_single, ntiles, nbh);
   return hipGetLastError();
 }
 
-#define GDN_INST_CHAIN(MT, DK, C, NT, ACC) \
-  template hipError_t launch_chain<MT, DK, C, NT, ACC>(const ScanArgs&, int, hipStream_t);
+#define GDN_INST_CHAIN(MT, DK, C, NT, BI) \
+  template hipError_t launch_chain<MT, DK, C, NT, BI>(const ScanArgs&, int, hipStream_t);
 #define GDN_INST_CHAIN_D(MT, DK, C, NT) GDN_INST_CHAIN(MT, DK, C, NT, false) GDN_INST_CHAIN(MT, DK, C, NT, true)
 #define GDN_INST_CHAIN_N(MT, DK, C) GDN_INST_CHAIN_D(MT, DK, C, 1) GDN_INST_CHAIN_D(MT, DK, C, 2)
 GDN_INST_CHAIN_N(float, 64, 32)

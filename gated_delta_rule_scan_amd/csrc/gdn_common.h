@@ -161,7 +161,7 @@ struct ScanArgs {
   int dv;
   int fwd_on, rev_on;  // which directions are computed
   int dirs;            // number of computed directions (slots)
-  int zero_out;        // the preparation kernel zeroes `out` (bidirectional: both directions add into it)
+  int zero_out;        // the preparation kernel fills `out` with the "not written yet" pattern (bidirectional)
 };
 
 }  // namespace gdn

@@ -354,15 +354,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     }
   }
 
-  // ---- bidirectional scans accumulate both readouts into `out` (the state
-  // chain runs after this kernel): zero this chunk's rows of it.  Last, so
-  // these stores never queue ahead of the loads above. ----
+  // ---- bidirectional scans: the second visitor of a chunk in the state
+  // chain recognises the first visitor's readout by this all-ones NaN fill
+  // ("not written yet"; arithmetic never produces it).  Last, so these stores
+  // never queue ahead of the loads above. ----
   if (a.zero_out) {
     const int dv4 = a.dv / 4;
+    const float fill = __uint_as_float(0xFFFFFFFFu);
     for (int p = tid; p < C * dv4; p += 256) {
       const int row = p / dv4, cp = (p % dv4) * 4;
       const int64_t t = t0 + row;
-      if (t < T) *reinterpret_cast<f32x4*>(a.out + ((b * T + t) * H + h) * a.dv + cp) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < T) *reinterpret_cast<f32x4*>(a.out + ((b * T + t) * H + h) * a.dv + cp) = f32x4{fill, fill, fill, fill};
     }
   }
 }
