@@ -140,6 +140,9 @@ struct Stage {
   frag tf[C / 32];
   frag pf[C / 32];
   f32x4 cv[VTile<MT, 16 * NT, C>::NVI];
+  // bidirectional second visit: the other direction's readout of this chunk
+  // (per output tile of the wave), loaded a step ahead like the rest
+  f32x4 pq[(C / 16 * NT + 3) / 4];
 };
 
 __device__ __forceinline__ bool tri_needed(bool rev, int kc, int rt) {
@@ -454,11 +457,12 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   // (the stage the next step's triangle loads overwrite only in its last
   // phase), Vnew (LDS until the next step's second phase) and the staged
   // scales (until the next step's last phase).  `on` = false: nothing is stored.
-  // Second visits of a bidirectional scan add the partial `part` the other
-  // direction stored, loaded and checked during the visit step.
-  f32x4 Zp[UPW], part[UPW], pnext[UPW];  // pnext: the partial of the step being computed
+  // Second visits of a bidirectional scan add the partial the other
+  // direction stored (the stage's pq, loaded a step ahead and checked at the
+  // end of the visit step).
+  f32x4 Zp[UPW];
 #pragma unroll
-  for (int j = 0; j < UPW; ++j) Zp[j] = part[j] = pnext[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < UPW; ++j) Zp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto readout = [&](const F& sp, const int s_prev, const bool on) {
     const unsigned char* sg = stg[s_prev & 1];
     frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
@@ -490,7 +494,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
             acc = M::mma(vh, diag_only[kc].apply(pdiag), acc);
           }
         }
-        if (add) acc += part[j];
+        if (add) acc += sp.pq[j];
         bstore16(ro, out_off + ct * 64, acc);
       }
     }
@@ -519,16 +523,6 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     }
     load_coop(nx, cn);
     load_rows(nx.kf, kbase, cn);
-    // bidirectional second visit of the next step's chunk: the other
-    // direction's partial, loaded a step ahead, checked at the end of the next
-    // step and consumed by its readout
-    f32x4 pq[UPW];
-    if constexpr (BI) {
-      const bool want = s + 1 < NC && !first_visit(s + 1);
-      const rsrc_t rp = make_rsrc(obase + (size_t)cn * C * HOB, want ? extent(cn, HOB, DT * 4) : 0u);
-#pragma unroll
-      for (int j = 0; j < UPW; ++j) pq[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
-    }
     readout(nx, s - 1, s > 0);  // the previous step's chunk (nx still holds its stage)
     f32x4 X[UPW], Vn[UPW];
 #pragma unroll
@@ -566,6 +560,16 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 
     // [B] Vnew = X + strict(Tinv) X
     load_rows(nx.qf, qbase, cn);
+    // bidirectional second visit of the next step's chunk: the other
+    // direction's partial, loaded a step ahead (after this step's readout has
+    // read nx's previous contents), checked at the end of the next step and
+    // consumed by its readout
+    if constexpr (BI) {
+      const bool want = s + 1 < NC && !first_visit(s + 1);
+      const rsrc_t rp = make_rsrc(obase + (size_t)cn * C * HOB, want ? extent(cn, HOB, DT * 4) : 0u);
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) nx.pq[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
+    }
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
       const int u = w + NW * j;
@@ -653,22 +657,17 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         for (int j = 0; j < UPW; ++j) {
           // first test outside any loop: a loop that reloads the tested value
           // makes the compiler wait for every load in flight at its head
-          if (__any(any_unwritten(pnext[j]))) {
+          if (__any(any_unwritten(st.pq[j]))) {
             const uint32_t off = out_off + ((w + NW * j) / RT) * 64;
-            f32x4 q = pnext[j];
+            f32x4 q = st.pq[j];
             for (int n = 0; n < kPollLimit; ++n) {
               __builtin_amdgcn_s_sleep(2);
               q = bload16_fresh(rp, off);
               if (!__any(any_unwritten(q))) break;
             }
-            pnext[j] = q;
+            st.pq[j] = q;
           }
         }
-      }
-#pragma unroll
-      for (int j = 0; j < UPW; ++j) {
-        part[j] = pnext[j];
-        pnext[j] = pq[j];
       }
     }
     stash(nx, buf ^ 1);  // next step's group-shared operands (its slot was last read one step ago)
@@ -687,7 +686,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     if constexpr (BI) {  // the partial of step 0 (a single-chunk scan's reverse visit)
       const rsrc_t rp = make_rsrc(obase + (size_t)c0 * C * HOB, first_visit(0) ? 0u : extent(c0, HOB, DT * 4));
 #pragma unroll
-      for (int j = 0; j < UPW; ++j) pnext[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
+      for (int j = 0; j < UPW; ++j) sA.pq[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
     }
     stash(sA, 0);
     __syncthreads();
