@@ -51,44 +51,6 @@
 
 namespace gdn {
 
-// ---- raw buffer access -----------------------------------------------------
-// Word 3 of a gfx9 buffer resource for raw (unstructured) access with 32-bit
-// elements; the hardware bounds every access by num_records bytes.
-constexpr int kRawBufferWord3 = 0x00020000;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
-}
-
-__device__ __forceinline__ f32x4 bload16(rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  f32x4 f;
-  __builtin_memcpy(&f, &v, 16);
-  return f;
-}
-
-__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, f32x4 x) {
-  u32x4 v;
-  __builtin_memcpy(&v, &x, 16);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
-}
-
-// A matrix-core fragment (8 consecutive elements) at byte offset `off`.
-template <typename MT>
-__device__ __forceinline__ typename Mma<MT>::frag bload_frag(rsrc_t r, uint32_t off) {
-  typename Mma<MT>::frag f;
-  if constexpr (sizeof(MT) == 2) {
-    const f32x4 v = bload16(r, off);
-    __builtin_memcpy(&f, &v, 16);
-  } else {
-    f.lo = bload16(r, off);
-    f.hi = bload16(r, off + 16);
-  }
-  return f;
-}
-
 template <typename MT, int DK, int C, int NT>
 struct ChainSmem {
   static constexpr int ES = (int)sizeof(MT);

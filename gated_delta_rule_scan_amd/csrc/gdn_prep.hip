@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   constexpr int EP = SM::EP, KP = SM::KP, NB = SM::NB, LP = SM::LP;
 
   __shared__ __align__(16) unsigned char smem[SM::region];
-  __shared__ float s_rk[C], s_rq[C];
-  __shared__ float s_la[2][C], s_bt[2][C], s_g[2][C];
+  __shared__ __align__(16) float s_rk[C], s_rq[C], s_lo[C];
+  __shared__ __align__(16) float s_bt[2][C], s_g[2][C];
 
   constexpr int PP = SM::PP;
   MT* Ks = reinterpret_cast<MT*>(smem);
@@ -81,85 +81,100 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   const int fwd_on = a.fwd_on, rev_on = a.rev_on;
   const int fslot = 0, rslot = fwd_on ? 1 : 0;
   const size_t nch = (size_t)a.B * a.H * a.NC;
+  const int nrows = (int)(T - t0 < C ? T - t0 : C);  // valid tokens of this chunk (>= 1)
+  constexpr float kLog2e = 1.4426950408889634f;
 
-  // ---- stage raw q and k of this chunk into LDS (padded rows are zero) ----
-  {
-    const MT* q = static_cast<const MT*>(a.q);
-    const MT* k = static_cast<const MT*>(a.k);
-    constexpr int PR = DK / EP;  // pieces per row
-    constexpr int NP = C * PR;   // pieces per matrix
+  // ---- every global read of the kernel, issued at once ----
+  // Raw q and k rows (16-byte pieces; rows past the sequence read as zero),
+  // and one gate per lane: wave 0 the forward log-gates in token order, wave 1
+  // the reverse log-gates in reverse token order (the reverse visiting
+  // order), waves 2 and 3 the forward and reverse write strengths.
+  constexpr int PR = DK / EP;    // pieces per row
+  constexpr int RPI = 256 / PR;  // rows per pass of the workgroup
+  constexpr int NPT = C / RPI;   // pieces per thread and matrix
+  static_assert(256 % PR == 0 && C % RPI == 0, "piece split");
+  const int prow = tid / PR, pcol = (tid % PR) * EP;
+  const uint32_t rowb = (uint32_t)(H * DK * (int64_t)sizeof(MT));
+  const size_t kq0 = (size_t)((b * T + t0) * H + h) * DK;
+  const uint32_t kq_ext = (uint32_t)(nrows - 1) * rowb + DK * (uint32_t)sizeof(MT);
+  const rsrc_t rq = make_rsrc(static_cast<const MT*>(a.q) + kq0, kq_ext);
+  const rsrc_t rk = make_rsrc(static_cast<const MT*>(a.k) + kq0, kq_ext);
+  f32x4 vq[NPT], vk[NPT];
 #pragma unroll
-    for (int p = tid; p < NP; p += 256) {
-      const int row = p / PR, cp = (p % PR) * EP;
-      const int64_t t = t0 + row;
-      f32x4 vq = {0.f, 0.f, 0.f, 0.f}, vk = {0.f, 0.f, 0.f, 0.f};
-      if (t < T) {
-        const int64_t off = ((b * T + t) * H + h) * DK + cp;
-        vq = *reinterpret_cast<const f32x4*>(q + off);
-        vk = *reinterpret_cast<const f32x4*>(k + off);
+  for (int i = 0; i < NPT; ++i) {
+    const uint32_t off = (uint32_t)(prow + RPI * i) * rowb + pcol * (uint32_t)sizeof(MT);
+    vq[i] = bload16(rq, off);
+    vk[i] = bload16(rk, off);
+  }
+  float gate;
+  {
+    const int dir = wave & 1;                   // waves 0, 2: forward; 1, 3: reverse
+    const bool on = dir == 0 ? fwd_on : rev_on;
+    const int slot = dir == 0 ? fslot : rslot;
+    const float* src = wave < 2 ? a.log_alpha : a.beta;
+    const rsrc_t rg = make_rsrc(src + ((slot * B + b) * T + t0) * H + h, on ? (uint32_t)((nrows - 1) * H + 1) * 4u : 0u);
+    const int tok = wave == 1 ? C - 1 - lane : lane;
+    gate = bload4(rg, lane < C ? (uint32_t)(tok * H) * 4u : 0xFFFFFFF0u);
+  }
+
+  // ---- row scales from the registers, operands into LDS ----
+  {
+    auto elem = [](const f32x4& v, int e) -> float {  // element e of a 16-byte piece
+      if constexpr (sizeof(MT) == 2) {
+        return (float)__builtin_bit_cast(bf16x8, v)[e];
+      } else {
+        return v[e];
       }
-      *reinterpret_cast<f32x4*>(Qs + row * KP + cp) = vq;
-      *reinterpret_cast<f32x4*>(Ks + row * KP + cp) = vk;
-    }
-  }
-  if (tid < C) {
-    const int64_t t = t0 + tid;
-    const bool in = t < T;
-    if (fwd_on) {
-      const int64_t gi = ((fslot * B + b) * T + t) * H + h;
-      s_la[0][tid] = in ? a.log_alpha[gi] : 0.f;
-      s_bt[0][tid] = in ? a.beta[gi] : 0.f;
-    }
-    if (rev_on) {
-      const int64_t gi = ((rslot * B + b) * T + t) * H + h;
-      s_la[1][tid] = in ? a.log_alpha[gi] : 0.f;
-      s_bt[1][tid] = in ? a.beta[gi] : 0.f;
-    }
-  }
-  __syncthreads();
-
-  // ---- row scales and chunk-local cumulative log-gates ----
-  {
-    constexpr int G = 256 / C;        // threads per row
-    constexpr int PER = DK / G;       // elements per thread (a multiple of 8)
-    const int row = tid / G, part = tid % G;
-    float sq = 0.f, sk = 0.f;
+    };
 #pragma unroll
-    for (int e8 = 0; e8 < PER; e8 += 8) {  // 8 elements per fragment-sized read
-      const typename M::frag fq = M::load(Qs + row * KP + part * PER + e8);
-      const typename M::frag fk = M::load(Ks + row * KP + part * PER + e8);
+    for (int i = 0; i < NPT; ++i) {
+      float sq = 0.f, sk = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xq = M::get(fq, e), xk = M::get(fk, e);
+      for (int e = 0; e < EP; ++e) {
+        const float xq = elem(vq[i], e), xk = elem(vk[i], e);
         sq = fmaf(xq, xq, sq);
         sk = fmaf(xk, xk, sk);
       }
-    }
 #pragma unroll
-    for (int m = 1; m < G; m <<= 1) {
-      sq += __shfl_xor(sq, m, 64);
-      sk += __shfl_xor(sk, m, 64);
-    }
-    if (part == 0) {
-      s_rq[row] = 1.0f / fmaxf(sqrtf(sq), kNormEps);
-      s_rk[row] = 1.0f / fmaxf(sqrtf(sk), kNormEps);
+      for (int m = 1; m < PR; m <<= 1) {
+        sq += __shfl_xor(sq, m, 64);
+        sk += __shfl_xor(sk, m, 64);
+      }
+      const int row = prow + RPI * i;
+      if (tid % PR == 0) {
+        s_rq[row] = 1.0f / fmaxf(sqrtf(sq), kNormEps);
+        s_rk[row] = 1.0f / fmaxf(sqrtf(sk), kNormEps);
+      }
+      *reinterpret_cast<f32x4*>(Qs + row * KP + pcol) = vq[i];
+      *reinterpret_cast<f32x4*>(Ks + row * KP + pcol) = vk[i];
     }
   }
-  // chunk-local cumulative log-gates, kept in log2 units so every decay
-  // factor below is one exp2 of a difference: wave 0 forms the inclusive
-  // prefix sums in token order, wave 1 the inclusive suffix sums (the reverse
-  // visiting order), each as a wave-wide scan
-  constexpr float kLog2e = 1.4426950408889634f;
-  if (wave < 2 && (wave == 0 ? fwd_on : rev_on)) {
-    const int dir = wave;
-    const int tok = dir == 0 ? lane : C - 1 - lane;  // position in visiting order = lane
-    float s = lane < C ? s_la[dir][tok] : 0.f;
+  // chunk-local cumulative log-gates in log2 units (every decay factor below
+  // is one exp2 of a difference): wave 0 the inclusive prefix sums in token
+  // order, wave 1 the inclusive suffix sums, each as a wave-wide scan
+  if (wave < 2) {
+    float s = gate;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const float o = __shfl_up(s, d, 64);
       if (lane >= d) s += o;
     }
-    if (lane < C) s_g[dir][tok] = s * kLog2e;
+    if (lane < C) s_g[wave][wave == 0 ? lane : C - 1 - lane] = s * kLog2e;
+  } else if (lane < C) {
+    s_bt[wave - 2][lane] = gate;
+  }
+
+  // ---- bidirectional scans: the second visitor of a chunk in the state
+  // chain recognises the first visitor's readout by this all-ones NaN fill
+  // ("not written yet"; arithmetic never produces it).  Issued after every
+  // read of the kernel has returned, so it never delays them. ----
+  if (a.zero_out) {
+    const int dv4 = a.dv / 4;
+    const uint32_t orow = (uint32_t)(H * a.dv) * 4u;
+    const rsrc_t ro = make_rsrc(a.out + ((b * T + t0) * H + h) * a.dv, (uint32_t)(nrows - 1) * orow + (uint32_t)a.dv * 4u);
+    const float fn = __uint_as_float(0xFFFFFFFFu);
+    const f32x4 fill = f32x4{fn, fn, fn, fn};
+    for (int p = tid; p < C * dv4; p += 256) bstore16(ro, (uint32_t)(p / dv4) * orow + (uint32_t)(p % dv4) * 16u, fill);
   }
   __syncthreads();
 
@@ -187,37 +202,36 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   __syncthreads();  // q/k staging area is reused below
 
   // ---- gated, scaled triangles: L and the decayed Q^K^^T into LDS ----
+  // Lane (l16, g4) of tile (ti, tj) holds column 16 tj + l16 of rows
+  // 16 ti + 4 g4 + i.  Below the diagonal the forward direction's entries,
+  // above it the reverse direction's; on it the self term q^_r . k^_r.
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     const int u = wave + 4 * j;
     if (u < NT2) {
       const int ti = u / NB, tj = u % NB;
-      const int col = 16 * tj + l16;
-      const float rkc = s_rk[col];
+      const int col = 16 * tj + l16, r0 = 16 * ti + 4 * g4;
+      const float gfc = s_g[0][col], grc = s_g[1][col], rkc = s_rk[col];
+      const f32x4 gf = *reinterpret_cast<const f32x4*>(&s_g[0][r0]);
+      const f32x4 gr = *reinterpret_cast<const f32x4*>(&s_g[1][r0]);
+      const f32x4 bf = *reinterpret_cast<const f32x4*>(&s_bt[0][r0]);
+      const f32x4 br = *reinterpret_cast<const f32x4*>(&s_bt[1][r0]);
+      const f32x4 rkr = *reinterpret_cast<const f32x4*>(&s_rk[r0]);
+      const f32x4 rqr = *reinterpret_cast<const f32x4*>(&s_rq[r0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * ti + 4 * g4 + i;
-        float lv = 0.f, pv = 0.f;
-        if (col < r) {
-          if (fwd_on) {
-            const float gam = exp2f(s_g[0][r] - s_g[0][col]);
-            lv = s_bt[0][r] * s_rk[r] * rkc * accG[j][i] * gam;
-            pv = s_rq[r] * rkc * accP[j][i] * gam;
-          }
-        } else if (col > r) {
-          if (rev_on) {
-            const float gam = exp2f(s_g[1][r] - s_g[1][col]);
-            lv = s_bt[1][r] * s_rk[r] * rkc * accG[j][i] * gam;
-            pv = s_rq[r] * rkc * accP[j][i] * gam;
-          }
-        } else {
-          // self term q^_r . k^_r: on the diagonal in the operand type, the
-          // remainder that type drops into each direction's record
-          pv = s_rq[r] * s_rk[r] * accP[j][i];
-          const float lo = pv - (float)(MT)pv;
-          if (fwd_on) a.pdg[((size_t)fslot * nch + cid) * (C + 4) + r] = lo;
-          if (rev_on) a.pdg[((size_t)rslot * nch + cid) * (C + 4) + r] = lo;
-        }
+        const int r = r0 + i;
+        const bool lower = col < r && fwd_on, upper = col > r && rev_on, diag = col == r;
+        // decay between the two tokens (<= 0 in log2 units); zero elsewhere,
+        // so the factor below is 1 on the diagonal and never overflows
+        const float gd = lower ? gf[i] - gfc : (upper ? gr[i] - grc : 0.f);
+        const float e = exp2f(gd);
+        const float lm = lower ? e * bf[i] : (upper ? e * br[i] : 0.f);
+        const float pm = (lower || upper || diag) ? e : 0.f;
+        const float lv = rkr[i] * rkc * accG[j][i] * lm;
+        const float pv = rqr[i] * rkc * accP[j][i] * pm;
+        // on the diagonal, the part of the self term the operand type drops
+        if (diag) s_lo[r] = pv - (float)(MT)pv;
         Lm[r * LP + col] = lv;
         Pst[r * PP + col] = (MT)pv;
       }
@@ -234,28 +248,46 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     // column jc of (I + L_bb)^{-1} by forward substitution in visiting
     // order, column-oriented: once x_i is known it is folded into every
     // later row's running sum, so the dependent chain is 16 steps long.
-    // One instance per direction keeps every index a compile-time constant
-    // (the running sums stay in registers).
+    // The column is written out only at the end, so every read of L can be
+    // issued ahead of the chain.  One instance per direction keeps every
+    // index a compile-time constant (the running sums stay in registers).
     auto solve = [&](auto rev_tag) {
       constexpr bool R = decltype(rev_tag)::value;
-      float acc[16];
+      float acc[16], x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
         const int i = R ? 15 - ii : ii;  // visiting order
         const bool after = R ? (i < jc) : (i > jc);
-        const float x = i == jc ? 1.f : (after ? -acc[i] : 0.f);
-        if (i == jc || after) Ti[(b0 + i) * LP + b0 + jc] = x;
+        x[i] = i == jc ? 1.f : (after ? -acc[i] : 0.f);
 #pragma unroll
         for (int rr = ii + 1; rr < 16; ++rr) {
           const int r = R ? 15 - rr : rr;
-          acc[r] = fmaf(Lm[(b0 + r) * LP + b0 + i], x, acc[r]);
+          acc[r] = fmaf(Lm[(b0 + r) * LP + b0 + i], x[i], acc[r]);
         }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (R ? i <= jc : i >= jc) Ti[(b0 + i) * LP + b0 + jc] = x[i];
     };
     if (dir == 0 && fwd_on) solve(std::false_type{});
     if (dir == 1 && rev_on) solve(std::true_type{});
+  } else if (tid - 2 * NB * 16 < 2 * C) {
+    // ---- meanwhile, per-token scales and the chunk decays ----
+    const int idx = tid - 2 * NB * 16;
+    const int dir = idx / C, tok = idx % C;
+    if (dir == 0 ? fwd_on : rev_on) {
+      const int slot = dir == 0 ? fslot : rslot;
+      const bool in = tok < nrows;
+      const float g = s_g[dir][tok], gl = s_g[dir][dir == 0 ? C - 1 : 0];
+      const float eg = exp2f(g), rk = s_rk[tok];
+      a.sc[(slot * nch + cid) * C + tok] =
+          in ? make_float4(s_bt[dir][tok], eg * rk, eg * s_rq[tok], exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      float* pd = a.pdg + ((size_t)slot * nch + cid) * (C + 4);
+      pd[tok] = s_lo[tok];
+      if (tok < 4) pd[C + tok] = tok == 0 ? exp2f(gl) : 0.f;
+    }
   }
   __syncthreads();
 
@@ -332,39 +364,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       }
       __builtin_memcpy(tri + p * EPS, tv, 16);
       __builtin_memcpy(pqk + p * EPS, pv, 16);
-    }
-  }
-  // ---- per-token scales and the chunk decay ----
-  if (tid < C) {
-    const bool in = (t0 + tid) < T;
-    const float rk = s_rk[tid], rq = s_rq[tid];
-    if (fwd_on) {
-      const float g = s_g[0][tid], gl = s_g[0][C - 1];
-      const float eg = exp2f(g);
-      float4 v = in ? make_float4(s_bt[0][tid], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
-      a.sc[(fslot * nch + cid) * C + tid] = v;
-      if (tid < 4) a.pdg[((size_t)fslot * nch + cid) * (C + 4) + C + tid] = tid == 0 ? exp2f(gl) : 0.f;
-    }
-    if (rev_on) {
-      const float g = s_g[1][tid], gl = s_g[1][0];
-      const float eg = exp2f(g);
-      float4 v = in ? make_float4(s_bt[1][tid], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
-      a.sc[(rslot * nch + cid) * C + tid] = v;
-      if (tid < 4) a.pdg[((size_t)rslot * nch + cid) * (C + 4) + C + tid] = tid == 0 ? exp2f(gl) : 0.f;
-    }
-  }
-
-  // ---- bidirectional scans: the second visitor of a chunk in the state
-  // chain recognises the first visitor's readout by this all-ones NaN fill
-  // ("not written yet"; arithmetic never produces it).  Last, so these stores
-  // never queue ahead of the loads above. ----
-  if (a.zero_out) {
-    const int dv4 = a.dv / 4;
-    const float fill = __uint_as_float(0xFFFFFFFFu);
-    for (int p = tid; p < C * dv4; p += 256) {
-      const int row = p / dv4, cp = (p % dv4) * 4;
-      const int64_t t = t0 + row;
-      if (t < T) *reinterpret_cast<f32x4*>(a.out + ((b * T + t) * H + h) * a.dv + cp) = f32x4{fill, fill, fill, fill};
     }
   }
 }
