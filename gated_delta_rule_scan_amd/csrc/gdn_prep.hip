@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   constexpr int EP = SM::EP, KP = SM::KP, NB = SM::NB, LP = SM::LP;
 
   __shared__ __align__(16) unsigned char smem[SM::region];
-  __shared__ __align__(16) float s_rk[C], s_rq[C], s_lo[C];
-  __shared__ __align__(16) float s_bt[2][C], s_g[2][C];
+  __shared__ __align__(16) float s_rk[C], s_rq[C], s_qk[C];  // row scales, raw q.k of each token
+  __shared__ __align__(16) float s_raw[4][64], s_g[2][C];  // raw gates as loaded (see below); cumulative log2-gates
 
   constexpr int PP = SM::PP;
   MT* Ks = reinterpret_cast<MT*>(smem);
@@ -128,55 +128,63 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     };
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      float sq = 0.f, sk = 0.f;
+      float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
       for (int e = 0; e < EP; ++e) {
         const float xq = elem(vq[i], e), xk = elem(vk[i], e);
         sq = fmaf(xq, xq, sq);
         sk = fmaf(xk, xk, sk);
+        sqk = fmaf(xq, xk, sqk);
       }
 #pragma unroll
       for (int m = 1; m < PR; m <<= 1) {
         sq += __shfl_xor(sq, m, 64);
         sk += __shfl_xor(sk, m, 64);
+        sqk += __shfl_xor(sqk, m, 64);
       }
       const int row = prow + RPI * i;
       if (tid % PR == 0) {
         s_rq[row] = 1.0f / fmaxf(sqrtf(sq), kNormEps);
         s_rk[row] = 1.0f / fmaxf(sqrtf(sk), kNormEps);
+        s_qk[row] = sqk;
       }
       *reinterpret_cast<f32x4*>(Qs + row * KP + pcol) = vq[i];
       *reinterpret_cast<f32x4*>(Ks + row * KP + pcol) = vk[i];
     }
   }
-  // chunk-local cumulative log-gates in log2 units (every decay factor below
-  // is one exp2 of a difference): wave 0 the inclusive prefix sums in token
-  // order, wave 1 the inclusive suffix sums, each as a wave-wide scan
-  if (wave < 2) {
-    float s = gate;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float o = __shfl_up(s, d, 64);
-      if (lane >= d) s += o;
-    }
-    if (lane < C) s_g[wave][wave == 0 ? lane : C - 1 - lane] = s * kLog2e;
-  } else if (lane < C) {
-    s_bt[wave - 2][lane] = gate;
-  }
+  // every wave parks its gate in LDS at once (so no path leaves the load
+  // pending); rows 2 and 3 are the write strengths in token order
+  s_raw[wave][lane] = gate;
+  const float (*s_bt)[64] = s_raw + 2;
 
   // ---- bidirectional scans: the second visitor of a chunk in the state
   // chain recognises the first visitor's readout by this all-ones NaN fill
   // ("not written yet"; arithmetic never produces it).  Issued after every
   // read of the kernel has returned, so it never delays them. ----
   if (a.zero_out) {
-    const int dv4 = a.dv / 4;
+    const int sh = 29 - __builtin_clz((unsigned)a.dv);  // log2(dv / 4): 16-byte pieces per row (a power of two)
     const uint32_t orow = (uint32_t)(H * a.dv) * 4u;
     const rsrc_t ro = make_rsrc(a.out + ((b * T + t0) * H + h) * a.dv, (uint32_t)(nrows - 1) * orow + (uint32_t)a.dv * 4u);
     const float fn = __uint_as_float(0xFFFFFFFFu);
     const f32x4 fill = f32x4{fn, fn, fn, fn};
-    for (int p = tid; p < C * dv4; p += 256) bstore16(ro, (uint32_t)(p / dv4) * orow + (uint32_t)(p % dv4) * 16u, fill);
+    for (int p = tid; p < (C << sh); p += 256)
+      bstore16(ro, (uint32_t)(p >> sh) * orow + (uint32_t)(p & ((1 << sh) - 1)) * 16u, fill);
   }
   __syncthreads();
+
+  // chunk-local cumulative log-gates in log2 units (every decay factor below
+  // is one exp2 of a difference): wave 0 the inclusive prefix sums in token
+  // order, wave 1 the inclusive suffix sums, each as a wave-wide scan; read
+  // only after the next barrier
+  if (wave < 2) {
+    float s = s_raw[wave][lane];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(s, d, 64);
+      if (lane >= d) s += o;
+    }
+    if (lane < C) s_g[wave][wave == 0 ? lane : C - 1 - lane] = s * kLog2e;
+  }
 
   // ---- Gram K K^T and Q K^T on the matrix cores (raw operands, fp32 accumulate) ----
   constexpr int NT2 = NB * NB;
@@ -204,7 +212,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   // ---- gated, scaled triangles: L and the decayed Q^K^^T into LDS ----
   // Lane (l16, g4) of tile (ti, tj) holds column 16 tj + l16 of rows
   // 16 ti + 4 g4 + i.  Below the diagonal the forward direction's entries,
-  // above it the reverse direction's; on it the self term q^_r . k^_r.
+  // above it the reverse direction's; the diagonal (the self terms) is
+  // written beside the diagonal solve below.
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     const int u = wave + 4 * j;
@@ -221,19 +230,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + i;
-        const bool lower = col < r && fwd_on, upper = col > r && rev_on, diag = col == r;
-        // decay between the two tokens (<= 0 in log2 units); zero elsewhere,
-        // so the factor below is 1 on the diagonal and never overflows
-        const float gd = lower ? gf[i] - gfc : (upper ? gr[i] - grc : 0.f);
-        const float e = exp2f(gd);
-        const float lm = lower ? e * bf[i] : (upper ? e * br[i] : 0.f);
-        const float pm = (lower || upper || diag) ? e : 0.f;
-        const float lv = rkr[i] * rkc * accG[j][i] * lm;
-        const float pv = rqr[i] * rkc * accP[j][i] * pm;
-        // on the diagonal, the part of the self term the operand type drops
-        if (diag) s_lo[r] = pv - (float)(MT)pv;
-        Lm[r * LP + col] = lv;
-        Pst[r * PP + col] = (MT)pv;
+        // 0/1 weights of the two directions (arithmetic selects: no branches)
+        const float wf = (col < r && fwd_on) ? 1.f : 0.f, wr = (col > r && rev_on) ? 1.f : 0.f;
+        // decay between the two tokens (<= 0 in log2 units; zero where
+        // unused, so it never overflows); below 2^-126 it may flush to zero
+        const float gd = fmaf(wf, gf[i] - gfc, wr * (gr[i] - grc));
+        const float e = __builtin_amdgcn_exp2f(gd);
+        const float lm = e * fmaf(wf, bf[i], wr * br[i]);
+        const float pm = e * (wf + wr);
+        Lm[r * LP + col] = (rkr[i] * rkc) * accG[j][i] * lm;
+        Pst[r * PP + col] = (MT)((rqr[i] * rkc) * accP[j][i] * pm);
       }
     }
   }
@@ -277,15 +283,21 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     // ---- meanwhile, per-token scales and the chunk decays ----
     const int idx = tid - 2 * NB * 16;
     const int dir = idx / C, tok = idx % C;
+    // self term q^_t . k^_t: the operand type's rounding on the diagonal of
+    // the decayed q.k tile, the part it drops into each direction's record
+    const float rk = s_rk[tok], rq = s_rq[tok];
+    const float self = rq * rk * s_qk[tok];
+    const MT self_mt = (MT)self;
+    if (dir == 0) Pst[tok * PP + tok] = self_mt;
     if (dir == 0 ? fwd_on : rev_on) {
       const int slot = dir == 0 ? fslot : rslot;
       const bool in = tok < nrows;
       const float g = s_g[dir][tok], gl = s_g[dir][dir == 0 ? C - 1 : 0];
-      const float eg = exp2f(g), rk = s_rk[tok];
+      const float eg = exp2f(g);
       a.sc[(slot * nch + cid) * C + tok] =
-          in ? make_float4(s_bt[dir][tok], eg * rk, eg * s_rq[tok], exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
+          in ? make_float4(s_bt[dir][tok], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
       float* pd = a.pdg + ((size_t)slot * nch + cid) * (C + 4);
-      pd[tok] = s_lo[tok];
+      pd[tok] = self - (float)self_mt;
       if (tok < 4) pd[C + tok] = tok == 0 ? exp2f(gl) : 0.f;
     }
   }
