@@ -35,11 +35,12 @@
 // workgroup's partner runs, so every wait ends (the polls are bounded too).
 
 // Every global access goes through a raw buffer resource whose extent is the
-// valid part of the chunk: reads past it return zero and writes past it are
-// dropped.  Rows past the end of the sequence therefore need no clamping and
-// no branches, and an access that must not happen this step (the partial of
-// a first visit, the store of a step that has nothing to store) is switched
-// off by an empty extent.  All loads of a step are issued by every wave
+// valid part of the workgroup's whole chain (built once; a chunk is a 32-bit
+// byte offset): reads past it return zero and writes past it are dropped.
+// Rows past the end of the sequence therefore need no clamping and no
+// branches, and an access that must not happen this step (the partial of a
+// first visit, the store of a step that has nothing to store) goes through a
+// resource with an empty extent.  All loads of a step are issued by every wave
 // unconditionally, a step ahead of their use, so no prefetch ever forces a
 // wait on the in-order memory counter.
 //
@@ -271,7 +272,6 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 
   // ---- loop-invariant addressing: per-lane byte offsets within a chunk,
   // wave-uniform chunk bases and strides ----
-  const int n_last = NC > 0 ? (int)(T - (int64_t)(NC - 1) * C) : C;
   const uint32_t HDB = (uint32_t)(H * DK * ES);  // token pitch of q, k
   const uint32_t HVB = (uint32_t)(H * dv * ES);  // token pitch of v
   const uint32_t HOB = (uint32_t)(H * dv * 4);   // token pitch of out
@@ -288,13 +288,12 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   const int o_row0 = 16 * rt + 4 * g4;
   const int kcd = rt / 2;  // k-chunk holding this row tile's diagonal
   // triangle fragments: the k-chunks of this row tile that hold no element
-  // of this direction's triangle are read past the buffer extent (zeros);
-  // the diagonal k-chunk is masked (Tinv strictly, P with its diagonal)
-  uint32_t tri_offs[C / 32];
+  // of this direction's triangle are read past the buffer extent (zeros, see
+  // the resources below); the diagonal k-chunk is masked (Tinv strictly, P
+  // with its diagonal)
   FragMask<MT> tmask[C / 32], pmask[C / 32];
 #pragma unroll
   for (int kc = 0; kc < C / 32; ++kc) {
-    tri_offs[kc] = tri_needed(rev, kc, rt) ? tri_off + 32 * kc * ES : (uint32_t)(C * C * ES);
     tmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, false, kc == kcd);
     pmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, true, kc == kcd);
   }
@@ -317,28 +316,24 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         else diag_only[kc].m[e] = 0xffffffffu;
       }
   }
-  // valid bytes of a chunk's rows: the last row ends after `tail` bytes
-  auto rows_of = [&](int c) -> uint32_t { return (uint32_t)(c == NC - 1 ? n_last : C); };
-  auto extent = [&](int c, uint32_t pitch, uint32_t tail) { return (rows_of(c) - 1) * pitch + tail; };
-
   // group-shared operand loads: which source this wave reads, per-lane offsets
   // and where each piece lands in the staging buffer
   const char* cbase;
-  size_t cstride;
-  uint32_t cbytes;  // extent of a whole chunk (the value tile is bounded per chunk below)
+  uint32_t cstride;  // bytes per chunk
+  uint32_t cbytes;   // extent of the whole chain
   uint32_t c_off[VT::NVI], c_lds[VT::NVI];
   if (cw == 0) {
     cbase = reinterpret_cast<const char*>(a.sc) + ((size_t)slot * nch + (size_t)chain * NC) * C * 16;
-    cstride = (size_t)C * 16;
-    cbytes = C * 16;
+    cstride = C * 16;
+    cbytes = (uint32_t)NC * cstride;
   } else if (cw == 1) {
     cbase = reinterpret_cast<const char*>(a.pdg) + ((size_t)slot * nch + (size_t)chain * NC) * (C + 4) * 4;
-    cstride = (size_t)(C + 4) * 4;
-    cbytes = (C + 4) * 4;
+    cstride = (C + 4) * 4;
+    cbytes = (uint32_t)NC * cstride;
   } else {
     cbase = vbase;
-    cstride = (size_t)C * HVB;
-    cbytes = 0;
+    cstride = C * HVB;
+    cbytes = (uint32_t)(T - 1) * HVB + DT * ES;
   }
 #pragma unroll
   for (int n = 0; n < VT::NVI; ++n) {
@@ -358,33 +353,44 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     }
   }
 
-  // ---- per-chunk resources ----
-  auto rs_rows = [&](const char* base, int c, uint32_t pitch, uint32_t tail) {
-    return make_rsrc(base + (size_t)c * C * pitch, extent(c, pitch, tail));
-  };
-  auto rs_tri = [&](const char* base, int c) { return make_rsrc(base + (size_t)c * C * C * ES, C * C * ES); };
-  auto rs_coop = [&](int c) {
-    return make_rsrc(cbase + (size_t)c * cstride, cw >= 2 ? extent(c, HVB, DT * ES) : cbytes);
-  };
-  auto rs_out = [&](int c) { return make_rsrc(obase + (size_t)c * C * HOB, extent(c, HOB, DT * 4)); };
+  // ---- whole-chain resources, built once: an access adds its chunk's byte
+  // offset (32 bits; the host bounds every extent below 4 GiB) to its
+  // per-lane offset.  Token rows past the end of the sequence lie past the
+  // extent (loads read zero, stores are dropped); an access that must not
+  // happen this step goes through `rnone` (empty extent) ----
+  const rsrc_t rnone = make_rsrc(obase, 0u);
+  const uint32_t kq_ext = (uint32_t)(T - 1) * HDB + DK * ES;
+  const rsrc_t rk = make_rsrc(kbase, kq_ext), rq = make_rsrc(qbase, kq_ext);
+  const rsrc_t rc = make_rsrc(cbase, cbytes);
+  const rsrc_t ro = make_rsrc(obase, (uint32_t)(T - 1) * HOB + DT * 4);
+  const uint32_t tri_bytes = (uint32_t)NC * (C * C * ES);
+  rsrc_t rtk[C / 32], rpk[C / 32];  // triangle k-chunks this row tile never needs: zeros
+#pragma unroll
+  for (int kc = 0; kc < C / 32; ++kc) {
+    const bool need = tri_needed(rev, kc, rt);
+    rtk[kc] = make_rsrc(trib, need ? tri_bytes : 0u);
+    rpk[kc] = make_rsrc(pqkb, need ? tri_bytes : 0u);
+  }
+  auto kq_at = [&](int c) { return (uint32_t)c * (C * HDB); };
+  auto out_at = [&](int c) { return (uint32_t)c * (C * HOB); };
 
   // ---- loaders (issued a step ahead) ----
-  auto load_rows = [&](frag* dst, const char* base, int c) {
-    const rsrc_t r = rs_rows(base, c, HDB, DK * ES);
+  auto load_rows = [&](frag* dst, const rsrc_t r, int c) {
+    const uint32_t o = kq_off + kq_at(c);
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) dst[ks] = bload_frag<MT>(r, kq_off + 32 * ks * ES);
+    for (int ks = 0; ks < DK / 32; ++ks) dst[ks] = bload_frag<MT>(r, o + 32 * ks * ES);
   };
   auto load_coop = [&](F& f, int c) {
-    const rsrc_t r = rs_coop(c);
+    const uint32_t o = (uint32_t)c * cstride;
 #pragma unroll
-    for (int n = 0; n < VT::NVI; ++n) f.cv[n] = bload16(r, c_off[n]);
+    for (int n = 0; n < VT::NVI; ++n) f.cv[n] = bload16(rc, c_off[n] + o);
   };
   auto load_tri = [&](F& f, int c) {  // every wave issues the same loads
-    const rsrc_t rt_ = rs_tri(trib, c), rp = rs_tri(pqkb, c);
+    const uint32_t o = tri_off + (uint32_t)c * (C * C * ES);
 #pragma unroll
     for (int kc = 0; kc < C / 32; ++kc) {
-      f.tf[kc] = bload_frag<MT>(rt_, tri_offs[kc]);
-      f.pf[kc] = bload_frag<MT>(rp, tri_offs[kc]);
+      f.tf[kc] = bload_frag<MT>(rtk[kc], o + 32 * kc * ES);
+      f.pf[kc] = bload_frag<MT>(rpk[kc], o + 32 * kc * ES);
     }
   };
   auto stash = [&](const F& f, int buf) {  // group-shared pieces of a loaded stage -> LDS
@@ -434,7 +440,8 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
       for (int e = 0; e < 8; ++e) pdiag[e] = r;
     }
     const int c = chunk_at(s_prev);
-    const rsrc_t ro = make_rsrc(obase + (size_t)c * C * HOB, on ? extent(c, HOB, DT * 4) : 0u);
+    const rsrc_t rs = on ? ro : rnone;
+    const uint32_t oo = out_off + out_at(c);
     const float zs = *reinterpret_cast<const float*>(sg + SM::ST_SC + kq_row * 16 + 8);  // e^g rq of the token
     const bool add = BI && !first_visit(s_prev);
 #pragma unroll
@@ -457,7 +464,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           }
         }
         if (add) acc += sp.pq[j];
-        bstore16(ro, out_off + ct * 64, acc);
+        bstore16(rs, oo + ct * 64, acc);
       }
     }
   };
@@ -484,7 +491,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
       }
     }
     load_coop(nx, cn);
-    load_rows(nx.kf, kbase, cn);
+    load_rows(nx.kf, rk, cn);
     readout(nx, s - 1, s > 0);  // the previous step's chunk (nx still holds its stage)
     f32x4 X[UPW], Vn[UPW];
 #pragma unroll
@@ -521,16 +528,17 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     __syncthreads();
 
     // [B] Vnew = X + strict(Tinv) X
-    load_rows(nx.qf, qbase, cn);
+    load_rows(nx.qf, rq, cn);
     // bidirectional second visit of the next step's chunk: the other
     // direction's partial, loaded a step ahead (after this step's readout has
     // read nx's previous contents), checked at the end of the next step and
     // consumed by its readout
     if constexpr (BI) {
       const bool want = s + 1 < NC && !first_visit(s + 1);
-      const rsrc_t rp = make_rsrc(obase + (size_t)cn * C * HOB, want ? extent(cn, HOB, DT * 4) : 0u);
+      const rsrc_t rp = want ? ro : rnone;
+      const uint32_t op = out_off + out_at(cn);
 #pragma unroll
-      for (int j = 0; j < UPW; ++j) nx.pq[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
+      for (int j = 0; j < UPW; ++j) nx.pq[j] = bload16(rp, op + ((w + NW * j) / RT) * 64);
     }
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
@@ -614,17 +622,16 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     // not stored it yet -- re-read it past the L1 cache
     if constexpr (BI) {
       if (!first_visit(s)) {
-        const rsrc_t rp = make_rsrc(obase + (size_t)c * C * HOB, extent(c, HOB, DT * 4));
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
           // first test outside any loop: a loop that reloads the tested value
           // makes the compiler wait for every load in flight at its head
           if (__any(any_unwritten(st.pq[j]))) {
-            const uint32_t off = out_off + ((w + NW * j) / RT) * 64;
+            const uint32_t off = out_off + out_at(c) + ((w + NW * j) / RT) * 64;
             f32x4 q = st.pq[j];
             for (int n = 0; n < kPollLimit; ++n) {
               __builtin_amdgcn_s_sleep(2);
-              q = bload16_fresh(rp, off);
+              q = bload16_fresh(ro, off);
               if (!__any(any_unwritten(q))) break;
             }
             st.pq[j] = q;
@@ -642,13 +649,13 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   if (NC > 0) {
     const int c0 = chunk_at(0);
     load_coop(sA, c0);
-    load_rows(sA.kf, kbase, c0);
-    load_rows(sA.qf, qbase, c0);
+    load_rows(sA.kf, rk, c0);
+    load_rows(sA.qf, rq, c0);
     load_tri(sA, c0);
     if constexpr (BI) {  // the partial of step 0 (a single-chunk scan's reverse visit)
-      const rsrc_t rp = make_rsrc(obase + (size_t)c0 * C * HOB, first_visit(0) ? 0u : extent(c0, HOB, DT * 4));
+      const rsrc_t rp = first_visit(0) ? rnone : ro;
 #pragma unroll
-      for (int j = 0; j < UPW; ++j) sA.pq[j] = bload16(rp, out_off + ((w + NW * j) / RT) * 64);
+      for (int j = 0; j < UPW; ++j) sA.pq[j] = bload16(rp, out_off + out_at(c0) + ((w + NW * j) / RT) * 64);
     }
     stash(sA, 0);
     __syncthreads();
