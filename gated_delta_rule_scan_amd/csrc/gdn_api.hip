@@ -60,6 +60,9 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   if (!supported_dim(p->dk) || !supported_dim(p->dv)) return GDN_ERR_UNSUPPORTED;
   if (p->B * p->H > 65535) return GDN_ERR_UNSUPPORTED;  // grid limit of the preparation kernel
   if (p->T > ((int64_t)1 << 31) / 2) return GDN_ERR_UNSUPPORTED;
+  // every kernel addresses one (batch, head) sequence -- its rows interleaved
+  // with the other heads' -- through 32-bit byte offsets
+  if ((p->T + 64) * p->H * (p->dk > p->dv ? p->dk : p->dv) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
   const int C = p->chunk == 0 ? 64 : p->chunk;
   if (C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
   int NT = 0;  // 0: chosen at launch (any choice divides dv)

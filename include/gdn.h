@@ -91,7 +91,9 @@ typedef enum {
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
  * chunk in {0 (= 64), 32, 64}; dv_tile in {0, 16, 32} (0: 32 when 16-wide
  * state-chain workgroups would outnumber the compute units of the current
- * device, else 16); B, H >= 1, B*H <= 65535; 0 <= T <= 2^30. */
+ * device, else 16); B, H >= 1, B*H <= 65535; 0 <= T <= 2^30 and
+ * (T + 64) * H * max(dk, dv) * 4 < 2^32 (one batch element's rows, fp32,
+ * fit 32-bit byte offsets). */
 typedef struct {
   int64_t B, T, H, dk, dv;
   int32_t dtype;            /* gdn_dtype_t: type of q, k, v */

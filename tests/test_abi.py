@@ -85,7 +85,7 @@ def test_workspace_bytes():
 
 @pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=80), dict(chunk=48), dict(chunk=16), dict(dv_tile=64),
                                 dict(dtype=7), dict(B=0), dict(H=0), dict(T=-1), dict(B=300, H=300),
-                                dict(dv_tile=48)])
+                                dict(dv_tile=48), dict(T=1 << 20, H=8, dk=128, dv=128)])
 def test_workspace_bytes_rejects(kw):
     assert gdn.gdn_workspace_bytes(_prob(**kw), gdn.GDN_DIR_FORWARD) == 0
 
