@@ -33,6 +33,8 @@ DIRECTIONS = {"fwd": GDN_DIR_FORWARD, "rev": GDN_DIR_REVERSE, "bi": GDN_DIR_BIDI
 GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
 
+GDN_OPT_SERIAL = 1
+
 EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_status_string", "gdn_version")
 
 
@@ -41,7 +43,7 @@ class gdn_problem_t(ctypes.Structure):
         ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
         ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
-        ("dv_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("dv_tile", ctypes.c_int32), ("options", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("timing_events", ctypes.c_void_p),
@@ -111,13 +113,16 @@ def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd"
 
 def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chunk: int = 0, dv_tile: int = 0,
             out=None, state_out=None, workspace=None, want_state: bool = True, stream=None,
-            timing_events: Optional[int] = None) -> Tuple:
+            timing_events: Optional[int] = None, serial: bool = False) -> Tuple:
     """Run the scan on torch CUDA tensors (layouts of include/gdn.h).
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv] (float32 or bfloat16, same dtype);
     log_alpha, beta: [dirs,B,T,H] float32; state_in: [dirs,B,H,dv,dk] float32 or None.
     Returns (out [B,T,H,dv] float32, state_out or None).  ``state_out`` may be
     passed as the same tensor as ``state_in`` for an in-place carry.
+    ``serial`` keeps both kernels on ``stream`` (GDN_OPT_SERIAL); otherwise the
+    library may run the chunk preparation concurrently on its own stream.
+    ``timing_events``: address of four caller-owned hipEvent_t (see gdn.h).
     """
     import torch
 
@@ -155,6 +160,7 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     prob.workspace_bytes = workspace.numel() if workspace is not None else 0
     prob.stream = s.cuda_stream
     prob.timing_events = timing_events
+    prob.options = GDN_OPT_SERIAL if serial else 0
     st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                      None if state_in is None else state_in.data_ptr(),
                      None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])

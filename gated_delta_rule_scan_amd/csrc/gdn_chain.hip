@@ -106,6 +106,9 @@ struct Stage {
   // bidirectional second visit: the other direction's readout of this chunk
   // (per output tile of the wave), loaded a step ahead like the rest
   f32x4 pq[(C / 16 * NT + 3) / 4];
+  // ready flag of the chunk this stage is loaded with next (read two steps
+  // ahead; 0 = ready)
+  uint32_t rdy;
 };
 
 __device__ __forceinline__ bool tri_needed(bool rev, int kc, int rt) {
@@ -204,6 +207,16 @@ __device__ __forceinline__ f32x4 bload16_fresh(rsrc_t r, uint32_t off) {
 }
 
 constexpr int kPollLimit = 1 << 20;
+
+// 4-byte flag load that misses the L1 cache, as a uint32
+__device__ __forceinline__ uint32_t bload4_fresh(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 17);
+}
+
+// Bound on the polls for one chunk's ready flag (about 0.1 s); a workgroup
+// that ever exhausts it stops waiting for the rest of the launch, so a launch
+// always ends.
+constexpr int kReadyPollLimit = 1 << 16;
 
 // Waves per state-chain workgroup.  Four: one per SIMD.  (Eight waves with
 // one output tile each measured 1.4x slower on MI355X: every wave then reads
@@ -327,8 +340,8 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     cstride = C * 16;
     cbytes = (uint32_t)NC * cstride;
   } else if (cw == 1) {
-    cbase = reinterpret_cast<const char*>(a.pdg) + ((size_t)slot * nch + (size_t)chain * NC) * (C + 4) * 4;
-    cstride = (C + 4) * 4;
+    cbase = reinterpret_cast<const char*>(a.pdg) + ((size_t)slot * nch + (size_t)chain * NC) * pdg_stride(C) * 4;
+    cstride = pdg_stride(C) * 4;
     cbytes = (uint32_t)NC * cstride;
   } else {
     cbase = vbase;
@@ -371,6 +384,24 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     rtk[kc] = make_rsrc(trib, need ? tri_bytes : 0u);
     rpk[kc] = make_rsrc(pqkb, need ? tri_bytes : 0u);
   }
+  // the chunks' ready flags, when the preparation kernel runs concurrently
+  // (a.ready set; 0 = ready): a chunk's prepared operands are read only once
+  // its flag is 0.  Without a.ready the flags read as 0 (empty extent).
+  const rsrc_t rrdy = a.ready ? make_rsrc(a.ready + (size_t)chain * NC, (uint32_t)NC * 4u) : rnone;
+  bool rdy_gave_up = false;
+  auto ensure_ready = [&](uint32_t fl, int c) {
+    // first test outside any loop: a loop that reloads the tested value makes
+    // the compiler wait for every load in flight at its head
+    if (__builtin_amdgcn_readfirstlane(fl) != 0u && !rdy_gave_up) {
+      int n = 0;
+      for (; n < kReadyPollLimit; ++n) {
+        __builtin_amdgcn_s_sleep(2);
+        if (__builtin_amdgcn_readfirstlane(bload4_fresh(rrdy, (uint32_t)c * 4u)) == 0u) break;
+      }
+      rdy_gave_up = n == kReadyPollLimit;
+    }
+  };
+  auto ready_flag = [&](int c) { return bload4_fresh(rrdy, (uint32_t)c * 4u); };
   auto kq_at = [&](int c) { return (uint32_t)c * (C * HDB); };
   auto out_at = [&](int c) { return (uint32_t)c * (C * HOB); };
 
@@ -490,6 +521,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           for (int e = 0; e < 8; ++e) KT[(32 * ks + 8 * g4 + e) * TP + kq_row] = (MT)M::get(st.kf[ks], e);
       }
     }
+    ensure_ready(nx.rdy, cn);  // before any read of chunk cn's prepared operands
     load_coop(nx, cn);
     load_rows(nx.kf, rk, cn);
     readout(nx, s - 1, s > 0);  // the previous step's chunk (nx still holds its stage)
@@ -529,6 +561,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 
     // [B] Vnew = X + strict(Tinv) X
     load_rows(nx.qf, rq, cn);
+    nx.rdy = ready_flag(chunk_at(min(s + 3, NC - 1)));  // what nx is loaded with two steps on
     // bidirectional second visit of the next step's chunk: the other
     // direction's partial, loaded a step ahead (after this step's readout has
     // read nx's previous contents), checked at the end of the next step and
@@ -648,6 +681,12 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   F sA, sB;
   if (NC > 0) {
     const int c0 = chunk_at(0);
+    ensure_ready(ready_flag(c0), c0);
+    // steps 0 and 1 load chunks 1 and 2 into sB and sA.  These flag loads come
+    // first: the loop's first wait for them must find the operand loads below
+    // issued after them, as every later iteration does
+    sB.rdy = ready_flag(chunk_at(min(1, NC - 1)));
+    sA.rdy = ready_flag(chunk_at(min(2, NC - 1)));
     load_coop(sA, c0);
     load_rows(sA.kf, rk, c0);
     load_rows(sA.qf, rq, c0);
@@ -681,18 +720,18 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 }
 
 template <typename MT, int DK, int C, int NT, bool BI>
-hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream) {
+hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query) {
+  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&chain_kernel<MT, DK, C, NT, BI>));
   const int ntiles = a.dv / (16 * NT);
   const int nbh = (int)(a.B * a.H);
-  const int groups = (nbh + 7) / 8;
-  const unsigned nblocks = (unsigned)(groups * 8 * ntiles * (BI ? 2 : 1));
+  const unsigned nblocks = (unsigned)chain_blocks(nbh, a.dv, NT, BI ? 2 : 1);
   hipLaunchKernelGGL((chain_kernel<MT, DK, C, NT, BI>), dim3(nblocks), dim3(64 * ChainWaves<C, NT>::value), 0, stream,
                      a, rev_single, ntiles, nbh);
   return hipGetLastError();
 }
 
 #define GDN_INST_CHAIN(MT, DK, C, NT, BI) \
-  template hipError_t launch_chain<MT, DK, C, NT, BI>(const ScanArgs&, int, hipStream_t);
+  template hipError_t launch_chain<MT, DK, C, NT, BI>(const ScanArgs&, int, hipStream_t, hipFuncAttributes*);
 #define GDN_INST_CHAIN_D(MT, DK, C, NT) GDN_INST_CHAIN(MT, DK, C, NT, false) GDN_INST_CHAIN(MT, DK, C, NT, true)
 #define GDN_INST_CHAIN_N(MT, DK, C) GDN_INST_CHAIN_D(MT, DK, C, 1) GDN_INST_CHAIN_D(MT, DK, C, 2)
 GDN_INST_CHAIN_N(float, 64, 32)

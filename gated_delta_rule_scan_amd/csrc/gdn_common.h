@@ -110,10 +110,27 @@ __device__ __forceinline__ float bload4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
+// s_waitcnt immediate that waits for every vector memory access of the
+// wave (vmcnt 0; the other counters at their maxima)
+constexpr int kWaitVmem = 0x0F70;
+
 __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, f32x4 x) {
   u32x4 v;
   __builtin_memcpy(&v, &x, 16);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// Stores with the agent-scope cache policy (sc1): written through this XCD's
+// L2 cache, so once the store counter has drained they are visible to every
+// XCD of the device without a cache write-back.
+constexpr int kAgentScope = 16;
+__device__ __forceinline__ void bstore16_agent(rsrc_t r, uint32_t off, f32x4 x) {
+  u32x4 v;
+  __builtin_memcpy(&v, &x, 16);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kAgentScope);
+}
+__device__ __forceinline__ void bstore4_agent(rsrc_t r, uint32_t off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, (int)off, 0, kAgentScope);
 }
 
 // A matrix-core fragment (8 consecutive elements) at byte offset `off`.
@@ -139,18 +156,26 @@ __device__ __forceinline__ typename Mma<MT>::frag bload_frag(rsrc_t r, uint32_t 
 //                             the diagonal; strictly-lower part = forward,
 //                             strictly-upper part = reverse
 //   sc   [dirs][NBH*NC][C] float4 : {beta, e^g rk, e^g rq, e^(gn-g) rk}
-//   pdg  [dirs][NBH*NC][C+4] float : per token, the part of the self term
+//   pdg  [dirs][NBH*NC][PDS] float : per token, the part of the self term
 //                             q^_t.k^_t that the operand type of pqk drops
 //                             (x - MT(x); zero for fp32 operands), then
 //                             e^(gn) (the chunk's total decay) and three
-//                             zeros, so one chunk record is a whole number of
-//                             16-byte pieces
+//                             zeros (C + 4 floats: whole 16-byte pieces),
+//                             padded to PDS = pdg_stride(C) floats so that no
+//                             128-byte cache line holds two chunks' records
+//   rdy  [NBH][NC] uint32 : 1 once the preparation kernel's outputs for the
+//                             chunk (and its output fill) are in place; the
+//                             state chain waits for it when the two kernels
+//                             run concurrently
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t tri, pqk, sc, pdg, total;
+  size_t tri, pqk, sc, pdg, rdy, total;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Floats per pdg chunk record: C + 4, rounded up to a whole 128-byte line.
+__host__ __device__ constexpr int pdg_stride(int C) { return (C + 4 + 31) / 32 * 32; }
 
 static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_t mt_bytes) {
   WsLayout L;
@@ -159,7 +184,8 @@ static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_
   L.tri = off; off = align_up(off + nch * C * C * mt_bytes, 256);
   L.pqk = off; off = align_up(off + nch * C * C * mt_bytes, 256);
   L.sc = off;  off = align_up(off + (size_t)dirs * nch * C * 16, 256);
-  L.pdg = off; off = align_up(off + (size_t)dirs * nch * (C + 4) * 4, 256);
+  L.pdg = off; off = align_up(off + (size_t)dirs * nch * pdg_stride(C) * 4, 256);
+  L.rdy = off; off = align_up(off + nch * 4, 256);
   L.total = off;
   return L;
 }
@@ -178,6 +204,7 @@ struct ScanArgs {
   void* pqk;
   float4* sc;
   float* pdg;
+  unsigned* ready;     // rdy, above
   int64_t B, T, H, NC;
   int dv;
   int fwd_on, rev_on;  // which directions are computed

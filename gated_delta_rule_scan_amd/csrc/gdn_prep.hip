@@ -72,8 +72,25 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int64_t c = blockIdx.x;
-  const int64_t bh = blockIdx.y;
+  // Workgroups are numbered in the order the state chain consumes the
+  // chunks (a bidirectional scan takes both ends first), and each (batch,
+  // head) sequence's chunks go to the XCD its state-chain workgroups run on
+  // (consecutive ids are dealt round-robin over the eight XCDs).
+  const int nbh = (int)(a.B * a.H), G = (nbh + 7) / 8;
+  const int id = blockIdx.x;
+  const int64_t bh = (int64_t)((id >> 3) % G) * 8 + (id & 7);
+  const int order = (id >> 3) / G;  // position in the consumption order
+  const int NCi = (int)a.NC;
+  int64_t c;
+  if (a.fwd_on && a.rev_on) {
+    const int J = (NCi + 1) / 2;  // even positions take chunks [0, J), odd ones [J, NC) from the end
+    const int j = order >> 1;
+    if ((order & 1) && j >= NCi - J) return;
+    c = (order & 1) ? NCi - 1 - j : j;
+  } else {
+    c = a.rev_on ? NCi - 1 - order : order;
+  }
+  if (bh >= nbh) return;
   const int64_t b = bh / a.H, h = bh % a.H;
   const int64_t T = a.T, H = a.H, B = a.B;
   const int64_t t0 = c * C;
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     const float fn = __uint_as_float(0xFFFFFFFFu);
     const f32x4 fill = f32x4{fn, fn, fn, fn};
     for (int p = tid; p < (C << sh); p += 256)
-      bstore16(ro, (uint32_t)(p >> sh) * orow + (uint32_t)(p & ((1 << sh) - 1)) * 16u, fill);
+      bstore16_agent(ro, (uint32_t)(p >> sh) * orow + (uint32_t)(p & ((1 << sh) - 1)) * 16u, fill);
   }
   __syncthreads();
 
@@ -294,11 +311,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       const bool in = tok < nrows;
       const float g = s_g[dir][tok], gl = s_g[dir][dir == 0 ? C - 1 : 0];
       const float eg = exp2f(g);
-      a.sc[(slot * nch + cid) * C + tok] =
-          in ? make_float4(s_bt[dir][tok], eg * rk, eg * rq, exp2f(gl - g) * rk) : make_float4(0.f, 0.f, 0.f, 0.f);
-      float* pd = a.pdg + ((size_t)slot * nch + cid) * (C + 4);
-      pd[tok] = self - (float)self_mt;
-      if (tok < 4) pd[C + tok] = tok == 0 ? exp2f(gl) : 0.f;
+      const rsrc_t rs = make_rsrc(a.sc + (slot * nch + cid) * C, C * 16);
+      bstore16_agent(rs, tok * 16, in ? f32x4{s_bt[dir][tok], eg * rk, eg * rq, exp2f(gl - g) * rk} : f32x4{0.f, 0.f, 0.f, 0.f});
+      const rsrc_t rp = make_rsrc(a.pdg + ((size_t)slot * nch + cid) * pdg_stride(C), (C + 4) * 4);
+      bstore4_agent(rp, tok * 4, self - (float)self_mt);
+      if (tok < 4) bstore4_agent(rp, (C + tok) * 4, tok == 0 ? exp2f(gl) : 0.f);
     }
   }
   __syncthreads();
@@ -362,8 +379,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   // ---- both triangles to the workspace, 16 bytes per store ----
   {
     constexpr int EPS = 16 / (int)sizeof(MT);
-    MT* tri = static_cast<MT*>(a.tri) + cid * C * C;
-    MT* pqk = static_cast<MT*>(a.pqk) + cid * C * C;
+    const rsrc_t rt = make_rsrc(static_cast<MT*>(a.tri) + cid * C * C, C * C * (int)sizeof(MT));
+    const rsrc_t rp = make_rsrc(static_cast<MT*>(a.pqk) + cid * C * C, C * C * (int)sizeof(MT));
     for (int p = tid; p < C * C / EPS; p += 256) {
       const int r = (p * EPS) / C, c0 = (p * EPS) % C;
       MT tv[EPS], pv[EPS];
@@ -374,20 +391,48 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
         tv[e] = (MT)(keep ? Ti[r * LP + col] : 0.f);
         pv[e] = (keep || col == r) ? Pst[r * PP + col] : (MT)0.f;
       }
-      __builtin_memcpy(tri + p * EPS, tv, 16);
-      __builtin_memcpy(pqk + p * EPS, pv, 16);
+      f32x4 t16, p16;
+      __builtin_memcpy(&t16, tv, 16);
+      __builtin_memcpy(&p16, pv, 16);
+      bstore16_agent(rt, p * 16, t16);
+      bstore16_agent(rp, p * 16, p16);
     }
+  }
+
+  // ---- publish: every store above is agent-scope (written through this
+  // XCD's L2: the state chain may run on another XCD, whose L2 misses on
+  // these lines -- none of them is read before the flag, and no cache line
+  // holds two chunks' data).  Once each wave's stores have drained, the
+  // chunk's ready flag ----
+  if (a.ready) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(a.ready + cid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
-template <typename MT, int DK, int C>
-hipError_t launch_prep(const ScanArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)a.NC, (unsigned)(a.B * a.H));
-  hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C>), grid, dim3(256), 0, stream, a);
+__global__ __launch_bounds__(256) void clear_ready_kernel(unsigned* ready, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) ready[i] = 1u;  // pending
+}
+
+hipError_t launch_clear_ready(unsigned* ready, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(clear_ready_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, ready, n);
   return hipGetLastError();
 }
 
-#define GDN_INST_PREP(MT, DK, C) template hipError_t launch_prep<MT, DK, C>(const ScanArgs&, hipStream_t);
+template <typename MT, int DK, int C>
+hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes* query) {
+  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&chunk_prep_kernel<MT, DK, C>));
+  const int64_t G = (a.B * a.H + 7) / 8;
+  const int64_t slots = (a.fwd_on && a.rev_on) ? 2 * ((a.NC + 1) / 2) : a.NC;
+  hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C>), dim3((unsigned)(slots * G * 8)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+#define GDN_INST_PREP(MT, DK, C) \
+  template hipError_t launch_prep<MT, DK, C>(const ScanArgs&, hipStream_t, hipFuncAttributes*);
 GDN_INST_PREP(float, 64, 32)
 GDN_INST_PREP(float, 64, 64)
 GDN_INST_PREP(float, 128, 32)

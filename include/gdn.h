@@ -42,17 +42,23 @@
  * dirs = 2 for GDN_DIR_BIDIRECTIONAL, else 1 (slot 0 then holds the single
  * direction's gates and states).
  *
- * Ownership and execution: every pointer is caller-owned device memory.  The
- * library allocates nothing, keeps no state between calls, does not
- * synchronise and reads no environment variables, so a call can be captured
- * in a HIP graph.  All work is enqueued on `stream` (NULL: the default stream)
- * and completes asynchronously.  state_in == state_out is allowed (in-place
- * streaming carry); any other overlap between `out`, the state buffers, the
- * workspace and the inputs is rejected.  Results are bitwise deterministic for
- * fixed inputs and chunk size: the only atomics are the two fp32 adds that
- * sum the forward and reverse readouts of a bidirectional scan into the
- * zeroed output, and two addends onto zero give the same sum in either
- * order.  The value-tile width changes the schedule, never the arithmetic.
+ * Ownership and execution: every pointer is caller-owned device memory; the
+ * library allocates no device memory, does not synchronise and reads no
+ * environment variables.  The work is ordered on `stream` (NULL: the default
+ * stream) and completes asynchronously.  For large problems the chunk
+ * preparation runs concurrently with the state chain, on a library stream
+ * forked from `stream` and joined back to it with events (one stream and two
+ * events per device, created on first use and kept until the process ends):
+ * the work still starts after earlier work on `stream`, later work on
+ * `stream` still waits for all of it, and a HIP graph capture of `stream`
+ * takes both branches.  GDN_OPT_SERIAL keeps everything on `stream`.
+ * state_in == state_out is allowed (in-place streaming carry); any other
+ * overlap between `out`, the state buffers, the workspace and the inputs is
+ * rejected.  Results are bitwise deterministic for fixed inputs and chunk
+ * size, concurrent or not: there are no atomic reductions (the second visit
+ * of a chunk in a bidirectional scan adds the stored readout of the first
+ * visit in a fixed order).  The value-tile width changes the schedule, never
+ * the arithmetic.
  *
  * Errors: argument problems are reported before anything is enqueued and
  * leave every output untouched.  GDN_ERR_HIP reports a failed launch; faults
@@ -88,6 +94,11 @@ typedef enum {
   GDN_DTYPE_BF16 = 1
 } gdn_dtype_t;
 
+/* Bits of gdn_problem_t.options. */
+typedef enum {
+  GDN_OPT_SERIAL = 1        /* run both kernels one after the other on `stream` */
+} gdn_option_t;
+
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
  * chunk in {0 (= 64), 32, 64}; dv_tile in {0, 16, 32} (0: 32 when 16-wide
  * state-chain workgroups would outnumber the compute units of the current
@@ -99,14 +110,15 @@ typedef struct {
   int32_t dtype;            /* gdn_dtype_t: type of q, k, v */
   int32_t chunk;            /* tokens per chunk of the chunked evaluation */
   int32_t dv_tile;          /* value columns per workgroup of the state chain */
-  int32_t reserved;         /* must be 0 */
+  int32_t options;          /* 0 or GDN_OPT_SERIAL; other bits are invalid */
   void* workspace;          /* caller-owned device memory, 256-byte aligned */
   size_t workspace_bytes;
   void* stream;             /* hipStream_t; NULL = default stream */
-  void* timing_events;      /* NULL, or hipEvent_t[3] recorded on `stream`
-                               before the chunk-preparation kernel, between the
-                               two kernels and after the state-chain kernel
-                               (per-kernel timing; caller-owned events) */
+  void* timing_events;      /* NULL, or hipEvent_t[4] (caller-owned): recorded
+                               before and after the chunk-preparation kernel on
+                               the stream it runs on, then before and after the
+                               state-chain kernel on `stream` (per-kernel
+                               timing) */
 } gdn_problem_t;
 
 /* Bytes of workspace gdn_forward needs for this problem and direction
