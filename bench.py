@@ -165,6 +165,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true", help="keep the preparation pass before the chain (no overlap)")
+    ap.add_argument("--no-erase", action="store_true",
+                    help="time the erase-free variant (gated linear attention, GDN_OPT_NO_ERASE) instead of the delta rule")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -203,7 +205,7 @@ def main() -> int:
     def step(ev_ptr=None):
         gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction, chunk=args.chunk,
                     dv_tile=args.dv_tile, out=out, state_out=s_out, workspace=ws, timing_events=ev_ptr,
-                    serial=args.serial)
+                    serial=args.serial, erase=not args.no_erase)
 
     for _ in range(args.warmup):
         step()
@@ -260,6 +262,7 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                    "direction": w.direction, "chunk": C, "dv_tile": args.dv_tile or "auto",
                    "prep": "concurrent with the chain" if concurrent else "before the chain",
+                   "operator": "erase-free (gated linear attention)" if args.no_erase else "gated delta rule",
                    "inputs": "seeded synthetic video-latent-shaped (synth.WORKLOADS)"},
         "tflops": tflops,
         "mfma_frac": tflops / peak_mfma,

@@ -34,6 +34,7 @@ GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
 
 GDN_OPT_SERIAL = 1
+GDN_OPT_NO_ERASE = 2
 
 EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_status_string", "gdn_version")
 
@@ -113,7 +114,7 @@ def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd"
 
 def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chunk: int = 0, dv_tile: int = 0,
             out=None, state_out=None, workspace=None, want_state: bool = True, stream=None,
-            timing_events: Optional[int] = None, serial: bool = False) -> Tuple:
+            timing_events: Optional[int] = None, serial: bool = False, erase: bool = True) -> Tuple:
     """Run the scan on torch CUDA tensors (layouts of include/gdn.h).
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv] (float32 or bfloat16, same dtype);
@@ -122,6 +123,8 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     passed as the same tensor as ``state_in`` for an in-place carry.
     ``serial`` keeps both kernels on ``stream`` (GDN_OPT_SERIAL); otherwise the
     library may run the chunk preparation concurrently on its own stream.
+    ``erase=False`` selects the erase-free variant (GDN_OPT_NO_ERASE: gated
+    linear attention with write strength beta).
     ``timing_events``: address of four caller-owned hipEvent_t (see gdn.h).
     """
     import torch
@@ -160,7 +163,7 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     prob.workspace_bytes = workspace.numel() if workspace is not None else 0
     prob.stream = s.cuda_stream
     prob.timing_events = timing_events
-    prob.options = GDN_OPT_SERIAL if serial else 0
+    prob.options = (GDN_OPT_SERIAL if serial else 0) | (0 if erase else GDN_OPT_NO_ERASE)
     st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                      None if state_in is None else state_in.data_ptr(),
                      None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])

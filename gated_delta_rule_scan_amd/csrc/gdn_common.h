@@ -210,6 +210,7 @@ struct ScanArgs {
   int fwd_on, rev_on;  // which directions are computed
   int dirs;            // number of computed directions (slots)
   int zero_out;        // the preparation kernel fills `out` with the "not written yet" pattern (bidirectional)
+  int erase;           // 1: delta rule; 0: erase-free variant (no -beta k k^T term: L = 0, T = I)
 };
 
 }  // namespace gdn

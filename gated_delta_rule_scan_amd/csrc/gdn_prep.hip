@@ -227,6 +227,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   __syncthreads();  // q/k staging area is reused below
 
   // ---- gated, scaled triangles: L and the decayed Q^K^^T into LDS ----
+  // (the erase-free variant has no erase term: L = 0, so (I + L)^{-1} = I)
+  const float erase_w = a.erase ? 1.f : 0.f;
   // Lane (l16, g4) of tile (ti, tj) holds column 16 tj + l16 of rows
   // 16 ti + 4 g4 + i.  Below the diagonal the forward direction's entries,
   // above it the reverse direction's; the diagonal (the self terms) is
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
         // unused, so it never overflows); below 2^-126 it may flush to zero
         const float gd = fmaf(wf, gf[i] - gfc, wr * (gr[i] - grc));
         const float e = __builtin_amdgcn_exp2f(gd);
-        const float lm = e * fmaf(wf, bf[i], wr * br[i]);
+        const float lm = e * fmaf(wf, bf[i], wr * br[i]) * erase_w;
         const float pm = e * (wf + wr);
         Lm[r * LP + col] = (rkr[i] * rkc) * accG[j][i] * lm;
         Pst[r * PP + col] = (MT)((rqr[i] * rkc) * accP[j][i] * pm);
@@ -312,7 +314,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       const float g = s_g[dir][tok], gl = s_g[dir][dir == 0 ? C - 1 : 0];
       const float eg = exp2f(g);
       const rsrc_t rs = make_rsrc(a.sc + (slot * nch + cid) * C, C * 16);
-      bstore16_agent(rs, tok * 16, in ? f32x4{s_bt[dir][tok], eg * rk, eg * rq, exp2f(gl - g) * rk} : f32x4{0.f, 0.f, 0.f, 0.f});
+      // {beta, e^g rk (erase term of the pseudo-values; 0 without it), e^g rq, e^(gn-g) rk}
+      bstore16_agent(rs, tok * 16,
+                     in ? f32x4{s_bt[dir][tok], a.erase ? eg * rk : 0.f, eg * rq, exp2f(gl - g) * rk} : f32x4{0.f, 0.f, 0.f, 0.f});
       const rsrc_t rp = make_rsrc(a.pdg + ((size_t)slot * nch + cid) * pdg_stride(C), (C + 4) * 4);
       bstore4_agent(rp, tok * 4, self - (float)self_mt);
       if (tok < 4) bstore4_agent(rp, (C + tok) * 4, tok == 0 ? exp2f(gl) : 0.f);

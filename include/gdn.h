@@ -96,7 +96,12 @@ typedef enum {
 
 /* Bits of gdn_problem_t.options. */
 typedef enum {
-  GDN_OPT_SERIAL = 1        /* run both kernels one after the other on `stream` */
+  GDN_OPT_SERIAL = 1,       /* run both kernels one after the other on `stream` */
+  GDN_OPT_NO_ERASE = 2      /* the erase-free variant: S_t = a_t S_{t-1} + beta_t v_t k^_t^T,
+                               i.e. gated linear attention with per-token write strength
+                               beta (SANA-Video 2.0 review: the hybrid's linear layers are
+                               gated linear attention, and its "Future work" relates them to
+                               the delta rule by dropping the delta-rule update) */
 } gdn_option_t;
 
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
@@ -110,7 +115,8 @@ typedef struct {
   int32_t dtype;            /* gdn_dtype_t: type of q, k, v */
   int32_t chunk;            /* tokens per chunk of the chunked evaluation */
   int32_t dv_tile;          /* value columns per workgroup of the state chain */
-  int32_t options;          /* 0 or GDN_OPT_SERIAL; other bits are invalid */
+  int32_t options;          /* OR of gdn_option_t bits (0: delta rule, chosen schedule);
+                               other bits are invalid */
   void* workspace;          /* caller-owned device memory, 256-byte aligned */
   size_t workspace_bytes;
   void* stream;             /* hipStream_t; NULL = default stream */

@@ -30,8 +30,9 @@
  *
  *   With erase == 0 the "- beta k k^T" erase term is dropped (S <- a S +
  *   beta v k^T): the plain gated linear attention that results from removing
- *   the delta-rule update (SANA-Video 2.0 review, "Future work").  That mode
- *   only exists to pin the oracle against brute-force linear attention.
+ *   the delta-rule update (SANA-Video 2.0 review, "Future work").  It pins the
+ *   oracle against brute-force linear attention and is the reference of the
+ *   library's erase-free variant.
  *
  * Layouts (all contiguous, row-major):
  *   q, k      [B, T, H, dk]   float (exact values of the inputs; bf16 widened)

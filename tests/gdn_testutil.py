@@ -20,7 +20,7 @@ def to_torch(x, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
-def run_gpu(inputs, direction, chunk=0, dv_tile=0, state_in="use", want_state=True, serial=False):
+def run_gpu(inputs, direction, chunk=0, dv_tile=0, state_in="use", want_state=True, serial=False, erase=True):
     import torch
 
     import gated_delta_rule_scan_amd as gdn
@@ -28,7 +28,7 @@ def run_gpu(inputs, direction, chunk=0, dv_tile=0, state_in="use", want_state=Tr
     d = {k: to_torch(v) for k, v in inputs.items()}
     s_in = d["state_in"] if state_in == "use" else state_in
     out, s_out = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s_in, direction, chunk=chunk,
-                             dv_tile=dv_tile, want_state=want_state, serial=serial)
+                             dv_tile=dv_tile, want_state=want_state, serial=serial, erase=erase)
     torch.cuda.synchronize()
     return out.cpu().numpy(), (None if s_out is None else s_out.cpu().numpy())
 

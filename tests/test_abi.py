@@ -43,11 +43,11 @@ def test_problem_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "gdn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %d\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %d %d\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
          offsetof(gdn_problem_t, chunk), offsetof(gdn_problem_t, dv_tile), offsetof(gdn_problem_t, options),
          offsetof(gdn_problem_t, workspace),
          offsetof(gdn_problem_t, workspace_bytes), offsetof(gdn_problem_t, stream),
-         offsetof(gdn_problem_t, timing_events), (int)GDN_OPT_SERIAL);
+         offsetof(gdn_problem_t, timing_events), (int)GDN_OPT_SERIAL, (int)GDN_OPT_NO_ERASE);
   return 0;
 }
 """)
@@ -56,7 +56,7 @@ int main(void) {
     got = [int(x) for x in subprocess.check_output([str(exe)], text=True).split()]
     P = gdn.gdn_problem_t
     want = [ctypes.sizeof(P), P.dtype.offset, P.chunk.offset, P.dv_tile.offset, P.options.offset, P.workspace.offset,
-            P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset, gdn.GDN_OPT_SERIAL]
+            P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset, gdn.GDN_OPT_SERIAL, gdn.GDN_OPT_NO_ERASE]
     assert got == want
 
 
@@ -170,7 +170,7 @@ def test_overlaps_are_invalid():
 def test_bad_problem_fields():
     p, a = _valid()
     assert _call(p, a, direction=5) == gdn.GDN_ERR_INVALID_ARGUMENT
-    p.options = 2  # undefined option bit
+    p.options = 4  # undefined option bit
     assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
     p, a = _valid(dk=96)
     assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED

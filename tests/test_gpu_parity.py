@@ -84,3 +84,29 @@ def test_concurrent_preparation_matches_serial(direction, dtype):
     ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction)
     check(o_con, ref, TOL[dtype], f"out {w}")
     check(s_con, ref_s, TOL[dtype], f"state {w}")
+
+
+@pytest.mark.parametrize("direction", ["fwd", "rev", "bi"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_erase_free_variant(direction, dtype):
+    """GDN_OPT_NO_ERASE: S_t = a_t S_{t-1} + beta_t v_t k^_t^T (gated linear
+    attention), against the oracle's erase-off mode, which is pinned to
+    brute-force gated linear attention."""
+    w = _case(dtype, direction, T=333, H=3, dk=64, dv=128, state_std=0.05, seed=14)
+    x = synth.generate(w)
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction,
+                                erase=False)
+    out, s = run_gpu(x, direction, erase=False)
+    e1 = check(out, ref, TOL[dtype], f"out {w} erase-free")
+    e2 = check(s, ref_s, TOL[dtype], f"state {w} erase-free")
+    print(f"\nerase-free {dtype} {direction}: out {e1:.2e} state {e2:.2e}", flush=True)
+
+
+def test_erase_free_variant_concurrent_matches_serial():
+    w = _case("bf16", "fwd", T=64 * 40 + 5, H=4, dk=128, dv=128, state_std=0.05, seed=15)
+    x = synth.generate(w)
+    o1, s1 = run_gpu(x, "fwd", serial=True, erase=False)
+    o2, s2 = run_gpu(x, "fwd", erase=False)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "fwd", erase=False)
+    check(o2, ref, TOL["bf16"], "out erase-free concurrent")
