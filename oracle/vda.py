@@ -1,0 +1,96 @@
+"""Double-precision oracle for the frame-wise delta operator (Video Delta Attention).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): the test suite, the
+smoke check and the benchmark's CPU-baseline leg may use it; the GPU library
+shares no code with it.
+
+Definition ("Video DeltaNet", "Key Contributions" item 2, and "Methodology in
+Plain English"): the memory is written once per latent frame, as the state
+that stays closest to the decayed memory while fitting all of the frame's
+key-value associations,
+
+    S_t = argmin_S  ||S - Sbar_t||_F^2 + sum_{i in frame t} beta_i ||S k^_i - v_i||^2,
+    Sbar_t = a_t S_{t-1},
+
+whose closed form is the one the page gives,
+
+    S_t = (Sbar_t + B_t) (I + A_t)^{-1},
+    A_t = sum_i beta_i k^_i k^_i^T  (dk x dk),   B_t = sum_i beta_i v_i k^_i^T  (dv x dk).
+
+Readings taken where the page is silent (listed in the design doc as well):
+  * q and k are normalised as in the token scan: x^ = x / max(|x|_2, 1e-6);
+  * one decay a_t = exp(log_alpha_t) per frame, one write strength beta_i per
+    token (beta >= 0 keeps A_t positive semi-definite);
+  * every token of frame t reads the state after its own frame's write,
+    o_i = S_t q^_i (as the token scan's readout includes the current token);
+  * frames are consecutive runs of ``frame`` tokens, the last one possibly
+    shorter; the reverse scan visits the frames last to first; the
+    bidirectional output is the sum of both readouts, each direction with its
+    own gates and initial state.
+
+The solve is a library routine (numpy.linalg.solve on the symmetric system);
+everything else is the definition written out.  Pins: tests/test_vda_oracle_pins.py.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import as_f32
+
+EPS = 1e-6
+
+
+def _normalise_rows(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, EPS)
+
+
+def frame_update(S_prev: np.ndarray, a: float, kh: np.ndarray, v: np.ndarray, beta: np.ndarray) -> np.ndarray:
+    """One frame's write: (a S_prev + B) (I + A)^{-1}; kh [n, dk] unit rows, v [n, dv], beta [n]."""
+    dk = kh.shape[1]
+    A = (kh * beta[:, None]).T @ kh
+    Bm = (v * beta[:, None]).T @ kh
+    R = a * S_prev + Bm
+    # S (I + A) = R  <=>  (I + A) S^T = R^T   (I + A symmetric)
+    return np.linalg.solve(np.eye(dk) + A, R.T).T
+
+
+def forward(q, k, v, log_alpha, beta, state_in: Optional[np.ndarray], direction: str, frame: int,
+            return_states: bool = False):
+    """q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bf16 bit patterns); log_alpha
+    [dirs,B,NF,H] (one per frame); beta [dirs,B,T,H]; state_in [dirs,B,H,dv,dk]
+    or None.  Returns (out [B,T,H,dv], state_out [dirs,B,H,dv,dk]) in float64,
+    plus the state after every frame [dirs,B,H,NF,dv,dk] if ``return_states``."""
+    q = as_f32(q).astype(np.float64)
+    k = as_f32(k).astype(np.float64)
+    v = as_f32(v).astype(np.float64)
+    la = np.asarray(log_alpha, dtype=np.float64)
+    bt = np.asarray(beta, dtype=np.float64)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dirs = 2 if direction == "bi" else 1
+    NF = (T + frame - 1) // frame
+    out = np.zeros((B, T, H, dv))
+    s_out = np.zeros((dirs, B, H, dv, dk))
+    states = np.zeros((dirs, B, H, NF, dv, dk)) if return_states else None
+    qh = _normalise_rows(q)
+    kh = _normalise_rows(k)
+    for slot in range(dirs):
+        rev = direction == "rev" or (direction == "bi" and slot == 1)
+        for b in range(B):
+            for h in range(H):
+                S = np.zeros((dv, dk)) if state_in is None else np.asarray(state_in, np.float64)[slot, b, h].copy()
+                order = range(NF - 1, -1, -1) if rev else range(NF)
+                for f in order:
+                    t0, t1 = f * frame, min(T, (f + 1) * frame)
+                    S = frame_update(S, float(np.exp(la[slot, b, f, h])), kh[b, t0:t1, h], v[b, t0:t1, h],
+                                     bt[slot, b, t0:t1, h])
+                    out[b, t0:t1, h] += qh[b, t0:t1, h] @ S.T
+                    if return_states:
+                        states[slot, b, h, f] = S
+                s_out[slot, b, h] = S
+    if return_states:
+        return out, s_out, states
+    return out, s_out

@@ -40,6 +40,7 @@ _lib = None
 # stream identifiers (one independent random stream per tensor)
 STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
 STREAM_BETA, STREAM_LOG_ALPHA, STREAM_STATE = 10, 20, 30
+STREAM_FRAME_LOG_ALPHA = 40
 
 
 def build(force: bool = True) -> str:
@@ -157,6 +158,19 @@ def generate(w: Workload, T: Optional[int] = None) -> dict:
         state_in = np.stack([_scalars(w.seed, STREAM_STATE + d, n, 0, w.state_std) for d in range(w.dirs)])
         state_in = state_in.reshape(w.dirs, B, H, dv, dk)
     return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, state_in=state_in)
+
+
+def generate_frames(w: Workload, frame: int, T: Optional[int] = None) -> dict:
+    """Inputs of the frame-wise operator for workload ``w`` with ``frame``
+    tokens per frame: as ``generate`` (per-token beta), but one log-decay per
+    frame, log_alpha [dirs,B,NF,H], drawn with the workload's recipe."""
+    x = generate(w, T)
+    T = x["q"].shape[1]
+    NF = (T + frame - 1) // frame
+    n = w.B * NF * w.H
+    la = np.stack([_scalars(w.seed, STREAM_FRAME_LOG_ALPHA + d, n, 2, w.la_shift) for d in range(w.dirs)])
+    x["log_alpha"] = la.reshape(w.dirs, w.B, NF, w.H)
+    return x
 
 
 def normals(seed: int, stream: int, shape, std: float = 1.0) -> np.ndarray:

@@ -1,0 +1,140 @@
+"""Pins of the frame-wise delta operator's oracle (oracle/vda.py), CPU only.
+
+Each pin checks the oracle against something other than its own formula:
+  * one token per frame: the closed form reduces (Sherman-Morrison) to the
+    token delta rule with write strength beta / (1 + beta) -- checked against
+    the independent C token oracle;
+  * least squares: every frame's state has a zero gradient of the objective
+    the page states ("Video DeltaNet", "Methodology in Plain English": stay
+    close to the decayed memory while fitting the frame's associations);
+  * hand-worked frames: orthonormal keys give a diagonal inverse, and two
+    identical keys average their values with the decayed memory;
+  * order of the tokens inside a frame does not matter;
+  * non-expansiveness ("Key Contributions" item 2) even where the additive
+    per-token update I - A_t expands ("Main Findings": eigenvalues leave
+    [-1, 1] once lambda_max(A_t) > 2);
+  * beta = 0 is pure decay; reverse is flip-forward-flip; bidirectional is the
+    sum of the two scans.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import vda
+
+
+def _inputs(T=90, frame=30, H=2, d=16, direction="fwd", shift=-3.0, std=0.1, seed=1):
+    w = synth.Workload("vda", 1, H, T, d, d, "f32", direction, shift, std, seed)
+    return synth.generate_frames(w, frame)
+
+
+def test_one_token_frames_equal_the_token_delta_rule():
+    for direction in ("fwd", "rev", "bi"):
+        x = _inputs(T=40, frame=1, direction=direction)
+        o_vda, s_vda = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction, 1)
+        b = x["beta"].astype(np.float64)
+        b2 = (b / (1.0 + b)).astype(np.float32)
+        # per-token gates: a frame of one token has its token's decay
+        o_tok, s_tok = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], b2, x["state_in"], direction)
+        # the transformed beta is rounded to fp32 for the C oracle: agreement to that precision
+        assert np.max(np.abs(o_vda - o_tok)) <= 1e-6 * max(1.0, np.max(np.abs(o_tok)))
+        assert np.max(np.abs(s_vda - s_tok)) <= 1e-6 * max(1.0, np.max(np.abs(s_tok)))
+
+
+def test_every_frame_state_minimises_the_objective():
+    x = _inputs(T=100, frame=32, direction="fwd")
+    _, _, states = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "fwd", 32,
+                               return_states=True)
+    q, k, v = (oracle.as_f32(x[n]).astype(np.float64) for n in ("q", "k", "v"))
+    kh = k / np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), 1e-6)
+    for h in range(2):
+        S_prev = x["state_in"][0, 0, h].astype(np.float64)
+        for f in range(states.shape[3]):
+            t0, t1 = 32 * f, min(100, 32 * (f + 1))
+            a = np.exp(float(x["log_alpha"][0, 0, f, h]))
+            S = states[0, 0, h, f]
+            grad = S - a * S_prev
+            for i in range(t0, t1):
+                r = S @ kh[0, i, h] - v[0, i, h]
+                grad += float(x["beta"][0, 0, i, h]) * np.outer(r, kh[0, i, h])
+            assert np.max(np.abs(grad)) < 1e-10 * max(1.0, np.max(np.abs(S)))
+            S_prev = S
+
+
+def test_hand_worked_frames():
+    # dk = dv = 2, one frame of two tokens, a = 0.5, S_in = [[1, 2], [3, 4]]
+    S0 = np.array([[1.0, 2.0], [3.0, 4.0]])
+    v1, v2 = np.array([1.0, -1.0]), np.array([2.0, 0.5])
+    # orthonormal keys e1, e2 with beta 1 and 3: column j becomes (a S0[:, j] + beta_j v_j) / (1 + beta_j)
+    S = vda.frame_update(S0, 0.5, np.array([[1.0, 0.0], [0.0, 1.0]]), np.stack([v1, v2]), np.array([1.0, 3.0]))
+    want = np.stack([(0.5 * S0[:, 0] + v1) / 2.0, (0.5 * S0[:, 1] + 3.0 * v2) / 4.0], axis=1)
+    assert np.allclose(S, want, rtol=0, atol=1e-14)
+    # two identical keys e1 with beta 1: the fitted column is the mean of a S0[:, 0], v1 and v2;
+    # the orthogonal column keeps the decayed memory
+    S = vda.frame_update(S0, 0.5, np.array([[1.0, 0.0], [1.0, 0.0]]), np.stack([v1, v2]), np.array([1.0, 1.0]))
+    want = np.stack([(0.5 * S0[:, 0] + v1 + v2) / 3.0, 0.5 * S0[:, 1]], axis=1)
+    assert np.allclose(S, want, rtol=0, atol=1e-14)
+
+
+def test_token_order_inside_a_frame_does_not_matter():
+    x = _inputs(T=64, frame=32, direction="bi", seed=3)
+    o1, s1 = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", 32)
+    perm = np.concatenate([np.random.default_rng(0).permutation(32), 32 + np.random.default_rng(1).permutation(32)])
+    y = dict(x)
+    for n in ("q", "k", "v"):
+        y[n] = x[n][:, perm]
+    y["beta"] = x["beta"][:, :, perm]
+    o2, s2 = vda.forward(y["q"], y["k"], y["v"], y["log_alpha"], y["beta"], y["state_in"], "bi", 32)
+    assert np.allclose(s1, s2, rtol=0, atol=1e-12)
+    assert np.allclose(o1[:, perm], o2, rtol=0, atol=1e-12)
+
+
+def test_transition_is_non_expansive_where_additive_writes_expand():
+    rng = np.random.default_rng(5)
+    d, n = 8, 40
+    # keys bunched around one direction, beta = 1: lambda_max(A) well above 2
+    base = rng.standard_normal(d)
+    kh = base[None, :] + 0.2 * rng.standard_normal((n, d))
+    kh /= np.linalg.norm(kh, axis=1, keepdims=True)
+    A = kh.T @ kh
+    assert np.max(np.linalg.eigvalsh(A)) > 2.0
+    assert np.max(np.abs(np.linalg.eigvalsh(np.eye(d) - A))) > 1.0  # the additive form expands
+    # the operator's transition (v = 0): S -> a S (I + A)^{-1}, never larger in spectral norm
+    S = rng.standard_normal((d, d))
+    for a in (1.0, 0.7):
+        S1 = vda.frame_update(S, a, kh, np.zeros((n, d)), np.ones(n))
+        assert np.linalg.norm(S1, 2) <= a * np.linalg.norm(S, 2) + 1e-12
+
+
+def test_zero_beta_is_pure_decay():
+    x = _inputs(T=60, frame=20, direction="fwd", seed=4)
+    x["beta"] = np.zeros_like(x["beta"])
+    o, s = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "fwd", 20)
+    a_tot = np.exp(np.sum(x["log_alpha"][0, 0].astype(np.float64), axis=0))  # [H]
+    assert np.allclose(s[0, 0], x["state_in"][0, 0] * a_tot[:, None, None], rtol=1e-12, atol=0)
+    q = oracle.as_f32(x["q"]).astype(np.float64)
+    qh = q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-6)
+    a_first = np.exp(x["log_alpha"][0, 0, 0].astype(np.float64))
+    for h in range(2):
+        want = qh[0, :20, h] @ (a_first[h] * x["state_in"][0, 0, h].astype(np.float64)).T
+        assert np.allclose(o[0, :20, h], want, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("T,frame", [(90, 30), (64, 16)])
+def test_reverse_and_bidirectional(T, frame):
+    x = _inputs(T=T, frame=frame, direction="bi", seed=6)
+    o_bi, s_bi = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", frame)
+    sl = lambda a, i: a[i:i + 1]
+    o_f, s_f = vda.forward(x["q"], x["k"], x["v"], sl(x["log_alpha"], 0), sl(x["beta"], 0), sl(x["state_in"], 0),
+                           "fwd", frame)
+    o_r, s_r = vda.forward(x["q"], x["k"], x["v"], sl(x["log_alpha"], 1), sl(x["beta"], 1), sl(x["state_in"], 1),
+                           "rev", frame)
+    assert np.allclose(o_bi, o_f + o_r, rtol=0, atol=1e-12)
+    assert np.allclose(s_bi[0], s_f[0]) and np.allclose(s_bi[1], s_r[0])
+    # reverse = flip . forward . flip (T a multiple of the frame: frames map onto frames)
+    fl = lambda a, ax: np.ascontiguousarray(np.flip(a, axis=ax))
+    o_ff, s_ff = vda.forward(fl(x["q"], 1), fl(x["k"], 1), fl(x["v"], 1), fl(sl(x["log_alpha"], 1), 2),
+                             fl(sl(x["beta"], 1), 2), sl(x["state_in"], 1), "fwd", frame)
+    assert np.allclose(fl(o_ff, 1), o_r, rtol=0, atol=1e-12)
+    assert np.allclose(s_ff, s_r, rtol=0, atol=1e-12)
