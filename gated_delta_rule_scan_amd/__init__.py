@@ -36,7 +36,8 @@ GDN_DTYPE_BF16 = 1
 GDN_OPT_SERIAL = 1
 GDN_OPT_NO_ERASE = 2
 
-EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_status_string", "gdn_version")
+EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_vda_workspace_bytes", "gdn_vda_forward", "gdn_status_string",
+            "gdn_version")
 
 
 class gdn_problem_t(ctypes.Structure):
@@ -45,6 +46,17 @@ class gdn_problem_t(ctypes.Structure):
         ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("dv_tile", ctypes.c_int32), ("options", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("timing_events", ctypes.c_void_p),
+    ]
+
+
+class gdn_vda_problem_t(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("frame", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("options", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("timing_events", ctypes.c_void_p),
@@ -73,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.gdn_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32]
         L.gdn_forward.restype = ctypes.c_int
+        PV = ctypes.POINTER(gdn_vda_problem_t)
+        L.gdn_vda_workspace_bytes.argtypes = [PV, ctypes.c_int32]
+        L.gdn_vda_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_vda_forward.argtypes = [PV, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32]
+        L.gdn_vda_forward.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -90,6 +107,17 @@ def gdn_forward(problem: gdn_problem_t, q: int, k: int, v: int, log_alpha: int, 
     """Raw call with integer device pointers (None for NULL); returns the status."""
     return int(lib().gdn_forward(ctypes.byref(problem), q, k, v, log_alpha, beta, state_in, state_out, out,
                                  int(direction)))
+
+
+def gdn_vda_workspace_bytes(problem: gdn_vda_problem_t, direction: int) -> int:
+    return int(lib().gdn_vda_workspace_bytes(ctypes.byref(problem), int(direction)))
+
+
+def gdn_vda_forward(problem: gdn_vda_problem_t, q: int, k: int, v: int, log_alpha: int, beta: int,
+                    state_in: Optional[int], state_out: Optional[int], out: int, direction: int) -> int:
+    """Raw call of the frame-wise operator with integer device pointers; returns the status."""
+    return int(lib().gdn_vda_forward(ctypes.byref(problem), q, k, v, log_alpha, beta, state_in, state_out, out,
+                                     int(direction)))
 
 
 def gdn_status_string(status: int) -> str:
@@ -167,6 +195,59 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                      None if state_in is None else state_in.data_ptr(),
                      None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])
+    if st != GDN_OK:
+        raise GdnError(st)
+    return out, state_out
+
+
+def vda_forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", frame: int = 1560, out=None,
+                state_out=None, workspace=None, want_state: bool = True, stream=None,
+                timing_events: Optional[int] = None) -> Tuple:
+    """Frame-wise delta operator on torch CUDA tensors (layouts of include/gdn.h):
+    q, k [B,T,H,dk], v [B,T,H,dv]; log_alpha [dirs,B,NF,H] (one per frame of
+    ``frame`` tokens); beta [dirs,B,T,H]; state_in [dirs,B,H,dv,dk] or None.
+    Returns (out [B,T,H,dv] float32, state_out or None)."""
+    import torch
+
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dirs = 2 if direction == "bi" else 1
+    NF = (T + frame - 1) // frame
+    if q.dtype == torch.bfloat16:
+        dt = GDN_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = GDN_DTYPE_F32
+    else:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous CUDA tensors of one dtype")
+    if log_alpha.dtype != torch.float32 or not log_alpha.is_contiguous() or tuple(log_alpha.shape) != (dirs, B, NF, H):
+        raise ValueError(f"log_alpha must be contiguous float32 [{dirs},{B},{NF},{H}]")
+    if beta.dtype != torch.float32 or not beta.is_contiguous() or tuple(beta.shape) != (dirs, B, T, H):
+        raise ValueError(f"beta must be contiguous float32 [{dirs},{B},{T},{H}]")
+    if state_in is not None and (state_in.dtype != torch.float32 or not state_in.is_contiguous()
+                                 or tuple(state_in.shape) != (dirs, B, H, dv, dk)):
+        raise ValueError(f"state_in must be contiguous float32 [{dirs},{B},{H},{dv},{dk}]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
+    prob = gdn_vda_problem_t(B, T, H, dk, dv, frame, dt, 0, None, 0, None, None)
+    nbytes = gdn_vda_workspace_bytes(prob, DIRECTIONS[direction])
+    if nbytes == 0 and T > 0:
+        raise GdnError(GDN_ERR_UNSUPPORTED)
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    prob.workspace = workspace.data_ptr() if workspace is not None else None
+    prob.workspace_bytes = workspace.numel() if workspace is not None else 0
+    prob.stream = s.cuda_stream
+    prob.timing_events = timing_events
+    st = gdn_vda_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
+                         None if state_in is None else state_in.data_ptr(),
+                         None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])
     if st != GDN_OK:
         raise GdnError(st)
     return out, state_out

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_prep.hip", "gdn_chain.hip"]
+SOURCES = ["gdn_api.hip", "gdn_prep.hip", "gdn_chain.hip", "gdn_vda.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.

@@ -289,6 +289,101 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   return GDN_OK;
 }
 
+// ---- frame-wise delta operator ----
+namespace gdn {
+namespace {
+
+typedef hipError_t (*vda_fn)(const VdaArgs&, hipStream_t, hipEvent_t*);
+
+template <typename MT>
+vda_fn vda_for(int64_t dk, int64_t dv) {
+  if (dk == 64) return dv == 64 ? launch_vda<MT, 64, 64> : launch_vda<MT, 64, 128>;
+  return dv == 64 ? launch_vda<MT, 128, 64> : launch_vda<MT, 128, 128>;
+}
+
+gdn_status_t vda_plan(const gdn_vda_problem_t* p, int32_t direction, int* dirs, int64_t* NF, VdaLayout* L) {
+  if (!p) return GDN_ERR_INVALID_ARGUMENT;
+  if (direction < GDN_DIR_FORWARD || direction > GDN_DIR_BIDIRECTIONAL) return GDN_ERR_INVALID_ARGUMENT;
+  if (p->B < 1 || p->H < 1 || p->T < 0 || p->dk < 1 || p->dv < 1 || p->frame < 1) return GDN_ERR_INVALID_ARGUMENT;
+  if (p->options != 0) return GDN_ERR_INVALID_ARGUMENT;
+  if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+  if (!supported_dim(p->dk) || !supported_dim(p->dv)) return GDN_ERR_UNSUPPORTED;
+  if (p->T > ((int64_t)1 << 31) / 2) return GDN_ERR_UNSUPPORTED;
+  if ((p->T + 64) * p->H * (p->dk > p->dv ? p->dk : p->dv) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
+  *dirs = direction == GDN_DIR_BIDIRECTIONAL ? 2 : 1;
+  *NF = (p->T + p->frame - 1) / p->frame;
+  if ((int64_t)*dirs * p->B * p->H * *NF > ((int64_t)1 << 31) - 1) return GDN_ERR_UNSUPPORTED;  // grid size
+  *L = vda_layout(p->B * p->H, *NF, *dirs, p->dk, p->dv);
+  return GDN_OK;
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" size_t gdn_vda_workspace_bytes(const gdn_vda_problem_t* p, int32_t direction) {
+  int dirs = 0;
+  int64_t NF = 0;
+  VdaLayout L;
+  if (vda_plan(p, direction, &dirs, &NF, &L) != GDN_OK || p->T == 0) return 0;
+  return L.total;
+}
+
+extern "C" gdn_status_t gdn_vda_forward(const gdn_vda_problem_t* p, const void* q, const void* k, const void* v,
+                                        const float* log_alpha, const float* beta, const float* state_in,
+                                        float* state_out, float* out, int32_t direction) {
+  int dirs = 0;
+  int64_t NF = 0;
+  VdaLayout L;
+  gdn_status_t st = vda_plan(p, direction, &dirs, &NF, &L);
+  if (st != GDN_OK) return st;
+  const int64_t B = p->B, T = p->T, H = p->H, dk = p->dk, dv = p->dv;
+  const size_t es = p->dtype == GDN_DTYPE_BF16 ? 2 : 4;
+  const size_t n_qk = (size_t)(B * T * H * dk), n_v = (size_t)(B * T * H * dv);
+  const size_t n_la = (size_t)(dirs * B * NF * H), n_b = (size_t)(dirs * B * T * H), n_s = (size_t)(dirs * B * H * dv * dk);
+  if (T > 0) {
+    if (!q || !k || !v || !log_alpha || !beta || !out) return GDN_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return GDN_ERR_INVALID_ARGUMENT;
+    if (!aligned(log_alpha, 4) || !aligned(beta, 4)) return GDN_ERR_INVALID_ARGUMENT;
+    if (!p->workspace || !aligned(p->workspace, 256)) return GDN_ERR_INVALID_ARGUMENT;
+    if (p->workspace_bytes < L.total) return GDN_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16))) return GDN_ERR_INVALID_ARGUMENT;
+  const Range r_q = rng(q, n_qk * es), r_k = rng(k, n_qk * es), r_v = rng(v, n_v * es);
+  const Range r_la = rng(log_alpha, n_la * 4), r_b = rng(beta, n_b * 4);
+  const Range r_si = rng(state_in, n_s * 4), r_so = rng(state_out, n_s * 4);
+  const Range r_o = rng(out, n_v * 4), r_ws = rng(T > 0 ? p->workspace : nullptr, L.total);
+  const Range ins[] = {r_q, r_k, r_v, r_la, r_b, r_si};
+  for (const Range& r : ins)
+    if (overlap(r_o, r) || overlap(r_ws, r)) return GDN_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 5; ++i)
+    if (overlap(r_so, ins[i])) return GDN_ERR_INVALID_ARGUMENT;
+  if (overlap(r_so, r_si) && state_in != state_out) return GDN_ERR_INVALID_ARGUMENT;
+  if (overlap(r_o, r_so) || overlap(r_o, r_ws) || overlap(r_so, r_ws)) return GDN_ERR_INVALID_ARGUMENT;
+  if (T == 0 && !state_out) return GDN_OK;
+
+  VdaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+  a.state_in = state_in; a.state_out = state_out; a.out = out;
+  unsigned char* ws = static_cast<unsigned char*>(p->workspace);
+  if (T > 0) {
+    a.minv = reinterpret_cast<float*>(ws + L.minv);
+    a.cmat = reinterpret_cast<float*>(ws + L.cmat);
+    a.sfr = reinterpret_cast<float*>(ws + L.sfr);
+  }
+  a.B = B; a.T = T; a.H = H; a.NF = NF; a.frame = p->frame; a.dv = (int)dv;
+  a.dirs = dirs;
+  a.fwd_on = direction != GDN_DIR_REVERSE;
+  a.rev_on = direction != GDN_DIR_FORWARD;
+  hipStream_t stream = static_cast<hipStream_t>(p->stream);
+  hipEvent_t* ev = static_cast<hipEvent_t*>(p->timing_events);
+  vda_fn fn = p->dtype == GDN_DTYPE_BF16 ? vda_for<bf16>(dk, dv) : vda_for<float>(dk, dv);
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return GDN_ERR_HIP;
+  if (fn(a, stream, ev) != hipSuccess) return GDN_ERR_HIP;
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
 extern "C" const char* gdn_status_string(int32_t s) {
   switch (s) {
     case GDN_OK: return "ok";

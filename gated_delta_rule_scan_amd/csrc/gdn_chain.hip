@@ -148,31 +148,6 @@ struct FragMask {
   }
 };
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-
-// ds_read_b64_tr_b16 transposes within each 16-lane group: lane i receives
-// res[i][e] = src[4e + i/4][i % 4], where src[s] is the four consecutive bf16
-// at source lane s's address (lane mapping checked on gfx950).
-__device__ __forceinline__ v4s lds_read_tr16(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(const_cast<void*>(p)));
-}
-
-// Transposed k fragment for the state update, read from a row-major bf16 k
-// tile in LDS.  The A operand (m = dk row dk0 + l16, k = 32 tokens from tok0)
-// holds, in lane (l16, g4), k[tok0 + 8 g4 + j][dk0 + l16] for j = 0..7.
-// Source lane s therefore points at k[tok + s/4][dk0 + 4 (s % 4)]; two reads
-// give j = 0..3 and j = 4..7.
-__device__ __forceinline__ bf16x8 load_kt_frag(const bf16* krow, int kp, int tok0, int dk0, int l16, int g4) {
-  const int o0 = (tok0 + 8 * g4 + (l16 >> 2)) * kp + dk0 + 4 * (l16 & 3);
-  const v4s lo = lds_read_tr16(krow + o0);
-  const v4s hi = lds_read_tr16(krow + o0 + 4 * kp);
-  bf16x8 r;
-  __builtin_memcpy(&r, &lo, 8);
-  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
-  return r;
-}
-
 // hi + lo bf16 split of four fp32 values (hi = rounded value, lo = rounded
 // remainder), written as two 8-byte LDS stores.
 __device__ __forceinline__ void store_split4(bf16* hi_p, bf16* lo_p, f32x4 x) {

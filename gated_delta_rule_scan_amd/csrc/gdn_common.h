@@ -147,6 +147,32 @@ __device__ __forceinline__ typename Mma<MT>::frag bload_frag(rsrc_t r, uint32_t 
   return f;
 }
 
+// ---- transposed bf16 operands from row-major LDS tiles ----
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// ds_read_b64_tr_b16 transposes within each 16-lane group: lane i receives
+// res[i][e] = src[4e + i/4][i % 4], where src[s] is the four consecutive bf16
+// at source lane s's address (lane mapping checked on gfx950).
+__device__ __forceinline__ v4s lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(const_cast<void*>(p)));
+}
+
+// Transposed k fragment for the state update, read from a row-major bf16 k
+// tile in LDS.  The A operand (m = dk row dk0 + l16, k = 32 tokens from tok0)
+// holds, in lane (l16, g4), k[tok0 + 8 g4 + j][dk0 + l16] for j = 0..7.
+// Source lane s therefore points at k[tok + s/4][dk0 + 4 (s % 4)]; two reads
+// give j = 0..3 and j = 4..7.
+__device__ __forceinline__ bf16x8 load_kt_frag(const bf16* krow, int kp, int tok0, int dk0, int l16, int g4) {
+  const int o0 = (tok0 + 8 * g4 + (l16 >> 2)) * kp + dk0 + 4 * (l16 & 3);
+  const v4s lo = lds_read_tr16(krow + o0);
+  const v4s hi = lds_read_tr16(krow + o0 + 4 * kp);
+  bf16x8 r;
+  __builtin_memcpy(&r, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout (per problem; NBH = B*H chunk chains, NC chunks each,
 // dirs = number of computed directions):
@@ -212,5 +238,41 @@ struct ScanArgs {
   int zero_out;        // the preparation kernel fills `out` with the "not written yet" pattern (bidirectional)
   int erase;           // 1: delta rule; 0: erase-free variant (no -beta k k^T term: L = 0, T = I)
 };
+
+// Arguments of the frame-wise operator's kernels.  Workspace, per
+// (direction slot, batch*head, frame): minv = (I + A_t)^{-1} [dk][dk], cmat =
+// B_t (I + A_t)^{-1} [dv][dk], sfr = the state after the frame [dv][dk]
+// (all fp32).
+struct VdaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;  // [dirs][B][NF][H], one per frame
+  const float* beta;       // [dirs][B][T][H]
+  const float* state_in;
+  float* state_out;
+  float* out;
+  float* minv;
+  float* cmat;
+  float* sfr;
+  int64_t B, T, H, NF, frame;
+  int dv;
+  int dirs, fwd_on, rev_on;
+};
+
+struct VdaLayout {
+  size_t minv, cmat, sfr, total;
+};
+
+static inline VdaLayout vda_layout(int64_t NBH, int64_t NF, int dirs, int64_t dk, int64_t dv) {
+  VdaLayout L;
+  const size_t nfr = (size_t)dirs * (size_t)NBH * (size_t)NF;
+  size_t off = 0;
+  L.minv = off; off = align_up(off + nfr * dk * dk * 4, 256);
+  L.cmat = off; off = align_up(off + nfr * dv * dk * 4, 256);
+  L.sfr = off;  off = align_up(off + nfr * dv * dk * 4, 256);
+  L.total = off;
+  return L;
+}
 
 }  // namespace gdn

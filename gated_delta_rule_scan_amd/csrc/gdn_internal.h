@@ -35,4 +35,10 @@ hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream, h
 // sequence; sequences padded to a multiple of eight).
 inline int64_t chain_blocks(int64_t nbh, int dv, int NT, int dirs) { return (nbh + 7) / 8 * 8 * (dv / (16 * NT)) * dirs; }
 
+// Frame-wise delta operator: per-frame products and inverses, the frame
+// chain, and the readout, enqueued in that order on `stream`; ev (optional)
+// receives events after the first and second kernels (ev[1], ev[2]).
+template <typename MT, int DK, int DV>
+hipError_t launch_vda(const VdaArgs& a, hipStream_t stream, hipEvent_t* ev);
+
 }  // namespace gdn

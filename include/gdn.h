@@ -140,6 +140,52 @@ gdn_status_t gdn_forward(const gdn_problem_t* p,
                          const float* state_in, float* state_out,
                          float* out, int32_t direction);
 
+/* ---- Frame-wise delta operator (Video Delta Attention) ---------------------
+ *
+ * The memory is written once per latent frame instead of once per token: the
+ * state that stays closest to the decayed memory while fitting all of the
+ * frame's key-value associations ("Video DeltaNet", "Key Contributions" item
+ * 2 and "Methodology in Plain English"), in the page's closed form
+ *
+ *   S_t = (a_t S_{t-1} + B_t) (I + A_t)^{-1},
+ *   A_t = sum_{i in frame t} beta_i k^_i k^_i^T,  B_t = sum_{i in frame t} beta_i v_i k^_i^T,
+ *
+ * and every token i of frame t reads o_i = S_t q^_i (q^, k^ normalised as
+ * above).  Frames are consecutive runs of `frame` tokens (the last may be
+ * shorter).  One decay per frame, a_t = exp(log_alpha_t); one write strength
+ * per token (beta >= 0 keeps the transition non-expansive).  Directions as for
+ * gdn_forward: the reverse scan visits the frames last to first, the
+ * bidirectional output is the sum of both readouts.
+ *
+ * Layouts: q, k, v, beta, state_in, state_out and out as for gdn_forward;
+ *   log_alpha  [dirs, B, NF, H] fp32, NF = ceil(T / frame).
+ * Supported: dk, dv in {64, 128}; frame >= 1; fp32 or bf16 q, k, v; the same
+ * size limit as gdn_problem_t.  Same ownership, execution and error contract
+ * as gdn_forward (everything on `stream`; no allocation; no synchronisation). */
+typedef struct {
+  int64_t B, T, H, dk, dv;
+  int64_t frame;            /* tokens per frame */
+  int32_t dtype;            /* gdn_dtype_t: type of q, k, v */
+  int32_t options;          /* must be 0 */
+  void* workspace;          /* caller-owned device memory, 256-byte aligned */
+  size_t workspace_bytes;
+  void* stream;             /* hipStream_t; NULL = default stream */
+  void* timing_events;      /* NULL, or hipEvent_t[4] (caller-owned), recorded on
+                               `stream` before the per-frame kernel, after it,
+                               after the frame chain and after the readout */
+} gdn_vda_problem_t;
+
+/* Workspace bytes of gdn_vda_forward (0 if invalid or unsupported, or T = 0):
+ * three fp32 matrices per frame, head and direction. */
+size_t gdn_vda_workspace_bytes(const gdn_vda_problem_t* p, int32_t direction);
+
+/* Enqueue the frame-wise operator described by `p` on p->stream. */
+gdn_status_t gdn_vda_forward(const gdn_vda_problem_t* p,
+                             const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta,
+                             const float* state_in, float* state_out,
+                             float* out, int32_t direction);
+
 /* Static description of a status code. */
 const char* gdn_status_string(int32_t status);
 
