@@ -154,6 +154,106 @@ def cpu_baseline(w, x, target_s: float) -> dict:
             "seconds": round(dt, 2)}
 
 
+VDA_FRAME = {"stream480": 1560, "bidir480": 1560, "causal720": 3600, "bidir720": 3600, "causal720_slow": 3600}
+
+
+def run_vda(args, w) -> int:
+    """One gdn_vda_forward per step on the workload's shape, frames of one
+    latent frame's tokens (30 x 52 at 480p, 45 x 80 at 720p)."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    import synth
+    from oracle import vda as vda_oracle
+
+    frame = VDA_FRAME.get(args.workload, 64)
+    x = synth.generate_frames(w, frame)
+    xs = 2 if w.dtype == "bf16" else 4
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    s_out = torch.empty((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+    ws = None
+
+    def step(ev_ptr=None):
+        nonlocal ws
+        _, _ = gdn.vda_forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction, frame,
+                               out=out, state_out=s_out, workspace=ws, timing_events=ev_ptr)
+
+    nb = gdn.gdn_vda_workspace_bytes(gdn.gdn_vda_problem_t(w.B, w.T, w.H, w.dk, w.dv, frame,
+                                                          gdn.GDN_DTYPE_BF16 if w.dtype == "bf16" else gdn.GDN_DTYPE_F32,
+                                                          0, None, 0, None, None), gdn.DIRECTIONS[w.direction])
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = HipEvents(4 * K)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        step(ev.ptr(4 * i))
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / K
+    km = {n: sum(ev.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(K)) / K
+          for n, a in (("vda_frame", 0), ("vda_chain", 1), ("vda_readout", 2))}
+    ev.close()
+    B, T, H, dk, dv, dirs = w.B, w.T, w.H, w.dk, w.dv, w.dirs
+    NF = (T + frame - 1) // frame
+    nfr = dirs * B * H * NF
+    tok_hd = B * T * H * dirs
+    # algorithmic bytes and flops per launch of each kernel (every tensor once)
+    kb = {"vda_frame": B * T * H * (dk + dv) * xs + dirs * B * T * H * 4 + nfr * (dk * dk + dv * dk) * 4,
+          "vda_chain": nfr * (dk * dk + 2 * dv * dk) * 4 + 2 * dirs * B * H * dv * dk * 4,
+          "vda_readout": B * T * H * dk * xs + nfr * dv * dk * 4 + B * T * H * dv * 4}
+    kf = {"vda_frame": tok_hd * 2 * (dk * dk + dv * dk) + nfr * (2 * dk ** 3 + 2 * dv * dk * dk),
+          "vda_chain": nfr * 2 * dv * dk * dk,
+          "vda_readout": tok_hd * 2 * dk * dv}
+    dom = max(km, key=km.get)
+    peak_mfma = MI355X_BF16_TFLOPS if w.dtype == "bf16" else MI355X_FP32_TFLOPS
+    res = {
+        "metric": "frame-wise delta operator (VDA) tokens/s, 1 MI355X",
+        "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "operator": "frame-wise delta (Video Delta Attention)", "frame": frame,
+                   "frames": NF, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "direction": w.direction},
+        "kernels_ms": km,
+        "tflops": sum(kf.values()) / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": kb[dom] / (km[dom] * 1e-3) / 1e9,
+                     "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": kb[dom] / (km[dom] * 1e-3) / 1e9 / MI355X_HBM_GBS,
+                     "traffic": None, "alg_bytes_per_launch": kb[dom], "avg_launch_ms": km[dom],
+                     "mfma_tflops": kf[dom] / (km[dom] * 1e-3) / 1e12,
+                     "mfma_frac": kf[dom] / (km[dom] * 1e-3) / 1e12 / peak_mfma},
+    }
+    if not args.no_cpu_baseline:
+        import time as _t
+        t0 = _t.perf_counter()
+        n = 0
+        for b, h in [(b_, h_) for b_ in range(B) for h_ in range(H)]:
+            if n and _t.perf_counter() - t0 > args.cpu_seconds:
+                break
+            sel = {k: x[k][b:b + 1, :, h:h + 1] for k in ("q", "k", "v")}
+            vda_oracle.forward(sel["q"], sel["k"], sel["v"], x["log_alpha"][:, b:b + 1, :, h:h + 1],
+                               x["beta"][:, b:b + 1, :, h:h + 1], None, w.direction, frame)
+            n += 1
+        dt = _t.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n * T / dt / H, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} (batch, head) chains, both directions, numpy double, {dt:.1f} s; "
+                                         f"tokens/s scaled to all {H} heads", "seconds": round(dt, 2)}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +267,8 @@ def main() -> int:
     ap.add_argument("--serial", action="store_true", help="keep the preparation pass before the chain (no overlap)")
     ap.add_argument("--no-erase", action="store_true",
                     help="time the erase-free variant (gated linear attention, GDN_OPT_NO_ERASE) instead of the delta rule")
+    ap.add_argument("--vda", action="store_true",
+                    help="time the frame-wise delta operator (gdn_vda_forward) on the workload's frames instead")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -183,6 +285,8 @@ def main() -> int:
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.vda:
+        return run_vda(args, w)
     if w.frame:
         raise SystemExit("the streaming workload is exercised by the tests; bench one-call workloads")
     xs = 2 if w.dtype == "bf16" else 4

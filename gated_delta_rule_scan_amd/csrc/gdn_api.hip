@@ -368,7 +368,7 @@ extern "C" gdn_status_t gdn_vda_forward(const gdn_vda_problem_t* p, const void* 
   unsigned char* ws = static_cast<unsigned char*>(p->workspace);
   if (T > 0) {
     a.minv = reinterpret_cast<float*>(ws + L.minv);
-    a.cmat = reinterpret_cast<float*>(ws + L.cmat);
+    a.bmat = reinterpret_cast<float*>(ws + L.bmat);
     a.sfr = reinterpret_cast<float*>(ws + L.sfr);
   }
   a.B = B; a.T = T; a.H = H; a.NF = NF; a.frame = p->frame; a.dv = (int)dv;

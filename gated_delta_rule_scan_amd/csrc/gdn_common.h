@@ -240,9 +240,8 @@ struct ScanArgs {
 };
 
 // Arguments of the frame-wise operator's kernels.  Workspace, per
-// (direction slot, batch*head, frame): minv = (I + A_t)^{-1} [dk][dk], cmat =
-// B_t (I + A_t)^{-1} [dv][dk], sfr = the state after the frame [dv][dk]
-// (all fp32).
+// (direction slot, batch*head, frame): minv = (I + A_t)^{-1} [dk][dk], bmat =
+// B_t [dv][dk], sfr = the state after the frame [dv][dk] (all fp32).
 struct VdaArgs {
   const void* q;
   const void* k;
@@ -253,7 +252,7 @@ struct VdaArgs {
   float* state_out;
   float* out;
   float* minv;
-  float* cmat;
+  float* bmat;
   float* sfr;
   int64_t B, T, H, NF, frame;
   int dv;
@@ -261,7 +260,7 @@ struct VdaArgs {
 };
 
 struct VdaLayout {
-  size_t minv, cmat, sfr, total;
+  size_t minv, bmat, sfr, total;
 };
 
 static inline VdaLayout vda_layout(int64_t NBH, int64_t NF, int dirs, int64_t dk, int64_t dv) {
@@ -269,7 +268,7 @@ static inline VdaLayout vda_layout(int64_t NBH, int64_t NF, int dirs, int64_t dk
   const size_t nfr = (size_t)dirs * (size_t)NBH * (size_t)NF;
   size_t off = 0;
   L.minv = off; off = align_up(off + nfr * dk * dk * 4, 256);
-  L.cmat = off; off = align_up(off + nfr * dv * dk * 4, 256);
+  L.bmat = off; off = align_up(off + nfr * dv * dk * 4, 256);
   L.sfr = off;  off = align_up(off + nfr * dv * dk * 4, 256);
   L.total = off;
   return L;

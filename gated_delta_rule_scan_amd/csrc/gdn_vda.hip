@@ -7,12 +7,12 @@
 //   A_t = sum_i beta_i k^_i k^_i^T (dk x dk),  B_t = sum_i beta_i v_i k^_i^T (dv x dk),
 //   o_i = S_t q^_i for every token i of frame t.
 //
-// Three kernels.  Everything that does not depend on the state -- A_t, B_t,
-// the inverse M_t = (I + A_t)^{-1} and C_t = B_t M_t -- is computed for all
-// frames at once (vda_frame_kernel), so the sequential part is one small
-// product per frame, S_t = a_t S_{t-1} M_t + C_t (vda_chain_kernel), and the
-// readout runs over all tokens at once (vda_readout_kernel), summing the two
-// directions of a bidirectional scan in one store.
+// Three kernels.  Everything that does not depend on the state -- A_t, B_t
+// and the inverse M_t = (I + A_t)^{-1} -- is computed for all frames at once
+// (vda_frame_kernel), so the sequential part is one small product per frame,
+// S_t = (a_t S_{t-1} + B_t) M_t (vda_chain_kernel), and the readout runs over
+// all tokens at once (vda_readout_kernel), summing the two directions of a
+// bidirectional scan in one store.
 //
 // M_t is symmetric; the kernels read its rows where a product wants its
 // columns (the Gauss-Jordan result is symmetric to rounding).
@@ -25,43 +25,70 @@ template <typename MT, int DK, int DV>
 struct VdaSmem {
   static constexpr bool BF = sizeof(MT) == 2;
   static constexpr int ES = (int)sizeof(MT);
-  static constexpr int EP = 16 / ES;           // elements per 16-byte piece
-  static constexpr int AP = DK + 4;            // fp32 pitch of the dk x dk and dv x dk matrices
-  static constexpr size_t mat_bytes = (size_t)(DK + DV) * AP * 4;
-  // one 64-token block: bf16 row-major tiles (read transposed), fp32 transposed tiles
-  static constexpr int RP = DK + 8, VP = DV + 8;
-  static constexpr int TP = 64 + 4;
-  static constexpr size_t stage_bytes = BF ? (size_t)64 * (3 * RP + 2 * VP) * 2 : (size_t)(2 * DK + DV) * TP * 4;
-  static constexpr size_t region = mat_bytes > stage_bytes ? mat_bytes : stage_bytes;
+  static constexpr int EP = 16 / ES;            // elements per 16-byte piece
+  static constexpr int TB = 32;                 // tokens per block: one matrix-core contraction
+  static constexpr int RP = DK + 8, VP = DV + 8;  // bf16 row-major staging pitches
+  static constexpr int TP = TB + 4;             // fp32 transposed staging pitch
+  static constexpr size_t stage_bytes = BF ? (size_t)TB * (RP + VP) * 2 : (size_t)(DK + DV) * TP * 4;
+  static constexpr int AP = DK + 4;             // fp32 pitch of I + A_t
+  static constexpr size_t mat_bytes = (size_t)DK * AP * 4;
+  // two staging buffers, later reused for I + A_t
+  static constexpr size_t region = 2 * stage_bytes > mat_bytes ? 2 * stage_bytes : mat_bytes;
 };
 
+// bf16 fragment of raw values times per-token weights (w0: tokens 0-3 of the
+// lane's eight, w1: tokens 4-7), split into hi + lo so that the product keeps
+// fp32 accuracy on the bf16 matrix cores.
+__device__ __forceinline__ void scale_split(const bf16x8& x, const f32x4& w0, const f32x4& w1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = (e < 4 ? w0[e] : w1[e - 4]) * (float)x[e];
+    hi[e] = (bf16)y;
+    lo[e] = (bf16)(y - (float)hi[e]);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Per frame: A_t and B_t on the matrix cores, M_t by Gauss-Jordan, C_t = B_t M_t.
-// One 256-thread workgroup per (direction, batch*head, frame).
+// Per frame: A_t and B_t on the matrix cores, M_t = (I + A_t)^{-1} by
+// Gauss-Jordan.  One 256-thread workgroup per (direction, batch*head, frame);
+// for two directions the pair of workgroups of one frame is launched
+// back-to-back on one XCD, so the second reads the frame's k and v from L2.
 // ---------------------------------------------------------------------------
 template <typename MT, int DK, int DV>
-__global__ __launch_bounds__(256) void vda_frame_kernel(VdaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void vda_frame_kernel(VdaArgs a) {
   using SM = VdaSmem<MT, DK, DV>;
   using M = Mma<MT>;
-  using F32 = Mma<float>;
   using frag = typename M::frag;
-  constexpr int ES = SM::ES, EP = SM::EP, AP = SM::AP, RP = SM::RP, VP = SM::VP, TP = SM::TP;
-  constexpr int NJA = DK / 16 / 4;  // dk tiles of A per wave (row tiles)
-  constexpr int NJB = DV / 64;      // dv tiles of B per wave
-  constexpr int NL = DK / 16;       // column tiles (dk)
+  constexpr int ES = SM::ES, EP = SM::EP, AP = SM::AP, RP = SM::RP, VP = SM::VP, TP = SM::TP, TB = SM::TB;
+  constexpr int NJA = DK / 64;      // dk row tiles of A per wave
+  constexpr int NJB = DV / 64;      // dv row tiles of B per wave
+  constexpr int NL = DK / 16;       // dk column tiles
+  constexpr int TPR = 256 / TB;     // threads per token row when staging
+  constexpr int NPK = DK / (TPR * EP), NPV = DV / (TPR * EP);  // 16-byte pieces per thread
   static_assert(DK % 64 == 0 && DV % 64 == 0, "head dimensions are multiples of 64");
+  static_assert(NPK >= 1 && NPV >= 1, "staging covers whole rows");
 
   __shared__ __align__(16) unsigned char smem[SM::region];
-  __shared__ float s_wv[64];                   // beta rk of each token of the block
-  __shared__ float s_pr[2][DK], s_pc[2][DK];   // Gauss-Jordan pivot row and column
+  __shared__ __align__(16) float s_wa[2][TB], s_wb[2][TB];  // beta rk^2 (for A) and beta rk (for B) per token
+  __shared__ __align__(16) float s_pr[2][DK], s_pc[2][DK];  // Gauss-Jordan pivot row and column
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int NF = (int)a.NF, BH = (int)(a.B * a.H);
-  const int f = blockIdx.x % NF;
-  const int bh = (blockIdx.x / NF) % BH;
-  const int slot = blockIdx.x / (NF * BH);
+  const int64_t U = (int64_t)BH * NF;
+  int slot;
+  int64_t u;
+  if (a.dirs == 2) {
+    const int64_t r = blockIdx.x >> 3;
+    slot = (int)(r & 1);
+    u = (r >> 1) * 8 + (blockIdx.x & 7);
+  } else {
+    slot = 0;
+    u = blockIdx.x;
+  }
+  if (u >= U) return;  // padding of the last group of eight
+  const int bh = (int)(u / NF), f = (int)(u % NF);
   const int64_t b = bh / a.H, h = bh % a.H;
   const int64_t T = a.T, H = a.H, Fr = a.frame;
   const int64_t t0 = (int64_t)f * Fr;
@@ -78,154 +105,135 @@ __global__ __launch_bounds__(256) void vda_frame_kernel(VdaArgs a) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) accB[j][l] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- A_t = K^T diag(beta rk^2) K and B_t = V^T diag(beta rk) K over the
-  // frame's tokens, 64 at a time (raw K and V enter the matrix cores; the
-  // scaled copies are split hi + lo for bf16 inputs) ----
-  constexpr int PRK = DK / EP, RPIK = 256 / PRK, NPK = 64 / RPIK;  // K pieces: per row, rows per pass, per thread
-  constexpr int PRV = DV / EP, RPIV = 256 / PRV, NPV = 64 / RPIV;
+  // ---- A_t = K^T diag(beta rk^2) K and B_t = V^T diag(beta rk) K, 32 tokens
+  // at a time.  Raw k and v are staged (double-buffered, one barrier per
+  // block); the weighted side is scaled in registers after the fragment read.
+  // Rows past the frame's end read as zero (buffer range checks), weight 0. ----
   const uint32_t HKB = (uint32_t)(H * DK * ES), HVB = (uint32_t)(H * a.dv * ES);
-  const int krow = tid / PRK, kcol = (tid % PRK) * EP;
-  const int vrow = tid / PRV, vcol = (tid % PRV) * EP;
-  MT* Ks = reinterpret_cast<MT*>(smem);        // bf16: [64][RP] raw k, then k w (hi, lo), then v w (hi, lo)
-  MT* Kwh = Ks + 64 * RP;
-  MT* Kwl = Kwh + 64 * RP;
-  MT* Vwh = Kwl + 64 * RP;
-  MT* Vwl = Vwh + 64 * VP;
-  float* KT = reinterpret_cast<float*>(smem);  // fp32: [DK][TP] raw k^T, then (k w)^T, then (v w)^T
-  float* KwT = KT + DK * TP;
-  float* VwT = KwT + DK * TP;
-
-  for (int blk = 0; blk < n; blk += 64) {
-    const int rows = n - blk < 64 ? n - blk : 64;
+  const int trow = tid / TPR, tpos = tid % TPR;
+  f32x4 kp[NPK], vp[NPV];
+  float bt;
+  auto issue = [&](int blk) {
+    const int rows = n - blk < TB ? n - blk : TB;
     const int64_t tb = t0 + blk;
     const rsrc_t rk = make_rsrc(static_cast<const MT*>(a.k) + ((b * T + tb) * H + h) * DK,
                                 (uint32_t)(rows - 1) * HKB + DK * ES);
     const rsrc_t rv = make_rsrc(static_cast<const MT*>(a.v) + ((b * T + tb) * H + h) * a.dv,
                                 (uint32_t)(rows - 1) * HVB + (uint32_t)a.dv * ES);
     const rsrc_t rb = make_rsrc(a.beta + ((slot * a.B + b) * T + tb) * H + h, (uint32_t)((rows - 1) * H + 1) * 4u);
-    f32x4 kp[NPK], vp[NPV];
-    float bk[NPK];
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) {
-      kp[i] = bload16(rk, (uint32_t)(krow + RPIK * i) * HKB + kcol * ES);
-      bk[i] = bload4(rb, (uint32_t)((krow + RPIK * i) * H) * 4u);
-    }
+    for (int i = 0; i < NPK; ++i) kp[i] = bload16(rk, (uint32_t)trow * HKB + (uint32_t)((i * TPR + tpos) * EP * ES));
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) vp[i] = bload16(rv, (uint32_t)(vrow + RPIV * i) * HVB + vcol * ES);
-
-    // k rows: norm over the row's lanes, then raw and scaled copies
+    for (int i = 0; i < NPV; ++i) vp[i] = bload16(rv, (uint32_t)trow * HVB + (uint32_t)((i * TPR + tpos) * EP * ES));
+    bt = bload4(rb, (uint32_t)(trow * H) * 4u);
+  };
+  issue(0);
+  for (int blk = 0, it = 0; blk < n; blk += TB, ++it) {
+    const int buf = it & 1;
+    unsigned char* stage = smem + (size_t)buf * SM::stage_bytes;
+    // row norm over the row's TPR threads
+    float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) {
-      float x[EP], ss = 0.f;
+    for (int i = 0; i < NPK; ++i)
 #pragma unroll
       for (int e = 0; e < EP; ++e) {
+        float x;
         if constexpr (SM::BF) {
-          x[e] = (float)__builtin_bit_cast(bf16x8, kp[i])[e];
+          x = (float)__builtin_bit_cast(bf16x8, kp[i])[e];
         } else {
-          x[e] = kp[i][e];
+          x = kp[i][e];
         }
-        ss = fmaf(x[e], x[e], ss);
+        ss = fmaf(x, x, ss);
       }
 #pragma unroll
-      for (int m = 1; m < PRK; m <<= 1) ss += __shfl_xor(ss, m, 64);
-      const float rkn = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-      const float wk = bk[i] * rkn * rkn;
-      const int row = krow + RPIK * i;
-      if (tid % PRK == 0) s_wv[row] = bk[i] * rkn;
-      if constexpr (SM::BF) {
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < EP; ++e) {
-          const float y = wk * x[e];
-          hi[e] = (bf16)y;
-          lo[e] = (bf16)(y - (float)hi[e]);
-        }
-        *reinterpret_cast<f32x4*>(Ks + row * RP + kcol) = kp[i];
-        *reinterpret_cast<bf16x8*>(Kwh + row * RP + kcol) = hi;
-        *reinterpret_cast<bf16x8*>(Kwl + row * RP + kcol) = lo;
-      } else {
-#pragma unroll
-        for (int e = 0; e < EP; ++e) {
-          KT[(kcol + e) * TP + row] = x[e];
-          KwT[(kcol + e) * TP + row] = wk * x[e];
-        }
-      }
+    for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+    const float rkn = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+    if (tpos == 0) {
+      s_wa[buf][trow] = bt * rkn * rkn;
+      s_wb[buf][trow] = bt * rkn;
     }
-    __syncthreads();
-    // v rows, scaled by beta rk of their token
+    if constexpr (SM::BF) {
+      MT* Ks = reinterpret_cast<MT*>(stage);
+      MT* Vs = Ks + TB * RP;
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int row = vrow + RPIV * i;
-      const float wv = s_wv[row];
-      if constexpr (SM::BF) {
-        bf16x8 hi, lo;
+      for (int i = 0; i < NPK; ++i) *reinterpret_cast<f32x4*>(Ks + trow * RP + (i * TPR + tpos) * EP) = kp[i];
 #pragma unroll
-        for (int e = 0; e < EP; ++e) {
-          const float y = wv * (float)__builtin_bit_cast(bf16x8, vp[i])[e];
-          hi[e] = (bf16)y;
-          lo[e] = (bf16)(y - (float)hi[e]);
-        }
-        *reinterpret_cast<bf16x8*>(Vwh + row * VP + vcol) = hi;
-        *reinterpret_cast<bf16x8*>(Vwl + row * VP + vcol) = lo;
-      } else {
+      for (int i = 0; i < NPV; ++i) *reinterpret_cast<f32x4*>(Vs + trow * VP + (i * TPR + tpos) * EP) = vp[i];
+    } else {
+      float* KT = reinterpret_cast<float*>(stage);
+      float* VT = KT + DK * TP;
 #pragma unroll
-        for (int e = 0; e < EP; ++e) VwT[(vcol + e) * TP + row] = wv * vp[i][e];
-      }
+      for (int i = 0; i < NPK; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) KT[((i * TPR + tpos) * 4 + e) * TP + trow] = kp[i][e];
+#pragma unroll
+      for (int i = 0; i < NPV; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) VT[((i * TPR + tpos) * 4 + e) * TP + trow] = vp[i][e];
     }
+    if (blk + TB < n) issue(blk + TB);
     __syncthreads();
 
-    // products: wave w owns dk row tiles NJA w.. of A and dv row tiles NJB w.. of B
+    // the lane's eight tokens are 8 g4 .. 8 g4 + 7 of the block
+    const f32x4 wa0 = *reinterpret_cast<const f32x4*>(&s_wa[buf][8 * g4]);
+    const f32x4 wa1 = *reinterpret_cast<const f32x4*>(&s_wa[buf][8 * g4 + 4]);
+    const f32x4 wb0 = *reinterpret_cast<const f32x4*>(&s_wb[buf][8 * g4]);
+    const f32x4 wb1 = *reinterpret_cast<const f32x4*>(&s_wb[buf][8 * g4 + 4]);
+    if constexpr (SM::BF) {
+      const MT* Ks = reinterpret_cast<const MT*>(stage);
+      const MT* Vs = Ks + TB * RP;
+      frag kr[NL];  // raw k^T, one fragment per dk column tile
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      frag kb[NL];  // raw k^T fragments, one per dk tile
+      for (int l = 0; l < NL; ++l) kr[l] = load_kt_frag(Ks, RP, 0, 16 * l, l16, g4);
 #pragma unroll
-      for (int l = 0; l < NL; ++l) {
-        if constexpr (SM::BF) {
-          kb[l] = load_kt_frag(Ks, RP, 32 * kc, 16 * l, l16, g4);
-        } else {
-          kb[l] = M::load(KT + (16 * l + l16) * TP + 32 * kc + 8 * g4);
-        }
-      }
+      for (int j = 0; j < NJA; ++j) {
+        frag xh, xl;
+        scale_split(load_kt_frag(Ks, RP, 0, 16 * (NJA * w + j), l16, g4), wa0, wa1, xh, xl);
 #pragma unroll
-      for (int l = 0; l < NL; ++l) {
-        if constexpr (SM::BF) {
-          const frag wh = load_kt_frag(Kwh, RP, 32 * kc, 16 * l, l16, g4);
-          const frag wl = load_kt_frag(Kwl, RP, 32 * kc, 16 * l, l16, g4);
-#pragma unroll
-          for (int j = 0; j < NJA; ++j) {
-            accA[j][l] = M::mma(kb[NJA * w + j], wh, accA[j][l]);
-            accA[j][l] = M::mma(kb[NJA * w + j], wl, accA[j][l]);
-          }
-        } else {
-          const frag wk = M::load(KwT + (16 * l + l16) * TP + 32 * kc + 8 * g4);
-#pragma unroll
-          for (int j = 0; j < NJA; ++j) accA[j][l] = M::mma(kb[NJA * w + j], wk, accA[j][l]);
+        for (int l = 0; l < NL; ++l) {
+          accA[j][l] = M::mma(xh, kr[l], accA[j][l]);
+          accA[j][l] = M::mma(xl, kr[l], accA[j][l]);
         }
       }
 #pragma unroll
       for (int j = 0; j < NJB; ++j) {
-        const int jv = NJB * w + j;
-        if constexpr (SM::BF) {
-          const frag vh = load_kt_frag(Vwh, VP, 32 * kc, 16 * jv, l16, g4);
-          const frag vl = load_kt_frag(Vwl, VP, 32 * kc, 16 * jv, l16, g4);
+        frag yh, yl;
+        scale_split(load_kt_frag(Vs, VP, 0, 16 * (NJB * w + j), l16, g4), wb0, wb1, yh, yl);
 #pragma unroll
-          for (int l = 0; l < NL; ++l) {
-            accB[j][l] = M::mma(vh, kb[l], accB[j][l]);
-            accB[j][l] = M::mma(vl, kb[l], accB[j][l]);
-          }
-        } else {
-          const frag vw = M::load(VwT + (16 * jv + l16) * TP + 32 * kc + 8 * g4);
-#pragma unroll
-          for (int l = 0; l < NL; ++l) accB[j][l] = M::mma(vw, kb[l], accB[j][l]);
+        for (int l = 0; l < NL; ++l) {
+          accB[j][l] = M::mma(yh, kr[l], accB[j][l]);
+          accB[j][l] = M::mma(yl, kr[l], accB[j][l]);
         }
       }
+    } else {
+      const float* KT = reinterpret_cast<const float*>(stage);
+      const float* VT = KT + DK * TP;
+      frag kr[NL];
+#pragma unroll
+      for (int l = 0; l < NL; ++l) kr[l] = M::load(KT + (16 * l + l16) * TP + 8 * g4);
+#pragma unroll
+      for (int j = 0; j < NJA; ++j) {
+        frag x = M::load(KT + (16 * (NJA * w + j) + l16) * TP + 8 * g4);
+        x.lo *= wa0;
+        x.hi *= wa1;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) accA[j][l] = M::mma(x, kr[l], accA[j][l]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJB; ++j) {
+        frag y = M::load(VT + (16 * (NJB * w + j) + l16) * TP + 8 * g4);
+        y.lo *= wb0;
+        y.hi *= wb1;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) accB[j][l] = M::mma(y, kr[l], accB[j][l]);
+      }
     }
-    __syncthreads();  // the staging area is rewritten by the next block (or the matrices)
   }
+  __syncthreads();  // the staging buffers become I + A_t
 
-  // ---- I + A_t and B_t into LDS (fp32) ----
+  // ---- I + A_t into LDS; B_t straight to the workspace.  Tile (j, l) of a
+  // wave holds, in lane (l16, g4), row 16 (tile) + 4 g4 + i, column 16 l + l16. ----
   float* Am = reinterpret_cast<float*>(smem);  // [DK][AP]
-  float* Bm = Am + DK * AP;                    // [DV][AP]
 #pragma unroll
   for (int j = 0; j < NJA; ++j)
 #pragma unroll
@@ -235,178 +243,190 @@ __global__ __launch_bounds__(256) void vda_frame_kernel(VdaArgs a) {
         const int r = 16 * (NJA * w + j) + 4 * g4 + i, c = 16 * l + l16;
         Am[r * AP + c] = accA[j][l][i] + (r == c ? 1.f : 0.f);
       }
+  {
+    float* bg = a.bmat + fid * (size_t)DV * DK;
 #pragma unroll
-  for (int j = 0; j < NJB; ++j)
+    for (int j = 0; j < NJB; ++j)
 #pragma unroll
-    for (int l = 0; l < NL; ++l)
+      for (int l = 0; l < NL; ++l)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Bm[(16 * (NJB * w + j) + 4 * g4 + i) * AP + 16 * l + l16] = accB[j][l][i];
+        for (int i = 0; i < 4; ++i) bg[(size_t)(16 * (NJB * w + j) + 4 * g4 + i) * DK + 16 * l + l16] = accB[j][l][i];
+  }
   __syncthreads();
 
   // ---- M_t = (I + A_t)^{-1}: Gauss-Jordan in place, no pivoting (I + A_t is
   // symmetric positive definite).  Thread (ty, tx) of a 16 x 16 grid keeps a
   // BS x BS block in registers; each pivot's row and column go through LDS
-  // (double-buffered: one barrier per pivot). ----
+  // (double-buffered: one barrier per pivot).  The pivot's position inside a
+  // block is a compile-time index. ----
   {
     constexpr int BS = DK / 16;
+    static_assert(BS % 2 == 0, "pivot buffers alternate within a block");
     const int ty = tid >> 4, tx = tid & 15;
     float m[BS][BS];
 #pragma unroll
     for (int i = 0; i < BS; ++i)
 #pragma unroll
-      for (int j = 0; j < BS; ++j) m[i][j] = Am[(ty * BS + i) * AP + tx * BS + j];
-    for (int p = 0; p < DK; ++p) {
-      const int buf = p & 1, pb = p / BS, pi = p % BS;
-      if (ty == pb) {  // row pi of the block (selects keep the register indices static)
+      for (int j = 0; j < BS; j += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(Am + (ty * BS + i) * AP + tx * BS + j);
 #pragma unroll
-        for (int j = 0; j < BS; ++j) {
-          float x = 0.f;
-#pragma unroll
-          for (int ii = 0; ii < BS; ++ii) x = ii == pi ? m[ii][j] : x;
-          s_pr[buf][tx * BS + j] = x;
-        }
+        for (int e = 0; e < 4; ++e) m[i][j + e] = x[e];
       }
-      if (tx == pb) {
+    for (int pb = 0; pb < 16; ++pb) {
+      const bool rowb = ty == pb, colb = tx == pb;
 #pragma unroll
-        for (int i = 0; i < BS; ++i) {
-          float x = 0.f;
+      for (int pi = 0; pi < BS; ++pi) {
+        const int buf = pi & 1, p = pb * BS + pi;
+        if (rowb) {
 #pragma unroll
-          for (int jj = 0; jj < BS; ++jj) x = jj == pi ? m[i][jj] : x;
-          s_pc[buf][ty * BS + i] = x;
+          for (int j = 0; j < BS; j += 4)
+            *reinterpret_cast<f32x4*>(&s_pr[buf][tx * BS + j]) = f32x4{m[pi][j], m[pi][j + 1], m[pi][j + 2], m[pi][j + 3]};
         }
+        if (colb) {
+#pragma unroll
+          for (int i = 0; i < BS; i += 4)
+            *reinterpret_cast<f32x4*>(&s_pc[buf][ty * BS + i]) = f32x4{m[i][pi], m[i + 1][pi], m[i + 2][pi], m[i + 3][pi]};
+        }
+        __syncthreads();
+        const float d = 1.0f / s_pr[buf][p];
+        float r[BS], fc[BS];
+#pragma unroll
+        for (int j = 0; j < BS; j += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&s_pr[buf][tx * BS + j]);
+          const f32x4 y = *reinterpret_cast<const f32x4*>(&s_pc[buf][ty * BS + j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[j + e] = x[e];
+            fc[j + e] = y[e] * d;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < BS; ++i)
+#pragma unroll
+          for (int j = 0; j < BS; ++j) m[i][j] = fmaf(-fc[i], r[j], m[i][j]);
+        // the pivot row becomes r d, the pivot column -f d, the pivot d
+#pragma unroll
+        for (int j = 0; j < BS; ++j) m[pi][j] = rowb ? r[j] * d : m[pi][j];
+#pragma unroll
+        for (int i = 0; i < BS; ++i) m[i][pi] = colb ? -fc[i] : m[i][pi];
+        m[pi][pi] = rowb && colb ? d : m[pi][pi];
       }
-      __syncthreads();
-      const float d = 1.0f / s_pr[buf][p];
-      float r[BS], fc[BS];
-#pragma unroll
-      for (int j = 0; j < BS; ++j) r[j] = s_pr[buf][tx * BS + j];
-#pragma unroll
-      for (int i = 0; i < BS; ++i) fc[i] = s_pc[buf][ty * BS + i] * d;
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) m[i][j] = fmaf(-fc[i], r[j], m[i][j]);
-      // the pivot row becomes r d, the pivot column -f d, the pivot d
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) {
-          const bool rowp = ty == pb && i == pi, colp = tx == pb && j == pi;
-          m[i][j] = rowp ? (colp ? d : r[j] * d) : (colp ? -fc[i] : m[i][j]);
-        }
     }
+    float* mg = a.minv + fid * (size_t)DK * DK;
 #pragma unroll
     for (int i = 0; i < BS; ++i)
 #pragma unroll
-      for (int j = 0; j < BS; ++j) Am[(ty * BS + i) * AP + tx * BS + j] = m[i][j];
-  }
-  __syncthreads();
-
-  // ---- C_t^T = M_t B_t^T on fp32 matrix cores (M_t symmetric): tile (l, j)
-  // lands in lane (l16, g4) as C_t[16 j + l16][16 l + 4 g4 + i], one 16-byte
-  // piece of a row of C_t; M_t rows are written out alongside ----
-  {
-    float* cg = a.cmat + fid * (size_t)DV * DK;
-    constexpr int NLW = NL / 4;  // dk tiles of C^T rows per wave
-#pragma unroll
-    for (int lw = 0; lw < NLW; ++lw) {
-      const int l = NLW * w + lw;
-      f32x4 acc[DV / 16];
-#pragma unroll
-      for (int j = 0; j < DV / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < DK / 32; ++c) {
-        const F32::frag mf = F32::load(Am + (16 * l + l16) * AP + 32 * c + 8 * g4);
-#pragma unroll
-        for (int j = 0; j < DV / 16; ++j)
-          acc[j] = F32::mma(mf, F32::load(Bm + (16 * j + l16) * AP + 32 * c + 8 * g4), acc[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < DV / 16; ++j)
-        *reinterpret_cast<f32x4*>(cg + (size_t)(16 * j + l16) * DK + 16 * l + 4 * g4) = acc[j];
-    }
-    float* mg = a.minv + fid * (size_t)DK * DK;
-    for (int p = tid; p < DK * DK / 4; p += 256) {
-      const int r = p / (DK / 4), c4 = (p % (DK / 4)) * 4;
-      *reinterpret_cast<f32x4*>(mg + (size_t)r * DK + c4) = *reinterpret_cast<const f32x4*>(Am + r * AP + c4);
-    }
+      for (int j = 0; j < BS; j += 4)
+        *reinterpret_cast<f32x4*>(mg + (size_t)(ty * BS + i) * DK + tx * BS + j) =
+            f32x4{m[i][j], m[i][j + 1], m[i][j + 2], m[i][j + 3]};
   }
 }
 
 // ---------------------------------------------------------------------------
-// Sequential over frames: S_t = a_t S_{t-1} M_t + C_t.  One workgroup per
-// (direction, batch*head, 16 state rows); the fp32 rows live in LDS.
+// Sequential over frames: S_t = R_t M_t with R_t = a_t S_{t-1} + B_t.  One
+// workgroup per (direction, batch*head, 16 state rows); R_t's fp32 rows live
+// in LDS, and the next frame's M, B and decay are loaded while this frame's
+// product runs.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
   using F32 = Mma<float>;
   constexpr int SP = DK + 4;
   constexpr int NLW = DK / 64;  // dk tiles per wave
-  __shared__ __align__(16) float Ss[16 * SP];
+  constexpr int KC = DK / 32;
+  __shared__ __align__(16) float Rs[16 * SP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int NF = (int)a.NF, BH = (int)(a.B * a.H), NT = DV / 16;
-  const int tile = blockIdx.x % NT;
-  const int bh = (blockIdx.x / NT) % BH;
-  const int slot = blockIdx.x / (NT * BH);
+  // the NT row tiles of one chain share an XCD (workgroup ids equal mod 8), so
+  // each frame's M_t is fetched into that XCD's L2 once
+  const int g = blockIdx.x >> 3;
+  const int tile = g % NT;
+  const int chain = (g / NT) * 8 + (blockIdx.x & 7);
+  if (chain >= a.dirs * BH) return;
+  const int bh = chain % BH;
+  const int slot = chain / BH;
   const bool rev = a.rev_on && (slot == 1 || !a.fwd_on);
   const int64_t b = bh / a.H, h = bh % a.H;
   const size_t srow = (((size_t)slot * a.B + b) * a.H + h) * DV * DK + (size_t)16 * tile * DK;  // state rows
+  const size_t fbase = ((size_t)slot * BH + bh) * NF;
+  const float* lag = a.log_alpha + ((size_t)slot * a.B + b) * NF * a.H + h;
 
-  for (int p = tid; p < 16 * DK / 4; p += 256) {
-    const int r = p / (DK / 4), c4 = (p % (DK / 4)) * 4;
-    *reinterpret_cast<f32x4*>(Ss + r * SP + c4) =
-        a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + srow + (size_t)r * DK + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int s = 0; s < NF; ++s) {
-    const int f = rev ? NF - 1 - s : s;
-    const size_t fid = ((size_t)slot * BH + bh) * NF + f;
-    const float* mg = a.minv + fid * (size_t)DK * DK;
-    const float* cg = a.cmat + fid * (size_t)DV * DK + (size_t)16 * tile * DK;
-    const float at = expf(a.log_alpha[((size_t)slot * a.B + b) * NF * a.H + (size_t)f * a.H + h]);
-    __syncthreads();  // Ss holds S_{t-1}
-    // (M S^T) tile l lands in lane (l16, g4) as S_new[l16][16 l + 4 g4 + i]
-    f32x4 snew[NLW];
+  // the lane's share of a 16 x DK row tile: row l16, columns 16 l + 4 g4 .. + 3
+  auto frame_of = [&](int s) { return rev ? NF - 1 - s : s; };
+  F32::frag mf[NLW][KC];
+  f32x4 bn[NLW];
+  float an = 0.f;
+  auto fetch = [&](int f) {
+    const float* mg = a.minv + (fbase + f) * (size_t)DK * DK;
+    const float* bg = a.bmat + (fbase + f) * (size_t)DV * DK + (size_t)16 * tile * DK;
 #pragma unroll
     for (int lw = 0; lw < NLW; ++lw) {
       const int l = NLW * w + lw;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) mf[lw][c] = F32::load(mg + (size_t)(16 * l + l16) * DK + 32 * c + 8 * g4);
+      bn[lw] = *reinterpret_cast<const f32x4*>(bg + (size_t)l16 * DK + 16 * l + 4 * g4);
+    }
+    an = expf(lag[(size_t)f * a.H]);
+  };
+  f32x4 snew[NLW];
+#pragma unroll
+  for (int lw = 0; lw < NLW; ++lw) {
+    const int l = NLW * w + lw;
+    snew[lw] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + srow + (size_t)l16 * DK + 16 * l + 4 * g4)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (NF > 0) fetch(frame_of(0));
+  for (int s = 0; s < NF; ++s) {
+    const int f = frame_of(s);
+#pragma unroll
+    for (int lw = 0; lw < NLW; ++lw) {
+      const int l = NLW * w + lw;
+      *reinterpret_cast<f32x4*>(Rs + l16 * SP + 16 * l + 4 * g4) = snew[lw] * an + bn[lw];
+    }
+    __syncthreads();  // Rs holds R_t
+    // (M R^T) tile l lands in lane (l16, g4) as S_t[l16][16 l + 4 g4 + i]
+#pragma unroll
+    for (int lw = 0; lw < NLW; ++lw) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < DK / 32; ++c) {
-        const F32::frag mf = F32::load(mg + (size_t)(16 * l + l16) * DK + 32 * c + 8 * g4);
-        acc = F32::mma(mf, F32::load(Ss + l16 * SP + 32 * c + 8 * g4), acc);
-      }
-      const f32x4 cv = *reinterpret_cast<const f32x4*>(cg + (size_t)l16 * DK + 16 * l + 4 * g4);
-      snew[lw] = acc * at + cv;
+      for (int c = 0; c < KC; ++c) acc = F32::mma(mf[lw][c], F32::load(Rs + l16 * SP + 32 * c + 8 * g4), acc);
+      snew[lw] = acc;
     }
-    __syncthreads();  // every wave has read S_{t-1}
-    float* sg = a.sfr + fid * (size_t)DV * DK + (size_t)16 * tile * DK;
+    if (s + 1 < NF) fetch(frame_of(s + 1));
+    float* sg = a.sfr + (fbase + f) * (size_t)DV * DK + (size_t)16 * tile * DK;
 #pragma unroll
     for (int lw = 0; lw < NLW; ++lw) {
       const int l = NLW * w + lw;
-      *reinterpret_cast<f32x4*>(Ss + l16 * SP + 16 * l + 4 * g4) = snew[lw];
       *reinterpret_cast<f32x4*>(sg + (size_t)l16 * DK + 16 * l + 4 * g4) = snew[lw];
     }
+    __syncthreads();  // every wave has read R_t
   }
-  __syncthreads();
   if (a.state_out) {
-    for (int p = tid; p < 16 * DK / 4; p += 256) {
-      const int r = p / (DK / 4), c4 = (p % (DK / 4)) * 4;
-      *reinterpret_cast<f32x4*>(a.state_out + srow + (size_t)r * DK + c4) = *reinterpret_cast<const f32x4*>(Ss + r * SP + c4);
+#pragma unroll
+    for (int lw = 0; lw < NLW; ++lw) {
+      const int l = NLW * w + lw;
+      *reinterpret_cast<f32x4*>(a.state_out + srow + (size_t)l16 * DK + 16 * l + 4 * g4) = snew[lw];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Readout: o_i = S_t q^_i for 64 tokens of one frame per workgroup, both
-// directions summed.  Computed transposed (O^T = S_t Q^T, Q raw), so each
-// lane holds four consecutive values of one token's output row.
+// Readout: o_i = S_t q^_i, both directions summed (o = (S_fwd + S_rev) q^).
+// One workgroup per (batch*head, frame, run of 64-token blocks); the summed
+// state is split once into the matrix cores' operands and kept in registers
+// while the run's blocks stream through.  Computed transposed (O^T = S Q^T,
+// Q raw, rows scaled by 1/|q| after), so each lane holds four consecutive
+// values of one token's output row; wave w owns the w-th quarter of the dv
+// columns.
 // ---------------------------------------------------------------------------
 template <typename MT, int DK, int DV>
-__global__ __launch_bounds__(256) void vda_readout_kernel(VdaArgs a, int nblk) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void vda_readout_kernel(VdaArgs a, int nblk,
+                                                                                                 int bpw) {
   using M = Mma<MT>;
   using frag = typename M::frag;
+  constexpr bool BF = sizeof(MT) == 2;
   constexpr int ES = (int)sizeof(MT);
   constexpr int CT = DV / 64;  // dv tiles per wave
   constexpr int KC = DK / 32;
@@ -414,95 +434,148 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(VdaArgs a, int nblk) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int NF = (int)a.NF, BH = (int)(a.B * a.H);
-  const int f = blockIdx.x / nblk, jb = blockIdx.x % nblk;
+  const int nsplit = (nblk + bpw - 1) / bpw;
+  const int f = blockIdx.x / nsplit, js = blockIdx.x % nsplit;
   const int bh = blockIdx.y;
+  const int jb0 = js * bpw, jb1 = jb0 + bpw < nblk ? jb0 + bpw : nblk;
   const int64_t b = bh / a.H, h = bh % a.H, T = a.T, H = a.H;
-  const int64_t fs = (int64_t)f * a.frame + 64 * jb;
-  int64_t rows = a.frame - 64 * jb;
-  if (T - fs < rows) rows = T - fs;
-  if (rows > 64) rows = 64;
-  if (rows <= 0) return;
-  const uint32_t HQB = (uint32_t)(H * DK * ES), HOB = (uint32_t)(H * DV * 4);
-  const rsrc_t rq = make_rsrc(static_cast<const MT*>(a.q) + ((b * T + fs) * H + h) * DK, (uint32_t)(rows - 1) * HQB + DK * ES);
-  const rsrc_t ro = make_rsrc(a.out + ((b * T + fs) * H + h) * DV, (uint32_t)(rows - 1) * HOB + DV * 4);
+  const int64_t f0 = (int64_t)f * a.frame;
+  const int64_t fend = f0 + a.frame < T ? f0 + a.frame : T;
+  if (f0 + 64 * (int64_t)jb0 >= fend) return;
 
-  frag qf[4][KC];
-  float rqs[4];
+  // summed state rows 16 ct + l16, columns 32 c + 8 g4 .. + 7
+  frag sh[CT][KC];
+  [[maybe_unused]] frag sl[CT][KC];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    float ss = 0.f;
+  for (int cc = 0; cc < CT; ++cc) {
+    const int ct = CT * w + cc;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      qf[rt][c] = bload_frag<MT>(rq, (uint32_t)(16 * rt + l16) * HQB + (32 * c + 8 * g4) * ES);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = M::get(qf[rt][c], e);
-        ss = fmaf(x, x, ss);
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      for (int slot = 0; slot < a.dirs; ++slot) {
+        const float* src = a.sfr + (((size_t)slot * BH + bh) * NF + f) * (size_t)DV * DK + (size_t)(16 * ct + l16) * DK +
+                           32 * c + 8 * g4;
+        s0 += *reinterpret_cast<const f32x4*>(src);
+        s1 += *reinterpret_cast<const f32x4*>(src + 4);
       }
-    }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    rqs[rt] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-  }
-  f32x4 acc[CT][4];
+      if constexpr (BF) {
 #pragma unroll
-  for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[cc][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int slot = 0; slot < a.dirs; ++slot) {
-    const float* sg = a.sfr + (((size_t)slot * BH + bh) * NF + f) * (size_t)DV * DK;
-#pragma unroll
-    for (int cc = 0; cc < CT; ++cc) {
-      const int ct = CT * w + cc;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const float* src = sg + (size_t)(16 * ct + l16) * DK + 32 * c + 8 * g4;
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(src), s1 = *reinterpret_cast<const f32x4*>(src + 4);
-        if constexpr (ES == 2) {
-          frag hi, lo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = e < 4 ? s0[e] : s1[e - 4];
-            hi[e] = (bf16)x;
-            lo[e] = (bf16)(x - (float)hi[e]);
-          }
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            acc[cc][rt] = M::mma(hi, qf[rt][c], acc[cc][rt]);
-            acc[cc][rt] = M::mma(lo, qf[rt][c], acc[cc][rt]);
-          }
-        } else {
-          frag sf;
-          sf.lo = s0;
-          sf.hi = s1;
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[cc][rt] = M::mma(sf, qf[rt][c], acc[cc][rt]);
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? s0[e] : s1[e - 4];
+          sh[cc][c][e] = (bf16)x;
+          sl[cc][c][e] = (bf16)(x - (float)sh[cc][c][e]);
         }
+      } else {
+        sh[cc][c].lo = s0;
+        sh[cc][c].hi = s1;
       }
     }
   }
-#pragma unroll
-  for (int cc = 0; cc < CT; ++cc)
+
+  const uint32_t HQB = (uint32_t)(H * DK * ES), HOB = (uint32_t)(H * DV * 4);
+  auto rows_of = [&](int jb) {
+    const int64_t r = fend - (f0 + 64 * (int64_t)jb);
+    return (int)(r < 64 ? r : 64);
+  };
+  auto qres = [&](int jb) {
+    const int64_t fs = f0 + 64 * (int64_t)jb;
+    return make_rsrc(static_cast<const MT*>(a.q) + ((b * T + fs) * H + h) * DK, (uint32_t)(rows_of(jb) - 1) * HQB + DK * ES);
+  };
+  auto load_q = [&](int jb, frag (&qf)[4][KC]) {
+    const rsrc_t rq = qres(jb);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
-      bstore16(ro, (uint32_t)(16 * rt + l16) * HOB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * 4u, acc[cc][rt] * rqs[rt]);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qf[rt][c] = bload_frag<MT>(rq, (uint32_t)(16 * rt + l16) * HQB + (32 * c + 8 * g4) * ES);
+  };
+  frag qf[4][KC];
+  load_q(jb0, qf);
+  for (int jb = jb0; jb < jb1; ++jb) {
+    const int rows = rows_of(jb);
+    if (rows <= 0) break;
+    float rqs[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = M::get(qf[rt][c], e);
+          ss = fmaf(x, x, ss);
+        }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      rqs[rt] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
+    }
+    f32x4 acc[CT][4];
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[cc][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF) {
+      // the next block's q is in flight while this block's products run
+      frag qn[4][KC];
+      const bool more = jb + 1 < jb1 && rows_of(jb + 1) > 0;
+      if (more) load_q(jb + 1, qn);
+#pragma unroll
+      for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            acc[cc][rt] = M::mma(sh[cc][c], qf[rt][c], acc[cc][rt]);
+            acc[cc][rt] = M::mma(sl[cc][c], qf[rt][c], acc[cc][rt]);
+          }
+      if (more) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int c = 0; c < KC; ++c) qf[rt][c] = qn[rt][c];
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) acc[cc][rt] = M::mma(sh[cc][c], qf[rt][c], acc[cc][rt]);
+      if (jb + 1 < jb1 && rows_of(jb + 1) > 0) load_q(jb + 1, qf);
+    }
+    const int64_t fs = f0 + 64 * (int64_t)jb;
+    const rsrc_t ro = make_rsrc(a.out + ((b * T + fs) * H + h) * DV, (uint32_t)(rows - 1) * HOB + DV * 4);
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        bstore16(ro, (uint32_t)(16 * rt + l16) * HOB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * 4u, acc[cc][rt] * rqs[rt]);
+  }
 }
 
 template <typename MT, int DK, int DV>
 hipError_t launch_vda(const VdaArgs& a, hipStream_t stream, hipEvent_t* ev) {
   const int BH = (int)(a.B * a.H);
   if (a.NF > 0) {
-    hipLaunchKernelGGL((vda_frame_kernel<MT, DK, DV>), dim3((unsigned)(a.dirs * BH * a.NF)), dim3(256), 0, stream, a);
+    const int64_t U = (int64_t)BH * a.NF;
+    const int64_t grid = a.dirs == 2 ? 2 * ((U + 7) / 8) * 8 : U;
+    hipLaunchKernelGGL((vda_frame_kernel<MT, DK, DV>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((vda_chain_kernel<DK, DV>), dim3((unsigned)(a.dirs * BH * (DV / 16))), dim3(256), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  {
+    const int64_t chains = (int64_t)a.dirs * BH;
+    hipLaunchKernelGGL((vda_chain_kernel<DK, DV>), dim3((unsigned)(((chains + 7) / 8) * 8 * (DV / 16))), dim3(256), 0,
+                       stream, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return hipErrorLaunchFailure;
   if (a.NF > 0) {
+    // runs of up to eight 64-token blocks, split evenly over the frame
     const int nblk = (int)((a.frame + 63) / 64);
-    hipLaunchKernelGGL((vda_readout_kernel<MT, DK, DV>), dim3((unsigned)(a.NF * nblk), (unsigned)BH), dim3(256), 0,
-                       stream, a, nblk);
+    const int nsplit = (nblk + 7) / 8;
+    const int bpw = (nblk + nsplit - 1) / nsplit;
+    hipLaunchKernelGGL((vda_readout_kernel<MT, DK, DV>), dim3((unsigned)(a.NF * ((nblk + bpw - 1) / bpw)), (unsigned)BH),
+                       dim3(256), 0, stream, a, nblk, bpw);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
