@@ -312,7 +312,11 @@ gdn_status_t vda_plan(const gdn_vda_problem_t* p, int32_t direction, int* dirs, 
   if ((p->T + 64) * p->H * (p->dk > p->dv ? p->dk : p->dv) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
   *dirs = direction == GDN_DIR_BIDIRECTIONAL ? 2 : 1;
   *NF = (p->T + p->frame - 1) / p->frame;
-  if ((int64_t)*dirs * p->B * p->H * *NF > ((int64_t)1 << 31) - 1) return GDN_ERR_UNSUPPORTED;  // grid size
+  // grid sizes: frame kernel (padded to groups of eight per direction) and
+  // readout (runs of up to eight 64-token blocks per frame)
+  const int64_t BH = p->B * p->H, nblk = (p->frame + 63) / 64;
+  if (2 * ((BH * *NF + 7) / 8) * 8 > ((int64_t)1 << 31) - 1) return GDN_ERR_UNSUPPORTED;
+  if (BH * *NF * ((nblk + 7) / 8) > ((int64_t)1 << 31) - 1) return GDN_ERR_UNSUPPORTED;
   *L = vda_layout(p->B * p->H, *NF, *dirs, p->dk, p->dv);
   return GDN_OK;
 }

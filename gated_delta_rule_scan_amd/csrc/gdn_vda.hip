@@ -88,7 +88,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     u = blockIdx.x;
   }
   if (u >= U) return;  // padding of the last group of eight
-  const int bh = (int)(u / NF), f = (int)(u % NF);
+  // batch*head fastest: workgroups running together read whole token rows
+  // (all heads) of the same frames
+  const int bh = (int)(u % BH), f = (int)(u / BH);
   const int64_t b = bh / a.H, h = bh % a.H;
   const int64_t T = a.T, H = a.H, Fr = a.frame;
   const int64_t t0 = (int64_t)f * Fr;
@@ -313,12 +315,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
       }
     }
     float* mg = a.minv + fid * (size_t)DK * DK;
+    if constexpr (SM::BF) {
+      // bf16 inputs: M_t as two bf16 planes, hi then lo (hi + lo = M_t to
+      // about 2^-17 relative), the operands of the chain's matrix cores
+      bf16* mh = reinterpret_cast<bf16*>(mg);
+      bf16* ml = mh + (size_t)DK * DK;
 #pragma unroll
-    for (int i = 0; i < BS; ++i)
+      for (int i = 0; i < BS; ++i)
 #pragma unroll
-      for (int j = 0; j < BS; j += 4)
-        *reinterpret_cast<f32x4*>(mg + (size_t)(ty * BS + i) * DK + tx * BS + j) =
-            f32x4{m[i][j], m[i][j + 1], m[i][j + 2], m[i][j + 3]};
+        for (int j = 0; j < BS; j += 4) {
+          bf16x4 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = (bf16)m[i][j + e];
+            lo[e] = (bf16)(m[i][j + e] - (float)hi[e]);
+          }
+          const size_t o = (size_t)(ty * BS + i) * DK + tx * BS + j;
+          *reinterpret_cast<bf16x4*>(mh + o) = hi;
+          *reinterpret_cast<bf16x4*>(ml + o) = lo;
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; j += 4)
+          *reinterpret_cast<f32x4*>(mg + (size_t)(ty * BS + i) * DK + tx * BS + j) =
+              f32x4{m[i][j], m[i][j + 1], m[i][j + 2], m[i][j + 3]};
+    }
   }
 }
 
@@ -353,22 +376,26 @@ __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
   const size_t fbase = ((size_t)slot * BH + bh) * NF;
   const float* lag = a.log_alpha + ((size_t)slot * a.B + b) * NF * a.H + h;
 
-  // the lane's share of a 16 x DK row tile: row l16, columns 16 l + 4 g4 .. + 3
+  // the lane's share of a 16 x DK row tile: row l16, columns 16 l + 4 g4 .. + 3.
+  // A ring of three register sets holds M, B and the decay of frames s .. s+2:
+  // each step consumes one and refills it for frame s + 3 (clamped at the last
+  // frame, so every step issues the same loads).
   auto frame_of = [&](int s) { return rev ? NF - 1 - s : s; };
-  F32::frag mf[NLW][KC];
-  f32x4 bn[NLW];
-  float an = 0.f;
-  auto fetch = [&](int f) {
+  F32::frag mf[3][NLW][KC];
+  f32x4 bn[3][NLW];
+  float an[3];
+  auto fetch = [&](int k, int s) {
+    const int f = frame_of(s < NF ? s : NF - 1);
     const float* mg = a.minv + (fbase + f) * (size_t)DK * DK;
     const float* bg = a.bmat + (fbase + f) * (size_t)DV * DK + (size_t)16 * tile * DK;
 #pragma unroll
     for (int lw = 0; lw < NLW; ++lw) {
       const int l = NLW * w + lw;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) mf[lw][c] = F32::load(mg + (size_t)(16 * l + l16) * DK + 32 * c + 8 * g4);
-      bn[lw] = *reinterpret_cast<const f32x4*>(bg + (size_t)l16 * DK + 16 * l + 4 * g4);
+      for (int c = 0; c < KC; ++c) mf[k][lw][c] = F32::load(mg + (size_t)(16 * l + l16) * DK + 32 * c + 8 * g4);
+      bn[k][lw] = *reinterpret_cast<const f32x4*>(bg + (size_t)l16 * DK + 16 * l + 4 * g4);
     }
-    an = expf(lag[(size_t)f * a.H]);
+    an[k] = lag[(size_t)f * a.H];
   };
   f32x4 snew[NLW];
 #pragma unroll
@@ -377,13 +404,23 @@ __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
     snew[lw] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + srow + (size_t)l16 * DK + 16 * l + 4 * g4)
                           : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (NF > 0) fetch(frame_of(0));
-  for (int s = 0; s < NF; ++s) {
-    const int f = frame_of(s);
+  if (NF > 0) {
+    fetch(0, 0);
+    fetch(1, 1);
+    fetch(2, 2);
+  }
+  // drain the prologue's loads: the loop head then sees only the loads of its
+  // own previous turn (issued in a fixed order), and waits for no more than it needs
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  auto step = [&](int s, int k) {
+    // keep each step's work inside the step: work hoisted from the next step
+    // would wait for loads issued just before
+    __builtin_amdgcn_sched_barrier(0);
+    const float at = expf(an[k]);
 #pragma unroll
     for (int lw = 0; lw < NLW; ++lw) {
       const int l = NLW * w + lw;
-      *reinterpret_cast<f32x4*>(Rs + l16 * SP + 16 * l + 4 * g4) = snew[lw] * an + bn[lw];
+      *reinterpret_cast<f32x4*>(Rs + l16 * SP + 16 * l + 4 * g4) = snew[lw] * at + bn[k][lw];
     }
     __syncthreads();  // Rs holds R_t
     // (M R^T) tile l lands in lane (l16, g4) as S_t[l16][16 l + 4 g4 + i]
@@ -391,18 +428,28 @@ __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
     for (int lw = 0; lw < NLW; ++lw) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) acc = F32::mma(mf[lw][c], F32::load(Rs + l16 * SP + 32 * c + 8 * g4), acc);
+      for (int c = 0; c < KC; ++c) acc = F32::mma(mf[k][lw][c], F32::load(Rs + l16 * SP + 32 * c + 8 * g4), acc);
       snew[lw] = acc;
     }
-    if (s + 1 < NF) fetch(frame_of(s + 1));
-    float* sg = a.sfr + (fbase + f) * (size_t)DV * DK + (size_t)16 * tile * DK;
+    float* sg = a.sfr + (fbase + frame_of(s)) * (size_t)DV * DK + (size_t)16 * tile * DK;
 #pragma unroll
     for (int lw = 0; lw < NLW; ++lw) {
       const int l = NLW * w + lw;
       *reinterpret_cast<f32x4*>(sg + (size_t)l16 * DK + 16 * l + 4 * g4) = snew[lw];
     }
+    fetch(k, s + 3);
     __syncthreads();  // every wave has read R_t
+  };
+  // whole turns of the ring, then the remainder (the loop is entered only
+  // from full turns, so the wait counts at its head stay exact)
+  int s0 = 0;
+  for (; s0 + 3 <= NF; s0 += 3) {
+    step(s0, 0);
+    step(s0 + 1, 1);
+    step(s0 + 2, 2);
   }
+  if (s0 < NF) step(s0, 0);
+  if (s0 + 1 < NF) step(s0 + 1, 1);
   if (a.state_out) {
 #pragma unroll
     for (int lw = 0; lw < NLW; ++lw) {
@@ -413,10 +460,162 @@ __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The same chain for bf16 inputs: 32 state rows per workgroup, and the
+// product R_t M_t on the bf16 matrix cores as Rh Mh + Rl Mh + Rh Ml, with
+// R_t and M_t split into hi + lo bf16 parts (M_t arrives split from the frame
+// kernel; the dropped Rl Ml term is about 2^-16 of the product).  A ring of
+// two register sets holds M, B and the decay of frames s and s + 1 (the
+// chain streams every frame's M_t and B_t from HBM; a deeper ring does not
+// make it faster).
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void vda_chain_bf16_kernel(VdaArgs a) {
+  using M = Mma<bf16>;
+  using frag = M::frag;
+  constexpr int RT = 2;               // 16-row sub-tiles per workgroup
+  constexpr int NT = DV / (16 * RT);  // workgroups per chain
+  constexpr int NLW = DK / 64;        // output column tiles per wave
+  constexpr int KC = DK / 32;         // contraction steps
+  constexpr int RP = DK + 8;          // bf16 pitch of R_t's rows
+  constexpr int kRing = 2;             // frames in flight
+  static_assert(NT >= 1, "dv is a multiple of 32");
+  __shared__ __align__(16) bf16 Rh[16 * RT * RP];
+  __shared__ __align__(16) bf16 Rl[16 * RT * RP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int NF = (int)a.NF, BH = (int)(a.B * a.H);
+  // the NT workgroups of one chain share an XCD (ids equal mod 8)
+  const int g = blockIdx.x >> 3;
+  const int tile = g % NT;
+  const int chain = (g / NT) * 8 + (blockIdx.x & 7);
+  if (chain >= a.dirs * BH) return;
+  const int bh = chain % BH;
+  const int slot = chain / BH;
+  const bool rev = a.rev_on && (slot == 1 || !a.fwd_on);
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const size_t srow = (((size_t)slot * a.B + b) * a.H + h) * DV * DK + (size_t)16 * RT * tile * DK;  // state rows
+  const size_t fbase = ((size_t)slot * BH + bh) * NF;
+  const float* lag = a.log_alpha + ((size_t)slot * a.B + b) * NF * a.H + h;
+
+  // the lane's share of the 32 x DK row tile: rows 16 rt + l16, columns 16 l + 4 g4 .. + 3
+  auto frame_of = [&](int s) { return rev ? NF - 1 - s : s; };
+  frag mh[kRing][NLW][KC], ml[kRing][NLW][KC];
+  f32x4 bn[kRing][RT][NLW];
+  float an[kRing];
+  auto fetch = [&](int k, int s) {
+    const int f = frame_of(s < NF ? s : NF - 1);
+    const bf16* mg = reinterpret_cast<const bf16*>(a.minv + (fbase + f) * (size_t)DK * DK);
+    const float* bg = a.bmat + (fbase + f) * (size_t)DV * DK + srow % ((size_t)DV * DK);
+#pragma unroll
+    for (int lw = 0; lw < NLW; ++lw) {
+      const int l = NLW * w + lw;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const size_t o = (size_t)(16 * l + l16) * DK + 32 * c + 8 * g4;
+        mh[k][lw][c] = M::load(mg + o);
+        ml[k][lw][c] = M::load(mg + (size_t)DK * DK + o);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        bn[k][rt][lw] = *reinterpret_cast<const f32x4*>(bg + (size_t)(16 * rt + l16) * DK + 16 * l + 4 * g4);
+    }
+    an[k] = lag[(size_t)f * a.H];
+  };
+  f32x4 snew[RT][NLW];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int lw = 0; lw < NLW; ++lw) {
+      const int l = NLW * w + lw;
+      snew[rt][lw] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + srow + (size_t)(16 * rt + l16) * DK +
+                                                                    16 * l + 4 * g4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  if (NF > 0) {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) fetch(k, k);
+  }
+  // drain the prologue's loads: the loop head then sees only the loads of its
+  // own previous turn (issued in a fixed order), and waits for no more than it needs
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  auto step = [&](int s, int k) {
+    // keep each step's work inside the step: work hoisted from the next step
+    // would wait for loads issued just before
+    __builtin_amdgcn_sched_barrier(0);
+    const float at = expf(an[k]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int lw = 0; lw < NLW; ++lw) {
+        const int l = NLW * w + lw;
+        const f32x4 r = snew[rt][lw] * at + bn[k][rt][lw];
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = (bf16)r[e];
+          lo[e] = (bf16)(r[e] - (float)hi[e]);
+        }
+        *reinterpret_cast<bf16x4*>(Rh + (16 * rt + l16) * RP + 16 * l + 4 * g4) = hi;
+        *reinterpret_cast<bf16x4*>(Rl + (16 * rt + l16) * RP + 16 * l + 4 * g4) = lo;
+      }
+    __syncthreads();  // Rh, Rl hold R_t
+    // (M R^T) tile (rt, l) lands in lane (l16, g4) as S_t[16 rt + l16][16 l + 4 g4 + i]
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int lw = 0; lw < NLW; ++lw) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const frag rh = M::load(Rh + (16 * rt + l16) * RP + 32 * c + 8 * g4);
+          const frag rl = M::load(Rl + (16 * rt + l16) * RP + 32 * c + 8 * g4);
+          acc = M::mma(mh[k][lw][c], rh, acc);
+          acc = M::mma(mh[k][lw][c], rl, acc);
+          acc = M::mma(ml[k][lw][c], rh, acc);
+        }
+        snew[rt][lw] = acc;
+      }
+    // the state store goes out before the next loads, so the wait that frees
+    // its registers at the next step does not wait for those loads
+    float* sg = a.sfr + (fbase + frame_of(s)) * (size_t)DV * DK + srow % ((size_t)DV * DK);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int lw = 0; lw < NLW; ++lw) {
+        const int l = NLW * w + lw;
+        *reinterpret_cast<f32x4*>(sg + (size_t)(16 * rt + l16) * DK + 16 * l + 4 * g4) = snew[rt][lw];
+      }
+    fetch(k, s + kRing);
+    __syncthreads();  // every wave has read R_t
+  };
+  // whole turns of the ring, then the remainder (the loop is entered only
+  // from whole turns, so the wait counts at its head stay exact)
+  int s0 = 0;
+  for (; s0 + kRing <= NF; s0 += kRing) {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) step(s0 + k, k);
+  }
+#pragma unroll
+  for (int k = 0; k < kRing - 1; ++k)
+    if (s0 + k < NF) step(s0 + k, k);
+  if (a.state_out) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int lw = 0; lw < NLW; ++lw) {
+        const int l = NLW * w + lw;
+        *reinterpret_cast<f32x4*>(a.state_out + srow + (size_t)(16 * rt + l16) * DK + 16 * l + 4 * g4) = snew[rt][lw];
+      }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
 // Readout: o_i = S_t q^_i, both directions summed (o = (S_fwd + S_rev) q^).
 // One workgroup per (batch*head, frame, run of 64-token blocks); the summed
 // state is split once into the matrix cores' operands and kept in registers
-// while the run's blocks stream through.  Computed transposed (O^T = S Q^T,
+// while the run's blocks stream through LDS.  Computed transposed (O^T = S Q^T,
 // Q raw, rows scaled by 1/|q| after), so each lane holds four consecutive
 // values of one token's output row; wave w owns the w-th quarter of the dv
 // columns.
@@ -435,29 +634,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   const int l16 = lane & 15, g4 = lane >> 4;
   const int NF = (int)a.NF, BH = (int)(a.B * a.H);
   const int nsplit = (nblk + bpw - 1) / bpw;
-  const int f = blockIdx.x / nsplit, js = blockIdx.x % nsplit;
-  const int bh = blockIdx.y;
+  // batch*head fastest: workgroups running together cover whole token rows
+  const int bh = (int)(blockIdx.x % (unsigned)BH);
+  const int fj = (int)(blockIdx.x / (unsigned)BH);
+  const int f = fj / nsplit, js = fj % nsplit;
   const int jb0 = js * bpw, jb1 = jb0 + bpw < nblk ? jb0 + bpw : nblk;
   const int64_t b = bh / a.H, h = bh % a.H, T = a.T, H = a.H;
   const int64_t f0 = (int64_t)f * a.frame;
   const int64_t fend = f0 + a.frame < T ? f0 + a.frame : T;
   if (f0 + 64 * (int64_t)jb0 >= fend) return;
 
-  // summed state rows 16 ct + l16, columns 32 c + 8 g4 .. + 7
+  // summed state rows 16 ct + l16, columns 32 c + 8 g4 .. + 7 (every load
+  // issued before the first use)
   frag sh[CT][KC];
   [[maybe_unused]] frag sl[CT][KC];
+  f32x4 sp[2][CT][KC][2];
+#pragma unroll
+  for (int slot = 0; slot < 2; ++slot)
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int ss = slot < a.dirs ? slot : 0;
+        const float* src = a.sfr + (((size_t)ss * BH + bh) * NF + f) * (size_t)DV * DK +
+                           (size_t)(16 * (CT * w + cc) + l16) * DK + 32 * c + 8 * g4;
+        sp[slot][cc][c][0] = *reinterpret_cast<const f32x4*>(src);
+        sp[slot][cc][c][1] = *reinterpret_cast<const f32x4*>(src + 4);
+      }
 #pragma unroll
   for (int cc = 0; cc < CT; ++cc) {
-    const int ct = CT * w + cc;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-      for (int slot = 0; slot < a.dirs; ++slot) {
-        const float* src = a.sfr + (((size_t)slot * BH + bh) * NF + f) * (size_t)DV * DK + (size_t)(16 * ct + l16) * DK +
-                           32 * c + 8 * g4;
-        s0 += *reinterpret_cast<const f32x4*>(src);
-        s1 += *reinterpret_cast<const f32x4*>(src + 4);
-      }
+      // the second direction's part enters scaled by 1 or 0 (a branch here
+      // would move its loads behind a wait of their own)
+      const float m1 = a.dirs == 2 ? 1.f : 0.f;
+      const f32x4 s0 = sp[0][cc][c][0] + sp[1][cc][c][0] * m1;
+      const f32x4 s1 = sp[0][cc][c][1] + sp[1][cc][c][1] * m1;
       if constexpr (BF) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -473,83 +685,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   }
 
   const uint32_t HQB = (uint32_t)(H * DK * ES), HOB = (uint32_t)(H * DV * 4);
+  // blocks jb0 .. jend-1 hold tokens of this frame
+  const int64_t nrem = (fend - (f0 + 64 * (int64_t)jb0) + 63) / 64;
+  const int jend = jb0 + (int)(nrem < jb1 - jb0 ? nrem : jb1 - jb0);
   auto rows_of = [&](int jb) {
     const int64_t r = fend - (f0 + 64 * (int64_t)jb);
     return (int)(r < 64 ? r : 64);
   };
-  auto qres = [&](int jb) {
+  // q blocks are staged through LDS (double-buffered): each thread loads its
+  // share of a block -- 16-byte pieces, a row's pieces on consecutive threads --
+  // kDepth blocks ahead of use, so every wave reads its fragments from LDS
+  constexpr int QP = DK + 16 / ES;            // row pitch in elements (16 bytes of padding)
+  constexpr int PR = DK * ES / 16;            // 16-byte pieces per row
+  constexpr int NPQ = 64 * PR / 256;          // pieces per thread per block
+  constexpr int kDepth = BF ? 3 : 1;          // blocks in flight per thread
+  __shared__ __align__(16) MT qs[2][64 * QP];
+  auto load_q = [&](int jb, f32x4 (&qr)[NPQ]) {
     const int64_t fs = f0 + 64 * (int64_t)jb;
-    return make_rsrc(static_cast<const MT*>(a.q) + ((b * T + fs) * H + h) * DK, (uint32_t)(rows_of(jb) - 1) * HQB + DK * ES);
-  };
-  auto load_q = [&](int jb, frag (&qf)[4][KC]) {
-    const rsrc_t rq = qres(jb);
+    const rsrc_t rq = make_rsrc(static_cast<const MT*>(a.q) + ((b * T + fs) * H + h) * DK,
+                                (uint32_t)(rows_of(jb) - 1) * HQB + DK * ES);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int c = 0; c < KC; ++c) qf[rt][c] = bload_frag<MT>(rq, (uint32_t)(16 * rt + l16) * HQB + (32 * c + 8 * g4) * ES);
+    for (int i = 0; i < NPQ; ++i) {
+      const int pc = i * 256 + tid;
+      qr[i] = bload16(rq, (uint32_t)(pc / PR) * HQB + (uint32_t)(pc % PR) * 16u);
+    }
   };
-  frag qf[4][KC];
-  load_q(jb0, qf);
-  for (int jb = jb0; jb < jb1; ++jb) {
-    const int rows = rows_of(jb);
-    if (rows <= 0) break;
+  f32x4 qr[kDepth][NPQ];
+  auto block = [&](int jb, int k) {
+    __builtin_amdgcn_sched_barrier(0);
+    MT* qb = qs[(jb - jb0) & 1];
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) {
+      const int pc = i * 256 + tid;
+      *reinterpret_cast<f32x4*>(qb + (pc / PR) * QP + (pc % PR) * (16 / ES)) = qr[k][i];
+    }
+    // refill this slot kDepth blocks ahead (clamped to the last block)
+    load_q(jb + kDepth < jend ? jb + kDepth : jend - 1, qr[k]);
+    __syncthreads();  // the block is in LDS; the buffer written two blocks ago is free
+    // one 16-token row tile at a time: its fragments, its norms, its products
+    f32x4 acc[CT][4];
     float rqs[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
+      frag qf[KC];
       float ss = 0.f;
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
+      for (int c = 0; c < KC; ++c) {
+        qf[c] = M::load(qb + (16 * rt + l16) * QP + 32 * c + 8 * g4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = M::get(qf[rt][c], e);
+          const float x = M::get(qf[c], e);
           ss = fmaf(x, x, ss);
         }
+      }
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
       rqs[rt] = 1.0f / fmaxf(sqrtf(ss), kNormEps);
-    }
-    f32x4 acc[CT][4];
 #pragma unroll
-    for (int cc = 0; cc < CT; ++cc)
+      for (int cc = 0; cc < CT; ++cc) {
+        acc[cc][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[cc][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF) {
-      // the next block's q is in flight while this block's products run
-      frag qn[4][KC];
-      const bool more = jb + 1 < jb1 && rows_of(jb + 1) > 0;
-      if (more) load_q(jb + 1, qn);
-#pragma unroll
-      for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            acc[cc][rt] = M::mma(sh[cc][c], qf[rt][c], acc[cc][rt]);
-            acc[cc][rt] = M::mma(sl[cc][c], qf[rt][c], acc[cc][rt]);
-          }
-      if (more) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int c = 0; c < KC; ++c) qf[rt][c] = qn[rt][c];
+        for (int c = 0; c < KC; ++c) {
+          acc[cc][rt] = M::mma(sh[cc][c], qf[c], acc[cc][rt]);
+          if constexpr (BF) acc[cc][rt] = M::mma(sl[cc][c], qf[c], acc[cc][rt]);
+        }
       }
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[cc][rt] = M::mma(sh[cc][c], qf[rt][c], acc[cc][rt]);
-      if (jb + 1 < jb1 && rows_of(jb + 1) > 0) load_q(jb + 1, qf);
     }
     const int64_t fs = f0 + 64 * (int64_t)jb;
-    const rsrc_t ro = make_rsrc(a.out + ((b * T + fs) * H + h) * DV, (uint32_t)(rows - 1) * HOB + DV * 4);
+    const rsrc_t ro = make_rsrc(a.out + ((b * T + fs) * H + h) * DV, (uint32_t)(rows_of(jb) - 1) * HOB + DV * 4);
 #pragma unroll
     for (int cc = 0; cc < CT; ++cc)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
         bstore16(ro, (uint32_t)(16 * rt + l16) * HOB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * 4u, acc[cc][rt] * rqs[rt]);
+  };
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) load_q(jb0 + k < jend ? jb0 + k : jend - 1, qr[k]);
+  // whole turns of the ring, then the remainder
+  int jb = jb0;
+  for (; jb + kDepth <= jend; jb += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) block(jb + k, k);
   }
+#pragma unroll
+  for (int k = 0; k < kDepth - 1; ++k)
+    if (jb + k < jend) block(jb + k, k);
 }
 
 template <typename MT, int DK, int DV>
@@ -563,9 +783,13 @@ hipError_t launch_vda(const VdaArgs& a, hipStream_t stream, hipEvent_t* ev) {
   }
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return hipErrorLaunchFailure;
   {
-    const int64_t chains = (int64_t)a.dirs * BH;
-    hipLaunchKernelGGL((vda_chain_kernel<DK, DV>), dim3((unsigned)(((chains + 7) / 8) * 8 * (DV / 16))), dim3(256), 0,
-                       stream, a);
+    const int64_t groups = ((int64_t)a.dirs * BH + 7) / 8;
+    if constexpr (sizeof(MT) == 2) {
+      hipLaunchKernelGGL((vda_chain_bf16_kernel<DK, DV>), dim3((unsigned)(groups * 8 * (DV / 32))), dim3(256), 0,
+                         stream, a);
+    } else {
+      hipLaunchKernelGGL((vda_chain_kernel<DK, DV>), dim3((unsigned)(groups * 8 * (DV / 16))), dim3(256), 0, stream, a);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return hipErrorLaunchFailure;
@@ -574,8 +798,8 @@ hipError_t launch_vda(const VdaArgs& a, hipStream_t stream, hipEvent_t* ev) {
     const int nblk = (int)((a.frame + 63) / 64);
     const int nsplit = (nblk + 7) / 8;
     const int bpw = (nblk + nsplit - 1) / nsplit;
-    hipLaunchKernelGGL((vda_readout_kernel<MT, DK, DV>), dim3((unsigned)(a.NF * ((nblk + bpw - 1) / bpw)), (unsigned)BH),
-                       dim3(256), 0, stream, a, nblk, bpw);
+    hipLaunchKernelGGL((vda_readout_kernel<MT, DK, DV>), dim3((unsigned)(BH * a.NF * ((nblk + bpw - 1) / bpw))), dim3(256),
+                       0, stream, a, nblk, bpw);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
