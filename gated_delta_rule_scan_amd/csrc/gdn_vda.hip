@@ -26,7 +26,7 @@ struct VdaSmem {
   static constexpr bool BF = sizeof(MT) == 2;
   static constexpr int ES = (int)sizeof(MT);
   static constexpr int EP = 16 / ES;            // elements per 16-byte piece
-  static constexpr int TB = 32;                 // tokens per block: one matrix-core contraction
+  static constexpr int TB = BF ? 64 : 32;       // tokens per block: one or two matrix-core contractions
   static constexpr int RP = DK + 8, VP = DV + 8;  // bf16 row-major staging pitches
   static constexpr int TP = TB + 4;             // fp32 transposed staging pitch
   static constexpr size_t stage_bytes = BF ? (size_t)TB * (RP + VP) * 2 : (size_t)(DK + DV) * TP * 4;
@@ -176,38 +176,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     if (blk + TB < n) issue(blk + TB);
     __syncthreads();
 
-    // the lane's eight tokens are 8 g4 .. 8 g4 + 7 of the block
-    const f32x4 wa0 = *reinterpret_cast<const f32x4*>(&s_wa[buf][8 * g4]);
-    const f32x4 wa1 = *reinterpret_cast<const f32x4*>(&s_wa[buf][8 * g4 + 4]);
-    const f32x4 wb0 = *reinterpret_cast<const f32x4*>(&s_wb[buf][8 * g4]);
-    const f32x4 wb1 = *reinterpret_cast<const f32x4*>(&s_wb[buf][8 * g4 + 4]);
+    // the lane's eight tokens of contraction kc are 32 kc + 8 g4 .. + 7 of the block
     if constexpr (SM::BF) {
       const MT* Ks = reinterpret_cast<const MT*>(stage);
       const MT* Vs = Ks + TB * RP;
-      frag kr[NL];  // raw k^T, one fragment per dk column tile
 #pragma unroll
-      for (int l = 0; l < NL; ++l) kr[l] = load_kt_frag(Ks, RP, 0, 16 * l, l16, g4);
+      for (int kc = 0; kc < TB / 32; ++kc) {
+        const f32x4 wa0 = *reinterpret_cast<const f32x4*>(&s_wa[buf][32 * kc + 8 * g4]);
+        const f32x4 wa1 = *reinterpret_cast<const f32x4*>(&s_wa[buf][32 * kc + 8 * g4 + 4]);
+        const f32x4 wb0 = *reinterpret_cast<const f32x4*>(&s_wb[buf][32 * kc + 8 * g4]);
+        const f32x4 wb1 = *reinterpret_cast<const f32x4*>(&s_wb[buf][32 * kc + 8 * g4 + 4]);
+        frag kr[NL];  // raw k^T, one fragment per dk column tile
 #pragma unroll
-      for (int j = 0; j < NJA; ++j) {
-        frag xh, xl;
-        scale_split(load_kt_frag(Ks, RP, 0, 16 * (NJA * w + j), l16, g4), wa0, wa1, xh, xl);
+        for (int l = 0; l < NL; ++l) kr[l] = load_kt_frag(Ks, RP, 32 * kc, 16 * l, l16, g4);
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          accA[j][l] = M::mma(xh, kr[l], accA[j][l]);
-          accA[j][l] = M::mma(xl, kr[l], accA[j][l]);
+        for (int j = 0; j < NJA; ++j) {
+          frag xh, xl;
+          scale_split(load_kt_frag(Ks, RP, 32 * kc, 16 * (NJA * w + j), l16, g4), wa0, wa1, xh, xl);
+#pragma unroll
+          for (int l = 0; l < NL; ++l) {
+            accA[j][l] = M::mma(xh, kr[l], accA[j][l]);
+            accA[j][l] = M::mma(xl, kr[l], accA[j][l]);
+          }
         }
-      }
 #pragma unroll
-      for (int j = 0; j < NJB; ++j) {
-        frag yh, yl;
-        scale_split(load_kt_frag(Vs, VP, 0, 16 * (NJB * w + j), l16, g4), wb0, wb1, yh, yl);
+        for (int j = 0; j < NJB; ++j) {
+          frag yh, yl;
+          scale_split(load_kt_frag(Vs, VP, 32 * kc, 16 * (NJB * w + j), l16, g4), wb0, wb1, yh, yl);
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          accB[j][l] = M::mma(yh, kr[l], accB[j][l]);
-          accB[j][l] = M::mma(yl, kr[l], accB[j][l]);
+          for (int l = 0; l < NL; ++l) {
+            accB[j][l] = M::mma(yh, kr[l], accB[j][l]);
+            accB[j][l] = M::mma(yl, kr[l], accB[j][l]);
+          }
         }
       }
     } else {
+      static_assert(SM::BF || TB == 32, "fp32 staging holds one contraction");
+      const f32x4 wa0 = *reinterpret_cast<const f32x4*>(&s_wa[buf][8 * g4]);
+      const f32x4 wa1 = *reinterpret_cast<const f32x4*>(&s_wa[buf][8 * g4 + 4]);
+      const f32x4 wb0 = *reinterpret_cast<const f32x4*>(&s_wb[buf][8 * g4]);
+      const f32x4 wb1 = *reinterpret_cast<const f32x4*>(&s_wb[buf][8 * g4 + 4]);
       const float* KT = reinterpret_cast<const float*>(stage);
       const float* VT = KT + DK * TP;
       frag kr[NL];
