@@ -138,3 +138,153 @@ def test_reverse_and_bidirectional(T, frame):
                              fl(sl(x["beta"], 1), 2), sl(x["state_in"], 1), "fwd", frame)
     assert np.allclose(fl(o_ff, 1), o_r, rtol=0, atol=1e-12)
     assert np.allclose(s_ff, s_r, rtol=0, atol=1e-12)
+
+
+# ---- additive frame writes (summed per-token corrections, keys / sqrt(U)) ----
+
+def test_additive_one_token_frames_equal_the_token_delta_rule():
+    # U = 1: the correction of the only token is the delta rule itself
+    for direction in ("fwd", "rev", "bi"):
+        x = _inputs(T=40, frame=1, direction=direction, seed=7)
+        o1, s1 = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction, 1,
+                             write="additive")
+        o2, s2 = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction)
+        assert np.max(np.abs(o1 - o2)) <= 1e-9 * max(1.0, np.max(np.abs(o2)))
+        assert np.max(np.abs(s1 - s2)) <= 1e-9 * max(1.0, np.max(np.abs(s2)))
+
+
+def test_additive_token_order_inside_a_frame_does_not_matter():
+    x = _inputs(T=64, frame=32, direction="bi", seed=8)
+    o1, s1 = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", 32, write="additive")
+    perm = np.concatenate([np.random.default_rng(2).permutation(32), 32 + np.random.default_rng(3).permutation(32)])
+    y = dict(x)
+    for n in ("q", "k", "v"):
+        y[n] = x[n][:, perm]
+    y["beta"] = x["beta"][:, :, perm]
+    o2, s2 = vda.forward(y["q"], y["k"], y["v"], y["log_alpha"], y["beta"], y["state_in"], "bi", 32, write="additive")
+    assert np.allclose(s1, s2, rtol=0, atol=1e-12)
+    assert np.allclose(o1[:, perm], o2, rtol=0, atol=1e-12)
+
+
+def test_additive_scaled_write_is_non_expansive_where_the_unscaled_one_expands():
+    rng = np.random.default_rng(9)
+    d, n = 8, 40
+    kh = rng.standard_normal(d)[None, :] + 0.2 * rng.standard_normal((n, d))
+    kh /= np.linalg.norm(kh, axis=1, keepdims=True)
+    S = rng.standard_normal((d, d))
+    # unscaled: S (I - A) with lambda_max(A) > 2 grows along the top eigenvector
+    A = kh.T @ kh
+    top = np.linalg.eigh(A)[1][:, -1]
+    S_top = np.outer(rng.standard_normal(d), top)
+    assert np.linalg.norm(S_top @ (np.eye(d) - A), 2) > np.linalg.norm(S_top, 2)
+    # scaled by 1/sqrt(U): never larger, for any beta in [0, 1]
+    for beta in (np.ones(n), rng.uniform(0, 1, n)):
+        for a in (1.0, 0.8):
+            S1 = vda.frame_update_additive(S, a, kh, np.zeros((n, d)), beta)
+            assert np.linalg.norm(S1, 2) <= a * np.linalg.norm(S, 2) + 1e-12
+            S2 = vda.frame_update_additive(S_top, a, kh, np.zeros((n, d)), beta)
+            assert np.linalg.norm(S2, 2) <= a * np.linalg.norm(S_top, 2) + 1e-12
+
+
+# ---- disjoint-region readout (lag) ----
+
+@pytest.mark.parametrize("lag", [1, 2])
+def test_lag_on_one_token_frames_is_the_lagged_token_readout(lag):
+    # forward, frames of one token: o_t = S_{t-lag} q^_t, where S_j is the token
+    # delta rule's state after token j (beta / (1 + beta)), taken from the C
+    # oracle run on the prefix; the initial state for t < lag
+    x = _inputs(T=12, frame=1, direction="fwd", seed=10)
+    o, _ = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "fwd", 1, lag=lag)
+    b2 = (x["beta"].astype(np.float64) / (1.0 + x["beta"].astype(np.float64))).astype(np.float32)
+    q = oracle.as_f32(x["q"]).astype(np.float64)
+    qh = q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-6)
+    for t in range(12):
+        j = t - lag + 1  # tokens 0 .. t-lag written
+        if j <= 0:
+            S = x["state_in"][0, 0].astype(np.float64)
+        else:
+            _, s = oracle.forward(x["q"][:, :j], x["k"][:, :j], x["v"][:, :j], x["log_alpha"][:, :, :j], b2[:, :, :j],
+                                  x["state_in"], "fwd")
+            S = s[0, 0]
+        want = np.einsum("hvk,hk->hv", S, qh[0, t])
+        assert np.allclose(o[0, t], want, rtol=0, atol=2e-6 * max(1.0, np.max(np.abs(want))))
+
+
+@pytest.mark.parametrize("lag", [0, 1, 3])
+def test_text_state_enters_once(lag):
+    # no writes (beta = 0) and no decay: every token reads S_T/2 from each direction
+    x = _inputs(T=48, frame=8, direction="bi", seed=11)
+    x["beta"] = np.zeros_like(x["beta"])
+    x["log_alpha"] = np.zeros_like(x["log_alpha"])
+    S_T = np.random.default_rng(4).standard_normal((1, 2, 16, 16))
+    half = np.stack([S_T / 2, S_T / 2])
+    o, _ = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], half, "bi", 8, lag=lag)
+    q = oracle.as_f32(x["q"]).astype(np.float64)
+    qh = q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-6)
+    assert np.allclose(o, np.einsum("bhvk,bthk->bthv", S_T, qh), rtol=0, atol=1e-12)
+
+
+def test_lagged_readouts_cover_disjoint_regions():
+    # lag 2, frames of 8 tokens, 6 frames: frame 2's writes reach the forward
+    # readout of frames >= 4 and the reverse readout of frames <= 0 only
+    x = _inputs(T=48, frame=8, direction="bi", seed=12)
+    o1, _ = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", 8, lag=2)
+    y = {n: np.array(x[n], copy=True) for n in ("k", "v", "beta")}
+    rng = np.random.default_rng(5)
+    y["k"][:, 16:24] = rng.standard_normal(y["k"][:, 16:24].shape).astype(np.float32)
+    y["v"][:, 16:24] = rng.standard_normal(y["v"][:, 16:24].shape).astype(np.float32)
+    y["beta"][:, :, 16:24] = rng.uniform(0, 1, y["beta"][:, :, 16:24].shape).astype(np.float32)
+    o2, _ = vda.forward(x["q"], y["k"], y["v"], x["log_alpha"], y["beta"], x["state_in"], "bi", 8, lag=2)
+    same = np.all(np.isclose(o1, o2, rtol=0, atol=1e-13), axis=(0, 2, 3)).reshape(6, 8).all(axis=1)
+    assert list(same) == [False, True, True, True, False, False]
+
+
+def test_lag_past_every_frame_reads_the_initial_states():
+    x = _inputs(T=40, frame=8, direction="bi", seed=13)
+    o, _ = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", 8, lag=5)
+    q = oracle.as_f32(x["q"]).astype(np.float64)
+    qh = q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-6)
+    S = x["state_in"].astype(np.float64).sum(axis=0)
+    assert np.allclose(o, np.einsum("bhvk,bthk->bthv", S, qh), rtol=0, atol=1e-12)
+
+
+# ---- readout epilogue (RMS normalisation and sigmoid gate) ----
+
+def _epilogue_case(seed=14):
+    x = _inputs(T=40, frame=8, direction="bi", seed=seed)
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((1, 40, 2, 16)).astype(np.float32)
+    wgt = rng.uniform(0.5, 1.5, 16)
+    return x, z, wgt
+
+
+def test_epilogue_is_invariant_to_the_scale_of_the_readout():
+    x, z, wgt = _epilogue_case()
+    o1, _ = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", 8, gate=z,
+                        norm_weight=wgt, norm_eps=0.0)
+    y = dict(x)
+    y["v"] = (x["v"] * 4.0).astype(np.float32)
+    y["state_in"] = (x["state_in"] * 4.0).astype(np.float32)
+    o2, _ = vda.forward(y["q"], y["k"], y["v"], y["log_alpha"], y["beta"], y["state_in"], "bi", 8, gate=z,
+                        norm_weight=wgt, norm_eps=0.0)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14)
+
+
+def test_epilogue_gives_unit_rms_per_token_and_head_with_an_open_gate():
+    x, z, _ = _epilogue_case(15)
+    o, _ = vda.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", 8,
+                       gate=np.full_like(z, 60.0), norm_weight=np.ones(16), norm_eps=0.0)
+    assert np.allclose(np.sqrt(np.mean(o * o, axis=-1)), 1.0, rtol=0, atol=1e-12)
+
+
+def test_epilogue_gate_and_weights():
+    x, z, wgt = _epilogue_case(16)
+    args = (x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", 8)
+    open_, _ = vda.forward(*args, gate=np.full_like(z, 60.0), norm_weight=np.ones(16), norm_eps=1e-6)
+    half, _ = vda.forward(*args, gate=np.zeros_like(z), norm_weight=np.ones(16), norm_eps=1e-6)
+    assert np.allclose(half, open_ / 2, rtol=1e-12, atol=0)  # sigmoid(0) = 1/2
+    one_hot = np.zeros(16)
+    one_hot[5] = 3.0
+    sel, _ = vda.forward(*args, gate=np.full_like(z, 60.0), norm_weight=one_hot, norm_eps=1e-6)
+    assert np.allclose(sel[..., 5], 3.0 * open_[..., 5], rtol=1e-12, atol=0)
+    assert np.all(np.delete(sel, 5, axis=-1) == 0)
