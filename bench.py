@@ -179,6 +179,10 @@ def run_vda(args, w) -> int:
         return torch.from_numpy(a).cuda()
 
     d = {k: dev(v) for k, v in x.items()}
+    epi = {}
+    if args.vda_epilogue:
+        e = synth.generate_epilogue(w)
+        epi = dict(gate=dev(e["gate"]), norm_weight=dev(e["norm_weight"]), norm_eps=1e-6)
     out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
     s_out = torch.empty((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
     ws = None
@@ -186,11 +190,12 @@ def run_vda(args, w) -> int:
     def step(ev_ptr=None):
         nonlocal ws
         _, _ = gdn.vda_forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction, frame,
-                               out=out, state_out=s_out, workspace=ws, timing_events=ev_ptr)
+                               out=out, state_out=s_out, workspace=ws, timing_events=ev_ptr, write=args.vda_write,
+                               lag=args.vda_lag, **epi)
 
-    nb = gdn.gdn_vda_workspace_bytes(gdn.gdn_vda_problem_t(w.B, w.T, w.H, w.dk, w.dv, frame,
-                                                          gdn.GDN_DTYPE_BF16 if w.dtype == "bf16" else gdn.GDN_DTYPE_F32,
-                                                          0, None, 0, None, None), gdn.DIRECTIONS[w.direction])
+    nb = gdn.gdn_vda_workspace_bytes(gdn.gdn_vda_problem_t(
+        B=w.B, T=w.T, H=w.H, dk=w.dk, dv=w.dv, frame=frame,
+        dtype=gdn.GDN_DTYPE_BF16 if w.dtype == "bf16" else gdn.GDN_DTYPE_F32), gdn.DIRECTIONS[w.direction])
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     for _ in range(args.warmup):
         step()
@@ -225,7 +230,9 @@ def run_vda(args, w) -> int:
         "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "operator": "frame-wise delta (Video Delta Attention)", "frame": frame,
+        "config": {"workload": w.name, "operator": ("frame-wise delta (Video Delta Attention)" if args.vda_write == "inverse"
+                                                 else "additive frame writes, keys / sqrt(U)"),
+                   "readout_lag": args.vda_lag, "epilogue": bool(args.vda_epilogue), "frame": frame,
                    "frames": NF, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "direction": w.direction},
         "kernels_ms": km,
         "tflops": sum(kf.values()) / (ms_step * 1e-3) / 1e12,
@@ -246,8 +253,12 @@ def run_vda(args, w) -> int:
                 if n and time.perf_counter() - t0 > args.cpu_seconds:
                     break
                 sel = {k: x[k][b:b + 1, :, h:h + 1] for k in ("q", "k", "v")}
+                ekw = {}
+                if args.vda_epilogue:
+                    ekw = dict(gate=e["gate"][b:b + 1, :, h:h + 1], norm_weight=e["norm_weight"], norm_eps=1e-6)
                 vda_oracle.forward(sel["q"], sel["k"], sel["v"], x["log_alpha"][:, b:b + 1, :, h:h + 1],
-                                   x["beta"][:, b:b + 1, :, h:h + 1], None, w.direction, frame)
+                                   x["beta"][:, b:b + 1, :, h:h + 1], None, w.direction, frame,
+                                   write=args.vda_write, lag=args.vda_lag, **ekw)
                 n += 1
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": n * T / dt / H, "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -274,6 +285,10 @@ def main() -> int:
                     help="time the erase-free variant (gated linear attention, GDN_OPT_NO_ERASE) instead of the delta rule")
     ap.add_argument("--vda", action="store_true",
                     help="time the frame-wise delta operator (gdn_vda_forward) on the workload's frames instead")
+    ap.add_argument("--vda-write", choices=("inverse", "additive"), default="inverse",
+                    help="--vda: the operator's inverse write or the additive write (keys / sqrt(U))")
+    ap.add_argument("--vda-lag", type=int, default=0, help="--vda: readout lag in frames (disjoint-region readout)")
+    ap.add_argument("--vda-epilogue", action="store_true", help="--vda: fused RMS-norm and sigmoid-gate epilogue")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()

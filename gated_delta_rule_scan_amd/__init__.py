@@ -36,6 +36,8 @@ GDN_DTYPE_BF16 = 1
 GDN_OPT_SERIAL = 1
 GDN_OPT_NO_ERASE = 2
 
+GDN_VDA_OPT_ADDITIVE = 1
+
 EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_vda_workspace_bytes", "gdn_vda_forward", "gdn_status_string",
             "gdn_version")
 
@@ -57,6 +59,8 @@ class gdn_vda_problem_t(ctypes.Structure):
         ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
         ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("frame", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("options", ctypes.c_int32),
+        ("readout_lag", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+        ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("timing_events", ctypes.c_void_p),
@@ -202,10 +206,14 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
 
 def vda_forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", frame: int = 1560, out=None,
                 state_out=None, workspace=None, want_state: bool = True, stream=None,
-                timing_events: Optional[int] = None) -> Tuple:
+                timing_events: Optional[int] = None, write: str = "inverse", lag: int = 0, gate=None,
+                norm_weight=None, norm_eps: float = 1e-6) -> Tuple:
     """Frame-wise delta operator on torch CUDA tensors (layouts of include/gdn.h):
     q, k [B,T,H,dk], v [B,T,H,dv]; log_alpha [dirs,B,NF,H] (one per frame of
     ``frame`` tokens); beta [dirs,B,T,H]; state_in [dirs,B,H,dv,dk] or None.
+    ``write``: "inverse" (the operator) or "additive" (GDN_VDA_OPT_ADDITIVE);
+    ``lag``: the readout lag in frames; ``gate`` [B,T,H,dv] (type of q) with
+    ``norm_weight`` [dv] float32: the readout epilogue.
     Returns (out [B,T,H,dv] float32, state_out or None)."""
     import torch
 
@@ -234,7 +242,17 @@ def vda_forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd",
         out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     if state_out is None and want_state:
         state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
-    prob = gdn_vda_problem_t(B, T, H, dk, dv, frame, dt, 0, None, 0, None, None)
+    if write not in ("inverse", "additive"):
+        raise ValueError("write must be 'inverse' or 'additive'")
+    if gate is not None:
+        if gate.dtype != q.dtype or not gate.is_contiguous() or tuple(gate.shape) != (B, T, H, dv):
+            raise ValueError(f"gate must be contiguous [{B},{T},{H},{dv}] of the type of q")
+        if norm_weight is None or norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (dv,):
+            raise ValueError(f"norm_weight must be float32 [{dv}] when gate is given")
+    prob = gdn_vda_problem_t(B=B, T=T, H=H, dk=dk, dv=dv, frame=frame, dtype=dt,
+                             options=GDN_VDA_OPT_ADDITIVE if write == "additive" else 0, readout_lag=lag,
+                             norm_eps=norm_eps, gate=None if gate is None else gate.data_ptr(),
+                             norm_weight=None if gate is None else norm_weight.contiguous().data_ptr())
     nbytes = gdn_vda_workspace_bytes(prob, DIRECTIONS[direction])
     if nbytes == 0 and T > 0:
         raise GdnError(GDN_ERR_UNSUPPORTED)

@@ -305,7 +305,8 @@ gdn_status_t vda_plan(const gdn_vda_problem_t* p, int32_t direction, int* dirs, 
   if (!p) return GDN_ERR_INVALID_ARGUMENT;
   if (direction < GDN_DIR_FORWARD || direction > GDN_DIR_BIDIRECTIONAL) return GDN_ERR_INVALID_ARGUMENT;
   if (p->B < 1 || p->H < 1 || p->T < 0 || p->dk < 1 || p->dv < 1 || p->frame < 1) return GDN_ERR_INVALID_ARGUMENT;
-  if (p->options != 0) return GDN_ERR_INVALID_ARGUMENT;
+  if ((p->options & ~GDN_VDA_OPT_ADDITIVE) != 0 || p->readout_lag < 0) return GDN_ERR_INVALID_ARGUMENT;
+  if (p->gate && (!p->norm_weight || !(p->norm_eps >= 0.f) || !(p->norm_eps <= 3.4e38f))) return GDN_ERR_INVALID_ARGUMENT;
   if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
   if (!supported_dim(p->dk) || !supported_dim(p->dv)) return GDN_ERR_UNSUPPORTED;
   if (p->T > ((int64_t)1 << 31) / 2) return GDN_ERR_UNSUPPORTED;
@@ -352,14 +353,16 @@ extern "C" gdn_status_t gdn_vda_forward(const gdn_vda_problem_t* p, const void* 
     if (p->workspace_bytes < L.total) return GDN_ERR_WORKSPACE_TOO_SMALL;
   }
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16))) return GDN_ERR_INVALID_ARGUMENT;
+  if (p->gate && (!aligned(p->gate, 16) || !aligned(p->norm_weight, 16))) return GDN_ERR_INVALID_ARGUMENT;
   const Range r_q = rng(q, n_qk * es), r_k = rng(k, n_qk * es), r_v = rng(v, n_v * es);
   const Range r_la = rng(log_alpha, n_la * 4), r_b = rng(beta, n_b * 4);
   const Range r_si = rng(state_in, n_s * 4), r_so = rng(state_out, n_s * 4);
   const Range r_o = rng(out, n_v * 4), r_ws = rng(T > 0 ? p->workspace : nullptr, L.total);
-  const Range ins[] = {r_q, r_k, r_v, r_la, r_b, r_si};
+  const Range r_g = rng(p->gate, n_v * es), r_nw = rng(p->gate ? p->norm_weight : nullptr, (size_t)dv * 4);
+  const Range ins[] = {r_q, r_k, r_v, r_la, r_b, r_g, r_nw, r_si};
   for (const Range& r : ins)
     if (overlap(r_o, r) || overlap(r_ws, r)) return GDN_ERR_INVALID_ARGUMENT;
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 7; ++i)
     if (overlap(r_so, ins[i])) return GDN_ERR_INVALID_ARGUMENT;
   if (overlap(r_so, r_si) && state_in != state_out) return GDN_ERR_INVALID_ARGUMENT;
   if (overlap(r_o, r_so) || overlap(r_o, r_ws) || overlap(r_so, r_ws)) return GDN_ERR_INVALID_ARGUMENT;
@@ -379,6 +382,11 @@ extern "C" gdn_status_t gdn_vda_forward(const gdn_vda_problem_t* p, const void* 
   a.dirs = dirs;
   a.fwd_on = direction != GDN_DIR_REVERSE;
   a.rev_on = direction != GDN_DIR_FORWARD;
+  a.additive = (p->options & GDN_VDA_OPT_ADDITIVE) != 0;
+  a.lag = p->readout_lag < NF ? p->readout_lag : (int)(NF < 1 ? 1 : NF);  // NF or more: only initial states
+  a.gate = p->gate;
+  a.norm_weight = p->gate ? p->norm_weight : nullptr;
+  a.norm_eps = p->norm_eps;
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
   hipEvent_t* ev = static_cast<hipEvent_t*>(p->timing_events);
   vda_fn fn = p->dtype == GDN_DTYPE_BF16 ? vda_for<bf16>(dk, dv) : vda_for<float>(dk, dv);

@@ -106,6 +106,12 @@ __device__ __forceinline__ f32x4 bload16(rsrc_t r, uint32_t off) {
   return f;
 }
 
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return uint2{v.x, v.y};
+}
+
 __device__ __forceinline__ float bload4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
@@ -257,6 +263,11 @@ struct VdaArgs {
   int64_t B, T, H, NF, frame;
   int dv;
   int dirs, fwd_on, rev_on;
+  int additive;             // 1: S_t = a S (I - A/U) + B / sqrt(U)
+  int lag;                  // readout lag in frames
+  const void* gate;         // epilogue gate logits, or null
+  const float* norm_weight; // epilogue weights [dv]
+  float norm_eps;
 };
 
 struct VdaLayout {

@@ -242,8 +242,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   __syncthreads();  // the staging buffers become I + A_t
 
   // ---- I + A_t into LDS; B_t straight to the workspace.  Tile (j, l) of a
-  // wave holds, in lane (l16, g4), row 16 (tile) + 4 g4 + i, column 16 l + l16. ----
+  // wave holds, in lane (l16, g4), row 16 (tile) + 4 g4 + i, column 16 l + l16.
+  // The additive write keeps I - A_t / U (no inverse) and B_t / sqrt(U),
+  // U = this frame's token count. ----
   float* Am = reinterpret_cast<float*>(smem);  // [DK][AP]
+  const float sa = a.additive ? -1.0f / (float)n : 1.0f;
+  const float sb = a.additive ? 1.0f / sqrtf((float)n) : 1.0f;
 #pragma unroll
   for (int j = 0; j < NJA; ++j)
 #pragma unroll
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * (NJA * w + j) + 4 * g4 + i, c = 16 * l + l16;
-        Am[r * AP + c] = accA[j][l][i] + (r == c ? 1.f : 0.f);
+        Am[r * AP + c] = accA[j][l][i] * sa + (r == c ? 1.f : 0.f);
       }
   {
     float* bg = a.bmat + fid * (size_t)DV * DK;
@@ -260,7 +264,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
 #pragma unroll
       for (int l = 0; l < NL; ++l)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bg[(size_t)(16 * (NJB * w + j) + 4 * g4 + i) * DK + 16 * l + l16] = accB[j][l][i];
+        for (int i = 0; i < 4; ++i)
+          bg[(size_t)(16 * (NJB * w + j) + 4 * g4 + i) * DK + 16 * l + l16] = accB[j][l][i] * sb;
   }
   __syncthreads();
 
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
 #pragma unroll
         for (int e = 0; e < 4; ++e) m[i][j + e] = x[e];
       }
-    for (int pb = 0; pb < 16; ++pb) {
+    for (int pb = 0; pb < (a.additive ? 0 : 16); ++pb) {
       const bool rowb = ty == pb, colb = tx == pb;
 #pragma unroll
       for (int pi = 0; pi < BS; ++pi) {
@@ -389,6 +394,9 @@ __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
   // each step consumes one and refills it for frame s + 3 (clamped at the last
   // frame, so every step issues the same loads).
   auto frame_of = [&](int s) { return rev ? NF - 1 - s : s; };
+  // B_t enters before the product (R_t = a S + B_t) or, for the additive
+  // write, after it (S_t = a S M_t + B_t)
+  const float wbefore = a.additive ? 0.f : 1.f, wafter = a.additive ? 1.f : 0.f;
   F32::frag mf[3][NLW][KC];
   f32x4 bn[3][NLW];
   float an[3];
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
 #pragma unroll
     for (int lw = 0; lw < NLW; ++lw) {
       const int l = NLW * w + lw;
-      *reinterpret_cast<f32x4*>(Rs + l16 * SP + 16 * l + 4 * g4) = snew[lw] * at + bn[k][lw];
+      *reinterpret_cast<f32x4*>(Rs + l16 * SP + 16 * l + 4 * g4) = snew[lw] * at + bn[k][lw] * wbefore;
     }
     __syncthreads();  // Rs holds R_t
     // (M R^T) tile l lands in lane (l16, g4) as S_t[l16][16 l + 4 g4 + i]
@@ -437,7 +445,7 @@ __global__ __launch_bounds__(256) void vda_chain_kernel(VdaArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c) acc = F32::mma(mf[k][lw][c], F32::load(Rs + l16 * SP + 32 * c + 8 * g4), acc);
-      snew[lw] = acc;
+      snew[lw] = acc + bn[k][lw] * wafter;
     }
     float* sg = a.sfr + (fbase + frame_of(s)) * (size_t)DV * DK + (size_t)16 * tile * DK;
 #pragma unroll
@@ -508,6 +516,9 @@ __global__ __launch_bounds__(256) void vda_chain_bf16_kernel(VdaArgs a) {
 
   // the lane's share of the 32 x DK row tile: rows 16 rt + l16, columns 16 l + 4 g4 .. + 3
   auto frame_of = [&](int s) { return rev ? NF - 1 - s : s; };
+  // B_t enters before the product (R_t = a S + B_t) or, for the additive
+  // write, after it (S_t = a S M_t + B_t)
+  const float wbefore = a.additive ? 0.f : 1.f, wafter = a.additive ? 1.f : 0.f;
   frag mh[kRing][NLW][KC], ml[kRing][NLW][KC];
   f32x4 bn[kRing][RT][NLW];
   float an[kRing];
@@ -557,7 +568,7 @@ __global__ __launch_bounds__(256) void vda_chain_bf16_kernel(VdaArgs a) {
 #pragma unroll
       for (int lw = 0; lw < NLW; ++lw) {
         const int l = NLW * w + lw;
-        const f32x4 r = snew[rt][lw] * at + bn[k][rt][lw];
+        const f32x4 r = snew[rt][lw] * at + bn[k][rt][lw] * wbefore;
         bf16x4 hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -582,7 +593,7 @@ __global__ __launch_bounds__(256) void vda_chain_bf16_kernel(VdaArgs a) {
           acc = M::mma(mh[k][lw][c], rl, acc);
           acc = M::mma(ml[k][lw][c], rh, acc);
         }
-        snew[rt][lw] = acc;
+        snew[rt][lw] = acc + bn[k][rt][lw] * wafter;
       }
     // the state store goes out before the next loads, so the wait that frees
     // its registers at the next step does not wait for those loads
@@ -628,7 +639,7 @@ __global__ __launch_bounds__(256) void vda_chain_bf16_kernel(VdaArgs a) {
 // values of one token's output row; wave w owns the w-th quarter of the dv
 // columns.
 // ---------------------------------------------------------------------------
-template <typename MT, int DK, int DV>
+template <typename MT, int DK, int DV, bool EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void vda_readout_kernel(VdaArgs a, int nblk,
                                                                                                  int bpw) {
   using M = Mma<MT>;
@@ -653,19 +664,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   if (f0 + 64 * (int64_t)jb0 >= fend) return;
 
   // summed state rows 16 ct + l16, columns 32 c + 8 g4 .. + 7 (every load
-  // issued before the first use)
+  // issued before the first use).  Each direction reads the state after frame
+  // f -+ lag (forward: f - lag, reverse: f + lag), or its initial state where
+  // that frame does not exist (zero without state_in).
   frag sh[CT][KC];
   [[maybe_unused]] frag sl[CT][KC];
   f32x4 sp[2][CT][KC][2];
+  const float* sbase[2];
+  float smul[2];
+#pragma unroll
+  for (int slot = 0; slot < 2; ++slot) {
+    const int ss = slot < a.dirs ? slot : 0;
+    const bool rev = a.rev_on && (ss == 1 || !a.fwd_on);
+    const int src = rev ? f + a.lag : f - a.lag;
+    const bool in_range = src >= 0 && src < NF;
+    const float* frame_state = a.sfr + (((size_t)ss * BH + bh) * NF + (in_range ? src : 0)) * (size_t)DV * DK;
+    sbase[slot] = in_range || !a.state_in ? frame_state : a.state_in + ((size_t)ss * BH + bh) * (size_t)DV * DK;
+    // the second direction's part and a missing initial state enter scaled by
+    // 0 (a branch here would move the loads behind a wait of their own)
+    smul[slot] = (slot < a.dirs && (in_range || a.state_in)) ? 1.f : 0.f;
+  }
 #pragma unroll
   for (int slot = 0; slot < 2; ++slot)
 #pragma unroll
     for (int cc = 0; cc < CT; ++cc)
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const int ss = slot < a.dirs ? slot : 0;
-        const float* src = a.sfr + (((size_t)ss * BH + bh) * NF + f) * (size_t)DV * DK +
-                           (size_t)(16 * (CT * w + cc) + l16) * DK + 32 * c + 8 * g4;
+        const float* src = sbase[slot] + (size_t)(16 * (CT * w + cc) + l16) * DK + 32 * c + 8 * g4;
         sp[slot][cc][c][0] = *reinterpret_cast<const f32x4*>(src);
         sp[slot][cc][c][1] = *reinterpret_cast<const f32x4*>(src + 4);
       }
@@ -673,11 +698,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   for (int cc = 0; cc < CT; ++cc) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      // the second direction's part enters scaled by 1 or 0 (a branch here
-      // would move its loads behind a wait of their own)
-      const float m1 = a.dirs == 2 ? 1.f : 0.f;
-      const f32x4 s0 = sp[0][cc][c][0] + sp[1][cc][c][0] * m1;
-      const f32x4 s1 = sp[0][cc][c][1] + sp[1][cc][c][1] * m1;
+      const f32x4 s0 = sp[0][cc][c][0] * smul[0] + sp[1][cc][c][0] * smul[1];
+      const f32x4 s1 = sp[0][cc][c][1] * smul[0] + sp[1][cc][c][1] * smul[1];
       if constexpr (BF) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -692,7 +714,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     }
   }
 
-  const uint32_t HQB = (uint32_t)(H * DK * ES), HOB = (uint32_t)(H * DV * 4);
+  const uint32_t HQB = (uint32_t)(H * DK * ES), HOB = (uint32_t)(H * DV * 4), HGB = (uint32_t)(H * DV * ES);
+  // epilogue: per-wave sums of squares per token, and this lane's weights
+  __shared__ float s_ss[EPI ? 4 : 1][64];
+  [[maybe_unused]] f32x4 nw[CT];
+  if constexpr (EPI) {
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc) nw[cc] = *reinterpret_cast<const f32x4*>(a.norm_weight + 16 * (CT * w + cc) + 4 * g4);
+  }
   // blocks jb0 .. jend-1 hold tokens of this frame
   const int64_t nrem = (fend - (f0 + 64 * (int64_t)jb0) + 63) / 64;
   const int jend = jb0 + (int)(nrem < jb1 - jb0 ? nrem : jb1 - jb0);
@@ -706,7 +735,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   constexpr int QP = DK + 16 / ES;            // row pitch in elements (16 bytes of padding)
   constexpr int PR = DK * ES / 16;            // 16-byte pieces per row
   constexpr int NPQ = 64 * PR / 256;          // pieces per thread per block
-  constexpr int kDepth = BF ? 3 : 1;          // blocks in flight per thread
+  constexpr int kDepth = BF ? (EPI ? 2 : 3) : 1;  // blocks in flight per thread (the epilogue needs registers)
   __shared__ __align__(16) MT qs[2][64 * QP];
   auto load_q = [&](int jb, f32x4 (&qr)[NPQ]) {
     const int64_t fs = f0 + 64 * (int64_t)jb;
@@ -764,8 +793,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
 #pragma unroll
     for (int cc = 0; cc < CT; ++cc)
 #pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[cc][rt] = acc[cc][rt] * rqs[rt];
+    if constexpr (EPI) {
+      // epilogue: out = w * o / sqrt(mean(o^2) + eps) * sigmoid(z) per token;
+      // the mean over dv spans the four waves (partial sums through LDS)
+      const rsrc_t rz = make_rsrc(static_cast<const MT*>(a.gate) + ((b * T + fs) * H + h) * DV,
+                                  (uint32_t)(rows_of(jb) - 1) * HGB + DV * ES);
+      f32x4 zv[CT][4];
+#pragma unroll
+      for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const uint32_t off = (uint32_t)(16 * rt + l16) * HGB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * ES;
+          if constexpr (BF) {
+            const uint2 raw = bload8(rz, off);
+            zv[cc][rt] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                               __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
+          } else {
+            zv[cc][rt] = bload16(rz, off);
+          }
+        }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        float ss = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = fmaf(acc[cc][rt][e], acc[cc][rt][e], ss);
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (g4 == 0) s_ss[w][16 * rt + l16] = ss;
+      }
+      __syncthreads();
+      // sigmoid(z) = 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and
+      // reciprocal (about 1 ulp each)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float tot = s_ss[0][16 * rt + l16] + s_ss[1][16 * rt + l16] + s_ss[2][16 * rt + l16] + s_ss[3][16 * rt + l16];
+        const float inv = 1.0f / sqrtf(tot * (1.0f / DV) + a.norm_eps);
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * zv[cc][rt][e]));
+            acc[cc][rt][e] = acc[cc][rt][e] * (inv * nw[cc][e]) * sg;
+          }
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        bstore16(ro, (uint32_t)(16 * rt + l16) * HOB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * 4u, acc[cc][rt] * rqs[rt]);
+        bstore16(ro, (uint32_t)(16 * rt + l16) * HOB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * 4u, acc[cc][rt]);
   };
 #pragma unroll
   for (int k = 0; k < kDepth; ++k) load_q(jb0 + k < jend ? jb0 + k : jend - 1, qr[k]);
@@ -806,8 +885,12 @@ hipError_t launch_vda(const VdaArgs& a, hipStream_t stream, hipEvent_t* ev) {
     const int nblk = (int)((a.frame + 63) / 64);
     const int nsplit = (nblk + 7) / 8;
     const int bpw = (nblk + nsplit - 1) / nsplit;
-    hipLaunchKernelGGL((vda_readout_kernel<MT, DK, DV>), dim3((unsigned)(BH * a.NF * ((nblk + bpw - 1) / bpw))), dim3(256),
-                       0, stream, a, nblk, bpw);
+    const dim3 grid((unsigned)(BH * a.NF * ((nblk + bpw - 1) / bpw)));
+    if (a.gate) {
+      hipLaunchKernelGGL((vda_readout_kernel<MT, DK, DV, true>), grid, dim3(256), 0, stream, a, nblk, bpw);
+    } else {
+      hipLaunchKernelGGL((vda_readout_kernel<MT, DK, DV, false>), grid, dim3(256), 0, stream, a, nblk, bpw);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;

@@ -157,16 +157,41 @@ gdn_status_t gdn_forward(const gdn_problem_t* p,
  * gdn_forward: the reverse scan visits the frames last to first, the
  * bidirectional output is the sum of both readouts.
  *
+ * Options on the same machinery:
+ *  - GDN_VDA_OPT_ADDITIVE: the additive frame write the page contrasts the
+ *    operator with ("Main Findings", last item: SANA-WM's batched per-token
+ *    corrections with 1/sqrt(U) key scaling, U = the frame's token count):
+ *    S_t = a_t S_{t-1} (I - A_t / U) + B_t / sqrt(U).
+ *  - readout_lag = d > 0: the disjoint-region readout ("Methodology in Plain
+ *    English": the forward and reverse memories cover disjoint regions, the
+ *    text enters as an initial state S_T/2 in each direction).  A token of
+ *    frame t reads the forward state after frame t - d and the reverse state
+ *    after frame t + d; where that frame does not exist, the direction's
+ *    initial state (zero without state_in).  d = 0 reads its own frame's state.
+ *  - gate != NULL: the readout epilogue ("Key Contributions" item 1: the
+ *    linear branch's RMS normalisation and sigmoid gate), applied to the
+ *    summed readout o of each (token, head) before it is stored:
+ *    out = norm_weight * o / sqrt(mean_dv(o^2) + norm_eps) * sigmoid(gate).
+ *
  * Layouts: q, k, v, beta, state_in, state_out and out as for gdn_forward;
- *   log_alpha  [dirs, B, NF, H] fp32, NF = ceil(T / frame).
+ *   log_alpha  [dirs, B, NF, H] fp32, NF = ceil(T / frame);
+ *   gate       [B, T, H, dv] of the type of q (16-byte aligned);
+ *   norm_weight [dv] fp32, shared by the heads.
  * Supported: dk, dv in {64, 128}; frame >= 1; fp32 or bf16 q, k, v; the same
  * size limit as gdn_problem_t.  Same ownership, execution and error contract
- * as gdn_forward (everything on `stream`; no allocation; no synchronisation). */
+ * as gdn_forward (everything on `stream`; no allocation; no synchronisation;
+ * `out` must not overlap any input, gate and norm_weight included). */
+typedef enum { GDN_VDA_OPT_ADDITIVE = 1 } gdn_vda_option_t;
+
 typedef struct {
   int64_t B, T, H, dk, dv;
   int64_t frame;            /* tokens per frame */
-  int32_t dtype;            /* gdn_dtype_t: type of q, k, v */
-  int32_t options;          /* must be 0 */
+  int32_t dtype;            /* gdn_dtype_t: type of q, k, v and gate */
+  int32_t options;          /* 0 or GDN_VDA_OPT_ADDITIVE */
+  int32_t readout_lag;      /* >= 0 */
+  float norm_eps;           /* epilogue only: finite, >= 0 */
+  const void* gate;         /* NULL (no epilogue) or [B, T, H, dv] */
+  const float* norm_weight; /* [dv]; required with gate */
   void* workspace;          /* caller-owned device memory, 256-byte aligned */
   size_t workspace_bytes;
   void* stream;             /* hipStream_t; NULL = default stream */

@@ -41,6 +41,7 @@ _lib = None
 STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
 STREAM_BETA, STREAM_LOG_ALPHA, STREAM_STATE = 10, 20, 30
 STREAM_FRAME_LOG_ALPHA = 40
+STREAM_GATE, STREAM_NORM_WEIGHT = 50, 60
 
 
 def build(force: bool = True) -> str:
@@ -171,6 +172,16 @@ def generate_frames(w: Workload, frame: int, T: Optional[int] = None) -> dict:
     la = np.stack([_scalars(w.seed, STREAM_FRAME_LOG_ALPHA + d, n, 2, w.la_shift) for d in range(w.dirs)])
     x["log_alpha"] = la.reshape(w.dirs, w.B, NF, w.H)
     return x
+
+
+def generate_epilogue(w: Workload, T: Optional[int] = None) -> dict:
+    """Inputs of the readout epilogue: gate logits [B,T,H,dv] ~ N(0, 1) in the
+    workload's dtype (bf16 bit patterns or float32) and one vector of norm
+    weights [dv] ~ 1 + N(0, 0.1^2), float32."""
+    T = w.T if T is None else T
+    z = _vectors(w.seed, STREAM_GATE, w.B * T * w.H, w.dv, False, w.dtype).reshape(w.B, T, w.H, w.dv)
+    nw = 1.0 + _scalars(w.seed, STREAM_NORM_WEIGHT, w.dv, 0, 0.1)
+    return dict(gate=z, norm_weight=nw.astype(np.float32))
 
 
 def normals(seed: int, stream: int, shape, std: float = 1.0) -> np.ndarray:

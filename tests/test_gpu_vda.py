@@ -23,26 +23,37 @@ def _workload(dtype, direction, T, frame, B=1, H=2, dk=64, dv=64, std=0.05, seed
     return w, synth.generate_frames(w, frame)
 
 
-def _run(x, direction, frame, want_state=True, state_in="use"):
+def _run(x, direction, frame, want_state=True, state_in="use", write="inverse", lag=0, epi=None):
     import torch
 
     import gated_delta_rule_scan_amd as gdn
 
     d = {k: to_torch(v) for k, v in x.items()}
     s_in = d["state_in"] if state_in == "use" else state_in
+    ekw = {}
+    if epi is not None:
+        ekw = dict(gate=to_torch(epi["gate"]), norm_weight=to_torch(epi["norm_weight"]), norm_eps=epi["eps"])
     out, s = gdn.vda_forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s_in, direction, frame,
-                             want_state=want_state)
+                             want_state=want_state, write=write, lag=lag, **ekw)
     torch.cuda.synchronize()
     return out.cpu().numpy(), (None if s is None else s.cpu().numpy())
 
 
-def _compare(dtype, direction, T, frame, **kw):
+def _compare(dtype, direction, T, frame, write="inverse", lag=0, epilogue=False, **kw):
     w, x = _workload(dtype, direction, T, frame, **kw)
-    ref, ref_s = vda_oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction, frame)
-    out, s = _run(x, direction, frame)
-    e1 = check(out, ref, TOL[dtype], f"vda out {w} frame={frame}")
-    e2 = check(s, ref_s, TOL[dtype], f"vda state {w} frame={frame}")
-    print(f"\nvda {dtype} {direction} T={T} frame={frame} d={w.dk}/{w.dv}: out {e1:.2e} state {e2:.2e}", flush=True)
+    epi = None
+    okw = {}
+    if epilogue:
+        epi = dict(synth.generate_epilogue(w), eps=1e-6)
+        okw = dict(gate=epi["gate"], norm_weight=epi["norm_weight"], norm_eps=1e-6)
+    ref, ref_s = vda_oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction, frame,
+                                    write=write, lag=lag, **okw)
+    out, s = _run(x, direction, frame, write=write, lag=lag, epi=epi)
+    tag = f"{w} frame={frame} write={write} lag={lag} epilogue={epilogue}"
+    e1 = check(out, ref, TOL[dtype], f"vda out {tag}")
+    e2 = check(s, ref_s, TOL[dtype], f"vda state {tag}")
+    print(f"\nvda {dtype} {direction} T={T} frame={frame} d={w.dk}/{w.dv} {write} lag={lag} epi={int(epilogue)}: "
+          f"out {e1:.2e} state {e2:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("direction", ["fwd", "rev", "bi"])
@@ -101,3 +112,62 @@ def test_full_size_480p_bidirectional_sampled_heads():
         e1 = check(out[b:b + 1, :, h:h + 1], ref, TOL["bf16"], f"vda480 out b{b} h{h}")
         e2 = check(s[:, b:b + 1, h:h + 1], ref_s, TOL["bf16"], f"vda480 state b{b} h{h}")
         print(f"\nvda480 b{b} h{h}: out {e1:.2e} state {e2:.2e}", flush=True)
+
+
+# ---- additive frame writes, readout lag, epilogue ----
+
+@pytest.mark.parametrize("direction", ["fwd", "rev", "bi"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_additive_write(dtype, direction):
+    _compare(dtype, direction, T=333, frame=100, H=3, write="additive")
+
+
+@pytest.mark.parametrize("frame", [1, 30])
+def test_additive_write_frame_sizes(frame):
+    _compare("f32", "bi", T=150 if frame > 1 else 40, frame=frame, write="additive", dk=128, dv=64)
+
+
+@pytest.mark.parametrize("lag", [1, 2, 5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_readout_lag(dtype, lag):
+    # ragged last frame; the initial states are read near the edges
+    _compare(dtype, "bi", T=290, frame=64, lag=lag, dk=128, dv=128, seed=23)
+
+
+def test_readout_lag_single_direction_without_initial_state():
+    _compare("bf16", "rev", T=200, frame=30, lag=2, std=0.0, seed=24)
+    _compare("bf16", "fwd", T=200, frame=30, lag=3, std=0.0, seed=25)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bi"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_epilogue(dtype, direction):
+    _compare(dtype, direction, T=260, frame=64, epilogue=True, dk=128, dv=128, seed=26)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
+def test_epilogue_with_lag_and_additive_write(dk, dv):
+    _compare("bf16", "bi", T=300, frame=50, epilogue=True, lag=2, write="additive", dk=dk, dv=dv, seed=27)
+
+
+def test_full_size_480p_disjoint_regions_with_epilogue():
+    """B2 H16 d128 bf16, 21 frames of 1560 tokens, both directions, a 15-frame
+    local window (readout lag 8), text state S_T/2 in each direction, and the
+    RMS-norm plus gate epilogue; the oracle recomputes two sampled heads."""
+    import numpy as np
+
+    w = synth.Workload("vda480", 2, 16, 32760, 128, 128, "bf16", "bi", -3.0, 0.0, 2)
+    x = synth.generate_frames(w, 1560)
+    S_T = synth.normals(5, 70, (2, 16, 128, 128), 0.05)
+    x["state_in"] = np.ascontiguousarray(np.stack([S_T / 2, S_T / 2]).astype(np.float32))
+    epi = dict(synth.generate_epilogue(w), eps=1e-6)
+    out, s = _run(x, "bi", 1560, lag=8, epi=epi)
+    for b, h in [(0, 3), (1, 12)]:
+        sel = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v")}
+        ref, ref_s = vda_oracle.forward(sel["q"], sel["k"], sel["v"], x["log_alpha"][:, b:b + 1, :, h:h + 1],
+                                        x["beta"][:, b:b + 1, :, h:h + 1], x["state_in"][:, b:b + 1, h:h + 1], "bi",
+                                        1560, lag=8, gate=epi["gate"][b:b + 1, :, h:h + 1],
+                                        norm_weight=epi["norm_weight"], norm_eps=1e-6)
+        e1 = check(out[b:b + 1, :, h:h + 1], ref, TOL["bf16"], f"vda480 lag8 epi out b{b} h{h}")
+        e2 = check(s[:, b:b + 1, h:h + 1], ref_s, TOL["bf16"], f"vda480 lag8 epi state b{b} h{h}")
+        print(f"\nvda480 lag8 epilogue b{b} h{h}: out {e1:.2e} state {e2:.2e}", flush=True)
