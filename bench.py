@@ -62,6 +62,9 @@ def kernel_bytes(w, xs: int, C: int) -> dict:
 KERNEL_SOURCES = {
     "chain_kernel": ["gdn_chain.hip", "gdn_common.h"],
     "chunk_prep_kernel": ["gdn_prep.hip", "gdn_common.h"],
+    "vda_frame_kernel": ["gdn_vda.hip", "gdn_common.h"],
+    "vda_chain_bf16_kernel": ["gdn_vda.hip", "gdn_common.h"],
+    "vda_readout_kernel": ["gdn_vda.hip", "gdn_common.h"],
 }
 
 
@@ -154,6 +157,7 @@ def cpu_baseline(w, x, target_s: float) -> dict:
             "seconds": round(dt, 2)}
 
 
+VDA_KERNEL = {"vda_frame": "vda_frame_kernel", "vda_chain": "vda_chain_bf16_kernel", "vda_readout": "vda_readout_kernel"}
 VDA_FRAME = {"stream480": 1560, "bidir480": 1560, "causal720": 3600, "bidir720": 3600, "causal720_slow": 3600}
 
 
@@ -212,6 +216,12 @@ def run_vda(args, w) -> int:
     km = {n: sum(ev.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(K)) / K
           for n, a in (("vda_frame", 0), ("vda_chain", 1), ("vda_readout", 2))}
     ev.close()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     B, T, H, dk, dv, dirs = w.B, w.T, w.H, w.dk, w.dv, w.dirs
     NF = (T + frame - 1) // frame
     nfr = dirs * B * H * NF
@@ -238,7 +248,10 @@ def run_vda(args, w) -> int:
         "tflops": sum(kf.values()) / (ms_step * 1e-3) / 1e12,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": kb[dom] / (km[dom] * 1e-3) / 1e9,
                      "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": kb[dom] / (km[dom] * 1e-3) / 1e9 / MI355X_HBM_GBS,
-                     "traffic": None, "alg_bytes_per_launch": kb[dom], "avg_launch_ms": km[dom],
+                     # counters were taken on the operator's default options only
+                     "traffic": (measured_traffic(VDA_KERNEL[dom], args.workload)
+                                 if (args.vda_write, args.vda_lag, args.vda_epilogue) == ("inverse", 0, False) else None),
+                     "alg_bytes_per_launch": kb[dom], "avg_launch_ms": km[dom],
                      "mfma_tflops": kf[dom] / (km[dom] * 1e-3) / 1e12,
                      "mfma_frac": kf[dom] / (km[dom] * 1e-3) / 1e12 / peak_mfma},
     }
