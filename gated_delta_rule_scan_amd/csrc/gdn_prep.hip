@@ -146,12 +146,28 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       float sq = 0.f, sk = 0.f, sqk = 0.f;
+      if constexpr (sizeof(MT) == 2) {
+        // two bf16 products per instruction (exact in fp32), fp32 sums; the
+        // pairs come from one bit cast of the whole piece and vector shuffles
+        const bf16x8 q8 = __builtin_bit_cast(bf16x8, vq[i]), k8 = __builtin_bit_cast(bf16x8, vk[i]);
+#define GDN_DOT2_PAIR(a, b)                                                                   \
+  {                                                                                           \
+    const auto xq = __builtin_shufflevector(q8, q8, a, b);                                    \
+    const auto xk = __builtin_shufflevector(k8, k8, a, b);                                    \
+    sq = __builtin_amdgcn_fdot2_f32_bf16(xq, xq, sq, false);                                  \
+    sk = __builtin_amdgcn_fdot2_f32_bf16(xk, xk, sk, false);                                  \
+    sqk = __builtin_amdgcn_fdot2_f32_bf16(xq, xk, sqk, false);                                \
+  }
+        GDN_DOT2_PAIR(0, 1) GDN_DOT2_PAIR(2, 3) GDN_DOT2_PAIR(4, 5) GDN_DOT2_PAIR(6, 7)
+#undef GDN_DOT2_PAIR
+      } else {
 #pragma unroll
-      for (int e = 0; e < EP; ++e) {
-        const float xq = elem(vq[i], e), xk = elem(vk[i], e);
-        sq = fmaf(xq, xq, sq);
-        sk = fmaf(xk, xk, sk);
-        sqk = fmaf(xq, xk, sqk);
+        for (int e = 0; e < EP; ++e) {
+          const float xq = elem(vq[i], e), xk = elem(vk[i], e);
+          sq = fmaf(xq, xq, sq);
+          sk = fmaf(xk, xk, sk);
+          sqk = fmaf(xq, xk, sqk);
+        }
       }
 #pragma unroll
       for (int m = 1; m < PR; m <<= 1) {

@@ -36,6 +36,20 @@ struct VdaSmem {
   static constexpr size_t region = 2 * stage_bytes > mat_bytes ? 2 * stage_bytes : mat_bytes;
 };
 
+// ss + the sum of squares of eight bf16 values (16 bytes), two per
+// instruction; bf16 products are exact in fp32
+__device__ __forceinline__ float sumsq_bf16x8(const f32x4& p, float ss) {
+  // the pairs come from one bit cast of the whole piece and vector shuffles
+  // (a bit cast of each extracted float element was compiled to one
+  // register for every pair)
+  const bf16x8 v = __builtin_bit_cast(bf16x8, p);
+  ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), __builtin_shufflevector(v, v, 0, 1), ss, false);
+  ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), __builtin_shufflevector(v, v, 2, 3), ss, false);
+  ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), __builtin_shufflevector(v, v, 4, 5), ss, false);
+  ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), __builtin_shufflevector(v, v, 6, 7), ss, false);
+  return ss;
+}
+
 // bf16 fragment of raw values times per-token weights (w0: tokens 0-3 of the
 // lane's eight, w1: tokens 4-7), split into hi + lo so that the product keeps
 // fp32 accuracy on the bf16 matrix cores.
@@ -136,17 +150,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     // row norm over the row's TPR threads
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < NPK; ++i)
+    for (int i = 0; i < NPK; ++i) {
+      if constexpr (SM::BF) {
+        ss = sumsq_bf16x8(kp[i], ss);
+      } else {
 #pragma unroll
-      for (int e = 0; e < EP; ++e) {
-        float x;
-        if constexpr (SM::BF) {
-          x = (float)__builtin_bit_cast(bf16x8, kp[i])[e];
-        } else {
-          x = kp[i][e];
-        }
-        ss = fmaf(x, x, ss);
+        for (int e = 0; e < 4; ++e) ss = fmaf(kp[i][e], kp[i][e], ss);
       }
+    }
 #pragma unroll
     for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
     const float rkn = 1.0f / fmaxf(sqrtf(ss), kNormEps);
@@ -769,10 +780,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         qf[c] = M::load(qb + (16 * rt + l16) * QP + 32 * c + 8 * g4);
+        if constexpr (BF) {
+          ss = sumsq_bf16x8(__builtin_bit_cast(f32x4, qf[c]), ss);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = M::get(qf[c], e);
-          ss = fmaf(x, x, ss);
+          for (int e = 0; e < 8; ++e) ss = fmaf(M::get(qf[c], e), M::get(qf[c], e), ss);
         }
       }
       ss += __shfl_xor(ss, 16, 64);
