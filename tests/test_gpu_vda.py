@@ -171,3 +171,18 @@ def test_full_size_480p_disjoint_regions_with_epilogue():
         e1 = check(out[b:b + 1, :, h:h + 1], ref, TOL["bf16"], f"vda480 lag8 epi out b{b} h{h}")
         e2 = check(s[:, b:b + 1, h:h + 1], ref_s, TOL["bf16"], f"vda480 lag8 epi state b{b} h{h}")
         print(f"\nvda480 lag8 epilogue b{b} h{h}: out {e1:.2e} state {e2:.2e}", flush=True)
+
+
+def test_full_size_720p_bidirectional_sampled_heads():
+    """B1 H24 d128 bf16, 31 frames of 3600 tokens (45 x 80 latent), both
+    directions; the oracle recomputes two sampled heads over every token."""
+    w = synth.Workload("vda720", 1, 24, 111600, 128, 128, "bf16", "bi", -3.0, 0.0, 4)
+    x = synth.generate_frames(w, 3600)
+    out, s = _run(x, "bi", 3600)
+    for b, h in [(0, 0), (0, 23)]:
+        sel = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v")}
+        ref, ref_s = vda_oracle.forward(sel["q"], sel["k"], sel["v"], x["log_alpha"][:, b:b + 1, :, h:h + 1],
+                                        x["beta"][:, b:b + 1, :, h:h + 1], None, "bi", 3600)
+        e1 = check(out[b:b + 1, :, h:h + 1], ref, TOL["bf16"], f"vda720 out b{b} h{h}")
+        e2 = check(s[:, b:b + 1, h:h + 1], ref_s, TOL["bf16"], f"vda720 state b{b} h{h}")
+        print(f"\nvda720 b{b} h{h}: out {e1:.2e} state {e2:.2e}", flush=True)
