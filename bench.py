@@ -307,8 +307,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; the scan shards over (batch, head, "
-                                   "direction) chains with no communication, see DESIGN.md; run with --gpus 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the scan shards over (batch, head, "
+                                   "direction) chains with no communication; run with --gpus 1"}))
         return 2
 
     import numpy as np

@@ -37,7 +37,7 @@ Readout epilogue ("Key Contributions" item 1: a sigmoid gate and RMS
 normalisation of the linear branch's readout), on the summed readout o of
 each (token, head): y = norm_weight * o / sqrt(mean(o^2) + eps) * sigmoid(gate).
 
-Readings taken where the page is silent (listed in the design doc as well):
+Readings taken where the page is silent:
   * q and k are normalised as in the token scan: x^ = x / max(|x|_2, 1e-6);
   * one decay a_t = exp(log_alpha_t) per frame, one write strength beta_i per
     token (beta >= 0 keeps A_t positive semi-definite);
