@@ -748,6 +748,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   constexpr int NPQ = 64 * PR / 256;          // pieces per thread per block
   constexpr int kDepth = BF ? (EPI ? 2 : 3) : 1;  // blocks in flight per thread (the epilogue needs registers)
   __shared__ __align__(16) MT qs[2][64 * QP];
+  // bf16 epilogue: the gate logits are staged through LDS beside q, loaded one
+  // block ahead (one register set: the q ring holds the rest); fp32 inputs
+  // load them per lane at use
+  constexpr bool ZST = EPI && BF;
+  constexpr int ZP = DV + 16 / ES, PZ = DV * ES / 16, NPZ = ZST ? 64 * PZ / 256 : 1;
+  __shared__ __align__(16) MT zs[ZST ? 2 : 1][ZST ? 64 * ZP : 8];
+  [[maybe_unused]] f32x4 zr[NPZ];
+  auto load_z = [&](int jb, f32x4 (&z)[NPZ]) {
+    const int64_t fs = f0 + 64 * (int64_t)jb;
+    const rsrc_t rz = make_rsrc(static_cast<const MT*>(a.gate) + ((b * T + fs) * H + h) * DV,
+                                (uint32_t)(rows_of(jb) - 1) * HGB + DV * ES);
+#pragma unroll
+    for (int i = 0; i < NPZ; ++i) {
+      const int pc = i * 256 + tid;
+      z[i] = bload16(rz, (uint32_t)(pc / PZ) * HGB + (uint32_t)(pc % PZ) * 16u);
+    }
+  };
   auto load_q = [&](int jb, f32x4 (&qr)[NPQ]) {
     const int64_t fs = f0 + 64 * (int64_t)jb;
     const rsrc_t rq = make_rsrc(static_cast<const MT*>(a.q) + ((b * T + fs) * H + h) * DK,
@@ -767,8 +784,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
       const int pc = i * 256 + tid;
       *reinterpret_cast<f32x4*>(qb + (pc / PR) * QP + (pc % PR) * (16 / ES)) = qr[k][i];
     }
-    // refill this slot kDepth blocks ahead (clamped to the last block)
+    if constexpr (ZST) {
+      MT* zb = zs[(jb - jb0) & 1];
+#pragma unroll
+      for (int i = 0; i < NPZ; ++i) {
+        const int pc = i * 256 + tid;
+        *reinterpret_cast<f32x4*>(zb + (pc / PZ) * ZP + (pc % PZ) * (16 / ES)) = zr[i];
+      }
+    }
+    // refill this slot kDepth blocks ahead (clamped to the last block); the
+    // gate one block ahead
     load_q(jb + kDepth < jend ? jb + kDepth : jend - 1, qr[k]);
+    if constexpr (ZST) load_z(jb + 1 < jend ? jb + 1 : jend - 1, zr);
     __syncthreads();  // the block is in LDS; the buffer written two blocks ago is free
     // one 16-token row tile at a time: its fragments, its norms, its products
     f32x4 acc[CT][4];
@@ -809,22 +836,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     if constexpr (EPI) {
       // epilogue: out = w * o / sqrt(mean(o^2) + eps) * sigmoid(z) per token;
       // the mean over dv spans the four waves (partial sums through LDS)
-      const rsrc_t rz = make_rsrc(static_cast<const MT*>(a.gate) + ((b * T + fs) * H + h) * DV,
-                                  (uint32_t)(rows_of(jb) - 1) * HGB + DV * ES);
-      f32x4 zv[CT][4];
-#pragma unroll
-      for (int cc = 0; cc < CT; ++cc)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const uint32_t off = (uint32_t)(16 * rt + l16) * HGB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * ES;
-          if constexpr (BF) {
-            const uint2 raw = bload8(rz, off);
-            zv[cc][rt] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
-                               __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
-          } else {
-            zv[cc][rt] = bload16(rz, off);
-          }
-        }
+      [[maybe_unused]] const MT* zb = zs[(jb - jb0) & 1];
+      [[maybe_unused]] const rsrc_t rz = make_rsrc(static_cast<const MT*>(a.gate) + ((b * T + fs) * H + h) * DV,
+                                                   (uint32_t)(rows_of(jb) - 1) * HGB + DV * ES);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         float ss = 0.f;
@@ -844,12 +858,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
         const float tot = s_ss[0][16 * rt + l16] + s_ss[1][16 * rt + l16] + s_ss[2][16 * rt + l16] + s_ss[3][16 * rt + l16];
         const float inv = 1.0f / sqrtf(tot * (1.0f / DV) + a.norm_eps);
 #pragma unroll
-        for (int cc = 0; cc < CT; ++cc)
+        for (int cc = 0; cc < CT; ++cc) {
+          // this lane's four gate logits: token 16 rt + l16, columns 16 (CT w + cc) + 4 g4 ..
+          f32x4 zv;
+          if constexpr (ZST) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(zb + (16 * rt + l16) * ZP + 16 * (CT * w + cc) + 4 * g4);
+            zv = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                       __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
+          } else {
+            zv = bload16(rz, (uint32_t)(16 * rt + l16) * HGB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * ES);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * zv[cc][rt][e]));
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * zv[e]));
             acc[cc][rt][e] = acc[cc][rt][e] * (inv * nw[cc][e]) * sg;
           }
+        }
       }
     }
 #pragma unroll
@@ -859,7 +883,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
         bstore16(ro, (uint32_t)(16 * rt + l16) * HOB + (uint32_t)(16 * (CT * w + cc) + 4 * g4) * 4u, acc[cc][rt]);
   };
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k) load_q(jb0 + k < jend ? jb0 + k : jend - 1, qr[k]);
+  for (int k = 0; k < kDepth; ++k) {
+    load_q(jb0 + k < jend ? jb0 + k : jend - 1, qr[k]);
+  }
+  if constexpr (ZST) load_z(jb0, zr);
   // whole turns of the ring, then the remainder
   int jb = jb0;
   for (; jb + kDepth <= jend; jb += kDepth) {
