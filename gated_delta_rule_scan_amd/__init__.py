@@ -269,3 +269,52 @@ def vda_forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd",
     if st != GDN_OK:
         raise GdnError(st)
     return out, state_out
+
+
+# ---- torch.library custom ops: the two calls as graph-safe operators ----
+# (torch.compile traces them as opaque nodes with the output shapes below,
+# instead of breaking the graph at the ctypes call)
+
+_ops_registered = False
+
+
+def register_torch_ops() -> None:
+    """Register torch.ops.gdn.forward and torch.ops.gdn.vda_forward (CUDA
+    tensors; outputs allocated by the op) with fake implementations for
+    tracing.  Idempotent."""
+    global _ops_registered
+    if _ops_registered:
+        return
+    import torch
+
+    @torch.library.custom_op("gdn::forward", mutates_args=(), device_types="cuda",
+                             schema="(Tensor q, Tensor k, Tensor v, Tensor log_alpha, Tensor beta, Tensor? state_in, "
+                                    "str direction, int chunk, int dv_tile, bool erase) -> (Tensor, Tensor)")
+    def _forward_op(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase):
+        return forward(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase=erase)
+
+    @_forward_op.register_fake
+    def _(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        dirs = 2 if direction == "bi" else 1
+        return (q.new_empty((B, T, H, dv), dtype=torch.float32),
+                q.new_empty((dirs, B, H, dv, dk), dtype=torch.float32))
+
+    @torch.library.custom_op("gdn::vda_forward", mutates_args=(), device_types="cuda",
+                             schema="(Tensor q, Tensor k, Tensor v, Tensor log_alpha, Tensor beta, Tensor? state_in, "
+                                    "str direction, int frame, str write, int lag, Tensor? gate, Tensor? norm_weight, "
+                                    "float norm_eps) -> (Tensor, Tensor)")
+    def _vda_op(q, k, v, log_alpha, beta, state_in, direction, frame, write, lag, gate, norm_weight, norm_eps):
+        return vda_forward(q, k, v, log_alpha, beta, state_in, direction, frame, write=write, lag=lag, gate=gate,
+                           norm_weight=norm_weight, norm_eps=norm_eps)
+
+    @_vda_op.register_fake
+    def _(q, k, v, log_alpha, beta, state_in, direction, frame, write, lag, gate, norm_weight, norm_eps):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        dirs = 2 if direction == "bi" else 1
+        return (q.new_empty((B, T, H, dv), dtype=torch.float32),
+                q.new_empty((dirs, B, H, dv, dk), dtype=torch.float32))
+
+    _ops_registered = True
