@@ -106,12 +106,6 @@ __device__ __forceinline__ f32x4 bload16(rsrc_t r, uint32_t off) {
   return f;
 }
 
-__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t off) {
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-  return uint2{v.x, v.y};
-}
-
 __device__ __forceinline__ float bload4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
@@ -195,10 +189,11 @@ __device__ __forceinline__ bf16x8 load_kt_frag(const bf16* krow, int kp, int tok
 //                             zeros (C + 4 floats: whole 16-byte pieces),
 //                             padded to PDS = pdg_stride(C) floats so that no
 //                             128-byte cache line holds two chunks' records
-//   rdy  [NBH][NC] uint32 : 1 once the preparation kernel's outputs for the
-//                             chunk (and its output fill) are in place; the
-//                             state chain waits for it when the two kernels
-//                             run concurrently
+//   rdy  [NBH][NC] uint32 : per-chunk ready flags of the concurrent
+//                             preparation: a small kernel marks every chunk 1
+//                             (pending), the preparation kernel stores 0 once
+//                             the chunk's outputs (and its output fill) are in
+//                             place, and the state chain waits for 0
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t tri, pqk, sc, pdg, rdy, total;
