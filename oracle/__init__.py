@@ -13,7 +13,9 @@ per-chunk quantities (triangular inverse, pseudo-values) the kernels build.
 Where each function stands relative to its pins (see ``tests/test_oracle_pins.py``):
 every function here is pinned; the inclusive reverse scan is a reading of the
 pages (the reverse readout includes the current token), not something the pages
-fix, so that single choice is "parity unpinned".
+fix, so that single choice is "parity unpinned".  The exclusive readouts (either
+direction reading before the token's own write) are pinned by brute force and
+by perturbation; where the decay a_t stands in them is a reading.
 """
 from __future__ import annotations
 
@@ -30,6 +32,8 @@ _SO = os.path.join(_HERE, "_build", "liboracle.so")
 _lib = None
 
 DIRECTIONS = {"fwd": 0, "rev": 1, "bi": 2}
+# which directions read their memory before the token's own write
+EXCLUSIVE = {"none": 0, "fwd": 1, "rev": 2, "both": 3}
 
 
 def build(force: bool = True) -> str:
@@ -53,7 +57,7 @@ def _load():
         lib = ctypes.CDLL(_SO)
         i64, p = ctypes.c_int64, ctypes.c_void_p
         lib.gdn_oracle_forward.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p,
-                                           ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.gdn_oracle_forward.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -74,11 +78,16 @@ def default_threads() -> int:
 
 
 def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", erase: bool = True,
-            nthreads: Optional[int] = None, want_state: bool = True) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+            nthreads: Optional[int] = None, want_state: bool = True,
+            exclusive: str = "none") -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Run the token-by-token recurrence in double precision.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv] (float32, or uint16 bf16 bit patterns);
     log_alpha, beta: [dirs,B,T,H]; state_in: [dirs,B,H,dv,dk] or None.
+    exclusive: "none", "fwd", "rev" or "both" -- the directions whose readout
+    is taken after the decay and before the token's own write (o_t = a_t
+    S_{t-1} q^_t), which makes the two scans of a bidirectional call cover
+    disjoint regions (see gdn_oracle.c).
     Returns (out [B,T,H,dv] float64, state_out [dirs,B,H,dv,dk] float64 or None).
     """
     q, k, v = as_f32(q), as_f32(k), as_f32(v)
@@ -95,7 +104,7 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", era
     rc = _load().gdn_oracle_forward(
         B, T, H, dk, dv, q.ctypes.data, k.ctypes.data, v.ctypes.data, la.ctypes.data, bt.ctypes.data,
         None if s_in is None else s_in.ctypes.data, None if s_out is None else s_out.ctypes.data,
-        out.ctypes.data, DIRECTIONS[direction], int(bool(erase)), nth)
+        out.ctypes.data, DIRECTIONS[direction], int(bool(erase)), EXCLUSIVE[exclusive], nth)
     if rc != 0:
         raise RuntimeError(f"oracle failed with code {rc}")
     return out, s_out

@@ -28,6 +28,16 @@
  *   final state (the two scans whose readouts are added, "Video DeltaNet",
  *   "Methodology in Plain English").
  *
+ *   Exclusive readout (bit 0 of `exclusive` for the forward direction, bit 1
+ *   for the reverse one): that direction reads its memory after the decay and
+ *   before the token's own write, o_t = a_t S_{t-1} q^_t (reverse:
+ *   a_t S_{t+1} q^_t).  With both bits set the two scans of a bidirectional
+ *   call cover the disjoint regions s < t and s > t, and with only the reverse
+ *   bit the regions s <= t and s > t, which together hold every token once
+ *   (the disjoint-region combine of "Video DeltaNet", "Methodology in Plain
+ *   English", at token granularity; the reading of where the decay a_t stands
+ *   is ours: the excluded part is exactly the token's own write).
+ *
  *   With erase == 0 the "- beta k k^T" erase term is dropped (S <- a S +
  *   beta v k^T): the plain gated linear attention that results from removing
  *   the delta-rule update (SANA-Video 2.0 review, "Future work").  It pins the
@@ -60,6 +70,7 @@ typedef struct {
   double *state_out, *out_fwd, *out_rev;
   int direction; /* 0 forward, 1 reverse, 2 both */
   int erase;
+  int exclusive; /* bit 0: forward direction reads before its write, bit 1: reverse */
   int64_t next_chain; /* work counter, protected by lock */
   pthread_mutex_t lock;
 } job_t;
@@ -95,6 +106,16 @@ static void run_chain(job_t* J, int64_t b, int64_t h, int dir_slot, int reverse,
     const float* vt = J->v + row * dv;
     /* S <- a S */
     for (int64_t i = 0; i < dv * dk; ++i) S[i] *= a;
+    double* o = out + row * dv;
+    const int excl = (J->exclusive >> (reverse ? 1 : 0)) & 1;
+    if (excl) {
+      /* o = (a S) q^, before the token's own write */
+      for (int64_t i = 0; i < dv; ++i) {
+        double s = 0.0;
+        for (int64_t j = 0; j < dk; ++j) s += S[i * dk + j] * qh[j];
+        o[i] = s;
+      }
+    }
     if (J->erase) {
       /* u = beta (v - S k^) */
       for (int64_t i = 0; i < dv; ++i) {
@@ -109,11 +130,12 @@ static void run_chain(job_t* J, int64_t b, int64_t h, int dir_slot, int reverse,
     for (int64_t i = 0; i < dv; ++i)
       for (int64_t j = 0; j < dk; ++j) S[i * dk + j] += u[i] * kh[j];
     /* o = S q^ */
-    double* o = out + row * dv;
-    for (int64_t i = 0; i < dv; ++i) {
-      double s = 0.0;
-      for (int64_t j = 0; j < dk; ++j) s += S[i * dk + j] * qh[j];
-      o[i] = s;
+    if (!excl) {
+      for (int64_t i = 0; i < dv; ++i) {
+        double s = 0.0;
+        for (int64_t j = 0; j < dk; ++j) s += S[i * dk + j] * qh[j];
+        o[i] = s;
+      }
     }
   }
   if (J->state_out) {
@@ -152,15 +174,16 @@ static void* worker(void* arg) {
 int gdn_oracle_forward(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, const float* q,
                        const float* k, const float* v, const float* log_alpha, const float* beta,
                        const float* state_in, double* state_out, double* out, int direction,
-                       int erase, int nthreads) {
+                       int erase, int exclusive, int nthreads) {
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || direction < 0 || direction > 2) return 1;
+  if (exclusive < 0 || exclusive > 3) return 1;
   if (!out || (T > 0 && (!q || !k || !v || !log_alpha || !beta))) return 1;
   job_t J;
   memset(&J, 0, sizeof(J));
   J.B = B; J.T = T; J.H = H; J.dk = dk; J.dv = dv;
   J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = beta;
   J.state_in = state_in; J.state_out = state_out;
-  J.direction = direction; J.erase = erase;
+  J.direction = direction; J.erase = erase; J.exclusive = exclusive;
   J.out_fwd = out;
   double* rev = NULL;
   const size_t n_out = (size_t)(B * T * H * dv);

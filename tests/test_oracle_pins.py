@@ -307,3 +307,134 @@ def test_forward_heads_matches_full_run():
     for i, (b, h) in enumerate(heads):
         np.testing.assert_array_equal(oh[i], o[b, :, h])
         np.testing.assert_array_equal(sh[:, i], s[:, b, h])
+
+
+def _bidirectional_linear_attention(q, k, v, la_f, bt_f, la_r, bt_r, incl_f, incl_r):
+    """Brute-force bidirectional gated linear attention (no erase), one chain.
+
+    Every pair (t, s) written out with its explicit product of gates: the
+    forward scan brings token s <= t (s < t when exclusive) with weight
+    prod_{r=s+1..t} a_r, the reverse scan token s >= t (s > t when exclusive)
+    with weight prod_{r=t..s-1} a'_r.
+    """
+    qh, kh = _unit(q.astype(np.float64)), _unit(k.astype(np.float64))
+    af, ar = np.exp(la_f.astype(np.float64)), np.exp(la_r.astype(np.float64))
+    T = q.shape[0]
+    out = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        for s in range(T):
+            c = qh[t] @ kh[s]
+            if s < t or (s == t and incl_f):
+                out[t] += np.prod(af[s + 1:t + 1]) * bt_f[s] * c * v[s]
+            if s > t or (s == t and incl_r):
+                w = np.prod(ar[t:s]) if s > t else 1.0
+                out[t] += w * bt_r[s] * c * v[s]
+    return out
+
+
+@pytest.mark.parametrize("exclusive", ["none", "fwd", "rev", "both"])
+def test_exclusive_readout_erase_free_brute_force(exclusive):
+    """Erase-free bidirectional scan with either readout against the pairwise sum.
+
+    With only the reverse direction exclusive the two regions s <= t and s > t
+    hold every token once; with both exclusive the token itself is in neither.
+    """
+    x = _rand_problem(21, T=27, direction="bi", state_std=0.0)
+    o, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None, "bi", erase=False,
+                          exclusive=exclusive)
+    incl_f = exclusive in ("none", "rev")
+    incl_r = exclusive in ("none", "fwd")
+    for h in range(2):
+        ref = _bidirectional_linear_attention(
+            x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h],
+            x["log_alpha"][0, 0, :, h], x["beta"][0, 0, :, h].astype(np.float64),
+            x["log_alpha"][1, 0, :, h], x["beta"][1, 0, :, h].astype(np.float64), incl_f, incl_r)
+        np.testing.assert_allclose(o[0, :, h], ref, rtol=0, atol=1e-12)
+
+
+def test_exclusive_partition_without_gates_is_noncausal_linear_attention():
+    """a = 1, beta = 1, reverse exclusive: out = (Q^ K^^T) V over the whole sequence."""
+    x = _rand_problem(22, T=31, direction="bi", state_std=0.0)
+    la, bt = np.zeros_like(x["log_alpha"]), np.ones_like(x["beta"])
+    o, _ = oracle.forward(x["q"], x["k"], x["v"], la, bt, None, "bi", erase=False, exclusive="rev")
+    qh, kh = _unit(x["q"][0].astype(np.float64)), _unit(x["k"][0].astype(np.float64))
+    ref = np.einsum("thk,shk,shv->thv", qh, kh, x["v"][0].astype(np.float64))
+    np.testing.assert_allclose(o[0], ref, rtol=0, atol=1e-12)
+
+
+def test_exclusive_readout_ignores_the_tokens_own_write():
+    """Changing token t's key, value and write strength leaves exclusive readouts at t untouched."""
+    x = _rand_problem(23, T=19, direction="bi")
+    t = 7
+    y = {n: a.copy() for n, a in x.items()}
+    y["k"][:, t] = -2.0 * y["k"][:, t] + 0.5
+    y["v"][:, t] += 3.0
+    y["beta"][:, :, t] = 1.0 - y["beta"][:, :, t]
+    args = lambda d, sl: (d["q"], d["k"], d["v"], d["log_alpha"][sl], d["beta"][sl], d["state_in"][sl])
+    # both exclusive: the two regions exclude t, bit for bit
+    o1, _ = oracle.forward(*args(x, slice(None)), "bi", exclusive="both")
+    o2, _ = oracle.forward(*args(y, slice(None)), "bi", exclusive="both")
+    np.testing.assert_array_equal(o1[:, t], o2[:, t])
+    assert np.abs(o1[:, t + 1] - o2[:, t + 1]).max() > 1e-3
+    # forward exclusive: every readout up to t; reverse exclusive: from t on
+    o1, _ = oracle.forward(*args(x, slice(0, 1)), "fwd", exclusive="fwd")
+    o2, _ = oracle.forward(*args(y, slice(0, 1)), "fwd", exclusive="fwd")
+    np.testing.assert_array_equal(o1[:, :t + 1], o2[:, :t + 1])
+    o1, _ = oracle.forward(*args(x, slice(1, 2)), "rev", exclusive="rev")
+    o2, _ = oracle.forward(*args(y, slice(1, 2)), "rev", exclusive="rev")
+    np.testing.assert_array_equal(o1[:, t:], o2[:, t:])
+    # the inclusive readout does see the token
+    o1, _ = oracle.forward(*args(x, slice(0, 1)), "fwd")
+    o2, _ = oracle.forward(*args(y, slice(0, 1)), "fwd")
+    assert np.abs(o1[:, t] - o2[:, t]).max() > 1e-3
+    # the exclusive option changes readouts only: final states are the inclusive ones
+    _, s1 = oracle.forward(*args(x, slice(None)), "bi")
+    _, s2 = oracle.forward(*args(x, slice(None)), "bi", exclusive="both")
+    np.testing.assert_array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("t", [0, 1, 12, 24])
+def test_exclusive_readout_is_decayed_prefix_state(t):
+    """Delta rule: exclusive o_t = a_t S_{t-1} q^_t with S_{t-1} the state after tokens < t.
+
+    S_{t-1} comes from a separate call over the prefix (its final state); the
+    reverse direction mirrors this with the suffix after t.
+    """
+    x = _rand_problem(24, T=25, direction="bi")
+    q, k, v, la, bt, s0 = x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"]
+    T = q.shape[1]
+    qh = _unit(q[0, t].astype(np.float64))
+    of, _ = oracle.forward(q, k, v, la[:1], bt[:1], s0[:1], "fwd", exclusive="fwd")
+    _, sp = oracle.forward(q[:, :t], k[:, :t], v[:, :t], la[:1, :, :t], bt[:1, :, :t], s0[:1], "fwd")
+    a = np.exp(la[0, 0, t].astype(np.float64))
+    ref = a[:, None] * np.einsum("hvk,hk->hv", sp[0, 0], qh)
+    np.testing.assert_allclose(of[0, t], ref, rtol=0, atol=1e-13)
+    orv, _ = oracle.forward(q, k, v, la[1:], bt[1:], s0[1:], "rev", exclusive="rev")
+    _, ss = oracle.forward(q[:, t + 1:], k[:, t + 1:], v[:, t + 1:], la[1:, :, t + 1:], bt[1:, :, t + 1:],
+                           s0[1:], "rev")
+    a = np.exp(la[1, 0, t].astype(np.float64))
+    ref = a[:, None] * np.einsum("hvk,hk->hv", ss[0, 0], qh)
+    np.testing.assert_allclose(orv[0, t], ref, rtol=0, atol=1e-13)
+    assert T == 25
+
+
+def test_exclusive_text_state_enters_once():
+    """Text folded in as S_T/2 per direction, nothing written, no decay: out = S_T q^_t.
+
+    A single token reads a_0 S_in q^_0 from each direction whatever its write.
+    """
+    x = _rand_problem(25, T=9, direction="bi")
+    S_T = np.random.default_rng(5).standard_normal((1, 2, 6, 8)).astype(np.float32)
+    half = np.stack([S_T / 2, S_T / 2])
+    la, bt = np.zeros_like(x["log_alpha"]), np.zeros_like(x["beta"])
+    o, _ = oracle.forward(x["q"], x["k"], x["v"], la, bt, half, "bi", exclusive="both")
+    qh = _unit(x["q"][0].astype(np.float64))
+    np.testing.assert_allclose(o[0], np.einsum("hvk,thk->thv", S_T[0].astype(np.float64), qh), rtol=0,
+                               atol=1e-13)
+    sl = slice(3, 4)
+    o, _ = oracle.forward(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], x["log_alpha"][:, :, sl],
+                          x["beta"][:, :, sl], x["state_in"], "bi", exclusive="both")
+    a = np.exp(x["log_alpha"][:, 0, 3].astype(np.float64))  # [dirs, H]
+    S = x["state_in"][:, 0].astype(np.float64)                 # [dirs, H, dv, dk]
+    ref = np.einsum("dh,dhvk,hk->hv", a, S, qh[3])
+    np.testing.assert_allclose(o[0, 0], ref, rtol=0, atol=1e-13)
