@@ -296,6 +296,8 @@ def main() -> int:
     ap.add_argument("--serial", action="store_true", help="keep the preparation pass before the chain (no overlap)")
     ap.add_argument("--no-erase", action="store_true",
                     help="time the erase-free variant (gated linear attention, GDN_OPT_NO_ERASE) instead of the delta rule")
+    ap.add_argument("--exclusive", choices=["none", "fwd", "rev", "both"], default="none",
+                    help="directions that read before the token's own write (GDN_OPT_EXCLUSIVE_*: disjoint regions)")
     ap.add_argument("--vda", action="store_true",
                     help="time the frame-wise delta operator (gdn_vda_forward) on the workload's frames instead")
     ap.add_argument("--vda-write", choices=("inverse", "additive"), default="inverse",
@@ -342,7 +344,7 @@ def main() -> int:
     def step(ev_ptr=None):
         gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction, chunk=args.chunk,
                     dv_tile=args.dv_tile, out=out, state_out=s_out, workspace=ws, timing_events=ev_ptr,
-                    serial=args.serial, erase=not args.no_erase)
+                    serial=args.serial, erase=not args.no_erase, exclusive=args.exclusive)
 
     for _ in range(args.warmup):
         step()
@@ -400,6 +402,7 @@ def main() -> int:
                    "direction": w.direction, "chunk": C, "dv_tile": args.dv_tile or "auto",
                    "prep": "concurrent with the chain" if concurrent else "before the chain",
                    "operator": "erase-free (gated linear attention)" if args.no_erase else "gated delta rule",
+                   "exclusive_readout": args.exclusive,
                    "inputs": "seeded synthetic video-latent-shaped (synth.WORKLOADS)"},
         "tflops": tflops,
         "mfma_frac": tflops / peak_mfma,
@@ -408,7 +411,10 @@ def main() -> int:
         "kernels_ms": {"chunk_prep": prep_ms, "state_chain": chain_ms},
         "roofline": {"kernel": dom_name, "bound": "hbm",
                      "achieved": achieved, "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": achieved / MI355X_HBM_GBS,
-                     "traffic": measured_traffic(dom_name, args.workload), "alg_bytes_per_launch": kb[dom],
+                     # the committed counters were taken with the default options
+                     "traffic": (measured_traffic(dom_name, args.workload)
+                                 if not args.no_erase and args.exclusive == "none" else None),
+                     "alg_bytes_per_launch": kb[dom],
                      "avg_launch_ms": kt[dom], "source_hash": kernel_source_hash(dom_name)},
         "wall_s_timed": wall,
     }

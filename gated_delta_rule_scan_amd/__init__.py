@@ -35,6 +35,11 @@ GDN_DTYPE_BF16 = 1
 
 GDN_OPT_SERIAL = 1
 GDN_OPT_NO_ERASE = 2
+GDN_OPT_EXCLUSIVE_FORWARD = 4
+GDN_OPT_EXCLUSIVE_REVERSE = 8
+# which directions read their memory before the token's own write
+EXCLUSIVE = {"none": 0, "fwd": GDN_OPT_EXCLUSIVE_FORWARD, "rev": GDN_OPT_EXCLUSIVE_REVERSE,
+             "both": GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE}
 
 GDN_VDA_OPT_ADDITIVE = 1
 
@@ -146,7 +151,8 @@ def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd"
 
 def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chunk: int = 0, dv_tile: int = 0,
             out=None, state_out=None, workspace=None, want_state: bool = True, stream=None,
-            timing_events: Optional[int] = None, serial: bool = False, erase: bool = True) -> Tuple:
+            timing_events: Optional[int] = None, serial: bool = False, erase: bool = True,
+            exclusive: str = "none") -> Tuple:
     """Run the scan on torch CUDA tensors (layouts of include/gdn.h).
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv] (float32 or bfloat16, same dtype);
@@ -157,10 +163,17 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     library may run the chunk preparation concurrently on its own stream.
     ``erase=False`` selects the erase-free variant (GDN_OPT_NO_ERASE: gated
     linear attention with write strength beta).
+    ``exclusive``: "none", "fwd", "rev" or "both" -- the directions that read
+    their memory before the token's own write, o_t = a_t S_{t-1} q^_t
+    (GDN_OPT_EXCLUSIVE_FORWARD / _REVERSE): "both" makes the two scans of a
+    bidirectional call cover disjoint regions, "rev" alone counts every
+    token once.
     ``timing_events``: address of four caller-owned hipEvent_t (see gdn.h).
     """
     import torch
 
+    if exclusive not in EXCLUSIVE:
+        raise ValueError(f"exclusive must be one of {sorted(EXCLUSIVE)}")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dirs = 2 if direction == "bi" else 1
@@ -195,7 +208,7 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     prob.workspace_bytes = workspace.numel() if workspace is not None else 0
     prob.stream = s.cuda_stream
     prob.timing_events = timing_events
-    prob.options = (GDN_OPT_SERIAL if serial else 0) | (0 if erase else GDN_OPT_NO_ERASE)
+    prob.options = (GDN_OPT_SERIAL if serial else 0) | (0 if erase else GDN_OPT_NO_ERASE) | EXCLUSIVE[exclusive]
     st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                      None if state_in is None else state_in.data_ptr(),
                      None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])
@@ -289,12 +302,14 @@ def register_torch_ops() -> None:
 
     @torch.library.custom_op("gdn::forward", mutates_args=(), device_types="cuda",
                              schema="(Tensor q, Tensor k, Tensor v, Tensor log_alpha, Tensor beta, Tensor? state_in, "
-                                    "str direction, int chunk, int dv_tile, bool erase) -> (Tensor, Tensor)")
-    def _forward_op(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase):
-        return forward(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase=erase)
+                                    "str direction, int chunk, int dv_tile, bool erase, str exclusive=\"none\") "
+                                    "-> (Tensor, Tensor)")
+    def _forward_op(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase, exclusive="none"):
+        return forward(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase=erase,
+                       exclusive=exclusive)
 
     @_forward_op.register_fake
-    def _(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase):
+    def _(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase, exclusive="none"):
         B, T, H, dk = q.shape
         dv = v.shape[-1]
         dirs = 2 if direction == "bi" else 1

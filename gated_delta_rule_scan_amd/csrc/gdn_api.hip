@@ -62,7 +62,8 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   if (!p) return GDN_ERR_INVALID_ARGUMENT;
   if (direction < GDN_DIR_FORWARD || direction > GDN_DIR_BIDIRECTIONAL) return GDN_ERR_INVALID_ARGUMENT;
   if (p->B < 1 || p->H < 1 || p->T < 0 || p->dk < 1 || p->dv < 1) return GDN_ERR_INVALID_ARGUMENT;
-  if ((p->options & ~(GDN_OPT_SERIAL | GDN_OPT_NO_ERASE)) != 0) return GDN_ERR_INVALID_ARGUMENT;
+  if ((p->options & ~(GDN_OPT_SERIAL | GDN_OPT_NO_ERASE | GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE)) != 0)
+    return GDN_ERR_INVALID_ARGUMENT;
   if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
   if (!supported_dim(p->dk) || !supported_dim(p->dv)) return GDN_ERR_UNSUPPORTED;
   if (p->B * p->H > 65535) return GDN_ERR_UNSUPPORTED;  // grid limit of the preparation kernel
@@ -246,6 +247,8 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   a.fwd_on = pl.fwd_on; a.rev_on = pl.rev_on; a.dirs = pl.dirs;
   a.zero_out = pl.dirs == 2;
   a.erase = (p->options & GDN_OPT_NO_ERASE) ? 0 : 1;
+  a.excl_fwd = (p->options & GDN_OPT_EXCLUSIVE_FORWARD) ? 1 : 0;
+  a.excl_rev = (p->options & GDN_OPT_EXCLUSIVE_REVERSE) ? 1 : 0;
 
   const bool bf = p->dtype == GDN_DTYPE_BF16;
   if (pl.NT == 0) pl.NT = pick_tiles(B * H, dv, pl.dirs);

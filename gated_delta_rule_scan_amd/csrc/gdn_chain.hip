@@ -278,12 +278,14 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   // triangle fragments: the k-chunks of this row tile that hold no element
   // of this direction's triangle are read past the buffer extent (zeros, see
   // the resources below); the diagonal k-chunk is masked (Tinv strictly, P
-  // with its diagonal)
+  // with its diagonal -- the self terms -- unless this direction reads
+  // before the token's own write, which is exactly P without its diagonal)
+  const bool self = !(rev ? a.excl_rev : a.excl_fwd);
   FragMask<MT> tmask[C / 32], pmask[C / 32];
 #pragma unroll
   for (int kc = 0; kc < C / 32; ++kc) {
     tmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, false, kc == kcd);
-    pmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, true, kc == kcd);
+    pmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, self, kc == kcd);
   }
   // readout offset of unit column tile 0 (transposed tile: token kq_row, four
   // columns from 4 g4)
@@ -296,7 +298,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   for (int kc = 0; kc < C / 32; ++kc) {
 #pragma unroll
     for (int i = 0; i < FragMask<MT>::NW; ++i) diag_only[kc].m[i] = 0u;
-    const int e0 = kq_row - 32 * kc - 8 * g4;
+    const int e0 = self ? kq_row - 32 * kc - 8 * g4 : -1;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (e == e0) {

@@ -238,6 +238,7 @@ struct ScanArgs {
   int dirs;            // number of computed directions (slots)
   int zero_out;        // the preparation kernel fills `out` with the "not written yet" pattern (bidirectional)
   int erase;           // 1: delta rule; 0: erase-free variant (no -beta k k^T term: L = 0, T = I)
+  int excl_fwd, excl_rev;  // 1: that direction reads before the token's own write (no self term)
 };
 
 // Arguments of the frame-wise operator's kernels.  Workspace, per

@@ -22,8 +22,9 @@
  *                         direction with its own (log_alpha, beta) and its own
  *                         initial state ("Video DeltaNet", "Methodology in
  *                         Plain English": forward and backward recurrent
- *                         states whose readouts are added).  The reverse
- *                         readout includes the current token.
+ *                         states whose readouts are added).  Both readouts
+ *                         include the current token unless an exclusive
+ *                         option bit (below) says otherwise.
  *
  * Streaming: the final state of one call is the initial state of the next
  * (the streaming state lifecycle of the issue's "Suggested phases", phase 1);
@@ -97,11 +98,23 @@ typedef enum {
 /* Bits of gdn_problem_t.options. */
 typedef enum {
   GDN_OPT_SERIAL = 1,       /* run both kernels one after the other on `stream` */
-  GDN_OPT_NO_ERASE = 2      /* the erase-free variant: S_t = a_t S_{t-1} + beta_t v_t k^_t^T,
+  GDN_OPT_NO_ERASE = 2,     /* the erase-free variant: S_t = a_t S_{t-1} + beta_t v_t k^_t^T,
                                i.e. gated linear attention with per-token write strength
                                beta (SANA-Video 2.0 review: the hybrid's linear layers are
                                gated linear attention, and its "Future work" relates them to
                                the delta rule by dropping the delta-rule update) */
+  GDN_OPT_EXCLUSIVE_FORWARD = 4,  /* the forward direction reads its memory before the
+                               token's own write: o_t = a_t S_{t-1} q^_t */
+  GDN_OPT_EXCLUSIVE_REVERSE = 8   /* the same for the reverse direction: o_t = a_t S_{t+1} q^_t.
+                               Both bits: the two scans of a bidirectional call cover the
+                               disjoint regions s < t and s > t (the current token is left to
+                               a local operator); the reverse bit alone: s <= t and s > t,
+                               every token once ("Video DeltaNet", "Methodology in Plain
+                               English": each direction sees its own non-overlapping part
+                               of the sequence, and the prompt's state enters each
+                               direction at half weight, S_T / 2 -- here the caller's
+                               state_in).
+                               Final states are unchanged by either bit. */
 } gdn_option_t;
 
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
@@ -163,8 +176,9 @@ gdn_status_t gdn_forward(const gdn_problem_t* p,
  *    corrections with 1/sqrt(U) key scaling, U = the frame's token count):
  *    S_t = a_t S_{t-1} (I - A_t / U) + B_t / sqrt(U).
  *  - readout_lag = d > 0: the disjoint-region readout ("Methodology in Plain
- *    English": the forward and reverse memories cover disjoint regions, the
- *    text enters as an initial state S_T/2 in each direction).  A token of
+ *    English": the forward and reverse memories see non-overlapping parts of
+ *    the video, and the text's state starts each direction at half weight,
+ *    S_T/2).  A token of
  *    frame t reads the forward state after frame t - d and the reverse state
  *    after frame t + d; where that frame does not exist, the direction's
  *    initial state (zero without state_in).  d = 0 reads its own frame's state.

@@ -26,9 +26,9 @@ token count,
 
     S_t = Sbar_t + sum_i beta_i (v_i - Sbar_t k~_i) k~_i^T,   k~_i = k^_i / sqrt(U).
 
-Disjoint-region readout ("Methodology in Plain English": the two scans cover
-disjoint regions, so their readouts add without counting a frame twice; the
-text enters as an initial state S_T/2 in each direction): with a readout lag
+Disjoint-region readout ("Methodology in Plain English": each scan sees its own
+non-overlapping part of the video, so adding the readouts counts no frame
+twice, and the text's state starts each direction at half weight, S_T/2): with a readout lag
 d >= 0, a token of frame t reads the forward state after frame t - d and the
 reverse state after frame t + d (the initial state where that frame does not
 exist).  d = 0 is the inclusive readout.

@@ -20,7 +20,8 @@ def to_torch(x, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
-def run_gpu(inputs, direction, chunk=0, dv_tile=0, state_in="use", want_state=True, serial=False, erase=True):
+def run_gpu(inputs, direction, chunk=0, dv_tile=0, state_in="use", want_state=True, serial=False, erase=True,
+            exclusive="none"):
     import torch
 
     import gated_delta_rule_scan_amd as gdn
@@ -28,7 +29,8 @@ def run_gpu(inputs, direction, chunk=0, dv_tile=0, state_in="use", want_state=Tr
     d = {k: to_torch(v) for k, v in inputs.items()}
     s_in = d["state_in"] if state_in == "use" else state_in
     out, s_out = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s_in, direction, chunk=chunk,
-                             dv_tile=dv_tile, want_state=want_state, serial=serial, erase=erase)
+                             dv_tile=dv_tile, want_state=want_state, serial=serial, erase=erase,
+                             exclusive=exclusive)
     torch.cuda.synchronize()
     return out.cpu().numpy(), (None if s_out is None else s_out.cpu().numpy())
 
@@ -46,3 +48,18 @@ def check(got, ref, tol, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     assert r <= tol, f"{what}: max abs err {err:.3e} = {r:.3e} x RMS {rms:.3e} > {tol:.1e} x RMS"
     return r
+
+
+def check_scaled(got, ref, tol, scale, what=""):
+    """max |got - ref| <= tol * scale, for outputs whose own RMS is not the
+    scale of the terms they sum (an exclusive readout is the inclusive one
+    with the dominant self term removed, computed by the same products, so
+    its rounding error is set by the inclusive readout's RMS, passed as
+    ``scale``).  Returns the error relative to ``scale``."""
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(np.asarray(got, np.float64) - ref))) if ref.size else 0.0
+    r = err / max(scale, 1e-30)
+    assert r <= tol, f"{what}: max abs err {err:.3e} = {r:.3e} x scale {scale:.3e} > {tol:.1e} x scale"
+    return r
+

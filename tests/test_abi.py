@@ -43,11 +43,12 @@ def test_problem_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "gdn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %d %d\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %d %d %d %d\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
          offsetof(gdn_problem_t, chunk), offsetof(gdn_problem_t, dv_tile), offsetof(gdn_problem_t, options),
          offsetof(gdn_problem_t, workspace),
          offsetof(gdn_problem_t, workspace_bytes), offsetof(gdn_problem_t, stream),
-         offsetof(gdn_problem_t, timing_events), (int)GDN_OPT_SERIAL, (int)GDN_OPT_NO_ERASE);
+         offsetof(gdn_problem_t, timing_events), (int)GDN_OPT_SERIAL, (int)GDN_OPT_NO_ERASE,
+         (int)GDN_OPT_EXCLUSIVE_FORWARD, (int)GDN_OPT_EXCLUSIVE_REVERSE);
   return 0;
 }
 """)
@@ -56,7 +57,8 @@ int main(void) {
     got = [int(x) for x in subprocess.check_output([str(exe)], text=True).split()]
     P = gdn.gdn_problem_t
     want = [ctypes.sizeof(P), P.dtype.offset, P.chunk.offset, P.dv_tile.offset, P.options.offset, P.workspace.offset,
-            P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset, gdn.GDN_OPT_SERIAL, gdn.GDN_OPT_NO_ERASE]
+            P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset, gdn.GDN_OPT_SERIAL, gdn.GDN_OPT_NO_ERASE,
+            gdn.GDN_OPT_EXCLUSIVE_FORWARD, gdn.GDN_OPT_EXCLUSIVE_REVERSE]
     assert got == want
 
 
@@ -170,7 +172,9 @@ def test_overlaps_are_invalid():
 def test_bad_problem_fields():
     p, a = _valid()
     assert _call(p, a, direction=5) == gdn.GDN_ERR_INVALID_ARGUMENT
-    p.options = 4  # undefined option bit
+    p.options = 16  # undefined option bit
+    assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    p.options = -1
     assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
     p, a = _valid(dk=96)
     assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED
@@ -190,6 +194,10 @@ def test_valid_call_without_gpu_reports_launch_failure(direction):
     assert _call(p, a, direction) == gdn.GDN_ERR_HIP
     # state_in == state_out (in-place carry) passes validation too
     assert _call(p, a, direction, s_out=a["s_in"]) == gdn.GDN_ERR_HIP
+    # so does every combination of defined option bits
+    for opts in range(16):
+        p.options = opts
+        assert _call(p, a, direction) == gdn.GDN_ERR_HIP
 
 
 def test_binding_raises_on_missing_library(monkeypatch, tmp_path):

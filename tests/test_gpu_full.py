@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from gdn_testutil import TOL, check, rel_err, to_torch
+from gdn_testutil import TOL, check, check_scaled, rel_err, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -72,5 +72,34 @@ def test_full_size_sampled_heads(name):
     e_o = check(got, ref, TOL[w.dtype], f"{name} out")
     e_s = check(got_s, ref_s, TOL[w.dtype], f"{name} state")
     print(f"[{name}] max|err|/RMS: out {e_o:.3e}  state {e_s:.3e}", flush=True)
+    del d, out, s_out
+    torch.cuda.empty_cache()
+
+
+def test_full_size_bidir480_disjoint_regions():
+    """The 480p bidirectional workload (B2 H16 T32760) with both directions
+    reading before the token's own write, sampled heads against the oracle
+    (output bar: the usual factor times the inclusive readout's RMS)."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+
+    w = synth.WORKLOADS["bidir480"]
+    print(f"\n[bidir480 exclusive] generating {w}", flush=True)
+    x = synth.generate(w)
+    d = {k: to_torch(v) for k, v in x.items()}
+    out, s_out = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction,
+                             exclusive="both")
+    torch.cuda.synchronize()
+    heads = _sample_heads(w)[:2]
+    print(f"[bidir480 exclusive] oracle on heads {heads}", flush=True)
+    ref, ref_s = oracle.forward_heads(x, heads, w.direction, exclusive="both")
+    ref_incl, _ = oracle.forward_heads(x, heads, w.direction)
+    got = np.stack([out[b, :, h].cpu().numpy() for b, h in heads])
+    got_s = np.stack([s_out[:, b, h].cpu().numpy() for b, h in heads], axis=1)
+    # bar: the inclusive readout's RMS (the exclusive output is a remainder of the same products)
+    e_o = check_scaled(got, ref, TOL[w.dtype], float(np.sqrt(np.mean(ref_incl ** 2))), "bidir480 exclusive out")
+    e_s = check(got_s, ref_s, TOL[w.dtype], "bidir480 exclusive state")
+    print(f"[bidir480 exclusive] max|err|/RMS: out {e_o:.3e}  state {e_s:.3e}", flush=True)
     del d, out, s_out
     torch.cuda.empty_cache()

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gdn_testutil import TOL, check, run_gpu
+from gdn_testutil import TOL, check, check_scaled, rel_err, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +110,64 @@ def test_erase_free_variant_concurrent_matches_serial():
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
     ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "fwd", erase=False)
     check(o2, ref, TOL["bf16"], "out erase-free concurrent")
+
+
+@pytest.mark.parametrize("direction,exclusive", [("fwd", "fwd"), ("rev", "rev"), ("bi", "both"), ("bi", "rev"),
+                                                 ("bi", "fwd")])
+@pytest.mark.parametrize("dtype,chunk,la_shift", [("f32", 32, 3.0), ("f32", 64, 3.0), ("bf16", 64, 3.0),
+                                                   ("f32", 64, -2.0), ("bf16", 64, -2.0)])
+def test_exclusive_readout(direction, exclusive, dtype, chunk, la_shift):
+    """GDN_OPT_EXCLUSIVE_*: the chosen directions read before the token's own
+    write (disjoint regions), against the oracle's exclusive mode; final
+    states are those of the inclusive scan, bit for bit.
+
+    The output bar is the usual factor times the RMS of the inclusive readout
+    of the same inputs: with the fast decay of these inputs the token's own
+    write is most of each inclusive output, and the exclusive output, a
+    remainder of the same products, is about ten times smaller than the terms
+    whose rounding it carries.  The slow-decay case has no such gap."""
+    w = _case(dtype, direction, T=203, H=3, dk=64, dv=64, la_shift=la_shift, state_std=0.05, seed=16)
+    x = synth.generate(w)
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction,
+                                exclusive=exclusive)
+    ref_incl, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction)
+    scale = float(np.sqrt(np.mean(ref_incl ** 2)))
+    out, s = run_gpu(x, direction, chunk=chunk, exclusive=exclusive)
+    e1 = check_scaled(out, ref, TOL[dtype], scale, f"out {w} exclusive={exclusive}")
+    if la_shift < 0:  # slow decay: the bar holds against the output's own RMS too
+        check(out, ref, TOL[dtype], f"out {w} exclusive={exclusive} (own RMS)")
+    e2 = check(s, ref_s, TOL[dtype], f"state {w} exclusive={exclusive}")
+    _, s_incl = run_gpu(x, direction, chunk=chunk)
+    assert np.array_equal(s, s_incl)
+    own = rel_err(out, ref)[0]
+    print(f"\nexclusive={exclusive} {dtype} {direction} C={chunk} la_shift={la_shift}: out {e1:.2e} x inclusive RMS "
+          f"({own:.2e} x own RMS {np.sqrt(np.mean(ref ** 2)):.2e} vs inclusive {scale:.2e}) state {e2:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("exclusive", ["both", "rev"])
+def test_exclusive_readout_erase_free_d128(exclusive):
+    """Exclusive readouts with the erase-free variant (brute-force pinned in the oracle), d = 128."""
+    w = _case("bf16", "bi", T=300, B=2, H=2, dk=128, dv=128, state_std=0.02, seed=17)
+    x = synth.generate(w)
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi",
+                                erase=False, exclusive=exclusive)
+    ref_incl, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi",
+                                 erase=False)
+    out, s = run_gpu(x, "bi", erase=False, exclusive=exclusive)
+    check_scaled(out, ref, TOL["bf16"], float(np.sqrt(np.mean(ref_incl ** 2))),
+                 f"out {w} erase-free exclusive={exclusive}")
+    check(s, ref_s, TOL["bf16"], f"state {w} erase-free exclusive={exclusive}")
+
+
+def test_exclusive_readout_concurrent_matches_serial():
+    """41 chunks with both directions exclusive: the concurrent schedule equals the serial one bit for bit."""
+    w = _case("bf16", "bi", T=64 * 40 + 17, H=4, dk=64, dv=64, state_std=0.05, seed=18)
+    x = synth.generate(w)
+    o_ser, s_ser = run_gpu(x, "bi", serial=True, exclusive="both")
+    o_con, s_con = run_gpu(x, "bi", exclusive="both")
+    assert np.array_equal(o_ser, o_con) and np.array_equal(s_ser, s_con)
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi",
+                                exclusive="both")
+    ref_incl, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi")
+    check_scaled(o_con, ref, TOL["bf16"], float(np.sqrt(np.mean(ref_incl ** 2))), f"out {w} exclusive concurrent")
+    check(s_con, ref_s, TOL["bf16"], f"state {w} exclusive concurrent")
