@@ -205,3 +205,24 @@ def test_binding_raises_on_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         gdn.lib()
+
+
+def test_size_limits_are_exact():
+    """The documented limits, checked on both sides: B*H <= 65535, and one
+    batch element's rows, (T + 64) * H * max(dk, dv) * 4 bytes, below 2^32."""
+    ws = lambda B, T, H, d=128, direction="bi": gdn.workspace_bytes(B, T, H, d, d, "bf16", direction)
+    assert ws(3, 5, 21845) > 0            # B*H = 65535
+    assert ws(1, 5, 65536) == 0
+    assert ws(65535, 5, 1) > 0
+    assert ws(2, 5, 32768) == 0
+    t_max = (1 << 32) // (128 * 4) - 64 - 1  # 8,388,543 tokens at H = 1, d = 128
+    assert ws(1, t_max, 1) > 0
+    assert ws(1, t_max + 1, 1) == 0
+    t_max64 = (1 << 32) // (64 * 4) - 64 - 1
+    assert gdn.workspace_bytes(1, t_max64, 1, 64, 64, "f32", "fwd") > 0
+    assert gdn.workspace_bytes(1, t_max64 + 1, 1, 64, 64, "f32", "fwd") == 0
+    # the same limits through gdn_forward (no GPU needed: rejected before any launch)
+    p, a = _valid(T=t_max + 1, H=1, dk=128, dv=128)
+    assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED
+    p, a = _valid(B=1, H=65536)
+    assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED

@@ -438,3 +438,34 @@ def test_exclusive_text_state_enters_once():
     S = x["state_in"][:, 0].astype(np.float64)                 # [dirs, H, dv, dk]
     ref = np.einsum("dh,dhvk,hk->hv", a, S, qh[3])
     np.testing.assert_allclose(o[0, 0], ref, rtol=0, atol=1e-13)
+
+
+def test_reset_gate_makes_windows_independent():
+    """log_alpha = -1000 gives a = 0 exactly, so a direction's memory restarts at that
+    token: with a forward reset at a window's first token and a reverse reset at its
+    last, the bidirectional outputs of the window equal a run on the window alone
+    (the method the longest-sequence GPU test relies on)."""
+    x = _rand_problem(26, T=400, H=2, dk=16, dv=12, direction="bi")
+    la = x["log_alpha"].copy()
+    W, m, T = 40, 181, 400
+    la[1, :, W - 1] = -1000.0
+    la[0, :, m] = -1000.0
+    la[1, :, m + W - 1] = -1000.0
+    la[0, :, T - W] = -1000.0
+    q, k, v, bt, s0 = x["q"], x["k"], x["v"], x["beta"], x["state_in"]
+    o, s = oracle.forward(q, k, v, la, bt, s0, "bi")
+    zero = np.zeros_like(s0[:1])
+    for t0, t1, st in ((0, W, np.concatenate([s0[:1], zero])), (m, m + W, None),
+                       (T - W, T, np.concatenate([zero, s0[1:]]))):
+        sl = slice(t0, t1)
+        ow, sw = oracle.forward(q[:, sl], k[:, sl], v[:, sl], la[:, :, sl], bt[:, :, sl], st, "bi")
+        np.testing.assert_allclose(o[:, sl], ow, rtol=0, atol=1e-13)
+        if t0 == 0:
+            np.testing.assert_allclose(s[1], sw[1], rtol=0, atol=1e-13)
+        if t1 == T:
+            np.testing.assert_allclose(s[0], sw[0], rtol=0, atol=1e-13)
+    # without the resets the windows do depend on the rest
+    o2, _ = oracle.forward(q, k, v, x["log_alpha"], bt, s0, "bi")
+    ow, _ = oracle.forward(q[:, m:m + W], k[:, m:m + W], v[:, m:m + W], x["log_alpha"][:, :, m:m + W],
+                           bt[:, :, m:m + W], None, "bi")
+    assert np.abs(o2[:, m:m + W] - ow).max() > 1e-6
