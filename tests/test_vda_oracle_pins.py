@@ -288,3 +288,39 @@ def test_epilogue_gate_and_weights():
     sel, _ = vda.forward(*args, gate=np.full_like(z, 60.0), norm_weight=one_hot, norm_eps=1e-6)
     assert np.allclose(sel[..., 5], 3.0 * open_[..., 5], rtol=1e-12, atol=0)
     assert np.all(np.delete(sel, 5, axis=-1) == 0)
+
+
+def test_reset_gate_makes_frame_windows_independent():
+    """A per-frame log-gate of -1000 gives a = 0 exactly: S_t = B_t (I + A_t)^-1
+    whatever came before.  With a forward reset at a window's first frame and a
+    reverse reset at its last, the window's outputs equal a run on it alone
+    (the method of the longest-sequence GPU test of the frame-wise operator)."""
+    frame, n = 20, 3
+    x = _inputs(T=215, frame=frame, direction="bi", shift=3.0)
+    la = x["log_alpha"].copy()
+    NF = la.shape[2]
+    fm = 5
+    la[1, :, n - 1] = -1000.0
+    la[0, :, fm] = -1000.0
+    la[1, :, fm + n - 1] = -1000.0
+    la[0, :, NF - n] = -1000.0
+    q, k, v, bt, s0 = x["q"], x["k"], x["v"], x["beta"], x["state_in"]
+    T = q.shape[1]
+    o, s = vda.forward(q, k, v, la, bt, s0, "bi", frame)
+    zero = np.zeros_like(s0[:1])
+    for f0, f1, st in ((0, n, np.concatenate([s0[:1], zero])), (fm, fm + n, None),
+                       (NF - n, NF, np.concatenate([zero, s0[1:]]))):
+        t0, t1 = f0 * frame, min(T, f1 * frame)
+        sl = slice(t0, t1)
+        ow, sw = vda.forward(q[:, sl], k[:, sl], v[:, sl], la[:, :, f0:f1], bt[:, :, sl], st, "bi", frame)
+        np.testing.assert_allclose(o[:, sl], ow, rtol=0, atol=1e-12)
+        if f0 == 0:
+            np.testing.assert_allclose(s[1], sw[1], rtol=0, atol=1e-12)
+        if f1 == NF:
+            np.testing.assert_allclose(s[0], sw[0], rtol=0, atol=1e-12)
+    # without the resets a window depends on the rest
+    o2, _ = vda.forward(q, k, v, x["log_alpha"], bt, s0, "bi", frame)
+    t0, t1 = fm * frame, (fm + n) * frame
+    ow, _ = vda.forward(q[:, t0:t1], k[:, t0:t1], v[:, t0:t1], x["log_alpha"][:, :, fm:fm + n], bt[:, :, t0:t1],
+                        None, "bi", frame)
+    assert np.abs(o2[:, t0:t1] - ow).max() > 1e-6
