@@ -125,10 +125,11 @@ class HipEvents:
             self.hip.hipEventDestroy(self.arr[i])
 
 
-def cpu_baseline(w, x, target_s: float) -> dict:
+def cpu_baseline(w, x, target_s: float, erase: bool = True, exclusive: str = "none") -> dict:
     """Time the double-precision oracle on the host on a bounded sample of the
     workload: every (batch, head) chain if that fits about `target_s` seconds,
-    else the first tokens of every chain."""
+    else the first tokens of every chain.  `erase` and `exclusive` select the
+    same operator the GPU leg runs."""
     import oracle
 
     threads = min(16, len(os.sched_getaffinity(0)))
@@ -146,7 +147,7 @@ def cpu_baseline(w, x, target_s: float) -> dict:
     xs = {"q": x["q"][:, :Ts], "k": x["k"][:, :Ts], "v": x["v"][:, :Ts],
           "log_alpha": x["log_alpha"][:, :, :Ts], "beta": x["beta"][:, :, :Ts], "state_in": x["state_in"]}
     t0 = time.perf_counter()
-    oracle.forward_heads(xs, heads, w.direction, nthreads=threads)
+    oracle.forward_heads(xs, heads, w.direction, nthreads=threads, erase=erase, exclusive=exclusive)
     dt = time.perf_counter() - t0
     thd = n_chains * Ts / dt                                # token-head-directions per second
     used = min(threads, n_chains)
@@ -419,7 +420,7 @@ def main() -> int:
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, erase=not args.no_erase, exclusive=args.exclusive)
         res["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]
     print(json.dumps(res), flush=True)
     return 0

@@ -110,7 +110,8 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", era
     return out, s_out
 
 
-def forward_heads(inputs: dict, heads, direction: str, nthreads: Optional[int] = None, exclusive: str = "none"):
+def forward_heads(inputs: dict, heads, direction: str, nthreads: Optional[int] = None, exclusive: str = "none",
+                  erase: bool = True):
     """Oracle on a subset of (batch, head) chains of a full-size input set.
 
     ``heads`` is a list of (b, h) pairs.  Chains are independent, so this is
@@ -126,5 +127,5 @@ def forward_heads(inputs: dict, heads, direction: str, nthreads: Optional[int] =
     las = np.stack([la[:, b, :, h] for b, h in heads], axis=1)[..., None]
     bts = np.stack([bt[:, b, :, h] for b, h in heads], axis=1)[..., None]
     ss = None if s_in is None else np.stack([s_in[:, b, h] for b, h in heads], axis=1)[:, :, None]
-    out, s_out = forward(qs, ks, vs, las, bts, ss, direction, nthreads=nthreads, exclusive=exclusive)
+    out, s_out = forward(qs, ks, vs, las, bts, ss, direction, erase=erase, nthreads=nthreads, exclusive=exclusive)
     return out[:, :, 0, :], (None if s_out is None else s_out[:, :, 0])
