@@ -37,6 +37,7 @@ GDN_OPT_SERIAL = 1
 GDN_OPT_NO_ERASE = 2
 GDN_OPT_EXCLUSIVE_FORWARD = 4
 GDN_OPT_EXCLUSIVE_REVERSE = 8
+GDN_OPT_TEST_NO_PREPARATION = 1 << 16  # testing only (see include/gdn.h)
 # which directions read their memory before the token's own write
 EXCLUSIVE = {"none": 0, "fwd": GDN_OPT_EXCLUSIVE_FORWARD, "rev": GDN_OPT_EXCLUSIVE_REVERSE,
              "both": GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE}

@@ -62,8 +62,11 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   if (!p) return GDN_ERR_INVALID_ARGUMENT;
   if (direction < GDN_DIR_FORWARD || direction > GDN_DIR_BIDIRECTIONAL) return GDN_ERR_INVALID_ARGUMENT;
   if (p->B < 1 || p->H < 1 || p->T < 0 || p->dk < 1 || p->dv < 1) return GDN_ERR_INVALID_ARGUMENT;
-  if ((p->options & ~(GDN_OPT_SERIAL | GDN_OPT_NO_ERASE | GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE)) != 0)
+  if ((p->options & ~(GDN_OPT_SERIAL | GDN_OPT_NO_ERASE | GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE |
+                      GDN_OPT_TEST_NO_PREPARATION)) != 0)
     return GDN_ERR_INVALID_ARGUMENT;
+  // the test option needs the ready-flag path, which the serial order does not take
+  if ((p->options & GDN_OPT_TEST_NO_PREPARATION) && (p->options & GDN_OPT_SERIAL)) return GDN_ERR_INVALID_ARGUMENT;
   if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
   if (!supported_dim(p->dk) || !supported_dim(p->dv)) return GDN_ERR_UNSUPPORTED;
   if (p->B * p->H > 65535) return GDN_ERR_UNSUPPORTED;  // grid limit of the preparation kernel
@@ -263,6 +266,15 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   hipEvent_t* ev = static_cast<hipEvent_t*>(p->timing_events);
   auto mark = [&](int i, hipStream_t st) { return !ev || hipEventRecord(ev[i], st) == hipSuccess; };
 
+  const bool skip_prep = (p->options & GDN_OPT_TEST_NO_PREPARATION) != 0;
+  if (skip_prep && pl.NC > 0) {
+    // flags marked pending and never cleared: the chain's bounded waits expire
+    a.ready = reinterpret_cast<unsigned*>(ws + pl.ws.rdy);
+    if (launch_clear_ready(a.ready, B * H * pl.NC, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (!mark(0, stream) || !mark(1, stream) || !mark(2, stream)) return GDN_ERR_HIP;
+    if (cf(a, rev_single, stream, nullptr) != hipSuccess || !mark(3, stream)) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   const bool concurrent = pl.NC > 0 && !(p->options & GDN_OPT_SERIAL) &&
                           may_overlap(pf, cf, chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
   if (concurrent) {

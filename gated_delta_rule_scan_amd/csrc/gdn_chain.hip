@@ -190,7 +190,9 @@ __device__ __forceinline__ uint32_t bload4_fresh(rsrc_t r, uint32_t off) {
 
 // Bound on the polls for one chunk's ready flag (about 0.1 s); a workgroup
 // that ever exhausts it stops waiting for the rest of the launch, so a launch
-// always ends.
+// always ends, and sets its state to NaN: every later output of its chain and
+// its final state are then NaN (the canonical quiet NaN, never the "not
+// written yet" pattern), so a starved preparation pass cannot pass unnoticed.
 constexpr int kReadyPollLimit = 1 << 16;
 
 // Waves per state-chain workgroup.  Four: one per SIMD.  (Eight waves with
@@ -472,6 +474,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           }
         }
         if (add) acc += sp.pq[j];
+        if (rdy_gave_up) acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
         bstore16(rs, oo + ct * 64, acc);
       }
     }
@@ -499,6 +502,10 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
       }
     }
     ensure_ready(nx.rdy, cn);  // before any read of chunk cn's prepared operands
+    if (rdy_gave_up) {
+#pragma unroll
+      for (int j = 0; j < SUPW; ++j) Sacc[j] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
     load_coop(nx, cn);
     load_rows(nx.kf, rk, cn);
     readout(nx, s - 1, s > 0);  // the previous step's chunk (nx still holds its stage)

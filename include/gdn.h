@@ -114,7 +114,13 @@ typedef enum {
                                of the sequence, and the prompt's state enters each
                                direction at half weight, S_T / 2 -- here the caller's
                                state_in).
-                               Final states are unchanged by either bit. */
+                               Final states are unchanged by either bit. */,
+  GDN_OPT_TEST_NO_PREPARATION = 1 << 16  /* testing only: the chunk preparation pass is not
+                               launched, so the state chain waits on ready flags that never
+                               clear; its bounded waits expire (about 0.1 s) and every
+                               output and final state is NaN.  This exercises the behaviour
+                               under a preparation pass starved of the GPU: results that
+                               cannot be trusted are NaN, never silently wrong. */
 } gdn_option_t;
 
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};

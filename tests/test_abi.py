@@ -43,12 +43,12 @@ def test_problem_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "gdn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %d %d %d %d\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %d %d %d %d %d\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
          offsetof(gdn_problem_t, chunk), offsetof(gdn_problem_t, dv_tile), offsetof(gdn_problem_t, options),
          offsetof(gdn_problem_t, workspace),
          offsetof(gdn_problem_t, workspace_bytes), offsetof(gdn_problem_t, stream),
          offsetof(gdn_problem_t, timing_events), (int)GDN_OPT_SERIAL, (int)GDN_OPT_NO_ERASE,
-         (int)GDN_OPT_EXCLUSIVE_FORWARD, (int)GDN_OPT_EXCLUSIVE_REVERSE);
+         (int)GDN_OPT_EXCLUSIVE_FORWARD, (int)GDN_OPT_EXCLUSIVE_REVERSE, (int)GDN_OPT_TEST_NO_PREPARATION);
   return 0;
 }
 """)
@@ -58,7 +58,7 @@ int main(void) {
     P = gdn.gdn_problem_t
     want = [ctypes.sizeof(P), P.dtype.offset, P.chunk.offset, P.dv_tile.offset, P.options.offset, P.workspace.offset,
             P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset, gdn.GDN_OPT_SERIAL, gdn.GDN_OPT_NO_ERASE,
-            gdn.GDN_OPT_EXCLUSIVE_FORWARD, gdn.GDN_OPT_EXCLUSIVE_REVERSE]
+            gdn.GDN_OPT_EXCLUSIVE_FORWARD, gdn.GDN_OPT_EXCLUSIVE_REVERSE, gdn.GDN_OPT_TEST_NO_PREPARATION]
     assert got == want
 
 
@@ -176,6 +176,11 @@ def test_bad_problem_fields():
     assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
     p.options = -1
     assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    p.options = 1 << 17
+    assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    # the test option needs the ready-flag path, which the serial order does not take
+    p.options = gdn.GDN_OPT_TEST_NO_PREPARATION | gdn.GDN_OPT_SERIAL
+    assert _call(p, a) == gdn.GDN_ERR_INVALID_ARGUMENT
     p, a = _valid(dk=96)
     assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED
     p, a = _valid(chunk=48)
@@ -198,6 +203,8 @@ def test_valid_call_without_gpu_reports_launch_failure(direction):
     for opts in range(16):
         p.options = opts
         assert _call(p, a, direction) == gdn.GDN_ERR_HIP
+    p.options = gdn.GDN_OPT_TEST_NO_PREPARATION
+    assert _call(p, a, direction) == gdn.GDN_ERR_HIP
 
 
 def test_binding_raises_on_missing_library(monkeypatch, tmp_path):

@@ -8,7 +8,9 @@
   allocation with 4 KiB guard zones of a known byte pattern on both sides; the
   zones must be intact after the call (no access writes out of bounds);
 * a streaming rollout (several calls, the state carried in place) captured as
-  one HIP graph and replayed, equal to the eager rollout.
+  one HIP graph and replayed, equal to the eager rollout;
+* a starved preparation pass (forced from the host with a test-only option):
+  the state chain's bounded waits expire and every result is NaN.
 """
 import numpy as np
 import pytest
@@ -192,3 +194,40 @@ def test_streaming_rollout_graph():
         torch.cuda.synchronize()
         for a, b in zip([o for o in outs] + [state], ref):
             assert torch.equal(a, b), f"replay {rep}"
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bi"])
+def test_starved_preparation_gives_nan_not_wrong_results(direction):
+    """GDN_OPT_TEST_NO_PREPARATION: the chunk preparation pass is not launched,
+    so the state chain's ready flags never clear.  Its bounded waits expire
+    and every output and final state is the canonical NaN (not the "not
+    written yet" pattern), instead of results computed from a stale
+    workspace.  A normal call afterwards is unaffected."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    import oracle
+    from gdn_testutil import TOL, check
+
+    w = synth.Workload("starved", 1, 2, 64 * 20 + 5, 64, 64, "bf16", direction, 3.0, 0.05, 41)
+    x = synth.generate(w)
+    d = {k: to_torch(v) for k, v in x.items()}
+    out = torch.zeros((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    s_out = torch.zeros((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+    dirn = gdn.DIRECTIONS[direction]
+    prob = gdn.make_problem(w.B, w.T, w.H, w.dk, w.dv, gdn.GDN_DTYPE_BF16)
+    ws = torch.empty(gdn.gdn_workspace_bytes(prob, dirn), dtype=torch.uint8, device="cuda")
+    prob.workspace, prob.workspace_bytes = ws.data_ptr(), ws.numel()
+    prob.stream = torch.cuda.current_stream().cuda_stream
+    prob.options = gdn.GDN_OPT_TEST_NO_PREPARATION
+    st = gdn.gdn_forward(prob, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["log_alpha"].data_ptr(),
+                         d["beta"].data_ptr(), d["state_in"].data_ptr(), s_out.data_ptr(), out.data_ptr(), dirn)
+    assert st == gdn.GDN_OK
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out).all()) and bool(torch.isnan(s_out).all())
+    assert bool((out.view(torch.int32) != -1).all())  # never the all-ones fill pattern
+    o2, s2 = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], direction, workspace=ws)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction)
+    check(o2.cpu().numpy(), ref, TOL["bf16"], "out after the starved call")
+    check(s2.cpu().numpy(), ref_s, TOL["bf16"], "state after the starved call")
