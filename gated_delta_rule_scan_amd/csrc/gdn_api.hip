@@ -161,7 +161,11 @@ bool may_overlap(prep_fn pf, chain_fn cf, int64_t chain_wgs, int64_t NC) {
       hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
     return false;
   auto granule = [](int r) { return (r + 7) / 8 * 8; };  // registers are allocated in blocks of 8
-  return granule(ap.numRegs) + granule(ac.numRegs) <= 512 && ap.sharedSizeBytes + ac.sharedSizeBytes <= (size_t)lds;
+  // per SIMD lane: one preparation wave beside the chain workgroup's waves on
+  // that SIMD (its block size spread over the four SIMDs)
+  const int chain_waves_per_simd = (ac.maxThreadsPerBlock + 255) / 256;
+  return granule(ap.numRegs) + chain_waves_per_simd * granule(ac.numRegs) <= 512 &&
+         ap.sharedSizeBytes + ac.sharedSizeBytes <= (size_t)lds;
 }
 
 template <typename MT>

@@ -41,8 +41,14 @@
 // branches, and an access that must not happen this step (the partial of a
 // first visit, the store of a step that has nothing to store) goes through a
 // resource with an empty extent.  All loads of a step are issued by every wave
-// unconditionally, a step ahead of their use, so no prefetch ever forces a
-// wait on the in-order memory counter.
+// of a role unconditionally, a step ahead of their use, so no prefetch ever
+// forces a wait on the in-order memory counter.
+//
+// A workgroup has two roles of four waves each, on the same four SIMDs.  The
+// chain waves carry the state: Y, X, Vnew and the state update, the critical
+// path.  The readout waves compute Z and the chunk outputs beside them, so
+// those leave the critical path; the two roles meet at the step's three
+// barriers (phases below).
 //
 // Workgroups are numbered so that all value tiles of one (batch, head) land
 // on the same XCD (consecutive workgroups are dealt round-robin over the
@@ -89,26 +95,30 @@ struct VTile {
   static constexpr int NVI = (C * LPR + 127) / 128;      // loads per wave (two waves share the tile)
 };
 
-// Raw operands of one chunk, loaded a step ahead of their use.  Every wave
-// loads its own matrix-core fragments (k, q rows of its token tile and the
-// matching rows of the two chunk triangles) and 16 bytes per lane of the
+// Raw operands of one chunk, loaded a step ahead of their use, per role.
+// Chain waves: the k rows of their token tile and the matching rows of the
+// strict inverse triangle (matrix-core fragments), 16 bytes per lane of the
 // group-shared operands (wave 0: scales, wave 1: self-term remainders and
 // chunk decay, waves 2-3: the value tile), which go to LDS at the end of the
-// step.
+// step, and the ready flag of the chunk the stage is loaded with next (read
+// two steps ahead; 0 = ready).
 template <typename MT, int DK, int C, int NT>
-struct Stage {
+struct StageC {
   typedef typename Mma<MT>::frag frag;
   frag kf[DK / 32];
-  frag qf[DK / 32];
   frag tf[C / 32];
-  frag pf[C / 32];
   f32x4 cv[VTile<MT, 16 * NT, C>::NVI];
-  // bidirectional second visit: the other direction's readout of this chunk
-  // (per output tile of the wave), loaded a step ahead like the rest
-  f32x4 pq[(C / 16 * NT + 3) / 4];
-  // ready flag of the chunk this stage is loaded with next (read two steps
-  // ahead; 0 = ready)
   uint32_t rdy;
+};
+// Readout waves: the q rows of their token tile, the matching rows of the
+// decayed q^.k^ triangle, and for a bidirectional second visit the other
+// direction's readout of the chunk (per output tile of the wave).
+template <typename MT, int DK, int C, int NT>
+struct StageR {
+  typedef typename Mma<MT>::frag frag;
+  frag qf[DK / 32];
+  frag pf[C / 32];
+  f32x4 pq[(C / 16 * NT + 3) / 4];
 };
 
 __device__ __forceinline__ bool tri_needed(bool rev, int kc, int rt) {
@@ -190,17 +200,21 @@ __device__ __forceinline__ uint32_t bload4_fresh(rsrc_t r, uint32_t off) {
 
 // Bound on the polls for one chunk's ready flag (about 0.1 s); a workgroup
 // that ever exhausts it stops waiting for the rest of the launch, so a launch
-// always ends, and sets its state to NaN: every later output of its chain and
-// its final state are then NaN (the canonical quiet NaN, never the "not
-// written yet" pattern), so a starved preparation pass cannot pass unnoticed.
+// always ends, and sets its state and pseudo-values to NaN: every later
+// output of its chain and its final state are then NaN (the canonical quiet
+// NaN, never the "not written yet" pattern), so a starved preparation pass
+// cannot pass unnoticed.
 constexpr int kReadyPollLimit = 1 << 16;
 
-// Waves per state-chain workgroup.  Four: one per SIMD.  (Eight waves with
-// one output tile each measured 1.4x slower on MI355X: every wave then reads
-// the whole update operand from LDS, and LDS is what a step waits on.)
+// Waves per state-chain workgroup: four chain waves (one per SIMD), which
+// carry the state, and four readout waves beside them, which compute Z = Q S^T
+// and the chunk outputs (measured on MI355X: the chain 2% faster than with
+// the readout on the chain waves, bitwise the same results).  (Eight waves
+// splitting the chain's own work, one output tile each, measured 1.4x slower:
+// every wave then reads the whole update operand from LDS.)
 template <int C, int NT>
 struct ChainWaves {
-  static constexpr int value = 4;
+  static constexpr int value = 8;
 };
 
 template <typename MT, int DK, int C, int NT, bool BI>
@@ -209,19 +223,19 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   using M = Mma<MT>;
   using frag = typename M::frag;
   using SM = ChainSmem<MT, DK, C, NT>;
-  using F = Stage<MT, DK, C, NT>;
   constexpr int ES = SM::ES;
   constexpr int TP = SM::TP, SP = SM::SP, DT = SM::DT;
   using VT = VTile<MT, DT, C>;
   constexpr int RT = C / 16;              // token row tiles per chunk
-  constexpr int NW = ChainWaves<C, NT>::value;  // waves per workgroup
-  constexpr int UPW = (RT * NT + NW - 1) / NW;  // chunk-output tiles per wave
-  constexpr int SRT = DK / 16;                  // state row tiles (dk)
-  constexpr int SUPW = SRT * NT / NW;           // state tiles per wave
+  constexpr int NWC = 4;                        // chain waves; readout waves follow them
+  constexpr int UPW = (RT * NT + NWC - 1) / NWC;  // chunk-output tiles per wave
+  constexpr int SRT = DK / 16;                    // state row tiles (dk)
+  constexpr int SUPW = SRT * NT / NWC;            // state tiles per chain wave
   constexpr bool SPLIT = SM::SPLIT;
-  constexpr bool ALL_UNITS = (RT * NT) % NW == 0;
-  static_assert(SRT % NW == 0 || NW % SRT == 0, "state tiles split evenly over the waves");
-  static_assert(NW % RT == 0, "every wave keeps one token row tile");
+  constexpr bool ALL_UNITS = (RT * NT) % NWC == 0;
+  static_assert(ChainWaves<C, NT>::value == 2 * NWC, "one readout wave per chain wave");
+  static_assert(SRT % NWC == 0 || NWC % SRT == 0, "state tiles split evenly over the waves");
+  static_assert(NWC % RT == 0, "every wave keeps one token row tile");
 
   __shared__ __align__(16) MT smem[SM::per_group];
   __shared__ __align__(16) unsigned char stg[2][SM::ST_BYTES];
@@ -248,7 +262,9 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int cw = w & 3;  // role in the group-shared loads (waves 4-7 repeat 0-3: same data, same place)
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int rt = w % RT;
+  const int wr = w & (NWC - 1);  // place among the chain waves (readout wave w mirrors chain wave w - NWC)
+  const bool reader = w >= NWC;  // readout waves: Z = Q S^T and the chunk outputs
+  const int rt = wr % RT;
 
   constexpr bool KROW = SM::KROW;
   constexpr int KP = SM::KP;
@@ -390,20 +406,22 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) dst[ks] = bload_frag<MT>(r, o + 32 * ks * ES);
   };
-  auto load_coop = [&](F& f, int c) {
+  auto load_coop = [&](auto& f, int c) {
     const uint32_t o = (uint32_t)c * cstride;
 #pragma unroll
     for (int n = 0; n < VT::NVI; ++n) f.cv[n] = bload16(rc, c_off[n] + o);
   };
-  auto load_tri = [&](F& f, int c) {  // every wave issues the same loads
+  auto load_tf = [&](auto& f, int c) {  // chain waves
     const uint32_t o = tri_off + (uint32_t)c * (C * C * ES);
 #pragma unroll
-    for (int kc = 0; kc < C / 32; ++kc) {
-      f.tf[kc] = bload_frag<MT>(rtk[kc], o + 32 * kc * ES);
-      f.pf[kc] = bload_frag<MT>(rpk[kc], o + 32 * kc * ES);
-    }
+    for (int kc = 0; kc < C / 32; ++kc) f.tf[kc] = bload_frag<MT>(rtk[kc], o + 32 * kc * ES);
   };
-  auto stash = [&](const F& f, int buf) {  // group-shared pieces of a loaded stage -> LDS
+  auto load_pf = [&](auto& f, int c) {  // readout waves
+    const uint32_t o = tri_off + (uint32_t)c * (C * C * ES);
+#pragma unroll
+    for (int kc = 0; kc < C / 32; ++kc) f.pf[kc] = bload_frag<MT>(rpk[kc], o + 32 * kc * ES);
+  };
+  auto stash = [&](const auto& f, int buf) {  // group-shared pieces of a loaded stage -> LDS
 #pragma unroll
     for (int n = 0; n < VT::NVI; ++n) *reinterpret_cast<f32x4*>(&stg[buf][c_lds[n]]) = f.cv[n];
   };
@@ -413,11 +431,11 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   const size_t sbase = (((size_t)slot * a.B + b) * a.H + h) * (size_t)dv * DK;
 #pragma unroll
   for (int j = 0; j < SUPW; ++j) {
-    const int u = w + NW * j;
+    const int u = wr + NWC * j;
     const int srt = u % SRT, sct = u / SRT;
     const size_t off = sbase + (size_t)(dv0 + 16 * sct + l16) * DK + 16 * srt + 4 * g4;
-    Sacc[j] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + off) : f32x4{0.f, 0.f, 0.f, 0.f};
-    M::store4(Sb + (16 * sct + l16) * SP + 16 * srt + 4 * g4, Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
+    Sacc[j] = a.state_in && !reader ? *reinterpret_cast<const f32x4*>(a.state_in + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!reader) M::store4(Sb + (16 * sct + l16) * SP + 16 * srt + 4 * g4, Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
   }
 
   auto chunk_at = [&](int s) { return rev ? NC - 1 - s : s; };
@@ -428,20 +446,18 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     return !BI || s < so || (s == so && !rev);
   };
 
-  // Readout of step sp (chunk chunk_at(sp)): O = (e^g rq) Z + P Vnew.  It is
-  // software-pipelined one phase late: computed at the start of the next
-  // step, where its products and stores overlap that step's state products.
-  // Everything it reads is still intact there: Z (registers), the P fragments
-  // (the stage the next step's triangle loads overwrite only in its last
-  // phase), Vnew (LDS until the next step's second phase) and the staged
-  // scales (until the next step's last phase).  `on` = false: nothing is stored.
-  // Second visits of a bidirectional scan add the partial the other
-  // direction stored (the stage's pq, loaded a step ahead and checked at the
-  // end of the visit step).
+  // Readout of step sp (chunk chunk_at(sp)) by the readout waves, in the
+  // step's last phase: O = (e^g rq) Z + P Vnew.  Everything it reads is
+  // intact there: Z (registers, from the step's first phase), the P fragments
+  // (the wave's own stage), Vnew (LDS until the next step's second phase) and
+  // the staged scales (until the next step's last phase).  `on` = false:
+  // nothing is stored.  Second visits of a bidirectional scan add the partial
+  // the other direction stored (the stage's pq, loaded a step ahead and
+  // checked just before).
   f32x4 Zp[UPW];
 #pragma unroll
   for (int j = 0; j < UPW; ++j) Zp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto readout = [&](const F& sp, const int s_prev, const bool on) {
+  auto readout = [&](const auto& sp, const int s_prev, const bool on) {
     const unsigned char* sg = stg[s_prev & 1];
     frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
     if constexpr (SPLIT) {
@@ -456,7 +472,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     const bool add = BI && !first_visit(s_prev);
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
-      const int u = w + NW * j;
+      const int u = wr + NWC * j;
       if (ALL_UNITS || u < RT * NT) {
         const int ct = u / RT;
         f32x4 acc = Zp[j] * zs;
@@ -474,22 +490,35 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           }
         }
         if (add) acc += sp.pq[j];
-        if (rdy_gave_up) acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
         bstore16(rs, oo + ct * 64, acc);
       }
     }
   };
 
-  auto step = [&](F& st, F& nx, const int s, const int cn) {
-    const int c = chunk_at(s);
+  // One step (chunk c = chunk_at(s); nx is loaded with chunk cn for the
+  // next step), one lambda per role with the same three barriers.  Chain
+  // waves (w < NWC) carry the state; readout waves compute Z = Q S^T and the
+  // chunk outputs beside them, on the same SIMDs, so the chain waves'
+  // critical path holds only Y, X, Vnew and the state update.
+  //   phase A  chain: k tile -> LDS, Y = K S^T, X -> LDS
+  //            readout: Z = Q S^T (the state copy is stable until phase C)
+  //   phase B  chain: Vnew = X + strict(T) X -> LDS
+  //            readout: next P fragments and partial (after phase A's wait on
+  //            the ready flag of chunk cn)
+  //   phase C  chain: state update, state copy and next scales -> LDS
+  //            readout: O = (e^g rq) Z + P Vnew (Vnew intact until the next phase B)
+  using FC = StageC<MT, DK, C, NT>;
+  using FR = StageR<MT, DK, C, NT>;
+  auto step_chain = [&](FC& st, FC& nx, const int s, const int cn) {
     const int buf = s & 1;
     const unsigned char* sg = stg[buf];
+    f32x4 X[UPW];
     float4 sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = *reinterpret_cast<const float4*>(sg + SM::ST_SC + (o_row0 + i) * 16);
 
-    // [A] k tile into LDS; Y = K S^T, Z = Q S^T; X
-    if (w < RT) {
+    // [A] k tile into LDS; Y = K S^T; X
+    if (wr < RT) {
       if constexpr (KROW) {
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
@@ -502,26 +531,21 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
       }
     }
     ensure_ready(nx.rdy, cn);  // before any read of chunk cn's prepared operands
-    if (rdy_gave_up) {
+    const bool poison = rdy_gave_up;  // see kReadyPollLimit
+    if (poison) {
 #pragma unroll
       for (int j = 0; j < SUPW; ++j) Sacc[j] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     }
     load_coop(nx, cn);
     load_rows(nx.kf, rk, cn);
-    readout(nx, s - 1, s > 0);  // the previous step's chunk (nx still holds its stage)
-    f32x4 X[UPW], Vn[UPW];
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
-      const int u = w + NW * j;
+      const int u = wr + NWC * j;
       if (ALL_UNITS || u < RT * NT) {
         const int ct = u / RT;
-        f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-          const frag sb = M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4);
-          y = M::mma(st.kf[ks], sb, y);
-          z = M::mma(sb, st.qf[ks], z);  // Z^T: lane (l16, g4) holds Z[token 16 rt + l16][16 ct + 4 g4 + i]
-        }
+        for (int ks = 0; ks < DK / 32; ++ks) y = M::mma(st.kf[ks], M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4), y);
         // raw values v[o_row0 + i][16 ct + l16], i = 0..3
         f32x4 vv;
         if constexpr (KROW) {
@@ -537,36 +561,23 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[j][i] = sc[i].x * (vv[i] - sc[i].y * y[i]);
-        Zp[j] = z;
+        if (poison) X[j] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
         M::store4(XT + (16 * ct + l16) * TP + o_row0, X[j][0], X[j][1], X[j][2], X[j][3]);
       }
     }
     __syncthreads();
 
-    // [B] Vnew = X + strict(Tinv) X
-    load_rows(nx.qf, rq, cn);
+    // [B] Vnew = X + strict(Tinv) X, and its scaled copy for the state update
     nx.rdy = ready_flag(chunk_at(min(s + 3, NC - 1)));  // what nx is loaded with two steps on
-    // bidirectional second visit of the next step's chunk: the other
-    // direction's partial, loaded a step ahead (after this step's readout has
-    // read nx's previous contents), checked at the end of the next step and
-    // consumed by its readout
-    if constexpr (BI) {
-      const bool want = s + 1 < NC && !first_visit(s + 1);
-      const rsrc_t rp = want ? ro : rnone;
-      const uint32_t op = out_off + out_at(cn);
-#pragma unroll
-      for (int j = 0; j < UPW; ++j) nx.pq[j] = bload16(rp, op + ((w + NW * j) / RT) * 64);
-    }
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
-      const int u = w + NW * j;
+      const int u = wr + NWC * j;
       if (ALL_UNITS || u < RT * NT) {
         const int ct = u / RT;
         f32x4 acc = X[j];
 #pragma unroll
         for (int kc = 0; kc < C / 32; ++kc)
           acc = M::mma(tmask[kc].apply(st.tf[kc]), M::load(XT + (16 * ct + l16) * TP + 32 * kc + 8 * g4), acc);
-        Vn[j] = acc;
         const int o = (16 * ct + l16) * TP + o_row0;
         f32x4 vs;
 #pragma unroll
@@ -582,19 +593,18 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     }
     __syncthreads();
 
-    // [C] state update (the readout of this chunk follows in the next step)
-    load_tri(nx, cn);
-    const float gn = *reinterpret_cast<const float*>(sg + SM::ST_GN);
-    // state update S^T = gn S^T + K^T Vs.  Wave w owns the state tiles
-    // u = w + NW j, i.e. dk tiles srt(js) and dv tiles sct(jt) below; every
-    // operand fragment is read once (the products only start after all
+    // [C] state update S^T = gn S^T + K^T Vs.  Chain wave wr owns the state
+    // tiles u = wr + NWC j, i.e. dk tiles srt(js) and dv tiles sct(jt) below;
+    // every operand fragment is read once (the products only start after all
     // reads, so no LDS store in between forces a re-read), then the operand
     // copy for the next step is written.
+    load_tf(nx, cn);
+    const float gn = *reinterpret_cast<const float*>(sg + SM::ST_GN);
     {
-      constexpr int JS = SRT >= NW ? SRT / NW : 1;  // dk tiles per wave
-      constexpr int JT = SUPW / JS;                 // dv tiles per wave
-      auto srt_of = [&](int js) { return (w % SRT) + NW * js; };
-      auto sct_of = [&](int jt) { return SRT >= NW ? jt : w / SRT + (NW / SRT) * jt; };
+      constexpr int JS = SRT >= NWC ? SRT / NWC : 1;  // dk tiles per wave
+      constexpr int JT = SUPW / JS;                   // dv tiles per wave
+      auto srt_of = [&](int js) { return (wr % SRT) + NWC * js; };
+      auto sct_of = [&](int jt) { return SRT >= NWC ? jt : wr / SRT + (NWC / SRT) * jt; };
       frag ka[JS][C / 32], vh[JT][C / 32], vl[JT][C / 32];
 #pragma unroll
       for (int js = 0; js < JS; ++js)
@@ -619,7 +629,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
         for (int js = 0; js < JS; ++js) {
-          const int j = jt * JS + js;  // tile u = w + NW j: srt = u % SRT = srt_of(js), sct = u / SRT = sct_of(jt)
+          const int j = jt * JS + js;  // tile u = wr + NWC j: srt = u % SRT = srt_of(js), sct = u / SRT = sct_of(jt)
           f32x4 acc = Sacc[j] * gn;
 #pragma unroll
           for (int kc = 0; kc < C / 32; ++kc) {
@@ -634,9 +644,47 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         M::store4(Sb + (16 * sct + l16) * SP + 16 * srt + 4 * g4, Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
       }
     }
-    // bidirectional second visit: this step's partial was loaded a step ago;
-    // while any of it still holds the fill pattern, the other direction has
-    // not stored it yet -- re-read it past the L1 cache
+    stash(nx, buf ^ 1);  // next step's group-shared operands (its slot was last read one step ago)
+    __syncthreads();
+  };
+
+  auto step_read = [&](FR& st, FR& nx, const int s, const int cn) {
+    const int c = chunk_at(s);
+
+    // [A] Z^T = S Q^T for this step's outputs (lane (l16, g4) holds
+    // Z[token 16 rt + l16][16 ct + 4 g4 + i]); the state copy is stable
+    // until the chain waves' phase C
+    load_rows(nx.qf, rq, cn);  // raw q of the next chunk
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+      const int u = wr + NWC * j;
+      if (ALL_UNITS || u < RT * NT) {
+        const int ct = u / RT;
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+          z = M::mma(M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4), st.qf[ks], z);
+        Zp[j] = z;
+      }
+    }
+    __syncthreads();
+
+    // [B] the next chunk's P fragments (prepared: the chain waves waited for
+    // its ready flag in phase A) and, for a bidirectional second visit, the
+    // other direction's partial, loaded a step ahead
+    load_pf(nx, cn);
+    if constexpr (BI) {
+      const bool want = s + 1 < NC && !first_visit(s + 1);
+      const rsrc_t rp = want ? ro : rnone;
+      const uint32_t op = out_off + out_at(cn);
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) nx.pq[j] = bload16(rp, op + ((wr + NWC * j) / RT) * 64);
+    }
+    __syncthreads();
+
+    // [C] bidirectional second visit: while any of the partial still holds
+    // the fill pattern, the other direction has not stored it yet -- re-read
+    // it past the L1 cache; then this chunk's outputs
     if constexpr (BI) {
       if (!first_visit(s)) {
 #pragma unroll
@@ -644,7 +692,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           // first test outside any loop: a loop that reloads the tested value
           // makes the compiler wait for every load in flight at its head
           if (__any(any_unwritten(st.pq[j]))) {
-            const uint32_t off = out_off + out_at(c) + ((w + NW * j) / RT) * 64;
+            const uint32_t off = out_off + out_at(c) + ((wr + NWC * j) / RT) * 64;
             f32x4 q = st.pq[j];
             for (int n = 0; n < kPollLimit; ++n) {
               __builtin_amdgcn_s_sleep(2);
@@ -656,46 +704,57 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         }
       }
     }
-    stash(nx, buf ^ 1);  // next step's group-shared operands (its slot was last read one step ago)
+    readout(st, s, true);
     __syncthreads();
   };
 
   // two operand stages in ping-pong: the loads for step s+1 are in flight
   // while step s computes (past the last step a valid chunk is reloaded)
-  F sA, sB;
   if (NC > 0) {
     const int c0 = chunk_at(0);
-    ensure_ready(ready_flag(c0), c0);
-    // steps 0 and 1 load chunks 1 and 2 into sB and sA.  These flag loads come
-    // first: the loop's first wait for them must find the operand loads below
-    // issued after them, as every later iteration does
-    sB.rdy = ready_flag(chunk_at(min(1, NC - 1)));
-    sA.rdy = ready_flag(chunk_at(min(2, NC - 1)));
-    load_coop(sA, c0);
-    load_rows(sA.kf, rk, c0);
-    load_rows(sA.qf, rq, c0);
-    load_tri(sA, c0);
-    if constexpr (BI) {  // the partial of step 0 (a single-chunk scan's reverse visit)
-      const rsrc_t rp = first_visit(0) ? rnone : ro;
+    if (!reader) {
+      FC sA, sB;
+      ensure_ready(ready_flag(c0), c0);
+      // steps 0 and 1 load chunks 1 and 2 into sB and sA.  These flag loads come
+      // first: the loop's first wait for them must find the operand loads below
+      // issued after them, as every later iteration does
+      sB.rdy = ready_flag(chunk_at(min(1, NC - 1)));
+      sA.rdy = ready_flag(chunk_at(min(2, NC - 1)));
+      load_coop(sA, c0);
+      load_rows(sA.kf, rk, c0);
+      load_tf(sA, c0);
+      stash(sA, 0);
+      __syncthreads();
+      int s = 0;
+      for (; s + 1 < NC; s += 2) {
+        step_chain(sA, sB, s, chunk_at(s + 1));
+        step_chain(sB, sA, s + 1, chunk_at(min(s + 2, NC - 1)));
+      }
+      if (s < NC) step_chain(sA, sB, s, chunk_at(s));
+    } else {
+      FR sA, sB;
+      load_rows(sA.qf, rq, c0);
+      __syncthreads();
+      load_pf(sA, c0);  // chunk c0's prepared operands: after the chain waves' wait above
+      if constexpr (BI) {  // the partial of step 0 (a single-chunk scan's reverse visit)
+        const rsrc_t rp = first_visit(0) ? rnone : ro;
 #pragma unroll
-      for (int j = 0; j < UPW; ++j) sA.pq[j] = bload16(rp, out_off + out_at(c0) + ((w + NW * j) / RT) * 64);
+        for (int j = 0; j < UPW; ++j) sA.pq[j] = bload16(rp, out_off + out_at(c0) + ((wr + NWC * j) / RT) * 64);
+      }
+      int s = 0;
+      for (; s + 1 < NC; s += 2) {
+        step_read(sA, sB, s, chunk_at(s + 1));
+        step_read(sB, sA, s + 1, chunk_at(min(s + 2, NC - 1)));
+      }
+      if (s < NC) step_read(sA, sB, s, chunk_at(s));
     }
-    stash(sA, 0);
-    __syncthreads();
-    int s = 0;
-    for (; s + 1 < NC; s += 2) {
-      step(sA, sB, s, chunk_at(s + 1));
-      step(sB, sA, s + 1, chunk_at(min(s + 2, NC - 1)));
-    }
-    if (s < NC) step(sA, sB, s, chunk_at(s));
-    readout((NC & 1) ? sA : sB, NC - 1, true);  // the last chunk's readout (its stage is the last one stepped)
   }
 
   // ---- final state ----
-  if (a.state_out) {
+  if (a.state_out && !reader) {
 #pragma unroll
     for (int j = 0; j < SUPW; ++j) {
-      const int u = w + NW * j;
+      const int u = wr + NWC * j;
       const int srt = u % SRT, sct = u / SRT;
       const size_t off = sbase + (size_t)(dv0 + 16 * sct + l16) * DK + 16 * srt + 4 * g4;
       *reinterpret_cast<f32x4*>(a.state_out + off) = Sacc[j];
