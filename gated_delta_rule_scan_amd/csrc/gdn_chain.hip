@@ -260,7 +260,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int cw = w & 3;  // role in the group-shared loads (waves 4-7 repeat 0-3: same data, same place)
+  const int cw = w & 3;  // chain wave's part of the group-shared loads (0: scales, 1: remainders, 2-3: value tile)
   const int l16 = lane & 15, g4 = lane >> 4;
   const int wr = w & (NWC - 1);  // place among the chain waves (readout wave w mirrors chain wave w - NWC)
   const bool reader = w >= NWC;  // readout waves: Z = Q S^T and the chunk outputs
