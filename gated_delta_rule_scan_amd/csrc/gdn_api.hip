@@ -135,23 +135,23 @@ bool side_stream(int dev, SideStream** out) {
 // Whether the preparation pass runs concurrently with the state chain.
 //
 // Worth it only when the chain leaves compute units free: a latency-bound
-// chain workgroup runs about 30% slower with preparation waves beside it on
-// its SIMDs, which costs more than the preparation pass when every unit
-// holds a chain (measured on MI355X: 480p bidirectional, 256 chain
-// workgroups, 1.60 ms concurrent vs 1.43 ms serial), while with half the
-// units free the pass hides almost entirely (720p causal, 128 chain
-// workgroups: 1.90 vs 2.05 ms).
+// chain workgroup runs slower with preparation waves beside it on its SIMDs,
+// which costs more than the preparation pass when every unit holds a chain
+// (measured on MI355X: 480p bidirectional, 256 chain workgroups, 1.52 ms
+// concurrent vs 1.40 ms serial), while with a quarter of the units free the
+// pass hides (720p bidirectional, 192 chain workgroups: 4.25 vs 4.46 ms; 720p
+// causal, 128: 1.88 vs 2.05 ms).
 //
 // Safe because the chain waits only for chunks the preparation pass
 // publishes, and a preparation workgroup can always be scheduled: the chain
-// workgroups occupy at most half the compute units, and one fits beside a
-// chain workgroup anyway (registers per SIMD lane -- both kernels run one
-// wave per SIMD -- and LDS).  The preparation pass is enqueued first, so a
-// device that runs the two streams one after the other still finishes it
-// before the chain starts.
+// workgroups occupy at most three quarters of the compute units, and one fits
+// beside a chain workgroup anyway (registers per SIMD lane, counting the
+// chain's waves per SIMD, and LDS).  The preparation pass is enqueued first,
+// so a device that runs the two streams one after the other still finishes
+// it before the chain starts.
 bool may_overlap(prep_fn pf, chain_fn cf, int64_t chain_wgs, int64_t NC) {
   constexpr int64_t kMinChunks = 16;  // below this the fork/join costs more than it hides
-  if (NC < kMinChunks || 2 * chain_wgs > compute_units()) return false;
+  if (NC < kMinChunks || 4 * chain_wgs > 3 * (int64_t)compute_units()) return false;
   hipFuncAttributes ap, ac;
   ScanArgs none;
   memset(&none, 0, sizeof(none));
