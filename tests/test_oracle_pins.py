@@ -469,3 +469,23 @@ def test_reset_gate_makes_windows_independent():
     ow, _ = oracle.forward(q[:, m:m + W], k[:, m:m + W], v[:, m:m + W], x["log_alpha"][:, :, m:m + W],
                            bt[:, :, m:m + W], None, "bi")
     assert np.abs(o2[:, m:m + W] - ow).max() > 1e-6
+
+
+def test_hand_worked_example_exclusive_readouts():
+    """The two-token example's exclusive readouts, worked by hand
+    (tests/golden/hand_worked_2token.json, "derivation_exclusive")."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_2token.json")))
+    inp, exp = g["inputs"], g["expected_exclusive"]
+    q = np.array(inp["q"], np.float32)[None, :, None, :]
+    k = np.array(inp["k"], np.float32)[None, :, None, :]
+    v = np.array(inp["v"], np.float32)[None, :, None, :]
+    la = np.log(np.array([inp["alpha_fwd"], inp["alpha_rev"]], np.float64)).astype(np.float32)[:, None, :, None]
+    bt = np.array([inp["beta_fwd"], inp["beta_rev"]], np.float32)[:, None, :, None]
+    tol = dict(rtol=0, atol=1e-7)
+    o, _ = oracle.forward(q, k, v, la[:1], bt[:1], None, "fwd", exclusive="fwd")
+    np.testing.assert_allclose(o[0, :, 0], exp["out_fwd"], **tol)
+    o, _ = oracle.forward(q, k, v, la[1:], bt[1:], None, "rev", exclusive="rev")
+    np.testing.assert_allclose(o[0, :, 0], exp["out_rev"], **tol)
+    for mode, key in (("both", "out_bi_both"), ("rev", "out_bi_rev"), ("fwd", "out_bi_fwd")):
+        o, _ = oracle.forward(q, k, v, la, bt, None, "bi", exclusive=mode)
+        np.testing.assert_allclose(o[0, :, 0], exp[key], **tol)
