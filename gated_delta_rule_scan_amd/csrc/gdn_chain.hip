@@ -191,20 +191,30 @@ __device__ __forceinline__ f32x4 bload16_fresh(rsrc_t r, uint32_t off) {
   return f;
 }
 
-constexpr int kPollLimit = 1 << 20;
+// Bound on the re-reads of one partial (about a second at ~0.14 us per
+// re-read, measured on MI355X).  Partners are dispatched together, so a wait
+// is normally short; a partner can start late only when other work holds
+// compute units.  A workgroup that ever exhausts the bound stops waiting for
+// the rest of the launch, so a launch always ends; the outputs it then adds
+// to an unwritten partial keep the fill pattern (a NaN), so they cannot pass
+// unnoticed.
+constexpr int kPollLimit = 1 << 23;
 
 // 4-byte flag load that misses the L1 cache, as a uint32
 __device__ __forceinline__ uint32_t bload4_fresh(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 17);
 }
 
-// Bound on the polls for one chunk's ready flag (about 0.1 s); a workgroup
-// that ever exhausts it stops waiting for the rest of the launch, so a launch
-// always ends, and sets its state and pseudo-values to NaN: every later
+// Bound on the polls for one chunk's ready flag (about a second at ~0.14 us
+// per poll, measured on MI355X: far longer than any preparation pass that
+// fits in device memory takes, also when it queues behind another call's pass
+// on the shared library stream); a
+// workgroup that ever exhausts it stops waiting for the rest of the launch,
+// so a launch always ends, and sets its state and pseudo-values to NaN: every later
 // output of its chain and its final state are then NaN (the canonical quiet
 // NaN, never the "not written yet" pattern), so a starved preparation pass
 // cannot pass unnoticed.
-constexpr int kReadyPollLimit = 1 << 16;
+constexpr int kReadyPollLimit = 1 << 23;
 
 // Waves per state-chain workgroup: four chain waves (one per SIMD), which
 // carry the state, and four readout waves beside them, which compute Z = Q S^T
@@ -648,6 +658,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     __syncthreads();
   };
 
+  bool pq_gave_up = false;  // see kPollLimit
   auto step_read = [&](FR& st, FR& nx, const int s, const int cn) {
     const int c = chunk_at(s);
 
@@ -691,14 +702,16 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         for (int j = 0; j < UPW; ++j) {
           // first test outside any loop: a loop that reloads the tested value
           // makes the compiler wait for every load in flight at its head
-          if (__any(any_unwritten(st.pq[j]))) {
+          if (__any(any_unwritten(st.pq[j])) && !pq_gave_up) {
             const uint32_t off = out_off + out_at(c) + ((wr + NWC * j) / RT) * 64;
             f32x4 q = st.pq[j];
-            for (int n = 0; n < kPollLimit; ++n) {
+            int n = 0;
+            for (; n < kPollLimit; ++n) {
               __builtin_amdgcn_s_sleep(2);
               q = bload16_fresh(ro, off);
               if (!__any(any_unwritten(q))) break;
             }
+            pq_gave_up = n == kPollLimit;
             st.pq[j] = q;
           }
         }

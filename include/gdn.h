@@ -53,6 +53,10 @@
  * the work still starts after earlier work on `stream`, later work on
  * `stream` still waits for all of it, and a HIP graph capture of `stream`
  * takes both branches.  GDN_OPT_SERIAL keeps everything on `stream`.
+ * Calls may come from several host threads at once, each with its own
+ * buffers and workspace: the library stream and events are shared under a
+ * lock, and the preparation passes of concurrent calls run one after another
+ * on that stream (results are those of the same calls made one at a time).
  * state_in == state_out is allowed (in-place streaming carry); any other
  * overlap between `out`, the state buffers, the workspace and the inputs is
  * rejected.  Results are bitwise deterministic for fixed inputs and chunk
@@ -117,7 +121,7 @@ typedef enum {
                                Final states are unchanged by either bit. */,
   GDN_OPT_TEST_NO_PREPARATION = 1 << 16  /* testing only: the chunk preparation pass is not
                                launched, so the state chain waits on ready flags that never
-                               clear; its bounded waits expire (about 0.1 s) and every
+                               clear; its bounded waits expire (about a second) and every
                                output and final state is NaN.  This exercises the behaviour
                                under a preparation pass starved of the GPU: results that
                                cannot be trusted are NaN, never silently wrong. */

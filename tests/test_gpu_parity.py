@@ -171,3 +171,53 @@ def test_exclusive_readout_concurrent_matches_serial():
     ref_incl, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi")
     check_scaled(o_con, ref, TOL["bf16"], float(np.sqrt(np.mean(ref_incl ** 2))), f"out {w} exclusive concurrent")
     check(s_con, ref_s, TOL["bf16"], f"state {w} exclusive concurrent")
+
+
+def test_calls_from_two_host_threads():
+    """Two host threads, each on its own stream with its own buffers, call the
+    scan at the same time (bidirectional and causal, both on the concurrent
+    preparation path, which shares the library stream and events); every
+    result equals the same call made alone, bit for bit."""
+    import threading
+
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    from gdn_testutil import to_torch
+
+    cases = [_case("bf16", "bi", T=64 * 30 + 7, H=4, dk=128, dv=128, state_std=0.05, seed=19),
+             _case("bf16", "fwd", T=64 * 40 + 3, H=3, dk=64, dv=64, state_std=0.05, seed=20)]
+    inputs = [{k: to_torch(v) for k, v in synth.generate(w).items()} for w in cases]
+
+    def call(d, w, stream=None):
+        with torch.cuda.stream(stream or torch.cuda.current_stream()):
+            o, s = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction)
+        return o, s
+
+    alone = []
+    for d, w in zip(inputs, cases):
+        o, s = call(d, w)
+        torch.cuda.synchronize()
+        alone.append((o.cpu().numpy(), s.cpu().numpy()))
+    results = [[None] * 8 for _ in cases]
+    errors = []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            for r in range(8):
+                o, s = call(inputs[i], cases[i], st)
+                results[i][r] = (o, s, st)
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(cases)):
+        for o, s, _ in results[i]:
+            assert np.array_equal(o.cpu().numpy(), alone[i][0]) and np.array_equal(s.cpu().numpy(), alone[i][1])
