@@ -206,15 +206,8 @@ def run_vda(args, w) -> int:
         step()
     torch.cuda.synchronize()
     K = args.steps
-    # the timed steps (no per-call events), then the same K calls with the
-    # library's four HIP events each for the per-kernel durations
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(K):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / K
+    # K calls with the library's four HIP events each for the per-kernel
+    # durations, then the timed steps: the same K calls without per-call events
     ev = HipEvents(4 * K)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -223,6 +216,13 @@ def run_vda(args, w) -> int:
     e1.record()
     torch.cuda.synchronize()
     ms_step_events = e0.elapsed_time(e1) / K
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / K
     km = {n: sum(ev.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(K)) / K
           for n, a in (("vda_frame", 0), ("vda_chain", 1), ("vda_readout", 2))}
     ev.close()
@@ -361,7 +361,19 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     K = args.steps
-    # the timed steps: K calls as a user makes them (no per-call events)
+    # per-kernel durations: K calls, each with four HIP events recorded by the
+    # library (prep start/end on its stream, chain start/end on the caller's
+    # stream)
+    ev = HipEvents(4 * K)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(K):
+        step(ev.ptr(4 * i))
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step_events = e0.elapsed_time(e1) / K
+    # the timed steps: the same K calls as a user makes them (no per-call events)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -372,18 +384,6 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(stop) / K
-    # per-kernel durations: the same K calls again, each with four HIP events
-    # recorded by the library (prep start/end on its stream, chain start/end
-    # on the caller's stream)
-    ev = HipEvents(4 * K)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(K):
-        step(ev.ptr(4 * i))
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step_events = e0.elapsed_time(e1) / K
     prep_ms = sum(ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)) / K
     chain_ms = sum(ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)) / K
     # the chain started before the preparation pass ended: the two ran concurrently
