@@ -138,6 +138,18 @@ def gdn_version() -> str:
     return lib().gdn_version().decode()
 
 
+def _record_on(stream, tensors) -> None:
+    """Tensors the binding allocated on the current stream but hands to work
+    on another ``stream``: tell torch's caching allocator that ``stream`` uses
+    them, so their memory is not given to new allocations until that work is
+    done (the workspace and any temporary are freed when the call returns)."""
+    import torch
+
+    if stream != torch.cuda.current_stream(stream.device):
+        for t in tensors:
+            t.record_stream(stream)
+
+
 def make_problem(B, T, H, dk, dv, dtype: int, chunk: int = 0, dv_tile: int = 0, workspace: int = 0,
                  workspace_bytes: int = 0, stream: int = 0) -> gdn_problem_t:
     return gdn_problem_t(B, T, H, dk, dv, dtype, chunk, dv_tile, 0, workspace or None, workspace_bytes,
@@ -194,17 +206,22 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
                                  or tuple(state_in.shape) != (dirs, B, H, dv, dk)):
         raise ValueError(f"state_in must be contiguous float32 [{dirs},{B},{H},{dv},{dk}]")
     dev = q.device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    mine = []  # tensors allocated here (on the current stream)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+        mine.append(out)
     if state_out is None and want_state:
         state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
+        mine.append(state_out)
     prob = make_problem(B, T, H, dk, dv, dt, chunk, dv_tile)
     nbytes = gdn_workspace_bytes(prob, DIRECTIONS[direction])
     if nbytes == 0 and T > 0:
         raise GdnError(GDN_ERR_UNSUPPORTED)
     if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
+        mine.append(workspace)
+    _record_on(s, mine)
     prob.workspace = workspace.data_ptr() if workspace is not None else None
     prob.workspace_bytes = workspace.numel() if workspace is not None else 0
     prob.stream = s.cuda_stream
@@ -252,10 +269,14 @@ def vda_forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd",
                                  or tuple(state_in.shape) != (dirs, B, H, dv, dk)):
         raise ValueError(f"state_in must be contiguous float32 [{dirs},{B},{H},{dv},{dk}]")
     dev = q.device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    mine = []  # tensors allocated here (on the current stream)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+        mine.append(out)
     if state_out is None and want_state:
         state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
+        mine.append(state_out)
     if write not in ("inverse", "additive"):
         raise ValueError("write must be 'inverse' or 'additive'")
     if gate is not None:
@@ -263,16 +284,20 @@ def vda_forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd",
             raise ValueError(f"gate must be contiguous [{B},{T},{H},{dv}] of the type of q")
         if norm_weight is None or norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (dv,):
             raise ValueError(f"norm_weight must be float32 [{dv}] when gate is given")
+        if not norm_weight.is_contiguous():
+            norm_weight = norm_weight.contiguous()
+            mine.append(norm_weight)
     prob = gdn_vda_problem_t(B=B, T=T, H=H, dk=dk, dv=dv, frame=frame, dtype=dt,
                              options=GDN_VDA_OPT_ADDITIVE if write == "additive" else 0, readout_lag=lag,
                              norm_eps=norm_eps, gate=None if gate is None else gate.data_ptr(),
-                             norm_weight=None if gate is None else norm_weight.contiguous().data_ptr())
+                             norm_weight=None if gate is None else norm_weight.data_ptr())
     nbytes = gdn_vda_workspace_bytes(prob, DIRECTIONS[direction])
     if nbytes == 0 and T > 0:
         raise GdnError(GDN_ERR_UNSUPPORTED)
     if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
+        mine.append(workspace)
+    _record_on(s, mine)
     prob.workspace = workspace.data_ptr() if workspace is not None else None
     prob.workspace_bytes = workspace.numel() if workspace is not None else 0
     prob.stream = s.cuda_stream

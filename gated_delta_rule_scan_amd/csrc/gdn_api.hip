@@ -5,10 +5,11 @@
 // enqueues the chunk preparation and the state chain and returns without
 // synchronising.  The two kernels run one after the other on the caller's
 // stream, or -- when the device provably has room for a preparation
-// workgroup beside every resident state-chain workgroup -- concurrently: the
-// preparation pass on a library stream forked from and joined back to the
-// caller's stream with events (graph-capture safe), the state chain on the
-// caller's stream waiting chunk by chunk on the ready flags.
+// workgroup beside every resident state-chain workgroup, and the stream is
+// not being captured -- concurrently: the preparation pass on a library
+// stream forked from and joined back to the caller's stream with events, the
+// state chain on the caller's stream waiting chunk by chunk on the ready
+// flags.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -168,6 +169,14 @@ bool may_overlap(prep_fn pf, chain_fn cf, int64_t chain_wgs, int64_t NC) {
          ap.sharedSizeBytes + ac.sharedSizeBytes <= (size_t)lds;
 }
 
+// Whether `stream` is being captured into a graph (any capture mode).  A
+// failed query counts as capturing, which only selects the serial order.
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return true;
+  return st != hipStreamCaptureStatusNone;
+}
+
 template <typename MT>
 prep_fn prep_for(int dk, int C) {
   if (dk == 64) return C == 32 ? launch_prep<MT, 64, 32> : launch_prep<MT, 64, 64>;
@@ -279,7 +288,11 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
     if (cf(a, rev_single, stream, nullptr) != hipSuccess || !mark(3, stream)) return GDN_ERR_HIP;
     return GDN_OK;
   }
-  const bool concurrent = pl.NC > 0 && !(p->options & GDN_OPT_SERIAL) &&
+  // Under stream capture the two kernels always run one after the other: a
+  // graph orders its nodes only by their dependencies, so nothing would make
+  // the preparation node start while the chain node waits on its flags, and
+  // no library stream or event may be created or joined into a capture.
+  const bool concurrent = pl.NC > 0 && !(p->options & GDN_OPT_SERIAL) && !capturing(stream) &&
                           may_overlap(pf, cf, chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
   if (concurrent) {
     int dev = 0;

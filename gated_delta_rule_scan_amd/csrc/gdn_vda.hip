@@ -1,6 +1,7 @@
 // Frame-wise delta operator (Video Delta Attention): the memory is written
-// once per latent frame as the state closest to the decayed memory that fits
-// all of the frame's key-value associations ("Video DeltaNet", "Key
+// once per latent frame, as the solution of a regularised least-squares
+// problem -- the squared distance from the decayed previous memory plus the
+// squared recall errors of all the frame's keys ("Video DeltaNet", "Key
 // Contributions" item 2 and "Methodology in Plain English"):
 //
 //   S_t = (a_t S_{t-1} + B_t) (I + A_t)^{-1},

@@ -32,8 +32,9 @@
  * concatenation.
  *
  * Layouts (all row-major and contiguous; base pointers 16-byte aligned):
- *   q, k       [B, T, H, dk]   dtype (fp32 or bf16)
- *   v          [B, T, H, dv]   dtype
+ *   q, k       [B, T, H, dk]   dtype (fp32 or bf16), finite (any length:
+ *                              the scan normalises them itself)
+ *   v          [B, T, H, dv]   dtype, finite
  *   log_alpha  [dirs, B, T, H] fp32, finite and <= 0 (caller's contract)
  *   beta       [dirs, B, T, H] fp32, finite (beta in [0,1] keeps the
  *                              transition non-expansive)
@@ -49,10 +50,13 @@
  * stream) and completes asynchronously.  For large problems the chunk
  * preparation runs concurrently with the state chain, on a library stream
  * forked from `stream` and joined back to it with events (one stream and two
- * events per device, created on first use and kept until the process ends):
- * the work still starts after earlier work on `stream`, later work on
- * `stream` still waits for all of it, and a HIP graph capture of `stream`
- * takes both branches.  GDN_OPT_SERIAL keeps everything on `stream`.
+ * events per device, created on the first such call and kept until the
+ * process ends): the work still starts after earlier work on `stream`, and
+ * later work on `stream` still waits for all of it.  While `stream` is being
+ * captured into a HIP graph, both kernels are enqueued one after the other on
+ * `stream` (no library stream or event is created or used), so a captured
+ * call -- the first call of the process included -- replays the serial order.
+ * GDN_OPT_SERIAL keeps everything on `stream` always.
  * Calls may come from several host threads at once, each with its own
  * buffers and workspace: the library stream and events are shared under a
  * lock, and the preparation passes of concurrent calls run one after another
@@ -165,10 +169,12 @@ gdn_status_t gdn_forward(const gdn_problem_t* p,
 
 /* ---- Frame-wise delta operator (Video Delta Attention) ---------------------
  *
- * The memory is written once per latent frame instead of once per token: the
- * state that stays closest to the decayed memory while fitting all of the
- * frame's key-value associations ("Video DeltaNet", "Key Contributions" item
- * 2 and "Methodology in Plain English"), in the page's closed form
+ * The memory is written once per latent frame instead of once per token.
+ * The write is a regularised least-squares problem: the new memory balances
+ * its squared distance from the decayed previous memory against the squared
+ * recall errors of all the frame's keys at once ("Video DeltaNet", "Key
+ * Contributions" item 2 and "Methodology in Plain English").  Its solution is
+ * the page's closed form
  *
  *   S_t = (a_t S_{t-1} + B_t) (I + A_t)^{-1},
  *   A_t = sum_{i in frame t} beta_i k^_i k^_i^T,  B_t = sum_{i in frame t} beta_i v_i k^_i^T,

@@ -6,9 +6,10 @@ smoke check and the benchmark's CPU-baseline leg may use it; the GPU library
 shares no code with it.
 
 Definition ("Video DeltaNet", "Key Contributions" item 2, and "Methodology in
-Plain English"): the memory is written once per latent frame, as the state
-that stays closest to the decayed memory while fitting all of the frame's
-key-value associations,
+Plain English"): the memory is written once per latent frame, as the minimiser
+of a regularised least-squares objective -- squared distance from the decayed
+previous memory plus the beta-weighted squared recall errors of the frame's
+keys,
 
     S_t = argmin_S  ||S - Sbar_t||_F^2 + sum_{i in frame t} beta_i ||S k^_i - v_i||^2,
     Sbar_t = a_t S_{t-1},

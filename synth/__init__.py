@@ -12,6 +12,10 @@ shapes the pages discuss: Wan-style 480p latents of 21 frames x 30x52 tokens
 
 * q, k ~ N(0, 1), then scaled to unit L2 norm per (batch, token, head) in
   double precision, then rounded to the input dtype (bf16: nearest-even);
+  a workload with ``qk="raw"`` instead leaves the rows un-normalised, scales
+  each by 10^(6u - 3), u ~ U(0, 1), and puts every 37th row at an L2 norm
+  between about 0.5e-6 and 2e-6 (the two sides of a 1e-6 norm clamp), so
+  that the consumer's own normalisation is exercised;
 * v ~ N(0, 1);
 * beta = sigmoid(N(0, 1));
 * log_alpha = -softplus(N(0, 1) + shift), shift = 3 (5 for the 720p causal
@@ -42,6 +46,7 @@ STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
 STREAM_BETA, STREAM_LOG_ALPHA, STREAM_STATE = 10, 20, 30
 STREAM_FRAME_LOG_ALPHA = 40
 STREAM_GATE, STREAM_NORM_WEIGHT = 50, 60
+STREAM_Q_SCALE, STREAM_K_SCALE = 70, 71
 
 
 def build(force: bool = True) -> str:
@@ -65,6 +70,8 @@ def _load():
         i64, u64 = ctypes.c_int64, ctypes.c_uint64
         lib.synth_vectors.argtypes = [u64, u64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, i64]
         lib.synth_vectors.restype = None
+        lib.synth_vectors_raw.argtypes = [u64, u64, u64, i64, i64, ctypes.c_int, ctypes.c_void_p, i64]
+        lib.synth_vectors_raw.restype = None
         lib.synth_scalars.argtypes = [u64, u64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, i64]
         lib.synth_scalars.restype = None
         lib.synth_bf16_to_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64]
@@ -89,6 +96,7 @@ class Workload:
     state_std: float = 0.0
     seed: int = 0
     frame: Optional[int] = None  # tokens per streaming call (None: one call)
+    qk: str = "unit"  # "unit": q, k rows of unit length; "raw": un-normalised rows (see the module notes)
 
     @property
     def dirs(self) -> int:
@@ -129,6 +137,19 @@ def _vectors(seed, stream, rows, d, unit, dtype):
     return out
 
 
+def _vectors_raw(seed, stream, scale_stream, rows, d, dtype):
+    if d > 1024:
+        raise ValueError("head dimension above 1024 is not supported by the generator")
+    lib = _load()
+    if dtype == "bf16":
+        out = np.empty((rows, d), dtype=np.uint16)
+        lib.synth_vectors_raw(seed, stream, scale_stream, rows, d, 1, out.ctypes.data, 0)
+    else:
+        out = np.empty((rows, d), dtype=np.float32)
+        lib.synth_vectors_raw(seed, stream, scale_stream, rows, d, 0, out.ctypes.data, 0)
+    return out
+
+
 def _scalars(seed, stream, n, kind, p0):
     lib = _load()
     out = np.empty(n, dtype=np.float32)
@@ -146,8 +167,14 @@ def generate(w: Workload, T: Optional[int] = None) -> dict:
     T = w.T if T is None else T
     B, H, dk, dv = w.B, w.H, w.dk, w.dv
     rows = B * T * H
-    q = _vectors(w.seed, STREAM_Q, rows, dk, True, w.dtype).reshape(B, T, H, dk)
-    k = _vectors(w.seed, STREAM_K, rows, dk, True, w.dtype).reshape(B, T, H, dk)
+    if w.qk == "raw":
+        q = _vectors_raw(w.seed, STREAM_Q, STREAM_Q_SCALE, rows, dk, w.dtype).reshape(B, T, H, dk)
+        k = _vectors_raw(w.seed, STREAM_K, STREAM_K_SCALE, rows, dk, w.dtype).reshape(B, T, H, dk)
+    elif w.qk == "unit":
+        q = _vectors(w.seed, STREAM_Q, rows, dk, True, w.dtype).reshape(B, T, H, dk)
+        k = _vectors(w.seed, STREAM_K, rows, dk, True, w.dtype).reshape(B, T, H, dk)
+    else:
+        raise ValueError(f"qk must be 'unit' or 'raw', not {w.qk!r}")
     v = _vectors(w.seed, STREAM_V, rows, dv, False, w.dtype).reshape(B, T, H, dv)
     la = np.stack([_scalars(w.seed, STREAM_LOG_ALPHA + d, rows, 2, w.la_shift) for d in range(w.dirs)])
     beta = np.stack([_scalars(w.seed, STREAM_BETA + d, rows, 1, 0.0) for d in range(w.dirs)])

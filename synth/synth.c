@@ -99,6 +99,40 @@ void synth_vectors(uint64_t seed, uint64_t stream, int64_t rows, int64_t d,
 }
 
 /*
+ * Raw (un-normalised) vectors for testing a consumer's own normalisation:
+ * each row ~ N(0, I_d) times a per-row scale 10^(6u - 3), u ~ U(0, 1) from
+ * stream `scale_stream` (row norms from about 1e-3 sqrt(d) to 1e3 sqrt(d)),
+ * except every 37th row (global row index 5 mod 37), which is rescaled to an
+ * L2 norm of 10^(-6 + 0.6 (u - 0.5)) -- between about 0.5e-6 and 2e-6, on
+ * both sides of a 1e-6 norm clamp.  dtype as for synth_vectors.
+ */
+void synth_vectors_raw(uint64_t seed, uint64_t stream, uint64_t scale_stream, int64_t rows, int64_t d,
+                       int dtype, void* dst, int64_t row0) {
+  uint64_t base = stream_base(seed, stream);
+  uint64_t sbase = stream_base(seed, scale_stream);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double buf[1024]; /* d <= 1024 is checked by the Python wrapper */
+    int64_t gr = row0 + r;
+    double ss = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      double z = normal_at(base, (uint64_t)(gr * d + j));
+      buf[j] = z;
+      ss += z * z;
+    }
+    double u = uniform_at(sbase, (uint64_t)gr);
+    double scale = (gr % 37 == 5) ? pow(10.0, -6.0 + 0.6 * (u - 0.5)) / sqrt(ss) : pow(10.0, 6.0 * u - 3.0);
+    if (dtype == 0) {
+      float* o = (float*)dst + r * d;
+      for (int64_t j = 0; j < d; ++j) o[j] = (float)(buf[j] * scale);
+    } else {
+      uint16_t* o = (uint16_t*)dst + r * d;
+      for (int64_t j = 0; j < d; ++j) o[j] = double_to_bf16_bits(buf[j] * scale);
+    }
+  }
+}
+
+/*
  * Fill n scalars from stream `stream` with one of these distributions:
  *   kind 0: N(0,1) * p0                         (plain normal, std p0)
  *   kind 1: sigmoid(N(0,1))                     (write-strength gates)

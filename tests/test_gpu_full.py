@@ -76,6 +76,32 @@ def test_full_size_sampled_heads(name):
     torch.cuda.empty_cache()
 
 
+def test_full_size_bidir480_raw_qk():
+    """The 480p bidirectional workload (B2 H16 T32760 d128 bf16) with
+    un-normalised q and k (per-row scales from 1e-3 to 1e3, rows at the norm
+    clamp): the kernels' own normalisation at full size, sampled heads."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+
+    w = synth.WORKLOADS["bidir480"].replace(qk="raw")
+    print(f"\n[bidir480 raw q/k] generating {w}", flush=True)
+    x = synth.generate(w)
+    d = {k: to_torch(v) for k, v in x.items()}
+    out, s_out = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction)
+    torch.cuda.synchronize()
+    heads = _sample_heads(w)
+    print(f"[bidir480 raw q/k] oracle on heads {heads}", flush=True)
+    ref, ref_s = oracle.forward_heads(x, heads, w.direction)
+    got = np.stack([out[b, :, h].cpu().numpy() for b, h in heads])
+    got_s = np.stack([s_out[:, b, h].cpu().numpy() for b, h in heads], axis=1)
+    e_o = check(got, ref, TOL[w.dtype], "bidir480 raw q/k out")
+    e_s = check(got_s, ref_s, TOL[w.dtype], "bidir480 raw q/k state")
+    print(f"[bidir480 raw q/k] max|err|/RMS: out {e_o:.3e}  state {e_s:.3e}", flush=True)
+    del d, out, s_out
+    torch.cuda.empty_cache()
+
+
 def test_full_size_bidir480_disjoint_regions():
     """The 480p bidirectional workload (B2 H16 T32760) with both directions
     reading before the token's own write, sampled heads against the oracle

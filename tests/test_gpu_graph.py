@@ -5,10 +5,15 @@ stream and events); the graph is then replayed several times with new inputs
 copied in eagerly between replays, and every replay must equal an eager call
 on the same inputs bit for bit (the kernels are deterministic).
 
-The token scan is captured in serial mode and with the concurrent preparation
-(side stream forked and joined with events, ready flags cleared by a kernel);
-the shapes below have 16 or more chunks and few chain workgroups, so the
-concurrent path is the one taken when `serial` is off."""
+The token scan is captured with and without GDN_OPT_SERIAL; the shapes below
+have 16 or more chunks and few chain workgroups, so an eager call takes the
+concurrent preparation path when `serial` is off, while a captured call takes
+the serial order (the library checks the stream's capture status).  A first
+call of the process made inside a capture is checked in a fresh process."""
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 
@@ -113,3 +118,70 @@ def test_frame_wise_capture(lag, epilogue):
         return f
 
     _replays(eager, run, inp, fresh)
+
+
+_FIRST_CALL_IN_CAPTURE = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + '/tests')
+import synth, gated_delta_rule_scan_amd as gdn
+from gdn_testutil import to_torch
+w = synth.Workload("graph first", 1, 2, 1100, 128, 128, "bf16", "bi", 3.0, 0.02, 33)
+inp = {k: to_torch(v) for k, v in synth.generate(w).items()}
+out = torch.empty((1, 1100, 2, 128), dtype=torch.float32, device="cuda")
+s_out = torch.empty((2, 1, 2, 128, 128), dtype=torch.float32, device="cuda")
+prob = gdn.gdn_problem_t(B=1, T=1100, H=2, dk=128, dv=128, dtype=gdn.GDN_DTYPE_BF16)
+ws = torch.empty(gdn.gdn_workspace_bytes(prob, gdn.GDN_DIR_BIDIRECTIONAL), dtype=torch.uint8, device="cuda")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):  # the first library call of this process
+    gdn.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["state_in"], "bi", out=out,
+                state_out=s_out, workspace=ws)
+for i in range(3):
+    y = synth.generate(w.replace(seed=300 + i))
+    for k in ("q", "k", "v", "log_alpha", "beta", "state_in"):
+        inp[k].copy_(to_torch(y[k]))
+    g.replay()
+    torch.cuda.synchronize()
+    got = (out.clone(), s_out.clone())
+    o2, s2 = gdn.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["state_in"], "bi")
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], o2) and torch.equal(got[1], s2), f"replay {i} differs from the eager call"
+print("FIRST_CALL_IN_CAPTURE_OK", flush=True)
+"""
+
+
+def test_first_call_of_the_process_inside_a_capture():
+    """A fresh process whose first library call is captured (no eager warm-up
+    has created the library's side stream): the capture takes the serial
+    order, and each of three replays with new inputs equals an eager call
+    (which does take the concurrent path) bit for bit."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_IN_CAPTURE, root], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0 and "FIRST_CALL_IN_CAPTURE_OK" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
+
+
+def test_call_on_a_non_current_stream_keeps_its_buffers():
+    """forward(stream=s) with s not the current stream: the workspace and
+    outputs the binding allocates are recorded on s, so memory allocated
+    right after the call on the current stream (and written at once) never
+    lands in a buffer the scan still uses; the result equals a call on the
+    current stream bit for bit."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+
+    w = synth.Workload("stream", 2, 8, 64 * 60 + 9, 128, 128, "bf16", "bi", 3.0, 0.02, 34)
+    inp = {k: to_torch(v) for k, v in synth.generate(w).items()}
+    ref_o, ref_s = gdn.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["state_in"], "bi")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        o, s = gdn.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["state_in"], "bi",
+                           stream=side)
+        # new allocations on the current stream, written at once
+        junk = [torch.full((1 << 22,), float("nan"), device="cuda") for _ in range(16)]
+        torch.cuda.current_stream().wait_stream(side)
+        assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
+        del junk, o, s

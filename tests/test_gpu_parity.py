@@ -15,8 +15,8 @@ from gdn_testutil import TOL, check, check_scaled, rel_err, run_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _case(dtype, direction, T, B=1, H=2, dk=64, dv=64, la_shift=3.0, state_std=0.0, seed=0):
-    return synth.Workload("t", B, H, T, dk, dv, dtype, direction, la_shift, state_std, seed)
+def _case(dtype, direction, T, B=1, H=2, dk=64, dv=64, la_shift=3.0, state_std=0.0, seed=0, qk="unit"):
+    return synth.Workload("t", B, H, T, dk, dv, dtype, direction, la_shift, state_std, seed, qk=qk)
 
 
 def _compare(w, chunk=0, dv_tile=0, tol=None):
@@ -40,6 +40,25 @@ def test_tiny_causal_fp32():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_directions_ragged(direction, dtype):
     _compare(_case(dtype, direction, T=203, H=3, state_std=0.05, seed=5))
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("direction", ["fwd", "rev", "bi"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_raw_qk_normalisation(dtype, direction, chunk):
+    """q and k as given, not of unit length: N(0, 1) rows times per-row
+    scales from 1e-3 to 1e3, and every 37th row at a norm between 0.5e-6 and
+    2e-6 (both sides of the 1e-6 clamp).  The kernels' own row scales
+    rq = 1/max(|q|, 1e-6), rk = 1/max(|k|, 1e-6) must reproduce the oracle's
+    normalisation in every product they enter (Y, Z, P, the state update)."""
+    w = _case(dtype, direction, T=203, H=3, dk=128, dv=64, state_std=0.05, seed=21, qk="raw")
+    _compare(w, chunk=chunk)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "rev", "bi"])
+def test_bf16_chunk32(direction):
+    """bf16 operands with 32-token chunks (unit-length q, k)."""
+    _compare(_case("bf16", direction, T=203, H=3, dk=128, dv=128, state_std=0.05, seed=22), chunk=32)
 
 
 @pytest.mark.parametrize("d", [64, 128])

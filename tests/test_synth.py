@@ -67,3 +67,26 @@ def test_bf16_is_nearest_even_of_the_sample():
         assert np.all(np.abs(rne[diff].astype(np.int32) - h[n][diff].astype(np.int32)) <= 1)
         back = synth.bf16_to_f32(h[n])
         assert np.all(np.abs(back - x32) <= np.abs(x32) * 2.0 ** -8 + 1e-30)
+
+
+def test_raw_rows_span_scales_and_the_clamp():
+    """qk="raw": rows are not unit length; norms span about 1e-3 sqrt(d) to
+    1e3 sqrt(d), and every 37th row (global index 5 mod 37) has a norm on
+    either side of 1e-6; v and the gates are those of the unit recipe."""
+    w = synth.Workload("t", 1, 3, 500, 128, 64, "f32", "bi", 3.0, 0.0, 9, qk="raw")
+    x = synth.generate(w)
+    u = synth.generate(w.replace(qk="unit"))
+    for n in ("v", "log_alpha", "beta"):
+        np.testing.assert_array_equal(x[n], u[n])
+    for t in ("q", "k"):
+        nrm = np.linalg.norm(x[t].astype(np.float64), axis=-1).ravel()
+        rows = np.arange(nrm.size)
+        tiny = rows % 37 == 5
+        assert np.all((nrm[tiny] > 0.45e-6) & (nrm[tiny] < 2.1e-6))
+        assert np.any(nrm[tiny] < 1e-6) and np.any(nrm[tiny] > 1e-6)
+        big = nrm[~tiny] / np.sqrt(128)
+        assert big.min() < 1e-2 and big.max() > 1e2 and big.min() > 1e-4 and big.max() < 1e4
+        # direction of each row is that of a N(0, I) draw: not unit length, not constant
+        assert not np.allclose(nrm[~tiny], 1.0)
+    xb = synth.generate(w.replace(dtype="bf16"))
+    np.testing.assert_allclose(synth.bf16_to_f32(xb["q"]), x["q"], rtol=2 ** -8, atol=0)

@@ -290,6 +290,40 @@ def test_epilogue_gate_and_weights():
     assert np.all(np.delete(sel, 5, axis=-1) == 0)
 
 
+def test_epilogue_eps_sits_inside_the_root_hand_worked():
+    """Where eps stands in the RMS normalisation, worked by hand at a size
+    where mean(o^2) and eps are comparable.  One frame of one token, no
+    initial state, beta = 1, k = q = e1 (dk = 2), v = (3e-3, 4e-3) (dv = 2):
+    A = e1 e1^T, B = v e1^T, S = B (I + A)^-1 = (v / 2) e1^T, so o = S q^ =
+    (1.5e-3, 2e-3) and mean(o^2) = (2.25e-6 + 4e-6) / 2 = 3.125e-6.  With
+    eps = 3.125e-6, sqrt(mean + eps) = sqrt(6.25e-6) = 2.5e-3 and an open
+    gate (z = 60: sigmoid = 1 in double) and unit weights, y = o / 2.5e-3 =
+    (0.6, 0.8).  The other placements give other values: sqrt(mean) + eps
+    -> (0.8470, 1.1294), no eps -> (0.8485, 1.1314).  Closed gate z = 0 halves
+    it: (0.3, 0.4); weights (2, -1) give (1.2, -0.8)."""
+    q = np.array([1.0, 0.0], np.float32).reshape(1, 1, 1, 2)
+    k = q.copy()
+    v = np.array([3e-3, 4e-3], np.float64).astype(np.float32).reshape(1, 1, 1, 2)
+    la = np.zeros((1, 1, 1, 1), np.float32)
+    bt = np.ones((1, 1, 1, 1), np.float32)
+    vv = v.astype(np.float64).ravel()  # the float32 inputs as the oracle sees them
+    o = vv / 2.0
+    eps = float(np.mean(o * o))  # 3.125e-6 up to the float32 rounding of v
+    assert abs(eps - 3.125e-6) < 1e-12
+    def run(z, w):
+        y, _ = vda.forward(q, k, v, la, bt, None, "fwd", 1, gate=np.full((1, 1, 1, 2), z, np.float32),
+                           norm_weight=np.asarray(w, np.float64), norm_eps=eps)
+        return y.ravel()
+    want = o / np.sqrt(2.0 * eps)
+    assert np.allclose(want, [0.6, 0.8], rtol=0, atol=2e-7)
+    np.testing.assert_allclose(run(60.0, [1.0, 1.0]), want, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(run(0.0, [1.0, 1.0]), want / 2, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(run(60.0, [2.0, -1.0]), want * [2.0, -1.0], rtol=1e-13, atol=0)
+    # the other placements are far from the oracle's values
+    for alt in (o / (np.sqrt(eps) + eps), o / np.sqrt(eps)):
+        assert np.max(np.abs(run(60.0, [1.0, 1.0]) - alt)) > 0.2
+
+
 def test_reset_gate_makes_frame_windows_independent():
     """A per-frame log-gate of -1000 gives a = 0 exactly: S_t = B_t (I + A_t)^-1
     whatever came before.  With a forward reset at a window's first frame and a
