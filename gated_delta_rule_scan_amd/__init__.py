@@ -44,8 +44,9 @@ EXCLUSIVE = {"none": 0, "fwd": GDN_OPT_EXCLUSIVE_FORWARD, "rev": GDN_OPT_EXCLUSI
 
 GDN_VDA_OPT_ADDITIVE = 1
 
-EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_vda_workspace_bytes", "gdn_vda_forward", "gdn_status_string",
-            "gdn_version")
+EXPORTED = ("gdn_workspace_bytes", "gdn_forward", "gdn_forward_noalloc", "gdn_vda_workspace_bytes", "gdn_vda_forward",
+            "gdn_status_string", "gdn_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES
 
 
 class gdn_problem_t(ctypes.Structure):
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32]
         L.gdn_forward.restype = ctypes.c_int
+        L.gdn_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32]
+        L.gdn_forward_noalloc.restype = ctypes.c_int
         PV = ctypes.POINTER(gdn_vda_problem_t)
         L.gdn_vda_workspace_bytes.argtypes = [PV, ctypes.c_int32]
         L.gdn_vda_workspace_bytes.restype = ctypes.c_size_t
@@ -117,6 +120,14 @@ def gdn_forward(problem: gdn_problem_t, q: int, k: int, v: int, log_alpha: int, 
     """Raw call with integer device pointers (None for NULL); returns the status."""
     return int(lib().gdn_forward(ctypes.byref(problem), q, k, v, log_alpha, beta, state_in, state_out, out,
                                  int(direction)))
+
+
+def gdn_forward_noalloc(problem: gdn_problem_t, q: int, k: int, v: int, log_alpha: int, beta: int,
+                        state_in: Optional[int], state_out: Optional[int], out: int, direction: int) -> int:
+    """Raw call of the no-allocation entry point (the library's fixed device
+    scratch replaces the workspace); returns the status."""
+    return int(lib().gdn_forward_noalloc(ctypes.byref(problem), q, k, v, log_alpha, beta, state_in, state_out, out,
+                                         int(direction)))
 
 
 def gdn_vda_workspace_bytes(problem: gdn_vda_problem_t, direction: int) -> int:

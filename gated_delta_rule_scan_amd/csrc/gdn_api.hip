@@ -206,9 +206,14 @@ extern "C" size_t gdn_workspace_bytes(const gdn_problem_t* p, int32_t direction)
   return pl.ws.total;
 }
 
-extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const void* k, const void* v,
-                                    const float* log_alpha, const float* beta, const float* state_in,
-                                    float* state_out, float* out, int32_t direction) {
+namespace gdn {
+namespace {
+
+// The whole call with an explicit workspace (ws, ws_bytes); `serial_only`
+// keeps both kernels on the caller's stream.
+gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes, bool serial_only, const void* q,
+                          const void* k, const void* v, const float* log_alpha, const float* beta,
+                          const float* state_in, float* state_out, float* out, int32_t direction) {
   Plan pl;
   gdn_status_t st = make_plan(p, direction, &pl);
   if (st != GDN_OK) return st;
@@ -226,8 +231,8 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16))) return GDN_ERR_INVALID_ARGUMENT;
   const bool need_ws = T > 0;
   if (need_ws) {
-    if (!p->workspace || !aligned(p->workspace, 256)) return GDN_ERR_INVALID_ARGUMENT;
-    if (p->workspace_bytes < pl.ws.total) return GDN_ERR_WORKSPACE_TOO_SMALL;
+    if (!ws_ptr || !aligned(ws_ptr, 256)) return GDN_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < pl.ws.total) return GDN_ERR_WORKSPACE_TOO_SMALL;
   }
 
   // aliasing: outputs and workspace must not overlap anything else;
@@ -235,7 +240,7 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   const Range r_q = rng(q, n_qk * es), r_k = rng(k, n_qk * es), r_v = rng(v, n_v * es);
   const Range r_la = rng(log_alpha, n_g * 4), r_b = rng(beta, n_g * 4);
   const Range r_si = rng(state_in, n_s * 4), r_so = rng(state_out, n_s * 4);
-  const Range r_o = rng(out, n_v * 4), r_ws = rng(need_ws ? p->workspace : nullptr, pl.ws.total);
+  const Range r_o = rng(out, n_v * 4), r_ws = rng(need_ws ? ws_ptr : nullptr, pl.ws.total);
   const Range ins[] = {r_q, r_k, r_v, r_la, r_b, r_si};
   for (const Range& r : ins) {
     if (overlap(r_o, r) || overlap(r_ws, r)) return GDN_ERR_INVALID_ARGUMENT;
@@ -252,7 +257,7 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   memset(&a, 0, sizeof(a));
   a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
   a.state_in = state_in; a.state_out = state_out; a.out = out;
-  unsigned char* ws = static_cast<unsigned char*>(p->workspace);
+  unsigned char* ws = static_cast<unsigned char*>(ws_ptr);
   if (need_ws) {
     a.tri = ws + pl.ws.tri;
     a.pqk = ws + pl.ws.pqk;
@@ -292,7 +297,7 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   // graph orders its nodes only by their dependencies, so nothing would make
   // the preparation node start while the chain node waits on its flags, and
   // no library stream or event may be created or joined into a capture.
-  const bool concurrent = pl.NC > 0 && !(p->options & GDN_OPT_SERIAL) && !capturing(stream) &&
+  const bool concurrent = pl.NC > 0 && !serial_only && !(p->options & GDN_OPT_SERIAL) && !capturing(stream) &&
                           may_overlap(pf, cf, chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
   if (concurrent) {
     int dev = 0;
@@ -319,6 +324,57 @@ extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const
   if (cf(a, rev_single, stream, nullptr) != hipSuccess) return GDN_ERR_HIP;
   if (!mark(3, stream)) return GDN_ERR_HIP;
   return GDN_OK;
+}
+
+// ---- the fixed device scratch of gdn_forward_noalloc ----
+// Each device that loads the library holds its own copy of this array until
+// the process ends.  Host code never passes the array's name to a kernel (in
+// host code it is only a stand-in for the symbol): it uses the device address
+// returned by hipGetSymbolAddress, looked up once per device with that device
+// current.
+constexpr size_t kScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+// Device address of the current device's scratch (nullptr on failure).
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" gdn_status_t gdn_forward(const gdn_problem_t* p, const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const float* beta, const float* state_in,
+                                    float* state_out, float* out, int32_t direction) {
+  if (!p) return GDN_ERR_INVALID_ARGUMENT;
+  return forward_impl(p, p->workspace, p->workspace_bytes, false, q, k, v, log_alpha, beta, state_in, state_out, out,
+                      direction);
+}
+
+extern "C" gdn_status_t gdn_forward_noalloc(const gdn_problem_t* p, const void* q, const void* k, const void* v,
+                                            const float* log_alpha, const float* beta, const float* state_in,
+                                            float* state_out, float* out, int32_t direction) {
+  if (!p) return GDN_ERR_INVALID_ARGUMENT;
+  Plan pl;
+  gdn_status_t st = make_plan(p, direction, &pl);
+  if (st != GDN_OK) return st;
+  // argument errors first (the rest of the checks follow in forward_impl)
+  if (p->T > 0 && (!q || !k || !v || !log_alpha || !beta || !out)) return GDN_ERR_INVALID_ARGUMENT;
+  if (p->T > 0 && pl.ws.total > kScratchBytes) return GDN_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (p->T > 0 && !(ws = scratch_address())) return GDN_ERR_HIP;
+  return forward_impl(p, ws, kScratchBytes, true, q, k, v, log_alpha, beta, state_in, state_out, out, direction);
 }
 
 // ---- frame-wise delta operator ----

@@ -167,6 +167,36 @@ gdn_status_t gdn_forward(const gdn_problem_t* p,
                          const float* state_in, float* state_out,
                          float* out, int32_t direction);
 
+/* ---- The same scan without a caller-provided workspace ----------------------
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is a fixed array the library holds in device memory,
+ * GDN_NOALLOC_SCRATCH_BYTES per device that loads the library, kept until the
+ * process ends.  Arguments, layouts, results and errors are those of
+ * gdn_forward, except:
+ *  - p->workspace and p->workspace_bytes are ignored;
+ *  - a problem whose workspace (gdn_workspace_bytes) exceeds
+ *    GDN_NOALLOC_SCRATCH_BYTES is rejected with GDN_ERR_WORKSPACE_TOO_SMALL
+ *    before anything is enqueued (e.g. 480p streaming frames of 1560 tokens at
+ *    12 heads need about 6 MB; a whole 480p bidirectional block, about 300 MB,
+ *    does not fit);
+ *  - both kernels always run one after the other on p->stream (no library
+ *    stream or event is created);
+ *  - the first call on a device looks up that device's array
+ *    (hipGetSymbolAddress); no call allocates device memory.
+ * Every call on one device uses that device's single array, which keeps the
+ * last call's contents: calls that overlap in time on one device (on
+ * different streams, or from several host threads) race on it and must be
+ * ordered by the caller.  Nothing in the array has to start at zero. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gdn_status_t gdn_forward_noalloc(const gdn_problem_t* p,
+                                 const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta,
+                                 const float* state_in, float* state_out,
+                                 float* out, int32_t direction);
+
 /* ---- Frame-wise delta operator (Video Delta Attention) ---------------------
  *
  * The memory is written once per latent frame instead of once per token.

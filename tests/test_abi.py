@@ -233,3 +233,26 @@ def test_size_limits_are_exact():
     assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED
     p, a = _valid(B=1, H=65536)
     assert _call(p, a) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_noalloc_limit_in_header_matches_binding():
+    src = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdn.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch_before_any_launch():
+    """A problem whose workspace exceeds the fixed scratch is refused with
+    GDN_ERR_WORKSPACE_TOO_SMALL before anything touches a device (this host
+    has none); one that fits passes that check."""
+    big = gdn.make_problem(2, 32760, 16, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert gdn.gdn_workspace_bytes(big, gdn.GDN_DIR_BIDIRECTIONAL) > gdn.NOALLOC_SCRATCH_BYTES
+    fake = 1 << 40  # never dereferenced: the call returns before any launch
+    st = gdn.gdn_forward_noalloc(big, fake, fake + (1 << 32), fake + (2 << 32), fake + (3 << 32), fake + (4 << 32),
+                                 None, None, fake + (5 << 32), gdn.GDN_DIR_BIDIRECTIONAL)
+    assert st == gdn.GDN_ERR_WORKSPACE_TOO_SMALL
+    small = gdn.make_problem(1, 1560, 12, 128, 128, gdn.GDN_DTYPE_BF16)
+    assert 0 < gdn.gdn_workspace_bytes(small, gdn.GDN_DIR_FORWARD) <= gdn.NOALLOC_SCRATCH_BYTES
+    # invalid arguments are still reported first
+    assert gdn.gdn_forward_noalloc(small, None, None, None, None, None, None, None, None,
+                                   gdn.GDN_DIR_FORWARD) == gdn.GDN_ERR_INVALID_ARGUMENT
