@@ -135,38 +135,22 @@ bool side_stream(int dev, SideStream** out) {
 
 // Whether the preparation pass runs concurrently with the state chain.
 //
-// Worth it only when the chain leaves compute units free: a latency-bound
-// chain workgroup runs slower with preparation waves beside it on its SIMDs,
-// which costs more than the preparation pass when every unit holds a chain
-// (measured on MI355X: 480p bidirectional, 256 chain workgroups, 1.52 ms
-// concurrent vs 1.40 ms serial), while with a quarter of the units free the
-// pass hides (720p bidirectional, 192 chain workgroups: 4.25 vs 4.46 ms; 720p
-// causal, 128: 1.88 vs 2.05 ms).
+// Worth it only when the chain leaves at least half of the compute units
+// free: the state chain is bound by how fast each unit's L1 fills from L2,
+// and preparation traffic beside it slows it down.  Measured on MI355X with
+// the bf16 column chain: 720p causal (128 chain workgroups on 256 units)
+// 1.90 ms concurrent against 2.14 ms serial; 720p bidirectional (192) 4.65
+// against 4.25 ms; 480p bidirectional (256) runs serial.
 //
 // Safe because the chain waits only for chunks the preparation pass
-// publishes, and a preparation workgroup can always be scheduled: the chain
-// workgroups occupy at most three quarters of the compute units, and one fits
-// beside a chain workgroup anyway (registers per SIMD lane, counting the
-// chain's waves per SIMD, and LDS).  The preparation pass is enqueued first,
-// so a device that runs the two streams one after the other still finishes
-// it before the chain starts.
-bool may_overlap(prep_fn pf, chain_fn cf, int64_t chain_wgs, int64_t NC) {
+// publishes, and a preparation workgroup can always be scheduled: there are
+// at most half as many chain workgroups as compute units, so at least half
+// of the units hold none, however the workgroups are packed.  The
+// preparation pass is enqueued first, so a device that runs the two streams
+// one after the other still finishes it before the chain starts.
+bool may_overlap(int64_t chain_wgs, int64_t NC) {
   constexpr int64_t kMinChunks = 16;  // below this the fork/join costs more than it hides
-  if (NC < kMinChunks || 4 * chain_wgs > 3 * (int64_t)compute_units()) return false;
-  hipFuncAttributes ap, ac;
-  ScanArgs none;
-  memset(&none, 0, sizeof(none));
-  if (pf(none, nullptr, &ap) != hipSuccess || cf(none, 0, nullptr, &ac) != hipSuccess) return false;
-  int dev = 0, lds = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
-    return false;
-  auto granule = [](int r) { return (r + 7) / 8 * 8; };  // registers are allocated in blocks of 8
-  // per SIMD lane: one preparation wave beside the chain workgroup's waves on
-  // that SIMD (its block size spread over the four SIMDs)
-  const int chain_waves_per_simd = (ac.maxThreadsPerBlock + 255) / 256;
-  return granule(ap.numRegs) + chain_waves_per_simd * granule(ac.numRegs) <= 512 &&
-         ap.sharedSizeBytes + ac.sharedSizeBytes <= (size_t)lds;
+  return NC >= kMinChunks && 2 * chain_wgs <= (int64_t)compute_units();
 }
 
 // Whether `stream` is being captured into a graph (any capture mode).  A
@@ -189,10 +173,22 @@ chain_fn chain_for3(int NT, int dirs) {
   return dirs == 2 ? launch_chain<MT, DK, C, 2, true> : launch_chain<MT, DK, C, 2, false>;
 }
 
+template <int DK, int C>
+chain_fn column_chain_for3(int NT, int dirs) {
+  if (NT == 1) return dirs == 2 ? launch_column_chain<DK, C, 1, true> : launch_column_chain<DK, C, 1, false>;
+  return dirs == 2 ? launch_column_chain<DK, C, 2, true> : launch_column_chain<DK, C, 2, false>;
+}
+
+// bf16 operands: the column-owning chain; fp32 operands: the two-role chain
 template <typename MT>
 chain_fn chain_for(int dk, int C, int NT, int dirs) {
-  if (dk == 64) return C == 32 ? chain_for3<MT, 64, 32>(NT, dirs) : chain_for3<MT, 64, 64>(NT, dirs);
-  return C == 32 ? chain_for3<MT, 128, 32>(NT, dirs) : chain_for3<MT, 128, 64>(NT, dirs);
+  if constexpr (sizeof(MT) == 2) {
+    if (dk == 64) return C == 32 ? column_chain_for3<64, 32>(NT, dirs) : column_chain_for3<64, 64>(NT, dirs);
+    return C == 32 ? column_chain_for3<128, 32>(NT, dirs) : column_chain_for3<128, 64>(NT, dirs);
+  } else {
+    if (dk == 64) return C == 32 ? chain_for3<MT, 64, 32>(NT, dirs) : chain_for3<MT, 64, 64>(NT, dirs);
+    return C == 32 ? chain_for3<MT, 128, 32>(NT, dirs) : chain_for3<MT, 128, 64>(NT, dirs);
+  }
 }
 
 }  // namespace
@@ -298,7 +294,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   // the preparation node start while the chain node waits on its flags, and
   // no library stream or event may be created or joined into a capture.
   const bool concurrent = pl.NC > 0 && !serial_only && !(p->options & GDN_OPT_SERIAL) && !capturing(stream) &&
-                          may_overlap(pf, cf, chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
+                          may_overlap(chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
   if (concurrent) {
     int dev = 0;
     SideStream* side = nullptr;

@@ -1,0 +1,744 @@
+// State chain for bf16 operands: column-owning chain waves.
+//
+// The chunked scan (derivation in the preparation kernel) walks the chunks of
+// one (batch, head, direction) in order; per chunk, with the entry state S
+// (dv x dk, fp32),
+//
+//   Y = K S^T,   X = beta * (V - (e^g rk) * Y),   Vnew = X + strict(Tinv) X,
+//   S' = e^{g_last} S + (e^{g_last - g} rk * Vnew)^T K,
+//   O  = (e^g rq) * (Q S^T) + P Vnew          (P: decayed q^.k^ with the self terms),
+//
+// the chunk form of S_t = a_t S_{t-1}(I - b_t k^_t k^_t^T) + b_t v_t k^_t^T,
+// o_t = S_t q^_t.
+//
+// Work split.  A workgroup owns a (batch, head, direction) sequence and
+// 16*NT value columns.  Each of its NT chain waves owns 16 of those columns of
+// the state over every dk, so Y, X, Vnew and the state update of its columns
+// need nothing from another wave: every matrix-core result is, in registers,
+// the operand of the next product.  Two index orders make that so:
+//   * token order tau: row m of row tile rt of Y (and of X and Vnew) is token
+//     32 (rt/2) + 8 (m/4) + 4 (rt%2) + m%4, so the four rows a lane holds in a
+//     result tile are the four consecutive tokens the next product's operand
+//     wants in that lane (the k and triangle rows are staged in this order);
+//   * dk order pi: row m of state tile 2 ks + u is dk 32 ks + 8 (m/4) + 4 u +
+//     m%4, so the state accumulators, rounded to bf16, are directly the
+//     operand of Y = K S^T (the transposed k operand of the update is read in
+//     this order).
+// The chain's critical path is therefore register-only: Y (matrix cores, k
+// from LDS) -> X (fp32) -> strict(Tinv) X (matrix cores) -> scaled Vnew as
+// hi + lo bf16 parts -> state update (matrix cores, transposed k from LDS).
+// Each of NT readout waves takes the chunk one step later: it reads the
+// chunk's entry state and Vnew (hi + lo) that its chain wave left in LDS and
+// computes the transposed output tile O^T = S Q^T + Vnew^T P^T, so each lane
+// stores four consecutive values of one output row.  One barrier per step.
+//
+// Operand staging.  Every operand a wave reads from LDS arrives there by
+// direct buffer-to-LDS loads (16 bytes per lane, 1 KB per instruction),
+// issued a step before its use into a two-slot ring per role: the chain
+// waves load k (rows in tau order), the strict inverse triangle (rows in tau
+// order), the value tile and the chunk scales; the readout waves load q, the
+// decayed q.k triangle and the chunk scales.  Tiles are XOR-swizzled in
+// 16-byte pieces so the operand reads are free of bank conflicts.  The waits
+// for these loads are explicit (a wave waits for its own loads before the
+// step's barrier); the ring slots and the exchange buffers are distinct
+// arrays, so the compiler can tell every LDS read from the loads in flight.
+//
+// Bidirectional scans run the two directions in separate workgroups (ids 8
+// apart, on one XCD); the first visitor of a chunk stores its readout and the
+// second adds it, recognising an unwritten partial by the preparation kernel's
+// fill pattern, as in the fp32 chain kernel.
+#include <type_traits>
+
+#include "gdn_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4v;
+
+namespace {
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n), lgkmcnt(0), expcnt at its maximum.
+template <int n>
+struct WaitVmLds {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  static constexpr int value = (n & 15) | ((n >> 4) << 14) | (7 << 4);
+};
+
+// The step barrier: this wave's own loads counted out (vmcnt(n)), its LDS
+// writes done, then s_barrier.  The empty asm statements keep the compiler
+// from moving memory accesses across it (a __syncthreads() would also make
+// the compiler wait for every direct-to-LDS load in flight).
+template <int n>
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(WaitVmLds<n>::value);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void mem_fence_compiler() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(rsrc_t r, lds_u8* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4s tr16(const lds_u8* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)const_cast<lds_u8*>(p));
+}
+
+// token order of the chain's product rows (see the file comment)
+__host__ __device__ constexpr int tau(int rt, int m) { return 32 * (rt >> 1) + 8 * (m >> 2) + 4 * (rt & 1) + (m & 3); }
+
+template <int DK, int C, int NT>
+struct Col {
+  static constexpr int DT = 16 * NT;             // value columns per workgroup
+  static constexpr int RT = C / 16;              // 16-token row tiles per chunk
+  static constexpr int KC = C / 32;              // 32-token k-chunks
+  static constexpr int KS = DK / 32;             // 32-wide dk slices
+  static constexpr int SRT = DK / 16;            // 16-row dk tiles of the state
+  static constexpr int KROWB = DK * 2;           // bytes per k / q row
+  static constexpr int TROWB = C * 2;            // bytes per triangle row
+  static constexpr int VROWB = DT * 2;           // bytes per value-tile row
+  static constexpr int KB = C * KROWB, TB = C * TROWB, VB = C * VROWB;
+  // chain slot: k | Tinv | v | scales | remainders and chunk decay
+  static constexpr int CK = 0, CT = CK + KB, CV = CT + TB, CS = CV + VB, CP = CS + 1024, CSLOT = CP + 1024;
+  // readout slot: q | P | scales | remainders
+  static constexpr int RQ = 0, RP = RQ + KB, RS = RP + TB, RD = RS + 1024, RSLOT = RD + 1024;
+  // exchange, per chain wave: entry-state fragments (bf16), Vnew (fp32, the
+  // eight values of a k-chunk operand fragment per lane)
+  static constexpr int XS = 0, XV = KS * 1024, XJ = XV + KC * 2048, XSLOT = NT * XJ;
+  static constexpr int NDC = CSLOT / 1024, NDR = RSLOT / 1024;  // 1-KB loads per slot
+  static_assert(KB % 1024 == 0 && TB % 1024 == 0 && VB % 1024 == 0, "whole 1-KB loads");
+  static_assert(C == 32 || C == 64, "chunk");
+};
+
+// XOR swizzle of the 16-byte pieces of a k / q row and of a triangle row:
+// the 16 rows one operand read touches land on distinct banks.
+template <int DK>
+__device__ __forceinline__ int swz_kq(int row) { return DK == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int C>
+__device__ __forceinline__ int swz_t(int row) { return C == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
+
+// Where the tokens and pieces of one staged chunk come from.  Region kinds:
+enum : int { R_KTAU = 0, R_QNAT = 1, R_TTAU = 2, R_PNAT = 3, R_VAL = 4, R_RAW = 5 };
+
+template <int DK, int C, int NT>
+__device__ __forceinline__ uint32_t dma_voff(int kind, int ii, int lane, uint32_t HDB, uint32_t HVB) {
+  using L = Col<DK, C, NT>;
+  const int b = ii * 1024 + 16 * lane;  // byte within the staged region
+  if (kind == R_KTAU || kind == R_QNAT) {
+    const int rho = b / L::KROWB, q = (b % L::KROWB) >> 4;
+    const int p = q ^ swz_kq<DK>(rho);
+    const int t = kind == R_KTAU ? tau(rho >> 4, rho & 15) : rho;
+    return (uint32_t)t * HDB + (uint32_t)p * 16u;
+  }
+  if (kind == R_TTAU || kind == R_PNAT) {
+    const int rho = b / L::TROWB, q = (b % L::TROWB) >> 4;
+    const int p = q ^ swz_t<C>(rho);
+    const int r = kind == R_TTAU ? tau(rho >> 4, rho & 15) : rho;
+    return (uint32_t)(r * L::TROWB + p * 16);
+  }
+  if (kind == R_VAL) {
+    const int rho = b / L::VROWB, piece = (b % L::VROWB) >> 4;
+    return (uint32_t)rho * HVB + (uint32_t)piece * 16u;
+  }
+  return (uint32_t)b;
+}
+
+// All-ones NaN: the fill the preparation kernel leaves in `out` before a
+// bidirectional scan ("not written yet"); arithmetic never produces it.
+constexpr uint32_t kColUnwritten = 0xFFFFFFFFu;
+constexpr int kColPollLimit = 1 << 23;      // about a second of re-reads
+constexpr int kColReadyPollLimit = 1 << 23;
+
+__device__ __forceinline__ bool col_any_unwritten(f32x4 p) {
+  return __float_as_uint(p[0]) == kColUnwritten || __float_as_uint(p[1]) == kColUnwritten ||
+         __float_as_uint(p[2]) == kColUnwritten || __float_as_uint(p[3]) == kColUnwritten;
+}
+
+__device__ __forceinline__ f32x4 col_load_fresh(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 17);
+  f32x4 f;
+  __builtin_memcpy(&f, &v, 16);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t col_flag_fresh(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 17);
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (bf16)a[i];
+    r[4 + i] = (bf16)b[i];
+  }
+  return r;
+}
+
+// hi + lo bf16 parts of eight fp32 values (hi = rounded value, lo = rounded remainder)
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (bf16)a[i];
+    hi[4 + i] = (bf16)b[i];
+    lo[i] = (bf16)(a[i] - (float)hi[i]);
+    lo[4 + i] = (bf16)(b[i] - (float)hi[4 + i]);
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const lds_u8* p) { return *(const lds_bf16x8*)p; }
+__device__ __forceinline__ void lds_put(lds_u8* p, bf16x8 v) { *(lds_bf16x8*)p = v; }
+__device__ __forceinline__ float lds_f(const lds_u8* p) { return *(const lds_f32*)p; }
+__device__ __forceinline__ f32x4 lds_f4(const lds_u8* p) { return *(const lds_f32x4v*)p; }
+
+__device__ __forceinline__ bf16x8 and_mask(bf16x8 f, const uint32_t (&m)[4]) {
+  uint32_t w[4];
+  __builtin_memcpy(w, &f, 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] &= m[i];
+  __builtin_memcpy(&f, w, 16);
+  return f;
+}
+
+// 8-element keep mask of a fragment lane: element e is column col0 + e of row `row`
+__device__ __forceinline__ void make_mask(uint32_t (&m)[4], int row, int col0, bool upper, bool diag) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[i] = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int col = col0 + e;
+    const bool keep = (upper ? (col > row) : (col < row)) || (diag && col == row);
+    if (keep) m[e / 2] |= 0xffffu << (16 * (e % 2));
+  }
+}
+
+}  // namespace
+
+template <int DK, int C, int NT, bool BI>
+__global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
+  using L = Col<DK, C, NT>;
+  using M = Mma<bf16>;
+  constexpr int RT = L::RT, KC = L::KC, KS = L::KS, SRT = L::SRT, DT = L::DT;
+
+  __shared__ __align__(1024) unsigned char cs0_[L::CSLOT], cs1_[L::CSLOT];  // chain ring
+  __shared__ __align__(1024) unsigned char rs0_[L::RSLOT], rs1_[L::RSLOT];  // readout ring
+  __shared__ __align__(1024) unsigned char xs0_[L::XSLOT], xs1_[L::XSLOT];  // exchange, by step parity
+  __shared__ __align__(1024) unsigned char pf_[1024];                        // L2-prefetch sink, never read
+  lds_u8* const cs0 = (lds_u8*)cs0_;
+  lds_u8* const cs1 = (lds_u8*)cs1_;
+  lds_u8* const rs0 = (lds_u8*)rs0_;
+  lds_u8* const rs1 = (lds_u8*)rs1_;
+  lds_u8* const xs0 = (lds_u8*)xs0_;
+  lds_u8* const xs1 = (lds_u8*)xs1_;
+  lds_u8* const pfs = (lds_u8*)pf_;
+
+  // workgroup id -> (sequence, value tile, direction): the value tiles of one
+  // (batch, head) share an XCD; the two directions of a tile are 8 ids apart
+  const int ndir = BI ? 2 : 1;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, kk = id >> 3;
+  const int chain = (kk / (ntiles * ndir)) * 8 + xcd;
+  const int dslot = BI ? (kk & 1) : 0;
+  const int tile = (kk / ndir) % ntiles;
+  if (chain >= nbh) return;
+  const int NC = (int)a.NC;
+  const int64_t T = a.T, H = a.H;
+  const int64_t b = chain / H, h = chain % H;
+  const int dv = a.dv;
+  const int dv0 = tile * DT;
+  const bool rev = BI ? (dslot == 1) : (rev_single != 0);
+  const int slot = dslot;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool chain_wave = w < NT;
+  const int j = w % NT;  // 16-column sub-tile of this wave
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  const uint32_t HDB = (uint32_t)(H * DK * 2);  // token pitch of q, k (bytes)
+  const uint32_t HVB = (uint32_t)(H * dv * 2);  // token pitch of v
+  const uint32_t HOB = (uint32_t)(H * dv * 4);  // token pitch of out
+  const size_t nch = (size_t)a.B * a.H * NC;
+  const char* kbase = static_cast<const char*>(a.k) + (size_t)((b * T * H + h) * DK) * 2;
+  const char* qbase = static_cast<const char*>(a.q) + (size_t)((b * T * H + h) * DK) * 2;
+  const char* vbase = static_cast<const char*>(a.v) + (size_t)((b * T * H + h) * dv + dv0) * 2;
+  char* obase = reinterpret_cast<char*>(a.out) + (size_t)((b * T * H + h) * dv + dv0) * 4;
+  const char* trib = static_cast<const char*>(a.tri) + (size_t)chain * NC * L::TB;
+  const char* pqkb = static_cast<const char*>(a.pqk) + (size_t)chain * NC * L::TB;
+  const char* scb = reinterpret_cast<const char*>(a.sc) + ((size_t)slot * nch + (size_t)chain * NC) * C * 16;
+  const char* pdb = reinterpret_cast<const char*>(a.pdg) + ((size_t)slot * nch + (size_t)chain * NC) * pdg_stride(C) * 4;
+  const rsrc_t rnone = make_rsrc(obase, 0u);
+
+  auto chunk_at = [&](int s) { return rev ? NC - 1 - s : s; };
+  auto first_visit = [&](int s) {  // bidirectional: this workgroup visits chunk_at(s) first
+    const int so = NC - 1 - s;
+    return !BI || s < so || (s == so && !rev);
+  };
+
+  // ---- direct-to-LDS staging of one chunk: wave J of a role issues the
+  // slot's 1-KB loads J, J + NT, ... (compile-time lists, one per wave); the
+  // per-lane offsets within a chunk are computed once (voff, below) ----
+  constexpr int kMaxDma = (L::NDC > L::NDR ? L::NDC : L::NDR + NT - 1) / NT + 1;
+  uint32_t voff[kMaxDma];
+  auto make_voffs = [&](auto Jc, auto chain_role_c) {
+    constexpr int J = decltype(Jc)::value;
+    constexpr bool chain_role = decltype(chain_role_c)::value;
+    constexpr int N = chain_role ? L::NDC : L::NDR;
+    int n = 0;
+#pragma unroll
+    for (int i = J; i < N; i += NT, ++n) {
+      const int byte = i * 1024;
+      if constexpr (chain_role) {
+        voff[n] = byte < L::CT   ? dma_voff<DK, C, NT>(R_KTAU, (byte - L::CK) / 1024, lane, HDB, HVB)
+                  : byte < L::CV ? dma_voff<DK, C, NT>(R_TTAU, (byte - L::CT) / 1024, lane, HDB, HVB)
+                  : byte < L::CS ? dma_voff<DK, C, NT>(R_VAL, (byte - L::CV) / 1024, lane, HDB, HVB)
+                                 : 16u * lane;
+      } else {
+        voff[n] = byte < L::RP   ? dma_voff<DK, C, NT>(R_QNAT, (byte - L::RQ) / 1024, lane, HDB, HVB)
+                  : byte < L::RS ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RP) / 1024, lane, HDB, HVB)
+                                 : 16u * lane;
+      }
+    }
+  };
+  auto stage_part = [&](auto Jc, lds_u8* slotp, int c, auto chain_role_c) {
+    constexpr int J = decltype(Jc)::value;
+    constexpr bool chain_role = decltype(chain_role_c)::value;
+    const uint32_t rows = (uint32_t)(T - (int64_t)c * C);  // valid tokens from the chunk start (>= 1)
+    const rsrc_t rkq = make_rsrc((chain_role ? kbase : qbase) + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
+    const rsrc_t rtp = make_rsrc((chain_role ? trib : pqkb) + (size_t)c * L::TB, (uint32_t)L::TB);
+    const rsrc_t rsc = make_rsrc(scb + (size_t)c * C * 16, (uint32_t)(C * 16));
+    const rsrc_t rpd = make_rsrc(pdb + (size_t)c * pdg_stride(C) * 4, (uint32_t)((C + 4) * 4));
+    if constexpr (chain_role) {
+      const rsrc_t rv = make_rsrc(vbase + (size_t)c * C * HVB, (rows - 1) * HVB + DT * 2);
+      int n = 0;
+#pragma unroll
+      for (int i = J; i < L::NDC; i += NT, ++n) {
+        const int byte = i * 1024;
+        const rsrc_t r = byte < L::CT ? rkq : byte < L::CV ? rtp : byte < L::CS ? rv : byte < L::CP ? rsc : rpd;
+        dma16(r, slotp + byte, voff[n]);
+      }
+    } else {
+      int n = 0;
+#pragma unroll
+      for (int i = J; i < L::NDR; i += NT, ++n) {
+        const int byte = i * 1024;
+        const rsrc_t r = byte < L::RP ? rkq : byte < L::RS ? rtp : byte < L::RD ? rsc : rpd;
+        dma16(r, slotp + byte, voff[n]);
+      }
+    }
+  };
+  auto stage = [&](lds_u8* slotp, int c, auto chain_role_c) {
+    if (NT == 1 || j == 0) stage_part(std::integral_constant<int, 0>{}, slotp, c, chain_role_c);
+    else stage_part(std::integral_constant<int, NT - 1>{}, slotp, c, chain_role_c);
+  };
+  using ChainRole = std::true_type;
+  using ReadRole = std::false_type;
+
+  // ---- L2 prefetch of the tiles the value-tile workgroups of one sequence
+  // share (k and Tinv for the chain role, q and P for the readout role) ----
+  // Those workgroups run in step and ask for the same lines at the same time,
+  // so every one of them would wait for the same HBM fill.  Instead the waves
+  // of a role across the sequence's workgroups each touch every 8th 1-KB unit
+  // of the chunk three ahead (direct-to-LDS into a sink nobody reads): when
+  // the chunk is staged two steps later, its lines are in this XCD's L2.
+  // (Measured on MI355X at the 480p bidirectional shape: state chain 1.20 ->
+  // 1.09 ms; five or eight chunks ahead, or also the unshared value tile:
+  // slower.)  The loads are counted out of the step-end waits (kPf below).
+  // With the preparation running concurrently (a.ready set) only the raw k
+  // and q are prefetched: a prepared tile read before its ready flag could
+  // leave a stale line in this XCD's L2 (the preparation workgroup may run on
+  // another XCD), which the staging load would then hit.
+  constexpr int NU = (L::KB + L::TB) / 1024;  // 1-KB units of k (or q) and the triangle
+  constexpr int kPf = (NU + 7) / 8;           // prefetch loads per wave per step
+  const int pfbase = (tile * NT + j) & 7;
+  constexpr int NUK = L::KB / 1024;
+  const bool pf_prepared = a.ready == nullptr;  // prepared tiles are final before the chain starts
+  auto pf_unit = [&](int m) {
+    const int u = min(pfbase + 8 * m, NU - 1);
+    return (u < NUK || pf_prepared) ? u : u % NUK;
+  };
+  uint32_t pfoff[kPf];
+#pragma unroll
+  for (int m = 0; m < kPf; ++m) {
+    const int u = pf_unit(m);
+    const int byte = u * 1024 + 16 * lane;
+    pfoff[m] = u < NUK ? (uint32_t)((byte / L::KROWB) * HDB + (byte % L::KROWB)) : (uint32_t)(byte - L::KB);
+  }
+  auto prefetch = [&](int c, auto chain_role_c) {
+    constexpr bool chain_role = decltype(chain_role_c)::value;
+    const uint32_t rows = (uint32_t)(T - (int64_t)c * C);
+    const rsrc_t rkq = make_rsrc((chain_role ? kbase : qbase) + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
+    const rsrc_t rtp = make_rsrc((chain_role ? trib : pqkb) + (size_t)c * L::TB, (uint32_t)L::TB);
+#pragma unroll
+    for (int m = 0; m < kPf; ++m) dma16(pf_unit(m) < NUK ? rkq : rtp, pfs, pfoff[m]);
+  };
+  if (chain_wave) {
+    if (NT == 1 || j == 0) make_voffs(std::integral_constant<int, 0>{}, ChainRole{});
+    else make_voffs(std::integral_constant<int, NT - 1>{}, ChainRole{});
+  } else {
+    if (NT == 1 || j == 0) make_voffs(std::integral_constant<int, 0>{}, ReadRole{});
+    else make_voffs(std::integral_constant<int, NT - 1>{}, ReadRole{});
+  }
+
+  const size_t sbase = (((size_t)slot * a.B + b) * a.H + h) * (size_t)dv * DK;
+
+  if (chain_wave) {
+    // ======================= chain wave =======================
+    // state accumulators: tile srt = 2 ks + u, lane (l16, g4) element i holds
+    // S[dv0 + 16 j + l16][32 ks + 8 g4 + 4 u + i]
+    f32x4 Sacc[SRT];
+    const int col = dv0 + 16 * j + l16;
+#pragma unroll
+    for (int srt = 0; srt < SRT; ++srt) {
+      const int ks = srt >> 1, u = srt & 1;
+      Sacc[srt] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + sbase + (size_t)col * DK + 32 * ks + 8 * g4 + 4 * u)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // triangle masks of the diagonal k-chunk of each row tile (strict)
+    uint32_t tmask[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) make_mask(tmask[rt], tau(rt, l16), 32 * (rt >> 1) + 8 * g4, rev, false);
+
+    // ready flags of the concurrent preparation (0 = ready; without a.ready
+    // they read 0 through an empty resource)
+    const rsrc_t rrdy = a.ready ? make_rsrc(a.ready + (size_t)chain * NC, (uint32_t)NC * 4u) : rnone;
+    // A wait that expires (a preparation pass starved of the GPU) sets the
+    // state to NaN: every later product of the chain then carries NaN, so
+    // its outputs and final state can never be values computed from a stale
+    // workspace; later waits are skipped.
+    bool gave_up = false;
+    auto ensure_ready = [&](uint32_t fl, int c) {
+      if (__builtin_amdgcn_readfirstlane(fl) != 0u && !gave_up) {
+        int n = 0;
+        for (; n < kColReadyPollLimit; ++n) {
+          __builtin_amdgcn_s_sleep(2);
+          if (__builtin_amdgcn_readfirstlane(col_flag_fresh(rrdy, (uint32_t)c * 4u)) == 0u) break;
+        }
+        if (n == kColReadyPollLimit) {
+          gave_up = true;
+#pragma unroll
+          for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        }
+      }
+    };
+    auto flag_of = [&](int s) { return col_flag_fresh(rrdy, (uint32_t)chunk_at(min(s, NC - 1)) * 4u); };
+
+    // one chain step on chunk chunk_at(s): `cur` holds it, `nxt` receives chunk s + 1
+    auto chain_step = [&](const lds_u8* cur, lds_u8* nxt, lds_u8* xw, uint32_t& fl, int s) {
+      const lds_u8* Kt = cur + L::CK;
+      const lds_u8* Tt = cur + L::CT;
+      const lds_u8* Vt = cur + L::CV;
+      const lds_u8* Sc = cur + L::CS;
+      const lds_u8* Pd = cur + L::CP;
+      lds_u8* X = xw + j * L::XJ;
+      // k fragments of Y, read first (they are in LDS since the last step)
+      bf16x8 ka[RT][KS];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int rho = 16 * rt + l16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ka[rt][ks] = lds_frag(Kt + rho * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(rho)) << 4));
+      }
+      // stage chunk s + 1 (its prepared operands only once its flag is clear)
+      if (s + 1 < NC) {
+        ensure_ready(fl, chunk_at(s + 1));
+        stage(nxt, chunk_at(s + 1), ChainRole{});
+      }
+      mem_fence_compiler();
+      prefetch(chunk_at(min(s + 3, NC - 1)), ChainRole{});
+      mem_fence_compiler();
+      fl = flag_of(s + 3);  // consumed two steps on
+      mem_fence_compiler();
+
+      // entry state as bf16 operand fragments (dk 32 ks + 8 g4 .. + 7 of column l16)
+      bf16x8 sb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sb[ks] = pack8(Sacc[2 * ks], Sacc[2 * ks + 1]);
+        lds_put(X + L::XS + ks * 1024 + lane * 16, sb[ks]);
+      }
+      // Y = K S^T (rows in token order tau); the row tiles are independent
+      // accumulators, so each slice's products issue back to back
+      f32x4 y[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) y[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) y[rt] = M::mma(ka[rt][ks], sb[ks], y[rt]);
+      }
+      // X = beta (V - e^g rk Y); lane (l16, g4) of row tile rt holds tokens t0 .. t0 + 3
+      f32x4 x[RT], dsc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int t0 = 32 * (rt >> 1) + 8 * g4 + 4 * (rt & 1);
+        const v4s t4 = tr16(Vt + (t0 + (l16 >> 2)) * L::VROWB + (16 * j + 4 * (l16 & 3)) * 2);
+        bf16x4 v4;
+        __builtin_memcpy(&v4, &t4, 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 s4 = lds_f4(Sc + (t0 + i) * 16);  // {beta, e^g rk, e^g rq, e^(gn-g) rk}
+          x[rt][i] = s4[0] * ((float)v4[i] - s4[1] * y[rt][i]);
+          dsc[rt][i] = s4[3];
+        }
+      }
+      // Vnew = X + strict(Tinv) X (X exact in fp32; the strict part on bf16 operands)
+      bf16x8 xb[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) xb[kc] = pack8(x[2 * kc], x[2 * kc + 1]);
+      f32x4 vn[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 acc = x[rt];
+        const int rho = 16 * rt + l16;
+        const int kd = rt >> 1;  // k-chunk of the diagonal
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          if (rev ? kc < kd : kc > kd) continue;  // no element of this direction's triangle
+          bf16x8 ta = lds_frag(Tt + rho * L::TROWB + (((4 * kc + g4) ^ swz_t<C>(rho)) << 4));
+          if (kc == kd) ta = and_mask(ta, tmask[rt]);
+          acc = M::mma(ta, xb[kc], acc);
+        }
+        vn[rt] = acc;
+      }
+      // Vnew (fp32) for the readout; the scaled Vs (hi + lo) for the update
+      bf16x8 vsh[KC], vsl[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        *(lds_f32x4v*)(X + L::XV + kc * 2048 + lane * 32) = vn[2 * kc];
+        *(lds_f32x4v*)(X + L::XV + kc * 2048 + lane * 32 + 16) = vn[2 * kc + 1];
+        split8(vn[2 * kc] * dsc[2 * kc], vn[2 * kc + 1] * dsc[2 * kc + 1], vsh[kc], vsl[kc]);
+      }
+      // S = e^{g_last} S + K^T Vs: the transposed k fragment of state tile
+      // srt = 2 ks + u and k-chunk kc holds k[32 kc + 8 g4 + e][pi(srt, l16)]
+      const float gn = lds_f(Pd + C * 4);
+      // S e^{g_last}: exactly zero when the chunk's decay is (finite states;
+      // a NaN state from an expired wait keeps its NaN)
+      if (gn != 0.f || gave_up) {
+#pragma unroll
+        for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = Sacc[srt] * gn;
+      } else {
+#pragma unroll
+        for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+        for (int srt = 0; srt < SRT; ++srt) {
+          const int ks = srt >> 1, u = srt & 1;
+          bf16x8 kt;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int rho = 16 * (2 * kc + hh) + 4 * g4 + (l16 >> 2);  // row of token 32 kc + 8 g4 + 4 hh + l16 / 4
+            const int p = 4 * ks + (l16 & 3);
+            const v4s r = tr16(Kt + rho * L::KROWB + ((p ^ swz_kq<DK>(rho)) << 4) + 8 * u);
+            __builtin_memcpy(reinterpret_cast<char*>(&kt) + 8 * hh, &r, 8);
+          }
+          Sacc[srt] = M::mma(kt, vsh[kc], Sacc[srt]);
+          Sacc[srt] = M::mma(kt, vsl[kc], Sacc[srt]);
+        }
+      }
+    };
+
+    if (NC > 0) {
+      ensure_ready(flag_of(0), chunk_at(0));
+      stage(cs0, chunk_at(0), ChainRole{});
+      uint32_t fa = flag_of(1), fb = flag_of(2);
+      step_barrier<2>();  // the chunk-0 loads done (the two flag loads may remain)
+      int s = 0;
+      for (; s + 1 < NC; s += 2) {
+        chain_step(cs0, cs1, xs0, fa, s);
+        step_barrier<1 + kPf>();
+        chain_step(cs1, cs0, xs1, fb, s + 1);
+        step_barrier<1 + kPf>();
+      }
+      if (s < NC) {
+        chain_step(cs0, cs1, xs0, fa, s);
+        step_barrier<1 + kPf>();
+        ++s;
+      }
+      // the readout's last step
+      step_barrier<1 + kPf>();
+    }
+    // final state
+    if (a.state_out) {
+#pragma unroll
+      for (int srt = 0; srt < SRT; ++srt) {
+        const int ks = srt >> 1, u = srt & 1;
+        *reinterpret_cast<f32x4*>(a.state_out + sbase + (size_t)col * DK + 32 * ks + 8 * g4 + 4 * u) = Sacc[srt];
+      }
+    }
+  } else {
+    // ======================= readout wave =======================
+    // P masks of the diagonal k-chunk of each 16-token output tile (the self
+    // terms kept unless this direction reads before the token's own write)
+    const bool self = !(rev ? a.excl_rev : a.excl_fwd);
+    uint32_t pmask[RT][4], dmask[RT][4];  // dmask: the element of this lane's own token (none: all zero)
+#pragma unroll
+    for (int tt = 0; tt < RT; ++tt) {
+      make_mask(pmask[tt], 16 * tt + l16, 32 * (tt >> 1) + 8 * g4, rev, self);
+      const int e0 = 16 * tt + l16 - (32 * (tt >> 1) + 8 * g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dmask[tt][i] = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (self && e == e0) dmask[tt][e / 2] |= 0xffffu << (16 * (e % 2));
+    }
+    const rsrc_t ro = make_rsrc(obase, (uint32_t)(T - 1) * HOB + DT * 4);
+    const uint32_t out_lane = (uint32_t)(16 * j + 4 * g4) * 4u;
+    auto out_off = [&](int c, int tt) { return (uint32_t)(c * C + 16 * tt + l16) * HOB + out_lane; };
+    bool pq_gave_up = false;
+
+    // partials of a bidirectional second visit, loaded a step ahead
+    auto load_partial = [&](f32x4 (&pq)[RT], int s) {
+      if constexpr (BI) {
+        const bool want = s < NC && !first_visit(s);
+        const rsrc_t rp = want ? ro : rnone;
+        const int c = chunk_at(min(s, NC - 1));
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt) pq[tt] = bload16(rp, out_off(c, tt));
+      }
+    };
+
+    // readout of visit sp (chunk chunk_at(sp)) from slot `cur` and exchange `xr`
+    auto read_step = [&](const lds_u8* cur, lds_u8* nxt, const lds_u8* xr, f32x4 (&pq)[RT],
+                         f32x4 (&pq_next)[RT], int s) {
+      // stage chunk s's q, P and scales (prepared: the chain waves waited for
+      // its flag a step ago); then the partials of visit s
+      if (s < NC) stage(nxt, chunk_at(s), ReadRole{});
+      mem_fence_compiler();
+      prefetch(chunk_at(min(s + 3, NC - 1)), ReadRole{});
+      mem_fence_compiler();
+      load_partial(pq_next, s);
+      mem_fence_compiler();
+      if (s == 0) return;
+      const int sp = s - 1;
+      const int c = chunk_at(sp);
+      const lds_u8* Qt = cur + L::RQ;
+      const lds_u8* Pt = cur + L::RP;
+      const lds_u8* Sc = cur + L::RS;
+      const lds_u8* Pd = cur + L::RD;
+      const lds_u8* X = xr + j * L::XJ;
+      bf16x8 sr[KS], vh[KC], vl[KC];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sr[ks] = lds_frag(X + L::XS + ks * 1024 + lane * 16);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const f32x4 v0 = *(const lds_f32x4v*)(X + L::XV + kc * 2048 + lane * 32);
+        const f32x4 v1 = *(const lds_f32x4v*)(X + L::XV + kc * 2048 + lane * 32 + 16);
+        split8(v0, v1, vh[kc], vl[kc]);
+      }
+      const bool add = BI && !first_visit(sp);
+#pragma unroll
+      for (int tt = 0; tt < RT; ++tt) {
+        const int t = 16 * tt + l16;  // this lane's token
+        // Z^T = S Q^T
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 qb = lds_frag(Qt + t * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(t)) << 4));
+          z = M::mma(sr[ks], qb, z);
+        }
+        const float zs = lds_f(Sc + t * 16 + 8);  // e^g rq of the token
+        f32x4 o = z * zs;
+        // + Vnew^T P^T
+        const int kd = tt >> 1;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          if (rev ? kc < kd : kc > kd) continue;
+          bf16x8 pb = lds_frag(Pt + t * L::TROWB + (((4 * kc + g4) ^ swz_t<C>(t)) << 4));
+          if (kc == kd) pb = and_mask(pb, pmask[tt]);
+          o = M::mma(vh[kc], pb, o);
+          o = M::mma(vl[kc], pb, o);
+          if (kc == kd) {
+            // the self term's remainder (P holds it rounded): a diagonal product with Vnew's hi part
+            const bf16 rmd = (bf16)lds_f(Pd + t * 4);
+            bf16x8 dg;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dg[e] = rmd;
+            o = M::mma(vh[kc], and_mask(dg, dmask[tt]), o);
+          }
+        }
+        if constexpr (BI) {
+          if (add) {
+            // the first visitor's partial: re-read past the L1 cache while any
+            // of it still holds the fill pattern
+            if (__any(col_any_unwritten(pq[tt])) && !pq_gave_up) {
+              f32x4 q = pq[tt];
+              int n = 0;
+              for (; n < kColPollLimit; ++n) {
+                __builtin_amdgcn_s_sleep(2);
+                q = col_load_fresh(ro, out_off(c, tt));
+                if (!__any(col_any_unwritten(q))) break;
+              }
+              pq_gave_up = n == kColPollLimit;
+              pq[tt] = q;
+            }
+            o += pq[tt];
+          }
+        }
+        bstore16(ro, out_off(c, tt), o);
+      }
+    };
+
+    f32x4 pqa[RT], pqb[RT];
+#pragma unroll
+    for (int tt = 0; tt < RT; ++tt) pqa[tt] = pqb[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // loads a readout wave leaves in flight at a step's end: its partials
+    // (bidirectional) and its output stores
+    constexpr int kTail = (BI ? 2 : 1) * RT + kPf;
+    if (NC > 0) {
+      step_barrier<0>();  // the chain waves' prologue
+      // step 0 stages chunk 0 and loads the partials of visit 0; no readout yet
+      read_step(rs1, rs0, xs1, pqb, pqa, 0);
+      step_barrier<(BI ? RT : 0) + kPf>();
+      // then steps 1 .. NC: odd steps read slot 0 and stage into slot 1
+      int s = 1;
+      for (; s + 1 <= NC; s += 2) {
+        read_step(rs0, rs1, xs0, pqa, pqb, s);
+        step_barrier<kTail>();
+        read_step(rs1, rs0, xs1, pqb, pqa, s + 1);
+        step_barrier<kTail>();
+      }
+      if (s <= NC) {
+        read_step(rs0, rs1, xs0, pqa, pqb, s);
+        step_barrier<kTail>();
+      }
+    }
+  }
+}
+
+template <int DK, int C, int NT, bool BI>
+hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query) {
+  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&column_chain_kernel<DK, C, NT, BI>));
+  const int ntiles = a.dv / (16 * NT);
+  const int nbh = (int)(a.B * a.H);
+  const unsigned nblocks = (unsigned)chain_blocks(nbh, a.dv, NT, BI ? 2 : 1);
+  hipLaunchKernelGGL((column_chain_kernel<DK, C, NT, BI>), dim3(nblocks), dim3(128 * NT), 0, stream, a, rev_single,
+                     ntiles, nbh);
+  return hipGetLastError();
+}
+
+#define GDN_INST_COL(DK, C, NT, BI) \
+  template hipError_t launch_column_chain<DK, C, NT, BI>(const ScanArgs&, int, hipStream_t, hipFuncAttributes*);
+#define GDN_INST_COL_D(DK, C, NT) GDN_INST_COL(DK, C, NT, false) GDN_INST_COL(DK, C, NT, true)
+#define GDN_INST_COL_N(DK, C) GDN_INST_COL_D(DK, C, 1) GDN_INST_COL_D(DK, C, 2)
+GDN_INST_COL_N(64, 32)
+GDN_INST_COL_N(64, 64)
+GDN_INST_COL_N(128, 32)
+GDN_INST_COL_N(128, 64)
+
+}  // namespace gdn

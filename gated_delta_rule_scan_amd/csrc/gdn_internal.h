@@ -31,6 +31,13 @@ hipError_t launch_clear_ready(unsigned* ready, int64_t n, hipStream_t stream);
 template <typename MT, int DK, int C, int NT, bool BI>
 hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query);
 
+// The state chain for bf16 operands: NT chain waves each own 16 value columns
+// of the state over every dk, NT readout waves compute the chunk outputs a
+// step later; operands are staged by direct buffer-to-LDS loads.  Same
+// arguments, grid and results contract as launch_chain<bf16, ...>.
+template <int DK, int C, int NT, bool BI>
+hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query);
+
 // Workgroups of a state-chain launch (one per value tile, direction and
 // sequence; sequences padded to a multiple of eight).
 inline int64_t chain_blocks(int64_t nbh, int dv, int NT, int dirs) { return (nbh + 7) / 8 * 8 * (dv / (16 * NT)) * dirs; }
