@@ -173,8 +173,9 @@ __device__ __forceinline__ void store_split4(bf16* hi_p, bf16* lo_p, f32x4 x) {
 
 
 // All-ones NaN: the value the preparation kernel fills `out` with before a
-// bidirectional scan, meaning "not written yet".  Arithmetic never produces
-// it (generated NaNs are the canonical quiet NaN).
+// bidirectional scan, meaning "not written yet".  First visitors store their
+// readouts with canonical NaNs (an input NaN's payload could otherwise carry
+// the pattern through the arithmetic), so they never produce it.
 constexpr uint32_t kUnwritten = 0xFFFFFFFFu;
 
 __device__ __forceinline__ bool any_unwritten(f32x4 p) {
@@ -500,6 +501,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           }
         }
         if (add) acc += sp.pq[j];
+        else if (BI) acc = canonical_nans(acc);  // a first visit: never the fill pattern
         bstore16(rs, oo + ct * 64, acc);
       }
     }

@@ -157,7 +157,8 @@ __device__ __forceinline__ uint32_t dma_voff(int kind, int ii, int lane, uint32_
 }
 
 // All-ones NaN: the fill the preparation kernel leaves in `out` before a
-// bidirectional scan ("not written yet"); arithmetic never produces it.
+// bidirectional scan ("not written yet"); first visitors store their
+// readouts with canonical NaNs, so they never produce it.
 constexpr uint32_t kColUnwritten = 0xFFFFFFFFu;
 constexpr int kColPollLimit = 1 << 23;      // about a second of re-reads
 constexpr int kColReadyPollLimit = 1 << 23;
@@ -688,6 +689,8 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
               pq[tt] = q;
             }
             o += pq[tt];
+          } else {
+            o = canonical_nans(o);  // a first visit: never the fill pattern
           }
         }
         bstore16(ro, out_off(c, tt), o);

@@ -133,6 +133,16 @@ __device__ __forceinline__ void bstore4_agent(rsrc_t r, uint32_t off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, (int)off, 0, kAgentScope);
 }
 
+// Every NaN replaced by the canonical quiet NaN.  A bidirectional scan's
+// first visitor stores its readout through this, so its stores can never
+// carry the all-ones "not written yet" pattern, whatever NaN payload an
+// input held.
+__device__ __forceinline__ f32x4 canonical_nans(f32x4 o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = o[i] != o[i] ? __builtin_nanf("") : o[i];
+  return o;
+}
+
 // A matrix-core fragment (8 consecutive elements) at byte offset `off`.
 template <typename MT>
 __device__ __forceinline__ typename Mma<MT>::frag bload_frag(rsrc_t r, uint32_t off) {

@@ -125,3 +125,39 @@ def test_bitwise_repeatable(direction):
     o1, s1 = run_gpu(x, direction)
     o2, s2 = run_gpu(x, direction)
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_ones_nan_input_finishes_promptly(dtype):
+    """An input NaN with every bit set (the pattern a bidirectional scan's
+    combine uses for "not written yet") is out of contract, but must not make
+    the second visitor of a chunk wait for its bounded poll: first visitors
+    store canonical NaNs.  41 chunks, bidirectional; the call returns in well
+    under the ~1 s a single expired wait would take, and the outputs the NaN
+    reaches are NaN."""
+    import time
+
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    from gdn_testutil import to_torch
+
+    w = synth.Workload("nan payload", 1, 2, 64 * 40 + 17, 64, 64, dtype, "bi", 3.0, 0.0, 51)
+    x = synth.generate(w)
+    v = x["v"].copy()
+    if dtype == "f32":
+        v.view(np.uint32)[0, 100, :, :] = 0xFFFFFFFF
+    else:
+        v.view(np.uint16)[0, 100, :, :] = 0xFFFF
+    d = {k: to_torch(a) for k, a in x.items()}
+    d["v"] = to_torch(v)
+    gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, "bi")  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out, s = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, "bi")
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert dt < 0.3, f"call took {dt:.3f} s: a combine wait expired"
+    o = out.cpu().numpy()
+    # the forward memory carries the NaN from token 100 on, the reverse one up to it
+    assert np.all(np.isnan(o[0, 100:])) and np.all(np.isnan(o[0, :101]))
