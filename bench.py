@@ -9,8 +9,14 @@ state and output, forward + reverse scans summed.
 
 Prints ONE JSON line with tokens/s (B*T tokens per step), the algorithmic
 TFLOP/s and fraction of the bf16 matrix-core peak, the per-kernel roofline of
-the dominant kernel measured live with HIP events, and the double-precision
+the dominant kernel measured live with HIP events (algorithmic bytes = the
+boundary tensors, each once; the workspace is reported apart), the error of
+sampled (batch, head) chains against the double-precision oracle, and that
 oracle timed on the host on a bounded sample of the same workload.
+
+The streaming workload (stream480) is timed as its rollout: 21 in-place calls
+of one latent frame each (1560 tokens, the state carried in place), eagerly
+and as one captured HIP graph replayed; one step = one rollout.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload bidir480]
 """
@@ -48,19 +54,72 @@ def path_bytes(w, xs: int) -> float:
     return th * per_th + states
 
 
-def kernel_bytes(w, xs: int, C: int) -> dict:
-    """Algorithmic bytes of each kernel: its own inputs and outputs, each once."""
+def kernel_bytes(w, xs: int) -> dict:
+    """Algorithmic bytes of each kernel, boundary tensors only, each once: the
+    preparation pass reads q, k and the gates; the chain reads q, k, v and the
+    states and writes out and the final states.  Workspace traffic (the
+    prepared triangles and scales) is excluded and reported apart."""
     th = w.B * w.T * w.H
-    chunk_ops = 2 * C * xs                      # Tinv and decayed QK^T (C x C per chunk) per token
-    scal = w.dirs * 16                          # per-token scales, per direction
-    prep = th * (2 * w.dk * xs + w.dirs * 8 + chunk_ops + scal)
     states = w.dirs * w.B * w.H * w.dv * w.dk * 4 * (2 if w.state_std > 0 else 1)
-    chain = th * ((2 * w.dk + w.dv) * xs + chunk_ops + scal + w.dv * 4) + states
-    return {"prep": prep, "chain": chain}
+    return {"prep": th * (2 * w.dk * xs + w.dirs * 8),
+            "chain": th * ((2 * w.dk + w.dv) * xs + w.dv * 4) + states,
+            "path": path_bytes(w, xs)}
+
+
+def chain_kernel_name(dtype: str) -> str:
+    """bf16 operands run the column-owning chain, fp32 operands the two-role one."""
+    return "column_chain_kernel" if dtype == "bf16" else "chain_kernel"
+
+
+def host_cores():
+    """(threads to use, cores visible): the affinity mask, capped by the
+    cgroup CPU quota and by OMP_NUM_THREADS when either is set (the host's
+    own thread budget)."""
+    visible = len(os.sched_getaffinity(0))
+    avail = visible
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            avail = min(avail, max(1, int(quota) // int(period)))
+    except (OSError, ValueError):
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        avail = min(avail, int(omp))
+    return avail, visible
+
+
+def sampled_parity(w, x, out, s_out, direction, erase=True, exclusive="none", threads=None) -> dict:
+    """max |gpu - oracle| / RMS(oracle) over two (batch, head) chains computed
+    in full by the oracle (every token, both directions when bidirectional,
+    and the final states).  Chains are independent, so this is the oracle
+    restricted to those chains."""
+    import numpy as np
+
+    import oracle
+
+    heads = list(dict.fromkeys([(0, 0), (w.B - 1, w.H - 1)]))
+    t0 = time.perf_counter()
+    ro, rs = oracle.forward_heads(x, heads, direction, nthreads=threads, erase=erase, exclusive=exclusive)
+    dt = time.perf_counter() - t0
+
+    def rel(got, ref):
+        ref = np.asarray(ref, np.float64)
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        return float(np.max(np.abs(np.asarray(got, np.float64) - ref))) / max(rms, 1e-30)
+
+    o = out.cpu().numpy()
+    so = s_out.cpu().numpy()
+    eo = max(rel(o[b, :, h], ro[i]) for i, (b, h) in enumerate(heads))
+    es = max(rel(so[:, b, h], rs[:, i]) for i, (b, h) in enumerate(heads))
+    return {"heads": [list(h) for h in heads], "out_max_err_over_rms": eo, "state_max_err_over_rms": es,
+            "tol": 2e-2 if w.dtype == "bf16" else 1e-4, "finite": bool(np.all(np.isfinite(o))),
+            "oracle_seconds": round(dt, 2)}
 
 
 KERNEL_SOURCES = {
     "chain_kernel": ["gdn_chain.hip", "gdn_common.h"],
+    "column_chain_kernel": ["gdn_colchain.hip", "gdn_common.h"],
     "chunk_prep_kernel": ["gdn_prep.hip", "gdn_common.h"],
     "vda_frame_kernel": ["gdn_vda.hip", "gdn_common.h"],
     "vda_chain_bf16_kernel": ["gdn_vda.hip", "gdn_common.h"],
@@ -132,7 +191,7 @@ def cpu_baseline(w, x, target_s: float, erase: bool = True, exclusive: str = "no
     same operator the GPU leg runs."""
     import oracle
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads, visible = host_cores()
     cal_T = min(w.T, 1024)
     t0 = time.perf_counter()
     oracle.forward_heads({"q": x["q"][:, :cal_T], "k": x["k"][:, :cal_T], "v": x["v"][:, :cal_T],
@@ -152,7 +211,8 @@ def cpu_baseline(w, x, target_s: float, erase: bool = True, exclusive: str = "no
     thd = n_chains * Ts / dt                                # token-head-directions per second
     used = min(threads, n_chains)
     what = "the whole workload" if Ts == w.T else f"the first {Ts} of {w.T} tokens of every chain"
-    return {"value": thd / (w.H * w.dirs), "unit": "tokens/s", "cores": used, "kind": "oracle",
+    return {"value": thd / (w.H * w.dirs), "unit": "tokens/s", "cores": used, "cores_available": threads,
+            "cores_visible": visible, "kind": "oracle",
             "sample": f"{what}: {len(heads)} heads x {w.dirs} direction(s), {used} threads, {dt:.1f} s; "
                       f"tokens/s = token-head-directions/s / (H*dirs)",
             "seconds": round(dt, 2)}
@@ -304,6 +364,7 @@ def main() -> int:
     ap.add_argument("--dv-tile", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle check of sampled chains")
     ap.add_argument("--serial", action="store_true", help="keep the preparation pass before the chain (no overlap)")
     ap.add_argument("--no-erase", action="store_true",
                     help="time the erase-free variant (gated linear attention, GDN_OPT_NO_ERASE) instead of the delta rule")
@@ -334,18 +395,10 @@ def main() -> int:
     if args.vda:
         return run_vda(args, w)
     if w.frame:
-        raise SystemExit("the streaming workload is exercised by the tests; bench one-call workloads")
+        return run_stream(args, w)
     xs = 2 if w.dtype == "bf16" else 4
     x = synth.generate(w)
-
-    def dev(a):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    d = {k: dev(v) for k, v in x.items()}
+    d = {k: _dev(v) for k, v in x.items()}
     out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
     s_out = torch.empty((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
     nws = gdn.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.direction, args.chunk, args.dv_tile)
@@ -362,8 +415,8 @@ def main() -> int:
     torch.cuda.synchronize()
     K = args.steps
     # per-kernel durations: K calls, each with four HIP events recorded by the
-    # library (prep start/end on its stream, chain start/end on the caller's
-    # stream)
+    # library (prep start/end on the stream prep runs on, chain start/end on
+    # the caller's stream)
     ev = HipEvents(4 * K)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -386,6 +439,8 @@ def main() -> int:
     ms_step = start.elapsed_time(stop) / K
     prep_ms = sum(ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)) / K
     chain_ms = sum(ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)) / K
+    # one call's span, prep start to chain end (the library's own events)
+    spans = sorted(max(ev.elapsed_ms(4 * i, 4 * i + 3), ev.elapsed_ms(4 * i + 2, 4 * i + 3)) for i in range(K))
     # the chain started before the preparation pass ended: the two ran concurrently
     concurrent = all(ev.elapsed_ms(4 * i + 1, 4 * i + 2) < 0 for i in range(K))
     ev.close()
@@ -401,12 +456,14 @@ def main() -> int:
     th_dirs = w.B * w.T * w.H * w.dirs
     flops = th_dirs * flops_per_token_head_dir(w.dk, w.dv)
     tflops = flops / (ms_step * 1e-3) / 1e12
-    pbytes = path_bytes(w, xs)
-    kb = kernel_bytes(w, xs, C)
+    kb = kernel_bytes(w, xs)
     kt = {"prep": prep_ms, "chain": chain_ms}
     dom = max(kt, key=kt.get)
-    dom_name = "chain_kernel" if dom == "chain" else "chunk_prep_kernel"
-    achieved = kb[dom] / (kt[dom] * 1e-3) / 1e9
+    dom_name = chain_kernel_name(w.dtype) if dom == "chain" else "chunk_prep_kernel"
+    # the dominant kernel's roofline: the chain moves every boundary tensor but
+    # the gates, so the path's boundary bytes are its algorithmic bytes
+    dom_bytes = kb["path"] if dom == "chain" else kb["prep"]
+    achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
     peak_mfma = MI355X_BF16_TFLOPS if w.dtype == "bf16" else MI355X_FP32_TFLOPS
     res = {
         "metric": "gated-delta scan tokens/s + TFLOP/s (% MFMA peak) at 480p latent, 1 MI355X",
@@ -429,21 +486,162 @@ def main() -> int:
                    "inputs": "seeded synthetic video-latent-shaped (synth.WORKLOADS)"},
         "tflops": tflops,
         "mfma_frac": tflops / peak_mfma,
-        "path_hbm_gbs": pbytes / (ms_step * 1e-3) / 1e9,
-        "path_hbm_frac": pbytes / (ms_step * 1e-3) / 1e9 / MI355X_HBM_GBS,
+        "path_bytes": kb["path"],
+        "path_hbm_gbs": kb["path"] / (ms_step * 1e-3) / 1e9,
+        "path_hbm_frac": kb["path"] / (ms_step * 1e-3) / 1e9 / MI355X_HBM_GBS,
         "kernels_ms": {"chunk_prep": prep_ms, "state_chain": chain_ms},
+        "call_ms_median": spans[K // 2], "call_ms_min": spans[0],
         "ms_per_step_with_kernel_events": ms_step_events,
         "roofline": {"kernel": dom_name, "bound": "hbm",
                      "achieved": achieved, "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": achieved / MI355X_HBM_GBS,
                      # the committed counters were taken with the default options
                      "traffic": (measured_traffic(dom_name, args.workload)
-                                 if not args.no_erase and args.exclusive == "none" else None),
-                     "alg_bytes_per_launch": kb[dom],
+                                 if not args.no_erase and args.exclusive == "none" and not args.chunk
+                                 and not args.dv_tile else None),
+                     "alg_bytes_per_launch": dom_bytes,
+                     "workspace_bytes_per_launch": nws,
                      "avg_launch_ms": kt[dom], "source_hash": kernel_source_hash(dom_name)},
         "wall_s_timed": wall,
     }
+    if not args.no_parity:
+        res["parity"] = sampled_parity(w, x, out, s_out, w.direction, erase=not args.no_erase,
+                                       exclusive=args.exclusive, threads=host_cores()[0])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, erase=not args.no_erase, exclusive=args.exclusive)
+        res["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_stream(args, w) -> int:
+    """The streaming rollout: one call per latent frame (w.frame tokens), the
+    state carried in place (state_in is state_out), as a causal video model
+    generating frame by frame calls it.  Inputs are cut into per-frame device
+    tensors beforehand; each step is the whole rollout, timed eagerly and as
+    one captured HIP graph replayed (the library takes its serial order under
+    capture).  Per-frame latency = rollout time / frames."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    import synth
+
+    xs = 2 if w.dtype == "bf16" else 4
+    x = synth.generate(w)
+    fr = w.frame
+    bounds = [(f0, min(w.T, f0 + fr)) for f0 in range(0, w.T, fr)]
+    NF = len(bounds)
+    frames = []
+    for f0, f1 in bounds:
+        frames.append({k: _dev(x[k][:, f0:f1]) for k in ("q", "k", "v")} |
+                      {k: _dev(x[k][:, :, f0:f1]) for k in ("log_alpha", "beta")})
+    s0 = _dev(x["state_in"]) if x["state_in"] is not None else None
+    state = torch.zeros((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+    outs = [torch.empty((w.B, f1 - f0, w.H, w.dv), dtype=torch.float32, device="cuda") for f0, f1 in bounds]
+    nws = gdn.workspace_bytes(w.B, fr, w.H, w.dk, w.dv, w.dtype, w.direction)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+    def reset():
+        if s0 is not None:
+            state.copy_(s0)
+        else:
+            state.zero_()
+
+    def rollout(evs=None):
+        for i, f in enumerate(frames):
+            gdn.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], state, w.direction, out=outs[i],
+                        state_out=state, workspace=ws, timing_events=None if evs is None else evs.ptr(4 * i))
+
+    for _ in range(max(1, args.warmup)):
+        reset()
+        rollout()
+    torch.cuda.synchronize()
+    K = args.steps
+    # per-kernel durations over one rollout (library events per call)
+    ev = HipEvents(4 * NF)
+    reset()
+    rollout(ev)
+    torch.cuda.synchronize()
+    prep_ms = sum(ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(NF)) / NF
+    chain_ms = sum(ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(NF)) / NF
+    ev.close()
+    # eager: K rollouts, the state reset (a 1-kernel fill or copy) before each
+    t_eager = 0.0
+    for _ in range(K):
+        reset()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        rollout()
+        b.record()
+        torch.cuda.synchronize()
+        t_eager += a.elapsed_time(b)
+    ms_eager = t_eager / K
+    # the rollout captured once as a HIP graph, replayed K times
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rollout()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rollout()
+    t_graph = 0.0
+    for _ in range(K):
+        reset()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t_graph += a.elapsed_time(b)
+    ms_graph = t_graph / K
+    # the graph's last replay is a full rollout from the initial state
+    out = torch.cat(outs, dim=1)
+    tokens = w.B * w.T
+    flops = tokens * w.H * w.dirs * flops_per_token_head_dir(w.dk, w.dv)
+    kb = kernel_bytes(w, xs)
+    # per frame: the boundary tensors of one call (the carried state read and written once)
+    sb = w.dirs * w.B * w.H * w.dv * w.dk * 4
+    fb = (kb["path"] - sb * (2 if w.state_std > 0 else 1)) / NF + 2 * sb
+    kt = {"prep": prep_ms, "chain": chain_ms}
+    dom = max(kt, key=kt.get)
+    dom_name = chain_kernel_name(w.dtype) if dom == "chain" else "chunk_prep_kernel"
+    dom_bytes = fb if dom == "chain" else kb["prep"] / NF
+    achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
+    res = {
+        "metric": "gated-delta scan tokens/s + TFLOP/s (% MFMA peak) at 480p latent, 1 MI355X",
+        "value": tokens / (ms_eager * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_eager, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "frame": fr, "frames": NF, "dk": w.dk,
+                   "dv": w.dv, "direction": w.direction, "chunk": 64, "calls_per_step": NF,
+                   "state": "carried in place across the calls",
+                   "inputs": "seeded synthetic video-latent-shaped (synth.WORKLOADS)"},
+        "ms_per_frame_eager": ms_eager / NF,
+        "ms_per_frame_graph": ms_graph / NF,
+        "tokens_per_s_graph": tokens / (ms_graph * 1e-3),
+        "tflops": flops / (ms_eager * 1e-3) / 1e12,
+        "kernels_ms_per_frame": {"chunk_prep": prep_ms, "state_chain": chain_ms},
+        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": achieved, "peak": MI355X_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / MI355X_HBM_GBS, "traffic": None,
+                     "alg_bytes_per_launch": dom_bytes, "workspace_bytes_per_launch": nws,
+                     "avg_launch_ms": kt[dom], "source_hash": kernel_source_hash(dom_name)},
+    }
+    if not args.no_parity:
+        res["parity"] = sampled_parity(w, x, out, state, w.direction, threads=host_cores()[0])
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
         res["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]
     print(json.dumps(res), flush=True)
     return 0
