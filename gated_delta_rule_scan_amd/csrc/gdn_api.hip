@@ -90,7 +90,7 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   pl->dirs = pl->fwd_on + pl->rev_on;
   pl->NC = (p->T + C - 1) / C;
   pl->mt = p->dtype == GDN_DTYPE_BF16 ? 2 : 4;
-  pl->ws = ws_layout(p->B * p->H, pl->NC, C, pl->dirs, pl->mt);
+  pl->ws = ws_layout(p->B * p->H, pl->NC, C, pl->dirs, pl->mt, p->dv);
   return GDN_OK;
 }
 
@@ -140,7 +140,8 @@ bool side_stream(int dev, SideStream** out) {
 // and preparation traffic beside it slows it down.  Measured on MI355X with
 // the bf16 column chain: 720p causal (128 chain workgroups on 256 units)
 // 1.90 ms concurrent against 2.14 ms serial; 720p bidirectional (192) 4.65
-// against 4.25 ms; 480p bidirectional (256) runs serial.
+// against 4.25 ms; 480p bidirectional (256) runs serial.  (Bidirectional
+// bf16 scans always run serial; see forward_impl.)
 //
 // Safe because the chain waits only for chunks the preparation pass
 // publishes, and a preparation workgroup can always be scheduled: there are
@@ -262,12 +263,16 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   }
   a.B = B; a.T = T; a.H = H; a.NC = pl.NC; a.dv = (int)dv;
   a.fwd_on = pl.fwd_on; a.rev_on = pl.rev_on; a.dirs = pl.dirs;
-  a.zero_out = pl.dirs == 2;
+  const bool bf = p->dtype == GDN_DTYPE_BF16;
+  // bidirectional combine: fp32 operands recognise an unwritten partial by
+  // the preparation kernel's fill of `out`; bf16 operands by per-chunk flags
+  // that the preparation kernel clears
+  a.zero_out = pl.dirs == 2 && !bf;
+  if (pl.dirs == 2 && bf && need_ws) a.part_flags = reinterpret_cast<unsigned*>(ws + pl.ws.pfl);
   a.erase = (p->options & GDN_OPT_NO_ERASE) ? 0 : 1;
   a.excl_fwd = (p->options & GDN_OPT_EXCLUSIVE_FORWARD) ? 1 : 0;
   a.excl_rev = (p->options & GDN_OPT_EXCLUSIVE_REVERSE) ? 1 : 0;
 
-  const bool bf = p->dtype == GDN_DTYPE_BF16;
   if (pl.NT == 0) pl.NT = pick_tiles(B * H, dv, pl.dirs);
   // bidirectional: one workgroup per direction, readouts accumulated into
   // the output the preparation kernel filled; single direction: told whether
@@ -293,8 +298,11 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   // graph orders its nodes only by their dependencies, so nothing would make
   // the preparation node start while the chain node waits on its flags, and
   // no library stream or event may be created or joined into a capture.
+  // A bidirectional bf16 scan always takes the serial order: its chain reads
+  // the combine flags ahead of the chunk-ready flags, so they must be clear
+  // before it starts.
   const bool concurrent = pl.NC > 0 && !serial_only && !(p->options & GDN_OPT_SERIAL) && !capturing(stream) &&
-                          may_overlap(chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
+                          !a.part_flags && may_overlap(chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
   if (concurrent) {
     int dev = 0;
     SideStream* side = nullptr;

@@ -44,9 +44,23 @@
 // arrays, so the compiler can tell every LDS read from the loads in flight.
 //
 // Bidirectional scans run the two directions in separate workgroups (ids 8
-// apart, on one XCD); the first visitor of a chunk stores its readout and the
-// second adds it, recognising an unwritten partial by the preparation kernel's
-// fill pattern, as in the fp32 chain kernel.
+// apart).  Chunk c is visited first by the direction that reaches it at the
+// lower step index (the forward one for the first half of the chunks, the
+// reverse one for the second half): that visitor stores its readout, the
+// other adds it to its own.  A readout wave signals its stored partial
+// through a flag per chunk and 16 columns (cleared by the preparation
+// kernel, which has finished before the chain starts):
+//   * the flag of visit v is stored at readout step v + 3, without a wait:
+//     the barrier that ends step v + 2 already counted the stores of step
+//     v + 1 out (each step issues its loads before its stores);
+//   * a second visitor loads the flag two steps before its readout and the
+//     partial one step before if the flag was set by then; otherwise it polls
+//     the flag (bounded) and loads the partial at the readout;
+//   * every readout wave, on reaching its first second visit, waits for its
+//     own stores and publishes all its flags.  First visits precede second
+//     visits in every workgroup, so no wave ever waits while holding an
+//     unpublished flag, and neither direction can wait for the other in a
+//     cycle.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -156,17 +170,8 @@ __device__ __forceinline__ uint32_t dma_voff(int kind, int ii, int lane, uint32_
   return (uint32_t)b;
 }
 
-// All-ones NaN: the fill the preparation kernel leaves in `out` before a
-// bidirectional scan ("not written yet"); first visitors store their
-// readouts with canonical NaNs, so they never produce it.
-constexpr uint32_t kColUnwritten = 0xFFFFFFFFu;
 constexpr int kColPollLimit = 1 << 23;      // about a second of re-reads
 constexpr int kColReadyPollLimit = 1 << 23;
-
-__device__ __forceinline__ bool col_any_unwritten(f32x4 p) {
-  return __float_as_uint(p[0]) == kColUnwritten || __float_as_uint(p[1]) == kColUnwritten ||
-         __float_as_uint(p[2]) == kColUnwritten || __float_as_uint(p[3]) == kColUnwritten;
-}
 
 __device__ __forceinline__ f32x4 col_load_fresh(rsrc_t r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 17);
@@ -453,11 +458,12 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) ka[rt][ks] = lds_frag(Kt + rho * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(rho)) << 4));
       }
-      // stage chunk s + 1 (its prepared operands only once its flag is clear)
-      if (s + 1 < NC) {
-        ensure_ready(fl, chunk_at(s + 1));
-        stage(nxt, chunk_at(s + 1), ChainRole{});
-      }
+      // stage chunk s + 1 (its prepared operands only once its flag is
+      // clear); the last step restages the last chunk into the idle slot, so
+      // that every step issues the same loads
+      const int cn = chunk_at(min(s + 1, NC - 1));
+      ensure_ready(fl, cn);
+      stage(nxt, cn, ChainRole{});
       mem_fence_compiler();
       prefetch(chunk_at(min(s + 3, NC - 1)), ChainRole{});
       mem_fence_compiler();
@@ -556,9 +562,17 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
 
     if (NC > 0) {
       ensure_ready(flag_of(0), chunk_at(0));
+      // after the first flag, the loads of a step in a step's order (stage,
+      // prefetch, flag): the compiler derives the loop's waits from every
+      // path into it, so the prologue must leave the same loads in flight
+      uint32_t fa = flag_of(1);
+      mem_fence_compiler();
       stage(cs0, chunk_at(0), ChainRole{});
-      uint32_t fa = flag_of(1), fb = flag_of(2);
-      step_barrier<2>();  // the chunk-0 loads done (the two flag loads may remain)
+      mem_fence_compiler();
+      prefetch(chunk_at(min(1, NC - 1)), ChainRole{});
+      mem_fence_compiler();
+      uint32_t fb = flag_of(2);
+      step_barrier<1 + kPf>();  // chunk 0 staged (the prefetch and the last flag may remain)
       int s = 0;
       for (; s + 1 < NC; s += 2) {
         chain_step(cs0, cs1, xs0, fa, s);
@@ -573,6 +587,7 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
       }
       // the readout's last step
       step_barrier<1 + kPf>();
+      __builtin_amdgcn_s_waitcnt(kWaitVmem);  // the last restage and prefetch
     }
     // final state
     if (a.state_out) {
@@ -603,29 +618,73 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
     auto out_off = [&](int c, int tt) { return (uint32_t)(c * C + 16 * tt + l16) * HOB + out_lane; };
     bool pq_gave_up = false;
 
-    // partials of a bidirectional second visit, loaded a step ahead
-    auto load_partial = [&](f32x4 (&pq)[RT], int s) {
+    // ---- bidirectional combine flags (see the file comment) ----
+    const int nfl = dv >> 4;          // flag columns per chunk
+    const int fcol = (dv0 >> 4) + j;  // this wave's
+    const rsrc_t rfl = BI && a.part_flags ? make_rsrc(a.part_flags + (size_t)chain * NC * nfl, (uint32_t)(NC * nfl) * 4u)
+                                          : rnone;
+    auto flag_off = [&](int v) { return (uint32_t)(chunk_at(min(v, NC - 1)) * nfl + fcol) * 4u; };
+    const int nfirst = BI ? (rev ? NC / 2 : (NC + 1) / 2) : NC;  // first visits are 0 .. nfirst - 1
+    int pub_next = 0;  // first visits before this one have their flags stored
+    // the flag of visit v, if it is an unpublished first visit (else a store
+    // through the empty resource: one store either way); every lane stores
+    // the same word
+    auto publish = [&](int v) {
+      const bool now = v >= pub_next && v < nfirst;
+      bstore4u_agent(now ? rfl : rnone, flag_off(v < 0 ? 0 : v), 1u);
+      if (now) pub_next = v + 1;
+    };
+    // the flag of visit v (a second visit), for the partial load a step later
+    auto load_flag = [&](uint32_t& fl, int v) {
+      if constexpr (BI) fl = col_flag_fresh(v < NC && !first_visit(v) ? rfl : rnone, flag_off(v));
+    };
+    // the partial of visit v, if its flag was set when loaded (`got`; else
+    // zeros: the readout polls)
+    auto load_partial = [&](f32x4 (&pq)[RT], bool got, int v) {
       if constexpr (BI) {
-        const bool want = s < NC && !first_visit(s);
-        const rsrc_t rp = want ? ro : rnone;
-        const int c = chunk_at(min(s, NC - 1));
+        const rsrc_t rp = got ? ro : rnone;
+        const int c = chunk_at(min(v, NC - 1));
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) pq[tt] = bload16(rp, out_off(c, tt));
+        for (int tt = 0; tt < RT; ++tt) pq[tt] = col_load_fresh(rp, out_off(c, tt));
       }
     };
 
-    // readout of visit sp (chunk chunk_at(sp)) from slot `cur` and exchange `xr`
-    auto read_step = [&](const lds_u8* cur, lds_u8* nxt, const lds_u8* xr, f32x4 (&pq)[RT],
-                         f32x4 (&pq_next)[RT], int s) {
-      // stage chunk s's q, P and scales (prepared: the chain waves waited for
-      // its flag a step ago); then the partials of visit s
-      if (s < NC) stage(nxt, chunk_at(s), ReadRole{});
+    // Readout step s: stage chunk s's q, P and scales (prepared: the chain
+    // waves waited for its flag a step ago), load the flag of visit s + 1 and
+    // the partial of visit s, then read out visit s - 1 from slot `cur` and
+    // exchange `xr`.  Every step issues the same vector memory operations in
+    // the same order -- a flag store, the stage, the flag, the partial, the
+    // prefetch, the output stores -- through an empty resource where there
+    // is nothing to load or store (the last step restages the last chunk).
+    // The step-end waits count on that, and so do the waits the compiler
+    // derives for the loop from every path into it.
+    auto read_step = [&](const lds_u8* cur, lds_u8* nxt, const lds_u8* xr, f32x4 (&pq)[RT], bool got,
+                         f32x4 (&pq_next)[RT], bool& got_next, uint32_t fl_s, uint32_t& fl_next, int s) {
+      // whether visit s's partial is published (its flag was loaded a step
+      // ago; tested first, while only the last step's tail is in flight)
+      if constexpr (BI) got_next = s < NC && !first_visit(s) && __builtin_amdgcn_readfirstlane(fl_s) != 0u;
+      if constexpr (BI) {
+        if (s - 1 == nfirst && nfirst > 0) {
+          // the first second visit: every flag of this wave stored first
+          __builtin_amdgcn_s_waitcnt(kWaitVmem);
+          while (pub_next < nfirst) publish(pub_next);
+        }
+        publish(s - 3);  // its stores were counted out by the barrier ending step s - 1
+      }
+      mem_fence_compiler();
+      stage(nxt, chunk_at(min(s, NC - 1)), ReadRole{});
+      mem_fence_compiler();
+      load_flag(fl_next, s + 1);
+      load_partial(pq_next, got_next, s);
       mem_fence_compiler();
       prefetch(chunk_at(min(s + 3, NC - 1)), ReadRole{});
       mem_fence_compiler();
-      load_partial(pq_next, s);
-      mem_fence_compiler();
-      if (s == 0) return;
+      if (s == 0) {
+        // no readout yet: the output stores go to the empty resource
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt) bstore16(rnone, out_off(0, tt), f32x4{0.f, 0.f, 0.f, 0.f});
+        return;
+      }
       const int sp = s - 1;
       const int c = chunk_at(sp);
       const lds_u8* Qt = cur + L::RQ;
@@ -633,6 +692,26 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
       const lds_u8* Sc = cur + L::RS;
       const lds_u8* Pd = cur + L::RD;
       const lds_u8* X = xr + j * L::XJ;
+      const bool add = BI && !first_visit(sp);
+      if (BI && add && !got) {
+        // the partial was not published two steps ago: wait for its flag
+        bool ok = false;
+        if (!pq_gave_up) {
+          int n = 0;
+          for (; n < kColPollLimit; ++n) {
+            if (__builtin_amdgcn_readfirstlane(col_flag_fresh(rfl, flag_off(sp))) != 0u) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+          ok = n < kColPollLimit;
+          pq_gave_up = !ok;
+        }
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt) pq[tt] = ok ? col_load_fresh(ro, out_off(c, tt)) : f32x4{nan, nan, nan, nan};
+        // waited for here, so that the compiler does not make the common
+        // path wait as if these loads were in flight there
+        __builtin_amdgcn_s_waitcnt(kWaitVmem);
+      }
       bf16x8 sr[KS], vh[KC], vl[KC];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sr[ks] = lds_frag(X + L::XS + ks * 1024 + lane * 16);
@@ -642,7 +721,6 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         const f32x4 v1 = *(const lds_f32x4v*)(X + L::XV + kc * 2048 + lane * 32 + 16);
         split8(v0, v1, vh[kc], vl[kc]);
       }
-      const bool add = BI && !first_visit(sp);
 #pragma unroll
       for (int tt = 0; tt < RT; ++tt) {
         const int t = 16 * tt + l16;  // this lane's token
@@ -673,52 +751,43 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
             o = M::mma(vh[kc], and_mask(dg, dmask[tt]), o);
           }
         }
-        if constexpr (BI) {
-          if (add) {
-            // the first visitor's partial: re-read past the L1 cache while any
-            // of it still holds the fill pattern
-            if (__any(col_any_unwritten(pq[tt])) && !pq_gave_up) {
-              f32x4 q = pq[tt];
-              int n = 0;
-              for (; n < kColPollLimit; ++n) {
-                __builtin_amdgcn_s_sleep(2);
-                q = col_load_fresh(ro, out_off(c, tt));
-                if (!__any(col_any_unwritten(q))) break;
-              }
-              pq_gave_up = n == kColPollLimit;
-              pq[tt] = q;
-            }
-            o += pq[tt];
-          } else {
-            o = canonical_nans(o);  // a first visit: never the fill pattern
-          }
-        }
-        bstore16(ro, out_off(c, tt), o);
+        if (BI && add) o += pq[tt];
+        if (BI && !add) bstore16_agent(ro, out_off(c, tt), o);  // a partial: read by the other direction
+        else bstore16(ro, out_off(c, tt), o);
       }
     };
 
     f32x4 pqa[RT], pqb[RT];
 #pragma unroll
     for (int tt = 0; tt < RT; ++tt) pqa[tt] = pqb[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // loads a readout wave leaves in flight at a step's end: its partials
-    // (bidirectional) and its output stores
-    constexpr int kTail = (BI ? 2 : 1) * RT + kPf;
+    bool ga = false, gb = false;
+    uint32_t fa = 0u, fb = 0u;
+    // memory operations a readout wave leaves in flight at a step's end: the
+    // flag and the partials it loads ahead (bidirectional), the prefetch and
+    // its output stores
+    constexpr int kTail = (BI ? 2 * RT + 1 : RT) + kPf;
     if (NC > 0) {
       step_barrier<0>();  // the chain waves' prologue
-      // step 0 stages chunk 0 and loads the partials of visit 0; no readout yet
-      read_step(rs1, rs0, xs1, pqb, pqa, 0);
-      step_barrier<(BI ? RT : 0) + kPf>();
+      load_flag(fa, 0);
+      // step 0 stages chunk 0 and loads the partial of visit 0; no readout yet
+      read_step(rs1, rs0, xs1, pqb, gb, pqa, ga, fa, fb, 0);
+      step_barrier<kTail>();
       // then steps 1 .. NC: odd steps read slot 0 and stage into slot 1
       int s = 1;
       for (; s + 1 <= NC; s += 2) {
-        read_step(rs0, rs1, xs0, pqa, pqb, s);
+        read_step(rs0, rs1, xs0, pqa, ga, pqb, gb, fb, fa, s);
         step_barrier<kTail>();
-        read_step(rs1, rs0, xs1, pqb, pqa, s + 1);
+        read_step(rs1, rs0, xs1, pqb, gb, pqa, ga, fa, fb, s + 1);
         step_barrier<kTail>();
       }
       if (s <= NC) {
-        read_step(rs0, rs1, xs0, pqa, pqb, s);
+        read_step(rs0, rs1, xs0, pqa, ga, pqb, gb, fb, fa, s);
         step_barrier<kTail>();
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmem);
+      if constexpr (BI) {
+        // flags not yet stored (short sequences)
+        while (pub_next < nfirst) publish(pub_next);
       }
     }
   }

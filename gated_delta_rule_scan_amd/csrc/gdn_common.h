@@ -132,6 +132,9 @@ __device__ __forceinline__ void bstore16_agent(rsrc_t r, uint32_t off, f32x4 x) 
 __device__ __forceinline__ void bstore4_agent(rsrc_t r, uint32_t off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, (int)off, 0, kAgentScope);
 }
+__device__ __forceinline__ void bstore4u_agent(rsrc_t r, uint32_t off, uint32_t x) {
+  __builtin_amdgcn_raw_buffer_store_b32((int)x, r, (int)off, 0, kAgentScope);
+}
 
 // Every NaN replaced by the canonical quiet NaN.  A bidirectional scan's
 // first visitor stores its readout through this, so its stores can never
@@ -204,9 +207,14 @@ __device__ __forceinline__ bf16x8 load_kt_frag(const bf16* krow, int kp, int tok
 //                             (pending), the preparation kernel stores 0 once
 //                             the chunk's outputs (and its output fill) are in
 //                             place, and the state chain waits for 0
+//   pfl  [NBH][NC][dv/16] uint32 : bidirectional scans on bf16 operands: per
+//                             chunk and 16 output columns, 1 once the first
+//                             visitor's readout (the partial the second
+//                             visitor adds) is in `out`; the preparation
+//                             kernel clears the chunk's flags
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t tri, pqk, sc, pdg, rdy, total;
+  size_t tri, pqk, sc, pdg, rdy, pfl, total;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -214,7 +222,7 @@ static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; 
 // Floats per pdg chunk record: C + 4, rounded up to a whole 128-byte line.
 __host__ __device__ constexpr int pdg_stride(int C) { return (C + 4 + 31) / 32 * 32; }
 
-static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_t mt_bytes) {
+static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_t mt_bytes, int64_t dv) {
   WsLayout L;
   size_t off = 0;
   const size_t nch = (size_t)NBH * (size_t)NC;
@@ -223,6 +231,7 @@ static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_
   L.sc = off;  off = align_up(off + (size_t)dirs * nch * C * 16, 256);
   L.pdg = off; off = align_up(off + (size_t)dirs * nch * pdg_stride(C) * 4, 256);
   L.rdy = off; off = align_up(off + nch * 4, 256);
+  L.pfl = off; off = align_up(off + (dirs == 2 ? nch * (size_t)(dv / 16) * 4 : 0), 256);
   L.total = off;
   return L;
 }
@@ -242,11 +251,12 @@ struct ScanArgs {
   float4* sc;
   float* pdg;
   unsigned* ready;     // rdy, above
+  unsigned* part_flags;  // pfl, above (bidirectional bf16 scans; else null)
   int64_t B, T, H, NC;
   int dv;
   int fwd_on, rev_on;  // which directions are computed
   int dirs;            // number of computed directions (slots)
-  int zero_out;        // the preparation kernel fills `out` with the "not written yet" pattern (bidirectional)
+  int zero_out;        // the preparation kernel fills `out` with the "not written yet" pattern (bidirectional fp32)
   int erase;           // 1: delta rule; 0: erase-free variant (no -beta k k^T term: L = 0, T = I)
   int excl_fwd, excl_rev;  // 1: that direction reads before the token's own write (no self term)
 };

@@ -8,9 +8,10 @@
 namespace gdn {
 
 // State-independent chunk quantities (triangular inverses, decayed q.k,
-// per-token scales); fills the output rows of its chunk with the "not written
-// yet" pattern when a.zero_out is set (bidirectional scans), then publishes
-// the chunk's ready flag.  One workgroup per (chunk, batch*head), numbered in
+// per-token scales); for bidirectional scans, fills the output rows of its
+// chunk with the "not written yet" pattern (a.zero_out, fp32 operands) or
+// clears the chunk's combine flags (a.part_flags, bf16 operands); then
+// publishes the chunk's ready flag.  One workgroup per (chunk, batch*head), numbered in
 // the order the state chain consumes the chunks.
 //
 // Every launcher, given `query`, fills it with the kernel's attributes
@@ -18,7 +19,8 @@ namespace gdn {
 template <typename MT, int DK, int C>
 hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes* query);
 
-// Zeroes the n chunk-ready flags (before a concurrent preparation pass).
+// Marks the n chunk-ready flags pending (1), before a concurrent preparation
+// pass; the preparation kernel stores 0 once a chunk is ready.
 hipError_t launch_clear_ready(unsigned* ready, int64_t n, hipStream_t stream);
 
 // Sequential inter-chunk state chain with the chunk outputs fused in.
@@ -26,15 +28,18 @@ hipError_t launch_clear_ready(unsigned* ready, int64_t n, hipStream_t stream);
 // per direction; the second visitor of a chunk adds the first one's readout,
 // which it recognises against the pattern the preparation kernel filled the
 // output with) instead of one direction (`rev_single` tells which).
-// The state chain reads a chunk's prepared operands only after the chunk's
-// ready flag is 1, so it may run concurrently with the preparation kernel.
+// With a.ready set, the state chain reads a chunk's prepared operands only
+// once the chunk's ready flag is 0, so it may run concurrently with the
+// preparation kernel.
 template <typename MT, int DK, int C, int NT, bool BI>
 hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query);
 
 // The state chain for bf16 operands: NT chain waves each own 16 value columns
 // of the state over every dk, NT readout waves compute the chunk outputs a
 // step later; operands are staged by direct buffer-to-LDS loads.  Same
-// arguments, grid and results contract as launch_chain<bf16, ...>.
+// arguments, grid and results contract as launch_chain<bf16, ...>, except
+// that a bidirectional launch signals its partial readouts through
+// a.part_flags (cleared by the preparation kernel, which must have finished).
 template <int DK, int C, int NT, bool BI>
 hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query);
 

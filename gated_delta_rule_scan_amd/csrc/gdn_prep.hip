@@ -191,9 +191,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   const float (*s_bt)[64] = s_raw + 2;
 
   // ---- bidirectional scans: the second visitor of a chunk in the state
-  // chain recognises the first visitor's readout by this all-ones NaN fill
-  // ("not written yet"; arithmetic never produces it).  Issued after every
-  // read of the kernel has returned, so it never delays them. ----
+  // chain must know when the first visitor's readout is in `out`.  bf16
+  // operands: the chunk's combine flags, cleared here (the state chain
+  // starts only after this kernel has finished).  fp32 operands: `out` is
+  // filled with the all-ones NaN ("not written yet"; first visitors store
+  // canonical NaNs, so a readout never carries it), issued after every read
+  // of the kernel has returned, so it never delays them. ----
+  if (a.part_flags) {
+    const int nfl = a.dv >> 4;
+    if (tid < nfl) a.part_flags[cid * nfl + tid] = 0u;
+  }
   if (a.zero_out) {
     const int sh = 29 - __builtin_clz((unsigned)a.dv);  // log2(dv / 4): 16-byte pieces per row (a power of two)
     const uint32_t orow = (uint32_t)(H * a.dv) * 4u;

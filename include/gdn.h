@@ -47,7 +47,8 @@
  * Ownership and execution: every pointer is caller-owned device memory; the
  * library allocates no device memory, does not synchronise and reads no
  * environment variables.  The work is ordered on `stream` (NULL: the default
- * stream) and completes asynchronously.  For large problems the chunk
+ * stream) and completes asynchronously.  For long single-direction scans
+ * with few (batch, head) sequences (and fp32 bidirectional ones) the chunk
  * preparation runs concurrently with the state chain, on a library stream
  * forked from `stream` and joined back to it with events (one stream and two
  * events per device, created on the first such call and kept until the
@@ -66,7 +67,8 @@
  * rejected.  Results are bitwise deterministic for fixed inputs and chunk
  * size, concurrent or not: there are no atomic reductions (the second visit
  * of a chunk in a bidirectional scan adds the stored readout of the first
- * visit in a fixed order).  The value-tile width changes the schedule, never
+ * visit in a fixed order; it waits for that readout's flag for about a
+ * second at most, after which the outputs it could not combine are NaN).  The value-tile width changes the schedule, never
  * the arithmetic.
  *
  * Errors: argument problems are reported before anything is enqueued and
