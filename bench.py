@@ -401,7 +401,8 @@ def main() -> int:
     d = {k: _dev(v) for k, v in x.items()}
     out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
     s_out = torch.empty((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
-    nws = gdn.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.direction, args.chunk, args.dv_tile)
+    nws = gdn.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.direction, args.chunk, args.dv_tile,
+                              args.exclusive)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
     C = args.chunk or 64
 

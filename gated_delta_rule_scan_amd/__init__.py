@@ -168,9 +168,11 @@ def make_problem(B, T, H, dk, dv, dtype: int, chunk: int = 0, dv_tile: int = 0, 
 
 
 def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd", chunk: int = 0,
-                    dv_tile: int = 0) -> int:
+                    dv_tile: int = 0, exclusive: str = "none") -> int:
     dt = GDN_DTYPE_BF16 if dtype == "bf16" else GDN_DTYPE_F32
-    return gdn_workspace_bytes(make_problem(B, T, H, dk, dv, dt, chunk, dv_tile), DIRECTIONS[direction])
+    prob = make_problem(B, T, H, dk, dv, dt, chunk, dv_tile)
+    prob.options = EXCLUSIVE[exclusive]  # exclusive readouts on bf16 operands need more
+    return gdn_workspace_bytes(prob, DIRECTIONS[direction])
 
 
 def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chunk: int = 0, dv_tile: int = 0,
@@ -226,6 +228,7 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
         state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
         mine.append(state_out)
     prob = make_problem(B, T, H, dk, dv, dt, chunk, dv_tile)
+    prob.options = (GDN_OPT_SERIAL if serial else 0) | (0 if erase else GDN_OPT_NO_ERASE) | EXCLUSIVE[exclusive]
     nbytes = gdn_workspace_bytes(prob, DIRECTIONS[direction])
     if nbytes == 0 and T > 0:
         raise GdnError(GDN_ERR_UNSUPPORTED)
@@ -237,7 +240,6 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     prob.workspace_bytes = workspace.numel() if workspace is not None else 0
     prob.stream = s.cuda_stream
     prob.timing_events = timing_events
-    prob.options = (GDN_OPT_SERIAL if serial else 0) | (0 if erase else GDN_OPT_NO_ERASE) | EXCLUSIVE[exclusive]
     st = gdn_forward(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                      None if state_in is None else state_in.data_ptr(),
                      None if state_out is None else state_out.data_ptr(), out.data_ptr(), DIRECTIONS[direction])

@@ -30,6 +30,7 @@ struct Plan {
   int fwd_on, rev_on;
   int64_t NC;   // chunks per sequence
   size_t mt;    // bytes per operand element
+  bool plo;     // the decayed q.k tile as hi + lo parts (exclusive readouts, bf16)
   WsLayout ws;
 };
 
@@ -90,7 +91,14 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   pl->dirs = pl->fwd_on + pl->rev_on;
   pl->NC = (p->T + C - 1) / C;
   pl->mt = p->dtype == GDN_DTYPE_BF16 ? 2 : 4;
-  pl->ws = ws_layout(p->B * p->H, pl->NC, C, pl->dirs, pl->mt, p->dv);
+  // exclusive readouts on bf16 operands carry the decayed q.k tile as hi + lo parts
+  pl->plo = p->dtype == GDN_DTYPE_BF16 && (p->options & (GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE)) != 0;
+  // (and the entry state's low parts: their exchange fits 16-column tiles only)
+  if (pl->plo) {
+    if (pl->NT == 2) return GDN_ERR_UNSUPPORTED;
+    pl->NT = 1;
+  }
+  pl->ws = ws_layout(p->B * p->H, pl->NC, C, pl->dirs, pl->mt, p->dv, pl->plo);
   return GDN_OK;
 }
 
@@ -175,17 +183,21 @@ chain_fn chain_for3(int NT, int dirs) {
 }
 
 template <int DK, int C>
-chain_fn column_chain_for3(int NT, int dirs) {
-  if (NT == 1) return dirs == 2 ? launch_column_chain<DK, C, 1, true> : launch_column_chain<DK, C, 1, false>;
-  return dirs == 2 ? launch_column_chain<DK, C, 2, true> : launch_column_chain<DK, C, 2, false>;
+chain_fn column_chain_for3(int NT, int dirs, bool plo) {
+  if (plo) {  // 16-column tiles only
+    if (NT != 1) return nullptr;
+    return dirs == 2 ? launch_column_chain<DK, C, 1, true, true> : launch_column_chain<DK, C, 1, false, true>;
+  }
+  if (NT == 1) return dirs == 2 ? launch_column_chain<DK, C, 1, true, false> : launch_column_chain<DK, C, 1, false, false>;
+  return dirs == 2 ? launch_column_chain<DK, C, 2, true, false> : launch_column_chain<DK, C, 2, false, false>;
 }
 
 // bf16 operands: the column-owning chain; fp32 operands: the two-role chain
 template <typename MT>
-chain_fn chain_for(int dk, int C, int NT, int dirs) {
+chain_fn chain_for(int dk, int C, int NT, int dirs, bool plo) {
   if constexpr (sizeof(MT) == 2) {
-    if (dk == 64) return C == 32 ? column_chain_for3<64, 32>(NT, dirs) : column_chain_for3<64, 64>(NT, dirs);
-    return C == 32 ? column_chain_for3<128, 32>(NT, dirs) : column_chain_for3<128, 64>(NT, dirs);
+    if (dk == 64) return C == 32 ? column_chain_for3<64, 32>(NT, dirs, plo) : column_chain_for3<64, 64>(NT, dirs, plo);
+    return C == 32 ? column_chain_for3<128, 32>(NT, dirs, plo) : column_chain_for3<128, 64>(NT, dirs, plo);
   } else {
     if (dk == 64) return C == 32 ? chain_for3<MT, 64, 32>(NT, dirs) : chain_for3<MT, 64, 64>(NT, dirs);
     return C == 32 ? chain_for3<MT, 128, 32>(NT, dirs) : chain_for3<MT, 128, 64>(NT, dirs);
@@ -269,6 +281,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   // that the preparation kernel clears
   a.zero_out = pl.dirs == 2 && !bf;
   if (pl.dirs == 2 && bf && need_ws) a.part_flags = reinterpret_cast<unsigned*>(ws + pl.ws.pfl);
+  if (pl.plo && need_ws) a.pq_lo = ws + pl.ws.pql;
   a.erase = (p->options & GDN_OPT_NO_ERASE) ? 0 : 1;
   a.excl_fwd = (p->options & GDN_OPT_EXCLUSIVE_FORWARD) ? 1 : 0;
   a.excl_rev = (p->options & GDN_OPT_EXCLUSIVE_REVERSE) ? 1 : 0;
@@ -277,8 +290,8 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   // bidirectional: one workgroup per direction, readouts accumulated into
   // the output the preparation kernel filled; single direction: told whether
   // it runs in reverse
-  chain_fn cf = bf ? chain_for<bf16>((int)dk, pl.C, pl.NT, pl.dirs)
-                   : chain_for<float>((int)dk, pl.C, pl.NT, pl.dirs);
+  chain_fn cf = bf ? chain_for<bf16>((int)dk, pl.C, pl.NT, pl.dirs, pl.plo)
+                   : chain_for<float>((int)dk, pl.C, pl.NT, pl.dirs, false);
   prep_fn pf = bf ? prep_for<bf16>((int)dk, pl.C) : prep_for<float>((int)dk, pl.C);
   if (!cf || !pf) return GDN_ERR_UNSUPPORTED;
   const int rev_single = direction == GDN_DIR_REVERSE ? 1 : 0;

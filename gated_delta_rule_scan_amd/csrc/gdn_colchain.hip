@@ -114,7 +114,7 @@ __device__ __forceinline__ v4s tr16(const lds_u8* p) {
 // token order of the chain's product rows (see the file comment)
 __host__ __device__ constexpr int tau(int rt, int m) { return 32 * (rt >> 1) + 8 * (m >> 2) + 4 * (rt & 1) + (m & 3); }
 
-template <int DK, int C, int NT>
+template <int DK, int C, int NT, bool PLO>
 struct Col {
   static constexpr int DT = 16 * NT;             // value columns per workgroup
   static constexpr int RT = C / 16;              // 16-token row tiles per chunk
@@ -127,11 +127,16 @@ struct Col {
   static constexpr int KB = C * KROWB, TB = C * TROWB, VB = C * VROWB;
   // chain slot: k | Tinv | v | scales | remainders and chunk decay
   static constexpr int CK = 0, CT = CK + KB, CV = CT + TB, CS = CV + VB, CP = CS + 1024, CSLOT = CP + 1024;
-  // readout slot: q | P | scales | remainders
-  static constexpr int RQ = 0, RP = RQ + KB, RS = RP + TB, RD = RS + 1024, RSLOT = RD + 1024;
-  // exchange, per chain wave: entry-state fragments (bf16), Vnew (fp32, the
-  // eight values of a k-chunk operand fragment per lane)
-  static constexpr int XS = 0, XV = KS * 1024, XJ = XV + KC * 2048, XSLOT = NT * XJ;
+  // readout slot: q | P | scales | remainders; with PLO: q | P | low parts
+  // of P (a direction reading before the token's own write) or the
+  // remainders (one that does not) | scales
+  static constexpr int RQ = 0, RP = RQ + KB, RL = RP + TB;
+  static constexpr int RS = PLO ? RL + TB : RL, RD = PLO ? RL : RS + 1024, RSLOT = RS + (PLO ? 1024 : 2048);
+  // exchange, per chain wave: entry-state fragments (bf16; with PLO also
+  // their low parts), Vnew (fp32, the eight values of a k-chunk operand
+  // fragment per lane)
+  static constexpr int XS = 0, XSL = KS * 1024, XV = XSL + (PLO ? KS * 1024 : 0), XJ = XV + KC * 2048,
+                       XSLOT = NT * XJ;
   static constexpr int NDC = CSLOT / 1024, NDR = RSLOT / 1024;  // 1-KB loads per slot
   static_assert(KB % 1024 == 0 && TB % 1024 == 0 && VB % 1024 == 0, "whole 1-KB loads");
   static_assert(C == 32 || C == 64, "chunk");
@@ -149,7 +154,7 @@ enum : int { R_KTAU = 0, R_QNAT = 1, R_TTAU = 2, R_PNAT = 3, R_VAL = 4, R_RAW = 
 
 template <int DK, int C, int NT>
 __device__ __forceinline__ uint32_t dma_voff(int kind, int ii, int lane, uint32_t HDB, uint32_t HVB) {
-  using L = Col<DK, C, NT>;
+  using L = Col<DK, C, NT, false>;
   const int b = ii * 1024 + 16 * lane;  // byte within the staged region
   if (kind == R_KTAU || kind == R_QNAT) {
     const int rho = b / L::KROWB, q = (b % L::KROWB) >> 4;
@@ -233,9 +238,9 @@ __device__ __forceinline__ void make_mask(uint32_t (&m)[4], int row, int col0, b
 
 }  // namespace
 
-template <int DK, int C, int NT, bool BI>
+template <int DK, int C, int NT, bool BI, bool PLO>
 __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
-  using L = Col<DK, C, NT>;
+  using L = Col<DK, C, NT, PLO>;
   using M = Mma<bf16>;
   constexpr int RT = L::RT, KC = L::KC, KS = L::KS, SRT = L::SRT, DT = L::DT;
 
@@ -267,6 +272,8 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
   const int dv0 = tile * DT;
   const bool rev = BI ? (dslot == 1) : (rev_single != 0);
   const int slot = dslot;
+  // this direction reads before the token's own write and adds P's low parts
+  const bool plo_dir = PLO && (rev ? a.excl_rev : a.excl_fwd);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -284,6 +291,7 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
   char* obase = reinterpret_cast<char*>(a.out) + (size_t)((b * T * H + h) * dv + dv0) * 4;
   const char* trib = static_cast<const char*>(a.tri) + (size_t)chain * NC * L::TB;
   const char* pqkb = static_cast<const char*>(a.pqk) + (size_t)chain * NC * L::TB;
+  const char* pqlb = PLO && a.pq_lo ? static_cast<const char*>(a.pq_lo) + (size_t)chain * NC * L::TB : pqkb;
   const char* scb = reinterpret_cast<const char*>(a.sc) + ((size_t)slot * nch + (size_t)chain * NC) * C * 16;
   const char* pdb = reinterpret_cast<const char*>(a.pdg) + ((size_t)slot * nch + (size_t)chain * NC) * pdg_stride(C) * 4;
   const rsrc_t rnone = make_rsrc(obase, 0u);
@@ -314,8 +322,9 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
                                  : 16u * lane;
       } else {
         voff[n] = byte < L::RP   ? dma_voff<DK, C, NT>(R_QNAT, (byte - L::RQ) / 1024, lane, HDB, HVB)
-                  : byte < L::RS ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RP) / 1024, lane, HDB, HVB)
-                                 : 16u * lane;
+                  : byte < L::RL ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RP) / 1024, lane, HDB, HVB)
+                  : (PLO && byte < L::RS && plo_dir) ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RL) / 1024, lane, HDB, HVB)
+                                                     : 16u * lane;
       }
     }
   };
@@ -337,11 +346,19 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         dma16(r, slotp + byte, voff[n]);
       }
     } else {
+      // PLO: the low parts of P, or the remainders followed by loads
+      // through the empty resource (the same count either way)
+      const rsrc_t rpl = make_rsrc(pqlb + (size_t)c * L::TB, (uint32_t)L::TB);
       int n = 0;
 #pragma unroll
       for (int i = J; i < L::NDR; i += NT, ++n) {
         const int byte = i * 1024;
-        const rsrc_t r = byte < L::RP ? rkq : byte < L::RS ? rtp : byte < L::RD ? rsc : rpd;
+        rsrc_t r;
+        if (byte < L::RP) r = rkq;
+        else if (byte < L::RL) r = rtp;
+        else if (PLO && byte < L::RS) r = plo_dir ? rpl : (byte == L::RL ? rpd : rnone);
+        else if (byte < L::RS + 1024) r = rsc;
+        else r = rpd;
         dma16(r, slotp + byte, voff[n]);
       }
     }
@@ -474,7 +491,13 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
       bf16x8 sb[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sb[ks] = pack8(Sacc[2 * ks], Sacc[2 * ks + 1]);
+        if constexpr (PLO) {
+          bf16x8 sl;
+          split8(Sacc[2 * ks], Sacc[2 * ks + 1], sb[ks], sl);
+          lds_put(X + L::XSL + ks * 1024 + lane * 16, sl);
+        } else {
+          sb[ks] = pack8(Sacc[2 * ks], Sacc[2 * ks + 1]);
+        }
         lds_put(X + L::XS + ks * 1024 + lane * 16, sb[ks]);
       }
       // Y = K S^T (rows in token order tau); the row tiles are independent
@@ -730,6 +753,10 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 qb = lds_frag(Qt + t * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(t)) << 4));
           z = M::mma(sr[ks], qb, z);
+          if constexpr (PLO) {
+            // the entry state's low parts (a direction reading before the token's own write)
+            if (plo_dir) z = M::mma(lds_frag(X + L::XSL + ks * 1024 + lane * 16), qb, z);
+          }
         }
         const float zs = lds_f(Sc + t * 16 + 8);  // e^g rq of the token
         f32x4 o = z * zs;
@@ -742,6 +769,14 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
           if (kc == kd) pb = and_mask(pb, pmask[tt]);
           o = M::mma(vh[kc], pb, o);
           o = M::mma(vl[kc], pb, o);
+          if constexpr (PLO) {
+            if (plo_dir) {
+              // P's low part (with Vnew's hi part: the product's next order)
+              bf16x8 pl = lds_frag(cur + L::RL + t * L::TROWB + (((4 * kc + g4) ^ swz_t<C>(t)) << 4));
+              if (kc == kd) pl = and_mask(pl, pmask[tt]);
+              o = M::mma(vh[kc], pl, o);
+            }
+          }
           if (kc == kd) {
             // the self term's remainder (P holds it rounded): a diagonal product with Vnew's hi part
             const bf16 rmd = (bf16)lds_f(Pd + t * 4);
@@ -793,20 +828,26 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
   }
 }
 
-template <int DK, int C, int NT, bool BI>
+template <int DK, int C, int NT, bool BI, bool PLO>
 hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query) {
-  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&column_chain_kernel<DK, C, NT, BI>));
+  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&column_chain_kernel<DK, C, NT, BI, PLO>));
   const int ntiles = a.dv / (16 * NT);
   const int nbh = (int)(a.B * a.H);
   const unsigned nblocks = (unsigned)chain_blocks(nbh, a.dv, NT, BI ? 2 : 1);
-  hipLaunchKernelGGL((column_chain_kernel<DK, C, NT, BI>), dim3(nblocks), dim3(128 * NT), 0, stream, a, rev_single,
-                     ntiles, nbh);
+  hipLaunchKernelGGL((column_chain_kernel<DK, C, NT, BI, PLO>), dim3(nblocks), dim3(128 * NT), 0, stream, a,
+                     rev_single, ntiles, nbh);
   return hipGetLastError();
 }
 
-#define GDN_INST_COL(DK, C, NT, BI) \
-  template hipError_t launch_column_chain<DK, C, NT, BI>(const ScanArgs&, int, hipStream_t, hipFuncAttributes*);
-#define GDN_INST_COL_D(DK, C, NT) GDN_INST_COL(DK, C, NT, false) GDN_INST_COL(DK, C, NT, true)
+#define GDN_INST_COL(DK, C, NT, BI, PLO) \
+  template hipError_t launch_column_chain<DK, C, NT, BI, PLO>(const ScanArgs&, int, hipStream_t, hipFuncAttributes*);
+// PLO (exclusive readouts): 16-column tiles only (its LDS would not fit 32)
+#define GDN_INST_COL_P(DK, C, NT, BI) GDN_INST_COL(DK, C, NT, BI, false) \
+  GDN_INST_COL_IF_NT1(DK, C, NT, BI)
+#define GDN_INST_COL_IF_NT1(DK, C, NT, BI) GDN_INST_COL_PLO_##NT(DK, C, BI)
+#define GDN_INST_COL_PLO_1(DK, C, BI) GDN_INST_COL(DK, C, 1, BI, true)
+#define GDN_INST_COL_PLO_2(DK, C, BI)
+#define GDN_INST_COL_D(DK, C, NT) GDN_INST_COL_P(DK, C, NT, false) GDN_INST_COL_P(DK, C, NT, true)
 #define GDN_INST_COL_N(DK, C) GDN_INST_COL_D(DK, C, 1) GDN_INST_COL_D(DK, C, 2)
 GDN_INST_COL_N(64, 32)
 GDN_INST_COL_N(64, 64)

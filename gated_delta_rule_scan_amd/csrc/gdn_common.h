@@ -212,9 +212,12 @@ __device__ __forceinline__ bf16x8 load_kt_frag(const bf16* krow, int kp, int tok
 //                             visitor's readout (the partial the second
 //                             visitor adds) is in `out`; the preparation
 //                             kernel clears the chunk's flags
+//   pql  [NBH*NC][C][C]  bf16 : exclusive readouts on bf16 operands: the
+//                             part of each strict entry of pqk that bf16
+//                             drops (x - bf16(x)); else absent
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t tri, pqk, sc, pdg, rdy, pfl, total;
+  size_t tri, pqk, sc, pdg, rdy, pfl, pql, total;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -222,7 +225,7 @@ static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; 
 // Floats per pdg chunk record: C + 4, rounded up to a whole 128-byte line.
 __host__ __device__ constexpr int pdg_stride(int C) { return (C + 4 + 31) / 32 * 32; }
 
-static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_t mt_bytes, int64_t dv) {
+static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_t mt_bytes, int64_t dv, bool plo) {
   WsLayout L;
   size_t off = 0;
   const size_t nch = (size_t)NBH * (size_t)NC;
@@ -232,6 +235,7 @@ static inline WsLayout ws_layout(int64_t NBH, int64_t NC, int C, int dirs, size_
   L.pdg = off; off = align_up(off + (size_t)dirs * nch * pdg_stride(C) * 4, 256);
   L.rdy = off; off = align_up(off + nch * 4, 256);
   L.pfl = off; off = align_up(off + (dirs == 2 ? nch * (size_t)(dv / 16) * 4 : 0), 256);
+  L.pql = off; off = align_up(off + (plo ? nch * C * C * 2 : 0), 256);
   L.total = off;
   return L;
 }
@@ -252,6 +256,7 @@ struct ScanArgs {
   float* pdg;
   unsigned* ready;     // rdy, above
   unsigned* part_flags;  // pfl, above (bidirectional bf16 scans; else null)
+  void* pq_lo;           // pql, above (exclusive readouts on bf16 operands; else null)
   int64_t B, T, H, NC;
   int dv;
   int fwd_on, rev_on;  // which directions are computed

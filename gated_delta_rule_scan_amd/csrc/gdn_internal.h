@@ -40,7 +40,9 @@ hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream, h
 // arguments, grid and results contract as launch_chain<bf16, ...>, except
 // that a bidirectional launch signals its partial readouts through
 // a.part_flags (cleared by the preparation kernel, which must have finished).
-template <int DK, int C, int NT, bool BI>
+// PLO: the decayed q.k tile also as its bf16 low parts (a.pq_lo), added in
+// the readouts of the directions that read before the token's own write.
+template <int DK, int C, int NT, bool BI, bool PLO>
 hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query);
 
 // Workgroups of a state-chain launch (one per value tile, direction and

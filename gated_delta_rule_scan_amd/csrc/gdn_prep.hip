@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
 
   __shared__ __align__(16) unsigned char smem[SM::region];
   __shared__ __align__(16) float s_rk[C], s_rq[C], s_qk[C];  // row scales, raw q.k of each token
-  __shared__ __align__(16) float s_raw[4][64], s_g[2][C];  // raw gates as loaded (see below); cumulative log2-gates
+  __shared__ __align__(16) float s_raw[4][64];  // raw gates as loaded (see below)
+  __shared__ __align__(16) double s_g[2][C];   // cumulative log2-gates (double: see the scan)
 
   constexpr int PP = SM::PP;
   MT* Ks = reinterpret_cast<MT*>(smem);
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   const int fslot = 0, rslot = fwd_on ? 1 : 0;
   const size_t nch = (size_t)a.B * a.H * a.NC;
   const int nrows = (int)(T - t0 < C ? T - t0 : C);  // valid tokens of this chunk (>= 1)
-  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr double kLog2eD = 1.4426950408889634;
 
   // ---- every global read of the kernel, issued at once ----
   // Raw q and k rows (16-byte pieces; rows past the sequence read as zero),
@@ -215,15 +216,18 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   // chunk-local cumulative log-gates in log2 units (every decay factor below
   // is one exp2 of a difference): wave 0 the inclusive prefix sums in token
   // order, wave 1 the inclusive suffix sums, each as a wave-wide scan; read
-  // only after the next barrier
+  // only after the next barrier.  The sums run in double: over a chunk they
+  // reach hundreds (fast decay), where one fp32 rounding is already a
+  // relative error of 1e-5 in every decay factor taken as a difference of
+  // two of them; in double, each difference is rounded once, to fp32.
   if (wave < 2) {
-    float s = s_raw[wave][lane];
+    double s = (double)s_raw[wave][lane] * kLog2eD;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const float o = __shfl_up(s, d, 64);
+      const double o = __shfl_up(s, d, 64);
       if (lane >= d) s += o;
     }
-    if (lane < C) s_g[wave][wave == 0 ? lane : C - 1 - lane] = s * kLog2e;
+    if (lane < C) s_g[wave][wave == 0 ? lane : C - 1 - lane] = s;
   }
 
   // ---- Gram K K^T and Q K^T on the matrix cores (raw operands, fp32 accumulate) ----
@@ -255,16 +259,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   // Lane (l16, g4) of tile (ti, tj) holds column 16 tj + l16 of rows
   // 16 ti + 4 g4 + i.  Below the diagonal the forward direction's entries,
   // above it the reverse direction's; the diagonal (the self terms) is
-  // written beside the diagonal solve below.
+  // written beside the diagonal solve below.  plo: the part of each decayed
+  // q.k entry that the operand type drops, kept for exclusive readouts.
+  float plo[UPW][4];
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     const int u = wave + 4 * j;
     if (u < NT2) {
       const int ti = u / NB, tj = u % NB;
       const int col = 16 * tj + l16, r0 = 16 * ti + 4 * g4;
-      const float gfc = s_g[0][col], grc = s_g[1][col], rkc = s_rk[col];
-      const f32x4 gf = *reinterpret_cast<const f32x4*>(&s_g[0][r0]);
-      const f32x4 gr = *reinterpret_cast<const f32x4*>(&s_g[1][r0]);
+      const double gfc = s_g[0][col], grc = s_g[1][col];
+      const float rkc = s_rk[col];
       const f32x4 bf = *reinterpret_cast<const f32x4*>(&s_bt[0][r0]);
       const f32x4 br = *reinterpret_cast<const f32x4*>(&s_bt[1][r0]);
       const f32x4 rkr = *reinterpret_cast<const f32x4*>(&s_rk[r0]);
@@ -276,12 +281,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
         const float wf = (col < r && fwd_on) ? 1.f : 0.f, wr = (col > r && rev_on) ? 1.f : 0.f;
         // decay between the two tokens (<= 0 in log2 units; zero where
         // unused, so it never overflows); below 2^-126 it may flush to zero
-        const float gd = fmaf(wf, gf[i] - gfc, wr * (gr[i] - grc));
+        const float gd = fmaf(wf, (float)(s_g[0][r] - gfc), wr * (float)(s_g[1][r] - grc));
         const float e = __builtin_amdgcn_exp2f(gd);
         const float lm = e * fmaf(wf, bf[i], wr * br[i]) * erase_w;
         const float pm = e * (wf + wr);
         Lm[r * LP + col] = (rkr[i] * rkc) * accG[j][i] * lm;
-        Pst[r * PP + col] = (MT)((rqr[i] * rkc) * accP[j][i] * pm);
+        const float pv = (rqr[i] * rkc) * accP[j][i] * pm;
+        const MT ph = (MT)pv;
+        Pst[r * PP + col] = ph;
+        plo[j][i] = pv - (float)ph;
       }
     }
   }
@@ -334,15 +342,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     if (dir == 0 ? fwd_on : rev_on) {
       const int slot = dir == 0 ? fslot : rslot;
       const bool in = tok < nrows;
-      const float g = s_g[dir][tok], gl = s_g[dir][dir == 0 ? C - 1 : 0];
-      const float eg = exp2f(g);
+      const double g = s_g[dir][tok], gl = s_g[dir][dir == 0 ? C - 1 : 0];
+      const float eg = exp2f((float)g);
       const rsrc_t rs = make_rsrc(a.sc + (slot * nch + cid) * C, C * 16);
       // {beta, e^g rk (erase term of the pseudo-values; 0 without it), e^g rq, e^(gn-g) rk}
       bstore16_agent(rs, tok * 16,
-                     in ? f32x4{s_bt[dir][tok], a.erase ? eg * rk : 0.f, eg * rq, exp2f(gl - g) * rk} : f32x4{0.f, 0.f, 0.f, 0.f});
+                     in ? f32x4{s_bt[dir][tok], a.erase ? eg * rk : 0.f, eg * rq, exp2f((float)(gl - g)) * rk}
+                        : f32x4{0.f, 0.f, 0.f, 0.f});
       const rsrc_t rp = make_rsrc(a.pdg + ((size_t)slot * nch + cid) * pdg_stride(C), (C + 4) * 4);
       bstore4_agent(rp, tok * 4, self - (float)self_mt);
-      if (tok < 4) bstore4_agent(rp, (C + tok) * 4, tok == 0 ? exp2f(gl) : 0.f);
+      if (tok < 4) bstore4_agent(rp, (C + tok) * 4, tok == 0 ? exp2f((float)gl) : 0.f);
     }
   }
   __syncthreads();
@@ -403,6 +412,23 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   }
   __syncthreads();
 
+  // ---- exclusive readouts on bf16 operands: the low parts of the decayed
+  // q.k tile, staged over the L tile (no longer read) ----
+  MT* Plo = reinterpret_cast<MT*>(Lm);
+  if (a.pq_lo) {
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+      const int u = wave + 4 * j;
+      if (u < NT2) {
+        const int ti = u / NB, tj = u % NB;
+        const int col = 16 * tj + l16, r0 = 16 * ti + 4 * g4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Plo[(r0 + i) * PP + col] = (MT)plo[j][i];
+      }
+    }
+    __syncthreads();
+  }
+
   // ---- both triangles to the workspace, 16 bytes per store ----
   {
     constexpr int EPS = 16 / (int)sizeof(MT);
@@ -423,6 +449,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       __builtin_memcpy(&p16, pv, 16);
       bstore16_agent(rt, p * 16, t16);
       bstore16_agent(rp, p * 16, p16);
+      if (a.pq_lo) {
+        const rsrc_t rl = make_rsrc(static_cast<MT*>(a.pq_lo) + cid * C * C, C * C * (int)sizeof(MT));
+        MT lv[EPS];
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const int col = c0 + e;
+          const bool keep = (col < r && fwd_on) || (col > r && rev_on);
+          lv[e] = keep ? Plo[r * PP + col] : (MT)0.f;
+        }
+        f32x4 l16v;
+        __builtin_memcpy(&l16v, lv, 16);
+        bstore16_agent(rl, p * 16, l16v);
+      }
     }
   }
 

@@ -136,7 +136,10 @@ typedef enum {
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
  * chunk in {0 (= 64), 32, 64}; dv_tile in {0, 16, 32} (0: 32 when 16-wide
  * state-chain workgroups would outnumber the compute units of the current
- * device, else 16); B, H >= 1, B*H <= 65535; 0 <= T <= 2^30 and
+ * device, else 16; exclusive readouts on bf16 operands take 16 and reject
+ * 32: they carry the state and the decayed q.k tile as bf16 hi + lo parts,
+ * whose staging fits 16-column tiles only); B, H >= 1, B*H <= 65535;
+ * 0 <= T <= 2^30 and
  * (T + 64) * H * max(dk, dv) * 4 < 2^32 (one batch element's rows, fp32,
  * fit 32-bit byte offsets). */
 typedef struct {
@@ -158,7 +161,9 @@ typedef struct {
 
 /* Bytes of workspace gdn_forward needs for this problem and direction
  * (0 if the problem is invalid or unsupported, and for T = 0, which needs
- * none).  Pure host arithmetic. */
+ * none).  It depends on p->options as well: exclusive readouts on bf16
+ * operands need about 2 C bytes more per token and head.  Pure host
+ * arithmetic. */
 size_t gdn_workspace_bytes(const gdn_problem_t* p, int32_t direction);
 
 /* Enqueue the scan described by `p` on p->stream.  See the file comment for

@@ -48,18 +48,3 @@ def check(got, ref, tol, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     assert r <= tol, f"{what}: max abs err {err:.3e} = {r:.3e} x RMS {rms:.3e} > {tol:.1e} x RMS"
     return r
-
-
-def check_scaled(got, ref, tol, scale, what=""):
-    """max |got - ref| <= tol * scale, for outputs whose own RMS is not the
-    scale of the terms they sum (an exclusive readout is the inclusive one
-    with the dominant self term removed, computed by the same products, so
-    its rounding error is set by the inclusive readout's RMS, passed as
-    ``scale``).  Returns the error relative to ``scale``."""
-    ref = np.asarray(ref, dtype=np.float64)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    err = float(np.max(np.abs(np.asarray(got, np.float64) - ref))) if ref.size else 0.0
-    r = err / max(scale, 1e-30)
-    assert r <= tol, f"{what}: max abs err {err:.3e} = {r:.3e} x scale {scale:.3e} > {tol:.1e} x scale"
-    return r
-

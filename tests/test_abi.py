@@ -86,6 +86,18 @@ def test_workspace_bytes():
     assert gdn.workspace_bytes(1, 0, 1, 64, 64, "bf16", "fwd") == 0  # an empty sequence needs none
 
 
+def test_workspace_bytes_of_exclusive_readouts():
+    """bf16 exclusive readouts also keep the low parts of the decayed q.k
+    tile: C x C bf16 per chunk and head (C = 64 here, 5 chunks, 2 heads);
+    fp32 operands need nothing more."""
+    for ex in ("fwd", "rev", "both"):
+        extra = (gdn.workspace_bytes(1, 300, 2, 128, 128, "bf16", "bi", exclusive=ex)
+                 - gdn.workspace_bytes(1, 300, 2, 128, 128, "bf16", "bi"))
+        assert 5 * 2 * 64 * 64 * 2 <= extra < 5 * 2 * 64 * 64 * 2 + 256
+        assert (gdn.workspace_bytes(1, 300, 2, 64, 64, "f32", "bi", exclusive=ex)
+                == gdn.workspace_bytes(1, 300, 2, 64, 64, "f32", "bi"))
+
+
 @pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=80), dict(chunk=48), dict(chunk=16), dict(dv_tile=64),
                                 dict(dtype=7), dict(B=0), dict(H=0), dict(T=-1), dict(B=300, H=300),
                                 dict(dv_tile=48), dict(T=1 << 20, H=8, dk=128, dv=128)])
@@ -256,3 +268,17 @@ def test_noalloc_rejects_problems_beyond_its_scratch_before_any_launch():
     # invalid arguments are still reported first
     assert gdn.gdn_forward_noalloc(small, None, None, None, None, None, None, None, None,
                                    gdn.GDN_DIR_FORWARD) == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_exclusive_bf16_rejects_32_wide_tiles():
+    """bf16 exclusive readouts run 16-column tiles only (the state's and the
+    q.k tile's low parts fit that staging): an explicit 32 is unsupported,
+    before anything is enqueued; fp32 and inclusive bf16 accept it."""
+    p = _prob(dv_tile=32)
+    p.options = gdn.GDN_OPT_EXCLUSIVE_FORWARD
+    assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_FORWARD) == 0
+    p.options = 0
+    assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_FORWARD) > 0
+    p = _prob(dv_tile=32, dtype=gdn.GDN_DTYPE_F32)
+    p.options = gdn.GDN_OPT_EXCLUSIVE_FORWARD
+    assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_FORWARD) > 0
