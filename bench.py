@@ -89,11 +89,12 @@ def host_cores():
     return avail, visible
 
 
-def sampled_parity(w, x, out, s_out, direction, erase=True, exclusive="none", threads=None) -> dict:
+def sampled_parity(w, x, out, s_out, direction, erase=True, exclusive="none", threads=None, epilogue=None) -> dict:
     """max |gpu - oracle| / RMS(oracle) over two (batch, head) chains computed
     in full by the oracle (every token, both directions when bidirectional,
-    and the final states).  Chains are independent, so this is the oracle
-    restricted to those chains."""
+    and the final states; with `epilogue`, the oracle's readout epilogue on
+    its output).  Chains are independent, so this is the oracle restricted
+    to those chains."""
     import numpy as np
 
     import oracle
@@ -101,6 +102,9 @@ def sampled_parity(w, x, out, s_out, direction, erase=True, exclusive="none", th
     heads = list(dict.fromkeys([(0, 0), (w.B - 1, w.H - 1)]))
     t0 = time.perf_counter()
     ro, rs = oracle.forward_heads(x, heads, direction, nthreads=threads, erase=erase, exclusive=exclusive)
+    if epilogue is not None:
+        gate = np.stack([epilogue["gate"][b, :, h] for b, h in heads])
+        ro = oracle.readout_epilogue(ro, gate, epilogue["norm_weight"], 1e-6)
     dt = time.perf_counter() - t0
 
     def rel(got, ref):
@@ -368,6 +372,8 @@ def main() -> int:
     ap.add_argument("--serial", action="store_true", help="keep the preparation pass before the chain (no overlap)")
     ap.add_argument("--no-erase", action="store_true",
                     help="time the erase-free variant (gated linear attention, GDN_OPT_NO_ERASE) instead of the delta rule")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="the readout epilogue (RMS norm over dv and sigmoid gate) after the scan")
     ap.add_argument("--exclusive", choices=["none", "fwd", "rev", "both"], default="none",
                     help="directions that read before the token's own write (GDN_OPT_EXCLUSIVE_*: disjoint regions)")
     ap.add_argument("--vda", action="store_true",
@@ -399,6 +405,10 @@ def main() -> int:
     xs = 2 if w.dtype == "bf16" else 4
     x = synth.generate(w)
     d = {k: _dev(v) for k, v in x.items()}
+    epi = {}
+    if args.epilogue:
+        e = synth.generate_epilogue(w)
+        epi = dict(gate=_dev(e["gate"]), norm_weight=_dev(e["norm_weight"]), norm_eps=1e-6)
     out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
     s_out = torch.empty((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
     nws = gdn.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.direction, args.chunk, args.dv_tile,
@@ -409,7 +419,7 @@ def main() -> int:
     def step(ev_ptr=None):
         gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction, chunk=args.chunk,
                     dv_tile=args.dv_tile, out=out, state_out=s_out, workspace=ws, timing_events=ev_ptr,
-                    serial=args.serial, erase=not args.no_erase, exclusive=args.exclusive)
+                    serial=args.serial, erase=not args.no_erase, exclusive=args.exclusive, **epi)
 
     for _ in range(args.warmup):
         step()
@@ -484,6 +494,7 @@ def main() -> int:
                    "prep": "concurrent with the chain" if concurrent else "before the chain",
                    "operator": "erase-free (gated linear attention)" if args.no_erase else "gated delta rule",
                    "exclusive_readout": args.exclusive,
+                   "readout_epilogue": bool(args.epilogue),
                    "inputs": "seeded synthetic video-latent-shaped (synth.WORKLOADS)"},
         "tflops": tflops,
         "mfma_frac": tflops / peak_mfma,
@@ -498,7 +509,7 @@ def main() -> int:
                      # the committed counters were taken with the default options
                      "traffic": (measured_traffic(dom_name, args.workload)
                                  if not args.no_erase and args.exclusive == "none" and not args.chunk
-                                 and not args.dv_tile else None),
+                                 and not args.dv_tile and not args.epilogue else None),
                      "alg_bytes_per_launch": dom_bytes,
                      "workspace_bytes_per_launch": nws,
                      "avg_launch_ms": kt[dom], "source_hash": kernel_source_hash(dom_name)},
@@ -506,7 +517,8 @@ def main() -> int:
     }
     if not args.no_parity:
         res["parity"] = sampled_parity(w, x, out, s_out, w.direction, erase=not args.no_erase,
-                                       exclusive=args.exclusive, threads=host_cores()[0])
+                                       exclusive=args.exclusive, threads=host_cores()[0],
+                                       epilogue=e if args.epilogue else None)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, erase=not args.no_erase, exclusive=args.exclusive)
         res["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]

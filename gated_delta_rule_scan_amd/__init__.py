@@ -58,6 +58,7 @@ class gdn_problem_t(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("timing_events", ctypes.c_void_p),
+        ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -164,7 +165,7 @@ def _record_on(stream, tensors) -> None:
 def make_problem(B, T, H, dk, dv, dtype: int, chunk: int = 0, dv_tile: int = 0, workspace: int = 0,
                  workspace_bytes: int = 0, stream: int = 0) -> gdn_problem_t:
     return gdn_problem_t(B, T, H, dk, dv, dtype, chunk, dv_tile, 0, workspace or None, workspace_bytes,
-                         stream or None, None)
+                         stream or None, None, None, None, 0.0)
 
 
 def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd", chunk: int = 0,
@@ -178,7 +179,7 @@ def workspace_bytes(B, T, H, dk, dv, dtype: str = "bf16", direction: str = "fwd"
 def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chunk: int = 0, dv_tile: int = 0,
             out=None, state_out=None, workspace=None, want_state: bool = True, stream=None,
             timing_events: Optional[int] = None, serial: bool = False, erase: bool = True,
-            exclusive: str = "none") -> Tuple:
+            exclusive: str = "none", gate=None, norm_weight=None, norm_eps: float = 1e-6) -> Tuple:
     """Run the scan on torch CUDA tensors (layouts of include/gdn.h).
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv] (float32 or bfloat16, same dtype);
@@ -195,6 +196,9 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     bidirectional call cover disjoint regions, "rev" alone counts every
     token once.
     ``timing_events``: address of four caller-owned hipEvent_t (see gdn.h).
+    ``gate`` [B,T,H,dv] (the type of q) with ``norm_weight`` [dv] float32: the
+    readout epilogue, out = norm_weight * o / sqrt(mean_dv(o^2) + norm_eps) *
+    sigmoid(gate) per (token, head).
     """
     import torch
 
@@ -227,8 +231,18 @@ def forward(q, k, v, log_alpha, beta, state_in=None, direction: str = "fwd", chu
     if state_out is None and want_state:
         state_out = torch.empty((dirs, B, H, dv, dk), dtype=torch.float32, device=dev)
         mine.append(state_out)
+    if gate is not None:
+        if gate.dtype != q.dtype or not gate.is_contiguous() or tuple(gate.shape) != (B, T, H, dv):
+            raise ValueError(f"gate must be contiguous [{B},{T},{H},{dv}] of the type of q")
+        if norm_weight is None or norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (dv,):
+            raise ValueError(f"norm_weight must be float32 [{dv}] when gate is given")
+        if not norm_weight.is_contiguous():
+            norm_weight = norm_weight.contiguous()
+            mine.append(norm_weight)
     prob = make_problem(B, T, H, dk, dv, dt, chunk, dv_tile)
     prob.options = (GDN_OPT_SERIAL if serial else 0) | (0 if erase else GDN_OPT_NO_ERASE) | EXCLUSIVE[exclusive]
+    if gate is not None:
+        prob.gate, prob.norm_weight, prob.norm_eps = gate.data_ptr(), norm_weight.data_ptr(), norm_eps
     nbytes = gdn_workspace_bytes(prob, DIRECTIONS[direction])
     if nbytes == 0 and T > 0:
         raise GdnError(GDN_ERR_UNSUPPORTED)
@@ -341,14 +355,17 @@ def register_torch_ops() -> None:
 
     @torch.library.custom_op("gdn::forward", mutates_args=(), device_types="cuda",
                              schema="(Tensor q, Tensor k, Tensor v, Tensor log_alpha, Tensor beta, Tensor? state_in, "
-                                    "str direction, int chunk, int dv_tile, bool erase, str exclusive=\"none\") "
+                                    "str direction, int chunk, int dv_tile, bool erase, str exclusive=\"none\", "
+                                    "Tensor? gate=None, Tensor? norm_weight=None, float norm_eps=1e-06) "
                                     "-> (Tensor, Tensor)")
-    def _forward_op(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase, exclusive="none"):
+    def _forward_op(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase, exclusive="none",
+                    gate=None, norm_weight=None, norm_eps=1e-6):
         return forward(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase=erase,
-                       exclusive=exclusive)
+                       exclusive=exclusive, gate=gate, norm_weight=norm_weight, norm_eps=norm_eps)
 
     @_forward_op.register_fake
-    def _(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase, exclusive="none"):
+    def _(q, k, v, log_alpha, beta, state_in, direction, chunk, dv_tile, erase, exclusive="none", gate=None,
+          norm_weight=None, norm_eps=1e-6):
         B, T, H, dk = q.shape
         dv = v.shape[-1]
         dirs = 2 if direction == "bi" else 1

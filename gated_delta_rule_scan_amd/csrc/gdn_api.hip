@@ -69,6 +69,8 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
     return GDN_ERR_INVALID_ARGUMENT;
   // the test option needs the ready-flag path, which the serial order does not take
   if ((p->options & GDN_OPT_TEST_NO_PREPARATION) && (p->options & GDN_OPT_SERIAL)) return GDN_ERR_INVALID_ARGUMENT;
+  // the readout epilogue: a weight vector and a finite, non-negative eps
+  if (p->gate && (!p->norm_weight || !(p->norm_eps >= 0.f) || !(p->norm_eps <= 3.4e38f))) return GDN_ERR_INVALID_ARGUMENT;
   if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
   if (!supported_dim(p->dk) || !supported_dim(p->dv)) return GDN_ERR_UNSUPPORTED;
   if (p->B * p->H > 65535) return GDN_ERR_UNSUPPORTED;  // grid limit of the preparation kernel
@@ -182,22 +184,27 @@ chain_fn chain_for3(int NT, int dirs) {
   return dirs == 2 ? launch_chain<MT, DK, C, 2, true> : launch_chain<MT, DK, C, 2, false>;
 }
 
+template <int DK, int C, int PREC>
+chain_fn column_chain_for4(int NT, int dirs) {
+  if (NT == 1) return dirs == 2 ? launch_column_chain<DK, C, 1, true, PREC> : launch_column_chain<DK, C, 1, false, PREC>;
+  return dirs == 2 ? launch_column_chain<DK, C, 2, true, PREC> : launch_column_chain<DK, C, 2, false, PREC>;
+}
+
 template <int DK, int C>
-chain_fn column_chain_for3(int NT, int dirs, bool plo) {
-  if (plo) {  // 16-column tiles only
+chain_fn column_chain_for3(int NT, int dirs, int prec) {
+  if (prec == 2) {  // 16-column tiles only
     if (NT != 1) return nullptr;
-    return dirs == 2 ? launch_column_chain<DK, C, 1, true, true> : launch_column_chain<DK, C, 1, false, true>;
+    return dirs == 2 ? launch_column_chain<DK, C, 1, true, 2> : launch_column_chain<DK, C, 1, false, 2>;
   }
-  if (NT == 1) return dirs == 2 ? launch_column_chain<DK, C, 1, true, false> : launch_column_chain<DK, C, 1, false, false>;
-  return dirs == 2 ? launch_column_chain<DK, C, 2, true, false> : launch_column_chain<DK, C, 2, false, false>;
+  return prec == 1 ? column_chain_for4<DK, C, 1>(NT, dirs) : column_chain_for4<DK, C, 0>(NT, dirs);
 }
 
 // bf16 operands: the column-owning chain; fp32 operands: the two-role chain
 template <typename MT>
-chain_fn chain_for(int dk, int C, int NT, int dirs, bool plo) {
+chain_fn chain_for(int dk, int C, int NT, int dirs, int prec) {
   if constexpr (sizeof(MT) == 2) {
-    if (dk == 64) return C == 32 ? column_chain_for3<64, 32>(NT, dirs, plo) : column_chain_for3<64, 64>(NT, dirs, plo);
-    return C == 32 ? column_chain_for3<128, 32>(NT, dirs, plo) : column_chain_for3<128, 64>(NT, dirs, plo);
+    if (dk == 64) return C == 32 ? column_chain_for3<64, 32>(NT, dirs, prec) : column_chain_for3<64, 64>(NT, dirs, prec);
+    return C == 32 ? column_chain_for3<128, 32>(NT, dirs, prec) : column_chain_for3<128, 64>(NT, dirs, prec);
   } else {
     if (dk == 64) return C == 32 ? chain_for3<MT, 64, 32>(NT, dirs) : chain_for3<MT, 64, 64>(NT, dirs);
     return C == 32 ? chain_for3<MT, 128, 32>(NT, dirs) : chain_for3<MT, 128, 64>(NT, dirs);
@@ -238,6 +245,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
     if (!aligned(log_alpha, 4) || !aligned(beta, 4)) return GDN_ERR_INVALID_ARGUMENT;
   }
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16))) return GDN_ERR_INVALID_ARGUMENT;
+  if (p->gate && (!aligned(p->gate, 16) || !aligned(p->norm_weight, 16))) return GDN_ERR_INVALID_ARGUMENT;
   const bool need_ws = T > 0;
   if (need_ws) {
     if (!ws_ptr || !aligned(ws_ptr, 256)) return GDN_ERR_INVALID_ARGUMENT;
@@ -250,11 +258,12 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   const Range r_la = rng(log_alpha, n_g * 4), r_b = rng(beta, n_g * 4);
   const Range r_si = rng(state_in, n_s * 4), r_so = rng(state_out, n_s * 4);
   const Range r_o = rng(out, n_v * 4), r_ws = rng(need_ws ? ws_ptr : nullptr, pl.ws.total);
-  const Range ins[] = {r_q, r_k, r_v, r_la, r_b, r_si};
+  const Range r_g = rng(p->gate, n_v * es), r_nw = rng(p->gate ? p->norm_weight : nullptr, (size_t)dv * 4);
+  const Range ins[] = {r_q, r_k, r_v, r_la, r_b, r_g, r_nw, r_si};
   for (const Range& r : ins) {
     if (overlap(r_o, r) || overlap(r_ws, r)) return GDN_ERR_INVALID_ARGUMENT;
   }
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 7; ++i)
     if (overlap(r_so, ins[i])) return GDN_ERR_INVALID_ARGUMENT;
   if (overlap(r_so, r_si) && state_in != state_out) return GDN_ERR_INVALID_ARGUMENT;
   if (overlap(r_o, r_so) || overlap(r_o, r_ws) || overlap(r_so, r_ws)) return GDN_ERR_INVALID_ARGUMENT;
@@ -290,14 +299,25 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   // bidirectional: one workgroup per direction, readouts accumulated into
   // the output the preparation kernel filled; single direction: told whether
   // it runs in reverse
-  chain_fn cf = bf ? chain_for<bf16>((int)dk, pl.C, pl.NT, pl.dirs, pl.plo)
-                   : chain_for<float>((int)dk, pl.C, pl.NT, pl.dirs, false);
+  chain_fn cf = bf ? chain_for<bf16>((int)dk, pl.C, pl.NT, pl.dirs, pl.plo ? 2 : (p->gate ? 1 : 0))
+                   : chain_for<float>((int)dk, pl.C, pl.NT, pl.dirs, 0);
   prep_fn pf = bf ? prep_for<bf16>((int)dk, pl.C) : prep_for<float>((int)dk, pl.C);
   if (!cf || !pf) return GDN_ERR_UNSUPPORTED;
   const int rev_single = direction == GDN_DIR_REVERSE ? 1 : 0;
   hipEvent_t* ev = static_cast<hipEvent_t*>(p->timing_events);
   auto mark = [&](int i, hipStream_t st) { return !ev || hipEventRecord(ev[i], st) == hipSuccess; };
 
+  // the readout epilogue, after the chain on `stream`
+  auto epilogue = [&]() -> bool {
+    if (!p->gate || T == 0) return true;
+    const int64_t rows = B * T * H;
+    hipError_t e;
+    if (bf) e = dv == 64 ? launch_epilogue<bf16, 64>(out, p->gate, p->norm_weight, p->norm_eps, rows, stream)
+                         : launch_epilogue<bf16, 128>(out, p->gate, p->norm_weight, p->norm_eps, rows, stream);
+    else e = dv == 64 ? launch_epilogue<float, 64>(out, p->gate, p->norm_weight, p->norm_eps, rows, stream)
+                      : launch_epilogue<float, 128>(out, p->gate, p->norm_weight, p->norm_eps, rows, stream);
+    return e == hipSuccess;
+  };
   const bool skip_prep = (p->options & GDN_OPT_TEST_NO_PREPARATION) != 0;
   if (skip_prep && pl.NC > 0) {
     // flags marked pending and never cleared: the chain's bounded waits expire
@@ -305,7 +325,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
     if (launch_clear_ready(a.ready, B * H * pl.NC, stream) != hipSuccess) return GDN_ERR_HIP;
     if (!mark(0, stream) || !mark(1, stream) || !mark(2, stream)) return GDN_ERR_HIP;
     if (cf(a, rev_single, stream, nullptr) != hipSuccess || !mark(3, stream)) return GDN_ERR_HIP;
-    return GDN_OK;
+    return epilogue() ? GDN_OK : GDN_ERR_HIP;
   }
   // Under stream capture the two kernels always run one after the other: a
   // graph orders its nodes only by their dependencies, so nothing would make
@@ -332,7 +352,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
     if (hipEventRecord(side->join, side->stream) != hipSuccess) return GDN_ERR_HIP;
     if (!mark(2, stream) || cf(a, rev_single, stream, nullptr) != hipSuccess || !mark(3, stream)) return GDN_ERR_HIP;
     if (hipStreamWaitEvent(stream, side->join, 0) != hipSuccess) return GDN_ERR_HIP;
-    return GDN_OK;
+    return epilogue() ? GDN_OK : GDN_ERR_HIP;
   }
   // one after the other on the caller's stream (no flags: a.ready stays null)
   if (!mark(0, stream)) return GDN_ERR_HIP;
@@ -340,7 +360,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   if (!mark(1, stream) || !mark(2, stream)) return GDN_ERR_HIP;
   if (cf(a, rev_single, stream, nullptr) != hipSuccess) return GDN_ERR_HIP;
   if (!mark(3, stream)) return GDN_ERR_HIP;
-  return GDN_OK;
+  return epilogue() ? GDN_OK : GDN_ERR_HIP;
 }
 
 // ---- the fixed device scratch of gdn_forward_noalloc ----

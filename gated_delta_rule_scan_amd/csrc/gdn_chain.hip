@@ -84,7 +84,7 @@ struct ChainSmem {
   // value tile.  Double buffered by step parity.
   static constexpr int ST_SC = 0;
   static constexpr int ST_PD = C * 16;
-  static constexpr int ST_GN = ST_PD + C * 4;
+  static constexpr int ST_GN = ST_PD;  // the record starts with the chunk's decay
   static constexpr int ST_V = ST_PD + (C + 4) * 4;
   static constexpr int ST_BYTES = ST_V + C * DT * ES;
 };
@@ -472,7 +472,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     const unsigned char* sg = stg[s_prev & 1];
     frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
     if constexpr (SPLIT) {
-      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + kq_row * 4));
+      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + 16 + kq_row * 4));
 #pragma unroll
       for (int e = 0; e < 8; ++e) pdiag[e] = r;
     }

@@ -106,6 +106,10 @@ __device__ __forceinline__ void mem_fence_compiler() {
 __device__ __forceinline__ void dma16(rsrc_t r, lds_u8* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, 0, 0, 0);
 }
+// 4 bytes per lane into LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma4(rsrc_t r, lds_u8* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, 0, 0, 0);
+}
 
 __device__ __forceinline__ v4s tr16(const lds_u8* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)const_cast<lds_u8*>(p));
@@ -114,8 +118,14 @@ __device__ __forceinline__ v4s tr16(const lds_u8* p) {
 // token order of the chain's product rows (see the file comment)
 __host__ __device__ constexpr int tau(int rt, int m) { return 32 * (rt >> 1) + 8 * (m >> 2) + 4 * (rt & 1) + (m & 3); }
 
-template <int DK, int C, int NT, bool PLO>
+// PREC: 0, the readout's entry state and the decayed q.k tile in bf16; 1,
+// the state as bf16 hi + lo parts (scans with the readout epilogue, whose
+// per-row normalisation magnifies the error of small rows); 2, also the tile
+// as hi + lo parts in the directions that read before the token's own write
+// (exclusive readouts: outputs ten times smaller than the terms they sum).
+template <int DK, int C, int NT, int PREC>
 struct Col {
+  static constexpr bool SLO = PREC >= 1, PLO = PREC >= 2;
   static constexpr int DT = 16 * NT;             // value columns per workgroup
   static constexpr int RT = C / 16;              // 16-token row tiles per chunk
   static constexpr int KC = C / 32;              // 32-token k-chunks
@@ -125,19 +135,21 @@ struct Col {
   static constexpr int TROWB = C * 2;            // bytes per triangle row
   static constexpr int VROWB = DT * 2;           // bytes per value-tile row
   static constexpr int KB = C * KROWB, TB = C * TROWB, VB = C * VROWB;
-  // chain slot: k | Tinv | v | scales | remainders and chunk decay
-  static constexpr int CK = 0, CT = CK + KB, CV = CT + TB, CS = CV + VB, CP = CS + 1024, CSLOT = CP + 1024;
-  // readout slot: q | P | scales | remainders; with PLO: q | P | low parts
-  // of P (a direction reading before the token's own write) or the
-  // remainders (one that does not) | scales
+  // chain slot: k | Tinv | v | scales | the head of the chunk record (its
+  // decay; one 4-byte-per-lane load of 256 bytes)
+  static constexpr int CK = 0, CT = CK + KB, CV = CT + TB, CS = CV + VB, CP = CS + 1024, CSLOT = CP + 256;
+  // readout slot: q | P | [PLO: P's low parts in a direction reading before
+  // the token's own write, else zeros] | e^g rq per token | the self-term
+  // remainders per token (the last two: one 4-byte-per-lane load each)
   static constexpr int RQ = 0, RP = RQ + KB, RL = RP + TB;
-  static constexpr int RS = PLO ? RL + TB : RL, RD = PLO ? RL : RS + 1024, RSLOT = RS + (PLO ? 1024 : 2048);
-  // exchange, per chain wave: entry-state fragments (bf16; with PLO also
+  static constexpr int RS = RL + (PLO ? TB : 0), RD = RS + 256, RSLOT = RD + 256;
+  // exchange, per chain wave: entry-state fragments (bf16; with SLO also
   // their low parts), Vnew (fp32, the eight values of a k-chunk operand
   // fragment per lane)
-  static constexpr int XS = 0, XSL = KS * 1024, XV = XSL + (PLO ? KS * 1024 : 0), XJ = XV + KC * 2048,
+  static constexpr int XS = 0, XSL = KS * 1024, XV = XSL + (SLO ? KS * 1024 : 0), XJ = XV + KC * 2048,
                        XSLOT = NT * XJ;
-  static constexpr int NDC = CSLOT / 1024, NDR = RSLOT / 1024;  // 1-KB loads per slot
+  // loads per slot: 1 KB each, but the chain's last and the readout's last two (256 B)
+  static constexpr int NDC = CP / 1024 + 1, NDR = RS / 1024 + 2;
   static_assert(KB % 1024 == 0 && TB % 1024 == 0 && VB % 1024 == 0, "whole 1-KB loads");
   static_assert(C == 32 || C == 64, "chunk");
 };
@@ -154,7 +166,7 @@ enum : int { R_KTAU = 0, R_QNAT = 1, R_TTAU = 2, R_PNAT = 3, R_VAL = 4, R_RAW = 
 
 template <int DK, int C, int NT>
 __device__ __forceinline__ uint32_t dma_voff(int kind, int ii, int lane, uint32_t HDB, uint32_t HVB) {
-  using L = Col<DK, C, NT, false>;
+  using L = Col<DK, C, NT, 0>;
   const int b = ii * 1024 + 16 * lane;  // byte within the staged region
   if (kind == R_KTAU || kind == R_QNAT) {
     const int rho = b / L::KROWB, q = (b % L::KROWB) >> 4;
@@ -238,9 +250,10 @@ __device__ __forceinline__ void make_mask(uint32_t (&m)[4], int row, int col0, b
 
 }  // namespace
 
-template <int DK, int C, int NT, bool BI, bool PLO>
+template <int DK, int C, int NT, bool BI, int PREC>
 __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
-  using L = Col<DK, C, NT, PLO>;
+  using L = Col<DK, C, NT, PREC>;
+  constexpr bool SLO = L::SLO, PLO = L::PLO;
   using M = Mma<bf16>;
   constexpr int RT = L::RT, KC = L::KC, KS = L::KS, SRT = L::SRT, DT = L::DT;
 
@@ -319,12 +332,17 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         voff[n] = byte < L::CT   ? dma_voff<DK, C, NT>(R_KTAU, (byte - L::CK) / 1024, lane, HDB, HVB)
                   : byte < L::CV ? dma_voff<DK, C, NT>(R_TTAU, (byte - L::CT) / 1024, lane, HDB, HVB)
                   : byte < L::CS ? dma_voff<DK, C, NT>(R_VAL, (byte - L::CV) / 1024, lane, HDB, HVB)
-                                 : 16u * lane;
-      } else {
+                  : byte < L::CP ? 16u * lane
+                                 : 4u * lane;
+      } else if (i < L::RS / 1024) {
         voff[n] = byte < L::RP   ? dma_voff<DK, C, NT>(R_QNAT, (byte - L::RQ) / 1024, lane, HDB, HVB)
                   : byte < L::RL ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RP) / 1024, lane, HDB, HVB)
-                  : (PLO && byte < L::RS && plo_dir) ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RL) / 1024, lane, HDB, HVB)
-                                                     : 16u * lane;
+                  : plo_dir      ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RL) / 1024, lane, HDB, HVB)
+                                 : 16u * lane;
+      } else {
+        // e^g rq: the third float of each token's scale record; the
+        // remainders: the record after its 16-byte head
+        voff[n] = i == L::RS / 1024 ? 16u * lane + 8u : 16u + 4u * lane;
       }
     }
   };
@@ -342,24 +360,29 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
 #pragma unroll
       for (int i = J; i < L::NDC; i += NT, ++n) {
         const int byte = i * 1024;
-        const rsrc_t r = byte < L::CT ? rkq : byte < L::CV ? rtp : byte < L::CS ? rv : byte < L::CP ? rsc : rpd;
-        dma16(r, slotp + byte, voff[n]);
+        if (byte >= L::CP) {
+          dma4(rpd, slotp + byte, voff[n]);  // the record's head: the chunk decay
+        } else {
+          const rsrc_t r = byte < L::CT ? rkq : byte < L::CV ? rtp : byte < L::CS ? rv : rsc;
+          dma16(r, slotp + byte, voff[n]);
+        }
       }
     } else {
-      // PLO: the low parts of P, or the remainders followed by loads
-      // through the empty resource (the same count either way)
+      // PLO: the low parts of P, or loads through the empty resource (the
+      // same count either way)
       const rsrc_t rpl = make_rsrc(pqlb + (size_t)c * L::TB, (uint32_t)L::TB);
       int n = 0;
 #pragma unroll
       for (int i = J; i < L::NDR; i += NT, ++n) {
         const int byte = i * 1024;
-        rsrc_t r;
-        if (byte < L::RP) r = rkq;
-        else if (byte < L::RL) r = rtp;
-        else if (PLO && byte < L::RS) r = plo_dir ? rpl : (byte == L::RL ? rpd : rnone);
-        else if (byte < L::RS + 1024) r = rsc;
-        else r = rpd;
-        dma16(r, slotp + byte, voff[n]);
+        if (i < L::RS / 1024) {
+          const rsrc_t r = byte < L::RP ? rkq : byte < L::RL ? rtp : plo_dir ? rpl : rnone;
+          dma16(r, slotp + byte, voff[n]);
+        } else if (i == L::RS / 1024) {
+          dma4(rsc, slotp + L::RS, voff[n]);
+        } else {
+          dma4(rpd, slotp + L::RD, voff[n]);
+        }
       }
     }
   };
@@ -491,7 +514,7 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
       bf16x8 sb[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (PLO) {
+        if constexpr (SLO) {
           bf16x8 sl;
           split8(Sacc[2 * ks], Sacc[2 * ks + 1], sb[ks], sl);
           lds_put(X + L::XSL + ks * 1024 + lane * 16, sl);
@@ -554,7 +577,7 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
       }
       // S = e^{g_last} S + K^T Vs: the transposed k fragment of state tile
       // srt = 2 ks + u and k-chunk kc holds k[32 kc + 8 g4 + e][pi(srt, l16)]
-      const float gn = lds_f(Pd + C * 4);
+      const float gn = lds_f(Pd);  // the record's head
       // S e^{g_last}: exactly zero when the chunk's decay is (finite states;
       // a NaN state from an expired wait keeps its NaN)
       if (gn != 0.f || gave_up) {
@@ -753,12 +776,9 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 qb = lds_frag(Qt + t * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(t)) << 4));
           z = M::mma(sr[ks], qb, z);
-          if constexpr (PLO) {
-            // the entry state's low parts (a direction reading before the token's own write)
-            if (plo_dir) z = M::mma(lds_frag(X + L::XSL + ks * 1024 + lane * 16), qb, z);
-          }
+          if constexpr (SLO) z = M::mma(lds_frag(X + L::XSL + ks * 1024 + lane * 16), qb, z);  // the state's low parts
         }
-        const float zs = lds_f(Sc + t * 16 + 8);  // e^g rq of the token
+        const float zs = lds_f(Sc + t * 4);  // e^g rq of the token
         f32x4 o = z * zs;
         // + Vnew^T P^T
         const int kd = tt >> 1;
@@ -828,24 +848,24 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
   }
 }
 
-template <int DK, int C, int NT, bool BI, bool PLO>
+template <int DK, int C, int NT, bool BI, int PREC>
 hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query) {
-  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&column_chain_kernel<DK, C, NT, BI, PLO>));
+  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&column_chain_kernel<DK, C, NT, BI, PREC>));
   const int ntiles = a.dv / (16 * NT);
   const int nbh = (int)(a.B * a.H);
   const unsigned nblocks = (unsigned)chain_blocks(nbh, a.dv, NT, BI ? 2 : 1);
-  hipLaunchKernelGGL((column_chain_kernel<DK, C, NT, BI, PLO>), dim3(nblocks), dim3(128 * NT), 0, stream, a,
+  hipLaunchKernelGGL((column_chain_kernel<DK, C, NT, BI, PREC>), dim3(nblocks), dim3(128 * NT), 0, stream, a,
                      rev_single, ntiles, nbh);
   return hipGetLastError();
 }
 
-#define GDN_INST_COL(DK, C, NT, BI, PLO) \
-  template hipError_t launch_column_chain<DK, C, NT, BI, PLO>(const ScanArgs&, int, hipStream_t, hipFuncAttributes*);
-// PLO (exclusive readouts): 16-column tiles only (its LDS would not fit 32)
-#define GDN_INST_COL_P(DK, C, NT, BI) GDN_INST_COL(DK, C, NT, BI, false) \
+#define GDN_INST_COL(DK, C, NT, BI, PREC) \
+  template hipError_t launch_column_chain<DK, C, NT, BI, PREC>(const ScanArgs&, int, hipStream_t, hipFuncAttributes*);
+// PREC 2 (exclusive readouts): 16-column tiles only (its LDS would not fit 32)
+#define GDN_INST_COL_P(DK, C, NT, BI) GDN_INST_COL(DK, C, NT, BI, 0) GDN_INST_COL(DK, C, NT, BI, 1) \
   GDN_INST_COL_IF_NT1(DK, C, NT, BI)
 #define GDN_INST_COL_IF_NT1(DK, C, NT, BI) GDN_INST_COL_PLO_##NT(DK, C, BI)
-#define GDN_INST_COL_PLO_1(DK, C, BI) GDN_INST_COL(DK, C, 1, BI, true)
+#define GDN_INST_COL_PLO_1(DK, C, BI) GDN_INST_COL(DK, C, 1, BI, 2)
 #define GDN_INST_COL_PLO_2(DK, C, BI)
 #define GDN_INST_COL_D(DK, C, NT) GDN_INST_COL_P(DK, C, NT, false) GDN_INST_COL_P(DK, C, NT, true)
 #define GDN_INST_COL_N(DK, C) GDN_INST_COL_D(DK, C, 1) GDN_INST_COL_D(DK, C, 2)

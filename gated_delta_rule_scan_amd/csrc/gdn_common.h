@@ -195,13 +195,13 @@ __device__ __forceinline__ bf16x8 load_kt_frag(const bf16* krow, int kp, int tok
 //                             the diagonal; strictly-lower part = forward,
 //                             strictly-upper part = reverse
 //   sc   [dirs][NBH*NC][C] float4 : {beta, e^g rk, e^g rq, e^(gn-g) rk}
-//   pdg  [dirs][NBH*NC][PDS] float : per token, the part of the self term
-//                             q^_t.k^_t that the operand type of pqk drops
-//                             (x - MT(x); zero for fp32 operands), then
-//                             e^(gn) (the chunk's total decay) and three
-//                             zeros (C + 4 floats: whole 16-byte pieces),
-//                             padded to PDS = pdg_stride(C) floats so that no
-//                             128-byte cache line holds two chunks' records
+//   pdg  [dirs][NBH*NC][PDS] float : e^(gn) (the chunk's total decay) and
+//                             three zeros, then per token the part of the
+//                             self term q^_t.k^_t that the operand type of
+//                             pqk drops (x - MT(x); zero for fp32 operands)
+//                             (C + 4 floats: whole 16-byte pieces), padded to
+//                             PDS = pdg_stride(C) floats so that no 128-byte
+//                             cache line holds two chunks' records
 //   rdy  [NBH][NC] uint32 : per-chunk ready flags of the concurrent
 //                             preparation: a small kernel marks every chunk 1
 //                             (pending), the preparation kernel stores 0 once

@@ -40,10 +40,18 @@ hipError_t launch_chain(const ScanArgs& a, int rev_single, hipStream_t stream, h
 // arguments, grid and results contract as launch_chain<bf16, ...>, except
 // that a bidirectional launch signals its partial readouts through
 // a.part_flags (cleared by the preparation kernel, which must have finished).
-// PLO: the decayed q.k tile also as its bf16 low parts (a.pq_lo), added in
-// the readouts of the directions that read before the token's own write.
-template <int DK, int C, int NT, bool BI, bool PLO>
+// PREC: 0, bf16 operands throughout; 1, the readout's entry state also as
+// its bf16 low parts (scans with the readout epilogue); 2, in addition the
+// decayed q.k tile's low parts (a.pq_lo), added in the readouts of the
+// directions that read before the token's own write (NT = 1 only).
+template <int DK, int C, int NT, bool BI, int PREC>
 hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t stream, hipFuncAttributes* query);
+
+// The token scan's readout epilogue, in place on `out` ([rows, DV] fp32):
+// out = norm_weight * o / sqrt(mean(o^2) + eps) * sigmoid(gate) per row.
+template <typename MT, int DV>
+hipError_t launch_epilogue(float* out, const void* gate, const float* norm_weight, float eps, int64_t rows,
+                           hipStream_t stream);
 
 // Workgroups of a state-chain launch (one per value tile, direction and
 // sequence; sequences padded to a multiple of eight).

@@ -350,8 +350,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
                      in ? f32x4{s_bt[dir][tok], a.erase ? eg * rk : 0.f, eg * rq, exp2f((float)(gl - g)) * rk}
                         : f32x4{0.f, 0.f, 0.f, 0.f});
       const rsrc_t rp = make_rsrc(a.pdg + ((size_t)slot * nch + cid) * pdg_stride(C), (C + 4) * 4);
-      bstore4_agent(rp, tok * 4, self - (float)self_mt);
-      if (tok < 4) bstore4_agent(rp, (C + tok) * 4, tok == 0 ? exp2f((float)gl) : 0.f);
+      bstore4_agent(rp, (4 + tok) * 4, self - (float)self_mt);
+      if (tok < 4) bstore4_agent(rp, tok * 4, tok == 0 ? exp2f((float)gl) : 0.f);
     }
   }
   __syncthreads();

@@ -156,7 +156,19 @@ typedef struct {
                                before and after the chunk-preparation kernel on
                                the stream it runs on, then before and after the
                                state-chain kernel on `stream` (per-kernel
-                               timing) */
+                               timing; the epilogue, if any, runs after the
+                               last of them) */
+  /* Readout epilogue ("Video DeltaNet", "Key Contributions" item 1: the
+   * linear branch's readout is RMS-normalised and sigmoid-gated).  With
+   * gate != NULL, after the scan, every (token, head) row of `out` becomes
+   *   out = norm_weight * o / sqrt(mean_dv(o^2) + norm_eps) * sigmoid(gate),
+   * o being the row as the scan computed it (inclusive or exclusive, both
+   * directions summed).  A separate pass on `stream`: the channels of one
+   * row are split over several state-chain workgroups.  Zero-initialise
+   * these fields (as make_problem-style helpers do) for no epilogue. */
+  const void* gate;          /* NULL, or [B, T, H, dv] of the type of q, 16-byte aligned */
+  const float* norm_weight;  /* [dv] fp32, shared by the heads; required with gate */
+  float norm_eps;            /* epilogue only: finite, >= 0 */
 } gdn_problem_t;
 
 /* Bytes of workspace gdn_forward needs for this problem and direction

@@ -70,6 +70,24 @@ def as_f32(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32)
 
 
+def readout_epilogue(out, gate, norm_weight, norm_eps: float = 1e-6) -> np.ndarray:
+    """The readout epilogue ("Video DeltaNet", "Key Contributions" item 1:
+    the linear branch's readout is RMS-normalised and passed through a
+    sigmoid gate), on every row of ``out`` [..., dv]:
+
+        y = norm_weight * o / sqrt(mean_dv(o^2) + norm_eps) * sigmoid(gate)
+
+    Readings (the page names the normalisation and the gate only): the mean
+    runs over the dv channels of one (token, head) row; eps sits inside the
+    root; ``norm_weight`` is one vector of dv weights shared by the heads;
+    ``gate`` has the shape of ``out`` (bf16 bit patterns or float32)."""
+    o = np.asarray(out, np.float64)
+    z = as_f32(gate).astype(np.float64)
+    w = np.asarray(norm_weight, np.float64)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + norm_eps)
+    return w * (o / rms) / (1.0 + np.exp(-z))
+
+
 def default_threads() -> int:
     try:
         return max(1, len(os.sched_getaffinity(0)))

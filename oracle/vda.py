@@ -61,7 +61,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import as_f32
+from . import as_f32, readout_epilogue
 
 EPS = 1e-6
 
@@ -139,10 +139,7 @@ def forward(q, k, v, log_alpha, beta, state_in: Optional[np.ndarray], direction:
                     out[b, t0:t1, h] += qh[b, t0:t1, h] @ R.T
                 s_out[slot, b, h] = S
     if gate is not None:
-        z = as_f32(gate).astype(np.float64)
-        w = np.asarray(norm_weight, np.float64)
-        rms = np.sqrt(np.mean(out * out, axis=-1, keepdims=True) + norm_eps)
-        out = w * (out / rms) / (1.0 + np.exp(-z))
+        out = readout_epilogue(out, gate, norm_weight, norm_eps)
     if return_states:
         return out, s_out, states
     return out, s_out

@@ -43,11 +43,13 @@ def test_problem_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "gdn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %d %d %d %d %d\\n", sizeof(gdn_problem_t), offsetof(gdn_problem_t, dtype),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %d %d %d %d %d\\n", sizeof(gdn_problem_t),
+         offsetof(gdn_problem_t, dtype),
          offsetof(gdn_problem_t, chunk), offsetof(gdn_problem_t, dv_tile), offsetof(gdn_problem_t, options),
          offsetof(gdn_problem_t, workspace),
          offsetof(gdn_problem_t, workspace_bytes), offsetof(gdn_problem_t, stream),
-         offsetof(gdn_problem_t, timing_events), (int)GDN_OPT_SERIAL, (int)GDN_OPT_NO_ERASE,
+         offsetof(gdn_problem_t, timing_events), offsetof(gdn_problem_t, gate), offsetof(gdn_problem_t, norm_weight),
+         offsetof(gdn_problem_t, norm_eps), (int)GDN_OPT_SERIAL, (int)GDN_OPT_NO_ERASE,
          (int)GDN_OPT_EXCLUSIVE_FORWARD, (int)GDN_OPT_EXCLUSIVE_REVERSE, (int)GDN_OPT_TEST_NO_PREPARATION);
   return 0;
 }
@@ -57,7 +59,8 @@ int main(void) {
     got = [int(x) for x in subprocess.check_output([str(exe)], text=True).split()]
     P = gdn.gdn_problem_t
     want = [ctypes.sizeof(P), P.dtype.offset, P.chunk.offset, P.dv_tile.offset, P.options.offset, P.workspace.offset,
-            P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset, gdn.GDN_OPT_SERIAL, gdn.GDN_OPT_NO_ERASE,
+            P.workspace_bytes.offset, P.stream.offset, P.timing_events.offset, P.gate.offset, P.norm_weight.offset,
+            P.norm_eps.offset, gdn.GDN_OPT_SERIAL, gdn.GDN_OPT_NO_ERASE,
             gdn.GDN_OPT_EXCLUSIVE_FORWARD, gdn.GDN_OPT_EXCLUSIVE_REVERSE, gdn.GDN_OPT_TEST_NO_PREPARATION]
     assert got == want
 
@@ -282,3 +285,30 @@ def test_exclusive_bf16_rejects_32_wide_tiles():
     p = _prob(dv_tile=32, dtype=gdn.GDN_DTYPE_F32)
     p.options = gdn.GDN_OPT_EXCLUSIVE_FORWARD
     assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_FORWARD) > 0
+
+
+def test_epilogue_arguments_are_validated_before_launch():
+    """The readout epilogue's arguments: a gate needs a norm weight, both
+    16-byte aligned, a finite non-negative eps, and `out` may not overlap
+    either; all rejected before anything is enqueued.  Valid ones reach the
+    launch (which fails here, with no GPU)."""
+    p, a = _valid()
+    end = max(a.values()) + (1 << 30) + 4096  # past the fake workspace
+    gate, nw = end, end + 300 * 2 * 128 * 2 + 256
+
+    def with_epi(g=gate, w=nw, eps=1e-6):
+        q, _ = _valid()
+        q.gate, q.norm_weight, q.norm_eps = g, w, eps
+        return q
+
+    assert _call(with_epi(w=None), a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert _call(with_epi(g=gate + 8), a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert _call(with_epi(w=nw + 4), a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert _call(with_epi(eps=eps), a) == gdn.GDN_ERR_INVALID_ARGUMENT
+    assert _call(with_epi(g=a["out"]), a) == gdn.GDN_ERR_INVALID_ARGUMENT  # gate overlaps out
+    assert _call(with_epi(w=a["out"] + 512), a) == gdn.GDN_ERR_INVALID_ARGUMENT  # weights inside out
+    assert _call(with_epi(), a) == gdn.GDN_ERR_HIP
+    assert _call(with_epi(eps=0.0), a) == gdn.GDN_ERR_HIP
+    # an invalid epilogue also makes the workspace query fail
+    assert gdn.gdn_workspace_bytes(with_epi(w=None), gdn.GDN_DIR_FORWARD) == 0

@@ -102,6 +102,37 @@ def test_full_size_bidir480_raw_qk():
     torch.cuda.empty_cache()
 
 
+def test_full_size_bidir480_readout_epilogue():
+    """The 480p bidirectional workload (B2 H16 T32760) with the readout
+    epilogue (gate and norm weights from the generator, eps 1e-6), in the
+    launch configuration the benchmark times: sampled heads against the
+    oracle's scan followed by the oracle's epilogue."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+
+    w = synth.WORKLOADS["bidir480"]
+    print(f"\n[bidir480 epilogue] generating {w}", flush=True)
+    x = synth.generate(w)
+    e = synth.generate_epilogue(w)
+    d = {k: to_torch(v) for k, v in x.items()}
+    y, s_out = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction,
+                           gate=to_torch(e["gate"]), norm_weight=to_torch(e["norm_weight"]), norm_eps=1e-6)
+    torch.cuda.synchronize()
+    heads = _sample_heads(w)[:2]
+    print(f"[bidir480 epilogue] oracle on heads {heads}", flush=True)
+    ref, ref_s = oracle.forward_heads(x, heads, w.direction)
+    gate = np.stack([e["gate"][b, :, h] for b, h in heads])
+    ref_y = oracle.readout_epilogue(ref, gate, e["norm_weight"], 1e-6)
+    got = np.stack([y[b, :, h].cpu().numpy() for b, h in heads])
+    got_s = np.stack([s_out[:, b, h].cpu().numpy() for b, h in heads], axis=1)
+    e_o = check(got, ref_y, TOL[w.dtype], "bidir480 epilogue out")
+    e_s = check(got_s, ref_s, TOL[w.dtype], "bidir480 epilogue state")
+    print(f"[bidir480 epilogue] max|err|/RMS: out {e_o:.3e}  state {e_s:.3e}", flush=True)
+    del d, y, s_out
+    torch.cuda.empty_cache()
+
+
 def test_full_size_bidir480_disjoint_regions():
     """The 480p bidirectional workload (B2 H16 T32760) with both directions
     reading before the token's own write, sampled heads against the oracle

@@ -234,3 +234,60 @@ def test_calls_from_two_host_threads():
     for i in range(len(cases)):
         for o, s, _ in results[i]:
             assert np.array_equal(o.cpu().numpy(), alone[i][0]) and np.array_equal(s.cpu().numpy(), alone[i][1])
+
+
+@pytest.mark.parametrize("direction,exclusive", [("fwd", "none"), ("rev", "none"), ("bi", "none"), ("bi", "both"),
+                                                 ("fwd", "fwd")])
+@pytest.mark.parametrize("dtype,dv", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_readout_epilogue(direction, exclusive, dtype, dv):
+    """The token scan's readout epilogue (gate and norm weights given):
+    against the oracle's scan followed by the oracle's epilogue formula,
+    y = w * o / sqrt(mean_dv(o^2) + eps) * sigmoid(gate) per (token, head),
+    for inclusive and exclusive readouts; the final states are those of the
+    same call without the epilogue, bit for bit."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    from gdn_testutil import to_torch
+
+    w = _case(dtype, direction, T=203, H=3, dk=64, dv=dv, state_std=0.05, seed=19)
+    x = synth.generate(w)
+    e = synth.generate_epilogue(w)
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], direction,
+                                exclusive=exclusive)
+    ref_y = oracle.readout_epilogue(ref, e["gate"], e["norm_weight"], 1e-6)
+    d = {k: to_torch(v) for k, v in x.items()}
+    y, s = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], direction,
+                       exclusive=exclusive, gate=to_torch(e["gate"]), norm_weight=to_torch(e["norm_weight"]),
+                       norm_eps=1e-6)
+    o2, s2 = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], direction,
+                         exclusive=exclusive)
+    torch.cuda.synchronize()
+    r = check(y.cpu().numpy(), ref_y, TOL[dtype], f"epilogue {w} exclusive={exclusive}")
+    assert torch.equal(s, s2)
+    print(f"\nepilogue {dtype} dv={dv} {direction} exclusive={exclusive}: {r:.2e} x RMS", flush=True)
+
+
+def test_readout_epilogue_eps_and_zero_rows():
+    """Rows whose readout is exactly zero (zero v and no initial state on
+    some heads: nothing is ever written) stay zero under the epilogue with
+    eps > 0, and a large eps dominates the root: against the oracle."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+    from gdn_testutil import to_torch
+
+    w = _case("bf16", "bi", T=150, H=3, dk=64, dv=64, seed=20)
+    x = synth.generate(w)
+    x["v"] = x["v"].copy()
+    x["v"][:, :, 1, :] = 0  # head 1 reads zeros everywhere
+    e = synth.generate_epilogue(w)
+    d = {k: to_torch(v) for k, v in x.items()}
+    ref, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi")
+    for eps in (1e-6, 0.5):
+        y, _ = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], "bi",
+                           gate=to_torch(e["gate"]), norm_weight=to_torch(e["norm_weight"]), norm_eps=eps)
+        torch.cuda.synchronize()
+        yn = y.cpu().numpy()
+        assert np.all(yn[:, :, 1, :] == 0)
+        check(yn, oracle.readout_epilogue(ref, e["gate"], e["norm_weight"], eps), TOL["bf16"], f"eps={eps}")

@@ -489,3 +489,33 @@ def test_hand_worked_example_exclusive_readouts():
     for mode, key in (("both", "out_bi_both"), ("rev", "out_bi_rev"), ("fwd", "out_bi_fwd")):
         o, _ = oracle.forward(q, k, v, la, bt, None, "bi", exclusive=mode)
         np.testing.assert_allclose(o[0, :, 0], exp[key], **tol)
+
+
+def test_readout_epilogue_hand_worked():
+    """The token scan's readout epilogue, worked by hand on rows where
+    mean(o^2) and eps are comparable: o = (1.5e-3, 2e-3) has mean(o^2) =
+    3.125e-6; with eps = 3.125e-6, sqrt(mean + eps) = 2.5e-3, so an open
+    gate (z = 60) and unit weights give (0.6, 0.8), a gate at z = 0 halves
+    it, weights (2, -1) give (1.2, -0.8), and z = ln 3 multiplies by 3/4.
+    A row of zeros stays zero (eps > 0); eps elsewhere (sqrt(mean) + eps, or
+    none) is far from these values.  Two rows of one head are normalised
+    separately (the mean runs over one row's channels only)."""
+    o = np.array([[1.5e-3, 2e-3], [3.0, 4.0]])
+    eps = 3.125e-6
+    g_open = np.full((2, 2), 60.0, np.float32)
+    y = oracle.readout_epilogue(o, g_open, [1.0, 1.0], eps)
+    np.testing.assert_allclose(y[0], [0.6, 0.8], rtol=1e-12, atol=0)
+    # second row: mean(o^2) = 12.5, eps negligible: o / sqrt(12.5)
+    np.testing.assert_allclose(y[1], np.array([3.0, 4.0]) / np.sqrt(12.5 + eps), rtol=1e-12)
+    np.testing.assert_allclose(oracle.readout_epilogue(o[:1], np.zeros((1, 2), np.float32), [1.0, 1.0], eps)[0],
+                               [0.3, 0.4], rtol=1e-12)
+    np.testing.assert_allclose(oracle.readout_epilogue(o[:1], g_open[:1], [2.0, -1.0], eps)[0], [1.2, -0.8],
+                               rtol=1e-12)
+    z3 = np.full((1, 2), np.log(3.0), np.float32)  # sigmoid(ln 3) = 3/4 up to the float32 rounding of ln 3
+    np.testing.assert_allclose(oracle.readout_epilogue(o[:1], z3, [1.0, 1.0], eps)[0], [0.45, 0.6], rtol=1e-7)
+    assert np.all(oracle.readout_epilogue(np.zeros((1, 2)), g_open[:1], [1.0, 1.0], eps) == 0)
+    for alt in (o[0] / (np.sqrt(np.mean(o[0] ** 2)) + eps), o[0] / np.sqrt(np.mean(o[0] ** 2))):
+        assert np.max(np.abs(alt - [0.6, 0.8])) > 0.2
+    # bf16 gate bit patterns are widened exactly: 0x3F80 is 1.0
+    yb = oracle.readout_epilogue(o[:1], np.full((1, 2), 0x3F80, np.uint16), [1.0, 1.0], eps)[0]
+    np.testing.assert_allclose(yb, np.array([0.6, 0.8]) / (1.0 + np.exp(-1.0)), rtol=1e-12)
