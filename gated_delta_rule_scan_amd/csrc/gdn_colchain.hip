@@ -33,15 +33,18 @@
 // stores four consecutive values of one output row.  One barrier per step.
 //
 // Operand staging.  Every operand a wave reads from LDS arrives there by
-// direct buffer-to-LDS loads (16 bytes per lane, 1 KB per instruction),
-// issued a step before its use into a two-slot ring per role: the chain
-// waves load k (rows in tau order), the strict inverse triangle (rows in tau
-// order), the value tile and the chunk scales; the readout waves load q, the
-// decayed q.k triangle and the chunk scales.  Tiles are XOR-swizzled in
-// 16-byte pieces so the operand reads are free of bank conflicts.  The waits
-// for these loads are explicit (a wave waits for its own loads before the
-// step's barrier); the ring slots and the exchange buffers are distinct
-// arrays, so the compiler can tell every LDS read from the loads in flight.
+// direct buffer-to-LDS loads (16 bytes per lane, 1 KB per instruction; the
+// per-token records 4 bytes per lane), issued a step before its use into a
+// two-slot ring per role by one more wave, the loader: the chain slot holds
+// k (rows in tau order), the strict inverse triangle (rows in tau order),
+// the value tile and the chunk scales; the readout slot holds q, the decayed
+// q.k triangle and the chunk scales.  The compute waves issue no staging
+// load, so none of them is held up while the address unit takes one.  Tiles
+// are XOR-swizzled in 16-byte pieces so the operand reads are free of bank
+// conflicts.  The loader waits for its own loads before each step's barrier
+// (an explicit vmcnt, not a fence); the ring slots and the exchange buffers
+// are distinct arrays, so the compiler can tell every LDS read from the
+// loads in flight.
 //
 // Bidirectional scans run the two directions in separate workgroups (ids 8
 // apart).  Chunk c is visited first by the direction that reaches it at the
@@ -251,7 +254,7 @@ __device__ __forceinline__ void make_mask(uint32_t (&m)[4], int row, int col0, b
 }  // namespace
 
 template <int DK, int C, int NT, bool BI, int PREC>
-__global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
+__global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a, int rev_single, int ntiles, int nbh) {
   using L = Col<DK, C, NT, PREC>;
   constexpr bool SLO = L::SLO, PLO = L::PLO;
   using M = Mma<bf16>;
@@ -261,6 +264,7 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
   __shared__ __align__(1024) unsigned char rs0_[L::RSLOT], rs1_[L::RSLOT];  // readout ring
   __shared__ __align__(1024) unsigned char xs0_[L::XSLOT], xs1_[L::XSLOT];  // exchange, by step parity
   __shared__ __align__(1024) unsigned char pf_[1024];                        // L2-prefetch sink, never read
+  __shared__ int s_gaveup[1];  // the loader's ready wait expired (chain waves: NaN state)
   lds_u8* const cs0 = (lds_u8*)cs0_;
   lds_u8* const cs1 = (lds_u8*)cs1_;
   lds_u8* const rs0 = (lds_u8*)rs0_;
@@ -291,7 +295,8 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool chain_wave = w < NT;
-  const int j = w % NT;  // 16-column sub-tile of this wave
+  const bool loader = w == 2 * NT;  // the staging wave
+  const int j = w % NT;             // 16-column sub-tile of a chain or readout wave
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const uint32_t HDB = (uint32_t)(H * DK * 2);  // token pitch of q, k (bytes)
@@ -315,130 +320,6 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
     return !BI || s < so || (s == so && !rev);
   };
 
-  // ---- direct-to-LDS staging of one chunk: wave J of a role issues the
-  // slot's 1-KB loads J, J + NT, ... (compile-time lists, one per wave); the
-  // per-lane offsets within a chunk are computed once (voff, below) ----
-  constexpr int kMaxDma = (L::NDC > L::NDR ? L::NDC : L::NDR + NT - 1) / NT + 1;
-  uint32_t voff[kMaxDma];
-  auto make_voffs = [&](auto Jc, auto chain_role_c) {
-    constexpr int J = decltype(Jc)::value;
-    constexpr bool chain_role = decltype(chain_role_c)::value;
-    constexpr int N = chain_role ? L::NDC : L::NDR;
-    int n = 0;
-#pragma unroll
-    for (int i = J; i < N; i += NT, ++n) {
-      const int byte = i * 1024;
-      if constexpr (chain_role) {
-        voff[n] = byte < L::CT   ? dma_voff<DK, C, NT>(R_KTAU, (byte - L::CK) / 1024, lane, HDB, HVB)
-                  : byte < L::CV ? dma_voff<DK, C, NT>(R_TTAU, (byte - L::CT) / 1024, lane, HDB, HVB)
-                  : byte < L::CS ? dma_voff<DK, C, NT>(R_VAL, (byte - L::CV) / 1024, lane, HDB, HVB)
-                  : byte < L::CP ? 16u * lane
-                                 : 4u * lane;
-      } else if (i < L::RS / 1024) {
-        voff[n] = byte < L::RP   ? dma_voff<DK, C, NT>(R_QNAT, (byte - L::RQ) / 1024, lane, HDB, HVB)
-                  : byte < L::RL ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RP) / 1024, lane, HDB, HVB)
-                  : plo_dir      ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RL) / 1024, lane, HDB, HVB)
-                                 : 16u * lane;
-      } else {
-        // e^g rq: the third float of each token's scale record; the
-        // remainders: the record after its 16-byte head
-        voff[n] = i == L::RS / 1024 ? 16u * lane + 8u : 16u + 4u * lane;
-      }
-    }
-  };
-  auto stage_part = [&](auto Jc, lds_u8* slotp, int c, auto chain_role_c) {
-    constexpr int J = decltype(Jc)::value;
-    constexpr bool chain_role = decltype(chain_role_c)::value;
-    const uint32_t rows = (uint32_t)(T - (int64_t)c * C);  // valid tokens from the chunk start (>= 1)
-    const rsrc_t rkq = make_rsrc((chain_role ? kbase : qbase) + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
-    const rsrc_t rtp = make_rsrc((chain_role ? trib : pqkb) + (size_t)c * L::TB, (uint32_t)L::TB);
-    const rsrc_t rsc = make_rsrc(scb + (size_t)c * C * 16, (uint32_t)(C * 16));
-    const rsrc_t rpd = make_rsrc(pdb + (size_t)c * pdg_stride(C) * 4, (uint32_t)((C + 4) * 4));
-    if constexpr (chain_role) {
-      const rsrc_t rv = make_rsrc(vbase + (size_t)c * C * HVB, (rows - 1) * HVB + DT * 2);
-      int n = 0;
-#pragma unroll
-      for (int i = J; i < L::NDC; i += NT, ++n) {
-        const int byte = i * 1024;
-        if (byte >= L::CP) {
-          dma4(rpd, slotp + byte, voff[n]);  // the record's head: the chunk decay
-        } else {
-          const rsrc_t r = byte < L::CT ? rkq : byte < L::CV ? rtp : byte < L::CS ? rv : rsc;
-          dma16(r, slotp + byte, voff[n]);
-        }
-      }
-    } else {
-      // PLO: the low parts of P, or loads through the empty resource (the
-      // same count either way)
-      const rsrc_t rpl = make_rsrc(pqlb + (size_t)c * L::TB, (uint32_t)L::TB);
-      int n = 0;
-#pragma unroll
-      for (int i = J; i < L::NDR; i += NT, ++n) {
-        const int byte = i * 1024;
-        if (i < L::RS / 1024) {
-          const rsrc_t r = byte < L::RP ? rkq : byte < L::RL ? rtp : plo_dir ? rpl : rnone;
-          dma16(r, slotp + byte, voff[n]);
-        } else if (i == L::RS / 1024) {
-          dma4(rsc, slotp + L::RS, voff[n]);
-        } else {
-          dma4(rpd, slotp + L::RD, voff[n]);
-        }
-      }
-    }
-  };
-  auto stage = [&](lds_u8* slotp, int c, auto chain_role_c) {
-    if (NT == 1 || j == 0) stage_part(std::integral_constant<int, 0>{}, slotp, c, chain_role_c);
-    else stage_part(std::integral_constant<int, NT - 1>{}, slotp, c, chain_role_c);
-  };
-  using ChainRole = std::true_type;
-  using ReadRole = std::false_type;
-
-  // ---- L2 prefetch of the tiles the value-tile workgroups of one sequence
-  // share (k and Tinv for the chain role, q and P for the readout role) ----
-  // Those workgroups run in step and ask for the same lines at the same time,
-  // so every one of them would wait for the same HBM fill.  Instead the waves
-  // of a role across the sequence's workgroups each touch every 8th 1-KB unit
-  // of the chunk three ahead (direct-to-LDS into a sink nobody reads): when
-  // the chunk is staged two steps later, its lines are in this XCD's L2.
-  // (Measured on MI355X at the 480p bidirectional shape: state chain 1.20 ->
-  // 1.09 ms; five or eight chunks ahead, or also the unshared value tile:
-  // slower.)  The loads are counted out of the step-end waits (kPf below).
-  // With the preparation running concurrently (a.ready set) only the raw k
-  // and q are prefetched: a prepared tile read before its ready flag could
-  // leave a stale line in this XCD's L2 (the preparation workgroup may run on
-  // another XCD), which the staging load would then hit.
-  constexpr int NU = (L::KB + L::TB) / 1024;  // 1-KB units of k (or q) and the triangle
-  constexpr int kPf = (NU + 7) / 8;           // prefetch loads per wave per step
-  const int pfbase = (tile * NT + j) & 7;
-  constexpr int NUK = L::KB / 1024;
-  const bool pf_prepared = a.ready == nullptr;  // prepared tiles are final before the chain starts
-  auto pf_unit = [&](int m) {
-    const int u = min(pfbase + 8 * m, NU - 1);
-    return (u < NUK || pf_prepared) ? u : u % NUK;
-  };
-  uint32_t pfoff[kPf];
-#pragma unroll
-  for (int m = 0; m < kPf; ++m) {
-    const int u = pf_unit(m);
-    const int byte = u * 1024 + 16 * lane;
-    pfoff[m] = u < NUK ? (uint32_t)((byte / L::KROWB) * HDB + (byte % L::KROWB)) : (uint32_t)(byte - L::KB);
-  }
-  auto prefetch = [&](int c, auto chain_role_c) {
-    constexpr bool chain_role = decltype(chain_role_c)::value;
-    const uint32_t rows = (uint32_t)(T - (int64_t)c * C);
-    const rsrc_t rkq = make_rsrc((chain_role ? kbase : qbase) + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
-    const rsrc_t rtp = make_rsrc((chain_role ? trib : pqkb) + (size_t)c * L::TB, (uint32_t)L::TB);
-#pragma unroll
-    for (int m = 0; m < kPf; ++m) dma16(pf_unit(m) < NUK ? rkq : rtp, pfs, pfoff[m]);
-  };
-  if (chain_wave) {
-    if (NT == 1 || j == 0) make_voffs(std::integral_constant<int, 0>{}, ChainRole{});
-    else make_voffs(std::integral_constant<int, NT - 1>{}, ChainRole{});
-  } else {
-    if (NT == 1 || j == 0) make_voffs(std::integral_constant<int, 0>{}, ReadRole{});
-    else make_voffs(std::integral_constant<int, NT - 1>{}, ReadRole{});
-  }
-
   const size_t sbase = (((size_t)slot * a.B + b) * a.H + h) * (size_t)dv * DK;
 
   if (chain_wave) {
@@ -458,32 +339,17 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) make_mask(tmask[rt], tau(rt, l16), 32 * (rt >> 1) + 8 * g4, rev, false);
 
-    // ready flags of the concurrent preparation (0 = ready; without a.ready
-    // they read 0 through an empty resource)
-    const rsrc_t rrdy = a.ready ? make_rsrc(a.ready + (size_t)chain * NC, (uint32_t)NC * 4u) : rnone;
-    // A wait that expires (a preparation pass starved of the GPU) sets the
-    // state to NaN: every later product of the chain then carries NaN, so
-    // its outputs and final state can never be values computed from a stale
-    // workspace; later waits are skipped.
+    // a preparation pass starved of the GPU (the loader wave's ready wait
+    // expired): the state becomes NaN, so every later output and the final
+    // state are NaN, never values computed from a stale workspace
     bool gave_up = false;
-    auto ensure_ready = [&](uint32_t fl, int c) {
-      if (__builtin_amdgcn_readfirstlane(fl) != 0u && !gave_up) {
-        int n = 0;
-        for (; n < kColReadyPollLimit; ++n) {
-          __builtin_amdgcn_s_sleep(2);
-          if (__builtin_amdgcn_readfirstlane(col_flag_fresh(rrdy, (uint32_t)c * 4u)) == 0u) break;
-        }
-        if (n == kColReadyPollLimit) {
-          gave_up = true;
+    // one chain step on chunk chunk_at(s), held by `cur`
+    auto chain_step = [&](const lds_u8* cur, lds_u8* xw, int s) {
+      if (s_gaveup[0] != 0 && !gave_up) {
+        gave_up = true;
 #pragma unroll
-          for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-        }
+        for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       }
-    };
-    auto flag_of = [&](int s) { return col_flag_fresh(rrdy, (uint32_t)chunk_at(min(s, NC - 1)) * 4u); };
-
-    // one chain step on chunk chunk_at(s): `cur` holds it, `nxt` receives chunk s + 1
-    auto chain_step = [&](const lds_u8* cur, lds_u8* nxt, lds_u8* xw, uint32_t& fl, int s) {
       const lds_u8* Kt = cur + L::CK;
       const lds_u8* Tt = cur + L::CT;
       const lds_u8* Vt = cur + L::CV;
@@ -498,17 +364,6 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) ka[rt][ks] = lds_frag(Kt + rho * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(rho)) << 4));
       }
-      // stage chunk s + 1 (its prepared operands only once its flag is
-      // clear); the last step restages the last chunk into the idle slot, so
-      // that every step issues the same loads
-      const int cn = chunk_at(min(s + 1, NC - 1));
-      ensure_ready(fl, cn);
-      stage(nxt, cn, ChainRole{});
-      mem_fence_compiler();
-      prefetch(chunk_at(min(s + 3, NC - 1)), ChainRole{});
-      mem_fence_compiler();
-      fl = flag_of(s + 3);  // consumed two steps on
-      mem_fence_compiler();
 
       // entry state as bf16 operand fragments (dk 32 ks + 8 g4 .. + 7 of column l16)
       bf16x8 sb[KS];
@@ -607,33 +462,21 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
     };
 
     if (NC > 0) {
-      ensure_ready(flag_of(0), chunk_at(0));
-      // after the first flag, the loads of a step in a step's order (stage,
-      // prefetch, flag): the compiler derives the loop's waits from every
-      // path into it, so the prologue must leave the same loads in flight
-      uint32_t fa = flag_of(1);
-      mem_fence_compiler();
-      stage(cs0, chunk_at(0), ChainRole{});
-      mem_fence_compiler();
-      prefetch(chunk_at(min(1, NC - 1)), ChainRole{});
-      mem_fence_compiler();
-      uint32_t fb = flag_of(2);
-      step_barrier<1 + kPf>();  // chunk 0 staged (the prefetch and the last flag may remain)
+      step_barrier<0>();  // the loader's prologue: chunk 0 staged
       int s = 0;
       for (; s + 1 < NC; s += 2) {
-        chain_step(cs0, cs1, xs0, fa, s);
-        step_barrier<1 + kPf>();
-        chain_step(cs1, cs0, xs1, fb, s + 1);
-        step_barrier<1 + kPf>();
+        chain_step(cs0, xs0, s);
+        step_barrier<0>();
+        chain_step(cs1, xs1, s + 1);
+        step_barrier<0>();
       }
       if (s < NC) {
-        chain_step(cs0, cs1, xs0, fa, s);
-        step_barrier<1 + kPf>();
+        chain_step(cs0, xs0, s);
+        step_barrier<0>();
         ++s;
       }
       // the readout's last step
-      step_barrier<1 + kPf>();
-      __builtin_amdgcn_s_waitcnt(kWaitVmem);  // the last restage and prefetch
+      step_barrier<0>();
     }
     // final state
     if (a.state_out) {
@@ -643,7 +486,7 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         *reinterpret_cast<f32x4*>(a.state_out + sbase + (size_t)col * DK + 32 * ks + 8 * g4 + 4 * u) = Sacc[srt];
       }
     }
-  } else {
+  } else if (!loader) {
     // ======================= readout wave =======================
     // P masks of the diagonal k-chunk of each 16-token output tile (the self
     // terms kept unless this direction reads before the token's own write)
@@ -695,16 +538,15 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
       }
     };
 
-    // Readout step s: stage chunk s's q, P and scales (prepared: the chain
-    // waves waited for its flag a step ago), load the flag of visit s + 1 and
-    // the partial of visit s, then read out visit s - 1 from slot `cur` and
-    // exchange `xr`.  Every step issues the same vector memory operations in
-    // the same order -- a flag store, the stage, the flag, the partial, the
-    // prefetch, the output stores -- through an empty resource where there
-    // is nothing to load or store (the last step restages the last chunk).
+    // Readout step s: load the flag of visit s + 1 and the partial of visit
+    // s, then read out visit s - 1 from slot `cur` (staged by the loader in
+    // step s - 1) and exchange `xr`.  Every step issues the same vector
+    // memory operations in the same order -- a flag store, the flag, the
+    // partial, the output stores -- through an empty resource where there is
+    // nothing to load or store.
     // The step-end waits count on that, and so do the waits the compiler
     // derives for the loop from every path into it.
-    auto read_step = [&](const lds_u8* cur, lds_u8* nxt, const lds_u8* xr, f32x4 (&pq)[RT], bool got,
+    auto read_step = [&](const lds_u8* cur, const lds_u8* xr, f32x4 (&pq)[RT], bool got,
                          f32x4 (&pq_next)[RT], bool& got_next, uint32_t fl_s, uint32_t& fl_next, int s) {
       // whether visit s's partial is published (its flag was loaded a step
       // ago; tested first, while only the last step's tail is in flight)
@@ -718,12 +560,8 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         publish(s - 3);  // its stores were counted out by the barrier ending step s - 1
       }
       mem_fence_compiler();
-      stage(nxt, chunk_at(min(s, NC - 1)), ReadRole{});
-      mem_fence_compiler();
       load_flag(fl_next, s + 1);
       load_partial(pq_next, got_next, s);
-      mem_fence_compiler();
-      prefetch(chunk_at(min(s + 3, NC - 1)), ReadRole{});
       mem_fence_compiler();
       if (s == 0) {
         // no readout yet: the output stores go to the empty resource
@@ -818,25 +656,25 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
     bool ga = false, gb = false;
     uint32_t fa = 0u, fb = 0u;
     // memory operations a readout wave leaves in flight at a step's end: the
-    // flag and the partials it loads ahead (bidirectional), the prefetch and
-    // its output stores
-    constexpr int kTail = (BI ? 2 * RT + 1 : RT) + kPf;
+    // flag and the partials it loads ahead (bidirectional) and its output
+    // stores
+    constexpr int kTail = BI ? 2 * RT + 1 : RT;
     if (NC > 0) {
-      step_barrier<0>();  // the chain waves' prologue
+      step_barrier<0>();  // the loader's prologue
       load_flag(fa, 0);
-      // step 0 stages chunk 0 and loads the partial of visit 0; no readout yet
-      read_step(rs1, rs0, xs1, pqb, gb, pqa, ga, fa, fb, 0);
+      // step 0 loads the partial of visit 0; no readout yet
+      read_step(rs1, xs1, pqb, gb, pqa, ga, fa, fb, 0);
       step_barrier<kTail>();
-      // then steps 1 .. NC: odd steps read slot 0 and stage into slot 1
+      // then steps 1 .. NC: odd steps read slot 0, even steps slot 1
       int s = 1;
       for (; s + 1 <= NC; s += 2) {
-        read_step(rs0, rs1, xs0, pqa, ga, pqb, gb, fb, fa, s);
+        read_step(rs0, xs0, pqa, ga, pqb, gb, fb, fa, s);
         step_barrier<kTail>();
-        read_step(rs1, rs0, xs1, pqb, gb, pqa, ga, fa, fb, s + 1);
+        read_step(rs1, xs1, pqb, gb, pqa, ga, fa, fb, s + 1);
         step_barrier<kTail>();
       }
       if (s <= NC) {
-        read_step(rs0, rs1, xs0, pqa, ga, pqb, gb, fb, fa, s);
+        read_step(rs0, xs0, pqa, ga, pqb, gb, fb, fa, s);
         step_barrier<kTail>();
       }
       __builtin_amdgcn_s_waitcnt(kWaitVmem);
@@ -844,6 +682,191 @@ __global__ __launch_bounds__(128 * NT) void column_chain_kernel(ScanArgs a, int 
         // flags not yet stored (short sequences)
         while (pub_next < nfirst) publish(pub_next);
       }
+    }
+  } else {
+    // ======================= loader wave =======================
+    // Every operand load of the workgroup: at step s the chain slot of chunk
+    // s + 1 and the readout slot of chunk s (direct buffer-to-LDS loads, all
+    // 1-KB units of both slots), the L2 prefetch three chunks ahead and, with
+    // the preparation running concurrently, the chunk-ready flags.  A
+    // buffer-to-LDS load holds up the wave that issues it until the compute
+    // unit's address unit takes it; issued by the chain and readout waves,
+    // these loads delayed their products (measured at the 480p bidirectional
+    // shape: ~1,400 of ~5,400 cycles per step before the first product).
+    if (lane == 0) s_gaveup[0] = 0;
+    uint32_t voffc[L::NDC], voffr[L::NDR];
+#pragma unroll
+    for (int i = 0; i < L::NDC; ++i) {
+      const int byte = i * 1024;
+      voffc[i] = byte < L::CT   ? dma_voff<DK, C, NT>(R_KTAU, (byte - L::CK) / 1024, lane, HDB, HVB)
+                 : byte < L::CV ? dma_voff<DK, C, NT>(R_TTAU, (byte - L::CT) / 1024, lane, HDB, HVB)
+                 : byte < L::CS ? dma_voff<DK, C, NT>(R_VAL, (byte - L::CV) / 1024, lane, HDB, HVB)
+                 : byte < L::CP ? 16u * lane
+                                : 4u * lane;  // the record's head (the chunk decay)
+    }
+#pragma unroll
+    for (int i = 0; i < L::NDR; ++i) {
+      const int byte = i * 1024;
+      if (i < L::RS / 1024) {
+        voffr[i] = byte < L::RP   ? dma_voff<DK, C, NT>(R_QNAT, (byte - L::RQ) / 1024, lane, HDB, HVB)
+                   : byte < L::RL ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RP) / 1024, lane, HDB, HVB)
+                   : plo_dir      ? dma_voff<DK, C, NT>(R_PNAT, (byte - L::RL) / 1024, lane, HDB, HVB)
+                                  : 16u * lane;
+      } else {
+        // e^g rq: the third float of each token's scale record; the
+        // remainders: the record after its 16-byte head
+        voffr[i] = i == L::RS / 1024 ? 16u * lane + 8u : 16u + 4u * lane;
+      }
+    }
+    auto rows_of = [&](int c) { return (uint32_t)(T - (int64_t)c * C); };  // valid tokens from the chunk start (>= 1)
+    auto stage_chain = [&](lds_u8* slotp, int c) {
+      const uint32_t rows = rows_of(c);
+      const rsrc_t rkq = make_rsrc(kbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
+      const rsrc_t rtp = make_rsrc(trib + (size_t)c * L::TB, (uint32_t)L::TB);
+      const rsrc_t rsc = make_rsrc(scb + (size_t)c * C * 16, (uint32_t)(C * 16));
+      const rsrc_t rpd = make_rsrc(pdb + (size_t)c * pdg_stride(C) * 4, (uint32_t)((C + 4) * 4));
+      const rsrc_t rv = make_rsrc(vbase + (size_t)c * C * HVB, (rows - 1) * HVB + DT * 2);
+#pragma unroll
+      for (int i = 0; i < L::NDC; ++i) {
+        const int byte = i * 1024;
+        if (byte >= L::CP) {
+          dma4(rpd, slotp + byte, voffc[i]);
+        } else {
+          const rsrc_t r = byte < L::CT ? rkq : byte < L::CV ? rtp : byte < L::CS ? rv : rsc;
+          dma16(r, slotp + byte, voffc[i]);
+        }
+      }
+    };
+    auto stage_read = [&](lds_u8* slotp, int c) {
+      const uint32_t rows = rows_of(c);
+      const rsrc_t rkq = make_rsrc(qbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
+      const rsrc_t rtp = make_rsrc(pqkb + (size_t)c * L::TB, (uint32_t)L::TB);
+      const rsrc_t rsc = make_rsrc(scb + (size_t)c * C * 16, (uint32_t)(C * 16));
+      const rsrc_t rpd = make_rsrc(pdb + (size_t)c * pdg_stride(C) * 4, (uint32_t)((C + 4) * 4));
+      // PLO: the low parts of P, or loads through the empty resource (the
+      // same count either way)
+      const rsrc_t rpl = make_rsrc(pqlb + (size_t)c * L::TB, (uint32_t)L::TB);
+#pragma unroll
+      for (int i = 0; i < L::NDR; ++i) {
+        const int byte = i * 1024;
+        if (i < L::RS / 1024) {
+          const rsrc_t r = byte < L::RP ? rkq : byte < L::RL ? rtp : plo_dir ? rpl : rnone;
+          dma16(r, slotp + byte, voffr[i]);
+        } else if (i == L::RS / 1024) {
+          dma4(rsc, slotp + L::RS, voffr[i]);
+        } else {
+          dma4(rpd, slotp + L::RD, voffr[i]);
+        }
+      }
+    };
+
+    // ---- L2 prefetch of the tiles the value-tile workgroups of one
+    // sequence share (k and Tinv, q and P) ----
+    // Those workgroups run in step and ask for the same lines at the same
+    // time, so every one of them would wait for the same HBM fill.  Instead
+    // the loaders of a sequence's tiles each touch every 4th 1-KB unit of the
+    // chunk three ahead (direct-to-LDS into a sink nobody reads): when the
+    // chunk is staged two steps later, its lines are in this XCD's L2.
+    // (Measured at the 480p bidirectional shape: state chain 1.20 -> 1.09 ms;
+    // two, five or eight chunks ahead, or also the unshared value tile:
+    // slower.)  With the preparation running concurrently (a.ready set) only
+    // the raw k and q are prefetched: a prepared tile read before its ready
+    // flag could leave a stale line in this XCD's L2 (the preparation
+    // workgroup may run on another XCD), which the staging load would hit.
+    constexpr int NU = (L::KB + L::TB) / 1024;  // 1-KB units of k (or q) and the triangle
+    constexpr int kPfR = (NU + 3) / 4;          // prefetch loads per role and step
+    constexpr int NUK = L::KB / 1024;
+    const int pfbase = tile & 3;
+    const bool pf_prepared = a.ready == nullptr;  // prepared tiles are final before the chain starts
+    auto pf_unit = [&](int m) {
+      const int u = min(pfbase + 4 * m, NU - 1);
+      return (u < NUK || pf_prepared) ? u : u % NUK;
+    };
+    uint32_t pfoff[kPfR];
+#pragma unroll
+    for (int m = 0; m < kPfR; ++m) {
+      const int u = pf_unit(m);
+      const int byte = u * 1024 + 16 * lane;
+      pfoff[m] = u < NUK ? (uint32_t)((byte / L::KROWB) * HDB + (byte % L::KROWB)) : (uint32_t)(byte - L::KB);
+    }
+    auto prefetch = [&](int c) {
+      const uint32_t rows = rows_of(c);
+      const rsrc_t rk = make_rsrc(kbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
+      const rsrc_t rq = make_rsrc(qbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
+      const rsrc_t rt = make_rsrc(trib + (size_t)c * L::TB, (uint32_t)L::TB);
+      const rsrc_t rp = make_rsrc(pqkb + (size_t)c * L::TB, (uint32_t)L::TB);
+#pragma unroll
+      for (int m = 0; m < kPfR; ++m) dma16(pf_unit(m) < NUK ? rk : rt, pfs, pfoff[m]);
+#pragma unroll
+      for (int m = 0; m < kPfR; ++m) dma16(pf_unit(m) < NUK ? rq : rp, pfs, pfoff[m]);
+    };
+
+    // ready flags of the concurrent preparation (0 = ready; without a.ready
+    // they read 0 through an empty resource).  A wait that expires (a
+    // preparation pass starved of the GPU) tells the chain waves through LDS
+    // to set their state to NaN; later waits are skipped.
+    const rsrc_t rrdy = a.ready ? make_rsrc(a.ready + (size_t)chain * NC, (uint32_t)NC * 4u) : rnone;
+    bool gave_up = false;
+    auto ensure_ready = [&](uint32_t fl, int c) {
+      if (__builtin_amdgcn_readfirstlane(fl) != 0u && !gave_up) {
+        int n = 0;
+        for (; n < kColReadyPollLimit; ++n) {
+          __builtin_amdgcn_s_sleep(2);
+          if (__builtin_amdgcn_readfirstlane(col_flag_fresh(rrdy, (uint32_t)c * 4u)) == 0u) break;
+        }
+        if (n == kColReadyPollLimit) {
+          gave_up = true;
+          if (lane == 0) s_gaveup[0] = 1;
+        }
+      }
+    };
+    auto flag_of = [&](int s) { return col_flag_fresh(rrdy, (uint32_t)chunk_at(min(s, NC - 1)) * 4u); };
+
+    // One loader step: the same loads in the same order at every step (the
+    // last steps restage the last chunk into idle slots), which the step-end
+    // waits and the compiler's loop waits count on.  `fl` is chunk s + 1's
+    // ready flag, loaded two steps ago, and receives chunk s + 3's.
+    constexpr int kLTail = 2 * kPfR + 1;  // loads left in flight at a step's end: the prefetch and the flag
+    auto load_step = [&](lds_u8* cnext, lds_u8* rcur, uint32_t& fl, int s) {
+      const int cn = chunk_at(min(s + 1, NC - 1));
+      ensure_ready(fl, cn);
+      mem_fence_compiler();
+      stage_chain(cnext, cn);
+      mem_fence_compiler();
+      stage_read(rcur, chunk_at(min(s, NC - 1)));
+      mem_fence_compiler();
+      prefetch(chunk_at(min(s + 3, NC - 1)));
+      mem_fence_compiler();
+      fl = flag_of(s + 3);
+      mem_fence_compiler();
+    };
+    if (NC > 0) {
+      ensure_ready(flag_of(0), chunk_at(0));
+      // after the first flag, a step's loads in a step's order (the readout
+      // slot staged here is read in no step)
+      uint32_t fa = flag_of(1);
+      mem_fence_compiler();
+      stage_chain(cs0, chunk_at(0));
+      mem_fence_compiler();
+      stage_read(rs1, chunk_at(0));
+      mem_fence_compiler();
+      prefetch(chunk_at(min(1, NC - 1)));
+      mem_fence_compiler();
+      uint32_t fb = flag_of(2);
+      step_barrier<kLTail>();  // chunk 0 in the chain slot
+      // steps 0 .. NC: the chain slot of chunk s + 1 and the readout slot of chunk s
+      int s = 0;
+      for (; s + 1 <= NC; s += 2) {
+        load_step(cs1, rs0, fa, s);
+        step_barrier<kLTail>();
+        load_step(cs0, rs1, fb, s + 1);
+        step_barrier<kLTail>();
+      }
+      if (s <= NC) {
+        load_step(cs1, rs0, fa, s);
+        step_barrier<kLTail>();
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmem);  // the last restages and prefetch
     }
   }
 }
@@ -854,7 +877,7 @@ hipError_t launch_column_chain(const ScanArgs& a, int rev_single, hipStream_t st
   const int ntiles = a.dv / (16 * NT);
   const int nbh = (int)(a.B * a.H);
   const unsigned nblocks = (unsigned)chain_blocks(nbh, a.dv, NT, BI ? 2 : 1);
-  hipLaunchKernelGGL((column_chain_kernel<DK, C, NT, BI, PREC>), dim3(nblocks), dim3(128 * NT), 0, stream, a,
+  hipLaunchKernelGGL((column_chain_kernel<DK, C, NT, BI, PREC>), dim3(nblocks), dim3(128 * NT + 64), 0, stream, a,
                      rev_single, ntiles, nbh);
   return hipGetLastError();
 }
