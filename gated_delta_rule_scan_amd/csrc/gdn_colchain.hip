@@ -315,6 +315,13 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
   const rsrc_t rnone = make_rsrc(obase, 0u);
 
   auto chunk_at = [&](int s) { return rev ? NC - 1 - s : s; };
+  // Slot order of a chunk's row tiles: slot pair p holds the two 16-token
+  // tiles of k-chunk kd_of(p), the k-chunks in reverse order for the reverse
+  // direction.  In slot order both directions' triangles are lower, so which
+  // k-chunks a slot's products take is known at compile time; only LDS
+  // addresses depend on the direction.
+  auto kd_of = [&](int p) { return rev ? KC - 1 - p : p; };
+  auto rt_of = [&](int u) { return 2 * kd_of(u >> 1) + (u & 1); };
   auto first_visit = [&](int s) {  // bidirectional: this workgroup visits chunk_at(s) first
     const int so = NC - 1 - s;
     return !BI || s < so || (s == so && !rev);
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     // triangle masks of the diagonal k-chunk of each row tile (strict)
     uint32_t tmask[RT][4];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) make_mask(tmask[rt], tau(rt, l16), 32 * (rt >> 1) + 8 * g4, rev, false);
+    for (int u = 0; u < RT; ++u) make_mask(tmask[u], tau(rt_of(u), l16), 32 * kd_of(u >> 1) + 8 * g4, rev, false);
 
     // a preparation pass starved of the GPU (the loader wave's ready wait
     // expired): the state becomes NaN, so every later output and the final
@@ -359,10 +366,10 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
       // k fragments of Y, read first (they are in LDS since the last step)
       bf16x8 ka[RT][KS];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int rho = 16 * rt + l16;
+      for (int u = 0; u < RT; ++u) {
+        const int rho = 16 * rt_of(u) + l16;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[rt][ks] = lds_frag(Kt + rho * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(rho)) << 4));
+        for (int ks = 0; ks < KS; ++ks) ka[u][ks] = lds_frag(Kt + rho * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(rho)) << 4));
       }
 
       // entry state as bf16 operand fragments (dk 32 ks + 8 g4 .. + 7 of column l16)
@@ -378,8 +385,9 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
         }
         lds_put(X + L::XS + ks * 1024 + lane * 16, sb[ks]);
       }
-      // Y = K S^T (rows in token order tau); the row tiles are independent
-      // accumulators, so each slice's products issue back to back
+      // Y = K S^T (rows in token order tau, row tiles in slot order); the row
+      // tiles are independent accumulators, so each slice's products issue
+      // back to back
       f32x4 y[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) y[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -388,11 +396,11 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) y[rt] = M::mma(ka[rt][ks], sb[ks], y[rt]);
       }
-      // X = beta (V - e^g rk Y); lane (l16, g4) of row tile rt holds tokens t0 .. t0 + 3
+      // X = beta (V - e^g rk Y); lane (l16, g4) of slot u holds tokens t0 .. t0 + 3
       f32x4 x[RT], dsc[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int t0 = 32 * (rt >> 1) + 8 * g4 + 4 * (rt & 1);
+        const int t0 = 32 * kd_of(rt >> 1) + 8 * g4 + 4 * (rt & 1);
         const v4s t4 = tr16(Vt + (t0 + (l16 >> 2)) * L::VROWB + (16 * j + 4 * (l16 & 3)) * 2);
         bf16x4 v4;
         __builtin_memcpy(&v4, &t4, 8);
@@ -409,18 +417,17 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
       for (int kc = 0; kc < KC; ++kc) xb[kc] = pack8(x[2 * kc], x[2 * kc + 1]);
       f32x4 vn[RT];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 acc = x[rt];
-        const int rho = 16 * rt + l16;
-        const int kd = rt >> 1;  // k-chunk of the diagonal
+      for (int u = 0; u < RT; ++u) {
+        f32x4 acc = x[u];
+        const int rho = 16 * rt_of(u) + l16;
+        const int p = u >> 1;  // slot pair of the diagonal
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          if (rev ? kc < kd : kc > kd) continue;  // no element of this direction's triangle
-          bf16x8 ta = lds_frag(Tt + rho * L::TROWB + (((4 * kc + g4) ^ swz_t<C>(rho)) << 4));
-          if (kc == kd) ta = and_mask(ta, tmask[rt]);
-          acc = M::mma(ta, xb[kc], acc);
+        for (int m = 0; m <= p; ++m) {  // the k-chunks of this direction's triangle
+          bf16x8 ta = lds_frag(Tt + rho * L::TROWB + (((4 * kd_of(m) + g4) ^ swz_t<C>(rho)) << 4));
+          if (m == p) ta = and_mask(ta, tmask[u]);
+          acc = M::mma(ta, xb[m], acc);
         }
-        vn[rt] = acc;
+        vn[u] = acc;
       }
       // Vnew (fp32) for the readout; the scaled Vs (hi + lo) for the update
       bf16x8 vsh[KC], vsl[KC];
@@ -435,13 +442,11 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
       const float gn = lds_f(Pd);  // the record's head
       // S e^{g_last}: exactly zero when the chunk's decay is (finite states;
       // a NaN state from an expired wait keeps its NaN)
-      if (gn != 0.f || gave_up) {
+      const bool keep = gn != 0.f || gave_up;
 #pragma unroll
-        for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = Sacc[srt] * gn;
-      } else {
+      for (int srt = 0; srt < SRT; ++srt)
 #pragma unroll
-        for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+        for (int i = 0; i < 4; ++i) Sacc[srt][i] = keep ? Sacc[srt][i] * gn : 0.f;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
           bf16x8 kt;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int rho = 16 * (2 * kc + hh) + 4 * g4 + (l16 >> 2);  // row of token 32 kc + 8 g4 + 4 hh + l16 / 4
+            const int rho = 16 * (2 * kd_of(kc) + hh) + 4 * g4 + (l16 >> 2);  // row of token 32 kd + 8 g4 + 4 hh + l16 / 4
             const int p = 4 * ks + (l16 & 3);
             const v4s r = tr16(Kt + rho * L::KROWB + ((p ^ swz_kq<DK>(rho)) << 4) + 8 * u);
             __builtin_memcpy(reinterpret_cast<char*>(&kt) + 8 * hh, &r, 8);
@@ -488,19 +493,22 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     }
   } else if (!loader) {
     // ======================= readout wave =======================
-    // P masks of the diagonal k-chunk of each 16-token output tile (the self
-    // terms kept unless this direction reads before the token's own write)
+    // P masks of the diagonal k-chunk of each 16-token output tile, in slot
+    // order (the self terms kept unless this direction reads before the
+    // token's own write)
     const bool self = !(rev ? a.excl_rev : a.excl_fwd);
+    const uint32_t plk = plo_dir ? ~0u : 0u;  // P's low parts: read in this direction
     uint32_t pmask[RT][4], dmask[RT][4];  // dmask: the element of this lane's own token (none: all zero)
 #pragma unroll
-    for (int tt = 0; tt < RT; ++tt) {
-      make_mask(pmask[tt], 16 * tt + l16, 32 * (tt >> 1) + 8 * g4, rev, self);
-      const int e0 = 16 * tt + l16 - (32 * (tt >> 1) + 8 * g4);
+    for (int u = 0; u < RT; ++u) {
+      const int tt = rt_of(u);
+      make_mask(pmask[u], 16 * tt + l16, 32 * kd_of(u >> 1) + 8 * g4, rev, self);
+      const int e0 = 16 * tt + l16 - (32 * kd_of(u >> 1) + 8 * g4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dmask[tt][i] = 0u;
+      for (int i = 0; i < 4; ++i) dmask[u][i] = 0u;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (self && e == e0) dmask[tt][e / 2] |= 0xffffu << (16 * (e % 2));
+        if (self && e == e0) dmask[u][e / 2] |= 0xffffu << (16 * (e % 2));
     }
     const rsrc_t ro = make_rsrc(obase, (uint32_t)(T - 1) * HOB + DT * 4);
     const uint32_t out_lane = (uint32_t)(16 * j + 4 * g4) * 4u;
@@ -534,7 +542,7 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
         const rsrc_t rp = got ? ro : rnone;
         const int c = chunk_at(min(v, NC - 1));
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) pq[tt] = col_load_fresh(rp, out_off(c, tt));
+        for (int u = 0; u < RT; ++u) pq[u] = col_load_fresh(rp, out_off(c, rt_of(u)));
       }
     };
 
@@ -591,7 +599,7 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
         }
         const float nan = __builtin_nanf("");
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) pq[tt] = ok ? col_load_fresh(ro, out_off(c, tt)) : f32x4{nan, nan, nan, nan};
+        for (int u = 0; u < RT; ++u) pq[u] = ok ? col_load_fresh(ro, out_off(c, rt_of(u))) : f32x4{nan, nan, nan, nan};
         // waited for here, so that the compiler does not make the common
         // path wait as if these loads were in flight there
         __builtin_amdgcn_s_waitcnt(kWaitVmem);
@@ -605,48 +613,85 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
         const f32x4 v1 = *(const lds_f32x4v*)(X + L::XV + kc * 2048 + lane * 32 + 16);
         split8(v0, v1, vh[kc], vl[kc]);
       }
+      // The slots' products are independent (one accumulator each) and take
+      // k-chunks known at compile time: every fragment is read first, then
+      // the products run slice by slice across the slots, so each product's
+      // accumulator was written RT products earlier.
+      bf16x8 qf[RT][KS];
+      float zs[RT], rmd[RT];
 #pragma unroll
-      for (int tt = 0; tt < RT; ++tt) {
-        const int t = 16 * tt + l16;  // this lane's token
-        // Z^T = S Q^T
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < RT; ++u) {
+        const int t = 16 * rt_of(u) + l16;  // this lane's token
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 qb = lds_frag(Qt + t * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(t)) << 4));
-          z = M::mma(sr[ks], qb, z);
-          if constexpr (SLO) z = M::mma(lds_frag(X + L::XSL + ks * 1024 + lane * 16), qb, z);  // the state's low parts
+        for (int ks = 0; ks < KS; ++ks) qf[u][ks] = lds_frag(Qt + t * L::KROWB + (((4 * ks + g4) ^ swz_kq<DK>(t)) << 4));
+        zs[u] = lds_f(Sc + t * 4);  // e^g rq of the token
+        rmd[u] = lds_f(Pd + t * 4);  // the self term's remainder
+      }
+      // Z^T = S Q^T
+      f32x4 o[RT];
+#pragma unroll
+      for (int u = 0; u < RT; ++u) o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 sl;
+        if constexpr (SLO) sl = lds_frag(X + L::XSL + ks * 1024 + lane * 16);  // the state's low parts
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+          o[u] = M::mma(sr[ks], qf[u][ks], o[u]);
+          if constexpr (SLO) o[u] = M::mma(sl, qf[u][ks], o[u]);
         }
-        const float zs = lds_f(Sc + t * 4);  // e^g rq of the token
-        f32x4 o = z * zs;
-        // + Vnew^T P^T
-        const int kd = tt >> 1;
+      }
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          if (rev ? kc < kd : kc > kd) continue;
-          bf16x8 pb = lds_frag(Pt + t * L::TROWB + (((4 * kc + g4) ^ swz_t<C>(t)) << 4));
-          if (kc == kd) pb = and_mask(pb, pmask[tt]);
-          o = M::mma(vh[kc], pb, o);
-          o = M::mma(vl[kc], pb, o);
+      for (int u = 0; u < RT; ++u) o[u] = o[u] * zs[u];
+      // + Vnew^T P^T over the k-chunks of each slot's triangle: chunk m
+      // enters the slots of pairs p >= m (the diagonal one, p == m, masked)
+#pragma unroll
+      for (int m = 0; m < KC; ++m) {
+        bf16x8 pf[RT], pl[RT];
+#pragma unroll
+        for (int u = 2 * m; u < RT; ++u) {
+          const int t = 16 * rt_of(u) + l16;
+          const int poff = t * L::TROWB + (((4 * kd_of(m) + g4) ^ swz_t<C>(t)) << 4);
+          pf[u] = lds_frag(Pt + poff);
+          if ((u >> 1) == m) pf[u] = and_mask(pf[u], pmask[u]);
           if constexpr (PLO) {
-            if (plo_dir) {
-              // P's low part (with Vnew's hi part: the product's next order)
-              bf16x8 pl = lds_frag(cur + L::RL + t * L::TROWB + (((4 * kc + g4) ^ swz_t<C>(t)) << 4));
-              if (kc == kd) pl = and_mask(pl, pmask[tt]);
-              o = M::mma(vh[kc], pl, o);
-            }
-          }
-          if (kc == kd) {
-            // the self term's remainder (P holds it rounded): a diagonal product with Vnew's hi part
-            const bf16 rmd = (bf16)lds_f(Pd + t * 4);
-            bf16x8 dg;
+            // P's low part (with Vnew's hi part: the product's next order),
+            // zero in a direction that reads its token's own write
+            uint32_t lm[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dg[e] = rmd;
-            o = M::mma(vh[kc], and_mask(dg, dmask[tt]), o);
+            for (int i = 0; i < 4; ++i) lm[i] = ((u >> 1) == m ? pmask[u][i] : ~0u) & plk;
+            pl[u] = and_mask(lds_frag(cur + L::RL + poff), lm);
           }
         }
-        if (BI && add) o += pq[tt];
-        if (BI && !add) bstore16_agent(ro, out_off(c, tt), o);  // a partial: read by the other direction
-        else bstore16(ro, out_off(c, tt), o);
+#pragma unroll
+        for (int u = 2 * m; u < RT; ++u) o[u] = M::mma(vh[m], pf[u], o[u]);
+#pragma unroll
+        for (int u = 2 * m; u < RT; ++u) o[u] = M::mma(vl[m], pf[u], o[u]);
+        if constexpr (PLO) {
+#pragma unroll
+          for (int u = 2 * m; u < RT; ++u) o[u] = M::mma(vh[m], pl[u], o[u]);
+        }
+        // the self terms' remainders (P holds them rounded): a diagonal
+        // product with Vnew's hi part in the slots of pair m
+#pragma unroll
+        for (int u = 2 * m; u < 2 * m + 2; ++u) {
+          const bf16 r = (bf16)rmd[u];
+          bf16x8 dg;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dg[e] = r;
+          o[u] = M::mma(vh[m], and_mask(dg, dmask[u]), o[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < RT; ++u) {
+        const uint32_t off = out_off(c, rt_of(u));
+        if constexpr (BI) {
+          // the partial is zero on a first visit, which stores its readout
+          // for the other direction
+          bstore16_agent(ro, off, o[u] + pq[u]);
+        } else {
+          bstore16(ro, off, o[u]);
+        }
       }
     };
 
