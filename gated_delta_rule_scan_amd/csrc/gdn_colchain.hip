@@ -264,7 +264,6 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
   __shared__ __align__(1024) unsigned char rs0_[L::RSLOT], rs1_[L::RSLOT];  // readout ring
   __shared__ __align__(1024) unsigned char xs0_[L::XSLOT], xs1_[L::XSLOT];  // exchange, by step parity
   __shared__ __align__(1024) unsigned char pf_[1024];                        // L2-prefetch sink, never read
-  __shared__ int s_gaveup[1];  // the loader's ready wait expired (chain waves: NaN state)
   lds_u8* const cs0 = (lds_u8*)cs0_;
   lds_u8* const cs1 = (lds_u8*)cs1_;
   lds_u8* const rs0 = (lds_u8*)rs0_;
@@ -346,17 +345,8 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
 #pragma unroll
     for (int u = 0; u < RT; ++u) make_mask(tmask[u], tau(rt_of(u), l16), 32 * kd_of(u >> 1) + 8 * g4, rev, false);
 
-    // a preparation pass starved of the GPU (the loader wave's ready wait
-    // expired): the state becomes NaN, so every later output and the final
-    // state are NaN, never values computed from a stale workspace
-    bool gave_up = false;
     // one chain step on chunk chunk_at(s), held by `cur`
     auto chain_step = [&](const lds_u8* cur, lds_u8* xw, int s) {
-      if (s_gaveup[0] != 0 && !gave_up) {
-        gave_up = true;
-#pragma unroll
-        for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      }
       const lds_u8* Kt = cur + L::CK;
       const lds_u8* Tt = cur + L::CT;
       const lds_u8* Vt = cur + L::CV;
@@ -440,13 +430,8 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
       // S = e^{g_last} S + K^T Vs: the transposed k fragment of state tile
       // srt = 2 ks + u and k-chunk kc holds k[32 kc + 8 g4 + e][pi(srt, l16)]
       const float gn = lds_f(Pd);  // the record's head
-      // S e^{g_last}: exactly zero when the chunk's decay is (finite states;
-      // a NaN state from an expired wait keeps its NaN)
-      const bool keep = gn != 0.f || gave_up;
 #pragma unroll
-      for (int srt = 0; srt < SRT; ++srt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Sacc[srt][i] = keep ? Sacc[srt][i] * gn : 0.f;
+      for (int srt = 0; srt < SRT; ++srt) Sacc[srt] = Sacc[srt] * gn;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
@@ -738,7 +723,6 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     // unit's address unit takes it; issued by the chain and readout waves,
     // these loads delayed their products (measured at the 480p bidirectional
     // shape: ~1,400 of ~5,400 cycles per step before the first product).
-    if (lane == 0) s_gaveup[0] = 0;
     uint32_t voffc[L::NDC], voffr[L::NDR];
 #pragma unroll
     for (int i = 0; i < L::NDC; ++i) {
@@ -848,22 +832,31 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
 
     // ready flags of the concurrent preparation (0 = ready; without a.ready
     // they read 0 through an empty resource).  A wait that expires (a
-    // preparation pass starved of the GPU) tells the chain waves through LDS
-    // to set their state to NaN; later waits are skipped.
+    // preparation pass starved of the GPU) returns true once; later waits are
+    // skipped.
     const rsrc_t rrdy = a.ready ? make_rsrc(a.ready + (size_t)chain * NC, (uint32_t)NC * 4u) : rnone;
     bool gave_up = false;
     auto ensure_ready = [&](uint32_t fl, int c) {
+      bool expired = false;
       if (__builtin_amdgcn_readfirstlane(fl) != 0u && !gave_up) {
         int n = 0;
         for (; n < kColReadyPollLimit; ++n) {
           __builtin_amdgcn_s_sleep(2);
           if (__builtin_amdgcn_readfirstlane(col_flag_fresh(rrdy, (uint32_t)c * 4u)) == 0u) break;
         }
-        if (n == kColReadyPollLimit) {
-          gave_up = true;
-          if (lane == 0) s_gaveup[0] = 1;
-        }
+        expired = gave_up = n == kColReadyPollLimit;
       }
+      return expired;
+    };
+    // The chunk whose wait expired: its staged scales and decay become NaN
+    // (after its loads have landed), so X, Vnew and the state the chain
+    // waves compute from it are NaN, and with them every later output and
+    // the final state -- never values computed from a stale workspace.
+    auto poison = [&](lds_u8* slotp) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmem);
+      const float nan = __builtin_nanf("");
+      *(lds_f32x4v*)(slotp + L::CS + 16 * lane) = f32x4{nan, nan, nan, nan};
+      *(lds_f32*)(slotp + L::CP + 4 * lane) = nan;
     };
     auto flag_of = [&](int s) { return col_flag_fresh(rrdy, (uint32_t)chunk_at(min(s, NC - 1)) * 4u); };
 
@@ -874,9 +867,10 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     constexpr int kLTail = 2 * kPfR + 1;  // loads left in flight at a step's end: the prefetch and the flag
     auto load_step = [&](lds_u8* cnext, lds_u8* rcur, uint32_t& fl, int s) {
       const int cn = chunk_at(min(s + 1, NC - 1));
-      ensure_ready(fl, cn);
+      const bool expired = ensure_ready(fl, cn);
       mem_fence_compiler();
       stage_chain(cnext, cn);
+      if (expired) poison(cnext);
       mem_fence_compiler();
       stage_read(rcur, chunk_at(min(s, NC - 1)));
       mem_fence_compiler();
@@ -886,12 +880,13 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
       mem_fence_compiler();
     };
     if (NC > 0) {
-      ensure_ready(flag_of(0), chunk_at(0));
+      const bool expired = ensure_ready(flag_of(0), chunk_at(0));
       // after the first flag, a step's loads in a step's order (the readout
       // slot staged here is read in no step)
       uint32_t fa = flag_of(1);
       mem_fence_compiler();
       stage_chain(cs0, chunk_at(0));
+      if (expired) poison(cs0);
       mem_fence_compiler();
       stage_read(rs1, chunk_at(0));
       mem_fence_compiler();

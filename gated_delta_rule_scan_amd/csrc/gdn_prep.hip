@@ -47,11 +47,15 @@ struct PrepSmem {
   static constexpr int PP = C + EP;                     // pitch of the staged decayed q.k tile
   static constexpr size_t kq_bytes = (size_t)2 * C * KP * sizeof(MT);
   static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)C * PP * sizeof(MT) + (size_t)4 * 16 * 17 * 4;
+  static_assert(NB * 16 * 16 <= 4 * 16 * 17, "transposed diagonal blocks fit the scratch");
   static constexpr size_t region = kq_bytes > inv_bytes ? kq_bytes : inv_bytes;
 };
 
-template <typename MT, int DK, int C>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
+// PLO: the low parts of the decayed q.k tile are kept and written (exclusive
+// readouts on bf16 operands); without them their registers are free, and
+// three workgroups per compute unit fit (as LDS allows).
+template <typename MT, int DK, int C, bool PLO>
+__global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a) {
   using SM = PrepSmem<MT, DK, C>;
   using M = Mma<MT>;
   constexpr int EP = SM::EP, KP = SM::KP, NB = SM::NB, LP = SM::LP;
@@ -68,6 +72,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   float* Ti = Lm + C * LP;
   MT* Pst = reinterpret_cast<MT*>(Ti + C * LP);                          // decayed q.k, staged
   float* Wsc = reinterpret_cast<float*>(Pst + C * PP);                   // [4 waves][16][17]
+  // the diagonal 16 x 16 blocks of L transposed (the forward entries below
+  // the diagonal, the reverse ones above), read by the diagonal solve; the
+  // off-diagonal blocks' scratch later reuses the space
+  float* Ld = Wsc;  // [NB][16][16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,8 +186,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       }
       const int row = prow + RPI * i;
       if (tid % PR == 0) {
-        s_rq[row] = 1.0f / fmaxf(sqrtf(sq), kNormEps);
-        s_rk[row] = 1.0f / fmaxf(sqrtf(sk), kNormEps);
+        // 1 / max(|x|, eps) as a reciprocal square root (one rounding more
+        // than a divide: relative error ~1e-7)
+        constexpr float e2 = kNormEps * kNormEps;
+        s_rq[row] = sq > e2 ? __builtin_amdgcn_rsqf(sq) : 1.0f / kNormEps;
+        s_rk[row] = sk > e2 ? __builtin_amdgcn_rsqf(sk) : 1.0f / kNormEps;
         s_qk[row] = sqk;
       }
       *reinterpret_cast<f32x4*>(Qs + row * KP + pcol) = vq[i];
@@ -261,35 +272,63 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   // above it the reverse direction's; the diagonal (the self terms) is
   // written beside the diagonal solve below.  plo: the part of each decayed
   // q.k entry that the operand type drops, kept for exclusive readouts.
-  float plo[UPW][4];
+  float plo[PLO ? UPW : 1][4];
+#pragma unroll
+  for (int j = 0; j < (PLO ? UPW : 1); ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) plo[j][i] = 0.f;
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     const int u = wave + 4 * j;
     if (u < NT2) {
       const int ti = u / NB, tj = u % NB;
       const int col = 16 * tj + l16, r0 = 16 * ti + 4 * g4;
-      const double gfc = s_g[0][col], grc = s_g[1][col];
       const float rkc = s_rk[col];
-      const f32x4 bf = *reinterpret_cast<const f32x4*>(&s_bt[0][r0]);
-      const f32x4 br = *reinterpret_cast<const f32x4*>(&s_bt[1][r0]);
       const f32x4 rkr = *reinterpret_cast<const f32x4*>(&s_rk[r0]);
       const f32x4 rqr = *reinterpret_cast<const f32x4*>(&s_rq[r0]);
+      if (ti != tj) {
+        // a tile off the diagonal holds one direction's entries (below: the
+        // forward one, above: the reverse one); the other direction never
+        // reads it
+        const int dir = ti > tj ? 0 : 1;
+        if (dir == 0 ? fwd_on : rev_on) {
+          const double gc = s_g[dir][col];
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(&s_bt[dir][r0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        // 0/1 weights of the two directions (arithmetic selects: no branches)
-        const float wf = (col < r && fwd_on) ? 1.f : 0.f, wr = (col > r && rev_on) ? 1.f : 0.f;
-        // decay between the two tokens (<= 0 in log2 units; zero where
-        // unused, so it never overflows); below 2^-126 it may flush to zero
-        const float gd = fmaf(wf, (float)(s_g[0][r] - gfc), wr * (float)(s_g[1][r] - grc));
-        const float e = __builtin_amdgcn_exp2f(gd);
-        const float lm = e * fmaf(wf, bf[i], wr * br[i]) * erase_w;
-        const float pm = e * (wf + wr);
-        Lm[r * LP + col] = (rkr[i] * rkc) * accG[j][i] * lm;
-        const float pv = (rqr[i] * rkc) * accP[j][i] * pm;
-        const MT ph = (MT)pv;
-        Pst[r * PP + col] = ph;
-        plo[j][i] = pv - (float)ph;
+          for (int i = 0; i < 4; ++i) {
+            const int r = r0 + i;
+            // decay between the two tokens (<= 0 in log2 units); below
+            // 2^-126 it may flush to zero
+            const float e = __builtin_amdgcn_exp2f((float)(s_g[dir][r] - gc));
+            Lm[r * LP + col] = (rkr[i] * rkc) * accG[j][i] * (e * bt[i] * erase_w);
+            const float pv = (rqr[i] * rkc) * accP[j][i] * e;
+            const MT ph = (MT)pv;
+            Pst[r * PP + col] = ph;
+            if constexpr (PLO) plo[j][i] = pv - (float)ph;
+          }
+        }
+      } else {
+        const double gfc = s_g[0][col], grc = s_g[1][col];
+        const f32x4 bf = *reinterpret_cast<const f32x4*>(&s_bt[0][r0]);
+        const f32x4 br = *reinterpret_cast<const f32x4*>(&s_bt[1][r0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          // 0/1 weights of the two directions (arithmetic selects: no branches)
+          const float wf = (col < r && fwd_on) ? 1.f : 0.f, wr = (col > r && rev_on) ? 1.f : 0.f;
+          // zero where unused, so it never overflows
+          const float gd = fmaf(wf, (float)(s_g[0][r] - gfc), wr * (float)(s_g[1][r] - grc));
+          const float e = __builtin_amdgcn_exp2f(gd);
+          const float lm = e * fmaf(wf, bf[i], wr * br[i]) * erase_w;
+          const float pm = e * (wf + wr);
+          const float lv = (rkr[i] * rkc) * accG[j][i] * lm;
+          Lm[r * LP + col] = lv;
+          Ld[(tj * 16 + l16) * 16 + (r - r0 + 4 * g4)] = lv;  // transposed copy of the block
+          const float pv = (rqr[i] * rkc) * accP[j][i] * pm;
+          const MT ph = (MT)pv;
+          Pst[r * PP + col] = ph;
+          if constexpr (PLO) plo[j][i] = pv - (float)ph;
+        }
       }
     }
   }
@@ -304,9 +343,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
     // column jc of (I + L_bb)^{-1} by forward substitution in visiting
     // order, column-oriented: once x_i is known it is folded into every
     // later row's running sum, so the dependent chain is 16 steps long.
-    // The column is written out only at the end, so every read of L can be
-    // issued ahead of the chain.  One instance per direction keeps every
-    // index a compile-time constant (the running sums stay in registers).
+    // Column i of L_bb is row i of the transposed copy, read four rows at a
+    // time; the column is written out only at the end, so every read of L
+    // can be issued ahead of the chain.  One instance per direction keeps
+    // every index a compile-time constant (the running sums stay in
+    // registers).
+    const float* ldb = Ld + blk * 256;
     auto solve = [&](auto rev_tag) {
       constexpr bool R = decltype(rev_tag)::value;
       float acc[16], x[16];
@@ -318,9 +360,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
         const bool after = R ? (i < jc) : (i > jc);
         x[i] = i == jc ? 1.f : (after ? -acc[i] : 0.f);
 #pragma unroll
-        for (int rr = ii + 1; rr < 16; ++rr) {
-          const int r = R ? 15 - rr : rr;
-          acc[r] = fmaf(Lm[(b0 + r) * LP + b0 + i], x[i], acc[r]);
+        for (int m = 0; m < 4; ++m) {
+          // rows 4 m .. 4 m + 3, where any of them comes after i
+          if (R ? 4 * m >= i : 4 * m + 3 <= i) continue;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldb + i * 16 + 4 * m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * m + e;
+            if (R ? r < i : r > i) acc[r] = fmaf(l4[e], x[i], acc[r]);
+          }
         }
       }
 #pragma unroll
@@ -415,7 +463,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
   // ---- exclusive readouts on bf16 operands: the low parts of the decayed
   // q.k tile, staged over the L tile (no longer read) ----
   MT* Plo = reinterpret_cast<MT*>(Lm);
-  if (a.pq_lo) {
+  if constexpr (PLO) {
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
       const int u = wave + 4 * j;
@@ -449,7 +497,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ScanArgs a) {
       __builtin_memcpy(&p16, pv, 16);
       bstore16_agent(rt, p * 16, t16);
       bstore16_agent(rp, p * 16, p16);
-      if (a.pq_lo) {
+      if constexpr (PLO) {
         const rsrc_t rl = make_rsrc(static_cast<MT*>(a.pq_lo) + cid * C * C, C * C * (int)sizeof(MT));
         MT lv[EPS];
 #pragma unroll
@@ -490,10 +538,16 @@ hipError_t launch_clear_ready(unsigned* ready, int64_t n, hipStream_t stream) {
 
 template <typename MT, int DK, int C>
 hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes* query) {
-  if (query) return hipFuncGetAttributes(query, reinterpret_cast<const void*>(&chunk_prep_kernel<MT, DK, C>));
+  // the low parts of the decayed q.k tile exist for bf16 operands only
+  const bool plo = std::is_same<MT, bf16>::value && a.pq_lo != nullptr;
+  const void* fn = plo ? reinterpret_cast<const void*>(&chunk_prep_kernel<MT, DK, C, true>)
+                       : reinterpret_cast<const void*>(&chunk_prep_kernel<MT, DK, C, false>);
+  if (query) return hipFuncGetAttributes(query, fn);
   const int64_t G = (a.B * a.H + 7) / 8;
   const int64_t slots = (a.fwd_on && a.rev_on) ? 2 * ((a.NC + 1) / 2) : a.NC;
-  hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C>), dim3((unsigned)(slots * G * 8)), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)(slots * G * 8));
+  if (plo) hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, true>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
