@@ -129,6 +129,10 @@ __device__ __forceinline__ void bstore16_agent(rsrc_t r, uint32_t off, f32x4 x) 
   __builtin_memcpy(&v, &x, 16);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kAgentScope);
 }
+__device__ __forceinline__ void bstore8_agent(rsrc_t r, uint32_t off, uint32_t lo, uint32_t hi) {
+  typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, (int)off, 0, kAgentScope);
+}
 __device__ __forceinline__ void bstore4_agent(rsrc_t r, uint32_t off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, (int)off, 0, kAgentScope);
 }

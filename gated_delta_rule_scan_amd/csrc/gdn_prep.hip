@@ -44,18 +44,17 @@ struct PrepSmem {
   static constexpr int KP = DK + EP;                    // padded row pitch of staged q/k
   static constexpr int NB = C / 16;                     // 16 x 16 blocks per side
   static constexpr int LP = C + 1;                      // pitch of fp32 C x C tiles
-  static constexpr int PP = C + EP;                     // pitch of the staged decayed q.k tile
   static constexpr size_t kq_bytes = (size_t)2 * C * KP * sizeof(MT);
-  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)C * PP * sizeof(MT) + (size_t)4 * 16 * 17 * 4;
+  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)4 * 16 * 17 * 4;
   static_assert(NB * 16 * 16 <= 4 * 16 * 17, "transposed diagonal blocks fit the scratch");
   static constexpr size_t region = kq_bytes > inv_bytes ? kq_bytes : inv_bytes;
 };
 
-// PLO: the low parts of the decayed q.k tile are kept and written (exclusive
-// readouts on bf16 operands); without them their registers are free, and
-// three workgroups per compute unit fit (as LDS allows).
+// PLO: the low parts of the decayed q.k tile are written too (exclusive
+// readouts on bf16 operands).  Without them, bf16 operands fit four
+// workgroups per compute unit (40 KB of LDS each) when the registers do too.
 template <typename MT, int DK, int C, bool PLO>
-__global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a) {
+__global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_prep_kernel(ScanArgs a) {
   using SM = PrepSmem<MT, DK, C>;
   using M = Mma<MT>;
   constexpr int EP = SM::EP, KP = SM::KP, NB = SM::NB, LP = SM::LP;
@@ -65,13 +64,11 @@ __global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a
   __shared__ __align__(16) float s_raw[4][64];  // raw gates as loaded (see below)
   __shared__ __align__(16) double s_g[2][C];   // cumulative log2-gates (double: see the scan)
 
-  constexpr int PP = SM::PP;
   MT* Ks = reinterpret_cast<MT*>(smem);
   MT* Qs = Ks + C * KP;
   float* Lm = reinterpret_cast<float*>(smem);  // reused after the Gram products
   float* Ti = Lm + C * LP;
-  MT* Pst = reinterpret_cast<MT*>(Ti + C * LP);                          // decayed q.k, staged
-  float* Wsc = reinterpret_cast<float*>(Pst + C * PP);                   // [4 waves][16][17]
+  float* Wsc = Ti + C * LP;                    // [4 waves][16][17]
   // the diagonal 16 x 16 blocks of L transposed (the forward entries below
   // the diagonal, the reverse ones above), read by the diagonal solve; the
   // off-diagonal blocks' scratch later reuses the space
@@ -241,7 +238,10 @@ __global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a
     if (lane < C) s_g[wave][wave == 0 ? lane : C - 1 - lane] = s;
   }
 
-  // ---- Gram K K^T and Q K^T on the matrix cores (raw operands, fp32 accumulate) ----
+  // ---- Gram K K^T and Q K^T on the matrix cores (raw operands, fp32
+  // accumulate), taken transposed: lane (l16, g4) of tile (ti, tj) ends up
+  // with row 16 ti + l16 and columns 16 tj + 4 g4 + i (i = 0..3), four
+  // consecutive entries of one row, as the decayed q.k tile is stored ----
   constexpr int NT2 = NB * NB;
   constexpr int UPW = (NT2 + 3) / 4;
   f32x4 accG[UPW], accP[UPW];
@@ -254,81 +254,89 @@ __global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a
       const int ti = u / NB, tj = u % NB;
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
-        const typename M::frag ka = M::load(Ks + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
-        const typename M::frag qa = M::load(Qs + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
-        const typename M::frag kb = M::load(Ks + (16 * tj + l16) * KP + 32 * ks + 8 * g4);
-        accG[j] = M::mma(ka, kb, accG[j]);
-        accP[j] = M::mma(qa, kb, accP[j]);
+        const typename M::frag kr = M::load(Ks + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
+        const typename M::frag qr = M::load(Qs + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
+        const typename M::frag kc = M::load(Ks + (16 * tj + l16) * KP + 32 * ks + 8 * g4);
+        accG[j] = M::mma(kc, kr, accG[j]);
+        accP[j] = M::mma(kc, qr, accP[j]);
       }
     }
   }
   __syncthreads();  // q/k staging area is reused below
 
-  // ---- gated, scaled triangles: L and the decayed Q^K^^T into LDS ----
+  // ---- gated, scaled triangles: L into LDS, the decayed Q^K^^T (with the
+  // self terms on its diagonal) straight to the workspace ----
   // (the erase-free variant has no erase term: L = 0, so (I + L)^{-1} = I)
+  // Below the diagonal the forward direction's entries, above it the
+  // reverse direction's; entries of a direction that is off are zero.  With
+  // PLO, the part of each decayed q.k entry that bf16 drops goes to its own
+  // tile (zero on the diagonal, whose remainder is in the chunk record).
   const float erase_w = a.erase ? 1.f : 0.f;
-  // Lane (l16, g4) of tile (ti, tj) holds column 16 tj + l16 of rows
-  // 16 ti + 4 g4 + i.  Below the diagonal the forward direction's entries,
-  // above it the reverse direction's; the diagonal (the self terms) is
-  // written beside the diagonal solve below.  plo: the part of each decayed
-  // q.k entry that the operand type drops, kept for exclusive readouts.
-  float plo[PLO ? UPW : 1][4];
+  {
+    const rsrc_t rpq = make_rsrc(static_cast<MT*>(a.pqk) + cid * C * C, C * C * (int)sizeof(MT));
+    const rsrc_t rpl = PLO ? make_rsrc(static_cast<MT*>(a.pq_lo) + cid * C * C, C * C * (int)sizeof(MT)) : rpq;
 #pragma unroll
-  for (int j = 0; j < (PLO ? UPW : 1); ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) plo[j][i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < UPW; ++j) {
-    const int u = wave + 4 * j;
-    if (u < NT2) {
+    for (int j = 0; j < UPW; ++j) {
+      const int u = wave + 4 * j;
+      if (u >= NT2) continue;
       const int ti = u / NB, tj = u % NB;
-      const int col = 16 * tj + l16, r0 = 16 * ti + 4 * g4;
-      const float rkc = s_rk[col];
-      const f32x4 rkr = *reinterpret_cast<const f32x4*>(&s_rk[r0]);
-      const f32x4 rqr = *reinterpret_cast<const f32x4*>(&s_rq[r0]);
+      const int r = 16 * ti + l16, c0 = 16 * tj + 4 * g4;
+      const float rkr = s_rk[r], rqr = s_rq[r];
+      const f32x4 rkc = *reinterpret_cast<const f32x4*>(&s_rk[c0]);
+      float pv[4] = {0.f, 0.f, 0.f, 0.f};
       if (ti != tj) {
-        // a tile off the diagonal holds one direction's entries (below: the
-        // forward one, above: the reverse one); the other direction never
-        // reads it
+        // a tile off the diagonal holds one direction's entries; the other
+        // direction never reads it
         const int dir = ti > tj ? 0 : 1;
         if (dir == 0 ? fwd_on : rev_on) {
-          const double gc = s_g[dir][col];
-          const f32x4 bt = *reinterpret_cast<const f32x4*>(&s_bt[dir][r0]);
+          const double gr = s_g[dir][r];
+          const float btr = s_bt[dir][r];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int r = r0 + i;
+            const int c = c0 + i;
             // decay between the two tokens (<= 0 in log2 units); below
             // 2^-126 it may flush to zero
-            const float e = __builtin_amdgcn_exp2f((float)(s_g[dir][r] - gc));
-            Lm[r * LP + col] = (rkr[i] * rkc) * accG[j][i] * (e * bt[i] * erase_w);
-            const float pv = (rqr[i] * rkc) * accP[j][i] * e;
-            const MT ph = (MT)pv;
-            Pst[r * PP + col] = ph;
-            if constexpr (PLO) plo[j][i] = pv - (float)ph;
+            const float e = __builtin_amdgcn_exp2f((float)(gr - s_g[dir][c]));
+            Lm[r * LP + c] = (rkr * rkc[i]) * accG[j][i] * (e * btr * erase_w);
+            pv[i] = (rqr * rkc[i]) * accP[j][i] * e;
           }
         }
       } else {
-        const double gfc = s_g[0][col], grc = s_g[1][col];
-        const f32x4 bf = *reinterpret_cast<const f32x4*>(&s_bt[0][r0]);
-        const f32x4 br = *reinterpret_cast<const f32x4*>(&s_bt[1][r0]);
+        const double grf = s_g[0][r], grr = s_g[1][r];
+        const float bfr = s_bt[0][r], brr = s_bt[1][r];
+        // the self term q^_t . k^_t (its remainder: the chunk record)
+        const float self = rqr * rkr * s_qk[r];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = r0 + i;
+          const int c = c0 + i;
           // 0/1 weights of the two directions (arithmetic selects: no branches)
-          const float wf = (col < r && fwd_on) ? 1.f : 0.f, wr = (col > r && rev_on) ? 1.f : 0.f;
+          const float wf = (c < r && fwd_on) ? 1.f : 0.f, wr = (c > r && rev_on) ? 1.f : 0.f;
           // zero where unused, so it never overflows
-          const float gd = fmaf(wf, (float)(s_g[0][r] - gfc), wr * (float)(s_g[1][r] - grc));
+          const float gd = fmaf(wf, (float)(grf - s_g[0][c]), wr * (float)(grr - s_g[1][c]));
           const float e = __builtin_amdgcn_exp2f(gd);
-          const float lm = e * fmaf(wf, bf[i], wr * br[i]) * erase_w;
-          const float pm = e * (wf + wr);
-          const float lv = (rkr[i] * rkc) * accG[j][i] * lm;
-          Lm[r * LP + col] = lv;
-          Ld[(tj * 16 + l16) * 16 + (r - r0 + 4 * g4)] = lv;  // transposed copy of the block
-          const float pv = (rqr[i] * rkc) * accP[j][i] * pm;
-          const MT ph = (MT)pv;
-          Pst[r * PP + col] = ph;
-          if constexpr (PLO) plo[j][i] = pv - (float)ph;
+          const float lm = e * fmaf(wf, bfr, wr * brr) * erase_w;
+          const float lv = (rkr * rkc[i]) * accG[j][i] * lm;
+          Lm[r * LP + c] = lv;
+          Ld[(tj * 16 + 4 * g4 + i) * 16 + l16] = lv;  // the block transposed
+          const float pm = (rqr * rkc[i]) * accP[j][i] * (e * (wf + wr));
+          pv[i] = c == r ? self : (wf + wr != 0.f ? pm : 0.f);
         }
+      }
+      const uint32_t off = (uint32_t)(r * C + c0) * (uint32_t)sizeof(MT);
+      if constexpr (sizeof(MT) == 2) {
+        bf16x4 ph, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ph[i] = (bf16)pv[i];
+          pl[i] = (c0 + i == r) ? (bf16)0.f : (bf16)(pv[i] - (float)ph[i]);
+        }
+        uint32_t w[2], wl[2];
+        __builtin_memcpy(w, &ph, 8);
+        __builtin_memcpy(wl, &pl, 8);
+        bstore8_agent(rpq, off, w[0], w[1]);
+        if constexpr (PLO) bstore8_agent(rpl, off, wl[0], wl[1]);
+      } else {
+        bstore16_agent(rpq, off, f32x4{pv[0], pv[1], pv[2], pv[3]});
       }
     }
   }
@@ -336,7 +344,8 @@ __global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a
 
   // ---- diagonal 16 x 16 blocks: one column of the inverse per thread ----
   if (tid < 2 * NB * 16) {
-    const int dir = tid / (NB * 16);
+    // with 64-token chunks each direction is one wave (uniform operands)
+    const int dir = NB == 4 ? (wave & 1) : tid / (NB * 16);
     const int blk = (tid / 16) % NB;
     const int jc = tid % 16;
     const int b0 = 16 * blk;
@@ -351,25 +360,48 @@ __global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a
     const float* ldb = Ld + blk * 256;
     auto solve = [&](auto rev_tag) {
       constexpr bool R = decltype(rev_tag)::value;
+      // the rows of group m (4 m .. 4 m + 3) that come after i
+      auto live = [](int i, int m) { return R ? 4 * m < i : 4 * m + 3 > i; };
       float acc[16], x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      // column i of L_bb, read one step ahead (a step is one scheduling
+      // region, so the reads are not all hoisted to the start)
+      f32x4 cur[4], nxt[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i0 = R ? 15 : 0;
+        cur[m] = live(i0, m) ? *reinterpret_cast<const f32x4*>(ldb + i0 * 16 + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
         const int i = R ? 15 - ii : ii;  // visiting order
+        if (ii < 15) {
+          const int in = R ? i - 1 : i + 1;
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            if (live(in, m)) nxt[m] = *reinterpret_cast<const f32x4*>(ldb + in * 16 + 4 * m);
+        }
         const bool after = R ? (i < jc) : (i > jc);
         x[i] = i == jc ? 1.f : (after ? -acc[i] : 0.f);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          // rows 4 m .. 4 m + 3, where any of them comes after i
-          if (R ? 4 * m >= i : 4 * m + 3 <= i) continue;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ldb + i * 16 + 4 * m);
+          if (!live(i, m)) continue;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * m + e;
-            if (R ? r < i : r > i) acc[r] = fmaf(l4[e], x[i], acc[r]);
+            if (R ? r < i : r > i) acc[r] = fmaf(cur[m][e], x[i], acc[r]);
           }
         }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) cur[m] = nxt[m];
+        // the step's products stay in the step (not sunk to their uses,
+        // which would keep every read of L live at once)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (R ? r < i : r > i) asm volatile("" : "+v"(acc[r]));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -380,13 +412,12 @@ __global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a
   } else if (tid - 2 * NB * 16 < 2 * C) {
     // ---- meanwhile, per-token scales and the chunk decays ----
     const int idx = tid - 2 * NB * 16;
-    const int dir = idx / C, tok = idx % C;
+    const int dir = NB == 4 ? (wave & 1) : idx / C, tok = idx % C;
     // self term q^_t . k^_t: the operand type's rounding on the diagonal of
     // the decayed q.k tile, the part it drops into each direction's record
     const float rk = s_rk[tok], rq = s_rq[tok];
     const float self = rq * rk * s_qk[tok];
     const MT self_mt = (MT)self;
-    if (dir == 0) Pst[tok * PP + tok] = self_mt;
     if (dir == 0 ? fwd_on : rev_on) {
       const int slot = dir == 0 ? fslot : rslot;
       const bool in = tok < nrows;
@@ -460,56 +491,22 @@ __global__ __launch_bounds__(256, PLO ? 2 : 3) void chunk_prep_kernel(ScanArgs a
   }
   __syncthreads();
 
-  // ---- exclusive readouts on bf16 operands: the low parts of the decayed
-  // q.k tile, staged over the L tile (no longer read) ----
-  MT* Plo = reinterpret_cast<MT*>(Lm);
-  if constexpr (PLO) {
-#pragma unroll
-    for (int j = 0; j < UPW; ++j) {
-      const int u = wave + 4 * j;
-      if (u < NT2) {
-        const int ti = u / NB, tj = u % NB;
-        const int col = 16 * tj + l16, r0 = 16 * ti + 4 * g4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Plo[(r0 + i) * PP + col] = (MT)plo[j][i];
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- both triangles to the workspace, 16 bytes per store ----
+  // ---- the inverse triangles to the workspace, 16 bytes per store ----
   {
     constexpr int EPS = 16 / (int)sizeof(MT);
     const rsrc_t rt = make_rsrc(static_cast<MT*>(a.tri) + cid * C * C, C * C * (int)sizeof(MT));
-    const rsrc_t rp = make_rsrc(static_cast<MT*>(a.pqk) + cid * C * C, C * C * (int)sizeof(MT));
     for (int p = tid; p < C * C / EPS; p += 256) {
       const int r = (p * EPS) / C, c0 = (p * EPS) % C;
-      MT tv[EPS], pv[EPS];
+      MT tv[EPS];
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
         const int col = c0 + e;
         const bool keep = (col < r && fwd_on) || (col > r && rev_on);
         tv[e] = (MT)(keep ? Ti[r * LP + col] : 0.f);
-        pv[e] = (keep || col == r) ? Pst[r * PP + col] : (MT)0.f;
       }
-      f32x4 t16, p16;
+      f32x4 t16;
       __builtin_memcpy(&t16, tv, 16);
-      __builtin_memcpy(&p16, pv, 16);
       bstore16_agent(rt, p * 16, t16);
-      bstore16_agent(rp, p * 16, p16);
-      if constexpr (PLO) {
-        const rsrc_t rl = make_rsrc(static_cast<MT*>(a.pq_lo) + cid * C * C, C * C * (int)sizeof(MT));
-        MT lv[EPS];
-#pragma unroll
-        for (int e = 0; e < EPS; ++e) {
-          const int col = c0 + e;
-          const bool keep = (col < r && fwd_on) || (col > r && rev_on);
-          lv[e] = keep ? Plo[r * PP + col] : (MT)0.f;
-        }
-        f32x4 l16v;
-        __builtin_memcpy(&l16v, lv, 16);
-        bstore16_agent(rl, p * 16, l16v);
-      }
     }
   }
 
@@ -545,7 +542,8 @@ hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes*
   if (query) return hipFuncGetAttributes(query, fn);
   const int64_t G = (a.B * a.H + 7) / 8;
   const int64_t slots = (a.fwd_on && a.rev_on) ? 2 * ((a.NC + 1) / 2) : a.NC;
-  const dim3 grid((unsigned)(slots * G * 8));
+  const int64_t nblocks = slots * G * 8;  // one per chunk id
+  const dim3 grid((unsigned)nblocks);
   if (plo) hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, true>), grid, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
