@@ -145,23 +145,25 @@ bool side_stream(int dev, SideStream** out) {
 
 // Whether the preparation pass runs concurrently with the state chain.
 //
-// Worth it only when the chain leaves at least half of the compute units
-// free: the state chain is bound by how fast each unit's L1 fills from L2,
-// and preparation traffic beside it slows it down.  Measured on MI355X with
+// Worth it only when the chain leaves most compute units free: preparation
+// workgroups beside the chain slow it down (they share L2 and the memory
+// path), and the preparation pass alone is short.  Measured on MI355X with
 // the bf16 column chain: 720p causal (128 chain workgroups on 256 units)
-// 1.90 ms concurrent against 2.14 ms serial; 720p bidirectional (192) 4.65
-// against 4.25 ms; 480p bidirectional (256) runs serial.  (Bidirectional
-// bf16 scans always run serial; see forward_impl.)
+// 1.80 ms concurrent against 1.74 ms serial (the chain 1.50 -> 1.79 ms
+// beside it); the streaming 480p frames (96 workgroups) 1.338 against 1.344
+// ms for 21 frames; 480p and 720p bidirectional run serial.  So the overlap
+// is taken only below a quarter of the units.  (Bidirectional bf16 scans
+// always run serial; see forward_impl.)
 //
 // Safe because the chain waits only for chunks the preparation pass
 // publishes, and a preparation workgroup can always be scheduled: there are
-// at most half as many chain workgroups as compute units, so at least half
-// of the units hold none, however the workgroups are packed.  The
-// preparation pass is enqueued first, so a device that runs the two streams
-// one after the other still finishes it before the chain starts.
+// at most a quarter as many chain workgroups as compute units, so most of
+// the units hold none, however the workgroups are packed.  The preparation
+// pass is enqueued first, so a device that runs the two streams one after
+// the other still finishes it before the chain starts.
 bool may_overlap(int64_t chain_wgs, int64_t NC) {
   constexpr int64_t kMinChunks = 16;  // below this the fork/join costs more than it hides
-  return NC >= kMinChunks && 2 * chain_wgs <= (int64_t)compute_units();
+  return NC >= kMinChunks && 4 * chain_wgs <= (int64_t)compute_units();
 }
 
 // Whether `stream` is being captured into a graph (any capture mode).  A
