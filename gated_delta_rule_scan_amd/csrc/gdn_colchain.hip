@@ -263,7 +263,7 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
   __shared__ __align__(1024) unsigned char cs0_[L::CSLOT], cs1_[L::CSLOT];  // chain ring
   __shared__ __align__(1024) unsigned char rs0_[L::RSLOT], rs1_[L::RSLOT];  // readout ring
   __shared__ __align__(1024) unsigned char xs0_[L::XSLOT], xs1_[L::XSLOT];  // exchange, by step parity
-  __shared__ __align__(1024) unsigned char pf_[1024];                        // L2-prefetch sink, never read
+  __shared__ __align__(256) unsigned char pf_[256];                          // L2-prefetch sink, never read
   lds_u8* const cs0 = (lds_u8*)cs0_;
   lds_u8* const cs1 = (lds_u8*)cs1_;
   lds_u8* const rs0 = (lds_u8*)rs0_;
@@ -793,41 +793,33 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     // sequence share (k and Tinv, q and P) ----
     // Those workgroups run in step and ask for the same lines at the same
     // time, so every one of them would wait for the same HBM fill.  Instead
-    // the loaders of a sequence's tiles each touch every 4th 1-KB unit of the
-    // chunk three ahead (direct-to-LDS into a sink nobody reads): when the
-    // chunk is staged two steps later, its lines are in this XCD's L2.
-    // (Measured at the 480p bidirectional shape: state chain 1.20 -> 1.09 ms;
-    // two, five or eight chunks ahead, or also the unshared value tile:
-    // slower.)  With the preparation running concurrently (a.ready set) only
-    // the raw k and q are prefetched: a prepared tile read before its ready
-    // flag could leave a stale line in this XCD's L2 (the preparation
-    // workgroup may run on another XCD), which the staging load would hit.
-    constexpr int NU = (L::KB + L::TB) / 1024;  // 1-KB units of k (or q) and the triangle
-    constexpr int kPfR = (NU + 3) / 4;          // prefetch loads per role and step
-    constexpr int NUK = L::KB / 1024;
-    const int pfbase = tile & 3;
+    // the loaders of a sequence's tiles each touch every ntiles-th 128-byte
+    // line of the chunk three ahead, one line per lane, with 4-byte loads
+    // into a sink nobody reads: when the chunk is staged two steps later,
+    // its lines are in this XCD's L2.  (Measured at the 480p bidirectional
+    // shape: state chain 1.20 -> 1.09 ms with the prefetch; two, five or
+    // eight chunks ahead, or also the unshared value tile: slower.)  With the
+    // preparation running concurrently (a.ready set) only the raw k and q
+    // are prefetched: a prepared tile read before its ready flag could leave
+    // a stale line in this XCD's L2 (the preparation workgroup may run on
+    // another XCD), which the staging load would hit.
+    constexpr int LPR = L::KROWB / 128;  // 128-byte lines per k (q) row
+    constexpr int KL = L::KB / 128, TL = L::TB / 128;
+    static_assert(KL <= 128 && TL <= 64, "a workgroup's lines fit one lane each when ntiles >= 2");
     const bool pf_prepared = a.ready == nullptr;  // prepared tiles are final before the chain starts
-    auto pf_unit = [&](int m) {
-      const int u = min(pfbase + 4 * m, NU - 1);
-      return (u < NUK || pf_prepared) ? u : u % NUK;
-    };
-    uint32_t pfoff[kPfR];
-#pragma unroll
-    for (int m = 0; m < kPfR; ++m) {
-      const int u = pf_unit(m);
-      const int byte = u * 1024 + 16 * lane;
-      pfoff[m] = u < NUK ? (uint32_t)((byte / L::KROWB) * HDB + (byte % L::KROWB)) : (uint32_t)(byte - L::KB);
-    }
+    const int lk = tile + ntiles * lane;  // this lane's line of the k (q) tile and of a triangle
+    const uint32_t pfk = lk < KL ? (uint32_t)((lk / LPR) * HDB + (lk % LPR) * 128) : 0xFFFFFFF0u;
+    const uint32_t pft = lk < TL ? (uint32_t)(lk * 128) : 0xFFFFFFF0u;
     auto prefetch = [&](int c) {
       const uint32_t rows = rows_of(c);
       const rsrc_t rk = make_rsrc(kbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
       const rsrc_t rq = make_rsrc(qbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
-      const rsrc_t rt = make_rsrc(trib + (size_t)c * L::TB, (uint32_t)L::TB);
-      const rsrc_t rp = make_rsrc(pqkb + (size_t)c * L::TB, (uint32_t)L::TB);
-#pragma unroll
-      for (int m = 0; m < kPfR; ++m) dma16(pf_unit(m) < NUK ? rk : rt, pfs, pfoff[m]);
-#pragma unroll
-      for (int m = 0; m < kPfR; ++m) dma16(pf_unit(m) < NUK ? rq : rp, pfs, pfoff[m]);
+      const rsrc_t rt = pf_prepared ? make_rsrc(trib + (size_t)c * L::TB, (uint32_t)L::TB) : rnone;
+      const rsrc_t rp = pf_prepared ? make_rsrc(pqkb + (size_t)c * L::TB, (uint32_t)L::TB) : rnone;
+      dma4(rk, pfs, pfk);
+      dma4(rt, pfs, pft);
+      dma4(rq, pfs, pfk);
+      dma4(rp, pfs, pft);
     };
 
     // ready flags of the concurrent preparation (0 = ready; without a.ready
@@ -864,7 +856,7 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     // last steps restage the last chunk into idle slots), which the step-end
     // waits and the compiler's loop waits count on.  `fl` is chunk s + 1's
     // ready flag, loaded two steps ago, and receives chunk s + 3's.
-    constexpr int kLTail = 2 * kPfR + 1;  // loads left in flight at a step's end: the prefetch and the flag
+    constexpr int kLTail = 5;  // loads left in flight at a step's end: the four prefetch loads and the flag
     auto load_step = [&](lds_u8* cnext, lds_u8* rcur, uint32_t& fl, int s) {
       const int cn = chunk_at(min(s + 1, NC - 1));
       const bool expired = ensure_ready(fl, cn);
