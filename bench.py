@@ -573,7 +573,8 @@ def run_stream(args, w) -> int:
     def rollout(evs=None):
         for i, f in enumerate(frames):
             gdn.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], state, w.direction, out=outs[i],
-                        state_out=state, workspace=ws, timing_events=None if evs is None else evs.ptr(4 * i))
+                        state_out=state, workspace=ws, timing_events=None if evs is None else evs.ptr(4 * i),
+                        serial=args.serial)
 
     for _ in range(max(1, args.warmup)):
         reset()

@@ -150,9 +150,9 @@ bool side_stream(int dev, SideStream** out) {
 // path), and the preparation pass alone is short.  Measured on MI355X with
 // the bf16 column chain: 720p causal (128 chain workgroups on 256 units)
 // 1.80 ms concurrent against 1.74 ms serial (the chain 1.50 -> 1.79 ms
-// beside it); the streaming 480p frames (96 workgroups) 1.338 against 1.344
-// ms for 21 frames; 480p and 720p bidirectional run serial.  So the overlap
-// is taken only below a quarter of the units.  (Bidirectional bf16 scans
+// beside it); the streaming 480p frames (96 workgroups) 0.064 against 0.047
+// ms per frame; 480p and 720p bidirectional run serial.  So the overlap is
+// taken only below a quarter of the units.  (Bidirectional bf16 scans
 // always run serial; see forward_impl.)
 //
 // Safe because the chain waits only for chunks the preparation pass
