@@ -45,8 +45,7 @@ struct PrepSmem {
   static constexpr int NB = C / 16;                     // 16 x 16 blocks per side
   static constexpr int LP = C + 1;                      // pitch of fp32 C x C tiles
   static constexpr size_t kq_bytes = (size_t)2 * C * KP * sizeof(MT);
-  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)4 * 16 * 17 * 4;
-  static_assert(NB * 16 * 16 <= 4 * 16 * 17, "transposed diagonal blocks fit the scratch");
+  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)NB * 16 * 16 * 4;
   static constexpr size_t region = kq_bytes > inv_bytes ? kq_bytes : inv_bytes;
 };
 
@@ -68,11 +67,9 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   MT* Qs = Ks + C * KP;
   float* Lm = reinterpret_cast<float*>(smem);  // reused after the Gram products
   float* Ti = Lm + C * LP;
-  float* Wsc = Ti + C * LP;                    // [4 waves][16][17]
   // the diagonal 16 x 16 blocks of L transposed (the forward entries below
-  // the diagonal, the reverse ones above), read by the diagonal solve; the
-  // off-diagonal blocks' scratch later reuses the space
-  float* Ld = Wsc;  // [NB][16][16]
+  // the diagonal, the reverse ones above), read by the diagonal solve
+  float* Ld = Ti + C * LP;  // [NB][16][16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -437,38 +434,40 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
 
   // ---- off-diagonal blocks: one block column per wave, on fp32 matrix cores ----
   // v_mfma_f32_16x16x4f32: lane (l16, g4) supplies A[l16][k] and B[k][l16]
-  // with k = 4 ks + g4; D lands as D[4 g4 + i][l16].
+  // for one k of the product's four; D lands as D[4 g4 + i][l16].  Product ks
+  // of a 16-wide contraction takes k = 4 g4 + ks, so the result W of the
+  // first contraction is, in each lane's registers, exactly the operand
+  // W[4 g4 + ks][l16] the second one needs (no trip through LDS).
   {
-    float* wsc = Wsc + wave * 16 * 17;
     auto column = [&](int dir, int J) {
       const bool up = dir == 1;
       const int I0 = up ? J - 1 : J + 1;
       const int I1 = up ? -1 : NB;
       const int dI = up ? -1 : 1;
       for (int I = I0; I != I1; I += dI) {
-        // W = sum_K L_IK T_KJ over K between J and I (T_JJ triangular)
-        f32x4 w = {0.f, 0.f, 0.f, 0.f};
+        // W = sum_K L_IK T_KJ over K between J and I (T_JJ triangular), in
+        // two accumulators (half the dependent chain)
+        f32x4 wa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         const int K0 = up ? I + 1 : J, K1 = up ? J : I - 1;
         for (int K = K0; K <= K1; ++K) {
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const int k = 4 * ks + g4;
+            const int k = 4 * g4 + ks;
             const float av = Lm[(16 * I + l16) * LP + 16 * K + k];
             float bv = Ti[(16 * K + k) * LP + 16 * J + l16];
             if (K == J && (up ? k > l16 : k < l16)) bv = 0.f;
-            w = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, w, 0, 0, 0);
+            wa[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, wa[ks & 1], 0, 0, 0);
           }
         }
-        // T_IJ = -T_II W (W through this wave's scratch; LDS is in order per wave)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wsc[(4 * g4 + i) * 17 + l16] = w[i];
+        const f32x4 w = wa[0] + wa[1];
+        // T_IJ = -T_II W
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int k = 4 * ks + g4;
+          const int k = 4 * g4 + ks;
           float av = Ti[(16 * I + l16) * LP + 16 * I + k];
           if (up ? k < l16 : k > l16) av = 0.f;
-          t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wsc[k * 17 + l16], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, w[ks], t, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ti[(16 * I + 4 * g4 + i) * LP + 16 * J + l16] = -t[i];
