@@ -494,14 +494,24 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   {
     constexpr int EPS = 16 / (int)sizeof(MT);
     const rsrc_t rt = make_rsrc(static_cast<MT*>(a.tri) + cid * C * C, C * C * (int)sizeof(MT));
-    for (int p = tid; p < C * C / EPS; p += 256) {
+    constexpr int NP = C * C / EPS;  // 16-byte pieces of the tile
+#pragma unroll
+    for (int it = 0; it < (NP + 255) / 256; ++it) {
+      const int p = tid + 256 * it;
+      if (NP % 256 != 0 && p >= NP) break;
       const int r = (p * EPS) / C, c0 = (p * EPS) % C;
+      // every entry is read (all lie inside the tile) and the unused ones
+      // are masked away afterwards: a read under the condition would become
+      // one branch and one LDS round trip per entry
+      float tf[EPS];
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) tf[e] = Ti[r * LP + c0 + e];
       MT tv[EPS];
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
         const int col = c0 + e;
         const bool keep = (col < r && fwd_on) || (col > r && rev_on);
-        tv[e] = (MT)(keep ? Ti[r * LP + col] : 0.f);
+        tv[e] = (MT)__uint_as_float(__float_as_uint(tf[e]) & (keep ? ~0u : 0u));
       }
       f32x4 t16;
       __builtin_memcpy(&t16, tv, 16);
