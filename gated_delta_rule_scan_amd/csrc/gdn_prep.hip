@@ -43,9 +43,21 @@ struct PrepSmem {
   static constexpr int EP = 16 / (int)sizeof(MT);       // elements per 16-byte piece
   static constexpr int KP = DK + EP;                    // padded row pitch of staged q/k
   static constexpr int NB = C / 16;                     // 16 x 16 blocks per side
-  static constexpr int LP = C + 1;                      // pitch of fp32 C x C tiles
+  // The inverse works on fp32 16 x 16 blocks, each stored as the register
+  // image of the matrix-core operand that reads it (fragment order below),
+  // so that a fragment read or a result write is one consecutive dword per
+  // lane, free of LDS bank conflicts:
+  //   * L's off-diagonal blocks in A order: entry (r, c) at 64 (c % 4) + 16 (c / 4) + r;
+  //   * the inverse's blocks in B order: entry (r, c) at 64 (r % 4) + 16 (r / 4) + c,
+  //     which is also where a 16 x 16 product leaves entry (r, c); block
+  //     stride 272 (16 dwords of padding), so the four diagonal blocks,
+  //     written column by column by the substitution, start in different banks;
+  //   * L's diagonal blocks transposed for the substitution: rows of 20, blocks
+  //     of 336 dwords (the same bank spreading for their 16-byte reads).
+  static constexpr int LB = 256, TB = 272, DR = 20, DB = 336;
+  static constexpr int LM_F = NB * (NB - 1) * LB, TI_F = NB * NB * TB, LD_F = NB * DB;
   static constexpr size_t kq_bytes = (size_t)2 * C * KP * sizeof(MT);
-  static constexpr size_t inv_bytes = (size_t)2 * C * LP * 4 + (size_t)NB * 16 * 16 * 4;
+  static constexpr size_t inv_bytes = (size_t)(LM_F + TI_F + LD_F) * 4;
   static constexpr size_t region = kq_bytes > inv_bytes ? kq_bytes : inv_bytes;
 };
 
@@ -56,7 +68,8 @@ template <typename MT, int DK, int C, bool PLO>
 __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_prep_kernel(ScanArgs a) {
   using SM = PrepSmem<MT, DK, C>;
   using M = Mma<MT>;
-  constexpr int EP = SM::EP, KP = SM::KP, NB = SM::NB, LP = SM::LP;
+  constexpr int EP = SM::EP, KP = SM::KP, NB = SM::NB;
+  constexpr int TB = SM::TB, DR = SM::DR, DB = SM::DB;
 
   __shared__ __align__(16) unsigned char smem[SM::region];
   __shared__ __align__(16) float s_rk[C], s_rq[C], s_qk[C];  // row scales, raw q.k of each token
@@ -65,11 +78,15 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
 
   MT* Ks = reinterpret_cast<MT*>(smem);
   MT* Qs = Ks + C * KP;
-  float* Lm = reinterpret_cast<float*>(smem);  // reused after the Gram products
-  float* Ti = Lm + C * LP;
+  // after the Gram products, the q/k staging area holds the inverse's blocks
+  float* Lm = reinterpret_cast<float*>(smem);  // L's off-diagonal blocks, A order
+  float* Ti = Lm + SM::LM_F;                   // the inverse's blocks, B order
   // the diagonal 16 x 16 blocks of L transposed (the forward entries below
   // the diagonal, the reverse ones above), read by the diagonal solve
-  float* Ld = Ti + C * LP;  // [NB][16][16]
+  float* Ld = Ti + SM::TI_F;
+  // block (I, K) of L (I != K) and block (R, Q) of the inverse
+  auto lblk = [&](int I, int K) { return Lm + (I * (NB - 1) + (K < I ? K : K - 1)) * SM::LB; };
+  auto tblk = [&](int R, int Q) { return Ti + (R * NB + Q) * TB; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -294,7 +311,8 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
             // decay between the two tokens (<= 0 in log2 units); below
             // 2^-126 it may flush to zero
             const float e = __builtin_amdgcn_exp2f((float)(gr - s_g[dir][c]));
-            Lm[r * LP + c] = (rkr * rkc[i]) * accG[j][i] * (e * btr * erase_w);
+            // entry (l16, 4 g4 + i) of block (ti, tj), A order
+            lblk(ti, tj)[64 * i + lane] = (rkr * rkc[i]) * accG[j][i] * (e * btr * erase_w);
             pv[i] = (rqr * rkc[i]) * accP[j][i] * e;
           }
         }
@@ -313,8 +331,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
           const float e = __builtin_amdgcn_exp2f(gd);
           const float lm = e * fmaf(wf, bfr, wr * brr) * erase_w;
           const float lv = (rkr * rkc[i]) * accG[j][i] * lm;
-          Lm[r * LP + c] = lv;
-          Ld[(tj * 16 + 4 * g4 + i) * 16 + l16] = lv;  // the block transposed
+          Ld[tj * DB + (4 * g4 + i) * DR + l16] = lv;  // the block transposed
           const float pm = (rqr * rkc[i]) * accP[j][i] * (e * (wf + wr));
           pv[i] = c == r ? self : (wf + wr != 0.f ? pm : 0.f);
         }
@@ -345,7 +362,6 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
     const int dir = NB == 4 ? (wave & 1) : tid / (NB * 16);
     const int blk = (tid / 16) % NB;
     const int jc = tid % 16;
-    const int b0 = 16 * blk;
     // column jc of (I + L_bb)^{-1} by forward substitution in visiting
     // order, column-oriented: once x_i is known it is folded into every
     // later row's running sum, so the dependent chain is 16 steps long.
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
     // can be issued ahead of the chain.  One instance per direction keeps
     // every index a compile-time constant (the running sums stay in
     // registers).
-    const float* ldb = Ld + blk * 256;
+    const float* ldb = Ld + blk * DB;
     auto solve = [&](auto rev_tag) {
       constexpr bool R = decltype(rev_tag)::value;
       // the rows of group m (4 m .. 4 m + 3) that come after i
@@ -368,7 +384,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int i0 = R ? 15 : 0;
-        cur[m] = live(i0, m) ? *reinterpret_cast<const f32x4*>(ldb + i0 * 16 + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
+        cur[m] = live(i0, m) ? *reinterpret_cast<const f32x4*>(ldb + i0 * DR + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
@@ -377,7 +393,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
           const int in = R ? i - 1 : i + 1;
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            if (live(in, m)) nxt[m] = *reinterpret_cast<const f32x4*>(ldb + in * 16 + 4 * m);
+            if (live(in, m)) nxt[m] = *reinterpret_cast<const f32x4*>(ldb + in * DR + 4 * m);
         }
         const bool after = R ? (i < jc) : (i > jc);
         x[i] = i == jc ? 1.f : (after ? -acc[i] : 0.f);
@@ -402,7 +418,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (R ? i <= jc : i >= jc) Ti[(b0 + i) * LP + b0 + jc] = x[i];
+        if (R ? i <= jc : i >= jc) tblk(blk, blk)[64 * (i & 3) + 16 * (i >> 2) + jc] = x[i];
     };
     if (dir == 0 && fwd_on) solve(std::false_type{});
     if (dir == 1 && rev_on) solve(std::true_type{});
@@ -437,7 +453,9 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   // for one k of the product's four; D lands as D[4 g4 + i][l16].  Product ks
   // of a 16-wide contraction takes k = 4 g4 + ks, so the result W of the
   // first contraction is, in each lane's registers, exactly the operand
-  // W[4 g4 + ks][l16] the second one needs (no trip through LDS).
+  // W[4 g4 + ks][l16] the second one needs (no trip through LDS), and every
+  // A or B fragment of a stored block is the dword 64 ks + lane of its
+  // block (the fragment orders above).
   {
     auto column = [&](int dir, int J) {
       const bool up = dir == 1;
@@ -453,8 +471,8 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const int k = 4 * g4 + ks;
-            const float av = Lm[(16 * I + l16) * LP + 16 * K + k];
-            float bv = Ti[(16 * K + k) * LP + 16 * J + l16];
+            const float av = lblk(I, K)[64 * ks + lane];
+            float bv = tblk(K, J)[64 * ks + lane];
             if (K == J && (up ? k > l16 : k < l16)) bv = 0.f;
             wa[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, wa[ks & 1], 0, 0, 0);
           }
@@ -464,13 +482,14 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+          // entry (l16, k) of the diagonal block, read across its B order
           const int k = 4 * g4 + ks;
-          float av = Ti[(16 * I + l16) * LP + 16 * I + k];
+          float av = tblk(I, I)[64 * (l16 & 3) + 16 * (l16 >> 2) + k];
           if (up ? k < l16 : k > l16) av = 0.f;
           t = __builtin_amdgcn_mfma_f32_16x16x4f32(av, w[ks], t, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Ti[(16 * I + 4 * g4 + i) * LP + 16 * J + l16] = -t[i];
+        for (int i = 0; i < 4; ++i) tblk(I, J)[64 * i + lane] = -t[i];
       }
     };
     if constexpr (NB == 4) {
@@ -500,12 +519,18 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
       const int p = tid + 256 * it;
       if (NP % 256 != 0 && p >= NP) break;
       const int r = (p * EPS) / C, c0 = (p * EPS) % C;
-      // every entry is read (all lie inside the tile) and the unused ones
-      // are masked away afterwards: a read under the condition would become
-      // one branch and one LDS round trip per entry
+      // EPS consecutive entries of row r, consecutive in its block's B order
+      // too.  Every entry is read (all lie inside the tile) and the unused
+      // ones are masked away afterwards: a read under the condition would
+      // become one branch and one LDS round trip per entry
+      const float* src = tblk(r >> 4, c0 >> 4) + 64 * (r & 3) + 16 * ((r >> 2) & 3) + (c0 & 15);
       float tf[EPS];
 #pragma unroll
-      for (int e = 0; e < EPS; ++e) tf[e] = Ti[r * LP + c0 + e];
+      for (int e = 0; e < EPS; e += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tf[e + u] = v[u];
+      }
       MT tv[EPS];
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
