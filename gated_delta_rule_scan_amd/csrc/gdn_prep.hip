@@ -38,6 +38,29 @@
 
 namespace gdn {
 
+// x plus its value in another lane of the same 16-lane row, moved by a data
+// parallel primitive (no LDS): 0xB1 and 0x4E swap neighbouring lanes and
+// lane pairs of each quad, 0x141 mirrors each half row, 0x140 each row
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over each aligned group of N consecutive lanes (N a power of two, 2 ..
+// 64), the same in every lane of the group: within a row by permutations,
+// across rows by lane shuffles
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "group size");
+  x = dpp_add<0xB1>(x);
+  if constexpr (N >= 4) x = dpp_add<0x4E>(x);
+  if constexpr (N >= 8) x = dpp_add<0x141>(x);
+  if constexpr (N >= 16) x = dpp_add<0x140>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
 template <typename MT, int DK, int C>
 struct PrepSmem {
   static constexpr int EP = 16 / (int)sizeof(MT);       // elements per 16-byte piece
@@ -189,12 +212,9 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
           sqk = fmaf(xq, xk, sqk);
         }
       }
-#pragma unroll
-      for (int m = 1; m < PR; m <<= 1) {
-        sq += __shfl_xor(sq, m, 64);
-        sk += __shfl_xor(sk, m, 64);
-        sqk += __shfl_xor(sqk, m, 64);
-      }
+      sq = group_sum<PR>(sq);
+      sk = group_sum<PR>(sk);
+      sqk = group_sum<PR>(sqk);
       const int row = prow + RPI * i;
       if (tid % PR == 0) {
         // 1 / max(|x|, eps) as a reciprocal square root (one rounding more
