@@ -324,36 +324,38 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
         const int dir = ti > tj ? 0 : 1;
         if (dir == 0 ? fwd_on : rev_on) {
           const double gr = s_g[dir][r];
-          const float btr = s_bt[dir][r];
+          const float fl = rkr * s_bt[dir][r] * erase_w;  // the row's factor of L
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int c = c0 + i;
-            // decay between the two tokens (<= 0 in log2 units); below
-            // 2^-126 it may flush to zero
-            const float e = __builtin_amdgcn_exp2f((float)(gr - s_g[dir][c]));
+            // decay between the two tokens (<= 0 in log2 units; below
+            // 2^-126 it may flush to zero) times the column's k scale
+            const float ek = __builtin_amdgcn_exp2f((float)(gr - s_g[dir][c])) * rkc[i];
             // entry (l16, 4 g4 + i) of block (ti, tj), A order
-            lblk(ti, tj)[64 * i + lane] = (rkr * rkc[i]) * accG[j][i] * (e * btr * erase_w);
-            pv[i] = (rqr * rkc[i]) * accP[j][i] * e;
+            lblk(ti, tj)[64 * i + lane] = (fl * ek) * accG[j][i];
+            pv[i] = (rqr * ek) * accP[j][i];
           }
         }
       } else {
         const double grf = s_g[0][r], grr = s_g[1][r];
-        const float bfr = s_bt[0][r], brr = s_bt[1][r];
+        const float flf = rkr * s_bt[0][r] * erase_w, flr = rkr * s_bt[1][r] * erase_w;
         // the self term q^_t . k^_t (its remainder: the chunk record)
         const float self = rqr * rkr * s_qk[r];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = c0 + i;
-          // 0/1 weights of the two directions (arithmetic selects: no branches)
-          const float wf = (c < r && fwd_on) ? 1.f : 0.f, wr = (c > r && rev_on) ? 1.f : 0.f;
-          // zero where unused, so it never overflows
-          const float gd = fmaf(wf, (float)(grf - s_g[0][c]), wr * (float)(grr - s_g[1][c]));
-          const float e = __builtin_amdgcn_exp2f(gd);
-          const float lm = e * fmaf(wf, bfr, wr * brr) * erase_w;
-          const float lv = (rkr * rkc[i]) * accG[j][i] * lm;
-          Ld[tj * DB + (4 * g4 + i) * DR + l16] = lv;  // the block transposed
-          const float pm = (rqr * rkc[i]) * accP[j][i] * (e * (wf + wr));
-          pv[i] = c == r ? self : (wf + wr != 0.f ? pm : 0.f);
+          // an entry is the reverse direction's above the diagonal, the
+          // forward one's below (selects, no branches); unused entries take a
+          // zero exponent, so they never overflow, and a zero factor
+          const bool up = c > r;
+          const uint32_t on = (up ? rev_on != 0 : (c < r && fwd_on)) ? ~0u : 0u;
+          // both directions' sums are read and one is kept (a read under the
+          // condition would become a branch and an LDS round trip per entry)
+          const double g0c = s_g[0][c], g1c = s_g[1][c];
+          const float gd = __uint_as_float(__float_as_uint((float)((up ? grr : grf) - (up ? g1c : g0c))) & on);
+          const float ek = __builtin_amdgcn_exp2f(gd) * __uint_as_float(__float_as_uint(rkc[i]) & on);
+          Ld[tj * DB + (4 * g4 + i) * DR + l16] = ((up ? flr : flf) * ek) * accG[j][i];  // the block transposed
+          pv[i] = c == r ? self : (rqr * ek) * accP[j][i];
         }
       }
       const uint32_t off = (uint32_t)(r * C + c0) * (uint32_t)sizeof(MT);
