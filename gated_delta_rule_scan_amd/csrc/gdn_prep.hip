@@ -61,6 +61,29 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// v from another lane (DPP control CTRL, rows in the mask ROWS; 0 where no
+// lane is read), a double moved as its two halves
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROWS, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROWS, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes within each row of 16, then the last lane of row 0 (2) added to row 1
+// (3), then the last lane of row 1 added to rows 2 and 3
+__device__ __forceinline__ double wave_prefix_sum(double x) {
+  x += dpp_f64<0x111, 0xF>(x);
+  x += dpp_f64<0x112, 0xF>(x);
+  x += dpp_f64<0x114, 0xF>(x);
+  x += dpp_f64<0x118, 0xF>(x);
+  x += dpp_f64<0x142, 0xA>(x);
+  x += dpp_f64<0x143, 0xC>(x);
+  return x;
+}
+
 template <typename MT, int DK, int C>
 struct PrepSmem {
   static constexpr int EP = 16 / (int)sizeof(MT);       // elements per 16-byte piece
@@ -263,12 +286,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   // relative error of 1e-5 in every decay factor taken as a difference of
   // two of them; in double, each difference is rounded once, to fp32.
   if (wave < 2) {
-    double s = (double)s_raw[wave][lane] * kLog2eD;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const double o = __shfl_up(s, d, 64);
-      if (lane >= d) s += o;
-    }
+    const double s = wave_prefix_sum((double)s_raw[wave][lane] * kLog2eD);
     if (lane < C) s_g[wave][wave == 0 ? lane : C - 1 - lane] = s;
   }
 
@@ -279,6 +297,13 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   constexpr int NT2 = NB * NB;
   constexpr int UPW = (NT2 + 3) / 4;
   f32x4 accG[UPW], accP[UPW];
+  // with four block columns a wave's tiles share their column block (tj =
+  // wave): its k fragments are read once
+  typename M::frag kcw[DK / 32];
+  if constexpr (NB == 4) {
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) kcw[ks] = M::load(Ks + (16 * wave + l16) * KP + 32 * ks + 8 * g4);
+  }
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     accG[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -290,7 +315,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
       for (int ks = 0; ks < DK / 32; ++ks) {
         const typename M::frag kr = M::load(Ks + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
         const typename M::frag qr = M::load(Qs + (16 * ti + l16) * KP + 32 * ks + 8 * g4);
-        const typename M::frag kc = M::load(Ks + (16 * tj + l16) * KP + 32 * ks + 8 * g4);
+        const typename M::frag kc = NB == 4 ? kcw[ks] : M::load(Ks + (16 * tj + l16) * KP + 32 * ks + 8 * g4);
         accG[j] = M::mma(kc, kr, accG[j]);
         accP[j] = M::mma(kc, qr, accP[j]);
       }
