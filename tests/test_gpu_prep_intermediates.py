@@ -23,14 +23,12 @@ from oracle import chunked_ref as cr
 
 pytestmark = pytest.mark.gpu
 
-C = 64
-
 
 def _align(x, a=256):
     return (x + a - 1) // a * a
 
 
-def _layout(nbh, nc, dirs, mt):
+def _layout(nbh, nc, dirs, mt, C):
     off = 0
     nch = nbh * nc
     tri = off
@@ -43,25 +41,30 @@ def _layout(nbh, nc, dirs, mt):
     return tri, pqk, sc, pdg
 
 
+# every block count of the inverse (two 16-token blocks per side at C = 32,
+# four at C = 64) and both head widths of the staged q / k
+@pytest.mark.parametrize("C,d", [(64, 64), (32, 64), (64, 128), (32, 128)])
 @pytest.mark.parametrize("dtype,tol", [("f32", 2e-5), ("bf16", 1e-2)])
-def test_chunk_preparation_outputs(dtype, tol):
+def test_chunk_preparation_outputs(dtype, tol, C, d):
     import torch
 
     import gated_delta_rule_scan_amd as gdn
 
-    B, H, T, d = 1, 2, 150, 64  # three chunks, the last of 22 tokens
+    B, H, T = 1, 2, 150  # the last chunk ragged: 22 tokens (of 64, or of 32)
     w = synth.Workload("prep", B, H, T, d, d, dtype, "bi", 3.0, 0.02, 61)
     x = synth.generate(w)
     dd = {k: to_torch(v) for k, v in x.items()}
     mt = 4 if dtype == "f32" else 2
-    prob = gdn.gdn_problem_t(B=B, T=T, H=H, dk=d, dv=d, dtype=gdn.GDN_DTYPE_F32 if dtype == "f32" else gdn.GDN_DTYPE_BF16)
+    prob = gdn.gdn_problem_t(B=B, T=T, H=H, dk=d, dv=d, chunk=C,
+                             dtype=gdn.GDN_DTYPE_F32 if dtype == "f32" else gdn.GDN_DTYPE_BF16)
     ws = torch.zeros(gdn.gdn_workspace_bytes(prob, gdn.GDN_DIR_BIDIRECTIONAL), dtype=torch.uint8, device="cuda")
-    gdn.forward(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], dd["state_in"], "bi", workspace=ws, serial=True)
+    gdn.forward(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], dd["state_in"], "bi", chunk=C,
+                workspace=ws, serial=True)
     torch.cuda.synchronize()
     raw = ws.cpu().numpy()
     nc = (T + C - 1) // C
     nbh = B * H
-    o_tri, o_pqk, o_sc, o_pdg = _layout(nbh, nc, 2, mt)
+    o_tri, o_pqk, o_sc, o_pdg = _layout(nbh, nc, 2, mt, C)
     mdt = np.float32 if mt == 4 else np.uint16
 
     def mat(off, cid):
@@ -117,4 +120,4 @@ def test_chunk_preparation_outputs(dtype, tol):
                 bad = np.abs(sc - want_sc) > (1e-6 + 1e-7 * arg) * np.abs(want_sc) + 1e-37
                 assert not bad.any(), (f"scales bh {bh} chunk {c} slot {slot}: {np.argwhere(bad)[:3]} "
                                        f"got {sc[bad][:3]} want {want_sc[bad][:3]}")
-    print(f"\nprep {dtype}: worst triangle error {worst:.2e}")
+    print(f"\nprep {dtype} C={C} d={d}: worst triangle error {worst:.2e}")
