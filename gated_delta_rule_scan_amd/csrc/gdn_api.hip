@@ -79,12 +79,23 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   // with the other heads' -- through 32-bit byte offsets
   if ((p->T + 64) * p->H * (p->dk > p->dv ? p->dk : p->dv) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
   const int C = p->chunk == 0 ? 64 : p->chunk;
-  if (C != 32 && C != 64) return GDN_ERR_UNSUPPORTED;
+  if (C != 32 && C != 64 && C != 128) return GDN_ERR_UNSUPPORTED;
+  const bool excl = (p->options & (GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE)) != 0;
+  // 128-token chunks run the two-role chain for both operand types, whose bf16
+  // readout carries the entry state and P in bf16 only: the exclusive readouts
+  // and the epilogue, which need their low parts, take 32- or 64-token chunks
+  if (C == 128 && p->dtype == GDN_DTYPE_BF16 && (excl || p->gate)) return GDN_ERR_UNSUPPORTED;
   int NT = 0;  // 0: chosen at launch (any choice divides dv)
   if (p->dv_tile != 0) {
     if (p->dv_tile != 16 && p->dv_tile != 32) return GDN_ERR_UNSUPPORTED;
     NT = p->dv_tile / 16;
     if (p->dv % (16 * NT) != 0) return GDN_ERR_UNSUPPORTED;
+  }
+  // fp32 operands with dk = 128 fit 16-column tiles only at 128-token chunks
+  const bool narrow = C == 128 && p->dtype == GDN_DTYPE_F32 && p->dk == 128;
+  if (narrow) {
+    if (NT == 2) return GDN_ERR_UNSUPPORTED;
+    NT = 1;
   }
   pl->C = C;
   pl->NT = NT;
@@ -94,7 +105,7 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   pl->NC = (p->T + C - 1) / C;
   pl->mt = p->dtype == GDN_DTYPE_BF16 ? 2 : 4;
   // exclusive readouts on bf16 operands carry the decayed q.k tile as hi + lo parts
-  pl->plo = p->dtype == GDN_DTYPE_BF16 && (p->options & (GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE)) != 0;
+  pl->plo = p->dtype == GDN_DTYPE_BF16 && excl;
   // (and the entry state's low parts: their exchange fits 16-column tiles only)
   if (pl->plo) {
     if (pl->NT == 2) return GDN_ERR_UNSUPPORTED;
@@ -176,6 +187,7 @@ bool capturing(hipStream_t stream) {
 
 template <typename MT>
 prep_fn prep_for(int dk, int C) {
+  if (C == 128) return dk == 64 ? launch_prep_wide<MT, 64> : launch_prep_wide<MT, 128>;
   if (dk == 64) return C == 32 ? launch_prep<MT, 64, 32> : launch_prep<MT, 64, 64>;
   return C == 32 ? launch_prep<MT, 128, 32> : launch_prep<MT, 128, 64>;
 }
@@ -201,9 +213,19 @@ chain_fn column_chain_for3(int NT, int dirs, int prec) {
   return prec == 1 ? column_chain_for4<DK, C, 1>(NT, dirs) : column_chain_for4<DK, C, 0>(NT, dirs);
 }
 
-// bf16 operands: the column-owning chain; fp32 operands: the two-role chain
+// bf16 operands: the column-owning chain; fp32 operands, and 128-token
+// chunks of either type: the two-role chain
 template <typename MT>
 chain_fn chain_for(int dk, int C, int NT, int dirs, int prec) {
+  if (C == 128) {
+    if (dk == 64) return chain_for3<MT, 64, 128>(NT, dirs);
+    if constexpr (sizeof(MT) == 4) {
+      if (NT != 1) return nullptr;
+      return dirs == 2 ? launch_chain<float, 128, 128, 1, true> : launch_chain<float, 128, 128, 1, false>;
+    } else {
+      return chain_for3<MT, 128, 128>(NT, dirs);
+    }
+  }
   if constexpr (sizeof(MT) == 2) {
     if (dk == 64) return C == 32 ? column_chain_for3<64, 32>(NT, dirs, prec) : column_chain_for3<64, 64>(NT, dirs, prec);
     return C == 32 ? column_chain_for3<128, 32>(NT, dirs, prec) : column_chain_for3<128, 64>(NT, dirs, prec);
@@ -287,11 +309,13 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   a.B = B; a.T = T; a.H = H; a.NC = pl.NC; a.dv = (int)dv;
   a.fwd_on = pl.fwd_on; a.rev_on = pl.rev_on; a.dirs = pl.dirs;
   const bool bf = p->dtype == GDN_DTYPE_BF16;
-  // bidirectional combine: fp32 operands recognise an unwritten partial by
-  // the preparation kernel's fill of `out`; bf16 operands by per-chunk flags
-  // that the preparation kernel clears
-  a.zero_out = pl.dirs == 2 && !bf;
-  if (pl.dirs == 2 && bf && need_ws) a.part_flags = reinterpret_cast<unsigned*>(ws + pl.ws.pfl);
+  // bidirectional combine: the two-role chain (fp32 operands, 128-token
+  // chunks) recognises an unwritten partial by the preparation kernel's fill
+  // of `out`; the column chain by per-chunk flags that the preparation kernel
+  // clears
+  const bool column = bf && pl.C != 128;
+  a.zero_out = pl.dirs == 2 && !column;
+  if (pl.dirs == 2 && column && need_ws) a.part_flags = reinterpret_cast<unsigned*>(ws + pl.ws.pfl);
   if (pl.plo && need_ws) a.pq_lo = ws + pl.ws.pql;
   a.erase = (p->options & GDN_OPT_NO_ERASE) ? 0 : 1;
   a.excl_fwd = (p->options & GDN_OPT_EXCLUSIVE_FORWARD) ? 1 : 0;

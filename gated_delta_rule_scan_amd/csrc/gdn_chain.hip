@@ -105,8 +105,9 @@ struct VTile {
 template <typename MT, int DK, int C, int NT>
 struct StageC {
   typedef typename Mma<MT>::frag frag;
-  frag kf[DK / 32];
-  frag tf[C / 32];
+  static constexpr int RPW = C > 64 ? C / 64 : 1;  // token row tiles per wave
+  frag kf[RPW][DK / 32];
+  frag tf[RPW][C / 32];
   f32x4 cv[VTile<MT, 16 * NT, C>::NVI];
   uint32_t rdy;
 };
@@ -116,8 +117,9 @@ struct StageC {
 template <typename MT, int DK, int C, int NT>
 struct StageR {
   typedef typename Mma<MT>::frag frag;
-  frag qf[DK / 32];
-  frag pf[C / 32];
+  static constexpr int RPW = C > 64 ? C / 64 : 1;
+  frag qf[RPW][DK / 32];
+  frag pf[RPW][C / 32];
   f32x4 pq[(C / 16 * NT + 3) / 4];
 };
 
@@ -239,6 +241,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   using VT = VTile<MT, DT, C>;
   constexpr int RT = C / 16;              // token row tiles per chunk
   constexpr int NWC = 4;                        // chain waves; readout waves follow them
+  constexpr int RPW = RT > NWC ? RT / NWC : 1;  // token row tiles per wave (wave wr: tiles wr + NWC r)
   constexpr int UPW = (RT * NT + NWC - 1) / NWC;  // chunk-output tiles per wave
   constexpr int SRT = DK / 16;                    // state row tiles (dk)
   constexpr int SUPW = SRT * NT / NWC;            // state tiles per chain wave
@@ -246,7 +249,8 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   constexpr bool ALL_UNITS = (RT * NT) % NWC == 0;
   static_assert(ChainWaves<C, NT>::value == 2 * NWC, "one readout wave per chain wave");
   static_assert(SRT % NWC == 0 || NWC % SRT == 0, "state tiles split evenly over the waves");
-  static_assert(NWC % RT == 0, "every wave keeps one token row tile");
+  static_assert(NWC % RT == 0 || RT % NWC == 0, "every wave keeps the same number of token row tiles");
+  static_assert(RPW == StageC<MT, DK, C, NT>::RPW && RPW == StageR<MT, DK, C, NT>::RPW, "stage layout");
 
   __shared__ __align__(16) MT smem[SM::per_group];
   __shared__ __align__(16) unsigned char stg[2][SM::ST_BYTES];
@@ -275,7 +279,8 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   const int l16 = lane & 15, g4 = lane >> 4;
   const int wr = w & (NWC - 1);  // place among the chain waves (readout wave w mirrors chain wave w - NWC)
   const bool reader = w >= NWC;  // readout waves: Z = Q S^T and the chunk outputs
-  const int rt = wr % RT;
+  // row tile of output unit j (u = wr + NWC j): tile wr % RT + NWC rj(j)
+  auto rj = [](int j) { return RT > NWC ? j % RPW : 0; };
 
   constexpr bool KROW = SM::KROW;
   constexpr int KP = SM::KP;
@@ -299,42 +304,54 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   char* obase = reinterpret_cast<char*>(a.out) + (size_t)((b * T * H + h) * dv + dv0) * 4;
   const char* trib = static_cast<const char*>(a.tri) + (size_t)chain * NC * C * C * ES;
   const char* pqkb = static_cast<const char*>(a.pqk) + (size_t)chain * NC * C * C * ES;
-  const int kq_row = 16 * rt + l16;
-  const uint32_t kq_off = kq_row * HDB + 8 * g4 * ES;
-  const uint32_t tri_off = (kq_row * C + 8 * g4) * ES;
-  const int o_row0 = 16 * rt + 4 * g4;
-  const int kcd = rt / 2;  // k-chunk holding this row tile's diagonal
+  int kq_row[RPW], o_row0[RPW];
+  uint32_t kq_off[RPW], tri_off[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int rt = wr % RT + NWC * r;
+    kq_row[r] = 16 * rt + l16;
+    kq_off[r] = kq_row[r] * HDB + 8 * g4 * ES;
+    tri_off[r] = (kq_row[r] * C + 8 * g4) * ES;
+    o_row0[r] = 16 * rt + 4 * g4;
+  }
   // triangle fragments: the k-chunks of this row tile that hold no element
   // of this direction's triangle are read past the buffer extent (zeros, see
   // the resources below); the diagonal k-chunk is masked (Tinv strictly, P
   // with its diagonal -- the self terms -- unless this direction reads
   // before the token's own write, which is exactly P without its diagonal)
   const bool self = !(rev ? a.excl_rev : a.excl_fwd);
-  FragMask<MT> tmask[C / 32], pmask[C / 32];
+  FragMask<MT> tmask[RPW][C / 32], pmask[RPW][C / 32];
 #pragma unroll
-  for (int kc = 0; kc < C / 32; ++kc) {
-    tmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, false, kc == kcd);
-    pmask[kc].make(kq_row, 32 * kc + 8 * g4, rev, self, kc == kcd);
-  }
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int kc = 0; kc < C / 32; ++kc) {
+      const int kcd = (wr % RT + NWC * r) / 2;  // k-chunk holding the row tile's diagonal
+      tmask[r][kc].make(kq_row[r], 32 * kc + 8 * g4, rev, false, kc == kcd);
+      pmask[r][kc].make(kq_row[r], 32 * kc + 8 * g4, rev, self, kc == kcd);
+    }
   // readout offset of unit column tile 0 (transposed tile: token kq_row, four
   // columns from 4 g4)
-  const uint32_t out_off = kq_row * HOB + 16 * g4;
+  uint32_t out_off[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) out_off[r] = kq_row[r] * HOB + 16 * g4;
   // bf16 operands: the self term's remainder enters as a diagonal fragment;
   // in k-chunk kc this lane (row kq_row of P) holds element `kq_row - 32 kc -
   // 8 g4` of it when that lies in 0..7 (only ever in the k-chunk of the diagonal)
-  FragMask<MT> diag_only[C / 32];
+  FragMask<MT> diag_only[RPW][C / 32];
 #pragma unroll
-  for (int kc = 0; kc < C / 32; ++kc) {
+  for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int i = 0; i < FragMask<MT>::NW; ++i) diag_only[kc].m[i] = 0u;
-    const int e0 = self ? kq_row - 32 * kc - 8 * g4 : -1;
+    for (int kc = 0; kc < C / 32; ++kc) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e == e0) {
-        if (sizeof(MT) == 2) diag_only[kc].m[e / 2] |= 0xffffu << (16 * (e % 2));
-        else diag_only[kc].m[e] = 0xffffffffu;
-      }
-  }
+      for (int i = 0; i < FragMask<MT>::NW; ++i) diag_only[r][kc].m[i] = 0u;
+      const int e0 = self ? kq_row[r] - 32 * kc - 8 * g4 : -1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e == e0) {
+          if (sizeof(MT) == 2) diag_only[r][kc].m[e / 2] |= 0xffffu << (16 * (e % 2));
+          else diag_only[r][kc].m[e] = 0xffffffffu;
+        }
+    }
   // group-shared operand loads: which source this wave reads, per-lane offsets
   // and where each piece lands in the staging buffer
   const char* cbase;
@@ -357,7 +374,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 #pragma unroll
   for (int n = 0; n < VT::NVI; ++n) {
     if (cw == 0) {
-      const int idx = lane % C;
+      const int idx = (lane + 64 * n) % C;
       c_off[n] = idx * 16;
       c_lds[n] = SM::ST_SC + idx * 16;
     } else if (cw == 1) {
@@ -383,13 +400,15 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   const rsrc_t rc = make_rsrc(cbase, cbytes);
   const rsrc_t ro = make_rsrc(obase, (uint32_t)(T - 1) * HOB + DT * 4);
   const uint32_t tri_bytes = (uint32_t)NC * (C * C * ES);
-  rsrc_t rtk[C / 32], rpk[C / 32];  // triangle k-chunks this row tile never needs: zeros
+  rsrc_t rtk[RPW][C / 32], rpk[RPW][C / 32];  // triangle k-chunks a row tile never needs: zeros
 #pragma unroll
-  for (int kc = 0; kc < C / 32; ++kc) {
-    const bool need = tri_needed(rev, kc, rt);
-    rtk[kc] = make_rsrc(trib, need ? tri_bytes : 0u);
-    rpk[kc] = make_rsrc(pqkb, need ? tri_bytes : 0u);
-  }
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int kc = 0; kc < C / 32; ++kc) {
+      const bool need = tri_needed(rev, kc, wr % RT + NWC * r);
+      rtk[r][kc] = make_rsrc(trib, need ? tri_bytes : 0u);
+      rpk[r][kc] = make_rsrc(pqkb, need ? tri_bytes : 0u);
+    }
   // the chunks' ready flags, when the preparation kernel runs concurrently
   // (a.ready set; 0 = ready): a chunk's prepared operands are read only once
   // its flag is 0.  Without a.ready the flags read as 0 (empty extent).
@@ -412,10 +431,13 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   auto out_at = [&](int c) { return (uint32_t)c * (C * HOB); };
 
   // ---- loaders (issued a step ahead) ----
-  auto load_rows = [&](frag* dst, const rsrc_t r, int c) {
-    const uint32_t o = kq_off + kq_at(c);
+  auto load_rows = [&](frag (*dst)[DK / 32], const rsrc_t rs, int c) {
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) dst[ks] = bload_frag<MT>(r, o + 32 * ks * ES);
+    for (int r = 0; r < RPW; ++r) {
+      const uint32_t o = kq_off[r] + kq_at(c);
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) dst[r][ks] = bload_frag<MT>(rs, o + 32 * ks * ES);
+    }
   };
   auto load_coop = [&](auto& f, int c) {
     const uint32_t o = (uint32_t)c * cstride;
@@ -423,14 +445,20 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     for (int n = 0; n < VT::NVI; ++n) f.cv[n] = bload16(rc, c_off[n] + o);
   };
   auto load_tf = [&](auto& f, int c) {  // chain waves
-    const uint32_t o = tri_off + (uint32_t)c * (C * C * ES);
 #pragma unroll
-    for (int kc = 0; kc < C / 32; ++kc) f.tf[kc] = bload_frag<MT>(rtk[kc], o + 32 * kc * ES);
+    for (int r = 0; r < RPW; ++r) {
+      const uint32_t o = tri_off[r] + (uint32_t)c * (C * C * ES);
+#pragma unroll
+      for (int kc = 0; kc < C / 32; ++kc) f.tf[r][kc] = bload_frag<MT>(rtk[r][kc], o + 32 * kc * ES);
+    }
   };
   auto load_pf = [&](auto& f, int c) {  // readout waves
-    const uint32_t o = tri_off + (uint32_t)c * (C * C * ES);
 #pragma unroll
-    for (int kc = 0; kc < C / 32; ++kc) f.pf[kc] = bload_frag<MT>(rpk[kc], o + 32 * kc * ES);
+    for (int r = 0; r < RPW; ++r) {
+      const uint32_t o = tri_off[r] + (uint32_t)c * (C * C * ES);
+#pragma unroll
+      for (int kc = 0; kc < C / 32; ++kc) f.pf[r][kc] = bload_frag<MT>(rpk[r][kc], o + 32 * kc * ES);
+    }
   };
   auto stash = [&](const auto& f, int buf) {  // group-shared pieces of a loaded stage -> LDS
 #pragma unroll
@@ -470,26 +498,30 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   for (int j = 0; j < UPW; ++j) Zp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto readout = [&](const auto& sp, const int s_prev, const bool on) {
     const unsigned char* sg = stg[s_prev & 1];
-    frag pdiag;  // this lane's self-term remainder in every element (bf16 operands)
+    frag pdiag[RPW];  // this lane's self-term remainder in every element (bf16 operands)
     if constexpr (SPLIT) {
-      const bf16 r = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + 16 + kq_row * 4));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pdiag[e] = r;
+      for (int r = 0; r < RPW; ++r) {
+        const bf16 x = (bf16)(*reinterpret_cast<const float*>(sg + SM::ST_PD + 16 + kq_row[r] * 4));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pdiag[r][e] = x;
+      }
     }
     const int c = chunk_at(s_prev);
     const rsrc_t rs = on ? ro : rnone;
-    const uint32_t oo = out_off + out_at(c);
-    const float zs = *reinterpret_cast<const float*>(sg + SM::ST_SC + kq_row * 16 + 8);  // e^g rq of the token
+    float zs[RPW];  // e^g rq of the token
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) zs[r] = *reinterpret_cast<const float*>(sg + SM::ST_SC + kq_row[r] * 16 + 8);
     const bool add = BI && !first_visit(s_prev);
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
       const int u = wr + NWC * j;
       if (ALL_UNITS || u < RT * NT) {
-        const int ct = u / RT;
-        f32x4 acc = Zp[j] * zs;
+        const int ct = u / RT, r = rj(j);
+        f32x4 acc = Zp[j] * zs[r];
 #pragma unroll
         for (int kc = 0; kc < C / 32; ++kc) {
-          const frag pf = pmask[kc].apply(sp.pf[kc]);
+          const frag pf = pmask[r][kc].apply(sp.pf[r][kc]);
           const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
           const frag vh = M::load(VnT + o);
           acc = M::mma(vh, pf, acc);
@@ -497,12 +529,12 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
             acc = M::mma(M::load(VnL + o), pf, acc);
             // self-term remainder (pqk holds the rounded self term): a
             // diagonal product with the hi part of Vnew
-            acc = M::mma(vh, diag_only[kc].apply(pdiag), acc);
+            acc = M::mma(vh, diag_only[r][kc].apply(pdiag[r]), acc);
           }
         }
         if (add) acc += sp.pq[j];
         else if (BI) acc = canonical_nans(acc);  // a first visit: never the fill pattern
-        bstore16(rs, oo + ct * 64, acc);
+        bstore16(rs, out_off[r] + out_at(c) + ct * 64, acc);
       }
     }
   };
@@ -525,21 +557,26 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     const int buf = s & 1;
     const unsigned char* sg = stg[buf];
     f32x4 X[UPW];
-    float4 sc[4];
+    float4 sc[RPW][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = *reinterpret_cast<const float4*>(sg + SM::ST_SC + (o_row0 + i) * 16);
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[r][i] = *reinterpret_cast<const float4*>(sg + SM::ST_SC + (o_row0[r] + i) * 16);
 
     // [A] k tile into LDS; Y = K S^T; X
     if (wr < RT) {
-      if constexpr (KROW) {
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks)
-          *reinterpret_cast<frag*>(KT + kq_row * KP + 32 * ks + 8 * g4) = st.kf[ks];
-      } else {
+      for (int r = 0; r < RPW; ++r) {
+        if constexpr (KROW) {
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks)
+          for (int ks = 0; ks < DK / 32; ++ks)
+            *reinterpret_cast<frag*>(KT + kq_row[r] * KP + 32 * ks + 8 * g4) = st.kf[r][ks];
+        } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) KT[(32 * ks + 8 * g4 + e) * TP + kq_row] = (MT)M::get(st.kf[ks], e);
+          for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) KT[(32 * ks + 8 * g4 + e) * TP + kq_row[r]] = (MT)M::get(st.kf[r][ks], e);
+        }
       }
     }
     ensure_ready(nx.rdy, cn);  // before any read of chunk cn's prepared operands
@@ -554,14 +591,15 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     for (int j = 0; j < UPW; ++j) {
       const int u = wr + NWC * j;
       if (ALL_UNITS || u < RT * NT) {
-        const int ct = u / RT;
+        const int ct = u / RT, r = rj(j);
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) y = M::mma(st.kf[ks], M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4), y);
+        for (int ks = 0; ks < DK / 32; ++ks)
+          y = M::mma(st.kf[r][ks], M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4), y);
         // raw values v[o_row0 + i][16 ct + l16], i = 0..3
         f32x4 vv;
         if constexpr (KROW) {
-          const v4s t4 = lds_read_tr16(sg + SM::ST_V + ((o_row0 + (l16 >> 2)) * DT + 16 * ct + 4 * (l16 & 3)) * 2);
+          const v4s t4 = lds_read_tr16(sg + SM::ST_V + ((o_row0[r] + (l16 >> 2)) * DT + 16 * ct + 4 * (l16 & 3)) * 2);
           bf16x4 b4;
           __builtin_memcpy(&b4, &t4, 8);
 #pragma unroll
@@ -569,12 +607,12 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            vv[i] = *reinterpret_cast<const float*>(sg + SM::ST_V + ((o_row0 + i) * DT + 16 * ct + l16) * 4);
+            vv[i] = *reinterpret_cast<const float*>(sg + SM::ST_V + ((o_row0[r] + i) * DT + 16 * ct + l16) * 4);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[j][i] = sc[i].x * (vv[i] - sc[i].y * y[i]);
+        for (int i = 0; i < 4; ++i) X[j][i] = sc[r][i].x * (vv[i] - sc[r][i].y * y[i]);
         if (poison) X[j] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-        M::store4(XT + (16 * ct + l16) * TP + o_row0, X[j][0], X[j][1], X[j][2], X[j][3]);
+        M::store4(XT + (16 * ct + l16) * TP + o_row0[r], X[j][0], X[j][1], X[j][2], X[j][3]);
       }
     }
     __syncthreads();
@@ -585,15 +623,15 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     for (int j = 0; j < UPW; ++j) {
       const int u = wr + NWC * j;
       if (ALL_UNITS || u < RT * NT) {
-        const int ct = u / RT;
+        const int ct = u / RT, r = rj(j);
         f32x4 acc = X[j];
 #pragma unroll
         for (int kc = 0; kc < C / 32; ++kc)
-          acc = M::mma(tmask[kc].apply(st.tf[kc]), M::load(XT + (16 * ct + l16) * TP + 32 * kc + 8 * g4), acc);
-        const int o = (16 * ct + l16) * TP + o_row0;
+          acc = M::mma(tmask[r][kc].apply(st.tf[r][kc]), M::load(XT + (16 * ct + l16) * TP + 32 * kc + 8 * g4), acc);
+        const int o = (16 * ct + l16) * TP + o_row0[r];
         f32x4 vs;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vs[i] = sc[i].w * acc[i];
+        for (int i = 0; i < 4; ++i) vs[i] = sc[r][i].w * acc[i];
         if constexpr (SPLIT) {
           store_split4(VnT + o, VnL + o, acc);
           store_split4(VsT + o, VsL + o, vs);
@@ -672,11 +710,11 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     for (int j = 0; j < UPW; ++j) {
       const int u = wr + NWC * j;
       if (ALL_UNITS || u < RT * NT) {
-        const int ct = u / RT;
+        const int ct = u / RT, r = rj(j);
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
-          z = M::mma(M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4), st.qf[ks], z);
+          z = M::mma(M::load(Sb + (16 * ct + l16) * SP + 32 * ks + 8 * g4), st.qf[r][ks], z);
         Zp[j] = z;
       }
     }
@@ -689,9 +727,8 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     if constexpr (BI) {
       const bool want = s + 1 < NC && !first_visit(s + 1);
       const rsrc_t rp = want ? ro : rnone;
-      const uint32_t op = out_off + out_at(cn);
 #pragma unroll
-      for (int j = 0; j < UPW; ++j) nx.pq[j] = bload16(rp, op + ((wr + NWC * j) / RT) * 64);
+      for (int j = 0; j < UPW; ++j) nx.pq[j] = bload16(rp, out_off[rj(j)] + out_at(cn) + ((wr + NWC * j) / RT) * 64);
     }
     __syncthreads();
 
@@ -705,7 +742,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           // first test outside any loop: a loop that reloads the tested value
           // makes the compiler wait for every load in flight at its head
           if (__any(any_unwritten(st.pq[j])) && !pq_gave_up) {
-            const uint32_t off = out_off + out_at(c) + ((wr + NWC * j) / RT) * 64;
+            const uint32_t off = out_off[rj(j)] + out_at(c) + ((wr + NWC * j) / RT) * 64;
             f32x4 q = st.pq[j];
             int n = 0;
             for (; n < kPollLimit; ++n) {
@@ -754,7 +791,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
       if constexpr (BI) {  // the partial of step 0 (a single-chunk scan's reverse visit)
         const rsrc_t rp = first_visit(0) ? rnone : ro;
 #pragma unroll
-        for (int j = 0; j < UPW; ++j) sA.pq[j] = bload16(rp, out_off + out_at(c0) + ((wr + NWC * j) / RT) * 64);
+        for (int j = 0; j < UPW; ++j) sA.pq[j] = bload16(rp, out_off[rj(j)] + out_at(c0) + ((wr + NWC * j) / RT) * 64);
       }
       int s = 0;
       for (; s + 1 < NC; s += 2) {
@@ -800,5 +837,10 @@ GDN_INST_CHAIN_N(bf16, 64, 32)
 GDN_INST_CHAIN_N(bf16, 64, 64)
 GDN_INST_CHAIN_N(bf16, 128, 32)
 GDN_INST_CHAIN_N(bf16, 128, 64)
+// 128-token chunks: fp32 operands with d = 128 fit 16-column tiles only
+GDN_INST_CHAIN_N(float, 64, 128)
+GDN_INST_CHAIN_D(float, 128, 128, 1)
+GDN_INST_CHAIN_N(bf16, 64, 128)
+GDN_INST_CHAIN_N(bf16, 128, 128)
 
 }  // namespace gdn

@@ -19,6 +19,11 @@ namespace gdn {
 template <typename MT, int DK, int C>
 hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes* query);
 
+// The same for 128-token chunks (C = 128): one 512-thread workgroup per
+// (chunk, batch*head), the inverse blocked over fp32 tiles in LDS.
+template <typename MT, int DK>
+hipError_t launch_prep_wide(const ScanArgs& a, hipStream_t stream, hipFuncAttributes* query);
+
 // Marks the n chunk-ready flags pending (1), before a concurrent preparation
 // pass; the preparation kernel stores 0 once a chunk is ready.
 hipError_t launch_clear_ready(unsigned* ready, int64_t n, hipStream_t stream);

@@ -312,3 +312,32 @@ def test_epilogue_arguments_are_validated_before_launch():
     assert _call(with_epi(eps=0.0), a) == gdn.GDN_ERR_HIP
     # an invalid epilogue also makes the workspace query fail
     assert gdn.gdn_workspace_bytes(with_epi(w=None), gdn.GDN_DIR_FORWARD) == 0
+
+
+def test_chunk128_is_accepted_with_its_limits():
+    """128-token chunks: accepted for both operand types in every direction;
+    the workspace holds C x C triangles per chunk (3 chunks of 300 tokens);
+    bf16 exclusive readouts and the bf16 epilogue (whose low parts only the
+    32/64-token chain carries) and 32-wide fp32 tiles at d = 128 (their
+    staging exceeds the compute unit's LDS) are unsupported, rejected before
+    anything is enqueued."""
+    for dtype in (gdn.GDN_DTYPE_BF16, gdn.GDN_DTYPE_F32):
+        for d in (gdn.GDN_DIR_FORWARD, gdn.GDN_DIR_REVERSE, gdn.GDN_DIR_BIDIRECTIONAL):
+            assert gdn.gdn_workspace_bytes(_prob(chunk=128, dtype=dtype), d) > 0
+    es = 2
+    assert gdn.gdn_workspace_bytes(_prob(chunk=128), gdn.GDN_DIR_FORWARD) >= 2 * 3 * 2 * 128 * 128 * es
+    for opt in (gdn.GDN_OPT_EXCLUSIVE_FORWARD, gdn.GDN_OPT_EXCLUSIVE_REVERSE):
+        p = _prob(chunk=128)
+        p.options = opt
+        assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_BIDIRECTIONAL) == 0
+        p = _prob(chunk=128, dtype=gdn.GDN_DTYPE_F32)
+        p.options = opt
+        assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_BIDIRECTIONAL) > 0
+    for dtype, want in ((gdn.GDN_DTYPE_BF16, False), (gdn.GDN_DTYPE_F32, True)):
+        p = _prob(chunk=128, dtype=dtype)
+        p.gate, p.norm_weight, p.norm_eps = 1 << 40, 1 << 41, 1e-6  # host-side validation only
+        assert (gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_FORWARD) > 0) == want
+    assert gdn.gdn_workspace_bytes(_prob(chunk=128, dtype=gdn.GDN_DTYPE_F32, dv_tile=32), gdn.GDN_DIR_FORWARD) == 0
+    assert gdn.gdn_workspace_bytes(_prob(chunk=128, dtype=gdn.GDN_DTYPE_F32, dk=64, dv=64, dv_tile=32),
+                                   gdn.GDN_DIR_FORWARD) > 0
+    assert gdn.gdn_workspace_bytes(_prob(chunk=128, dv_tile=32), gdn.GDN_DIR_FORWARD) > 0
