@@ -76,6 +76,35 @@ def test_full_size_sampled_heads(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ["bidir480", "causal720", "bidir720"])
+def test_full_size_every_head(name):
+    """Every (batch, head) chain of the full-size workload against the oracle
+    (run over all chains on the host's threads), so the workgroup numbering
+    that maps ids to (chain, value tile, direction) across the eight XCDs is
+    covered for every head, not only the sampled ones."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+
+    w = synth.WORKLOADS[name]
+    print(f"\n[{name} every head] generating {w}", flush=True)
+    x = synth.generate(w)
+    d = {k: to_torch(v) for k, v in x.items()}
+    out, s_out = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction)
+    torch.cuda.synchronize()
+    got, got_s = out.cpu().numpy(), s_out.cpu().numpy()
+    del d, out, s_out
+    torch.cuda.empty_cache()
+    print(f"[{name} every head] oracle over {w.B * w.H} chains x {w.dirs} direction(s)", flush=True)
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], w.direction)
+    e_o = check(got, ref, TOL[w.dtype], f"{name} out")
+    e_s = check(got_s, ref_s, TOL[w.dtype], f"{name} state")
+    # and per chain: no head may hide behind the others' RMS
+    worst = max(rel_err(got[b, :, h], ref[b, :, h])[0] for b in range(w.B) for h in range(w.H))
+    assert worst <= TOL[w.dtype], f"{name}: worst chain {worst:.3e} x its own RMS"
+    print(f"[{name} every head] max|err|/RMS: out {e_o:.3e}  state {e_s:.3e}  worst chain {worst:.3e}", flush=True)
+
+
 def test_full_size_bidir480_raw_qk():
     """The 480p bidirectional workload (B2 H16 T32760 d128 bf16) with
     un-normalised q and k (per-row scales from 1e-3 to 1e3, rows at the norm
