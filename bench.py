@@ -66,9 +66,15 @@ def kernel_bytes(w, xs: int) -> dict:
             "path": path_bytes(w, xs)}
 
 
-def chain_kernel_name(dtype: str) -> str:
-    """bf16 operands run the column-owning chain, fp32 operands the two-role one."""
-    return "column_chain_kernel" if dtype == "bf16" else "chain_kernel"
+def chain_kernel_name(dtype: str, chunk: int = 0) -> str:
+    """bf16 operands run the column-owning chain, fp32 operands and 128-token
+    chunks the two-role one."""
+    return "column_chain_kernel" if dtype == "bf16" and chunk != 128 else "chain_kernel"
+
+
+def prep_kernel_name(chunk: int = 0) -> str:
+    """128-token chunks have a preparation kernel of their own."""
+    return "chunk_prep_wide_kernel" if chunk == 128 else "chunk_prep_kernel"
 
 
 def host_cores():
@@ -125,6 +131,7 @@ KERNEL_SOURCES = {
     "chain_kernel": ["gdn_chain.hip", "gdn_common.h"],
     "column_chain_kernel": ["gdn_colchain.hip", "gdn_common.h"],
     "chunk_prep_kernel": ["gdn_prep.hip", "gdn_common.h"],
+    "chunk_prep_wide_kernel": ["gdn_prep_wide.hip", "gdn_common.h"],
     "vda_frame_kernel": ["gdn_vda.hip", "gdn_common.h"],
     "vda_chain_bf16_kernel": ["gdn_vda.hip", "gdn_common.h"],
     "vda_readout_kernel": ["gdn_vda.hip", "gdn_common.h"],
@@ -470,7 +477,7 @@ def main() -> int:
     kb = kernel_bytes(w, xs)
     kt = {"prep": prep_ms, "chain": chain_ms}
     dom = max(kt, key=kt.get)
-    dom_name = chain_kernel_name(w.dtype) if dom == "chain" else "chunk_prep_kernel"
+    dom_name = chain_kernel_name(w.dtype, args.chunk) if dom == "chain" else prep_kernel_name(args.chunk)
     # the dominant kernel's roofline: the chain moves every boundary tensor but
     # the gates, so the path's boundary bytes are its algorithmic bytes
     dom_bytes = kb["path"] if dom == "chain" else kb["prep"]
@@ -630,7 +637,7 @@ def run_stream(args, w) -> int:
     fb = (kb["path"] - sb * (2 if w.state_std > 0 else 1)) / NF + 2 * sb
     kt = {"prep": prep_ms, "chain": chain_ms}
     dom = max(kt, key=kt.get)
-    dom_name = chain_kernel_name(w.dtype) if dom == "chain" else "chunk_prep_kernel"
+    dom_name = chain_kernel_name(w.dtype, args.chunk) if dom == "chain" else prep_kernel_name(args.chunk)
     dom_bytes = fb if dom == "chain" else kb["prep"] / NF
     achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
     res = {
