@@ -139,14 +139,29 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   // Workgroups are numbered in the order the state chain consumes the
-  // chunks (a bidirectional scan takes both ends first), and each (batch,
-  // head) sequence's chunks go to the XCD its state-chain workgroups run on
-  // (consecutive ids are dealt round-robin over the eight XCDs).
+  // chunks (a bidirectional scan takes both ends first); consecutive ids are
+  // dealt round-robin over the eight XCDs.  Run before the chain, all heads of
+  // one (batch, chunk) go to one XCD: a 128-byte line of gates ([dirs, B, T,
+  // H] layout) holds every head of a few tokens, so the line is fetched into
+  // that XCD's L2 once (dealt by sequence, every XCD fetched every gate line:
+  // eight times the gates' bytes, 0.12 of the 0.55 GB the pass reads at the
+  // 480p bidirectional shape).  Run beside the chain, each sequence's chunks
+  // go to the XCD its state-chain workgroups run on.
   const int nbh = (int)(a.B * a.H), G = (nbh + 7) / 8;
   const int id = blockIdx.x;
-  const int64_t bh = (int64_t)((id >> 3) % G) * 8 + (id & 7);
-  const int order = (id >> 3) / G;  // position in the consumption order
   const int NCi = (int)a.NC;
+  int64_t bh;
+  int order;  // position in the consumption order
+  if (a.ready) {
+    bh = (int64_t)((id >> 3) % G) * 8 + (id & 7);
+    order = (id >> 3) / G;
+  } else {
+    const int Hi = (int)a.H, Bi = (int)a.B, p = id >> 3;
+    const int gi = (p / Hi) * 8 + (id & 7);  // (position, batch) group
+    order = gi / Bi;
+    bh = (int64_t)(gi % Bi) * Hi + p % Hi;
+  }
+  if (order >= ((a.fwd_on && a.rev_on) ? 2 * ((NCi + 1) / 2) : NCi)) return;
   int64_t c;
   if (a.fwd_on && a.rev_on) {
     const int J = (NCi + 1) / 2;  // even positions take chunks [0, J), odd ones [J, NC) from the end
@@ -623,7 +638,8 @@ hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes*
   if (query) return hipFuncGetAttributes(query, fn);
   const int64_t G = (a.B * a.H + 7) / 8;
   const int64_t slots = (a.fwd_on && a.rev_on) ? 2 * ((a.NC + 1) / 2) : a.NC;
-  const int64_t nblocks = slots * G * 8;  // one per chunk id
+  // one per chunk id (numbering: see the kernel)
+  const int64_t nblocks = a.ready ? slots * G * 8 : (slots * a.B + 7) / 8 * 8 * a.H;
   const dim3 grid((unsigned)nblocks);
   if (plo) hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, true>), grid, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, false>), grid, dim3(256), 0, stream, a);
