@@ -158,3 +158,26 @@ def test_chunk128_full_size_sampled_heads(name):
     print(f"[{name} C=128] max|err|/RMS: out {e_o:.3e}  state {e_s:.3e}", flush=True)
     del d, out, s_out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("exclusive", ["none", "both"])
+def test_chunk128_readout_epilogue_fp32(exclusive):
+    """The readout epilogue on fp32 operands at 128-token chunks, inclusive and
+    exclusive readouts: against the oracle's scan followed by the oracle's
+    epilogue formula (bf16 operands reject this combination)."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+
+    w = _case("f32", "bi", T=300, H=2, dk=64, dv=64, state_std=0.05, seed=41)
+    x = synth.generate(w)
+    e = synth.generate_epilogue(w)
+    ref, _ = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi", exclusive=exclusive)
+    ref_y = oracle.readout_epilogue(ref, e["gate"], e["norm_weight"], 1e-6)
+    d = {k: to_torch(v) for k, v in x.items()}
+    y, _ = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], "bi", chunk=128,
+                       exclusive=exclusive, gate=to_torch(e["gate"]), norm_weight=to_torch(e["norm_weight"]),
+                       norm_eps=1e-6)
+    torch.cuda.synchronize()
+    r = check(y.cpu().numpy(), ref_y, TOL["f32"], f"epilogue C=128 exclusive={exclusive}")
+    print(f"\nepilogue fp32 C=128 exclusive={exclusive}: {r:.2e} x RMS", flush=True)
