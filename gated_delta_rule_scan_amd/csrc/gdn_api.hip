@@ -36,18 +36,7 @@ struct Plan {
 
 bool supported_dim(int64_t d) { return d == 64 || d == 128; }
 
-// Compute units of the current device (cached per device; 256 on MI355X).
-int compute_units() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
+int compute_units() { return device_compute_units(); }
 
 int pick_tiles(int64_t nbh, int64_t dv, int dirs) {
   // A 32-wide value tile amortises the per-step fixed work of a chain (k
@@ -239,6 +228,22 @@ chain_fn chain_for(int dk, int C, int NT, int dirs, int prec) {
 }  // namespace gdn
 
 using namespace gdn;
+
+namespace gdn {
+
+int device_compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace gdn
 
 extern "C" size_t gdn_workspace_bytes(const gdn_problem_t* p, int32_t direction) {
   Plan pl;

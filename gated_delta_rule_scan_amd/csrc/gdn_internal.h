@@ -24,6 +24,10 @@ hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes*
 template <typename MT, int DK>
 hipError_t launch_prep_wide(const ScanArgs& a, hipStream_t stream, hipFuncAttributes* query);
 
+// Compute units of the current device (queried once per device; 256 on
+// MI355X, also when the query fails).
+int device_compute_units();
+
 // Marks the n chunk-ready flags pending (1), before a concurrent preparation
 // pass; the preparation kernel stores 0 once a chunk is ready.
 hipError_t launch_clear_ready(unsigned* ready, int64_t n, hipStream_t stream);

@@ -494,28 +494,19 @@ __global__ __launch_bounds__(512) void chunk_prep_wide_kernel(ScanArgs a, int ni
   }
 }
 
-// Compute units of the current device (cached per device; 256 on MI355X).
-int resident_units() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <typename MT, int DK>
 hipError_t launch_prep_wide(const ScanArgs& a, hipStream_t stream, hipFuncAttributes* query) {
   const void* fn = reinterpret_cast<const void*>(&chunk_prep_wide_kernel<MT, DK>);
   if (query) return hipFuncGetAttributes(query, fn);
   const int64_t G = (a.B * a.H + 7) / 8;
   const int64_t nitems = a.NC * G * 8;
-  // one resident workgroup per compute unit (the two tiles take most of its
-  // LDS), a multiple of eight so that an item keeps its XCD
-  const int64_t ncu = (resident_units() + 7) / 8 * 8;
+  // One resident workgroup per compute unit (the two tiles take most of its
+  // LDS), a multiple of eight so that an item keeps its XCD.  Beside the
+  // state chain (which then holds at most a quarter of the units), half as
+  // many, so that every one of them finds a unit at once: a workgroup left
+  // waiting for one would hold back the chunks it is dealt.
+  const int64_t units = a.ready ? device_compute_units() / 2 : device_compute_units();
+  const int64_t ncu = (units + 7) / 8 * 8;
   const dim3 grid((unsigned)(nitems < ncu ? nitems : ncu));
   hipLaunchKernelGGL((chunk_prep_wide_kernel<MT, DK>), grid, dim3(512), 0, stream, a, (int)nitems);
   return hipGetLastError();
