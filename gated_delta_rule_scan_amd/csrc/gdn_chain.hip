@@ -534,7 +534,11 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         }
         if (add) acc += sp.pq[j];
         else if (BI) acc = canonical_nans(acc);  // a first visit: never the fill pattern
-        bstore16(rs, out_off[r] + out_at(c) + ct * 64, acc);
+        // a first visit's readout is the other direction's partial: agent
+        // scope, visible to it on any XCD once stored; sums and single-direction
+        // readouts are read by no later step of this launch
+        if (BI && !add) bstore16_agent(rs, out_off[r] + out_at(c) + ct * 64, acc);
+        else bstore16(rs, out_off[r] + out_at(c) + ct * 64, acc);
       }
     }
   };
