@@ -145,23 +145,28 @@ bool side_stream(int dev, SideStream** out) {
 
 // Whether the preparation pass runs concurrently with the state chain.
 //
-// Worth it only when the chain leaves most compute units free: preparation
-// workgroups beside the chain slow it down (they share L2 and the memory
-// path), and the preparation pass alone is short.  Measured on MI355X with
-// the bf16 column chain: 720p causal (128 chain workgroups on 256 units)
-// 1.80 ms concurrent against 1.74 ms serial (the chain 1.50 -> 1.79 ms
-// beside it); the streaming 480p frames (96 workgroups) 0.064 against 0.047
-// ms per frame; 480p and 720p bidirectional run serial.  So the overlap is
-// taken only below a quarter of the units.  (Bidirectional bf16 scans
-// always run serial; see forward_impl.)
+// Worth it only when the chain leaves compute units free and is long enough
+// to hide the pass: preparation workgroups beside the chain slow it down
+// (they share L2 and the memory path).  Measured on MI355X with the bf16
+// column chain, which prefetches a chunk's prepared tiles into L2 once its
+// ready flag reads ready: 720p causal (128 chain workgroups on 256 units,
+// 1182 chunks) 1.60 ms concurrent against 1.71 ms serial; the streaming 480p
+// frames (96 workgroups, 25 chunks) 0.060 against 0.045 ms per frame; 480p
+// and 720p bidirectional hold every unit and run serial.  So the overlap is
+// taken when the chain holds at most half of the units and has at least 128
+// chunks (the column chain), or at most a quarter of the units and 16 chunks
+// (the two-role chain, which has no such prefetch).  (Bidirectional
+// column-chain scans always run serial; see forward_impl.)
 //
 // Safe because the chain waits only for chunks the preparation pass
-// publishes, and a preparation workgroup can always be scheduled: there are
-// at most a quarter as many chain workgroups as compute units, so most of
-// the units hold none, however the workgroups are packed.  The preparation
-// pass is enqueued first, so a device that runs the two streams one after
-// the other still finishes it before the chain starts.
-bool may_overlap(int64_t chain_wgs, int64_t NC) {
+// publishes, and a preparation workgroup can always be scheduled: at most
+// half of the compute units hold a chain workgroup, and the preparation,
+// which never waits, is kept off those units beside a 16-column chain (it
+// then asks for more LDS than such a unit has left).  The preparation pass
+// is enqueued first, so a device that runs the two streams one after the
+// other still finishes it before the chain starts.
+bool may_overlap(int64_t chain_wgs, int64_t NC, bool column) {
+  if (column) return NC >= 128 && 2 * chain_wgs <= (int64_t)compute_units();
   constexpr int64_t kMinChunks = 16;  // below this the fork/join costs more than it hides
   return NC >= kMinChunks && 4 * chain_wgs <= (int64_t)compute_units();
 }
@@ -366,7 +371,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   // the combine flags ahead of the chunk-ready flags, so they must be clear
   // before it starts.
   const bool concurrent = pl.NC > 0 && !serial_only && !(p->options & GDN_OPT_SERIAL) && !capturing(stream) &&
-                          !a.part_flags && may_overlap(chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC);
+                          !a.part_flags && may_overlap(chain_blocks(B * H, (int)dv, pl.NT, pl.dirs), pl.NC, column);
   if (concurrent) {
     int dev = 0;
     SideStream* side = nullptr;

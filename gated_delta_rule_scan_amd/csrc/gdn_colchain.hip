@@ -811,10 +811,13 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     // its lines are in this XCD's L2.  (Measured at the 480p bidirectional
     // shape: state chain 1.20 -> 1.09 ms with the prefetch; two, five or
     // eight chunks ahead, or also the unshared value tile: slower.)  With the
-    // preparation running concurrently (a.ready set) only the raw k and q
-    // are prefetched: a prepared tile read before its ready flag could leave
-    // a stale line in this XCD's L2 (the preparation workgroup may run on
-    // another XCD), which the staging load would hit.
+    // preparation running concurrently (a.ready set) a chunk's prepared
+    // tiles are prefetched only once its ready flag, loaded a step before,
+    // has read ready: a prepared tile read before its flag could leave a
+    // stale line in this XCD's L2 (the preparation workgroup may run on
+    // another XCD), which the staging load would hit.  (Measured at the 720p
+    // causal shape: chain 1.80 ms beside the preparation with only k and q
+    // prefetched, 1.59 ms with the prepared tiles too.)
     constexpr int LPR = L::KROWB / 128;  // 128-byte lines per k (q) row
     constexpr int KL = L::KB / 128, TL = L::TB / 128;
     static_assert(KL <= 128 && TL <= 64, "a workgroup's lines fit one lane each when ntiles >= 2");
@@ -822,12 +825,13 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     const int lk = tile + ntiles * lane;  // this lane's line of the k (q) tile and of a triangle
     const uint32_t pfk = lk < KL ? (uint32_t)((lk / LPR) * HDB + (lk % LPR) * 128) : 0xFFFFFFF0u;
     const uint32_t pft = lk < TL ? (uint32_t)(lk * 128) : 0xFFFFFFF0u;
-    auto prefetch = [&](int c) {
+    auto prefetch = [&](int c, bool prepared) {
       const uint32_t rows = rows_of(c);
       const rsrc_t rk = make_rsrc(kbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
       const rsrc_t rq = make_rsrc(qbase + (size_t)c * C * HDB, (rows - 1) * HDB + DK * 2);
-      const rsrc_t rt = pf_prepared ? make_rsrc(trib + (size_t)c * L::TB, (uint32_t)L::TB) : rnone;
-      const rsrc_t rp = pf_prepared ? make_rsrc(pqkb + (size_t)c * L::TB, (uint32_t)L::TB) : rnone;
+      const bool pp = pf_prepared || prepared;
+      const rsrc_t rt = pp ? make_rsrc(trib + (size_t)c * L::TB, (uint32_t)L::TB) : rnone;
+      const rsrc_t rp = pp ? make_rsrc(pqkb + (size_t)c * L::TB, (uint32_t)L::TB) : rnone;
       dma4(rk, pfs, pfk);
       dma4(rt, pfs, pft);
       dma4(rq, pfs, pfk);
@@ -867,9 +871,11 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
     // One loader step: the same loads in the same order at every step (the
     // last steps restage the last chunk into idle slots), which the step-end
     // waits and the compiler's loop waits count on.  `fl` is chunk s + 1's
-    // ready flag, loaded two steps ago, and receives chunk s + 3's.
-    constexpr int kLTail = 5;  // loads left in flight at a step's end: the four prefetch loads and the flag
-    auto load_step = [&](lds_u8* cnext, lds_u8* rcur, uint32_t& fl, int s) {
+    // ready flag, loaded two steps ago, and receives chunk s + 3's; `gu` is
+    // chunk s + 3's, loaded a step ago (it gates that chunk's prepared-tile
+    // prefetch), and `gn` receives chunk s + 4's.
+    constexpr int kLTail = 6;  // loads left in flight at a step's end: the four prefetch loads and two flags
+    auto load_step = [&](lds_u8* cnext, lds_u8* rcur, uint32_t& fl, uint32_t gu, uint32_t& gn, int s) {
       const int cn = chunk_at(min(s + 1, NC - 1));
       const bool expired = ensure_ready(fl, cn);
       mem_fence_compiler();
@@ -878,9 +884,10 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
       mem_fence_compiler();
       stage_read(rcur, chunk_at(min(s, NC - 1)));
       mem_fence_compiler();
-      prefetch(chunk_at(min(s + 3, NC - 1)));
+      prefetch(chunk_at(min(s + 3, NC - 1)), __builtin_amdgcn_readfirstlane(gu) == 0u);
       mem_fence_compiler();
       fl = flag_of(s + 3);
+      gn = flag_of(s + 4);
       mem_fence_compiler();
     };
     if (NC > 0) {
@@ -894,20 +901,21 @@ __global__ __launch_bounds__(128 * NT + 64) void column_chain_kernel(ScanArgs a,
       mem_fence_compiler();
       stage_read(rs1, chunk_at(0));
       mem_fence_compiler();
-      prefetch(chunk_at(min(1, NC - 1)));
+      prefetch(chunk_at(min(1, NC - 1)), false);
       mem_fence_compiler();
-      uint32_t fb = flag_of(2);
+      uint32_t fb = flag_of(2), ga = flag_of(3), gb = 0u;
+      mem_fence_compiler();
       step_barrier<kLTail>();  // chunk 0 in the chain slot
       // steps 0 .. NC: the chain slot of chunk s + 1 and the readout slot of chunk s
       int s = 0;
       for (; s + 1 <= NC; s += 2) {
-        load_step(cs1, rs0, fa, s);
+        load_step(cs1, rs0, fa, ga, gb, s);
         step_barrier<kLTail>();
-        load_step(cs0, rs1, fb, s + 1);
+        load_step(cs0, rs1, fb, gb, ga, s + 1);
         step_barrier<kLTail>();
       }
       if (s <= NC) {
-        load_step(cs1, rs0, fa, s);
+        load_step(cs1, rs0, fa, ga, gb, s);
         step_barrier<kLTail>();
       }
       __builtin_amdgcn_s_waitcnt(kWaitVmem);  // the last restages and prefetch

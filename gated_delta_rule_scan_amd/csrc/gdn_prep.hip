@@ -641,8 +641,12 @@ hipError_t launch_prep(const ScanArgs& a, hipStream_t stream, hipFuncAttributes*
   // one per chunk id (numbering: see the kernel)
   const int64_t nblocks = a.ready ? slots * G * 8 : (slots * a.B + 7) / 8 * 8 * a.H;
   const dim3 grid((unsigned)nblocks);
-  if (plo) hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, true>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, false>), grid, dim3(256), 0, stream, a);
+  // Beside the state chain, 2 KB more LDS than the kernel declares: a
+  // 16-column chain workgroup leaves exactly the kernel's own 37 KB of a
+  // compute unit free, and the preparation is kept off the chain's units.
+  const unsigned dyn = a.ready ? 2048u : 0u;
+  if (plo) hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, true>), grid, dim3(256), dyn, stream, a);
+  else hipLaunchKernelGGL((chunk_prep_kernel<MT, DK, C, false>), grid, dim3(256), dyn, stream, a);
   return hipGetLastError();
 }
 

@@ -154,7 +154,7 @@ def test_first_call_of_the_process_inside_a_capture():
     """A fresh process whose first library call is captured (no eager warm-up
     has created the library's side stream): the capture takes the serial
     order, and each of three replays with new inputs equals an eager call
-    (which does take the concurrent path) bit for bit."""
+    bit for bit."""
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", _FIRST_CALL_IN_CAPTURE, root], capture_output=True, text=True,
                        timeout=240)

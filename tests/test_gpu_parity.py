@@ -92,10 +92,13 @@ def test_tile_width_does_not_change_results(dv_tile):
 @pytest.mark.parametrize("direction", ["fwd", "rev", "bi"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_concurrent_preparation_matches_serial(direction, dtype):
-    """41 chunks: the preparation pass runs beside the state chain (the chain
-    waits on per-chunk ready flags); the results are bitwise those of the
-    serial order, and within tolerance of the oracle."""
-    w = _case(dtype, direction, T=64 * 40 + 17, H=4, dk=64, dv=64, state_std=0.05, seed=13)
+    """131 chunks on 32 chain workgroups: single-direction scans run the
+    preparation pass beside the state chain (the chain waits on per-chunk
+    ready flags, and the bf16 chain prefetches a chunk's prepared tiles once
+    its flag reads ready); bidirectional bf16 scans run serially.  The
+    results are bitwise those of the serial order, and within tolerance of
+    the oracle."""
+    w = _case(dtype, direction, T=64 * 130 + 17, H=4, dk=64, dv=64, state_std=0.05, seed=13)
     x = synth.generate(w)
     o_ser, s_ser = run_gpu(x, direction, serial=True)
     o_con, s_con = run_gpu(x, direction)
@@ -122,7 +125,8 @@ def test_erase_free_variant(direction, dtype):
 
 
 def test_erase_free_variant_concurrent_matches_serial():
-    w = _case("bf16", "fwd", T=64 * 40 + 5, H=4, dk=128, dv=128, state_std=0.05, seed=15)
+    """The erase-free variant on the concurrent preparation path (131 chunks)."""
+    w = _case("bf16", "fwd", T=64 * 130 + 5, H=4, dk=128, dv=128, state_std=0.05, seed=15)
     x = synth.generate(w)
     o1, s1 = run_gpu(x, "fwd", serial=True, erase=False)
     o2, s2 = run_gpu(x, "fwd", erase=False)
@@ -174,21 +178,22 @@ def test_exclusive_readout_erase_free_d128(exclusive):
 
 
 def test_exclusive_readout_concurrent_matches_serial():
-    """41 chunks with both directions exclusive: the concurrent schedule equals the serial one bit for bit."""
-    w = _case("bf16", "bi", T=64 * 40 + 17, H=4, dk=64, dv=64, state_std=0.05, seed=18)
+    """131 chunks, the reverse scan reading before each token's own write, on
+    the concurrent preparation path: equal to the serial order bit for bit."""
+    w = _case("bf16", "rev", T=64 * 130 + 17, H=4, dk=64, dv=64, state_std=0.05, seed=18)
     x = synth.generate(w)
-    o_ser, s_ser = run_gpu(x, "bi", serial=True, exclusive="both")
-    o_con, s_con = run_gpu(x, "bi", exclusive="both")
+    o_ser, s_ser = run_gpu(x, "rev", serial=True, exclusive="rev")
+    o_con, s_con = run_gpu(x, "rev", exclusive="rev")
     assert np.array_equal(o_ser, o_con) and np.array_equal(s_ser, s_con)
-    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi",
-                                exclusive="both")
+    ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "rev",
+                                exclusive="rev")
     check(o_con, ref, TOL["bf16"], f"out {w} exclusive concurrent")
     check(s_con, ref_s, TOL["bf16"], f"state {w} exclusive concurrent")
 
 
 def test_calls_from_two_host_threads():
     """Two host threads, each on its own stream with its own buffers, call the
-    scan at the same time (bidirectional and causal, both on the concurrent
+    scan at the same time (bidirectional, serial, and causal on the concurrent
     preparation path, which shares the library stream and events); every
     result equals the same call made alone, bit for bit."""
     import threading
@@ -199,7 +204,7 @@ def test_calls_from_two_host_threads():
     from gdn_testutil import to_torch
 
     cases = [_case("bf16", "bi", T=64 * 30 + 7, H=4, dk=128, dv=128, state_std=0.05, seed=19),
-             _case("bf16", "fwd", T=64 * 40 + 3, H=3, dk=64, dv=64, state_std=0.05, seed=20)]
+             _case("bf16", "fwd", T=64 * 130 + 3, H=3, dk=64, dv=64, state_std=0.05, seed=20)]
     inputs = [{k: to_torch(v) for k, v in synth.generate(w).items()} for w in cases]
 
     def call(d, w, stream=None):
