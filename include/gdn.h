@@ -48,7 +48,8 @@
  * library allocates no device memory, does not synchronise and reads no
  * environment variables.  The work is ordered on `stream` (NULL: the default
  * stream) and completes asynchronously.  For long single-direction scans
- * with few (batch, head) sequences (and fp32 bidirectional ones) the chunk
+ * whose state chain leaves compute units free (and fp32 bidirectional ones
+ * with few sequences) the chunk
  * preparation runs concurrently with the state chain, on a library stream
  * forked from `stream` and joined back to it with events (one stream and two
  * events per device, created on the first such call and kept until the
