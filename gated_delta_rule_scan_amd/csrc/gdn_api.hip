@@ -68,12 +68,13 @@ gdn_status_t make_plan(const gdn_problem_t* p, int32_t direction, Plan* pl) {
   // with the other heads' -- through 32-bit byte offsets
   if ((p->T + 64) * p->H * (p->dk > p->dv ? p->dk : p->dv) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
   const int C = p->chunk == 0 ? 64 : p->chunk;
-  if (C != 32 && C != 64 && C != 128) return GDN_ERR_UNSUPPORTED;
+  if (C != 16 && C != 32 && C != 64 && C != 128) return GDN_ERR_UNSUPPORTED;
   const bool excl = (p->options & (GDN_OPT_EXCLUSIVE_FORWARD | GDN_OPT_EXCLUSIVE_REVERSE)) != 0;
-  // 128-token chunks run the two-role chain for both operand types, whose bf16
-  // readout carries the entry state and P in bf16 only: the exclusive readouts
-  // and the epilogue, which need their low parts, take 32- or 64-token chunks
-  if (C == 128 && p->dtype == GDN_DTYPE_BF16 && (excl || p->gate)) return GDN_ERR_UNSUPPORTED;
+  // 16- and 128-token chunks run the two-role chain for both operand types,
+  // whose bf16 readout carries the entry state and P in bf16 only: the
+  // exclusive readouts and the epilogue, which need their low parts, take 32-
+  // or 64-token chunks
+  if ((C == 16 || C == 128) && p->dtype == GDN_DTYPE_BF16 && (excl || p->gate)) return GDN_ERR_UNSUPPORTED;
   int NT = 0;  // 0: chosen at launch (any choice divides dv)
   if (p->dv_tile != 0) {
     if (p->dv_tile != 16 && p->dv_tile != 32) return GDN_ERR_UNSUPPORTED;
@@ -182,6 +183,7 @@ bool capturing(hipStream_t stream) {
 template <typename MT>
 prep_fn prep_for(int dk, int C) {
   if (C == 128) return dk == 64 ? launch_prep_wide<MT, 64> : launch_prep_wide<MT, 128>;
+  if (C == 16) return dk == 64 ? launch_prep<MT, 64, 16> : launch_prep<MT, 128, 16>;
   if (dk == 64) return C == 32 ? launch_prep<MT, 64, 32> : launch_prep<MT, 64, 64>;
   return C == 32 ? launch_prep<MT, 128, 32> : launch_prep<MT, 128, 64>;
 }
@@ -207,10 +209,11 @@ chain_fn column_chain_for3(int NT, int dirs, int prec) {
   return prec == 1 ? column_chain_for4<DK, C, 1>(NT, dirs) : column_chain_for4<DK, C, 0>(NT, dirs);
 }
 
-// bf16 operands: the column-owning chain; fp32 operands, and 128-token
-// chunks of either type: the two-role chain
+// bf16 operands: the column-owning chain; fp32 operands, and 16- and
+// 128-token chunks of either type: the two-role chain
 template <typename MT>
 chain_fn chain_for(int dk, int C, int NT, int dirs, int prec) {
+  if (C == 16) return dk == 64 ? chain_for3<MT, 64, 16>(NT, dirs) : chain_for3<MT, 128, 16>(NT, dirs);
   if (C == 128) {
     if (dk == 64) return chain_for3<MT, 64, 128>(NT, dirs);
     if constexpr (sizeof(MT) == 4) {
@@ -323,7 +326,7 @@ gdn_status_t forward_impl(const gdn_problem_t* p, void* ws_ptr, size_t ws_bytes,
   // chunks) recognises an unwritten partial by the preparation kernel's fill
   // of `out`; the column chain by per-chunk flags that the preparation kernel
   // clears
-  const bool column = bf && pl.C != 128;
+  const bool column = bf && pl.C != 128 && pl.C != 16;
   a.zero_out = pl.dirs == 2 && !column;
   if (pl.dirs == 2 && column && need_ws) a.part_flags = reinterpret_cast<unsigned*>(ws + pl.ws.pfl);
   if (pl.plo && need_ws) a.pq_lo = ws + pl.ws.pql;

@@ -58,11 +58,21 @@
 
 namespace gdn {
 
+// Tokens a chunk's products contract over: the chunk itself, padded to one
+// 32-wide matrix-core contraction for 16-token chunks (the padding entries
+// are zero in every operand, so the products are those of the 16 tokens).
+template <int C>
+struct ChainK {
+  static constexpr int CK = C < 32 ? 32 : C;
+  static constexpr int KCN = CK / 32;  // 32-token contraction slices per chunk
+};
+
 template <typename MT, int DK, int C, int NT>
 struct ChainSmem {
   static constexpr int ES = (int)sizeof(MT);
   static constexpr int EP = 16 / ES;
-  static constexpr int TP = C + EP;   // pitch of token-contiguous rows
+  static constexpr int CK = ChainK<C>::CK;
+  static constexpr int TP = CK + EP;  // pitch of token-contiguous rows
   static constexpr int SP = DK + EP;  // pitch of the state copy
   static constexpr int DT = 16 * NT;
   // k tile of the chunk.  bf16: row-major [C][DK + 8] (the transposed
@@ -73,7 +83,7 @@ struct ChainSmem {
   // fp32: token-contiguous [DK][TP].
   static constexpr bool KROW = ES == 2;
   static constexpr int KP = DK + 8;
-  static constexpr int k_elems = KROW ? C * KP : DK * TP;
+  static constexpr int k_elems = KROW ? CK * KP : DK * TP;
   // bf16 operands: Vnew and the scaled update vectors are carried as hi + lo
   // bf16 pairs (two products each), so their rounding stays at fp32 level.
   static constexpr bool SPLIT = ES == 2;
@@ -107,7 +117,7 @@ struct StageC {
   typedef typename Mma<MT>::frag frag;
   static constexpr int RPW = C > 64 ? C / 64 : 1;  // token row tiles per wave
   frag kf[RPW][DK / 32];
-  frag tf[RPW][C / 32];
+  frag tf[RPW][ChainK<C>::KCN];
   f32x4 cv[VTile<MT, 16 * NT, C>::NVI];
   uint32_t rdy;
 };
@@ -119,7 +129,7 @@ struct StageR {
   typedef typename Mma<MT>::frag frag;
   static constexpr int RPW = C > 64 ? C / 64 : 1;
   frag qf[RPW][DK / 32];
-  frag pf[RPW][C / 32];
+  frag pf[RPW][ChainK<C>::KCN];
   f32x4 pq[(C / 16 * NT + 3) / 4];
 };
 
@@ -137,13 +147,15 @@ template <typename MT>
 struct FragMask {
   static constexpr int NW = (int)(sizeof(typename Mma<MT>::frag) / 4);
   uint32_t m[NW];
-  __device__ __forceinline__ void make(int row, int col0, bool upper, bool diag, bool active) {
+  // `limit`: columns from it on lie past the chunk (16-token chunks, whose
+  // fragments span 32 columns) and are dropped
+  __device__ __forceinline__ void make(int row, int col0, bool upper, bool diag, bool active, int limit) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) m[i] = 0u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int col = col0 + e;
-      const bool keep = !active || (upper ? (col > row) : (col < row)) || (diag && col == row);
+      const bool keep = col < limit && (!active || (upper ? (col > row) : (col < row)) || (diag && col == row));
       if (keep) {
         if (sizeof(MT) == 2) m[e / 2] |= 0xffffu << (16 * (e % 2));
         else m[e] = 0xffffffffu;
@@ -240,6 +252,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   constexpr int TP = SM::TP, SP = SM::SP, DT = SM::DT;
   using VT = VTile<MT, DT, C>;
   constexpr int RT = C / 16;              // token row tiles per chunk
+  constexpr int KCN = ChainK<C>::KCN;     // 32-token contraction slices per chunk
   constexpr int NWC = 4;                        // chain waves; readout waves follow them
   constexpr int RPW = RT > NWC ? RT / NWC : 1;  // token row tiles per wave (wave wr: tiles wr + NWC r)
   constexpr int UPW = (RT * NT + NWC - 1) / NWC;  // chunk-output tiles per wave
@@ -320,14 +333,14 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   // with its diagonal -- the self terms -- unless this direction reads
   // before the token's own write, which is exactly P without its diagonal)
   const bool self = !(rev ? a.excl_rev : a.excl_fwd);
-  FragMask<MT> tmask[RPW][C / 32], pmask[RPW][C / 32];
+  FragMask<MT> tmask[RPW][KCN], pmask[RPW][KCN];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int kc = 0; kc < C / 32; ++kc) {
+    for (int kc = 0; kc < KCN; ++kc) {
       const int kcd = (wr % RT + NWC * r) / 2;  // k-chunk holding the row tile's diagonal
-      tmask[r][kc].make(kq_row[r], 32 * kc + 8 * g4, rev, false, kc == kcd);
-      pmask[r][kc].make(kq_row[r], 32 * kc + 8 * g4, rev, self, kc == kcd);
+      tmask[r][kc].make(kq_row[r], 32 * kc + 8 * g4, rev, false, kc == kcd, C);
+      pmask[r][kc].make(kq_row[r], 32 * kc + 8 * g4, rev, self, kc == kcd, C);
     }
   // readout offset of unit column tile 0 (transposed tile: token kq_row, four
   // columns from 4 g4)
@@ -337,11 +350,11 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   // bf16 operands: the self term's remainder enters as a diagonal fragment;
   // in k-chunk kc this lane (row kq_row of P) holds element `kq_row - 32 kc -
   // 8 g4` of it when that lies in 0..7 (only ever in the k-chunk of the diagonal)
-  FragMask<MT> diag_only[RPW][C / 32];
+  FragMask<MT> diag_only[RPW][KCN];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int kc = 0; kc < C / 32; ++kc) {
+    for (int kc = 0; kc < KCN; ++kc) {
 #pragma unroll
       for (int i = 0; i < FragMask<MT>::NW; ++i) diag_only[r][kc].m[i] = 0u;
       const int e0 = self ? kq_row[r] - 32 * kc - 8 * g4 : -1;
@@ -400,11 +413,11 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
   const rsrc_t rc = make_rsrc(cbase, cbytes);
   const rsrc_t ro = make_rsrc(obase, (uint32_t)(T - 1) * HOB + DT * 4);
   const uint32_t tri_bytes = (uint32_t)NC * (C * C * ES);
-  rsrc_t rtk[RPW][C / 32], rpk[RPW][C / 32];  // triangle k-chunks a row tile never needs: zeros
+  rsrc_t rtk[RPW][KCN], rpk[RPW][KCN];  // triangle k-chunks a row tile never needs: zeros
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int kc = 0; kc < C / 32; ++kc) {
+    for (int kc = 0; kc < KCN; ++kc) {
       const bool need = tri_needed(rev, kc, wr % RT + NWC * r);
       rtk[r][kc] = make_rsrc(trib, need ? tri_bytes : 0u);
       rpk[r][kc] = make_rsrc(pqkb, need ? tri_bytes : 0u);
@@ -449,7 +462,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     for (int r = 0; r < RPW; ++r) {
       const uint32_t o = tri_off[r] + (uint32_t)c * (C * C * ES);
 #pragma unroll
-      for (int kc = 0; kc < C / 32; ++kc) f.tf[r][kc] = bload_frag<MT>(rtk[r][kc], o + 32 * kc * ES);
+      for (int kc = 0; kc < KCN; ++kc) f.tf[r][kc] = bload_frag<MT>(rtk[r][kc], o + 32 * kc * ES);
     }
   };
   auto load_pf = [&](auto& f, int c) {  // readout waves
@@ -457,13 +470,21 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
     for (int r = 0; r < RPW; ++r) {
       const uint32_t o = tri_off[r] + (uint32_t)c * (C * C * ES);
 #pragma unroll
-      for (int kc = 0; kc < C / 32; ++kc) f.pf[r][kc] = bload_frag<MT>(rpk[r][kc], o + 32 * kc * ES);
+      for (int kc = 0; kc < KCN; ++kc) f.pf[r][kc] = bload_frag<MT>(rpk[r][kc], o + 32 * kc * ES);
     }
   };
   auto stash = [&](const auto& f, int buf) {  // group-shared pieces of a loaded stage -> LDS
 #pragma unroll
     for (int n = 0; n < VT::NVI; ++n) *reinterpret_cast<f32x4*>(&stg[buf][c_lds[n]]) = f.cv[n];
   };
+
+  // 16-token chunks: the padding tokens of every token-contiguous operand
+  // (the k tile's rows or columns 16..31, the value arrays' columns) stay
+  // zero for the whole launch; the steps write only the chunk's own tokens
+  if constexpr (C < 32) {
+    for (int i = threadIdx.x; i < SM::per_group; i += 64 * ChainWaves<C, NT>::value) smem[i] = (MT)0.f;
+    __syncthreads();
+  }
 
   // ---- initial state into accumulators (S^T tiles) and the operand copy ----
   f32x4 Sacc[SUPW];
@@ -520,7 +541,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         const int ct = u / RT, r = rj(j);
         f32x4 acc = Zp[j] * zs[r];
 #pragma unroll
-        for (int kc = 0; kc < C / 32; ++kc) {
+        for (int kc = 0; kc < KCN; ++kc) {
           const frag pf = pmask[r][kc].apply(sp.pf[r][kc]);
           const int o = (16 * ct + l16) * TP + 32 * kc + 8 * g4;
           const frag vh = M::load(VnT + o);
@@ -630,7 +651,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
         const int ct = u / RT, r = rj(j);
         f32x4 acc = X[j];
 #pragma unroll
-        for (int kc = 0; kc < C / 32; ++kc)
+        for (int kc = 0; kc < KCN; ++kc)
           acc = M::mma(tmask[r][kc].apply(st.tf[r][kc]), M::load(XT + (16 * ct + l16) * TP + 32 * kc + 8 * g4), acc);
         const int o = (16 * ct + l16) * TP + o_row0[r];
         f32x4 vs;
@@ -659,11 +680,11 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
       constexpr int JT = SUPW / JS;                   // dv tiles per wave
       auto srt_of = [&](int js) { return (wr % SRT) + NWC * js; };
       auto sct_of = [&](int jt) { return SRT >= NWC ? jt : wr / SRT + (NWC / SRT) * jt; };
-      frag ka[JS][C / 32], vh[JT][C / 32], vl[JT][C / 32];
+      frag ka[JS][KCN], vh[JT][KCN], vl[JT][KCN];
 #pragma unroll
       for (int js = 0; js < JS; ++js)
 #pragma unroll
-        for (int kc = 0; kc < C / 32; ++kc) {
+        for (int kc = 0; kc < KCN; ++kc) {
           const int srt = srt_of(js);
           if constexpr (KROW) {
             ka[js][kc] = load_kt_frag(KT, KP, 32 * kc, 16 * srt, l16, g4);
@@ -674,7 +695,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-        for (int kc = 0; kc < C / 32; ++kc) {
+        for (int kc = 0; kc < KCN; ++kc) {
           const int o = (16 * sct_of(jt) + l16) * TP + 32 * kc + 8 * g4;
           vh[jt][kc] = M::load(VsT + o);
           if (SPLIT) vl[jt][kc] = M::load(VsL + o);
@@ -686,7 +707,7 @@ __global__ __launch_bounds__((64 * ChainWaves<C, NT>::value)) void chain_kernel(
           const int j = jt * JS + js;  // tile u = wr + NWC j: srt = u % SRT = srt_of(js), sct = u / SRT = sct_of(jt)
           f32x4 acc = Sacc[j] * gn;
 #pragma unroll
-          for (int kc = 0; kc < C / 32; ++kc) {
+          for (int kc = 0; kc < KCN; ++kc) {
             acc = M::mma(ka[js][kc], vh[jt][kc], acc);
             if (SPLIT) acc = M::mma(ka[js][kc], vl[jt][kc], acc);
           }
@@ -841,6 +862,11 @@ GDN_INST_CHAIN_N(bf16, 64, 32)
 GDN_INST_CHAIN_N(bf16, 64, 64)
 GDN_INST_CHAIN_N(bf16, 128, 32)
 GDN_INST_CHAIN_N(bf16, 128, 64)
+// 16-token chunks (contractions padded to 32 tokens)
+GDN_INST_CHAIN_N(float, 64, 16)
+GDN_INST_CHAIN_N(float, 128, 16)
+GDN_INST_CHAIN_N(bf16, 64, 16)
+GDN_INST_CHAIN_N(bf16, 128, 16)
 // 128-token chunks: fp32 operands with d = 128 fit 16-column tiles only
 GDN_INST_CHAIN_N(float, 64, 128)
 GDN_INST_CHAIN_D(float, 128, 128, 1)

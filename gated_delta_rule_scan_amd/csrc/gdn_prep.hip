@@ -189,8 +189,11 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   // order), waves 2 and 3 the forward and reverse write strengths.
   constexpr int PR = DK / EP;    // pieces per row
   constexpr int RPI = 256 / PR;  // rows per pass of the workgroup
-  constexpr int NPT = C / RPI;   // pieces per thread and matrix
-  static_assert(256 % PR == 0 && C % RPI == 0, "piece split");
+  constexpr int NPT = (C + RPI - 1) / RPI;  // pieces per thread and matrix
+  static_assert(256 % PR == 0 && (C % RPI == 0 || NPT == 1), "piece split");
+  // a 16-token chunk with 64-wide bf16 rows: a pass covers 32 rows, and the
+  // lanes of rows 16..31 take part in the row sums but store nothing
+  constexpr bool ROWS_PAST = C % RPI != 0;
   const int prow = tid / PR, pcol = (tid % PR) * EP;
   const uint32_t rowb = (uint32_t)(H * DK * (int64_t)sizeof(MT));
   const size_t kq0 = (size_t)((b * T + t0) * H + h) * DK;
@@ -254,6 +257,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
       sk = group_sum<PR>(sk);
       sqk = group_sum<PR>(sqk);
       const int row = prow + RPI * i;
+      if (ROWS_PAST && row >= C) continue;
       if (tid % PR == 0) {
         // 1 / max(|x|, eps) as a reciprocal square root (one rounding more
         // than a divide: relative error ~1e-7)
@@ -564,10 +568,10 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
       } else {
         if (rev_on) { column(1, 2); column(1, 1); }
       }
-    } else {
+    } else if constexpr (NB == 2) {
       if (wave == 0 && fwd_on) column(0, 0);
       if (wave == 1 && rev_on) column(1, 1);
-    }
+    }  // one block (16-token chunks): no off-diagonal blocks
   }
   __syncthreads();
 
@@ -660,5 +664,9 @@ GDN_INST_PREP(bf16, 64, 32)
 GDN_INST_PREP(bf16, 64, 64)
 GDN_INST_PREP(bf16, 128, 32)
 GDN_INST_PREP(bf16, 128, 64)
+GDN_INST_PREP(float, 64, 16)
+GDN_INST_PREP(float, 128, 16)
+GDN_INST_PREP(bf16, 64, 16)
+GDN_INST_PREP(bf16, 128, 16)
 
 }  // namespace gdn

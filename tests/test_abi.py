@@ -101,7 +101,7 @@ def test_workspace_bytes_of_exclusive_readouts():
                 == gdn.workspace_bytes(1, 300, 2, 64, 64, "f32", "bi"))
 
 
-@pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=80), dict(chunk=48), dict(chunk=16), dict(dv_tile=64),
+@pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=80), dict(chunk=48), dict(chunk=8), dict(chunk=256), dict(dv_tile=64),
                                 dict(dtype=7), dict(B=0), dict(H=0), dict(T=-1), dict(B=300, H=300),
                                 dict(dv_tile=48), dict(T=1 << 20, H=8, dk=128, dv=128)])
 def test_workspace_bytes_rejects(kw):
@@ -341,3 +341,25 @@ def test_chunk128_is_accepted_with_its_limits():
     assert gdn.gdn_workspace_bytes(_prob(chunk=128, dtype=gdn.GDN_DTYPE_F32, dk=64, dv=64, dv_tile=32),
                                    gdn.GDN_DIR_FORWARD) > 0
     assert gdn.gdn_workspace_bytes(_prob(chunk=128, dv_tile=32), gdn.GDN_DIR_FORWARD) > 0
+
+
+def test_chunk16_is_accepted_with_its_limits():
+    """16-token chunks: accepted for both operand types in every direction;
+    bf16 exclusive readouts and the bf16 epilogue are unsupported there (as at
+    128 tokens), fp32 takes every option."""
+    for dtype in (gdn.GDN_DTYPE_BF16, gdn.GDN_DTYPE_F32):
+        for d in (gdn.GDN_DIR_FORWARD, gdn.GDN_DIR_REVERSE, gdn.GDN_DIR_BIDIRECTIONAL):
+            assert gdn.gdn_workspace_bytes(_prob(chunk=16, dtype=dtype), d) > 0
+        for dv_tile in (16, 32):
+            assert gdn.gdn_workspace_bytes(_prob(chunk=16, dtype=dtype, dv_tile=dv_tile), gdn.GDN_DIR_FORWARD) > 0
+    # 19 chunks of 300 tokens, 2 heads: the triangles are 16 x 16 per chunk
+    assert gdn.gdn_workspace_bytes(_prob(chunk=16), gdn.GDN_DIR_FORWARD) >= 2 * 19 * 2 * 16 * 16 * 2
+    p = _prob(chunk=16)
+    p.options = gdn.GDN_OPT_EXCLUSIVE_FORWARD
+    assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_BIDIRECTIONAL) == 0
+    p = _prob(chunk=16, dtype=gdn.GDN_DTYPE_F32)
+    p.options = gdn.GDN_OPT_EXCLUSIVE_FORWARD
+    assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_BIDIRECTIONAL) > 0
+    p = _prob(chunk=16)
+    p.gate, p.norm_weight, p.norm_eps = 1 << 40, 1 << 41, 1e-6  # host-side validation only
+    assert gdn.gdn_workspace_bytes(p, gdn.GDN_DIR_FORWARD) == 0

@@ -91,19 +91,19 @@ def test_chunk128_single_token_and_exact_multiple():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_chunk_length_invariance(dtype):
-    """The same inputs at chunk lengths 32, 64 and 128: every output and final
-    state within the bar of the oracle, and of each other (the chunked form is
-    exact, so only rounding may differ between chunk lengths)."""
+    """The same inputs at chunk lengths 16, 32, 64 and 128: every output and
+    final state within the bar of the oracle, and of each other (the chunked
+    form is exact, so only rounding may differ between chunk lengths)."""
     w = _case(dtype, "bi", T=520, H=2, dk=128, dv=128, state_std=0.05, seed=38)
     x = synth.generate(w)
     ref, ref_s = oracle.forward(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["state_in"], "bi")
     runs = {}
-    for C in (32, 64, 128):
+    for C in (16, 32, 64, 128):
         out, s = run_gpu(x, "bi", chunk=C)
         check(out, ref, TOL[dtype], f"out C={C}")
         check(s, ref_s, TOL[dtype], f"state C={C}")
         runs[C] = (out, s)
-    for C in (32, 64):
+    for C in (16, 32, 64):
         e_o, _, _ = rel_err(runs[128][0], runs[C][0])
         e_s, _, _ = rel_err(runs[128][1], runs[C][1])
         print(f"\n{dtype}: C=128 against C={C}: out {e_o:.2e} state {e_s:.2e} x RMS", flush=True)

@@ -41,17 +41,18 @@ def _layout(nbh, nc, dirs, mt, C):
     return tri, pqk, sc, pdg
 
 
-# every block count of the inverse (two 16-token blocks per side at C = 32,
-# four at C = 64, eight at C = 128: the 128-token preparation kernel) and both
-# head widths of the staged q / k
-@pytest.mark.parametrize("C,d", [(64, 64), (32, 64), (64, 128), (32, 128), (128, 64), (128, 128)])
+# every block count of the inverse (one 16-token block per side at C = 16,
+# two at C = 32, four at C = 64, eight at C = 128: the 128-token preparation
+# kernel) and both head widths of the staged q / k
+@pytest.mark.parametrize("C,d", [(64, 64), (32, 64), (64, 128), (32, 128), (128, 64), (128, 128), (16, 64),
+                                 (16, 128)])
 @pytest.mark.parametrize("dtype,tol", [("f32", 2e-5), ("bf16", 1e-2)])
 def test_chunk_preparation_outputs(dtype, tol, C, d):
     import torch
 
     import gated_delta_rule_scan_amd as gdn
 
-    B, H, T = 1, 2, 150  # the last chunk ragged: 22 tokens (of 128 or 64, or of 32)
+    B, H, T = 1, 2, 150  # the last chunk ragged: 22 tokens of 128, 64 or 32, 6 of 16
     w = synth.Workload("prep", B, H, T, d, d, dtype, "bi", 3.0, 0.02, 61)
     x = synth.generate(w)
     dd = {k: to_torch(v) for k, v in x.items()}
