@@ -135,16 +135,17 @@ typedef enum {
 } gdn_option_t;
 
 /* Problem description.  Supported: dk in {64, 128}; dv in {64, 128};
- * chunk in {0 (= 64), 32, 64, 128} (the chunked form is exact at any chunk
+ * chunk in {0 (= 64), 16, 32, 64, 128} (the chunked form is exact at any chunk
  * length: "Video DeltaNet", Key Contributions item 4, chunk-wise scans; results
  * agree between chunk lengths to rounding, 64 is the fastest on MI355X);
  * dv_tile in {0, 16, 32} (0: 32 when 16-wide
  * state-chain workgroups would outnumber the compute units of the current
  * device, else 16; exclusive readouts on bf16 operands take 16 and reject
  * 32: they carry the state and the decayed q.k tile as bf16 hi + lo parts,
- * whose staging fits 16-column tiles only).  128-token chunks: bf16 operands
- * reject the exclusive readouts and the readout epilogue (their low parts are
- * carried by the 32/64-token chain only), and fp32 operands with dk = 128
+ * whose staging fits 16-column tiles only).  16- and 128-token chunks: bf16
+ * operands reject the exclusive readouts and the readout epilogue (their low
+ * parts are carried by the 32/64-token chain only); 128-token chunks: fp32
+ * operands with dk = 128
  * take dv_tile 16 and reject 32 (the chain's staging would exceed a compute
  * unit's LDS); B, H >= 1, B*H <= 65535;
  * 0 <= T <= 2^30 and
