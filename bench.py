@@ -568,7 +568,7 @@ def run_stream(args, w) -> int:
     s0 = _dev(x["state_in"]) if x["state_in"] is not None else None
     state = torch.zeros((w.dirs, w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
     outs = [torch.empty((w.B, f1 - f0, w.H, w.dv), dtype=torch.float32, device="cuda") for f0, f1 in bounds]
-    nws = gdn.workspace_bytes(w.B, fr, w.H, w.dk, w.dv, w.dtype, w.direction)
+    nws = gdn.workspace_bytes(w.B, fr, w.H, w.dk, w.dv, w.dtype, w.direction, args.chunk, args.dv_tile)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
 
     def reset():
@@ -581,7 +581,7 @@ def run_stream(args, w) -> int:
         for i, f in enumerate(frames):
             gdn.forward(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], state, w.direction, out=outs[i],
                         state_out=state, workspace=ws, timing_events=None if evs is None else evs.ptr(4 * i),
-                        serial=args.serial)
+                        serial=args.serial, chunk=args.chunk, dv_tile=args.dv_tile)
 
     for _ in range(max(1, args.warmup)):
         reset()
@@ -646,7 +646,7 @@ def run_stream(args, w) -> int:
         "ms_per_step": ms_eager, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "frame": fr, "frames": NF, "dk": w.dk,
-                   "dv": w.dv, "direction": w.direction, "chunk": 64, "calls_per_step": NF,
+                   "dv": w.dv, "direction": w.direction, "chunk": args.chunk or 64, "calls_per_step": NF,
                    "state": "carried in place across the calls",
                    "inputs": "seeded synthetic video-latent-shaped (synth.WORKLOADS)"},
         "ms_per_frame_eager": ms_eager / NF,
