@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   const size_t nch = (size_t)a.B * a.H * a.NC;
   const int nrows = (int)(T - t0 < C ? T - t0 : C);  // valid tokens of this chunk (>= 1)
   constexpr double kLog2eD = 1.4426950408889634;
+  const bool ag = ws_agent_stores(a);  // workspace stores at agent scope (see there)
 
   // ---- every global read of the kernel, issued at once ----
   // Raw q and k rows (16-byte pieces; rows past the sequence read as zero),
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
     const float fn = __uint_as_float(0xFFFFFFFFu);
     const f32x4 fill = f32x4{fn, fn, fn, fn};
     for (int p = tid; p < (C << sh); p += 256)
-      bstore16_agent(ro, (uint32_t)(p >> sh) * orow + (uint32_t)(p & ((1 << sh) - 1)) * 16u, fill);
+      bstore16_ws(ag, ro, (uint32_t)(p >> sh) * orow + (uint32_t)(p & ((1 << sh) - 1)) * 16u, fill);
   }
   __syncthreads();
 
@@ -413,10 +414,10 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
         uint32_t w[2], wl[2];
         __builtin_memcpy(w, &ph, 8);
         __builtin_memcpy(wl, &pl, 8);
-        bstore8_agent(rpq, off, w[0], w[1]);
-        if constexpr (PLO) bstore8_agent(rpl, off, wl[0], wl[1]);
+        bstore8_ws(ag, rpq, off, w[0], w[1]);
+        if constexpr (PLO) bstore8_ws(ag, rpl, off, wl[0], wl[1]);
       } else {
-        bstore16_agent(rpq, off, f32x4{pv[0], pv[1], pv[2], pv[3]});
+        bstore16_ws(ag, rpq, off, f32x4{pv[0], pv[1], pv[2], pv[3]});
       }
     }
   }
@@ -504,12 +505,12 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
       const float eg = exp2f((float)g);
       const rsrc_t rs = make_rsrc(a.sc + (slot * nch + cid) * C, C * 16);
       // {beta, e^g rk (erase term of the pseudo-values; 0 without it), e^g rq, e^(gn-g) rk}
-      bstore16_agent(rs, tok * 16,
+      bstore16_ws(ag, rs, tok * 16,
                      in ? f32x4{s_bt[dir][tok], a.erase ? eg * rk : 0.f, eg * rq, exp2f((float)(gl - g)) * rk}
                         : f32x4{0.f, 0.f, 0.f, 0.f});
       const rsrc_t rp = make_rsrc(a.pdg + ((size_t)slot * nch + cid) * pdg_stride(C), (C + 4) * 4);
-      bstore4_agent(rp, (4 + tok) * 4, self - (float)self_mt);
-      if (tok < 4) bstore4_agent(rp, tok * 4, tok == 0 ? exp2f((float)gl) : 0.f);
+      bstore4_ws(ag, rp, (4 + tok) * 4, self - (float)self_mt);
+      if (tok < 4) bstore4_ws(ag, rp, tok * 4, tok == 0 ? exp2f((float)gl) : 0.f);
     }
   }
   __syncthreads();
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
       }
       f32x4 t16;
       __builtin_memcpy(&t16, tv, 16);
-      bstore16_agent(rt, p * 16, t16);
+      bstore16_ws(ag, rt, p * 16, t16);
     }
   }
 

@@ -160,6 +160,7 @@ __global__ __launch_bounds__(512) void chunk_prep_wide_kernel(ScanArgs a, int ni
   const size_t nch = (size_t)a.B * a.H * a.NC;
   constexpr double kLog2eD = 1.4426950408889634;
   const float erase_w = a.erase ? 1.f : 0.f;
+  const bool ag = ws_agent_stores(a);  // workspace stores at agent scope (see there)
   const uint32_t rowb = (uint32_t)(H * DK * ES);
   const int tok = tid >> 2, part = tid & 3;
 
@@ -343,9 +344,9 @@ __global__ __launch_bounds__(512) void chunk_prep_wide_kernel(ScanArgs a, int ni
           for (int i = 0; i < 4; ++i) ph[i] = (bf16)pv[i];
           uint32_t w2[2];
           __builtin_memcpy(w2, &ph, 8);
-          bstore8_agent(rpq, off, w2[0], w2[1]);
+          bstore8_ws(ag, rpq, off, w2[0], w2[1]);
         } else {
-          bstore16_agent(rpq, off, f32x4{pv[0], pv[1], pv[2], pv[3]});
+          bstore16_ws(ag, rpq, off, f32x4{pv[0], pv[1], pv[2], pv[3]});
         }
       }
     }
@@ -415,12 +416,12 @@ __global__ __launch_bounds__(512) void chunk_prep_wide_kernel(ScanArgs a, int ni
         const float eg = exp2f((float)g);
         const rsrc_t rs = make_rsrc(a.sc + (slot * nch + cid) * C, C * 16);
         // {beta, e^g rk (erase term of the pseudo-values; 0 without it), e^g rq, e^(gn-g) rk}
-        bstore16_agent(rs, t * 16,
+        bstore16_ws(ag, rs, t * 16,
                        in ? f32x4{s_bt[dir][t], a.erase ? eg * rkt : 0.f, eg * rqt, exp2f((float)(gl - g)) * rkt}
                           : f32x4{0.f, 0.f, 0.f, 0.f});
         const rsrc_t rp = make_rsrc(a.pdg + ((size_t)slot * nch + cid) * pdg_stride(C), (C + 4) * 4);
-        bstore4_agent(rp, (4 + t) * 4, self - (float)self_mt);
-        if (t < 4) bstore4_agent(rp, t * 4, t == 0 ? exp2f((float)gl) : 0.f);
+        bstore4_ws(ag, rp, (4 + t) * 4, self - (float)self_mt);
+        if (t < 4) bstore4_ws(ag, rp, t * 4, t == 0 ? exp2f((float)gl) : 0.f);
       }
     }
     lds_barrier();
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(512) void chunk_prep_wide_kernel(ScanArgs a, int ni
         }
         f32x4 t16;
         __builtin_memcpy(&t16, tv, 16);
-        bstore16_agent(rt, (uint32_t)(pp * 16), t16);
+        bstore16_ws(ag, rt, (uint32_t)(pp * 16), t16);
       }
     }
 
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(512) void chunk_prep_wide_kernel(ScanArgs a, int ni
       const float fn = __uint_as_float(0xFFFFFFFFu);
       const f32x4 fill = f32x4{fn, fn, fn, fn};
       for (int pp = tid; pp < (C << sh); pp += 512)
-        bstore16_agent(ro, (uint32_t)(pp >> sh) * orow + (uint32_t)(pp & ((1 << sh) - 1)) * 16u, fill);
+        bstore16_ws(ag, ro, (uint32_t)(pp >> sh) * orow + (uint32_t)(pp & ((1 << sh) - 1)) * 16u, fill);
     }
 
     // ---- publish (concurrent preparation): every store above is
