@@ -18,10 +18,12 @@
 // shorter chunks, so this kernel keeps L and the inverse as two fp32 128 x 128
 // tiles in LDS (135 KB, one workgroup per compute unit) and takes the plain
 // blocked route:
-//   1. row norms and raw self terms q.k (four lanes per token), gates;
+//   1. row norms and raw self terms q.k (four lanes per token), gates; the
+//      chunk's raw q and k rows staged in LDS (in the space of the two
+//      tiles, before L exists);
 //   2. chunk-local cumulative log-gates in double (one wave per direction);
-//      the Gram products K K^T and Q K^T on the matrix cores from operands
-//      read straight from global memory (eight 16-row tiles per wave);
+//      the Gram products K K^T and Q K^T on the matrix cores from the staged
+//      rows (wave w: row tile w against all eight column tiles);
 //   3. L into LDS, the decayed q.k tile to the workspace;
 //   4. the sixteen diagonal 16 x 16 blocks of (I + L)^{-1} by substitution,
 //      one column per thread; meanwhile the per-token scales;
