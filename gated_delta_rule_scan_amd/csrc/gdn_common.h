@@ -293,10 +293,15 @@ struct ScanArgs {
   int excl_fwd, excl_rev;  // 1: that direction reads before the token's own write (no self term)
 };
 
-// Whether a preparation pass stores its workspace at agent scope (see
-// bstore16_ws): beside the chain, or for a small pass.
+// Whether a preparation pass at chunk length C stores its workspace at
+// agent scope (see bstore16_ws): beside the chain, or for a small pass; and
+// always at 16 and 128 tokens, where plain stores measured slower on large
+// passes too (480p bidirectional, 128-token chunks: 0.669 against 0.688 ms;
+// 16-token chunks: 0.213 against 0.222 ms).
+template <int C>
 __device__ __forceinline__ bool ws_agent_stores(const ScanArgs& a) {
   constexpr int64_t kSmallPass = 2048;  // (chunk, sequence) items
+  if constexpr (C == 16 || C == 128) return true;
   return a.ready != nullptr || a.NC * a.B * a.H < kSmallPass;
 }
 

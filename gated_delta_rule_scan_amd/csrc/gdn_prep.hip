@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256, (PLO || sizeof(MT) == 4) ? 2 : 4) void chunk_p
   const size_t nch = (size_t)a.B * a.H * a.NC;
   const int nrows = (int)(T - t0 < C ? T - t0 : C);  // valid tokens of this chunk (>= 1)
   constexpr double kLog2eD = 1.4426950408889634;
-  const bool ag = ws_agent_stores(a);  // workspace stores at agent scope (see there)
+  const bool ag = ws_agent_stores<C>(a);  // workspace stores at agent scope (see there)
 
   // ---- every global read of the kernel, issued at once ----
   // Raw q and k rows (16-byte pieces; rows past the sequence read as zero),

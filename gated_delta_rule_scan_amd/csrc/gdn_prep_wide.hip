@@ -162,7 +162,7 @@ __global__ __launch_bounds__(512) void chunk_prep_wide_kernel(ScanArgs a, int ni
   const size_t nch = (size_t)a.B * a.H * a.NC;
   constexpr double kLog2eD = 1.4426950408889634;
   const float erase_w = a.erase ? 1.f : 0.f;
-  const bool ag = ws_agent_stores(a);  // workspace stores at agent scope (see there)
+  const bool ag = ws_agent_stores<C>(a);  // workspace stores at agent scope (see there)
   const uint32_t rowb = (uint32_t)(H * DK * ES);
   const int tok = tid >> 2, part = tid & 3;
 
