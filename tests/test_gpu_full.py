@@ -76,6 +76,37 @@ def test_full_size_sampled_heads(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,serial", [("bidir480", False), ("causal720", True), ("causal720", False)])
+def test_full_size_chunk32_sampled_heads(name, serial):
+    """32-token chunks at full size: the preparation before the chain over
+    tens of thousands of (chunk, sequence) items (the workspace stored with
+    the default cache policy, read by the chain after the preparation kernel
+    has ended), and at causal720 also beside the chain (agent-scope stores
+    published by per-chunk ready flags).  The GPU computes every head, the
+    oracle two (batch, head) chains in full."""
+    import torch
+
+    import gated_delta_rule_scan_amd as gdn
+
+    w = synth.WORKLOADS[name]
+    print(f"\n[{name} C=32 serial={serial}] generating {w}", flush=True)
+    x = synth.generate(w)
+    d = {k: to_torch(v) for k, v in x.items()}
+    out, s_out = gdn.forward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["state_in"], w.direction, chunk=32,
+                             serial=serial)
+    torch.cuda.synchronize()
+    hs = list(dict.fromkeys([(0, 0), (w.B - 1, w.H - 1)]))
+    print(f"[{name} C=32] oracle on heads {hs}", flush=True)
+    ref, ref_s = oracle.forward_heads(x, hs, w.direction)
+    got = np.stack([out[b, :, h].cpu().numpy() for b, h in hs])
+    got_s = np.stack([s_out[:, b, h].cpu().numpy() for b, h in hs], axis=1)
+    e_o = check(got, ref, TOL[w.dtype], f"{name} C=32 out")
+    e_s = check(got_s, ref_s, TOL[w.dtype], f"{name} C=32 state")
+    print(f"[{name} C=32 serial={serial}] max|err|/RMS: out {e_o:.3e}  state {e_s:.3e}", flush=True)
+    del d, out, s_out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["bidir480", "causal720", "bidir720"])
 def test_full_size_every_head(name):
     """Every (batch, head) chain of the full-size workload against the oracle
