@@ -522,6 +522,19 @@ def main() -> int:
                      "avg_launch_ms": kt[dom], "source_hash": kernel_source_hash(dom_name)},
         "wall_s_timed": wall,
     }
+    if dom == "chain" and prep_ms > 0:
+        # the path's other kernel, the same way: its boundary reads (q, k and
+        # the gates, each once) per launch over its average launch time
+        pname = prep_kernel_name(args.chunk)
+        pa = kb["prep"] / (prep_ms * 1e-3) / 1e9
+        res["prep_roofline"] = {
+            "kernel": pname, "bound": "hbm", "achieved": pa, "peak": MI355X_HBM_GBS, "unit": "GB/s",
+            "frac": pa / MI355X_HBM_GBS,
+            "traffic": (measured_traffic(pname, args.workload)
+                        if not args.no_erase and args.exclusive == "none" and not args.chunk
+                        and not args.dv_tile and not args.epilogue else None),
+            "alg_bytes_per_launch": kb["prep"], "avg_launch_ms": prep_ms, "beside_chain": bool(concurrent),
+            "source_hash": kernel_source_hash(pname)}
     if not args.no_parity:
         res["parity"] = sampled_parity(w, x, out, s_out, w.direction, erase=not args.no_erase,
                                        exclusive=args.exclusive, threads=host_cores()[0],
